@@ -35,9 +35,12 @@ Readings where the pages are silent (each one is also listed in the design doc):
   2j+1 in its high nibble; scales are one byte per block, row-major.
 
 Exactness: the inputs here are BF16 or FP32 (at most 24 significant bits) and g
-is FP32.  The rounding thresholds used below, 6*g*m for an E4M3 midpoint m and
-t*s*g for an E2M1 midpoint t, have at most 31 significant bits, so they are
-exact FP64 numbers and every comparison below decides on the exact reals.
+is FP32.  The rounding thresholds, 6*g*m for an E4M3 midpoint m and t*s*g for
+an E2M1 midpoint t, have at most 31 significant bits, so they are exact FP64
+numbers.  An input equal to a threshold is therefore detected exactly, and an
+input that differs from one differs by at least 2^-32 of its value; an FP64
+quotient (relative error 2^-53) thus lands on the same side of every midpoint
+as the real quotient.  Every decision below is the exact-real decision.
 """
 from __future__ import annotations
 
@@ -103,6 +106,19 @@ def round_quotient_to_grid(num: np.ndarray, den: np.ndarray, grid: np.ndarray) -
     den = np.asarray(den, dtype=np.float64)
     mids = _midpoints(grid)
     upper_is_even = (np.arange(1, len(grid)) % 2) == 0
+    if den.ndim == 0 and len(grid) <= 16:
+        # Few midpoints: count the crossed ones directly.
+        out = np.zeros(num.shape, dtype=np.int64)
+        for m, up in zip(float(den) * mids, upper_is_even):
+            out += (num > m) | ((num == m) & up)
+        return out
+    if den.ndim == 0:
+        # One denominator for all: the thresholds den*mid form one sorted list.
+        thr = float(den) * mids
+        crossed = np.searchsorted(thr, num, side="left")      # #{mid : num > den*mid}
+        at = np.minimum(crossed, len(thr) - 1)
+        tie = (crossed < len(thr)) & (num == thr[at]) & upper_is_even[at]
+        return crossed + tie
     num_b, den_b = np.broadcast_arrays(num, den)
     out = np.zeros(num_b.shape, dtype=np.int64)
     flat_n, flat_d, flat_o = num_b.reshape(-1), den_b.reshape(-1), out.reshape(-1)
@@ -131,31 +147,45 @@ def global_scale(x) -> np.float32:
 # --------------------------------------------------------------------------
 # Quantise / dequantise.
 # --------------------------------------------------------------------------
-def quantize(x, g) -> tuple[np.ndarray, np.ndarray]:
-    """Encode ``x`` [..., K] (K % 16 == 0) with global scale ``g``.
-
-    Returns (codes uint8 [..., K] with values 0..15, scales uint8 [..., K/16]).
-    """
+def block_scales(x, g) -> np.ndarray:
+    """E4M3 scale codes uint8 [..., K/16]: nearest E4M3 value to amax/(6 g)."""
     x = np.asarray(x, dtype=np.float64)
     K = x.shape[-1]
     if K % BLOCK:
         raise ValueError("contraction length must be a multiple of 16")
     g = float(np.float32(g))
+    amax = np.abs(x.reshape(*x.shape[:-1], K // BLOCK, BLOCK)).max(axis=-1)
+    scale_code = round_quotient_to_grid(amax, np.float64(E2M1_MAX * g), E4M3_POS)
+    return np.where(amax == 0.0, 0, scale_code).astype(np.uint8)
+
+
+def encode_with_scales(x, scales, g) -> np.ndarray:
+    """E2M1 codes uint8 [..., K] of x given its block scale codes."""
+    x = np.asarray(x, dtype=np.float64)
+    K = x.shape[-1]
+    g = float(np.float32(g))
     blocks = x.reshape(*x.shape[:-1], K // BLOCK, BLOCK)
     mag = np.abs(blocks)
-    amax = mag.max(axis=-1)
-    # Block scale: nearest E4M3 value to amax / (6 g).
-    scale_code = round_quotient_to_grid(amax, np.full_like(amax, E2M1_MAX * g), E4M3_POS)
-    scale_code = np.where(amax == 0.0, 0, scale_code)
-    s_val = E4M3_POS[scale_code]
-    # Element magnitudes: nearest E2M1 magnitude to |x| / (s g).
+    s_val = E4M3_POS[np.asarray(scales, dtype=np.int64)]
+    # Element magnitudes: nearest E2M1 magnitude to r = |x| / (s g).  The FP64
+    # quotient is exact when r is an E2M1 midpoint and otherwise stays on the
+    # same side of every midpoint (see the module note), so rounding it
+    # decides as the real quotient would.
     den = (s_val * g)[..., None]
-    safe_den = np.where(den > 0.0, den, 1.0)
-    mag_code = round_quotient_to_grid(mag, safe_den, E2M1_MAGS)
+    r = mag / np.where(den > 0.0, den, 1.0)
+    mag_code = round_quotient_to_grid(r, np.float64(1.0), E2M1_MAGS)
     mag_code = np.where((s_val[..., None] == 0.0) | (mag == 0.0), 0, mag_code)
     sign = np.signbit(blocks).astype(np.int64)
-    codes = (mag_code | (sign << 3)).reshape(x.shape).astype(np.uint8)
-    return codes, scale_code.astype(np.uint8)
+    return (mag_code | (sign << 3)).reshape(x.shape).astype(np.uint8)
+
+
+def quantize(x, g) -> tuple[np.ndarray, np.ndarray]:
+    """Encode ``x`` [..., K] (K % 16 == 0) with global scale ``g``.
+
+    Returns (codes uint8 [..., K] with values 0..15, scales uint8 [..., K/16]).
+    """
+    scales = block_scales(x, g)
+    return encode_with_scales(x, scales, g), scales
 
 
 def pack_codes(codes: np.ndarray) -> np.ndarray:
