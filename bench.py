@@ -1,0 +1,263 @@
+"""Benchmark of the NVFP4 MoE expert layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+                    [--variant w4a4|w4a16] [--mode graph|eager] [--no-cpu]
+
+A step is one pass of the whole layer path on one batch: global activation
+scale, activation quantisation, permutation by expert, grouped GEMM1 with
+SwiGLU and requantisation, grouped GEMM2 with the top-k weighted combine
+(W4A16: permutation and the two GEMMs).  Inputs (activations, routing,
+prepared weights) are resident in HBM before timing starts; routing and weight
+preparation are outside the step.  Several copies of the weights are rotated
+between steps so the 256 MB Infinity Cache cannot serve repeats.
+
+Prints one JSON line: throughput in tokens/s, the dominant kernel's roofline
+figures measured with HIP events inside the timed region, and the CPU oracle's
+throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import moe_inputs  # noqa: E402
+from nvfp4_block_scaled_03_amd import ops  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense FP16/BF16 matrix peak
+INFINITY_CACHE = 256 << 20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="decode", choices=moe_inputs.ORDER)
+    p.add_argument("--variant", default="w4a4", choices=["w4a4", "w4a16"])
+    p.add_argument("--mode", default="eager", choices=["eager", "graph"])
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_layer(w, dev):
+    d = ops.dims(w.T, w.topk, w.E, w.H, w.I, w.shared)
+    x = moe_inputs.activations(w, device=dev)
+    logits = moe_inputs.router_logits(w, device=dev)
+    ids, tw = ops.route_topk(logits, w.topk)
+    # Quantise the weights expert-group by expert-group to bound FP32 memory.
+    S = w.n_experts
+    chunk = max(1, min(S, (8 << 30) // (4 * 3 * w.I * w.H)))
+    parts = []
+    for s0 in range(0, S, chunk):
+        sel = range(s0, min(S, s0 + chunk))
+        sub = ops.dims(w.T, w.topk, len(sel), w.H, w.I, 0)
+        w13 = moe_inputs.expert_weights(w, 13, device=dev, experts=sel)
+        w2 = moe_inputs.expert_weights(w, 2, device=dev, experts=sel)
+        g13 = ops.global_scale(w13, batches=len(sel))
+        q13, sf13 = ops.quantize(w13.reshape(-1, w.H), g13, rows_per_g=2 * w.I)
+        g2w = ops.global_scale(w2, batches=len(sel))
+        q2, sf2 = ops.quantize(w2.reshape(-1, w.I), g2w, rows_per_g=w.H)
+        parts.append((q13.view(len(sel), 2 * w.I, -1), sf13.view(len(sel), 2 * w.I, -1), g13,
+                      q2.view(len(sel), w.H, -1), sf2.view(len(sel), w.H, -1), g2w))
+        del w13, w2, sub
+    cat = [torch.cat([p[i] for p in parts]) for i in range(6)]
+    del parts
+    prep13 = ops.prep_weights(d, 13, cat[0], cat[1])
+    prep2 = ops.prep_weights(d, 2, cat[3], cat[4])
+    empty = torch.empty(0, dtype=torch.uint8, device=dev)
+    wq = ops.ExpertWeights(empty, empty, cat[2], empty, empty, cat[5], prep13, prep2)
+    del cat
+    g2 = ops.calibrate_g2(d, x, ids, wq)
+    torch.cuda.synchronize()
+    return d, x, ids, tw, wq, g2
+
+
+def weight_copies(wq, n):
+    out = [wq]
+    for _ in range(n - 1):
+        out.append(ops.ExpertWeights(wq.q13, wq.sf13, wq.g13.clone(), wq.q2, wq.sf2, wq.g2.clone(),
+                                     wq.prep13.clone(), wq.prep2.clone()))
+    return out
+
+
+def cpu_baseline(w, dev, ids, tw, seconds):
+    """The FP64 oracle on a bounded sample of the workload's tokens (host cores)."""
+    from oracle import moe as omoe
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) \
+            if threadpoolctl.threadpool_info() else 1
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    n_tok = min(w.T, 16)
+    toks = np.arange(n_tok)
+    x = moe_inputs.activations(w, device=dev).float().cpu().numpy().astype(np.float64)
+    ids_np, tw_np = ids.cpu().numpy(), tw.cpu().numpy()
+    cache13, cache2 = {}, {}
+
+    def src13(e):
+        if e not in cache13:
+            cache13[e] = moe_inputs.expert_weight(w, 13, e, device=dev).cpu().numpy()
+        return cache13[e]
+
+    def src2(e):
+        if e not in cache2:
+            cache2[e] = moe_inputs.expert_weight(w, 2, e, device=dev).cpu().numpy()
+        return cache2[e]
+
+    ew = omoe.ExpertWeights(src13, src2)
+    # Offline weight quantisation is outside the timed scope, as on the GPU.
+    used = set(int(e) for e in ids_np[:n_tok].reshape(-1)) | ({w.E} if w.shared else set())
+    for e in used:
+        ew.quantized(13, e)
+        ew.quantized(2, e)
+    g2 = np.float32(1e-3)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        omoe.layer(x, ids_np, tw_np, ew, w.E, w.I, variant="w4a4", g2=g2, shared=w.shared,
+                   tokens=toks)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 1000:
+            break
+    return {"value": n_tok * reps / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_tok} of {w.T} tokens of the {w.name} layer, W4A4, FP64 NumPy, "
+                      f"{reps} repetitions in {el:.1f} s (weight quantisation excluded)"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    w = moe_inputs.WORKLOADS[a.workload]
+    log(f"[bench] building {w.name} layer")
+    d, x, ids, tw, wq, g2 = build_layer(w, dev)
+    P = w.pairs
+    al = ops.moe_align(d, ids)
+    offs = al.offsets.cpu().numpy()
+    rows_per_expert = np.diff(offs)
+    touched = int((rows_per_expert > 0).sum())
+    wbytes13 = (2 * w.I * w.H) // 2 + (2 * w.I * w.H) // 16
+    wbytes2 = (w.I * w.H) // 2 + (w.I * w.H) // 16
+    n_copies = max(1, math.ceil(4 * INFINITY_CACHE / max(1, touched * (wbytes13 + wbytes2))))
+    n_copies = min(n_copies, 8)
+    copies = weight_copies(wq, n_copies)
+    layer = ops.MoELayer(d, wq, g2, device=dev)
+    out = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev)
+
+    # Events around the dominant kernel (GEMM1) in every timed step.
+    ev = []
+
+    def step(i, record):
+        wc = copies[i % len(copies)]
+        if record:
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            layer.forward(x, ids, tw, a.variant, out=out, weights=wc,
+                          marks=(e0, e1, e2))
+            ev.append((e0, e1, e2))
+        else:
+            layer.forward(x, ids, tw, a.variant, out=out, weights=wc)
+
+    graphs = []
+    if a.mode == "graph":
+        for i in range(len(copies)):
+            for _ in range(2):
+                step(i, False)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i, False)
+            graphs.append(g)
+
+    log(f"[bench] warmup {a.warmup}")
+    for i in range(a.warmup):
+        graphs[i % len(graphs)].replay() if graphs else step(i, False)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {a.steps} steps ({a.mode})")
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        if graphs:
+            graphs[i % len(graphs)].replay()
+        else:
+            step(i, True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / a.steps
+
+    # Dominant kernel: GEMM1 (two thirds of the weight bytes and of the FLOPs).
+    g1_flops = 2.0 * P * (2 * w.I) * w.H
+    g1_bytes = touched * wbytes13 + w.T * (w.H // 2 + w.H // 16) + P * (w.I // 2 + w.I // 16)
+    if ev:
+        gemm1_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in ev]))
+    else:
+        # graph mode: time GEMM1 launches on their own with events
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        layer.forward(x, ids, tw, a.variant, out=out)
+        torch.cuda.synchronize()
+        n = 20
+        e0.record()
+        for i in range(n):
+            layer.gemm1(a.variant, copies[i % len(copies)])
+        e1.record()
+        torch.cuda.synchronize()
+        gemm1_ms = e0.elapsed_time(e1) / n
+    decode_like = P / max(1, w.n_experts) < 64
+    if decode_like:
+        ach = g1_bytes / (gemm1_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        ach = g1_flops / (gemm1_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
+    roof["kernel"] = "grouped_gemm1_swiglu" + ("" if a.variant == "w4a4" else "_w4a16")
+    roof["kernel_ms"] = round(gemm1_ms, 5)
+    layer_flops = moe_inputs.flops(w)
+    layer_bytes = moe_inputs.touched_bytes(w, rows_per_expert)
+    res = {
+        "metric": "NVFP4 MoE layer tokens/s (30B-A3B expert shape)",
+        "value": round(w.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 codes, f16 matrix ops, f32 accumulate" if a.variant == "w4a4"
+                 else "nvfp4 weights, bf16 activations, bf16 matrix ops, f32 accumulate",
+        "data": "synthetic (seeded), random-init weights",
+        "config": {"workload": w.name, **w.describe(), "variant": a.variant, "mode": a.mode,
+                   "experts_touched": touched, "weight_copies": len(copies)},
+        "layer_tflops": round(layer_flops / (ms * 1e-3) / 1e12, 2),
+        "layer_gbs": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
+        "layer_hbm_frac": round(layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": roof,
+    }
+    if not a.no_cpu:
+        log("[bench] cpu baseline")
+        res["cpu_baseline"] = cpu_baseline(w, dev, ids, tw, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

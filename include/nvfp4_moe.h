@@ -1,0 +1,254 @@
+/*
+ * nvfp4_moe.h -- C ABI of libnvfp4moe.so, the NVFP4 mixture-of-experts expert
+ * path for AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (title -> short tag):
+ *   "[Kernel] Add NVFP4 MoE CUTLASS support for SM120"               vLLM PR #29242
+ *   "SM120 (RTX Blackwell) NVFP4 MoE: CUTLASS Grouped Block-Scaled
+ *    GEMM Produces Invalid Output; FlashInfer Requires Extensive
+ *    Patching"                                                      FlashInfer #2723
+ *   "[NVFP4] NVFP4 MOE emulation fallback for H100/MI300/MI350, ..." vLLM PR #35737
+ *   "Report: NVFP4 kernel selection on SM120/SM121"                 unsloth PR #10417
+ *
+ * The path (one layer):
+ *   nvfp4_global_scale  activations -> g1                    (W4A4 only)
+ *   nvfp4_quantize      activations, g1 -> a1 codes + scales (W4A4 only)
+ *   moe_align           top-k expert ids -> rows grouped by expert
+ *   grouped_gemm1_swiglu[_w4a16]   gate/up GEMM, SwiGLU, requantisation
+ *   grouped_gemm2_combine[_w4a16]  down GEMM, top-k weighted combine
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers are DEVICE pointers unless stated; `dims` is a host pointer.
+ * - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *   NULL is the null stream).  The library never synchronises, never
+ *   allocates or frees device memory, and keeps no state between calls: all
+ *   scratch memory is a caller-owned workspace sized by the *_size queries.
+ *   Calls that touch the same buffers must be ordered by the caller.
+ * - The caller owns every buffer.  Nothing is retained after a call returns.
+ * - bfloat16 buffers are passed as uint16_t*.
+ * - Canonical NVFP4 layout (the layout bit-exactness is judged on): a matrix
+ *   [rows][K] is stored as codes uint8 [rows][K/2] -- element 2j in the low
+ *   nibble of byte j, element 2j+1 in the high nibble, each a 4-bit E2M1 code
+ *   (sign | 2 exponent bits | 1 mantissa bit, bias 1) -- and scales uint8
+ *   [rows][K/16], one unsigned E4M3 (OCP "FN", bias 7) byte per 16
+ *   consecutive elements.  A value is E2M1[code] * E4M3[scale] * g with one
+ *   FP32 global scale g per tensor (activations) or per expert matrix
+ *   (weights).  The element type and the per-16 unsigned E4M3 scale are those
+ *   of the native block-scaled instruction named in unsloth PR #10417 ("Why it
+ *   matters"); "FP4 weights with FP8 block scales" is FlashInfer #2723
+ *   ("Model" table).
+ * - Errors: every argument is validated on the host before anything is
+ *   launched.  A failing call returns a negative NVFP4_E* code, launches
+ *   nothing, writes nothing, and sets a thread-local message readable with
+ *   nvfp4_last_error(); GEMM messages carry num_experts, M, N, K and the
+ *   workspace size, like the grouped-GEMM initialisation error in vLLM PR
+ *   #29242 (review of nvfp4_blockwise_moe_kernel.cu).  A failed kernel launch
+ *   returns NVFP4_ELAUNCH with the HIP error string.  Values that live on the
+ *   device (expert ids, per-expert row counts) cannot be checked on the host:
+ *   out-of-range expert ids are dropped (see moe_align), and row counts come
+ *   from moe_align and are trusted, as the per-group shapes of the grouped
+ *   GEMM in vLLM PR #29242 (debug trace) are device-resident and unchecked.
+ * - Inputs must be finite; NaN or Inf inputs give unspecified (but in-bounds)
+ *   results.  T == 0 is a no-op that still validates the other arguments.
+ */
+#ifndef NVFP4_MOE_H
+#define NVFP4_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_MOE_ABI_VERSION 1
+
+/* Status codes. */
+#define NVFP4_OK 0
+#define NVFP4_EINVAL (-1)     /* null pointer, bad enum, misaligned pointer   */
+#define NVFP4_ESHAPE (-2)     /* unsupported or inconsistent dimensions       */
+#define NVFP4_EWORKSPACE (-3) /* workspace smaller than the size query        */
+#define NVFP4_ELAUNCH (-4)    /* a kernel launch failed (HIP error in message) */
+
+/* Element types of dense inputs/outputs. */
+#define NVFP4_BF16 0
+#define NVFP4_F32 1
+
+/* Layer dimensions (host struct).
+ *   T      tokens (>= 0)
+ *   topk   routed experts per token (1..E)
+ *   E      routed experts (>= 1)
+ *   H      hidden size; multiple of 128 (contraction of GEMM1, output of GEMM2)
+ *   I      expert intermediate size; multiple of 128
+ *   shared 0 or 1; 1 adds an always-on shared expert as expert slot E, which
+ *          every token visits with weight 1 (the "512 routed + 1 shared"
+ *          layout of FlashInfer #2723, "Model" table)
+ * E + shared <= 1024.  P = T*topk + shared*T is the number of (token, expert)
+ * pairs, i.e. of rows in the grouped GEMMs; P < 2^31. */
+typedef struct nvfp4_moe_dims {
+  int32_t T;
+  int32_t topk;
+  int32_t E;
+  int32_t H;
+  int32_t I;
+  int32_t shared;
+} nvfp4_moe_dims;
+
+/* ABI version of the loaded library (NVFP4_MOE_ABI_VERSION). */
+int nvfp4_abi_version(void);
+
+/* Message of the last failed call on this thread ("" if none).  The pointer is
+ * valid until the next library call on the same thread. */
+const char* nvfp4_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Global scale.                                                             */
+/* ------------------------------------------------------------------------ */
+/* g[b] = fl32(max_i |x[b][i]| / 2688) for b < batches, over n contiguous
+ * elements per batch (x is [batches][n], dtype NVFP4_BF16 or NVFP4_F32).
+ * 2688 = 6 * 448, the largest E2M1 magnitude times the largest E4M3 scale, so
+ * the block holding the tensor's amax gets the top E4M3 scale.  The pages fix
+ * FP32 for the scale arithmetic (FlashInfer #2723, "2. FP32 Amax
+ * Computation"); the amax itself is exact.  The quotient is correctly rounded.
+ * Use batches = 1 for an activation tensor, batches = experts for a stack of
+ * expert weight matrices.
+ * ws: workspace of nvfp4_global_scale_workspace_size(batches, n) bytes
+ * (may be NULL when that size is 0).  x must be 16-byte aligned and n a
+ * multiple of 8. */
+size_t nvfp4_global_scale_workspace_size(int64_t batches, int64_t n);
+int nvfp4_global_scale(const void* x, int dtype, int64_t batches, int64_t n, float* g,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Quantisation to NVFP4.                                                    */
+/* ------------------------------------------------------------------------ */
+/* Encode rows of x ([rows][ldx] elements, dtype NVFP4_BF16 or NVFP4_F32, the
+ * first K of each row used) into canonical NVFP4: q uint8 [rows][K/2], sf
+ * uint8 [rows][K/16].  Row r uses the global scale g[r / rows_per_g] (a device
+ * array): rows_per_g = rows for one activation tensor, rows_per_g = N for a
+ * stack of [N][K] expert matrices.
+ * Per 16-element block: s = round(amax / (6 g)) to the nearest E4M3 value,
+ * ties to the even code, saturating at 448; each element gets sign(x) |
+ * round(|x| / (s g)) to the nearest E2M1 magnitude, ties to even, saturating
+ * at 6; a block with s = 0 gets magnitude 0 everywhere.  Decisions are exact
+ * (taken on the real quotients).  This is the per-token activation
+ * quantisation of FlashInfer #2723 ("Why 39 vs 49 tok/s?"), with per-block
+ * amax by a wavefront reduction in FP32 ("2. FP32 Amax Computation").
+ * Requirements: K % 16 == 0, ldx >= K, ldx % 8 == 0, x 16-byte aligned,
+ * q 4-byte aligned, g != NULL, rows_per_g >= 1. */
+int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx,
+                   const float* g, int64_t rows_per_g, uint8_t* q, uint8_t* sf, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Router (runs before the path; not part of the timed layer).               */
+/* ------------------------------------------------------------------------ */
+/* Softmax / top-k / renormalise router over FP32 logits [T][E]: ids int32
+ * [T][topk] are the topk largest logits in decreasing order (equal logits:
+ * lower id first) and weights float32 [T][topk] the softmax over the selected
+ * logits (equal to the full softmax renormalised over the selection).  The
+ * pages route each token to its top experts ("10 routed per token",
+ * FlashInfer #2723, "Model" table) without spelling out the router; this is
+ * the usual reading.  1 <= topk <= min(E, 32), E <= 1024. */
+int moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t topk, int32_t* ids,
+                   float* weights, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Permutation by expert.                                                    */
+/* ------------------------------------------------------------------------ */
+/* Group the P (token, expert) pairs by expert, the role of
+ * get_cutlass_moe_mm_data in vLLM PR #29242 (commit list).  Pair f = t*topk+j
+ * has expert topk_ids[t][j]; with dims->shared, pair T*topk + t has expert E.
+ * Outputs (all exact integers):
+ *   expert_offsets int32 [E+shared+1]: rows of expert e are
+ *                  offsets[e] <= p < offsets[e+1]; offsets[E+shared] = number
+ *                  of kept pairs.
+ *   sorted_pair    int32 [P]: the pair index f at row p; within an expert,
+ *                  rows are in increasing f (a stable sort by expert).
+ *   inv_pos        int32 [P]: row of pair f, or -1 when its expert id is
+ *                  outside [0, E) (such pairs are dropped and contribute
+ *                  nothing).
+ *   plan           int32 [moe_align_plan_size/4]: opaque tile lists consumed
+ *                  by the grouped GEMMs (must come from a moe_align call with
+ *                  the same dims).
+ * ws: moe_align_workspace_size(dims) bytes of scratch. */
+size_t moe_align_workspace_size(const nvfp4_moe_dims* dims);
+size_t moe_align_plan_size(const nvfp4_moe_dims* dims);
+int moe_align(const nvfp4_moe_dims* dims, const int32_t* topk_ids, int32_t* expert_offsets,
+              int32_t* sorted_pair, int32_t* inv_pos, int32_t* plan, void* ws, size_t ws_bytes,
+              void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Weight preparation (offline).                                             */
+/* ------------------------------------------------------------------------ */
+/* Rearrange canonical NVFP4 expert weights into the library's streaming
+ * layout `prep` (opaque; the same bytes, permuted).  which = 13: the gate/up
+ * weights q [E+shared][2I][H/2], sf [E+shared][2I][H/16] (rows [0, I) gate,
+ * rows [I, 2I) up); which = 2: the down weights q [E+shared][H][I/2], sf
+ * [E+shared][H][I/16].  prep must hold nvfp4_prep_weights_size bytes and be
+ * 16-byte aligned. */
+size_t nvfp4_prep_weights_size(const nvfp4_moe_dims* dims, int which);
+int nvfp4_prep_weights(const nvfp4_moe_dims* dims, int which, const uint8_t* q, const uint8_t* sf,
+                       uint8_t* prep, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Grouped expert GEMMs.                                                     */
+/* ------------------------------------------------------------------------ */
+/* GEMM1 (W4A4).  For every row p of expert e (token t = the token of pair
+ * sorted_pair[p]):
+ *   c = alpha1[e] * (a1_hat[t] . w13_hat[e]^T)      (FP32 accumulation)
+ *   h = silu(c[0:I]) * c[I:2I]                      silu(z) = z / (1 + e^-z)
+ *   a2 row p = NVFP4 encoding of h with global scale *g2 (as nvfp4_quantize)
+ * where a1_hat, w13_hat are the dequantised codes times block scales and
+ * alpha1[e] = fl32((*g1) * gw13[e]): the per-expert FP32 alpha with no C input
+ * of the grouped GEMM epilogue in vLLM PR #29242 (review of
+ * nvfp4_blockwise_moe_kernel.cu).  g1 is a device scalar (nvfp4_global_scale
+ * output), gw13 a device array [E+shared], g2 a device scalar chosen by the
+ * caller (a static calibration of the intermediate).  Outputs a2_q uint8
+ * [P][I/2] and a2_sf uint8 [P][I/16] are in sorted-row order.  a1_q/a1_sf are
+ * the canonical [T][H/2] / [T][H/16] activations. */
+int grouped_gemm1_swiglu(const nvfp4_moe_dims* dims, const uint8_t* a1_q, const uint8_t* a1_sf,
+                         const float* g1, const int32_t* sorted_pair, const int32_t* expert_offsets,
+                         const int32_t* plan, const uint8_t* w13_prep, const float* gw13,
+                         const float* g2, uint8_t* a2_q, uint8_t* a2_sf, void* stream);
+
+/* Workspace of the GEMM2 calls: the per-row FP32 down-projection outputs
+ * [P][H] that the combine reads. */
+size_t grouped_gemm_workspace_size(const nvfp4_moe_dims* dims);
+
+/* GEMM2 (W4A4) + combine.  For every row p of expert e:
+ *   d[p] = alpha2[e] * (a2_hat[p] . w2_hat[e]^T),  alpha2[e] = fl32((*g2) * gw2[e])
+ * then out[t] = sum_j topk_w[t][j] * d[inv_pos[t*topk + j]] (+ d of the shared
+ * pair with weight 1), summed in FP32 in the order j = 0..topk-1, shared last,
+ * rows with inv_pos = -1 skipped.  out is [T][H] bfloat16 (out_dtype
+ * NVFP4_BF16, round to nearest even: the bf16-only output of vLLM PR #29242,
+ * "Force bf16 only") or float32 (NVFP4_F32, the same sums unrounded). */
+int grouped_gemm2_combine(const nvfp4_moe_dims* dims, const uint8_t* a2_q, const uint8_t* a2_sf,
+                          const float* g2, const int32_t* expert_offsets, const int32_t* inv_pos,
+                          const int32_t* plan, const float* topk_w, const uint8_t* w2_prep,
+                          const float* gw2, void* out, int out_dtype, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* GEMM1, weight-only variant (W4A16, the Marlin-style dequantising path of
+ * FlashInfer #2723, "Speed Comparison"; unsloth PR #10417, "Why it
+ * matters"): activations stay bfloat16 (x [T][H]), weights are dequantised
+ * in-kernel, alpha1[e] = gw13[e], and the intermediate a2 [P][I] is h rounded
+ * to bfloat16 (nearest even). */
+int grouped_gemm1_swiglu_w4a16(const nvfp4_moe_dims* dims, const uint16_t* x,
+                               const int32_t* sorted_pair, const int32_t* expert_offsets,
+                               const int32_t* plan, const uint8_t* w13_prep, const float* gw13,
+                               uint16_t* a2, void* stream);
+
+/* GEMM2 + combine, weight-only variant: a2 bfloat16 [P][I], alpha2[e] =
+ * gw2[e]; combine and output as grouped_gemm2_combine. */
+int grouped_gemm2_combine_w4a16(const nvfp4_moe_dims* dims, const uint16_t* a2,
+                                const int32_t* expert_offsets, const int32_t* inv_pos,
+                                const int32_t* plan, const float* topk_w, const uint8_t* w2_prep,
+                                const float* gw2, void* out, int out_dtype, void* ws,
+                                size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_MOE_H */

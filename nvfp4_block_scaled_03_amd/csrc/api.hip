@@ -1,0 +1,317 @@
+// C ABI of libnvfp4moe.so: host-side validation, error reporting and kernel
+// dispatch.  Every argument is checked before anything is launched; a failed
+// check returns a negative status, launches nothing and leaves a thread-local
+// message naming the call and the offending values (num_experts, M, N, K and
+// the workspace size for the GEMMs, like the grouped-GEMM initialisation error
+// of vLLM PR #29242, review of nvfp4_blockwise_moe_kernel.cu).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/nvfp4_moe.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return NVFP4_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(NVFP4_ELAUNCH, "%s: ELAUNCH %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+hipStream_t S(void* s) { return static_cast<hipStream_t>(s); }
+
+// Shared validation of the layer dimensions.
+int check_dims(const nvfp4_moe_dims* d, const char* what) {
+  if (!d) return fail(NVFP4_EINVAL, "%s: EINVAL dims is NULL", what);
+  if (d->T < 0 || d->topk < 1 || d->E < 1 || d->topk > d->E || d->H <= 0 || d->I <= 0 ||
+      (d->shared != 0 && d->shared != 1))
+    return fail(NVFP4_ESHAPE, "%s: ESHAPE T=%d topk=%d num_experts=%d H=%d I=%d shared=%d", what,
+                d->T, d->topk, d->E, d->H, d->I, d->shared);
+  if (d->H % 128 || d->I % 128)
+    return fail(NVFP4_ESHAPE, "%s: ESHAPE H=%d and I=%d must be multiples of 128", what, d->H, d->I);
+  if (d->E + d->shared > nvfp4::kMaxExperts)
+    return fail(NVFP4_ESHAPE, "%s: ESHAPE num_experts=%d (+%d shared) exceeds %d", what, d->E,
+                d->shared, nvfp4::kMaxExperts);
+  const int64_t P = (int64_t)d->T * d->topk + (int64_t)d->shared * d->T;
+  if (P > ((int64_t)1 << 24))
+    return fail(NVFP4_ESHAPE, "%s: ESHAPE pairs=%lld exceeds 2^24", what, (long long)P);
+  return NVFP4_OK;
+}
+
+int64_t pairs(const nvfp4_moe_dims* d) {
+  return (int64_t)d->T * d->topk + (int64_t)d->shared * d->T;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_abi_version(void) { return NVFP4_MOE_ABI_VERSION; }
+
+const char* nvfp4_last_error(void) { return g_err.c_str(); }
+
+// ------------------------------------------------------------------ scales
+size_t nvfp4_global_scale_workspace_size(int64_t batches, int64_t n) {
+  if (batches <= 0 || n <= 0) return 0;
+  return nvfp4::global_scale_ws_bytes(batches, n);
+}
+
+int nvfp4_global_scale(const void* x, int dtype, int64_t batches, int64_t n, float* g, void* ws,
+                       size_t ws_bytes, void* stream) {
+  const char* W = "nvfp4_global_scale";
+  if (dtype != NVFP4_BF16 && dtype != NVFP4_F32)
+    return fail(NVFP4_EINVAL, "%s: EINVAL dtype=%d", W, dtype);
+  if (batches < 0 || n < 0 || n % 8 || batches > 65535)
+    return fail(NVFP4_ESHAPE, "%s: ESHAPE batches=%lld n=%lld (n %% 8 == 0, batches <= 65535)", W,
+                (long long)batches, (long long)n);
+  if (batches == 0) return ok();
+  if (!g || (n > 0 && !x)) return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
+  if (!aligned(x, 16) || !aligned(g, 4)) return fail(NVFP4_EINVAL, "%s: EINVAL misaligned x", W);
+  const size_t need = nvfp4_global_scale_workspace_size(batches, n);
+  if (ws_bytes < need || (need && !ws))
+    return fail(NVFP4_EWORKSPACE, "%s: EWORKSPACE workspace_size=%zu needed=%zu", W, ws_bytes, need);
+  return launched(nvfp4::launch_global_scale(x, dtype, batches, n, g, ws, S(stream)), W);
+}
+
+int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx, const float* g,
+                   int64_t rows_per_g, uint8_t* q, uint8_t* sf, void* stream) {
+  const char* W = "nvfp4_quantize";
+  if (dtype != NVFP4_BF16 && dtype != NVFP4_F32)
+    return fail(NVFP4_EINVAL, "%s: EINVAL dtype=%d", W, dtype);
+  if (rows < 0 || K <= 0 || K % 16 || ldx < K || ldx % 8 || rows_per_g < 1)
+    return fail(NVFP4_ESHAPE, "%s: ESHAPE rows=%lld K=%lld ldx=%lld rows_per_g=%lld", W,
+                (long long)rows, (long long)K, (long long)ldx, (long long)rows_per_g);
+  if ((rows * (K / 8) + 255) / 256 > 0x7FFFFFFFLL)
+    return fail(NVFP4_ESHAPE, "%s: ESHAPE rows=%lld K=%lld too large", W, (long long)rows,
+                (long long)K);
+  if (rows == 0) return ok();
+  if (!x || !g || !q || !sf) return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
+  if (!aligned(x, 16) || !aligned(q, 4) || !aligned(g, 4))
+    return fail(NVFP4_EINVAL, "%s: EINVAL misaligned pointer (x 16 B, q 4 B)", W);
+  return launched(nvfp4::launch_quantize(x, dtype, rows, K, ldx, g, rows_per_g, q, sf, S(stream)), W);
+}
+
+// ------------------------------------------------------------------ router
+int moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t topk, int32_t* ids,
+                   float* weights, void* stream) {
+  const char* W = "moe_route_topk";
+  if (T < 0 || E < 1 || E > 1024 || topk < 1 || topk > E || topk > 32)
+    return fail(NVFP4_ESHAPE, "%s: ESHAPE T=%d num_experts=%d topk=%d", W, T, E, topk);
+  if (T == 0) return ok();
+  if (!logits || !ids || !weights) return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
+  return launched(nvfp4::launch_route_topk(logits, T, E, topk, ids, weights, S(stream)), W);
+}
+
+// ------------------------------------------------------------------ align
+size_t moe_align_workspace_size(const nvfp4_moe_dims* d) {
+  if (check_dims(d, "moe_align_workspace_size")) return 0;
+  const nvfp4::AlignShape a = nvfp4::align_shape(d->T, d->topk, d->E, d->shared);
+  return nvfp4::align_ws_bytes(a);
+}
+
+size_t moe_align_plan_size(const nvfp4_moe_dims* d) {
+  if (check_dims(d, "moe_align_plan_size")) return 0;
+  const nvfp4::AlignShape a = nvfp4::align_shape(d->T, d->topk, d->E, d->shared);
+  return nvfp4::align_plan_ints(a) * sizeof(int32_t);
+}
+
+int moe_align(const nvfp4_moe_dims* d, const int32_t* topk_ids, int32_t* expert_offsets,
+              int32_t* sorted_pair, int32_t* inv_pos, int32_t* plan, void* ws, size_t ws_bytes,
+              void* stream) {
+  const char* W = "moe_align";
+  if (int r = check_dims(d, W)) return r;
+  const nvfp4::AlignShape a = nvfp4::align_shape(d->T, d->topk, d->E, d->shared);
+  if (!expert_offsets || !plan) return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
+  if (a.P > 0 && (!sorted_pair || !inv_pos || (d->T * d->topk > 0 && !topk_ids)))
+    return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
+  const size_t need = nvfp4::align_ws_bytes(a);
+  if (ws_bytes < need || (need && !ws))
+    return fail(NVFP4_EWORKSPACE, "%s: EWORKSPACE num_experts=%d M=%lld workspace_size=%zu needed=%zu",
+                W, d->E, (long long)a.P, ws_bytes, need);
+  return launched(nvfp4::launch_align(a, topk_ids, expert_offsets, sorted_pair, inv_pos, plan, ws,
+                                      S(stream)), W);
+}
+
+// ------------------------------------------------------------------ weights
+size_t nvfp4_prep_weights_size(const nvfp4_moe_dims* d, int which) {
+  if (check_dims(d, "nvfp4_prep_weights_size") || (which != 13 && which != 2)) return 0;
+  const int64_t slots = d->E + d->shared;
+  return which == 13 ? nvfp4::prep_bytes(slots, 2 * (int64_t)d->I, d->H)
+                     : nvfp4::prep_bytes(slots, d->H, d->I);
+}
+
+int nvfp4_prep_weights(const nvfp4_moe_dims* d, int which, const uint8_t* q, const uint8_t* sf,
+                       uint8_t* prep, void* stream) {
+  const char* W = "nvfp4_prep_weights";
+  if (int r = check_dims(d, W)) return r;
+  if (which != 13 && which != 2) return fail(NVFP4_EINVAL, "%s: EINVAL which=%d (13 or 2)", W, which);
+  if (!q || !sf || !prep) return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
+  if (!aligned(q, 16) || !aligned(prep, 16))
+    return fail(NVFP4_EINVAL, "%s: EINVAL q and prep must be 16-byte aligned", W);
+  const int64_t slots = d->E + d->shared;
+  const int64_t N = which == 13 ? 2 * (int64_t)d->I : d->H;
+  const int64_t K = which == 13 ? d->H : d->I;
+  return launched(nvfp4::launch_prep(slots, N, K, which == 13 ? d->I : 0, q, sf, prep, S(stream)), W);
+}
+
+// ------------------------------------------------------------------ GEMMs
+size_t grouped_gemm_workspace_size(const nvfp4_moe_dims* d) {
+  if (check_dims(d, "grouped_gemm_workspace_size")) return 0;
+  return (size_t)pairs(d) * (size_t)d->H * sizeof(float);
+}
+
+static int gemm_fail_shape(const char* W, const nvfp4_moe_dims* d, int N, int K, size_t ws) {
+  return fail(NVFP4_EINVAL, "%s: EINVAL null or misaligned pointer num_experts=%d M=%lld N=%d K=%d "
+              "workspace_size=%zu", W, d->E + d->shared, (long long)pairs(d), N, K, ws);
+}
+
+static nvfp4::GemmArgs gemm_args(const nvfp4_moe_dims* d) {
+  nvfp4::GemmArgs a{};
+  a.T = d->T;
+  a.topk = d->topk;
+  a.E = d->E;
+  a.shared = d->shared;
+  a.H = d->H;
+  a.I = d->I;
+  a.P = pairs(d);
+  return a;
+}
+
+int grouped_gemm1_swiglu(const nvfp4_moe_dims* d, const uint8_t* a1_q, const uint8_t* a1_sf,
+                         const float* g1, const int32_t* sorted_pair, const int32_t* expert_offsets,
+                         const int32_t* plan, const uint8_t* w13_prep, const float* gw13,
+                         const float* g2, uint8_t* a2_q, uint8_t* a2_sf, void* stream) {
+  const char* W = "grouped_gemm1_swiglu";
+  if (int r = check_dims(d, W)) return r;
+  if (d->T == 0) return ok();
+  if (!a1_q || !a1_sf || !g1 || !sorted_pair || !expert_offsets || !plan || !w13_prep || !gw13 ||
+      !g2 || !a2_q || !a2_sf || !aligned(a1_q, 16) || !aligned(a1_sf, 2) || !aligned(w13_prep, 16))
+    return gemm_fail_shape(W, d, 2 * d->I, d->H, 0);
+  nvfp4::GemmArgs a = gemm_args(d);
+  a.offsets = expert_offsets;
+  a.sorted_pair = sorted_pair;
+  a.plan = plan;
+  a.a_q = a1_q;
+  a.a_sf = a1_sf;
+  a.g_a = g1;
+  a.w_prep = w13_prep;
+  a.g_w = gw13;
+  a.g2 = g2;
+  a.out_q = a2_q;
+  a.out_sf = a2_sf;
+  return launched(nvfp4::launch_gemm1(a, true, S(stream)), W);
+}
+
+int grouped_gemm1_swiglu_w4a16(const nvfp4_moe_dims* d, const uint16_t* x,
+                               const int32_t* sorted_pair, const int32_t* expert_offsets,
+                               const int32_t* plan, const uint8_t* w13_prep, const float* gw13,
+                               uint16_t* a2, void* stream) {
+  const char* W = "grouped_gemm1_swiglu_w4a16";
+  if (int r = check_dims(d, W)) return r;
+  if (d->T == 0) return ok();
+  if (!x || !sorted_pair || !expert_offsets || !plan || !w13_prep || !gw13 || !a2 ||
+      !aligned(x, 16) || !aligned(w13_prep, 16) || !aligned(a2, 2))
+    return gemm_fail_shape(W, d, 2 * d->I, d->H, 0);
+  nvfp4::GemmArgs a = gemm_args(d);
+  a.offsets = expert_offsets;
+  a.sorted_pair = sorted_pair;
+  a.plan = plan;
+  a.a_bf16 = x;
+  a.w_prep = w13_prep;
+  a.g_w = gw13;
+  a.out_bf16 = a2;
+  return launched(nvfp4::launch_gemm1(a, false, S(stream)), W);
+}
+
+static int gemm2_common(const char* W, const nvfp4_moe_dims* d, const int32_t* expert_offsets,
+                        const int32_t* inv_pos, const int32_t* plan, const float* topk_w,
+                        const uint8_t* w2_prep, const float* gw2, void* out, int out_dtype,
+                        void* ws, size_t ws_bytes) {
+  if (int r = check_dims(d, W)) return r;
+  if (out_dtype != NVFP4_BF16 && out_dtype != NVFP4_F32)
+    return fail(NVFP4_EINVAL, "%s: EINVAL out_dtype=%d", W, out_dtype);
+  const size_t need = grouped_gemm_workspace_size(d);
+  if (d->T == 0) return NVFP4_OK;
+  if (ws_bytes < need || !ws)
+    return fail(NVFP4_EWORKSPACE, "%s: EWORKSPACE num_experts=%d M=%lld N=%d K=%d workspace_size=%zu "
+                "needed=%zu", W, d->E + d->shared, (long long)pairs(d), d->H, d->I, ws_bytes, need);
+  if (!expert_offsets || !inv_pos || !plan || !topk_w || !w2_prep || !gw2 || !out ||
+      !aligned(w2_prep, 16) || !aligned(ws, 16) || !aligned(out, out_dtype == NVFP4_F32 ? 16 : 8))
+    return gemm_fail_shape(W, d, d->H, d->I, ws_bytes);
+  return NVFP4_OK;
+}
+
+int grouped_gemm2_combine(const nvfp4_moe_dims* d, const uint8_t* a2_q, const uint8_t* a2_sf,
+                          const float* g2, const int32_t* expert_offsets, const int32_t* inv_pos,
+                          const int32_t* plan, const float* topk_w, const uint8_t* w2_prep,
+                          const float* gw2, void* out, int out_dtype, void* ws, size_t ws_bytes,
+                          void* stream) {
+  const char* W = "grouped_gemm2_combine";
+  if (int r = gemm2_common(W, d, expert_offsets, inv_pos, plan, topk_w, w2_prep, gw2, out,
+                           out_dtype, ws, ws_bytes))
+    return r;
+  if (d->T == 0) return ok();
+  if (!a2_q || !a2_sf || !g2 || !aligned(a2_q, 16) || !aligned(a2_sf, 2))
+    return gemm_fail_shape(W, d, d->H, d->I, ws_bytes);
+  nvfp4::GemmArgs a = gemm_args(d);
+  a.offsets = expert_offsets;
+  a.inv_pos = inv_pos;
+  a.plan = plan;
+  a.topk_w = topk_w;
+  a.a_q = a2_q;
+  a.a_sf = a2_sf;
+  a.g_a = g2;
+  a.w_prep = w2_prep;
+  a.g_w = gw2;
+  a.d_ws = static_cast<float*>(ws);
+  a.out = out;
+  a.out_dtype = out_dtype;
+  return launched(nvfp4::launch_gemm2_combine(a, true, S(stream)), W);
+}
+
+int grouped_gemm2_combine_w4a16(const nvfp4_moe_dims* d, const uint16_t* a2,
+                                const int32_t* expert_offsets, const int32_t* inv_pos,
+                                const int32_t* plan, const float* topk_w, const uint8_t* w2_prep,
+                                const float* gw2, void* out, int out_dtype, void* ws,
+                                size_t ws_bytes, void* stream) {
+  const char* W = "grouped_gemm2_combine_w4a16";
+  if (int r = gemm2_common(W, d, expert_offsets, inv_pos, plan, topk_w, w2_prep, gw2, out,
+                           out_dtype, ws, ws_bytes))
+    return r;
+  if (d->T == 0) return ok();
+  if (!a2 || !aligned(a2, 16)) return gemm_fail_shape(W, d, d->H, d->I, ws_bytes);
+  nvfp4::GemmArgs a = gemm_args(d);
+  a.offsets = expert_offsets;
+  a.inv_pos = inv_pos;
+  a.plan = plan;
+  a.topk_w = topk_w;
+  a.a_bf16 = a2;
+  a.w_prep = w2_prep;
+  a.g_w = gw2;
+  a.d_ws = static_cast<float*>(ws);
+  a.out = out;
+  a.out_dtype = out_dtype;
+  return launched(nvfp4::launch_gemm2_combine(a, false, S(stream)), W);
+}
+
+}  // extern "C"

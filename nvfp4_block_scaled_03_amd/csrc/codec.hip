@@ -1,0 +1,161 @@
+// NVFP4 global scale and block quantisation kernels (gfx950).
+//
+// Global scale g = fl32(amax / 2688) per tensor (activations) or per expert
+// matrix (weights); block quantisation with one E4M3 scale per 16 elements
+// and exact round-to-nearest-even decisions.  The per-block amax is taken in
+// FP32 (FlashInfer #2723, "2. FP32 Amax Computation") with a wavefront (DPP)
+// reduction across the two lanes that share a block.
+#include "common.h"
+#include "launch.h"
+
+namespace nvfp4 {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Load 8 consecutive elements as floats (x is 16-byte aligned at i).
+__device__ __forceinline__ void load8(const uint16_t* x, int64_t i, float v[8]) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(x + i);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = bf16_bits_to_f32(w[j] & 0xFFFFu);
+    v[2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+  }
+}
+__device__ __forceinline__ void load8(const float* x, int64_t i, float v[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(x + i);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(x + i + 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[j] = a[j];
+    v[4 + j] = b[j];
+  }
+}
+
+__device__ __forceinline__ float block_max(float m) {
+  __shared__ float red[kThreads / kWave];
+  // Reduce within the wave.
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = m;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / kWave; ++i) r = fmaxf(r, red[i]);
+  return r;
+}
+
+__device__ __forceinline__ float scale_of_amax(float amax) {
+  // Correctly rounded FP32 quotient: FP64 division then one rounding to FP32
+  // (53 >= 2 * 24 + 2 makes the double rounding innocuous).
+  return (float)((double)amax / 2688.0);
+}
+
+// grid (nblk, batches).  nblk == 1: write g directly; else write partials.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void amax_kernel(const T* __restrict__ x, int64_t n,
+                                                        float* __restrict__ out, int direct) {
+  const int64_t b = blockIdx.y;
+  const T* xb = x + b * n;
+  const int64_t stride = (int64_t)gridDim.x * kThreads * 8;
+  float m = 0.0f;
+  for (int64_t i = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8; i < n; i += stride) {
+    float v[8];
+    load8(xb, i, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+  }
+  m = block_max(m);
+  if (threadIdx.x == 0) {
+    if (direct)
+      out[b] = scale_of_amax(m);
+    else
+      out[b * gridDim.x + blockIdx.x] = m;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void amax_finalize_kernel(const float* __restrict__ partial,
+                                                                 int nblk, float* __restrict__ g) {
+  const int b = blockIdx.x;
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < nblk; i += kThreads) m = fmaxf(m, partial[(int64_t)b * nblk + i]);
+  m = block_max(m);
+  if (threadIdx.x == 0) g[b] = scale_of_amax(m);
+}
+
+// One thread per 8 elements; the two threads of a 16-element block are
+// adjacent lanes (K % 16 == 0 and the grid starts at an even index), so the
+// block amax is one DPP exchange.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(const T* __restrict__ x, int64_t rows,
+                                                            int64_t K, int64_t ldx,
+                                                            const float* __restrict__ g,
+                                                            int64_t rows_per_g,
+                                                            uint8_t* __restrict__ q,
+                                                            uint8_t* __restrict__ sf) {
+  const int64_t hb_per_row = K >> 3;
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= rows * hb_per_row) return;  // whole lane pairs leave together
+  const int64_t row = i / hb_per_row;
+  const int64_t c8 = (i - row * hb_per_row) << 3;
+  float v[8];
+  load8(x, row * ldx + c8, v);
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+  m = fmaxf(m, dpp_xor1(m));
+  const float gv = g[row / rows_per_g];
+  const uint32_t sc = e4m3_scale_code(m, gv);
+  const float s = e4m3_value(sc);
+  const E2M1Bounds bd = e2m1_bounds(s, gv);
+  uint32_t word = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) word |= e2m1_code(v[j], bd, sc == 0) << (4 * j);
+  *reinterpret_cast<uint32_t*>(q + row * (K >> 1) + (c8 >> 1)) = word;
+  if ((c8 & 15) == 0) sf[row * (K >> 4) + (c8 >> 4)] = (uint8_t)sc;
+}
+
+int64_t amax_blocks(int64_t n) {
+  if (n <= (int64_t)1 << 20) return 1;
+  int64_t nb = (n + 65535) / 65536;
+  return nb > 256 ? 256 : nb;
+}
+
+}  // namespace
+
+size_t global_scale_ws_bytes(int64_t batches, int64_t n) {
+  const int64_t nb = amax_blocks(n);
+  return nb == 1 ? 0 : (size_t)(batches * nb) * sizeof(float);
+}
+
+hipError_t launch_global_scale(const void* x, int dtype, int64_t batches, int64_t n, float* g,
+                               void* ws, hipStream_t s) {
+  const int64_t nb = amax_blocks(n);
+  float* out = nb == 1 ? g : static_cast<float*>(ws);
+  dim3 grid((unsigned)nb, (unsigned)batches);
+  if (dtype == 0)
+    amax_kernel<uint16_t><<<grid, kThreads, 0, s>>>(static_cast<const uint16_t*>(x), n, out, nb == 1);
+  else
+    amax_kernel<float><<<grid, kThreads, 0, s>>>(static_cast<const float*>(x), n, out, nb == 1);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nb == 1) return e;
+  amax_finalize_kernel<<<(unsigned)batches, kThreads, 0, s>>>(out, (int)nb, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx,
+                           const float* g, int64_t rows_per_g, uint8_t* q, uint8_t* sf,
+                           hipStream_t s) {
+  const int64_t threads = rows * (K >> 3);
+  const int64_t blocks = (threads + kThreads - 1) / kThreads;
+  if (dtype == 0)
+    quantize_kernel<uint16_t><<<(unsigned)blocks, kThreads, 0, s>>>(
+        static_cast<const uint16_t*>(x), rows, K, ldx, g, rows_per_g, q, sf);
+  else
+    quantize_kernel<float><<<(unsigned)blocks, kThreads, 0, s>>>(
+        static_cast<const float*>(x), rows, K, ldx, g, rows_per_g, q, sf);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,412 @@
+// Grouped NVFP4 expert GEMMs with fused SwiGLU + requantisation (GEMM1) and
+// the down projection + top-k weighted combine (GEMM2), for gfx950.
+//
+// Contraction strategy: NVFP4 operands are dequantised exactly in registers
+// (code * E4M3 block scale, at most six significant bits) and multiplied on
+// the 16x16x32 f16 (W4A4) or bf16 (W4A16) matrix instructions with FP32
+// accumulation; the FP32 global scales enter as one per-expert alpha in the
+// epilogue (the alpha-pointer-array epilogue with beta = 0 of vLLM PR #29242,
+// review of nvfp4_blockwise_moe_kernel.cu).  The native FP4 instructions of
+// gfx950 take power-of-two scales per 32 elements, which cannot carry E4M3
+// scales per 16 exactly; see the design doc for the comparison.
+//
+// Work decomposition: the alignment plan lists (expert, 16..128-row tile)
+// pairs on the device; a workgroup takes one tile and BN = 4 * WN output
+// columns.  Each wavefront owns WN columns for all BM rows: it streams its
+// weight columns straight from HBM into registers (one coalesced 16-byte load
+// per lane per 16 columns x 128 k, see prep.hip) while the BM x 128 activation
+// chunk is staged once per workgroup in LDS, dequantised, double-buffered.
+// Workgroup ids are remapped so that consecutive tiles land on the same XCD
+// (shared L2 for the expert's weights and the tile's activation rows).
+#include "common.h"
+#include "launch.h"
+
+namespace nvfp4 {
+namespace {
+
+constexpr int kNW = 4;      // wavefronts per workgroup
+constexpr int kBK = 128;    // contraction chunk
+constexpr int kLDA = kBK + 8;  // LDS row stride in 16-bit elements (272 bytes)
+
+enum Epi { kEpiSwigluFp4 = 0, kEpiSwigluBf16 = 1, kEpiStoreF32 = 2 };
+
+struct KParams {
+  int T, topk, I, N, K;
+  int n_blocks;
+  int list_idx;            // which plan list (tile height)
+  const int32_t* offsets;
+  const int32_t* sorted_pair;  // GEMM1: row -> pair; GEMM2: null (row is the A row)
+  const int32_t* plan;
+  const uint8_t* a_q;
+  const uint8_t* a_sf;
+  const uint16_t* a_bf16;
+  const float* g_a;
+  const uint8_t* w_q;      // prepped codes
+  const uint8_t* w_sf;     // prepped scales
+  const float* g_w;
+  const float* g2;
+  uint8_t* out_q;
+  uint8_t* out_sf;
+  uint16_t* out_bf16;
+  float* out_f32;
+};
+
+// Bijection from the launch order to the work order such that each XCD (the
+// hardware deals workgroups round-robin over 8 XCDs) receives a contiguous
+// range of work items.
+__device__ __forceinline__ int xcd_remap(int bid, int G) {
+  const int q = G >> 3, r = G & 7, x = bid & 7, idx = bid >> 3;
+  return x * q + min(x, r) + idx;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+template <bool W4A4, int EPI, int BM, int WN>
+__global__ __launch_bounds__(kNW * kWave) void grouped_gemm_kernel(KParams p) {
+  constexpr int MT = BM / 16;
+  constexpr int NTW = WN / 16;
+  // A staging pieces per chunk: 16-byte pieces of codes (32 elements) for
+  // W4A4, 16-byte pieces of bf16 (8 elements) for W4A16.
+  constexpr int PIECES = W4A4 ? BM * 4 : BM * 16;
+  constexpr int PPT = (PIECES + kNW * kWave - 1) / (kNW * kWave);
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kLDA];
+
+  const int ntiles = p.plan[p.list_idx];
+  const int G = ntiles * p.n_blocks;
+  if ((int)blockIdx.x >= G) return;
+  const int v = xcd_remap(blockIdx.x, G);
+  const int tile = v / p.n_blocks, nb = v - tile * p.n_blocks;
+  const int packed = p.plan[p.plan[4 + p.list_idx] + tile];
+  const int e = packed & 2047, mt = packed >> 11;
+  const int row0 = p.offsets[e] + mt * BM;
+  const int nrows = min(BM, p.offsets[e + 1] - row0);
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n_wave0 = (nb * kNW + wv) * WN;
+  const bool wave_on = n_wave0 < p.N;
+  const int K = p.K, KC = K / kBK, NT = p.N / 16;
+
+  // ---- A staging: source row of each piece this thread moves.
+  int64_t a_row[PPT];
+  bool a_ok[PPT];
+#pragma unroll
+  for (int j = 0; j < PPT; ++j) {
+    const int pc = tid + j * kNW * kWave;
+    const int r = W4A4 ? (pc >> 2) : (pc >> 4);
+    a_ok[j] = pc < PIECES && r < nrows;
+    int src = 0;
+    if (a_ok[j]) {
+      src = row0 + r;
+      if (p.sorted_pair) src = pair_token(p.sorted_pair[src], p.T, p.topk);
+    }
+    a_row[j] = src;
+  }
+  u32x4 a_reg[PPT];
+  uint32_t a_sreg[PPT];
+  auto load_a = [&](int kc) {
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const int pc = tid + j * kNW * kWave;
+      if (a_ok[j]) {
+        if constexpr (W4A4) {
+          const int qq = pc & 3;
+          a_reg[j] = *reinterpret_cast<const u32x4*>(p.a_q + a_row[j] * (K >> 1) + kc * 64 + qq * 16);
+          a_sreg[j] = *reinterpret_cast<const uint16_t*>(p.a_sf + a_row[j] * (K >> 4) + kc * 8 + qq * 2);
+        } else {
+          const int qq = pc & 15;
+          a_reg[j] = *reinterpret_cast<const u32x4*>(p.a_bf16 + a_row[j] * K + kc * kBK + qq * 8);
+        }
+      } else {
+        a_reg[j] = u32x4{0u, 0u, 0u, 0u};
+        a_sreg[j] = 0u;
+      }
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const int pc = tid + j * kNW * kWave;
+      if (pc < PIECES) {
+        if constexpr (W4A4) {
+          const int r = pc >> 2, qq = pc & 3;
+          uint16_t* dst = &As[buf][r * kLDA + qq * 32];
+          const f16x2 s_lo = f16x2_splat(e4m3_value(a_sreg[j] & 0xFFu));
+          const f16x2 s_hi = f16x2_splat(e4m3_value((a_sreg[j] >> 8) & 0xFFu));
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const f16x8 d = dequant8_f16(a_reg[j][w], w < 2 ? s_lo : s_hi);
+            *reinterpret_cast<f16x8*>(dst + 8 * w) = d;
+          }
+        } else {
+          const int r = pc >> 4, qq = pc & 15;
+          *reinterpret_cast<u32x4*>(&As[buf][r * kLDA + qq * 8]) = a_reg[j];
+        }
+      }
+    }
+  };
+
+  // ---- B (weights): this wave's column tiles, one chunk per load.
+  const int64_t codes_total = (int64_t)(p.N) * (K >> 1);  // per expert
+  const int nt0 = n_wave0 >> 4;
+  u32x4 b_cur[NTW], b_nxt[NTW];
+  uint32_t s_cur[NTW], s_nxt[NTW];
+  auto load_b = [&](int kc, u32x4* bq, uint32_t* bs) {
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const int64_t unit = ((int64_t)(e * NT + nt0 + j) * KC + kc) * kWave + lane;
+      bq[j] = *reinterpret_cast<const u32x4*>(p.w_q + unit * 16);
+      bs[j] = *reinterpret_cast<const uint16_t*>(p.w_sf + unit * 2);
+    }
+  };
+  (void)codes_total;
+
+  f32x4 acc[MT][NTW];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load_a(0);
+  if (wave_on) load_b(0, b_cur, s_cur);
+  store_a(0);
+  __syncthreads();
+
+  const int a_lrow = lane & 15, a_kq = (lane >> 4) * 32;
+  for (int kc = 0; kc < KC; ++kc) {
+    const int buf = kc & 1;
+    const bool more = kc + 1 < KC;
+    if (more) {
+      load_a(kc + 1);
+      if (wave_on) load_b(kc + 1, b_nxt, s_nxt);
+    }
+    if (wave_on) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if constexpr (W4A4) {
+          f16x8 bf[NTW];
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) {
+            const uint32_t sb = s < 2 ? (s_cur[j] & 0xFFu) : ((s_cur[j] >> 8) & 0xFFu);
+            bf[j] = dequant8_f16(b_cur[j][s], f16x2_splat(e4m3_value(sb)));
+          }
+#pragma unroll
+          for (int i = 0; i < MT; ++i) {
+            const f16x8 af = *reinterpret_cast<const f16x8*>(
+                &As[buf][(i * 16 + a_lrow) * kLDA + a_kq + 8 * s]);
+#pragma unroll
+            for (int j = 0; j < NTW; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[j], acc[i][j], 0, 0, 0);
+          }
+        } else {
+          bf16x8 bf[NTW];
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) {
+            const uint32_t sb = s < 2 ? (s_cur[j] & 0xFFu) : ((s_cur[j] >> 8) & 0xFFu);
+            bf[j] = dequant8_bf16(b_cur[j][s], e4m3_value(sb));
+          }
+#pragma unroll
+          for (int i = 0; i < MT; ++i) {
+            const bf16x8 af = *reinterpret_cast<const bf16x8*>(
+                &As[buf][(i * 16 + a_lrow) * kLDA + a_kq + 8 * s]);
+#pragma unroll
+            for (int j = 0; j < NTW; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if (more) store_a(buf ^ 1);
+    __syncthreads();
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        b_cur[j] = b_nxt[j];
+        s_cur[j] = s_nxt[j];
+      }
+    }
+  }
+  if (!wave_on) return;
+
+  // ---- Epilogue.
+  const float alpha = p.g_a ? (*p.g_a) * p.g_w[e] : p.g_w[e];
+  const int ln = lane & 15, lg = lane >> 4;
+  if constexpr (EPI == kEpiStoreF32) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = i * 16 + lg * 4 + r;
+          if (row < nrows)
+            p.out_f32[(int64_t)(row0 + row) * p.N + n_wave0 + 16 * j + ln] = alpha * acc[i][j][r];
+        }
+  } else {
+    const float g2 = (EPI == kEpiSwigluFp4) ? *p.g2 : 0.0f;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int q = 0; q < NTW / 2; ++q) {
+        const int hb = (n_wave0 >> 5) + q;  // 16-column block of h
+        float h[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float gate = alpha * acc[i][2 * q][r];
+          const float up = alpha * acc[i][2 * q + 1][r];
+          h[r] = silu(gate) * up;
+        }
+        if constexpr (EPI == kEpiSwigluFp4) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float am = row16_max(fabsf(h[r]));
+            const uint32_t sc = e4m3_scale_code(am, g2);
+            const E2M1Bounds bd = e2m1_bounds(e4m3_value(sc), g2);
+            const uint32_t code = e2m1_code(h[r], bd, sc == 0);
+            const uint32_t other = (uint32_t)dpp_xor1_i((int)code);
+            const int row = i * 16 + lg * 4 + r;
+            if (row < nrows) {
+              const int64_t pr = row0 + row;
+              if ((ln & 1) == 0)
+                p.out_q[pr * (p.I >> 1) + hb * 8 + (ln >> 1)] = (uint8_t)(code | (other << 4));
+              if (ln == 0) p.out_sf[pr * (p.I >> 4) + hb] = (uint8_t)sc;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = i * 16 + lg * 4 + r;
+            if (row < nrows)
+              p.out_bf16[(int64_t)(row0 + row) * p.I + hb * 16 + ln] = (uint16_t)f32_to_bf16_bits(h[r]);
+          }
+        }
+      }
+  }
+}
+
+// out[t] = sum_j w[t][j] * d[inv_pos[t*k + j]] (+ shared row), FP32, j ascending.
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ d,
+                                                      const int32_t* __restrict__ inv_pos,
+                                                      const float* __restrict__ topk_w, int T,
+                                                      int topk, int shared, int H, void* out) {
+  const int t = blockIdx.x;
+  for (int c = threadIdx.x * 4; c < H; c += 1024) {
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < topk; ++j) {
+      const int pos = inv_pos[(int64_t)t * topk + j];
+      if (pos >= 0) {
+        const float w = topk_w[(int64_t)t * topk + j];
+        const f32x4 x = *reinterpret_cast<const f32x4*>(d + (int64_t)pos * H + c);
+        a += w * x;
+      }
+    }
+    if (shared) {
+      const int pos = inv_pos[(int64_t)T * topk + t];
+      if (pos >= 0) a += *reinterpret_cast<const f32x4*>(d + (int64_t)pos * H + c);
+    }
+    if constexpr (BF16) {
+      uint32_t lo = f32_to_bf16_bits(a[0]) | (f32_to_bf16_bits(a[1]) << 16);
+      uint32_t hi = f32_to_bf16_bits(a[2]) | (f32_to_bf16_bits(a[3]) << 16);
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + (int64_t)t * H + c) = u32x2{lo, hi};
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + (int64_t)t * H + c) = a;
+    }
+  }
+}
+
+// Tile height from the mean rows per expert (host side, from dims only).
+int pick_list(int64_t P, int slots) {
+  const int64_t avg = P / (slots > 0 ? slots : 1);
+  if (avg <= 16) return 0;
+  if (avg <= 40) return 1;
+  if (avg <= 96) return 2;
+  return 3;
+}
+
+template <bool W4A4, int EPI, int BM, int WN>
+hipError_t launch_one(const KParams& kp, int list_len, hipStream_t s) {
+  const int64_t G = (int64_t)list_len * kp.n_blocks;
+  const int64_t grid = (G + 7) / 8 * 8;
+  grouped_gemm_kernel<W4A4, EPI, BM, WN><<<(unsigned)grid, kNW * kWave, 0, s>>>(kp);
+  return hipGetLastError();
+}
+
+template <bool W4A4, int EPI>
+hipError_t launch_gemm(KParams kp, const AlignShape& al, hipStream_t s) {
+  const int li = pick_list(al.P, al.slots);
+  kp.list_idx = li;
+  const int wn = li <= 1 ? 32 : 64;
+  kp.n_blocks = (kp.N + kNW * wn - 1) / (kNW * wn);
+  const int len = (int)al.list_len[li];
+  switch (li) {
+    case 0: return launch_one<W4A4, EPI, 16, 32>(kp, len, s);
+    case 1: return launch_one<W4A4, EPI, 32, 32>(kp, len, s);
+    case 2: return launch_one<W4A4, EPI, 64, 64>(kp, len, s);
+    default: return launch_one<W4A4, EPI, 128, 64>(kp, len, s);
+  }
+}
+
+KParams base_params(const GemmArgs& a) {
+  KParams k{};
+  k.T = a.T;
+  k.topk = a.topk;
+  k.I = a.I;
+  k.offsets = a.offsets;
+  k.plan = a.plan;
+  k.g_w = a.g_w;
+  return k;
+}
+
+}  // namespace
+
+hipError_t launch_gemm1(const GemmArgs& a, bool w4a4, hipStream_t s) {
+  const AlignShape al = align_shape(a.T, a.topk, a.E, a.shared);
+  KParams k = base_params(a);
+  k.N = 2 * a.I;
+  k.K = a.H;
+  k.sorted_pair = a.sorted_pair;
+  k.w_q = a.w_prep;
+  k.w_sf = a.w_prep + (size_t)al.slots * k.N * (k.K / 2);
+  if (w4a4) {
+    k.a_q = a.a_q;
+    k.a_sf = a.a_sf;
+    k.g_a = a.g_a;
+    k.g2 = a.g2;
+    k.out_q = a.out_q;
+    k.out_sf = a.out_sf;
+    return launch_gemm<true, kEpiSwigluFp4>(k, al, s);
+  }
+  k.a_bf16 = a.a_bf16;
+  k.out_bf16 = a.out_bf16;
+  return launch_gemm<false, kEpiSwigluBf16>(k, al, s);
+}
+
+hipError_t launch_gemm2_combine(const GemmArgs& a, bool w4a4, hipStream_t s) {
+  const AlignShape al = align_shape(a.T, a.topk, a.E, a.shared);
+  KParams k = base_params(a);
+  k.N = a.H;
+  k.K = a.I;
+  k.sorted_pair = nullptr;
+  k.w_q = a.w_prep;
+  k.w_sf = a.w_prep + (size_t)al.slots * k.N * (k.K / 2);
+  k.out_f32 = a.d_ws;
+  hipError_t e;
+  if (w4a4) {
+    k.a_q = a.a_q;
+    k.a_sf = a.a_sf;
+    k.g_a = a.g_a;
+    e = launch_gemm<true, kEpiStoreF32>(k, al, s);
+  } else {
+    k.a_bf16 = a.a_bf16;
+    e = launch_gemm<false, kEpiStoreF32>(k, al, s);
+  }
+  if (e != hipSuccess) return e;
+  if (a.T == 0) return hipSuccess;
+  if (a.out_dtype == 0)
+    combine_kernel<true><<<a.T, 256, 0, s>>>(a.d_ws, a.inv_pos, a.topk_w, a.T, a.topk, a.shared, a.H, a.out);
+  else
+    combine_kernel<false><<<a.T, 256, 0, s>>>(a.d_ws, a.inv_pos, a.topk_w, a.T, a.topk, a.shared, a.H, a.out);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,79 @@
+// Internal launch functions behind the C ABI (host side).  Arguments are
+// validated by api.hip before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// Tile heights the alignment plan lists, in this order.
+constexpr int kPlanBMs[4] = {16, 32, 64, 128};
+constexpr int kPlanHeader = 8;   // counts[4], list offsets[4] (in int32 units)
+constexpr int kMaxExperts = 1024;
+
+size_t global_scale_ws_bytes(int64_t batches, int64_t n);
+hipError_t launch_global_scale(const void* x, int dtype, int64_t batches, int64_t n, float* g,
+                               void* ws, hipStream_t s);
+hipError_t launch_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx,
+                           const float* g, int64_t rows_per_g, uint8_t* q, uint8_t* sf,
+                           hipStream_t s);
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                             hipStream_t s);
+
+struct AlignShape {
+  int T, topk, E, shared;
+  int64_t P;        // pairs
+  int slots;        // E + shared
+  int nchunks;      // pair chunks of kAlignChunk
+  int64_t list_off[4];
+  int64_t list_len[4];
+};
+constexpr int kAlignChunk = 1024;
+AlignShape align_shape(int T, int topk, int E, int shared);
+size_t align_ws_bytes(const AlignShape& a);
+size_t align_plan_ints(const AlignShape& a);
+hipError_t launch_align(const AlignShape& a, const int32_t* topk_ids, int32_t* offsets,
+                        int32_t* sorted_pair, int32_t* inv_pos, int32_t* plan, void* ws,
+                        hipStream_t s);
+
+// Weight streaming layout.  For an expert matrix [N][K] (N output columns,
+// K contraction): codes [N/16][K/128][64 lanes][16 B] followed (after all
+// experts' codes) by scales [N/16][K/128][64 lanes][2 B].
+size_t prep_bytes(int64_t slots, int64_t N, int64_t K);
+hipError_t launch_prep(int64_t slots, int64_t N, int64_t K, int interleave_I, const uint8_t* q,
+                       const uint8_t* sf, uint8_t* prep, hipStream_t s);
+
+struct GemmArgs {
+  // dims
+  int T, topk, E, shared, H, I;
+  int64_t P;
+  // routing
+  const int32_t* offsets;
+  const int32_t* sorted_pair;  // GEMM1 only
+  const int32_t* inv_pos;      // combine only
+  const int32_t* plan;
+  const float* topk_w;
+  // operands
+  const uint8_t* a_q;
+  const uint8_t* a_sf;
+  const uint16_t* a_bf16;
+  const float* g_a;     // activation global scale (W4A4) or null
+  const uint8_t* w_prep;
+  const float* g_w;
+  // GEMM1 outputs
+  const float* g2;
+  uint8_t* out_q;
+  uint8_t* out_sf;
+  uint16_t* out_bf16;
+  // GEMM2 outputs
+  float* d_ws;
+  void* out;
+  int out_dtype;
+};
+hipError_t launch_gemm1(const GemmArgs& a, bool w4a4, hipStream_t s);
+hipError_t launch_gemm2_combine(const GemmArgs& a, bool w4a4, hipStream_t s);
+
+}  // namespace nvfp4

@@ -1,0 +1,301 @@
+"""Thin torch binding over the C ABI: argument marshalling only.
+
+Every step runs in the HIP library; torch provides device memory and the
+current stream.  Names follow include/nvfp4_moe.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import NVFP4_BF16, NVFP4_F32, Dims, call
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return NVFP4_BF16
+    if t.dtype == torch.float32:
+        return NVFP4_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+def dims(T: int, topk: int, E: int, H: int, I: int, shared: int = 0) -> Dims:
+    return Dims(T, topk, E, H, I, shared)
+
+
+# ---------------------------------------------------------------- codec
+def global_scale(x: torch.Tensor, batches: int = 1, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """g[b] = fl32(max |x[b]| / 2688) over ``batches`` equal contiguous slices."""
+    _need_cuda(x)
+    x = x.contiguous()
+    n = x.numel() // batches if batches else 0
+    g = out if out is not None else torch.empty(batches, dtype=torch.float32, device=x.device)
+    lib = _lib.load()
+    wsb = lib.nvfp4_global_scale_workspace_size(batches, n)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=x.device)
+    call("nvfp4_global_scale", _p(x), _dtype_code(x), batches, n, _p(g), _p(ws), wsb, _stream())
+    return g
+
+
+def quantize(x: torch.Tensor, g: torch.Tensor, rows_per_g: Optional[int] = None,
+             q: Optional[torch.Tensor] = None, sf: Optional[torch.Tensor] = None):
+    """NVFP4-encode the rows of ``x`` [rows, K]: (codes [rows, K/2], scales [rows, K/16])."""
+    _need_cuda(x, g)
+    K = x.shape[-1]
+    x2 = x.reshape(-1, K)
+    if x2.stride(-1) != 1:
+        x2 = x2.contiguous()
+    rows = x2.shape[0]
+    if q is None:
+        q = torch.empty(rows, K // 2, dtype=torch.uint8, device=x.device)
+    if sf is None:
+        sf = torch.empty(rows, K // 16, dtype=torch.uint8, device=x.device)
+    call("nvfp4_quantize", _p(x2), _dtype_code(x2), rows, K, x2.stride(0), _p(g),
+         rows if rows_per_g is None else rows_per_g, _p(q), _p(sf), _stream())
+    return q, sf
+
+
+# ---------------------------------------------------------------- routing
+def route_topk(logits: torch.Tensor, k: int):
+    _need_cuda(logits)
+    logits = logits.contiguous().float()
+    T, E = logits.shape
+    ids = torch.empty(T, k, dtype=torch.int32, device=logits.device)
+    w = torch.empty(T, k, dtype=torch.float32, device=logits.device)
+    call("moe_route_topk", _p(logits), T, E, k, _p(ids), _p(w), _stream())
+    return ids, w
+
+
+@dataclasses.dataclass
+class Alignment:
+    offsets: torch.Tensor
+    sorted_pair: torch.Tensor
+    inv_pos: torch.Tensor
+    plan: torch.Tensor
+    workspace: torch.Tensor
+
+
+def alloc_alignment(d: Dims, device) -> Alignment:
+    lib = _lib.load()
+    P = d.T * d.topk + d.shared * d.T
+    return Alignment(
+        offsets=torch.empty(d.E + d.shared + 1, dtype=torch.int32, device=device),
+        sorted_pair=torch.empty(max(P, 1), dtype=torch.int32, device=device),
+        inv_pos=torch.empty(max(P, 1), dtype=torch.int32, device=device),
+        plan=torch.empty(lib.moe_align_plan_size(ctypes.byref(d)) // 4, dtype=torch.int32,
+                         device=device),
+        workspace=torch.empty(max(lib.moe_align_workspace_size(ctypes.byref(d)), 16),
+                              dtype=torch.uint8, device=device))
+
+
+def moe_align(d: Dims, topk_ids: torch.Tensor, al: Optional[Alignment] = None) -> Alignment:
+    _need_cuda(topk_ids)
+    al = al or alloc_alignment(d, topk_ids.device)
+    call("moe_align", ctypes.byref(d), _p(topk_ids.contiguous()), _p(al.offsets),
+         _p(al.sorted_pair), _p(al.inv_pos), _p(al.plan), _p(al.workspace),
+         al.workspace.numel(), _stream())
+    return al
+
+
+# ---------------------------------------------------------------- weights
+def prep_weights(d: Dims, which: int, q: torch.Tensor, sf: torch.Tensor) -> torch.Tensor:
+    _need_cuda(q, sf)
+    n = _lib.load().nvfp4_prep_weights_size(ctypes.byref(d), which)
+    prep = torch.empty(n, dtype=torch.uint8, device=q.device)
+    call("nvfp4_prep_weights", ctypes.byref(d), which, _p(q.contiguous()), _p(sf.contiguous()),
+         _p(prep), _stream())
+    return prep
+
+
+@dataclasses.dataclass
+class ExpertWeights:
+    """NVFP4 expert weights of one layer: canonical codes/scales, per-matrix
+    global scales, and the library's streaming layout."""
+    q13: torch.Tensor    # uint8 [S, 2I, H/2]
+    sf13: torch.Tensor   # uint8 [S, 2I, H/16]
+    g13: torch.Tensor    # f32 [S]
+    q2: torch.Tensor     # uint8 [S, H, I/2]
+    sf2: torch.Tensor    # uint8 [S, H, I/16]
+    g2: torch.Tensor     # f32 [S]
+    prep13: torch.Tensor
+    prep2: torch.Tensor
+
+
+def quantize_expert_weights(d: Dims, w13: torch.Tensor, w2: torch.Tensor,
+                            keep_canonical: bool = True) -> ExpertWeights:
+    """Quantise FP32 expert weights (w13 [S, 2I, H], w2 [S, H, I]) on the GPU:
+    one global scale per expert matrix, then block quantisation and prep."""
+    S = d.E + d.shared
+    assert w13.shape == (S, 2 * d.I, d.H) and w2.shape == (S, d.H, d.I)
+    g13 = global_scale(w13, batches=S)
+    q13, sf13 = quantize(w13.reshape(S * 2 * d.I, d.H), g13, rows_per_g=2 * d.I)
+    g2 = global_scale(w2, batches=S)
+    q2, sf2 = quantize(w2.reshape(S * d.H, d.I), g2, rows_per_g=d.H)
+    q13 = q13.view(S, 2 * d.I, d.H // 2)
+    sf13 = sf13.view(S, 2 * d.I, d.H // 16)
+    q2 = q2.view(S, d.H, d.I // 2)
+    sf2 = sf2.view(S, d.H, d.I // 16)
+    prep13 = prep_weights(d, 13, q13, sf13)
+    prep2 = prep_weights(d, 2, q2, sf2)
+    if not keep_canonical:
+        empty = torch.empty(0, dtype=torch.uint8, device=w13.device)
+        q13 = sf13 = q2 = sf2 = empty
+    return ExpertWeights(q13, sf13, g13, q2, sf2, g2, prep13, prep2)
+
+
+# ---------------------------------------------------------------- GEMMs
+def gemm1_w4a4(d: Dims, a1_q, a1_sf, g1, al: Alignment, w: ExpertWeights, g2, a2_q=None, a2_sf=None):
+    P = d.T * d.topk + d.shared * d.T
+    dev = a1_q.device
+    a2_q = a2_q if a2_q is not None else torch.empty(max(P, 1), d.I // 2, dtype=torch.uint8, device=dev)
+    a2_sf = a2_sf if a2_sf is not None else torch.empty(max(P, 1), d.I // 16, dtype=torch.uint8, device=dev)
+    call("grouped_gemm1_swiglu", ctypes.byref(d), _p(a1_q), _p(a1_sf), _p(g1), _p(al.sorted_pair),
+         _p(al.offsets), _p(al.plan), _p(w.prep13), _p(w.g13), _p(g2), _p(a2_q), _p(a2_sf),
+         _stream())
+    return a2_q, a2_sf
+
+
+def gemm1_w4a16(d: Dims, x, al: Alignment, w: ExpertWeights, a2=None):
+    P = d.T * d.topk + d.shared * d.T
+    a2 = a2 if a2 is not None else torch.empty(max(P, 1), d.I, dtype=torch.bfloat16, device=x.device)
+    call("grouped_gemm1_swiglu_w4a16", ctypes.byref(d), _p(x), _p(al.sorted_pair), _p(al.offsets),
+         _p(al.plan), _p(w.prep13), _p(w.g13), _p(a2), _stream())
+    return a2
+
+
+def gemm_workspace(d: Dims, device) -> torch.Tensor:
+    n = _lib.load().grouped_gemm_workspace_size(ctypes.byref(d))
+    return torch.empty(max(n // 4, 4), dtype=torch.float32, device=device)
+
+
+def gemm2_w4a4(d: Dims, a2_q, a2_sf, g2, al: Alignment, topk_w, w: ExpertWeights,
+               out_dtype=torch.bfloat16, out=None, ws=None):
+    dev = a2_q.device
+    out = out if out is not None else torch.empty(d.T, d.H, dtype=out_dtype, device=dev)
+    ws = ws if ws is not None else gemm_workspace(d, dev)
+    call("grouped_gemm2_combine", ctypes.byref(d), _p(a2_q), _p(a2_sf), _p(g2), _p(al.offsets),
+         _p(al.inv_pos), _p(al.plan), _p(topk_w), _p(w.prep2), _p(w.g2), _p(out),
+         _dtype_code(out), _p(ws), ws.numel() * 4, _stream())
+    return out
+
+
+def gemm2_w4a16(d: Dims, a2, al: Alignment, topk_w, w: ExpertWeights, out_dtype=torch.bfloat16,
+                out=None, ws=None):
+    dev = a2.device
+    out = out if out is not None else torch.empty(d.T, d.H, dtype=out_dtype, device=dev)
+    ws = ws if ws is not None else gemm_workspace(d, dev)
+    call("grouped_gemm2_combine_w4a16", ctypes.byref(d), _p(a2), _p(al.offsets), _p(al.inv_pos),
+         _p(al.plan), _p(topk_w), _p(w.prep2), _p(w.g2), _p(out), _dtype_code(out), _p(ws),
+         ws.numel() * 4, _stream())
+    return out
+
+
+# ---------------------------------------------------------------- the layer
+class MoELayer:
+    """One NVFP4 expert layer with all intermediates preallocated, so that a
+    call launches kernels only (and can be captured in a HIP graph)."""
+
+    def __init__(self, d: Dims, weights: ExpertWeights, g2: torch.Tensor, device="cuda"):
+        self.d = d
+        self.w = weights
+        self.g2 = g2
+        P = d.T * d.topk + d.shared * d.T
+        self.P = P
+        dev = torch.device(device)
+        lib = _lib.load()
+        self.g1 = torch.empty(1, dtype=torch.float32, device=dev)
+        wsb = lib.nvfp4_global_scale_workspace_size(1, d.T * d.H)
+        self.gs_ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        self.gs_ws_bytes = wsb
+        self.a1_q = torch.empty(max(d.T, 1), d.H // 2, dtype=torch.uint8, device=dev)
+        self.a1_sf = torch.empty(max(d.T, 1), d.H // 16, dtype=torch.uint8, device=dev)
+        self.al = alloc_alignment(d, dev)
+        self.a2_q = torch.empty(max(P, 1), d.I // 2, dtype=torch.uint8, device=dev)
+        self.a2_sf = torch.empty(max(P, 1), d.I // 16, dtype=torch.uint8, device=dev)
+        self.a2_bf16 = torch.empty(max(P, 1), d.I, dtype=torch.bfloat16, device=dev)
+        self.ws = gemm_workspace(d, dev)
+
+    def gemm1(self, variant: str, weights: Optional[ExpertWeights] = None, x=None):
+        """GEMM1 alone on the layer's current buffers (for kernel timing)."""
+        d, w, s = self.d, weights or self.w, _stream()
+        if variant == "w4a4":
+            call("grouped_gemm1_swiglu", ctypes.byref(d), _p(self.a1_q), _p(self.a1_sf),
+                 _p(self.g1), _p(self.al.sorted_pair), _p(self.al.offsets), _p(self.al.plan),
+                 _p(w.prep13), _p(w.g13), _p(self.g2), _p(self.a2_q), _p(self.a2_sf), s)
+        else:
+            call("grouped_gemm1_swiglu_w4a16", ctypes.byref(d), _p(x if x is not None else self.x_last),
+                 _p(self.al.sorted_pair), _p(self.al.offsets), _p(self.al.plan), _p(w.prep13),
+                 _p(w.g13), _p(self.a2_bf16), s)
+
+    def forward(self, x, topk_ids, topk_w, variant: str = "w4a4", out=None,
+                out_dtype=torch.bfloat16, weights: Optional[ExpertWeights] = None, marks=None):
+        """Run the layer; ``marks`` = three torch.cuda.Events recorded before
+        GEMM1, between the GEMMs and after GEMM2 + combine."""
+        d, w = self.d, weights or self.w
+        self.x_last = x
+        if out is None:
+            out = torch.empty(d.T, d.H, dtype=out_dtype, device=x.device)
+        s = _stream()
+        if variant == "w4a4":
+            call("nvfp4_global_scale", _p(x), NVFP4_BF16, 1, d.T * d.H, _p(self.g1),
+                 _p(self.gs_ws), self.gs_ws_bytes, s)
+            call("nvfp4_quantize", _p(x), NVFP4_BF16, d.T, d.H, d.H, _p(self.g1), d.T,
+                 _p(self.a1_q), _p(self.a1_sf), s)
+        call("moe_align", ctypes.byref(d), _p(topk_ids), _p(self.al.offsets),
+             _p(self.al.sorted_pair), _p(self.al.inv_pos), _p(self.al.plan),
+             _p(self.al.workspace), self.al.workspace.numel(), s)
+        if marks:
+            marks[0].record()
+        if variant == "w4a4":
+            call("grouped_gemm1_swiglu", ctypes.byref(d), _p(self.a1_q), _p(self.a1_sf),
+                 _p(self.g1), _p(self.al.sorted_pair), _p(self.al.offsets), _p(self.al.plan),
+                 _p(w.prep13), _p(w.g13), _p(self.g2), _p(self.a2_q), _p(self.a2_sf), s)
+            if marks:
+                marks[1].record()
+            call("grouped_gemm2_combine", ctypes.byref(d), _p(self.a2_q), _p(self.a2_sf),
+                 _p(self.g2), _p(self.al.offsets), _p(self.al.inv_pos), _p(self.al.plan),
+                 _p(topk_w), _p(w.prep2), _p(w.g2), _p(out), _dtype_code(out), _p(self.ws),
+                 self.ws.numel() * 4, s)
+        elif variant == "w4a16":
+            call("grouped_gemm1_swiglu_w4a16", ctypes.byref(d), _p(x), _p(self.al.sorted_pair),
+                 _p(self.al.offsets), _p(self.al.plan), _p(w.prep13), _p(w.g13),
+                 _p(self.a2_bf16), s)
+            if marks:
+                marks[1].record()
+            call("grouped_gemm2_combine_w4a16", ctypes.byref(d), _p(self.a2_bf16),
+                 _p(self.al.offsets), _p(self.al.inv_pos), _p(self.al.plan), _p(topk_w),
+                 _p(w.prep2), _p(w.g2), _p(out), _dtype_code(out), _p(self.ws),
+                 self.ws.numel() * 4, s)
+        else:
+            raise ValueError(variant)
+        if marks:
+            marks[2].record()
+        return out
+
+
+def calibrate_g2(d: Dims, x, topk_ids, weights: ExpertWeights) -> torch.Tensor:
+    """A static intermediate global scale from the GPU path itself: the
+    global scale of the W4A16 intermediate (bf16 SwiGLU output) of this
+    batch."""
+    al = moe_align(d, topk_ids)
+    a2 = gemm1_w4a16(d, x, al, weights)
+    P = d.T * d.topk + d.shared * d.T
+    return global_scale(a2[:P])

@@ -1,0 +1,119 @@
+"""Helpers shared by the GPU parity tests (not collected by pytest).
+
+Inputs come from ``moe_inputs`` (generated on the GPU, copied to the host for
+the oracle); expected values come from ``oracle`` only.  Where FP32
+accumulation on the GPU may legitimately round the requantised intermediate
+the other way than the FP64 oracle (a value within a hair of a rounding
+midpoint), the checks below accept exactly the neighbouring code, only at
+positions the oracle itself flags, and bound how often that happens.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import nvfp4 as onv
+
+
+def device() -> torch.device:
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from nvfp4_block_scaled_03_amd import _lib
+
+    _lib.load()  # raises LibraryNotBuilt: no silent fallback on a GPU machine
+    return torch.device("cuda:0")
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.numpy()
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().view(torch.int16).numpy().astype(np.uint16)
+
+
+def relf(got, ref) -> float:
+    n = np.linalg.norm(ref)
+    return float(np.linalg.norm(got - ref) / (n if n > 0 else 1.0))
+
+
+def rms(a) -> float:
+    return float(np.sqrt(np.mean(np.square(a)))) if a.size else 0.0
+
+
+def check_layer_out(got, ref, what=""):
+    """The layer gate: relative Frobenius <= 2e-3, max-abs <= 1e-2 * rms(ref)."""
+    rf = relf(got, ref)
+    ma = float(np.abs(got - ref).max()) if ref.size else 0.0
+    r = rms(ref)
+    assert rf <= 2e-3, f"{what}: relative Frobenius {rf:.3e}"
+    assert ma <= 1e-2 * r, f"{what}: max-abs {ma:.3e} > 1e-2 * rms {r:.3e}"
+    return rf, ma / r if r else 0.0
+
+
+class A2Check:
+    """Result of judging a GPU-requantised NVFP4 intermediate."""
+
+    def __init__(self, codes, scales, exact, flips):
+        self.codes = codes      # admissible codes (the GPU's, once validated)
+        self.scales = scales
+        self.exact = exact      # bool: bit-identical to the oracle's own rounding
+        self.flips = flips      # number of differing codes/scales
+
+
+def check_a2_nvfp4(gpu_q: np.ndarray, gpu_sf: np.ndarray, h: np.ndarray, g2, max_rate=1e-4,
+                   rel=2.0 ** -12) -> A2Check:
+    """Judge GPU a2 bytes (rows x I/2, rows x I/16) against the oracle's FP64 h.
+
+    Exact everywhere except where the oracle flags a near tie (within ``rel``
+    of a rounding midpoint of a block scale or of an element code); there the
+    GPU may hold the neighbouring code, and element codes of a block whose
+    scale flipped must equal the oracle's encoding of h with that scale."""
+    ref_codes, ref_sf = onv.quantize(h, g2)
+    got_codes = onv.unpack_codes(gpu_q)
+    elem_flag, block_flag = onv.near_tie_mask(h, g2, rel)
+    sf_diff = gpu_sf != ref_sf
+    bad_sf = sf_diff & ~(block_flag & (np.abs(gpu_sf.astype(int) - ref_sf.astype(int)) == 1))
+    assert not bad_sf.any(), f"block scales differ outside near ties at {np.argwhere(bad_sf)[:5]}"
+    # Codes expected under the GPU's own (validated) scales.
+    exp_codes = onv.encode_with_scales(h, gpu_sf, g2)
+    # +0 and -0 codes have the same value; a sign difference there is not a flip.
+    zero_mag = ((got_codes & 7) == 0) & ((exp_codes & 7) == 0)
+    cd = (got_codes != exp_codes) & ~zero_mag
+    mag_step = np.abs((got_codes & 7).astype(int) - (exp_codes & 7).astype(int))
+    same_sign = (got_codes & 8) == (exp_codes & 8)
+    ok_flip = elem_flag & (mag_step <= 1) & same_sign
+    bad = cd & ~ok_flip
+    assert not bad.any(), (f"codes differ outside near ties: {bad.sum()} at {np.argwhere(bad)[:5]} "
+                           f"got {got_codes[bad][:5]} want {exp_codes[bad][:5]}")
+    flips = int(cd.sum()) + int(sf_diff.sum())
+    assert flips <= max(2, max_rate * h.size), \
+        f"too many near-tie flips: {int(cd.sum())} codes, {int(sf_diff.sum())} scales of {h.size}"
+    exact = bool(np.array_equal(got_codes, ref_codes) and np.array_equal(gpu_sf, ref_sf))
+    return A2Check(got_codes, gpu_sf.copy(), exact, flips)
+
+
+def check_a2_bf16(gpu_bits: np.ndarray, h: np.ndarray, max_rate=1e-3) -> np.ndarray:
+    """GPU bf16 a2 vs the oracle's FP64 h: equal to round-to-nearest-even of h
+    except near midpoints, where it must be the other neighbour (a faithful
+    rounding).  Returns the GPU values as FP64."""
+    got = (gpu_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = onv.round_to_bf16(h)
+    diff = got != ref
+    if diff.any():
+        hv = h[diff]
+        _, e = np.frexp(hv)
+        q = np.ldexp(1.0, np.maximum(e, -125) - 8)      # bf16 spacing around h
+        lo, hi = np.floor(hv / q) * q, np.ceil(hv / q) * q
+        gv = got[diff]
+        faithful = (gv == lo) | (gv == hi)
+        assert faithful.all(), f"bf16 a2 not a faithful rounding: got {gv[~faithful][:5]} h {hv[~faithful][:5]}"
+        scale = np.maximum(np.abs(hv), rms(h))
+        near = np.abs(hv - (lo + hi) / 2) <= 2.0 ** -12 * scale
+        assert near.all(), f"bf16 a2 differs away from a midpoint: h {hv[~near][:5]}"
+    assert diff.sum() <= max(1, max_rate * h.size), f"too many bf16 flips: {diff.sum()}"
+    return got

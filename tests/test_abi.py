@@ -1,0 +1,122 @@
+"""Host-side checks of the C ABI (CPU only: no kernel is launched).
+
+The library must load, export every function include/nvfp4_moe.h declares,
+answer the size queries, and reject bad arguments with the documented status
+codes before touching the GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from nvfp4_block_scaled_03_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "nvfp4_moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("library not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^[a-z_ ]+[ *]+([a-z0-9_]+)\s*\(", text, flags=re.M))
+
+
+def test_header_symbols_exported(lib):
+    names = _declared()
+    assert len(names) >= 16
+    assert names == set(_lib.SIGNATURES), names ^ set(_lib.SIGNATURES)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version(lib):
+    assert lib.nvfp4_abi_version() == _lib.ABI_VERSION
+
+
+def _d(T=64, topk=8, E=128, H=2048, I=768, shared=0):
+    return _lib.Dims(T, topk, E, H, I, shared)
+
+
+def test_size_queries(lib):
+    d = _d()
+    P = 64 * 8
+    assert lib.grouped_gemm_workspace_size(ctypes.byref(d)) == P * 2048 * 4
+    # The streaming layout is a permutation of the canonical bytes.
+    assert lib.nvfp4_prep_weights_size(ctypes.byref(d), 13) == 128 * 1536 * (1024 + 128)
+    assert lib.nvfp4_prep_weights_size(ctypes.byref(d), 2) == 128 * 2048 * (384 + 48)
+    assert lib.nvfp4_prep_weights_size(ctypes.byref(d), 5) == 0
+    assert lib.moe_align_workspace_size(ctypes.byref(d)) == 1 * 128 * 4
+    plan = lib.moe_align_plan_size(ctypes.byref(d))
+    assert plan == 4 * (8 + sum((P + bm - 1) // bm + 128 for bm in (16, 32, 64, 128)))
+    assert lib.nvfp4_global_scale_workspace_size(1, 64 * 2048) == 0
+    assert lib.nvfp4_global_scale_workspace_size(4, 1 << 22) == 4 * 64 * 4
+    ds = _d(T=256, topk=10, E=512, H=4096, I=1024, shared=1)
+    assert lib.grouped_gemm_workspace_size(ctypes.byref(ds)) == (2560 + 256) * 4096 * 4
+
+
+@pytest.mark.parametrize("dims,code,frag", [
+    (dict(H=2000), _lib.NVFP4_ESHAPE, "multiples of 128"),
+    (dict(I=700), _lib.NVFP4_ESHAPE, "multiples of 128"),
+    (dict(topk=0), _lib.NVFP4_ESHAPE, "topk=0"),
+    (dict(topk=200), _lib.NVFP4_ESHAPE, "num_experts=128"),
+    (dict(E=1024, shared=1), _lib.NVFP4_ESHAPE, "exceeds 1024"),
+    (dict(shared=2), _lib.NVFP4_ESHAPE, "shared=2"),
+    (dict(T=-1), _lib.NVFP4_ESHAPE, "T=-1"),
+    (dict(T=1 << 22), _lib.NVFP4_ESHAPE, "exceeds 2^24"),
+])
+def test_dims_rejected(lib, dims, code, frag):
+    d = _d(**dims)
+    rc = lib.moe_align(ctypes.byref(d), None, None, None, None, None, None, 0, None)
+    assert rc == code
+    assert frag in _lib.last_error() and _lib.last_error().startswith("moe_align:")
+    rc = lib.grouped_gemm1_swiglu(ctypes.byref(d), *([None] * 11), None)
+    assert rc == code
+
+
+def test_null_and_enum_errors(lib):
+    assert lib.nvfp4_quantize(None, 7, 1, 16, 16, None, 1, None, None, None) == _lib.NVFP4_EINVAL
+    assert "dtype=7" in _lib.last_error()
+    assert lib.nvfp4_quantize(None, 0, 4, 24, 24, None, 1, None, None, None) == _lib.NVFP4_ESHAPE
+    assert lib.nvfp4_quantize(None, 0, 4, 32, 36, None, 1, None, None, None) == _lib.NVFP4_ESHAPE
+    assert lib.nvfp4_quantize(None, 0, 4, 32, 32, None, 1, None, None, None) == _lib.NVFP4_EINVAL
+    assert lib.nvfp4_global_scale(None, 0, 1, 12, None, None, 0, None) == _lib.NVFP4_ESHAPE
+    assert lib.moe_route_topk(None, 4, 8, 9, None, None, None) == _lib.NVFP4_ESHAPE
+    assert lib.moe_route_topk(None, 4, 2048, 4, None, None, None) == _lib.NVFP4_ESHAPE
+    d = _d()
+    assert lib.nvfp4_prep_weights(ctypes.byref(d), 7, None, None, None, None) == _lib.NVFP4_EINVAL
+
+
+def test_gemm2_errors_name_the_problem(lib):
+    d = _d()
+    rc = lib.grouped_gemm2_combine(ctypes.byref(d), *([None] * 9), None, 0, None, 0, None)
+    assert rc == _lib.NVFP4_EWORKSPACE
+    msg = _lib.last_error()
+    for f in ("num_experts=128", "M=512", "N=2048", "K=768", "workspace_size=0"):
+        assert f in msg, msg
+    rc = lib.grouped_gemm2_combine(ctypes.byref(d), *([None] * 9), None, 5, None, 0, None)
+    assert rc == _lib.NVFP4_EINVAL and "out_dtype=5" in _lib.last_error()
+
+
+def test_zero_tokens_is_a_noop(lib):
+    d = _d(T=0)
+    assert lib.grouped_gemm1_swiglu(ctypes.byref(d), *([None] * 11), None) == _lib.NVFP4_OK
+    assert lib.nvfp4_quantize(None, 0, 0, 32, 32, None, 1, None, None, None) == _lib.NVFP4_OK
+    assert lib.moe_route_topk(None, 0, 8, 2, None, None, None) == _lib.NVFP4_OK
+    assert _lib.last_error() == ""
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(_lib.LibraryNotBuilt):
+        old = _lib._lib
+        _lib._lib = None
+        try:
+            _lib.load(str(tmp_path / "nope.so"))
+        finally:
+            _lib._lib = old

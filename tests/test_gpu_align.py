@@ -1,0 +1,102 @@
+"""GPU parity: router and permutation by expert, bit for bit (gate G1)."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs
+from nvfp4_block_scaled_03_amd import _lib, ops
+from oracle import moe as omoe
+from oracle import routing as oroute
+
+from parity import device, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return device()
+
+
+@pytest.mark.parametrize("name", moe_inputs.ORDER)
+def test_router(dev, name):
+    w = moe_inputs.WORKLOADS[name]
+    z = moe_inputs.router_logits(w, device=dev)
+    ids, wt = ops.route_topk(z, w.topk)
+    rid, rw = oroute.route_topk(to_np(z), w.topk)
+    assert np.array_equal(to_np(ids), rid)
+    np.testing.assert_allclose(to_np(wt), rw, rtol=4e-7, atol=0)
+
+
+def test_router_ties(dev):
+    z = torch.tensor(np.random.default_rng(1).integers(-2, 3, (300, 40)), dtype=torch.float32, device=dev)
+    z[0] = 0.0
+    z[1, ::2] = -0.0
+    ids, wt = ops.route_topk(z, 7)
+    rid, rw = oroute.route_topk(to_np(z), 7)
+    assert np.array_equal(to_np(ids), rid)
+    np.testing.assert_allclose(to_np(wt), rw, rtol=4e-7, atol=0)
+
+
+def _check_align(dev, ids_np, E, shared):
+    T, k = ids_np.shape
+    d = ops.dims(T, k, E, 128, 128, shared)
+    al = ops.moe_align(d, torch.from_numpy(ids_np).to(dev))
+    off, sp, inv = omoe.align(ids_np, E, shared)
+    P = T * k + shared * T
+    n_kept = int(off[-1])
+    assert np.array_equal(to_np(al.offsets), off)
+    assert np.array_equal(to_np(al.sorted_pair)[:n_kept], sp)
+    assert np.array_equal(to_np(al.inv_pos)[:P], inv)
+    # The tile lists cover every expert's rows in order, for each tile height.
+    plan = to_np(al.plan)
+    for b, bm in enumerate((16, 32, 64, 128)):
+        cnt, lo = plan[b], plan[4 + b]
+        want = [e | (m << 11) for e in range(E + shared)
+                for m in range((int(off[e + 1] - off[e]) + bm - 1) // bm)]
+        assert cnt == len(want) and list(plan[lo:lo + cnt]) == want, bm
+    return al
+
+
+@pytest.mark.parametrize("name", moe_inputs.ORDER)
+def test_align_workloads(dev, name):
+    w = moe_inputs.WORKLOADS[name]
+    ids, _ = oroute.route_topk(to_np(moe_inputs.router_logits(w, device=dev)), w.topk)
+    _check_align(dev, ids, w.E, w.shared)
+
+
+@pytest.mark.parametrize("T,k,E,shared", [(1, 1, 1, 0), (1023, 1, 4, 0), (128, 8, 3, 1),
+                                          (1025, 1, 1000, 0), (5000, 3, 17, 1), (7, 2, 1023, 1)])
+def test_align_shapes(dev, T, k, E, shared):
+    rng = np.random.default_rng(T + k + E)
+    z = rng.standard_normal((T, E)).astype(np.float32)
+    ids, _ = oroute.route_topk(z, k)
+    _check_align(dev, ids, E, shared)
+
+
+def test_align_drops_invalid_ids(dev):
+    rng = np.random.default_rng(3)
+    ids = rng.integers(0, 12, (700, 4)).astype(np.int32)
+    ids[::7, 1] = -3
+    ids[::11, 2] = 12
+    ids[5] = 99
+    _check_align(dev, ids, 12, 0)
+    _check_align(dev, ids, 12, 1)
+
+
+def test_align_is_deterministic(dev):
+    w = moe_inputs.WORKLOADS["skew"]
+    ids, _ = oroute.route_topk(to_np(moe_inputs.router_logits(w, device=dev)), w.topk)
+    t = torch.from_numpy(ids).to(dev)
+    d = ops.dims(w.T, w.topk, w.E, w.H, w.I, 0)
+    a = ops.moe_align(d, t)
+    b = ops.moe_align(d, t)
+    assert torch.equal(a.sorted_pair, b.sorted_pair) and torch.equal(a.plan, b.plan)
+
+
+def test_align_plan_size_matches(dev):
+    d = ops.dims(64, 8, 128, 2048, 768, 0)
+    lib = _lib.load()
+    assert lib.moe_align_plan_size(ctypes.byref(d)) // 4 == ops.alloc_alignment(d, dev).plan.numel()

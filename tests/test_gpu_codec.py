@@ -1,0 +1,148 @@
+"""GPU parity: global scale and NVFP4 quantisation, bit for bit (gate G1)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs
+from nvfp4_block_scaled_03_amd import ops
+from oracle import nvfp4 as onv
+
+from parity import device, to_np
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "nvfp4_blocks.txt")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return device()
+
+
+def _golden():
+    rows = []
+    for line in open(GOLDEN):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            name, g, vals, sc, packed = [p.strip() for p in line.split("|")]
+            rows.append((name, float(g), [float(v) for v in vals.split()], int(sc, 16),
+                         [int(b, 16) for b in packed.split()]))
+    return rows
+
+
+def test_golden_blocks(dev):
+    rows = _golden()
+    x = torch.tensor([r[2] for r in rows], dtype=torch.float32, device=dev)
+    g = torch.tensor([r[1] for r in rows], dtype=torch.float32, device=dev)
+    q, sf = ops.quantize(x, g, rows_per_g=1)
+    q, sf = to_np(q), to_np(sf)
+    for i, (name, _, _, sc, packed) in enumerate(rows):
+        assert sf[i, 0] == sc, name
+        assert list(q[i]) == packed, name
+    # bf16 input path for the blocks whose values are bf16-exact
+    xb = x.to(torch.bfloat16)
+    keep = [i for i in range(len(rows)) if torch.equal(xb[i].float(), x[i])]
+    assert len(keep) >= 6
+    qb, sfb = ops.quantize(xb[keep].contiguous(), g[keep].contiguous(), rows_per_g=1)
+    assert np.array_equal(to_np(qb), q[keep]) and np.array_equal(to_np(sfb), sf[keep])
+
+
+@pytest.mark.parametrize("shape", [(16, 256), (64, 2048), (1, 8), (3, 24), (4096, 2048),
+                                   (8192, 2048), (600, 4096)])
+def test_global_scale_bitexact(dev, shape):
+    gen = torch.Generator(device=dev).manual_seed(shape[0] * 31 + shape[1])
+    x = (torch.randn(*shape, generator=gen, device=dev) * 3).to(torch.bfloat16)
+    x.view(-1)[(shape[0] * shape[1]) // 2] = -77.5
+    g = ops.global_scale(x)
+    assert to_np(g)[0] == onv.global_scale(to_np(x))
+
+
+def test_global_scale_batched_and_zero(dev):
+    gen = torch.Generator(device=dev).manual_seed(5)
+    w = torch.randn(5, 3 * 1024, 512, generator=gen, device=dev) * 0.02
+    w[3] = 0.0
+    g = to_np(ops.global_scale(w, batches=5))
+    ref = [onv.global_scale(to_np(w[i])) for i in range(5)]
+    assert list(g) == ref and g[3] == 0.0
+    small = torch.randn(7, 64, generator=gen, device=dev)
+    assert list(to_np(ops.global_scale(small, batches=7))) == [onv.global_scale(to_np(small[i])) for i in range(7)]
+
+
+@pytest.mark.parametrize("name", moe_inputs.ORDER)
+def test_quantize_activations(dev, name):
+    w = moe_inputs.WORKLOADS[name]
+    x = moe_inputs.activations(w, device=dev)
+    g = ops.global_scale(x)
+    q, sf = ops.quantize(x, g)
+    xf = to_np(x).astype(np.float64)
+    g_ref = onv.global_scale(xf)
+    assert to_np(g)[0] == g_ref
+    rows = np.arange(w.T) if w.T <= 1024 else np.random.default_rng(0).choice(w.T, 1024, replace=False)
+    codes, scales = onv.quantize(xf[rows], g_ref)
+    assert np.array_equal(to_np(sf)[rows], scales)
+    assert np.array_equal(to_np(q)[rows], onv.pack_codes(codes))
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "large_e"])
+def test_quantize_weights(dev, name):
+    w = moe_inputs.WORKLOADS[name]
+    sel = sorted({0, w.E // 2, w.n_experts - 1})
+    w13 = moe_inputs.expert_weights(w, 13, device=dev, experts=sel)
+    w2 = moe_inputs.expert_weights(w, 2, device=dev, experts=sel)
+    for mat, N, K in ((w13, 2 * w.I, w.H), (w2, w.H, w.I)):
+        g = ops.global_scale(mat, batches=len(sel))
+        q, sf = ops.quantize(mat.reshape(-1, K), g, rows_per_g=N)
+        q = to_np(q).reshape(len(sel), N, K // 2)
+        sf = to_np(sf).reshape(len(sel), N, K // 16)
+        for i in range(len(sel)):
+            m = to_np(mat[i])
+            gr = onv.global_scale(m)
+            assert to_np(g)[i] == gr
+            c, s = onv.quantize(m, gr)
+            assert np.array_equal(sf[i], s)
+            assert np.array_equal(q[i], onv.pack_codes(c))
+
+
+def test_quantize_ties_and_edges(dev):
+    rng = np.random.default_rng(17)
+    e4_mid = (onv.E4M3_POS[:-1] + onv.E4M3_POS[1:]) / 2
+    e2_mid = (onv.E2M1_MAGS[:-1] + onv.E2M1_MAGS[1:]) / 2
+    rows, gs = [], []
+    for i in range(512):
+        g = float(np.float32(2.0 ** rng.integers(-10, 6) * rng.choice([1.0, 1.5, 0.75])))
+        x = np.zeros(32)
+        for b in range(2):
+            blk = np.zeros(16)
+            blk[0] = 6 * g * rng.choice(e4_mid[8:] if rng.random() < 0.5 else onv.E4M3_POS[1:])
+            s = onv.E4M3_POS[onv.block_scales(blk[None, :], g)[0, 0]]
+            blk[1:] = rng.choice(np.concatenate([e2_mid, onv.E2M1_MAGS, [7.5, 0.1]]), 15) * s * g
+            blk[1:] *= rng.choice([-1.0, 1.0], 15)
+            x[16 * b:16 * b + 16] = blk
+        rows.append(x)
+        gs.append(g)
+    x = np.array(rows, dtype=np.float32).astype(np.float64)   # representable in FP32
+    x[0, :16] = 0.0
+    x[0, 3] = -0.0
+    x[1, :16] = 3e-41            # denormal inputs, scale rounds to zero
+    x[2, 16:] = -1e30            # saturating scale
+    xt = torch.tensor(x, dtype=torch.float32, device=dev)
+    gt = torch.tensor(gs, dtype=torch.float32, device=dev)
+    q, sf = ops.quantize(xt, gt, rows_per_g=1)
+    q, sf = to_np(q), to_np(sf)
+    for r in range(len(rows)):
+        c, s = onv.quantize(x[r:r + 1], gs[r])
+        assert np.array_equal(sf[r:r + 1], s), r
+        assert np.array_equal(q[r:r + 1], onv.pack_codes(c)), r
+
+
+def test_quantize_strided_rows(dev):
+    gen = torch.Generator(device=dev).manual_seed(2)
+    big = (torch.randn(40, 96, generator=gen, device=dev) * 2).to(torch.bfloat16)
+    x = big[:, :64]                      # ldx = 96 > K = 64
+    g = ops.global_scale(x.contiguous())
+    q, sf = ops.quantize(x, g)
+    xf = to_np(x).astype(np.float64)
+    c, s = onv.quantize(xf, to_np(g)[0])
+    assert np.array_equal(to_np(sf), s) and np.array_equal(to_np(q), onv.pack_codes(c))
