@@ -225,29 +225,28 @@ def dequantize_packed(packed, scales, g) -> np.ndarray:
 # Near ties: where an FP32-accumulated input may legitimately round the other
 # way.  Used to judge the requantised intermediate of the expert layer.
 # --------------------------------------------------------------------------
-def near_tie_mask(x, g, rel: float = 2.0 ** -12) -> tuple[np.ndarray, np.ndarray]:
+def near_tie_mask(x, g, rel: float = 2.0 ** -12, abs_tol: float = 0.0) -> tuple[np.ndarray, np.ndarray]:
     """Flags (element_mask [..., K], block_mask [..., K/16]).
 
-    A block is flagged when amax/(6g) lies within ``rel`` (relative) of an
-    E4M3 rounding midpoint; an element is flagged when |x|/(s g) lies within
-    ``rel`` of an E2M1 midpoint.
+    A block is flagged when amax lies within ``rel`` (relative) plus
+    ``abs_tol`` (absolute, in units of x) of a value 6*g*m at which its E4M3
+    scale would round differently; an element is flagged when |x| lies that
+    close to a value t*s*g at which its E2M1 code would.  Used to judge an
+    input computed with accumulation error: both roundings are correct there.
     """
     x = np.asarray(x, dtype=np.float64)
     K = x.shape[-1]
     g = float(np.float32(g))
     blocks = np.abs(x.reshape(*x.shape[:-1], K // BLOCK, BLOCK))
     amax = blocks.max(axis=-1)
-    q = amax / (E2M1_MAX * g)
-    mids = _midpoints(E4M3_POS)
-    d = np.min(np.abs(q[..., None] - mids) / mids, axis=-1)
-    block_flag = d <= rel
-    _, sc = quantize(x, g)
-    s_val = E4M3_POS[sc.astype(np.int64)][..., None]
-    with np.errstate(divide="ignore", invalid="ignore"):
-        r = np.where(s_val > 0, blocks / (s_val * g), 0.0)
-    emids = _midpoints(E2M1_MAGS)
-    de = np.min(np.abs(r[..., None] - emids) / emids, axis=-1)
-    elem_flag = (de <= rel).reshape(x.shape)
+    b4 = 6.0 * g * _midpoints(E4M3_POS)
+    d = np.min(np.abs(amax[..., None] - b4) - rel * b4, axis=-1)
+    block_flag = d <= abs_tol
+    sc = block_scales(x, g)
+    sg = (E4M3_POS[sc.astype(np.int64)] * g)[..., None, None]
+    b2 = sg * _midpoints(E2M1_MAGS)                    # [..., K/16, 1, 7]
+    de = np.min(np.abs(blocks[..., None] - b2) - rel * b2, axis=-1)
+    elem_flag = ((de <= abs_tol) & (sg[..., 0] > 0)).reshape(x.shape)
     return elem_flag, block_flag
 
 

@@ -75,7 +75,7 @@ def check_a2_nvfp4(gpu_q: np.ndarray, gpu_sf: np.ndarray, h: np.ndarray, g2, max
     scale flipped must equal the oracle's encoding of h with that scale."""
     ref_codes, ref_sf = onv.quantize(h, g2)
     got_codes = onv.unpack_codes(gpu_q)
-    elem_flag, block_flag = onv.near_tie_mask(h, g2, rel)
+    elem_flag, block_flag = onv.near_tie_mask(h, g2, rel, abs_tol=2.0 ** -16 * rms(h))
     sf_diff = gpu_sf != ref_sf
     bad_sf = sf_diff & ~(block_flag & (np.abs(gpu_sf.astype(int) - ref_sf.astype(int)) == 1))
     assert not bad_sf.any(), f"block scales differ outside near ties at {np.argwhere(bad_sf)[:5]}"
@@ -97,23 +97,23 @@ def check_a2_nvfp4(gpu_q: np.ndarray, gpu_sf: np.ndarray, h: np.ndarray, g2, max
     return A2Check(got_codes, gpu_sf.copy(), exact, flips)
 
 
-def check_a2_bf16(gpu_bits: np.ndarray, h: np.ndarray, max_rate=1e-3) -> np.ndarray:
-    """GPU bf16 a2 vs the oracle's FP64 h: equal to round-to-nearest-even of h
-    except near midpoints, where it must be the other neighbour (a faithful
-    rounding).  Returns the GPU values as FP64."""
+def check_a2_bf16(gpu_bits: np.ndarray, h: np.ndarray, max_rate=5e-3) -> np.ndarray:
+    """GPU bf16 a2 vs the oracle's FP64 h.
+
+    The GPU's h carries FP32 accumulation error, which is absolute (about
+    2^-24 of the accumulated magnitudes), so a small h may be off by more than
+    a bf16 ulp of itself.  Admissible: the bf16 rounding (nearest even) of any
+    value within delta = 2^-16 * rms(h) of h.  Exact bf16(h) elsewhere; the
+    rate of differences is bounded.  Returns the GPU values as FP64."""
     got = (gpu_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     ref = onv.round_to_bf16(h)
     diff = got != ref
     if diff.any():
-        hv = h[diff]
-        _, e = np.frexp(hv)
-        q = np.ldexp(1.0, np.maximum(e, -125) - 8)      # bf16 spacing around h
-        lo, hi = np.floor(hv / q) * q, np.ceil(hv / q) * q
-        gv = got[diff]
-        faithful = (gv == lo) | (gv == hi)
-        assert faithful.all(), f"bf16 a2 not a faithful rounding: got {gv[~faithful][:5]} h {hv[~faithful][:5]}"
-        scale = np.maximum(np.abs(hv), rms(h))
-        near = np.abs(hv - (lo + hi) / 2) <= 2.0 ** -12 * scale
-        assert near.all(), f"bf16 a2 differs away from a midpoint: h {hv[~near][:5]}"
-    assert diff.sum() <= max(1, max_rate * h.size), f"too many bf16 flips: {diff.sum()}"
+        hv, gv = h[diff], got[diff]
+        delta = 2.0 ** -16 * rms(h)
+        lo = onv.round_to_bf16(hv - delta)
+        hi = onv.round_to_bf16(hv + delta)
+        ok = (gv >= lo) & (gv <= hi)
+        assert ok.all(), f"bf16 a2 outside the admissible roundings: got {gv[~ok][:5]} h {hv[~ok][:5]}"
+    assert diff.sum() <= max(2, max_rate * h.size), f"too many bf16 differences: {diff.sum()}"
     return got
