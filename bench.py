@@ -45,7 +45,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode", choices=moe_inputs.ORDER)
     p.add_argument("--variant", default="w4a4", choices=["w4a4", "w4a16"])
-    p.add_argument("--mode", default="eager", choices=["eager", "graph"])
+    p.add_argument("--mode", default="graph", choices=["eager", "graph"])
+    p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     return p.parse_args()
@@ -141,6 +142,91 @@ def cpu_baseline(w, dev, ids, tw, seconds):
                       f"{reps} repetitions in {el:.1f} s (weight quantisation excluded)"}
 
 
+def time_steps(layer, x, ids, tw, copies, variant, steps, warmup, mode):
+    """Mean wall time of one layer step (ms) over ``steps`` steps."""
+    out = torch.empty(x.shape[0], layer.d.H, dtype=torch.bfloat16, device=x.device)
+    graphs = []
+    if mode == "graph":
+        for wc in copies:
+            for _ in range(2):
+                layer.forward(x, ids, tw, variant, out=out, weights=wc)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                layer.forward(x, ids, tw, variant, out=out, weights=wc)
+            graphs.append(g)
+
+    def run(i):
+        if graphs:
+            graphs[i % len(graphs)].replay()
+        else:
+            layer.forward(x, ids, tw, variant, out=out, weights=copies[i % len(copies)])
+
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        run(i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def time_gemm1(layer, x, ids, tw, copies, variant, n=50):
+    """Mean duration (ms) of GEMM1 launched back to back, bracketed by events
+    recorded on the stream the kernels run on."""
+    layer.forward(x, ids, tw, variant, weights=copies[0])
+    for i in range(5):
+        layer.gemm1(variant, copies[i % len(copies)], x)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        layer.gemm1(variant, copies[i % len(copies)], x)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def measure(w, d, x, ids, tw, wq, g2, a, steps, warmup):
+    """Step time, GEMM1 time and the derived figures for one batch shape."""
+    P = w.pairs
+    al = ops.moe_align(d, ids)
+    rows_per_expert = np.diff(al.offsets.cpu().numpy())
+    touched = int((rows_per_expert > 0).sum())
+    wbytes13 = (2 * w.I * w.H) // 2 + (2 * w.I * w.H) // 16
+    wbytes2 = (w.I * w.H) // 2 + (w.I * w.H) // 16
+    n_copies = max(1, math.ceil(4 * INFINITY_CACHE / max(1, touched * (wbytes13 + wbytes2))))
+    copies = weight_copies(wq, min(n_copies, 8))
+    layer = ops.MoELayer(d, wq, g2, device=x.device)
+    ms = time_steps(layer, x, ids, tw, copies, a.variant, steps, warmup, a.mode)
+    g1_ms = time_gemm1(layer, x, ids, tw, copies, a.variant)
+    g1_flops = 2.0 * P * (2 * w.I) * w.H
+    g1_bytes = touched * wbytes13 + w.T * (w.H // 2 + w.H // 16) + P * (w.I // 2 + w.I // 16)
+    decode_like = P / max(1, w.n_experts) < 64
+    if decode_like:
+        ach = g1_bytes / (g1_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        ach = g1_flops / (g1_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
+    roof.update({"kernel": "grouped_gemm1_swiglu" + ("" if a.variant == "w4a4" else "_w4a16"),
+                 "kernel_ms": round(g1_ms, 5), "algorithmic_bytes": int(g1_bytes),
+                 "algorithmic_flops": g1_flops})
+    layer_flops = moe_inputs.flops(w)
+    layer_bytes = moe_inputs.touched_bytes(w, rows_per_expert)
+    return {
+        "ms": ms, "tokens_per_s": w.T / (ms * 1e-3), "touched": touched,
+        "copies": len(copies), "roofline": roof,
+        "layer_tflops": round(layer_flops / (ms * 1e-3) / 1e12, 2),
+        "layer_gbs": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
+        "layer_hbm_frac": round(layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "layer_mfma_frac": round(layer_flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+    }
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -148,98 +234,18 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     w = moe_inputs.WORKLOADS[a.workload]
-    log(f"[bench] building {w.name} layer")
+    log(f"[bench] building {w.name} layer ({a.variant}, {a.mode})")
     d, x, ids, tw, wq, g2 = build_layer(w, dev)
-    P = w.pairs
-    al = ops.moe_align(d, ids)
-    offs = al.offsets.cpu().numpy()
-    rows_per_expert = np.diff(offs)
-    touched = int((rows_per_expert > 0).sum())
-    wbytes13 = (2 * w.I * w.H) // 2 + (2 * w.I * w.H) // 16
-    wbytes2 = (w.I * w.H) // 2 + (w.I * w.H) // 16
-    n_copies = max(1, math.ceil(4 * INFINITY_CACHE / max(1, touched * (wbytes13 + wbytes2))))
-    n_copies = min(n_copies, 8)
-    copies = weight_copies(wq, n_copies)
-    layer = ops.MoELayer(d, wq, g2, device=dev)
-    out = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev)
-
-    # Events around the dominant kernel (GEMM1) in every timed step.
-    ev = []
-
-    def step(i, record):
-        wc = copies[i % len(copies)]
-        if record:
-            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-            layer.forward(x, ids, tw, a.variant, out=out, weights=wc,
-                          marks=(e0, e1, e2))
-            ev.append((e0, e1, e2))
-        else:
-            layer.forward(x, ids, tw, a.variant, out=out, weights=wc)
-
-    graphs = []
-    if a.mode == "graph":
-        for i in range(len(copies)):
-            for _ in range(2):
-                step(i, False)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(i, False)
-            graphs.append(g)
-
-    log(f"[bench] warmup {a.warmup}")
-    for i in range(a.warmup):
-        graphs[i % len(graphs)].replay() if graphs else step(i, False)
-    torch.cuda.synchronize()
-    log(f"[bench] timing {a.steps} steps ({a.mode})")
-    t0 = time.perf_counter()
-    for i in range(a.steps):
-        if graphs:
-            graphs[i % len(graphs)].replay()
-        else:
-            step(i, True)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / a.steps
-
-    # Dominant kernel: GEMM1 (two thirds of the weight bytes and of the FLOPs).
-    g1_flops = 2.0 * P * (2 * w.I) * w.H
-    g1_bytes = touched * wbytes13 + w.T * (w.H // 2 + w.H // 16) + P * (w.I // 2 + w.I // 16)
-    if ev:
-        gemm1_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1, _ in ev]))
-    else:
-        # graph mode: time GEMM1 launches on their own with events
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        layer.forward(x, ids, tw, a.variant, out=out)
-        torch.cuda.synchronize()
-        n = 20
-        e0.record()
-        for i in range(n):
-            layer.gemm1(a.variant, copies[i % len(copies)])
-        e1.record()
-        torch.cuda.synchronize()
-        gemm1_ms = e0.elapsed_time(e1) / n
-    decode_like = P / max(1, w.n_experts) < 64
-    if decode_like:
-        ach = g1_bytes / (gemm1_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
-    else:
-        ach = g1_flops / (gemm1_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_F16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
-    roof["kernel"] = "grouped_gemm1_swiglu" + ("" if a.variant == "w4a4" else "_w4a16")
-    roof["kernel_ms"] = round(gemm1_ms, 5)
-    layer_flops = moe_inputs.flops(w)
-    layer_bytes = moe_inputs.touched_bytes(w, rows_per_expert)
+    log(f"[bench] timing {a.steps} steps")
+    m = measure(w, d, x, ids, tw, wq, g2, a, a.steps, a.warmup)
     res = {
         "metric": "NVFP4 MoE layer tokens/s (30B-A3B expert shape)",
-        "value": round(w.T / (ms * 1e-3), 1),
+        "value": round(m["tokens_per_s"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": round(ms, 5),
+        "ms_per_step": round(m["ms"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -247,12 +253,23 @@ def main():
                  else "nvfp4 weights, bf16 activations, bf16 matrix ops, f32 accumulate",
         "data": "synthetic (seeded), random-init weights",
         "config": {"workload": w.name, **w.describe(), "variant": a.variant, "mode": a.mode,
-                   "experts_touched": touched, "weight_copies": len(copies)},
-        "layer_tflops": round(layer_flops / (ms * 1e-3) / 1e12, 2),
-        "layer_gbs": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
-        "layer_hbm_frac": round(layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "roofline": roof,
+                   "experts_touched": m["touched"], "weight_copies": m["copies"]},
+        "layer_tflops": m["layer_tflops"], "layer_gbs": m["layer_gbs"],
+        "layer_hbm_frac": m["layer_hbm_frac"],
+        "roofline": m["roofline"],
     }
+    if a.workload == "decode" and not a.no_prefill:
+        # The prefill-shaped batch (T = 4096) on the same layer weights.
+        wp = moe_inputs.WORKLOADS["prefill"]
+        log("[bench] prefill batch on the same layer")
+        dp = ops.dims(wp.T, wp.topk, wp.E, wp.H, wp.I, wp.shared)
+        xp = moe_inputs.activations(wp, device=dev)
+        idp, twp = ops.route_topk(moe_inputs.router_logits(wp, device=dev), wp.topk)
+        g2p = ops.calibrate_g2(dp, xp, idp, wq)
+        mp = measure(wp, dp, xp, idp, twp, wq, g2p, a, max(5, a.steps // 4), max(2, a.warmup // 2))
+        res["prefill"] = {"T": wp.T, "tokens_per_s": round(mp["tokens_per_s"], 1),
+                          "ms_per_step": round(mp["ms"], 5), "layer_tflops": mp["layer_tflops"],
+                          "layer_mfma_frac": mp["layer_mfma_frac"], "roofline": mp["roofline"]}
     if not a.no_cpu:
         log("[bench] cpu baseline")
         res["cpu_baseline"] = cpu_baseline(w, dev, ids, tw, a.cpu_seconds)

@@ -113,9 +113,12 @@ const char* nvfp4_last_error(void);
  * Computation"); the amax itself is exact.  The quotient is correctly rounded.
  * Use batches = 1 for an activation tensor, batches = experts for a stack of
  * expert weight matrices.
- * ws: workspace of nvfp4_global_scale_workspace_size(batches, n) bytes
- * (may be NULL when that size is 0).  x must be 16-byte aligned and n a
- * multiple of 8. */
+ * ws: workspace of nvfp4_global_scale_workspace_size(batches, n) bytes (8
+ * per batch), 4-byte aligned, which must be zero-filled before its first use:
+ * the call folds partial maxima into it across workgroups and leaves it zero
+ * again when it finishes, so one buffer serves every later call on the same
+ * stream (concurrent calls need separate buffers).  x must be 16-byte aligned
+ * and n a multiple of 8. */
 size_t nvfp4_global_scale_workspace_size(int64_t batches, int64_t n);
 int nvfp4_global_scale(const void* x, int dtype, int64_t batches, int64_t n, float* g,
                        void* ws, size_t ws_bytes, void* stream);

@@ -9,7 +9,10 @@ import ctypes
 import os
 from ctypes import c_char_p, c_int, c_int32, c_int64, c_size_t, c_void_p
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4moe.so")
+# NVFP4_MOE_LIB may point at another build of the same library (e.g. a
+# variant with different tile settings); the default is the in-tree build.
+LIB_PATH = os.environ.get("NVFP4_MOE_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libnvfp4moe.so")
 ABI_VERSION = 1
 
 NVFP4_OK = 0

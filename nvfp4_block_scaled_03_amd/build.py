@@ -40,20 +40,22 @@ def _run(cmd, verbose):
     return out
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, jobs: int = 8, out: str = LIB, defines=(), build_dir: str = BUILD) -> str:
+    """Compile and link; ``defines`` are extra -D settings, ``out`` the library path."""
+    os.makedirs(build_dir, exist_ok=True)
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *FLAGS, *["-D" + d for d in defines], "-c", os.path.join(CSRC, src),
+                     "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(cmds)))) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

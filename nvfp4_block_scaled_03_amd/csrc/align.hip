@@ -173,6 +173,104 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(AlignP a,
   }
 }
 
+// ---------------------------------------------------------------- one workgroup
+// The whole alignment in one launch when P <= 4 * kAlignChunk: histogram,
+// scan, tile lists and the stable scatter, by 1024 threads in rounds of 1024
+// pairs (the in-round order of equal experts comes from wavefront ballots and
+// per-wavefront counts, as in the multi-workgroup path).
+constexpr int kFusedRounds = 4;
+
+__global__ __launch_bounds__(1024) void align_fused_kernel(AlignP a, int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ sorted_pair,
+                                                           int32_t* __restrict__ inv_pos,
+                                                           int32_t* __restrict__ plan, int4 list_off) {
+  __shared__ int hist[kMaxExperts];
+  __shared__ int running[kMaxExperts];
+  __shared__ int tstart[kMaxExperts + 1];
+  __shared__ int wcnt[16][kMaxExperts];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  if (tid < a.slots) hist[tid] = 0;
+  for (int i = tid; i < 16 * kMaxExperts; i += 1024) (&wcnt[0][0])[i] = 0;
+  __syncthreads();
+  for (int r = 0; r < kFusedRounds; ++r) {
+    const int64_t f = (int64_t)r * 1024 + tid;
+    if (f < a.P) {
+      bool valid;
+      const int e = expert_of(a, f, valid);
+      if (valid) atomicAdd(&hist[e], 1);
+    }
+  }
+  __syncthreads();
+  const int n_e = tid < a.slots ? hist[tid] : 0;
+  int total;
+  const int off_e = block_exclusive_scan_1024(n_e, &total);
+  if (tid < a.slots) {
+    offsets[tid] = off_e;
+    running[tid] = off_e;
+  }
+  if (tid == 0) offsets[a.slots] = total;
+
+  const int lo[4] = {list_off.x, list_off.y, list_off.z, list_off.w};
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int BM = kPlanBMs[b];
+    const int tiles = tid < a.slots ? (n_e + BM - 1) / BM : 0;
+    int ntiles;
+    const int ts = block_exclusive_scan_1024(tiles, &ntiles);
+    if (tid < a.slots) tstart[tid] = ts;
+    if (tid == 0) {
+      tstart[a.slots] = ntiles;
+      plan[b] = ntiles;
+      plan[4 + b] = lo[b];
+    }
+    __syncthreads();
+    for (int slot = tid; slot < ntiles; slot += 1024) {
+      int l = 0, h = a.slots;
+      while (h - l > 1) {
+        const int m = (l + h) >> 1;
+        if (tstart[m] <= slot) l = m; else h = m;
+      }
+      plan[lo[b] + slot] = l | ((slot - tstart[l]) << 11);
+    }
+    __syncthreads();
+  }
+
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int r = 0; r < kFusedRounds; ++r) {
+    const int64_t f = (int64_t)r * 1024 + tid;
+    const bool in = f < a.P;
+    bool valid = false;
+    const int e = in ? expert_of(a, f, valid) : 0;
+    valid = valid && in;
+    const int key = valid ? e : 2047;
+    uint64_t same = ~0ull;
+#pragma unroll
+    for (int bit = 0; bit < 11; ++bit) {
+      const bool bb = (key >> bit) & 1;
+      const uint64_t bal = __ballot(bb);
+      same &= bb ? bal : ~bal;
+    }
+    const int rank = __popcll(same & lt);
+    const int cnt = __popcll(same);
+    if (valid && rank == 0) wcnt[w][e] = cnt;
+    __syncthreads();
+    if (valid) {
+      int pos = running[e] + rank;
+      for (int v = 0; v < w; ++v) pos += wcnt[v][e];
+      sorted_pair[pos] = (int32_t)f;
+      inv_pos[f] = pos;
+    } else if (in) {
+      inv_pos[f] = -1;
+    }
+    __syncthreads();
+    if (valid && rank == 0) {
+      atomicAdd(&running[e], cnt);
+      wcnt[w][e] = 0;
+    }
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------- router
 // One wavefront per token: k rounds of (max logit, lowest id) selection.
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
@@ -269,6 +367,11 @@ hipError_t launch_align(const AlignShape& a, const int32_t* topk_ids, int32_t* o
   p.nchunks = a.nchunks;
   p.P = a.P;
   int32_t* counts = static_cast<int32_t*>(ws);
+  int4 lo0 = make_int4((int)a.list_off[0], (int)a.list_off[1], (int)a.list_off[2], (int)a.list_off[3]);
+  if (a.P <= (int64_t)kFusedRounds * 1024) {
+    align_fused_kernel<<<1, 1024, 0, s>>>(p, offsets, sorted_pair, inv_pos, plan, lo0);
+    return hipGetLastError();
+  }
   if (a.nchunks > 0) {
     align_count_kernel<<<a.nchunks, 256, 0, s>>>(p, counts);
     hipError_t e = hipGetLastError();

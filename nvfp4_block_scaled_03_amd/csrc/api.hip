@@ -72,7 +72,7 @@ const char* nvfp4_last_error(void) { return g_err.c_str(); }
 
 // ------------------------------------------------------------------ scales
 size_t nvfp4_global_scale_workspace_size(int64_t batches, int64_t n) {
-  if (batches <= 0 || n <= 0) return 0;
+  if (batches <= 0 || n < 0) return 0;
   return nvfp4::global_scale_ws_bytes(batches, n);
 }
 
@@ -86,9 +86,10 @@ int nvfp4_global_scale(const void* x, int dtype, int64_t batches, int64_t n, flo
                 (long long)batches, (long long)n);
   if (batches == 0) return ok();
   if (!g || (n > 0 && !x)) return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
-  if (!aligned(x, 16) || !aligned(g, 4)) return fail(NVFP4_EINVAL, "%s: EINVAL misaligned x", W);
+  if (!aligned(x, 16) || !aligned(g, 4) || !aligned(ws, 4))
+    return fail(NVFP4_EINVAL, "%s: EINVAL misaligned x, g or ws", W);
   const size_t need = nvfp4_global_scale_workspace_size(batches, n);
-  if (ws_bytes < need || (need && !ws))
+  if (ws_bytes < need || !ws)
     return fail(NVFP4_EWORKSPACE, "%s: EWORKSPACE workspace_size=%zu needed=%zu", W, ws_bytes, need);
   return launched(nvfp4::launch_global_scale(x, dtype, batches, n, g, ws, S(stream)), W);
 }

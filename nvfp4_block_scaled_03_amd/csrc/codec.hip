@@ -52,10 +52,15 @@ __device__ __forceinline__ float scale_of_amax(float amax) {
   return (float)((double)amax / 2688.0);
 }
 
-// grid (nblk, batches).  nblk == 1: write g directly; else write partials.
+// One launch per call: grid (nblk, batches).  Every workgroup folds its
+// maximum into ws_max[b] (float bits of a non-negative value order like
+// unsigned integers), then counts itself in ws_cnt[b]; the last workgroup of a
+// batch computes g[b] and puts both words back to zero, so the workspace is
+// ready for the next call (it must be zero before the first one).
 template <typename T>
-__global__ __launch_bounds__(kThreads) void amax_kernel(const T* __restrict__ x, int64_t n,
-                                                        float* __restrict__ out, int direct) {
+__global__ __launch_bounds__(kThreads) void global_scale_kernel(const T* __restrict__ x, int64_t n,
+                                                                float* __restrict__ g,
+                                                                uint32_t* __restrict__ ws) {
   const int64_t b = blockIdx.y;
   const T* xb = x + b * n;
   const int64_t stride = (int64_t)gridDim.x * kThreads * 8;
@@ -68,20 +73,23 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const T* __restrict__ x,
   }
   m = block_max(m);
   if (threadIdx.x == 0) {
-    if (direct)
-      out[b] = scale_of_amax(m);
-    else
-      out[b * gridDim.x + blockIdx.x] = m;
+    uint32_t* ws_cnt = ws + 2 * b;
+    uint32_t* ws_max = ws + 2 * b + 1;
+    if (gridDim.x == 1) {
+      g[b] = scale_of_amax(m);
+      return;
+    }
+    __hip_atomic_fetch_max(ws_max, (uint32_t)__float_as_int(m), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t done = __hip_atomic_fetch_add(ws_cnt, 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    if (done == gridDim.x - 1) {
+      const uint32_t bits = __hip_atomic_load(ws_max, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+      g[b] = scale_of_amax(__int_as_float((int)bits));
+      __hip_atomic_store(ws_max, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ws_cnt, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
-}
-
-__global__ __launch_bounds__(kThreads) void amax_finalize_kernel(const float* __restrict__ partial,
-                                                                 int nblk, float* __restrict__ g) {
-  const int b = blockIdx.x;
-  float m = 0.0f;
-  for (int i = threadIdx.x; i < nblk; i += kThreads) m = fmaxf(m, partial[(int64_t)b * nblk + i]);
-  m = block_max(m);
-  if (threadIdx.x == 0) g[b] = scale_of_amax(m);
 }
 
 // One thread per 8 elements; the two threads of a 16-element block are
@@ -117,30 +125,27 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const T* __restrict_
 }
 
 int64_t amax_blocks(int64_t n) {
-  if (n <= (int64_t)1 << 20) return 1;
-  int64_t nb = (n + 65535) / 65536;
-  return nb > 256 ? 256 : nb;
+  // About 32 elements per thread; at most 1024 workgroups per batch.
+  int64_t nb = (n + kThreads * 32 - 1) / (kThreads * 32);
+  return nb < 1 ? 1 : (nb > 1024 ? 1024 : nb);
 }
 
 }  // namespace
 
 size_t global_scale_ws_bytes(int64_t batches, int64_t n) {
-  const int64_t nb = amax_blocks(n);
-  return nb == 1 ? 0 : (size_t)(batches * nb) * sizeof(float);
+  (void)n;
+  return (size_t)batches * 2 * sizeof(uint32_t);
 }
 
 hipError_t launch_global_scale(const void* x, int dtype, int64_t batches, int64_t n, float* g,
                                void* ws, hipStream_t s) {
   const int64_t nb = amax_blocks(n);
-  float* out = nb == 1 ? g : static_cast<float*>(ws);
   dim3 grid((unsigned)nb, (unsigned)batches);
+  uint32_t* w = static_cast<uint32_t*>(ws);
   if (dtype == 0)
-    amax_kernel<uint16_t><<<grid, kThreads, 0, s>>>(static_cast<const uint16_t*>(x), n, out, nb == 1);
+    global_scale_kernel<uint16_t><<<grid, kThreads, 0, s>>>(static_cast<const uint16_t*>(x), n, g, w);
   else
-    amax_kernel<float><<<grid, kThreads, 0, s>>>(static_cast<const float*>(x), n, out, nb == 1);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nb == 1) return e;
-  amax_finalize_kernel<<<(unsigned)batches, kThreads, 0, s>>>(out, (int)nb, g);
+    global_scale_kernel<float><<<grid, kThreads, 0, s>>>(static_cast<const float*>(x), n, g, w);
   return hipGetLastError();
 }
 

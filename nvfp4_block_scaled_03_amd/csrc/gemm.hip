@@ -24,6 +24,23 @@
 namespace nvfp4 {
 namespace {
 
+// Tile configuration (compile-time; the defaults are the measured best).
+#ifndef NVFP4_DIRECT_NTW
+#define NVFP4_DIRECT_NTW 2     // 16-column tiles per wavefront, short-tile kernel
+#endif
+#ifndef NVFP4_DIRECT_PFMAX
+#define NVFP4_DIRECT_PFMAX 4   // deepest register prefetch ring (128-k chunks)
+#endif
+#ifndef NVFP4_LIST_MAX
+#define NVFP4_LIST_MAX 2       // tallest tile list used (2: 64 rows, 3: 128 rows)
+#endif
+#ifndef NVFP4_BIG_WN
+#define NVFP4_BIG_WN 64        // columns per wavefront, LDS-staged kernel
+#endif
+#ifndef NVFP4_BIG_NW
+#define NVFP4_BIG_NW 4         // wavefronts per workgroup, LDS-staged kernel
+#endif
+
 constexpr int kNW = 4;      // wavefronts per workgroup
 constexpr int kBK = 128;    // contraction chunk
 constexpr int kLDA = kBK + 8;  // LDS row stride in 16-bit elements (272 bytes)
@@ -61,28 +78,100 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-template <bool W4A4, int EPI, int BM, int WN>
-__global__ __launch_bounds__(kNW * kWave) void grouped_gemm_kernel(KParams p) {
+// Epilogue of a wavefront's MT x NTW accumulator tiles (rows row0 + [0, 16 MT),
+// columns n_wave0 + [0, 16 NTW) of the streaming column order).
+template <int EPI, int MT, int NTW>
+__device__ __forceinline__ void epilogue(const KParams& p, f32x4 (&acc)[MT][NTW], int e, int row0,
+                                         int nrows, int n_wave0, int lane) {
+  const float alpha = p.g_a ? (*p.g_a) * p.g_w[e] : p.g_w[e];
+  const int ln = lane & 15, lg = lane >> 4;
+  if constexpr (EPI == kEpiStoreF32) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = i * 16 + lg * 4 + r;
+          if (row < nrows)
+            p.out_f32[(int64_t)(row0 + row) * p.N + n_wave0 + 16 * j + ln] = alpha * acc[i][j][r];
+        }
+  } else {
+    const float g2 = (EPI == kEpiSwigluFp4) ? *p.g2 : 0.0f;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int q = 0; q < NTW / 2; ++q) {
+        const int hb = (n_wave0 >> 5) + q;  // 16-column block of h
+        float h[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float gate = alpha * acc[i][2 * q][r];
+          const float up = alpha * acc[i][2 * q + 1][r];
+          h[r] = silu(gate) * up;
+        }
+        if constexpr (EPI == kEpiSwigluFp4) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float am = row16_max(fabsf(h[r]));
+            const uint32_t sc = e4m3_scale_code(am, g2);
+            const E2M1Bounds bd = e2m1_bounds(e4m3_value(sc), g2);
+            const uint32_t code = e2m1_code(h[r], bd, sc == 0);
+            const uint32_t other = (uint32_t)dpp_xor1_i((int)code);
+            const int row = i * 16 + lg * 4 + r;
+            if (row < nrows) {
+              const int64_t pr = row0 + row;
+              if ((ln & 1) == 0)
+                p.out_q[pr * (p.I >> 1) + hb * 8 + (ln >> 1)] = (uint8_t)(code | (other << 4));
+              if (ln == 0) p.out_sf[pr * (p.I >> 4) + hb] = (uint8_t)sc;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = i * 16 + lg * 4 + r;
+            if (row < nrows)
+              p.out_bf16[(int64_t)(row0 + row) * p.I + hb * 16 + ln] = (uint16_t)f32_to_bf16_bits(h[r]);
+          }
+        }
+      }
+  }
+}
+
+// Work item of this workgroup: (expert, first row, valid rows, column block).
+struct Tile {
+  int e, row0, nrows, nb;
+};
+__device__ __forceinline__ bool decode_tile(const KParams& p, int BM, Tile& t) {
+  const int ntiles = p.plan[p.list_idx];
+  const int G = ntiles * p.n_blocks;
+  if ((int)blockIdx.x >= G) return false;
+  const int v = xcd_remap(blockIdx.x, G);
+  const int tile = v / p.n_blocks;
+  t.nb = v - tile * p.n_blocks;
+  const int packed = p.plan[p.plan[4 + p.list_idx] + tile];
+  t.e = packed & 2047;
+  t.row0 = p.offsets[t.e] + (packed >> 11) * BM;
+  t.nrows = min(BM, p.offsets[t.e + 1] - t.row0);
+  return true;
+}
+
+template <bool W4A4, int EPI, int BM, int WN, int NW>
+__global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
   constexpr int MT = BM / 16;
   constexpr int NTW = WN / 16;
   // A staging pieces per chunk: 16-byte pieces of codes (32 elements) for
   // W4A4, 16-byte pieces of bf16 (8 elements) for W4A16.
   constexpr int PIECES = W4A4 ? BM * 4 : BM * 16;
-  constexpr int PPT = (PIECES + kNW * kWave - 1) / (kNW * kWave);
+  constexpr int PPT = (PIECES + NW * kWave - 1) / (NW * kWave);
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kLDA];
 
-  const int ntiles = p.plan[p.list_idx];
-  const int G = ntiles * p.n_blocks;
-  if ((int)blockIdx.x >= G) return;
-  const int v = xcd_remap(blockIdx.x, G);
-  const int tile = v / p.n_blocks, nb = v - tile * p.n_blocks;
-  const int packed = p.plan[p.plan[4 + p.list_idx] + tile];
-  const int e = packed & 2047, mt = packed >> 11;
-  const int row0 = p.offsets[e] + mt * BM;
-  const int nrows = min(BM, p.offsets[e + 1] - row0);
+  Tile t;
+  if (!decode_tile(p, BM, t)) return;
+  const int e = t.e, row0 = t.row0, nrows = t.nrows, nb = t.nb;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int n_wave0 = (nb * kNW + wv) * WN;
+  const int n_wave0 = (nb * NW + wv) * WN;
   const bool wave_on = n_wave0 < p.N;
   const int K = p.K, KC = K / kBK, NT = p.N / 16;
 
@@ -91,7 +180,7 @@ __global__ __launch_bounds__(kNW * kWave) void grouped_gemm_kernel(KParams p) {
   bool a_ok[PPT];
 #pragma unroll
   for (int j = 0; j < PPT; ++j) {
-    const int pc = tid + j * kNW * kWave;
+    const int pc = tid + j * NW * kWave;
     const int r = W4A4 ? (pc >> 2) : (pc >> 4);
     a_ok[j] = pc < PIECES && r < nrows;
     int src = 0;
@@ -106,7 +195,7 @@ __global__ __launch_bounds__(kNW * kWave) void grouped_gemm_kernel(KParams p) {
   auto load_a = [&](int kc) {
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
-      const int pc = tid + j * kNW * kWave;
+      const int pc = tid + j * NW * kWave;
       if (a_ok[j]) {
         if constexpr (W4A4) {
           const int qq = pc & 3;
@@ -125,7 +214,7 @@ __global__ __launch_bounds__(kNW * kWave) void grouped_gemm_kernel(KParams p) {
   auto store_a = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
-      const int pc = tid + j * kNW * kWave;
+      const int pc = tid + j * NW * kWave;
       if (pc < PIECES) {
         if constexpr (W4A4) {
           const int r = pc >> 2, qq = pc & 3;
@@ -227,60 +316,127 @@ __global__ __launch_bounds__(kNW * kWave) void grouped_gemm_kernel(KParams p) {
   }
   if (!wave_on) return;
 
-  // ---- Epilogue.
-  const float alpha = p.g_a ? (*p.g_a) * p.g_w[e] : p.g_w[e];
-  const int ln = lane & 15, lg = lane >> 4;
-  if constexpr (EPI == kEpiStoreF32) {
+  epilogue<EPI, MT, NTW>(p, acc, e, row0, nrows, n_wave0, lane);
+}
+
+// Main loop for short tiles (16 or 32 rows): no LDS and no barriers.  Every
+// wavefront streams its own activation fragments (L2-resident rows, the same
+// 16-byte-per-lane fragment layout as the weights: lane 16g + m holds the 32
+// k values [32g, 32g + 32) of row m of a 128-k chunk) and its weight columns
+// into a ring of PF chunks of registers, so PF chunks of loads are in flight
+// while the matrix instructions consume the oldest one.
+template <bool W4A4, int EPI, int MT, int NTW, int PF>
+__global__ __launch_bounds__(kNW * kWave) void grouped_gemm_direct_kernel(KParams p) {
+  constexpr int BM = MT * 16;
+  Tile t;
+  if (!decode_tile(p, BM, t)) return;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int n_wave0 = (t.nb * kNW + wv) * (NTW * 16);
+  if (n_wave0 >= p.N) return;  // no barriers below: idle wavefronts may leave
+  const int K = p.K, KC = K / kBK, NT = p.N / 16;
+  const int g = lane >> 4;
+
+  // Source rows of this lane's A fragments (rows past the tile end read a
+  // valid row; their results are never stored).
+  int64_t arow[MT];
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+  for (int i = 0; i < MT; ++i) {
+    int r = min(i * 16 + (lane & 15), t.nrows - 1);
+    int src = t.row0 + r;
+    if (p.sorted_pair) src = pair_token(p.sorted_pair[src], p.T, p.topk);
+    arow[i] = src;
+  }
+  const int nt0 = n_wave0 >> 4;
+  const int64_t wbase = ((int64_t)(t.e * NT + nt0) * KC) * kWave + lane;
+
+  u32x4 bq[PF][NTW];
+  uint32_t bs[PF][NTW];
+  u32x4 aq[PF][MT][W4A4 ? 1 : 4];
+  uint32_t as[PF][MT];
+
+  auto load = [&](int kc, int u) {
 #pragma unroll
-      for (int j = 0; j < NTW; ++j)
+    for (int j = 0; j < NTW; ++j) {
+      const int64_t unit = wbase + ((int64_t)j * KC + kc) * kWave;
+      bq[u][j] = *reinterpret_cast<const u32x4*>(p.w_q + unit * 16);
+      bs[u][j] = *reinterpret_cast<const uint16_t*>(p.w_sf + unit * 2);
+    }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = i * 16 + lg * 4 + r;
-          if (row < nrows)
-            p.out_f32[(int64_t)(row0 + row) * p.N + n_wave0 + 16 * j + ln] = alpha * acc[i][j][r];
+    for (int i = 0; i < MT; ++i) {
+      if constexpr (W4A4) {
+        aq[u][i][0] = *reinterpret_cast<const u32x4*>(p.a_q + arow[i] * (K >> 1) + kc * 64 + g * 16);
+        as[u][i] = *reinterpret_cast<const uint16_t*>(p.a_sf + arow[i] * (K >> 4) + kc * 8 + g * 2);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          aq[u][i][s] = *reinterpret_cast<const u32x4*>(p.a_bf16 + arow[i] * K + kc * kBK + g * 32 + s * 8);
+      }
+    }
+  };
+
+  f32x4 acc[MT][NTW];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int u) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if constexpr (W4A4) {
+        f16x8 bf[NTW], af[MT];
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+          const uint32_t sb = (bs[u][j] >> (s < 2 ? 0 : 8)) & 0xFFu;
+          bf[j] = dequant8_f16(bq[u][j][s], f16x2_splat(e4m3_value(sb)));
         }
-  } else {
-    const float g2 = (EPI == kEpiSwigluFp4) ? *p.g2 : 0.0f;
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int q = 0; q < NTW / 2; ++q) {
-        const int hb = (n_wave0 >> 5) + q;  // 16-column block of h
-        float h[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float gate = alpha * acc[i][2 * q][r];
-          const float up = alpha * acc[i][2 * q + 1][r];
-          h[r] = silu(gate) * up;
+        for (int i = 0; i < MT; ++i) {
+          const uint32_t sa = (as[u][i] >> (s < 2 ? 0 : 8)) & 0xFFu;
+          af[i] = dequant8_f16(aq[u][i][0][s], f16x2_splat(e4m3_value(sa)));
         }
-        if constexpr (EPI == kEpiSwigluFp4) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float am = row16_max(fabsf(h[r]));
-            const uint32_t sc = e4m3_scale_code(am, g2);
-            const E2M1Bounds bd = e2m1_bounds(e4m3_value(sc), g2);
-            const uint32_t code = e2m1_code(h[r], bd, sc == 0);
-            const uint32_t other = (uint32_t)dpp_xor1_i((int)code);
-            const int row = i * 16 + lg * 4 + r;
-            if (row < nrows) {
-              const int64_t pr = row0 + row;
-              if ((ln & 1) == 0)
-                p.out_q[pr * (p.I >> 1) + hb * 8 + (ln >> 1)] = (uint8_t)(code | (other << 4));
-              if (ln == 0) p.out_sf[pr * (p.I >> 4) + hb] = (uint8_t)sc;
-            }
-          }
-        } else {
+        for (int i = 0; i < MT; ++i)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = i * 16 + lg * 4 + r;
-            if (row < nrows)
-              p.out_bf16[(int64_t)(row0 + row) * p.I + hb * 16 + ln] = (uint16_t)f32_to_bf16_bits(h[r]);
-          }
+          for (int j = 0; j < NTW; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      } else {
+        bf16x8 bf[NTW];
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+          const uint32_t sb = (bs[u][j] >> (s < 2 ? 0 : 8)) & 0xFFu;
+          bf[j] = dequant8_bf16(bq[u][j][s], e4m3_value(sb));
+        }
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          const bf16x8 af = __builtin_bit_cast(bf16x8, aq[u][i][s]);
+#pragma unroll
+          for (int j = 0; j < NTW; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0, 0, 0);
         }
       }
+    }
+  };
+
+  // PF divides KC (chosen by the launcher): prologue, steady state with
+  // unconditional loads, drain.
+  // Keep the prologue's loads in slot order (the compiler would otherwise
+  // cluster them by type, and every later wait would have to drain the ring).
+#pragma unroll
+  for (int u = 0; u < PF; ++u) {
+    load(u, u);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  for (int kc0 = PF; kc0 < KC; kc0 += PF) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      compute(u);
+      load(kc0 + u, u);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < PF; ++u) compute(u);
+  epilogue<EPI, MT, NTW>(p, acc, t.e, t.row0, t.nrows, n_wave0, lane);
 }
 
 // out[t] = sum_j w[t][j] * d[inv_pos[t*k + j]] (+ shared row), FP32, j ascending.
@@ -290,7 +446,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const float* __restrict__ topk_w, int T,
                                                       int topk, int shared, int H, void* out) {
   const int t = blockIdx.x;
-  for (int c = threadIdx.x * 4; c < H; c += 1024) {
+  {
+    const int c = blockIdx.y * 1024 + threadIdx.x * 4;
+    if (c >= H) return;
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < topk; ++j) {
       const int pos = inv_pos[(int64_t)t * topk + j];
@@ -324,25 +482,50 @@ int pick_list(int64_t P, int slots) {
 }
 
 template <bool W4A4, int EPI, int BM, int WN>
-hipError_t launch_one(const KParams& kp, int list_len, hipStream_t s) {
+hipError_t launch_one(KParams kp, int list_len, hipStream_t s) {
+  constexpr int NW = NVFP4_BIG_NW;
+  kp.n_blocks = (kp.N + NW * WN - 1) / (NW * WN);
   const int64_t G = (int64_t)list_len * kp.n_blocks;
   const int64_t grid = (G + 7) / 8 * 8;
-  grouped_gemm_kernel<W4A4, EPI, BM, WN><<<(unsigned)grid, kNW * kWave, 0, s>>>(kp);
+  grouped_gemm_kernel<W4A4, EPI, BM, WN, NW><<<(unsigned)grid, NW * kWave, 0, s>>>(kp);
   return hipGetLastError();
+}
+
+template <bool W4A4, int EPI, int MT, int NTW, int PF>
+hipError_t launch_direct(const KParams& kp, int list_len, hipStream_t s) {
+  const int64_t G = (int64_t)list_len * kp.n_blocks;
+  const int64_t grid = (G + 7) / 8 * 8;
+  grouped_gemm_direct_kernel<W4A4, EPI, MT, NTW, PF><<<(unsigned)grid, kNW * kWave, 0, s>>>(kp);
+  return hipGetLastError();
+}
+
+// Prefetch depth: the largest of 8, 6, 4, 3, 2, 1 chunks that divides the
+// chunk count (fewer for bf16 activations, whose fragments are 4x larger).
+template <bool W4A4, int EPI, int MT, int NTW>
+hipError_t launch_direct_pf(const KParams& kp, int len, hipStream_t s) {
+  const int KC = kp.K / kBK;
+  if (NVFP4_DIRECT_PFMAX >= 8 && W4A4 && KC % 8 == 0)
+    return launch_direct<W4A4, EPI, MT, NTW, 8>(kp, len, s);
+  if (NVFP4_DIRECT_PFMAX >= 6 && W4A4 && KC % 6 == 0)
+    return launch_direct<W4A4, EPI, MT, NTW, 6>(kp, len, s);
+  if (KC % 4 == 0) return launch_direct<W4A4, EPI, MT, NTW, 4>(kp, len, s);
+  if (KC % 3 == 0) return launch_direct<W4A4, EPI, MT, NTW, 3>(kp, len, s);
+  if (KC % 2 == 0) return launch_direct<W4A4, EPI, MT, NTW, 2>(kp, len, s);
+  return launch_direct<W4A4, EPI, MT, NTW, 1>(kp, len, s);
 }
 
 template <bool W4A4, int EPI>
 hipError_t launch_gemm(KParams kp, const AlignShape& al, hipStream_t s) {
-  const int li = pick_list(al.P, al.slots);
+  const int li = min(pick_list(al.P, al.slots), NVFP4_LIST_MAX);
   kp.list_idx = li;
-  const int wn = li <= 1 ? 32 : 64;
+  const int wn = li <= 1 ? 16 * NVFP4_DIRECT_NTW : 64;
   kp.n_blocks = (kp.N + kNW * wn - 1) / (kNW * wn);
   const int len = (int)al.list_len[li];
   switch (li) {
-    case 0: return launch_one<W4A4, EPI, 16, 32>(kp, len, s);
-    case 1: return launch_one<W4A4, EPI, 32, 32>(kp, len, s);
-    case 2: return launch_one<W4A4, EPI, 64, 64>(kp, len, s);
-    default: return launch_one<W4A4, EPI, 128, 64>(kp, len, s);
+    case 0: return launch_direct_pf<W4A4, EPI, 1, NVFP4_DIRECT_NTW>(kp, len, s);
+    case 1: return launch_direct_pf<W4A4, EPI, 2, NVFP4_DIRECT_NTW>(kp, len, s);
+    case 2: return launch_one<W4A4, EPI, 64, NVFP4_BIG_WN>(kp, len, s);
+    default: return launch_one<W4A4, EPI, 128, NVFP4_BIG_WN>(kp, len, s);
   }
 }
 
@@ -402,10 +585,11 @@ hipError_t launch_gemm2_combine(const GemmArgs& a, bool w4a4, hipStream_t s) {
   }
   if (e != hipSuccess) return e;
   if (a.T == 0) return hipSuccess;
+  const dim3 cgrid(a.T, (a.H + 1023) / 1024);
   if (a.out_dtype == 0)
-    combine_kernel<true><<<a.T, 256, 0, s>>>(a.d_ws, a.inv_pos, a.topk_w, a.T, a.topk, a.shared, a.H, a.out);
+    combine_kernel<true><<<cgrid, 256, 0, s>>>(a.d_ws, a.inv_pos, a.topk_w, a.T, a.topk, a.shared, a.H, a.out);
   else
-    combine_kernel<false><<<a.T, 256, 0, s>>>(a.d_ws, a.inv_pos, a.topk_w, a.T, a.topk, a.shared, a.H, a.out);
+    combine_kernel<false><<<cgrid, 256, 0, s>>>(a.d_ws, a.inv_pos, a.topk_w, a.T, a.topk, a.shared, a.H, a.out);
   return hipGetLastError();
 }
 

@@ -50,7 +50,7 @@ def global_scale(x: torch.Tensor, batches: int = 1, out: Optional[torch.Tensor] 
     g = out if out is not None else torch.empty(batches, dtype=torch.float32, device=x.device)
     lib = _lib.load()
     wsb = lib.nvfp4_global_scale_workspace_size(batches, n)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=x.device)
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=x.device)
     call("nvfp4_global_scale", _p(x), _dtype_code(x), batches, n, _p(g), _p(ws), wsb, _stream())
     return g
 
@@ -223,7 +223,7 @@ class MoELayer:
         lib = _lib.load()
         self.g1 = torch.empty(1, dtype=torch.float32, device=dev)
         wsb = lib.nvfp4_global_scale_workspace_size(1, d.T * d.H)
-        self.gs_ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        self.gs_ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)  # zero once
         self.gs_ws_bytes = wsb
         self.a1_q = torch.empty(max(d.T, 1), d.H // 2, dtype=torch.uint8, device=dev)
         self.a1_sf = torch.empty(max(d.T, 1), d.H // 16, dtype=torch.uint8, device=dev)
@@ -245,12 +245,27 @@ class MoELayer:
                  _p(self.al.sorted_pair), _p(self.al.offsets), _p(self.al.plan), _p(w.prep13),
                  _p(w.g13), _p(self.a2_bf16), s)
 
+    def gemm2(self, variant: str, out, weights: Optional[ExpertWeights] = None, topk_w=None):
+        """GEMM2 + combine alone on the layer's current buffers (for kernel timing)."""
+        d, w, s = self.d, weights or self.w, _stream()
+        tw = topk_w if topk_w is not None else self.tw_last
+        if variant == "w4a4":
+            call("grouped_gemm2_combine", ctypes.byref(d), _p(self.a2_q), _p(self.a2_sf),
+                 _p(self.g2), _p(self.al.offsets), _p(self.al.inv_pos), _p(self.al.plan),
+                 _p(tw), _p(w.prep2), _p(w.g2), _p(out), _dtype_code(out), _p(self.ws),
+                 self.ws.numel() * 4, s)
+        else:
+            call("grouped_gemm2_combine_w4a16", ctypes.byref(d), _p(self.a2_bf16),
+                 _p(self.al.offsets), _p(self.al.inv_pos), _p(self.al.plan), _p(tw),
+                 _p(w.prep2), _p(w.g2), _p(out), _dtype_code(out), _p(self.ws),
+                 self.ws.numel() * 4, s)
+
     def forward(self, x, topk_ids, topk_w, variant: str = "w4a4", out=None,
                 out_dtype=torch.bfloat16, weights: Optional[ExpertWeights] = None, marks=None):
         """Run the layer; ``marks`` = three torch.cuda.Events recorded before
         GEMM1, between the GEMMs and after GEMM2 + combine."""
         d, w = self.d, weights or self.w
-        self.x_last = x
+        self.x_last, self.tw_last = x, topk_w
         if out is None:
             out = torch.empty(d.T, d.H, dtype=out_dtype, device=x.device)
         s = _stream()
