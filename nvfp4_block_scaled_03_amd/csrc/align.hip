@@ -73,12 +73,22 @@ __device__ int block_exclusive_scan_1024(int v, int* total) {
   return base + x - v;
 }
 
+// One tile-list entry: {expert | m_tile << 11, first row | rows << 24}, so a
+// GEMM workgroup learns its expert, rows and row count from one 8-byte read.
+__device__ __forceinline__ void write_tile(int32_t* dst, int e, int mt, int BM, const int* soff) {
+  const int row0 = soff[e] + mt * BM;
+  const int rows = min(BM, soff[e + 1] - row0);
+  dst[0] = e | (mt << 11);
+  dst[1] = (int32_t)((uint32_t)row0 | ((uint32_t)rows << 24));
+}
+
 // ---------------------------------------------------------------- scan + plan
 __global__ __launch_bounds__(1024) void align_scan_kernel(AlignP a, int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ plan,
                                                           int4 list_off) {
   __shared__ int tstart[kMaxExperts + 1];
+  __shared__ int soff[kMaxExperts + 1];
   const int e = threadIdx.x;
   int n_e = 0;
   if (e < a.slots) {
@@ -94,8 +104,12 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(AlignP a, int32_t* __r
   if (e < a.slots) {
     for (int c = 0; c < a.nchunks; ++c) counts[(int64_t)c * a.slots + e] += off_e;
     offsets[e] = off_e;
+    soff[e] = off_e;
   }
-  if (e == 0) offsets[a.slots] = total;
+  if (e == 0) {
+    offsets[a.slots] = total;
+    soff[a.slots] = total;
+  }
 
   const int lo[4] = {list_off.x, list_off.y, list_off.z, list_off.w};
 #pragma unroll
@@ -118,7 +132,7 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(AlignP a, int32_t* __r
         const int m = (l + h) >> 1;
         if (tstart[m] <= slot) l = m; else h = m;
       }
-      plan[lo[b] + slot] = l | ((slot - tstart[l]) << 11);
+      write_tile(plan + lo[b] + 2 * slot, l, slot - tstart[l], BM, soff);
     }
     __syncthreads();
   }
@@ -187,6 +201,7 @@ __global__ __launch_bounds__(1024) void align_fused_kernel(AlignP a, int32_t* __
   __shared__ int hist[kMaxExperts];
   __shared__ int running[kMaxExperts];
   __shared__ int tstart[kMaxExperts + 1];
+  __shared__ int soff[kMaxExperts + 1];
   __shared__ int wcnt[16][kMaxExperts];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   if (tid < a.slots) hist[tid] = 0;
@@ -207,8 +222,12 @@ __global__ __launch_bounds__(1024) void align_fused_kernel(AlignP a, int32_t* __
   if (tid < a.slots) {
     offsets[tid] = off_e;
     running[tid] = off_e;
+    soff[tid] = off_e;
   }
-  if (tid == 0) offsets[a.slots] = total;
+  if (tid == 0) {
+    offsets[a.slots] = total;
+    soff[a.slots] = total;
+  }
 
   const int lo[4] = {list_off.x, list_off.y, list_off.z, list_off.w};
 #pragma unroll
@@ -230,7 +249,7 @@ __global__ __launch_bounds__(1024) void align_fused_kernel(AlignP a, int32_t* __
         const int m = (l + h) >> 1;
         if (tstart[m] <= slot) l = m; else h = m;
       }
-      plan[lo[b] + slot] = l | ((slot - tstart[l]) << 11);
+      write_tile(plan + lo[b] + 2 * slot, l, slot - tstart[l], BM, soff);
     }
     __syncthreads();
   }
@@ -343,7 +362,7 @@ AlignShape align_shape(int T, int topk, int E, int shared) {
   for (int b = 0; b < 4; ++b) {
     a.list_off[b] = off;
     a.list_len[b] = (a.P + kPlanBMs[b] - 1) / kPlanBMs[b] + a.slots;
-    off += a.list_len[b];
+    off += 2 * a.list_len[b];
   }
   return a;
 }
@@ -352,7 +371,7 @@ size_t align_ws_bytes(const AlignShape& a) {
   return (size_t)a.nchunks * (size_t)a.slots * sizeof(int32_t);
 }
 
-size_t align_plan_ints(const AlignShape& a) { return (size_t)(a.list_off[3] + a.list_len[3]); }
+size_t align_plan_ints(const AlignShape& a) { return (size_t)(a.list_off[3] + 2 * a.list_len[3]); }
 
 hipError_t launch_align(const AlignShape& a, const int32_t* topk_ids, int32_t* offsets,
                         int32_t* sorted_pair, int32_t* inv_pos, int32_t* plan, void* ws,

@@ -35,10 +35,13 @@ namespace {
 #define NVFP4_LIST_MAX 2       // tallest tile list used (2: 64 rows, 3: 128 rows)
 #endif
 #ifndef NVFP4_BIG_WN
-#define NVFP4_BIG_WN 64        // columns per wavefront, LDS-staged kernel
+#define NVFP4_BIG_WN 32        // columns per wavefront, LDS-staged kernel
 #endif
 #ifndef NVFP4_BIG_NW
 #define NVFP4_BIG_NW 4         // wavefronts per workgroup, LDS-staged kernel
+#endif
+#ifndef NVFP4_DIRECT_AF16
+#define NVFP4_DIRECT_AF16 0    // short tiles: stage activations dequantised (f16)
 #endif
 
 constexpr int kNW = 4;      // wavefronts per workgroup
@@ -142,17 +145,20 @@ __device__ __forceinline__ void epilogue(const KParams& p, f32x4 (&acc)[MT][NTW]
 struct Tile {
   int e, row0, nrows, nb;
 };
-__device__ __forceinline__ bool decode_tile(const KParams& p, int BM, Tile& t) {
+// Tiles whose work shares data are kept on one XCD (``remap``): the launch
+// order is mapped so that each XCD receives a contiguous range of tiles.
+__device__ __forceinline__ bool decode_tile(const KParams& p, bool remap, Tile& t) {
   const int ntiles = p.plan[p.list_idx];
   const int G = ntiles * p.n_blocks;
   if ((int)blockIdx.x >= G) return false;
-  const int v = xcd_remap(blockIdx.x, G);
+  const int v = remap ? xcd_remap(blockIdx.x, G) : (int)blockIdx.x;
   const int tile = v / p.n_blocks;
   t.nb = v - tile * p.n_blocks;
-  const int packed = p.plan[p.plan[4 + p.list_idx] + tile];
-  t.e = packed & 2047;
-  t.row0 = p.offsets[t.e] + (packed >> 11) * BM;
-  t.nrows = min(BM, p.offsets[t.e + 1] - t.row0);
+  const int* ent = p.plan + p.plan[4 + p.list_idx] + 2 * tile;
+  t.e = ent[0] & 2047;
+  const uint32_t rr = (uint32_t)ent[1];
+  t.row0 = (int)(rr & 0xFFFFFFu);
+  t.nrows = (int)(rr >> 24);
   return true;
 }
 
@@ -160,94 +166,89 @@ template <bool W4A4, int EPI, int BM, int WN, int NW>
 __global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
   constexpr int MT = BM / 16;
   constexpr int NTW = WN / 16;
+  static_assert(NTW % 2 == 0, "scale words cover column tiles in pairs");
   // A staging pieces per chunk: 16-byte pieces of codes (32 elements) for
   // W4A4, 16-byte pieces of bf16 (8 elements) for W4A16.
   constexpr int PIECES = W4A4 ? BM * 4 : BM * 16;
-  constexpr int PPT = (PIECES + NW * kWave - 1) / (NW * kWave);
+  static_assert(PIECES % (NW * kWave) == 0, "staging pieces split evenly over the threads");
+  constexpr int PPT = PIECES / (NW * kWave);
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kLDA];
 
   Tile t;
-  if (!decode_tile(p, BM, t)) return;
-  const int e = t.e, row0 = t.row0, nrows = t.nrows, nb = t.nb;
-
+  if (!decode_tile(p, true, t)) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int n_wave0 = (nb * NW + wv) * WN;
+  const int n_wave0 = (t.nb * NW + wv) * WN;
   const bool wave_on = n_wave0 < p.N;
   const int K = p.K, KC = K / kBK, NT = p.N / 16;
 
-  // ---- A staging: source row of each piece this thread moves.
-  int64_t a_row[PPT];
-  bool a_ok[PPT];
+  // ---- A staging: each thread moves PPT pieces per chunk.  Rows past the
+  // tile end repeat its last valid row (their results are never stored), so
+  // every load is unconditional.
+  const uint8_t* a_src[PPT];
+  const uint8_t* s_src[PPT];
+  int a_dst[PPT];  // element offset in a buffer
 #pragma unroll
   for (int j = 0; j < PPT; ++j) {
     const int pc = tid + j * NW * kWave;
     const int r = W4A4 ? (pc >> 2) : (pc >> 4);
-    a_ok[j] = pc < PIECES && r < nrows;
-    int src = 0;
-    if (a_ok[j]) {
-      src = row0 + r;
-      if (p.sorted_pair) src = pair_token(p.sorted_pair[src], p.T, p.topk);
+    const int qq = W4A4 ? (pc & 3) : (pc & 15);
+    int src = t.row0 + min(r, t.nrows - 1);
+    if (p.sorted_pair) src = pair_token(p.sorted_pair[src], p.T, p.topk);
+    if constexpr (W4A4) {
+      a_src[j] = p.a_q + (int64_t)src * (K >> 1) + qq * 16;
+      s_src[j] = p.a_sf + (int64_t)src * (K >> 4) + qq * 2;
+      a_dst[j] = r * kLDA + qq * 32;
+    } else {
+      a_src[j] = reinterpret_cast<const uint8_t*>(p.a_bf16 + (int64_t)src * K + qq * 8);
+      s_src[j] = nullptr;
+      a_dst[j] = r * kLDA + qq * 8;
     }
-    a_row[j] = src;
   }
   u32x4 a_reg[PPT];
   uint32_t a_sreg[PPT];
   auto load_a = [&](int kc) {
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
-      const int pc = tid + j * NW * kWave;
-      if (a_ok[j]) {
-        if constexpr (W4A4) {
-          const int qq = pc & 3;
-          a_reg[j] = *reinterpret_cast<const u32x4*>(p.a_q + a_row[j] * (K >> 1) + kc * 64 + qq * 16);
-          a_sreg[j] = *reinterpret_cast<const uint16_t*>(p.a_sf + a_row[j] * (K >> 4) + kc * 8 + qq * 2);
-        } else {
-          const int qq = pc & 15;
-          a_reg[j] = *reinterpret_cast<const u32x4*>(p.a_bf16 + a_row[j] * K + kc * kBK + qq * 8);
-        }
+      if constexpr (W4A4) {
+        a_reg[j] = *reinterpret_cast<const u32x4*>(a_src[j] + kc * 64);
+        a_sreg[j] = *reinterpret_cast<const uint16_t*>(s_src[j] + kc * 8);
       } else {
-        a_reg[j] = u32x4{0u, 0u, 0u, 0u};
-        a_sreg[j] = 0u;
+        a_reg[j] = *reinterpret_cast<const u32x4*>(a_src[j] + kc * 256);
       }
     }
   };
   auto store_a = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
-      const int pc = tid + j * NW * kWave;
-      if (pc < PIECES) {
-        if constexpr (W4A4) {
-          const int r = pc >> 2, qq = pc & 3;
-          uint16_t* dst = &As[buf][r * kLDA + qq * 32];
-          const f16x2 s_lo = f16x2_splat(e4m3_value(a_sreg[j] & 0xFFu));
-          const f16x2 s_hi = f16x2_splat(e4m3_value((a_sreg[j] >> 8) & 0xFFu));
+      uint16_t* dst = &As[buf][a_dst[j]];
+      if constexpr (W4A4) {
+        const f16x2 s2 = e4m3x2_to_f16x2(a_sreg[j]);
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const f16x8 d = dequant8_f16(a_reg[j][w], w < 2 ? s_lo : s_hi);
-            *reinterpret_cast<f16x8*>(dst + 8 * w) = d;
-          }
-        } else {
-          const int r = pc >> 4, qq = pc & 15;
-          *reinterpret_cast<u32x4*>(&As[buf][r * kLDA + qq * 8]) = a_reg[j];
-        }
+        for (int w = 0; w < 4; ++w)
+          *reinterpret_cast<f16x8*>(dst + 8 * w) =
+              dequant8_f16(a_reg[j][w], w < 2 ? f16x2_lo(s2) : f16x2_hi(s2));
+      } else {
+        *reinterpret_cast<u32x4*>(dst) = a_reg[j];
       }
     }
   };
 
-  // ---- B (weights): this wave's column tiles, one chunk per load.
-  const int64_t codes_total = (int64_t)(p.N) * (K >> 1);  // per expert
+  // ---- B (weights): this wave's column tiles, one 128-k chunk per load,
+  // in two register sets used alternately.
   const int nt0 = n_wave0 >> 4;
-  u32x4 b_cur[NTW], b_nxt[NTW];
-  uint32_t s_cur[NTW], s_nxt[NTW];
-  auto load_b = [&](int kc, u32x4* bq, uint32_t* bs) {
+  const int64_t wbase = ((int64_t)(t.e * NT + nt0) * KC) * kWave + lane;
+  const int64_t sbase = ((int64_t)(t.e * (NT >> 1) + (nt0 >> 1)) * KC) * kWave + lane;
+  u32x4 bq0[NTW], bq1[NTW];
+  uint32_t bs0[NTW / 2], bs1[NTW / 2];
+  auto load_b = [&](int kc, u32x4 (&bq)[NTW], uint32_t (&bs)[NTW / 2]) {
+    if (!wave_on) return;
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const int64_t unit = ((int64_t)(e * NT + nt0 + j) * KC + kc) * kWave + lane;
-      bq[j] = *reinterpret_cast<const u32x4*>(p.w_q + unit * 16);
-      bs[j] = *reinterpret_cast<const uint16_t*>(p.w_sf + unit * 2);
-    }
+    for (int j = 0; j < NTW; ++j)
+      bq[j] = *reinterpret_cast<const u32x4*>(p.w_q + (wbase + ((int64_t)j * KC + kc) * kWave) * 16);
+#pragma unroll
+    for (int j = 0; j < NTW / 2; ++j)
+      bs[j] = *reinterpret_cast<const uint32_t*>(p.w_sf + (sbase + ((int64_t)j * KC + kc) * kWave) * 4);
   };
-  (void)codes_total;
 
   f32x4 acc[MT][NTW];
 #pragma unroll
@@ -255,124 +256,201 @@ __global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
 #pragma unroll
     for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_a(0);
-  if (wave_on) load_b(0, b_cur, s_cur);
-  store_a(0);
-  __syncthreads();
-
   const int a_lrow = lane & 15, a_kq = (lane >> 4) * 32;
-  for (int kc = 0; kc < KC; ++kc) {
-    const int buf = kc & 1;
-    const bool more = kc + 1 < KC;
-    if (more) {
-      load_a(kc + 1);
-      if (wave_on) load_b(kc + 1, b_nxt, s_nxt);
-    }
-    if (wave_on) {
+  auto compute = [&](int buf, const u32x4 (&bq)[NTW], const uint32_t (&bs)[NTW / 2]) {
+    if (!wave_on) return;
+    const uint16_t* abase = &As[buf][a_lrow * kLDA + a_kq];
+    if constexpr (W4A4) {
+      f16x2 sb2[NTW];
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) sb2[j] = e4m3x2_to_f16x2(bs[j >> 1] >> ((j & 1) * 16));
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        if constexpr (W4A4) {
-          f16x8 bf[NTW];
+        f16x8 bf[NTW];
 #pragma unroll
-          for (int j = 0; j < NTW; ++j) {
-            const uint32_t sb = s < 2 ? (s_cur[j] & 0xFFu) : ((s_cur[j] >> 8) & 0xFFu);
-            bf[j] = dequant8_f16(b_cur[j][s], f16x2_splat(e4m3_value(sb)));
-          }
+        for (int j = 0; j < NTW; ++j)
+          bf[j] = dequant8_f16(bq[j][s], s < 2 ? f16x2_lo(sb2[j]) : f16x2_hi(sb2[j]));
 #pragma unroll
-          for (int i = 0; i < MT; ++i) {
-            const f16x8 af = *reinterpret_cast<const f16x8*>(
-                &As[buf][(i * 16 + a_lrow) * kLDA + a_kq + 8 * s]);
+        for (int i = 0; i < MT; ++i) {
+          const f16x8 af = *reinterpret_cast<const f16x8*>(abase + i * 16 * kLDA + 8 * s);
 #pragma unroll
-            for (int j = 0; j < NTW; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[j], acc[i][j], 0, 0, 0);
-          }
-        } else {
-          bf16x8 bf[NTW];
+          for (int j = 0; j < NTW; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[j], acc[i][j], 0, 0, 0);
+        }
+      }
+    } else {
+      float sb[NTW][2];
 #pragma unroll
-          for (int j = 0; j < NTW; ++j) {
-            const uint32_t sb = s < 2 ? (s_cur[j] & 0xFFu) : ((s_cur[j] >> 8) & 0xFFu);
-            bf[j] = dequant8_bf16(b_cur[j][s], e4m3_value(sb));
-          }
+      for (int j = 0; j < NTW; ++j) {
+        const uint32_t w = bs[j >> 1] >> ((j & 1) * 16);
+        sb[j][0] = e4m3_value(w & 0xFFu);
+        sb[j][1] = e4m3_value((w >> 8) & 0xFFu);
+      }
 #pragma unroll
-          for (int i = 0; i < MT; ++i) {
-            const bf16x8 af = *reinterpret_cast<const bf16x8*>(
-                &As[buf][(i * 16 + a_lrow) * kLDA + a_kq + 8 * s]);
+      for (int s = 0; s < 4; ++s) {
+        bf16x8 bf[NTW];
 #pragma unroll
-            for (int j = 0; j < NTW; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0, 0, 0);
-          }
+        for (int j = 0; j < NTW; ++j) bf[j] = dequant8_bf16(bq[j][s], sb[j][s >> 1]);
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          const bf16x8 af = *reinterpret_cast<const bf16x8*>(abase + i * 16 * kLDA + 8 * s);
+#pragma unroll
+          for (int j = 0; j < NTW; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0, 0, 0);
         }
       }
     }
-    if (more) store_a(buf ^ 1);
-    __syncthreads();
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) {
-        b_cur[j] = b_nxt[j];
-        s_cur[j] = s_nxt[j];
-      }
+  };
+
+  // ---- Pipeline: chunk kc computes from LDS buffer kc & 1 and register set
+  // kc & 1 while chunk kc + 1 is in flight; one barrier per chunk.  A trip
+  // runs two chunks so the register sets alternate statically; the
+  // scheduling fences keep the next chunk's loads ahead of the compute.
+  load_a(0);
+  load_b(0, bq0, bs0);
+  store_a(0);
+  __syncthreads();
+  for (int kc = 0;; kc += 2) {
+    const bool more1 = kc + 1 < KC;
+    if (more1) {
+      load_a(kc + 1);
+      load_b(kc + 1, bq1, bs1);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(0, bq0, bs0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!more1) break;
+    store_a(1);
+    __syncthreads();
+    const bool more2 = kc + 2 < KC;
+    if (more2) {
+      load_a(kc + 2);
+      load_b(kc + 2, bq0, bs0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1, bq1, bs1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!more2) break;
+    store_a(0);
+    __syncthreads();
   }
   if (!wave_on) return;
-
-  epilogue<EPI, MT, NTW>(p, acc, e, row0, nrows, n_wave0, lane);
+  epilogue<EPI, MT, NTW>(p, acc, t.e, t.row0, t.nrows, n_wave0, lane);
 }
 
-// Main loop for short tiles (16 or 32 rows): no LDS and no barriers.  Every
-// wavefront streams its own activation fragments (L2-resident rows, the same
-// 16-byte-per-lane fragment layout as the weights: lane 16g + m holds the 32
-// k values [32g, 32g + 32) of row m of a 128-k chunk) and its weight columns
-// into a ring of PF chunks of registers, so PF chunks of loads are in flight
-// while the matrix instructions consume the oldest one.
+// Main loop for short tiles (16 or 32 rows), the decode regime where the
+// weights are read once and the path is bound by HBM bandwidth.  The tile's
+// activation rows (packed NVFP4 or bf16, all of K) are staged into LDS once,
+// behind a single barrier; after that every wavefront only streams its own
+// weight columns, through a register ring of PF 128-k chunks, so PF chunks of
+// loads are in flight while the matrix instructions consume the oldest one.
+// Activation fragments use the weights' lane layout: lane 16g + m reads the
+// 32 k values [32g, 32g + 32) of row m of a chunk.
 template <bool W4A4, int EPI, int MT, int NTW, int PF>
 __global__ __launch_bounds__(kNW * kWave) void grouped_gemm_direct_kernel(KParams p) {
   constexpr int BM = MT * 16;
+  extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];
   Tile t;
-  if (!decode_tile(p, BM, t)) return;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // Column blocks of a tile read disjoint weights: no XCD grouping needed.
+  if (!decode_tile(p, false, t)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n_wave0 = (t.nb * kNW + wv) * (NTW * 16);
-  if (n_wave0 >= p.N) return;  // no barriers below: idle wavefronts may leave
+  const bool wave_on = n_wave0 < p.N;
   const int K = p.K, KC = K / kBK, NT = p.N / 16;
   const int g = lane >> 4;
 
-  // Source rows of this lane's A fragments (rows past the tile end read a
-  // valid row; their results are never stored).
-  int64_t arow[MT];
-#pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    int r = min(i * 16 + (lane & 15), t.nrows - 1);
-    int src = t.row0 + r;
-    if (p.sorted_pair) src = pair_token(p.sorted_pair[src], p.T, p.topk);
-    arow[i] = src;
-  }
   const int nt0 = n_wave0 >> 4;
   const int64_t wbase = ((int64_t)(t.e * NT + nt0) * KC) * kWave + lane;
-
+  const int64_t sbase = ((int64_t)(t.e * (NT >> 1) + (nt0 >> 1)) * KC) * kWave + lane;
   u32x4 bq[PF][NTW];
-  uint32_t bs[PF][NTW];
-  u32x4 aq[PF][MT][W4A4 ? 1 : 4];
-  uint32_t as[PF][MT];
-
+  uint32_t bs[PF][NTW / 2];
+  // bf16 activation fragments ride in the ring too (W4A16: a bf16 tile is 4x
+  // the packed size, too large to stage whole in LDS without costing
+  // occupancy).  Rows past the tile end read a valid row; never stored.
+  constexpr int AR = W4A4 ? 1 : MT;
+  u32x4 ab[PF][AR][W4A4 ? 1 : 4];
+  int64_t arow_g[AR];
+#pragma unroll
+  for (int i = 0; i < AR; ++i) {
+    int src = t.row0 + min(i * 16 + (lane & 15), t.nrows - 1);
+    if (!W4A4 && p.sorted_pair) src = pair_token(p.sorted_pair[src], p.T, p.topk);
+    arow_g[i] = src;
+  }
   auto load = [&](int kc, int u) {
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
       const int64_t unit = wbase + ((int64_t)j * KC + kc) * kWave;
       bq[u][j] = *reinterpret_cast<const u32x4*>(p.w_q + unit * 16);
-      bs[u][j] = *reinterpret_cast<const uint16_t*>(p.w_sf + unit * 2);
     }
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      if constexpr (W4A4) {
-        aq[u][i][0] = *reinterpret_cast<const u32x4*>(p.a_q + arow[i] * (K >> 1) + kc * 64 + g * 16);
-        as[u][i] = *reinterpret_cast<const uint16_t*>(p.a_sf + arow[i] * (K >> 4) + kc * 8 + g * 2);
-      } else {
+    for (int j = 0; j < NTW / 2; ++j) {
+      const int64_t unit = sbase + ((int64_t)j * KC + kc) * kWave;
+      bs[u][j] = *reinterpret_cast<const uint32_t*>(p.w_sf + unit * 4);
+    }
+    if constexpr (!W4A4) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          aq[u][i][s] = *reinterpret_cast<const u32x4*>(p.a_bf16 + arow[i] * K + kc * kBK + g * 32 + s * 8);
-      }
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+          ab[u][i][s4] = *reinterpret_cast<const u32x4*>(p.a_bf16 + arow_g[i] * K + kc * kBK + g * 32 + s4 * 8);
     }
   };
+  // The weight stream does not depend on the activations: start it first,
+  // in slot order (the compiler would otherwise cluster the loads by type,
+  // and every later wait would have to drain the ring).
+  if (wave_on) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      load(u, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // ---- W4A4: stage the tile's activation rows (rows past the tile end
+  // repeat the last valid row; their results are never stored), packed, or
+  // dequantised to f16 once for all wavefronts (AF16).  Row stride is padded
+  // by 16 bytes so the 16 rows read by one fragment load spread over the
+  // banks.
+  constexpr bool AF16 = W4A4 && NVFP4_DIRECT_AF16;
+  const int row_bytes = K >> 1;
+  const int stride = AF16 ? K * 2 + 16 : row_bytes + 16;
+  const int sf_bytes = K >> 4;
+  uint8_t* a_sf_lds = a_lds + BM * stride;
+  if constexpr (AF16) {
+    const int pieces = K >> 5;  // 32-element pieces per row
+    for (int pc = tid; pc < BM * pieces; pc += kNW * kWave) {
+      const int r = pc / pieces, c = pc - r * pieces;
+      int src = t.row0 + min(r, t.nrows - 1);
+      if (p.sorted_pair) src = pair_token(p.sorted_pair[src], p.T, p.topk);
+      const u32x4 cw = *reinterpret_cast<const u32x4*>(p.a_q + (int64_t)src * row_bytes + c * 16);
+      const f16x2 s2 = e4m3x2_to_f16x2(
+          *reinterpret_cast<const uint16_t*>(p.a_sf + (int64_t)src * sf_bytes + c * 2));
+      uint8_t* dst = a_lds + r * stride + c * 64;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        *reinterpret_cast<f16x8*>(dst + 16 * w) = dequant8_f16(cw[w], w < 2 ? f16x2_lo(s2) : f16x2_hi(s2));
+    }
+    __syncthreads();
+  } else if constexpr (W4A4) {
+    const int pieces = row_bytes >> 4;  // 16-byte pieces per row
+    for (int pc = tid; pc < BM * pieces; pc += kNW * kWave) {
+      const int r = pc / pieces, c = pc - r * pieces;
+      int src = t.row0 + min(r, t.nrows - 1);
+      if (p.sorted_pair) src = pair_token(p.sorted_pair[src], p.T, p.topk);
+      *reinterpret_cast<u32x4*>(a_lds + r * stride + c * 16) =
+          *reinterpret_cast<const u32x4*>(p.a_q + (int64_t)src * row_bytes + c * 16);
+    }
+    const int spieces = sf_bytes >> 1;  // 2-byte pieces per row
+    for (int pc = tid; pc < BM * spieces; pc += kNW * kWave) {
+      const int r = pc / spieces, c = pc - r * spieces;
+      int src = t.row0 + min(r, t.nrows - 1);
+      if (p.sorted_pair) src = pair_token(p.sorted_pair[src], p.T, p.topk);
+      *reinterpret_cast<uint16_t*>(a_sf_lds + r * sf_bytes + c * 2) =
+          *reinterpret_cast<const uint16_t*>(p.a_sf + (int64_t)src * sf_bytes + c * 2);
+    }
+    __syncthreads();
+  }
+  if (!wave_on) return;  // no barriers below
 
   f32x4 acc[MT][NTW];
 #pragma unroll
@@ -380,20 +458,37 @@ __global__ __launch_bounds__(kNW * kWave) void grouped_gemm_direct_kernel(KParam
 #pragma unroll
     for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int u) {
+  const int arow = lane & 15;
+  auto compute = [&](int kc, int u) {
+    // Packed activation fragments of this chunk for every m-tile (W4A4), and
+    // the f16 block scales of this chunk ({k-steps 0-1, k-steps 2-3}).
+    u32x4 aq[MT];
+    f16x2 sa2[MT], sb2[NTW];
+    if constexpr (W4A4) {
+#pragma unroll
+      for (int i = 0; i < MT && !AF16; ++i) {
+        aq[i] = *reinterpret_cast<const u32x4*>(a_lds + (i * 16 + arow) * stride + kc * 64 + g * 16);
+        sa2[i] = e4m3x2_to_f16x2(*reinterpret_cast<const uint16_t*>(
+            a_sf_lds + (i * 16 + arow) * sf_bytes + kc * 8 + g * 2));
+      }
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) sb2[j] = e4m3x2_to_f16x2(bs[u][j >> 1] >> ((j & 1) * 16));
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      const int sh = (s < 2 ? 0 : 8);
       if constexpr (W4A4) {
         f16x8 bf[NTW], af[MT];
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-          const uint32_t sb = (bs[u][j] >> (s < 2 ? 0 : 8)) & 0xFFu;
-          bf[j] = dequant8_f16(bq[u][j][s], f16x2_splat(e4m3_value(sb)));
-        }
+        for (int j = 0; j < NTW; ++j)
+          bf[j] = dequant8_f16(bq[u][j][s], s < 2 ? f16x2_lo(sb2[j]) : f16x2_hi(sb2[j]));
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
-          const uint32_t sa = (as[u][i] >> (s < 2 ? 0 : 8)) & 0xFFu;
-          af[i] = dequant8_f16(aq[u][i][0][s], f16x2_splat(e4m3_value(sa)));
+          if constexpr (AF16)
+            af[i] = *reinterpret_cast<const f16x8*>(a_lds + (i * 16 + arow) * stride +
+                                                     (kc * kBK + g * 32 + s * 8) * 2);
+          else
+            af[i] = dequant8_f16(aq[i][s], s < 2 ? f16x2_lo(sa2[i]) : f16x2_hi(sa2[i]));
         }
 #pragma unroll
         for (int i = 0; i < MT; ++i)
@@ -404,12 +499,12 @@ __global__ __launch_bounds__(kNW * kWave) void grouped_gemm_direct_kernel(KParam
         bf16x8 bf[NTW];
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
-          const uint32_t sb = (bs[u][j] >> (s < 2 ? 0 : 8)) & 0xFFu;
+          const uint32_t sb = (bs[u][j >> 1] >> ((j & 1) * 16 + sh)) & 0xFFu;
           bf[j] = dequant8_bf16(bq[u][j][s], e4m3_value(sb));
         }
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
-          const bf16x8 af = __builtin_bit_cast(bf16x8, aq[u][i][s]);
+          const bf16x8 af = __builtin_bit_cast(bf16x8, ab[u][i][s]);
 #pragma unroll
           for (int j = 0; j < NTW; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0, 0, 0);
@@ -418,25 +513,35 @@ __global__ __launch_bounds__(kNW * kWave) void grouped_gemm_direct_kernel(KParam
     }
   };
 
-  // PF divides KC (chosen by the launcher): prologue, steady state with
-  // unconditional loads, drain.
-  // Keep the prologue's loads in slot order (the compiler would otherwise
-  // cluster them by type, and every later wait would have to drain the ring).
-#pragma unroll
-  for (int u = 0; u < PF; ++u) {
-    load(u, u);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  // PF divides KC (chosen by the launcher): the prologue above, a steady
+  // state with unconditional loads, then the drain.  The scheduling fences
+  // pin each refill right behind the compute that frees its slot (left
+  // alone, the scheduler sinks all refills to the end of the loop body and
+  // the ring runs empty).
   for (int kc0 = PF; kc0 < KC; kc0 += PF) {
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
-      compute(u);
+      compute(kc0 - PF + u, u);
+      __builtin_amdgcn_sched_barrier(0);
       load(kc0 + u, u);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 #pragma unroll
-  for (int u = 0; u < PF; ++u) compute(u);
+  for (int u = 0; u < PF; ++u) compute(KC - PF + u, u);
   epilogue<EPI, MT, NTW>(p, acc, t.e, t.row0, t.nrows, n_wave0, lane);
+}
+
+// Largest activation tile the short-tile kernel stages (larger ones, e.g. bf16
+// rows with a long K, take the chunked LDS kernel instead).
+constexpr size_t kDirectLdsMax = 96 * 1024;
+
+// LDS bytes of the short-tile kernel: padded packed activation rows + scales
+// (W4A4 only; the bf16 variant keeps its activations in registers).
+size_t direct_lds_bytes(bool w4a4, int BM, int K) {
+  if (!w4a4) return 0;
+  if (NVFP4_DIRECT_AF16) return (size_t)BM * (K * 2 + 16) + (size_t)BM * (K / 16);
+  return (size_t)BM * (K / 2 + 16) + (size_t)BM * (K / 16);
 }
 
 // out[t] = sum_j w[t][j] * d[inv_pos[t*k + j]] (+ shared row), FP32, j ascending.
@@ -495,7 +600,17 @@ template <bool W4A4, int EPI, int MT, int NTW, int PF>
 hipError_t launch_direct(const KParams& kp, int list_len, hipStream_t s) {
   const int64_t G = (int64_t)list_len * kp.n_blocks;
   const int64_t grid = (G + 7) / 8 * 8;
-  grouped_gemm_direct_kernel<W4A4, EPI, MT, NTW, PF><<<(unsigned)grid, kNW * kWave, 0, s>>>(kp);
+  const size_t lds = direct_lds_bytes(W4A4, MT * 16, kp.K);
+  auto kern = grouped_gemm_direct_kernel<W4A4, EPI, MT, NTW, PF>;
+  static bool attr_set = false;  // raise the dynamic LDS limit once per instantiation
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)kDirectLdsMax);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  kern<<<(unsigned)grid, kNW * kWave, lds, s>>>(kp);
   return hipGetLastError();
 }
 
@@ -521,6 +636,10 @@ hipError_t launch_gemm(KParams kp, const AlignShape& al, hipStream_t s) {
   const int wn = li <= 1 ? 16 * NVFP4_DIRECT_NTW : 64;
   kp.n_blocks = (kp.N + kNW * wn - 1) / (kNW * wn);
   const int len = (int)al.list_len[li];
+  if (li <= 1 && direct_lds_bytes(W4A4, li == 0 ? 16 : 32, kp.K) > kDirectLdsMax) {
+    kp.list_idx = 2;
+    return launch_one<W4A4, EPI, 64, NVFP4_BIG_WN>(kp, (int)al.list_len[2], s);
+  }
   switch (li) {
     case 0: return launch_direct_pf<W4A4, EPI, 1, NVFP4_DIRECT_NTW>(kp, len, s);
     case 1: return launch_direct_pf<W4A4, EPI, 2, NVFP4_DIRECT_NTW>(kp, len, s);

@@ -8,9 +8,11 @@
 
 namespace nvfp4 {
 
-// Tile heights the alignment plan lists, in this order.
+// Tile heights the alignment plan lists, in this order.  Plan layout (int32):
+// counts[4], list offsets[4], then per list 2 ints per tile
+// {expert | m_tile << 11, first row | rows << 24}, expert-major.
 constexpr int kPlanBMs[4] = {16, 32, 64, 128};
-constexpr int kPlanHeader = 8;   // counts[4], list offsets[4] (in int32 units)
+constexpr int kPlanHeader = 8;
 constexpr int kMaxExperts = 1024;
 
 size_t global_scale_ws_bytes(int64_t batches, int64_t n);

@@ -54,7 +54,7 @@ def test_size_queries(lib):
     assert lib.nvfp4_prep_weights_size(ctypes.byref(d), 5) == 0
     assert lib.moe_align_workspace_size(ctypes.byref(d)) == 1 * 128 * 4
     plan = lib.moe_align_plan_size(ctypes.byref(d))
-    assert plan == 4 * (8 + sum((P + bm - 1) // bm + 128 for bm in (16, 32, 64, 128)))
+    assert plan == 4 * (8 + sum(2 * ((P + bm - 1) // bm + 128) for bm in (16, 32, 64, 128)))
     assert lib.nvfp4_global_scale_workspace_size(1, 64 * 2048) == 8
     assert lib.nvfp4_global_scale_workspace_size(4, 1 << 22) == 4 * 8
     ds = _d(T=256, topk=10, E=512, H=4096, I=1024, shared=1)

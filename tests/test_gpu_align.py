@@ -51,12 +51,16 @@ def _check_align(dev, ids_np, E, shared):
     assert np.array_equal(to_np(al.sorted_pair)[:n_kept], sp)
     assert np.array_equal(to_np(al.inv_pos)[:P], inv)
     # The tile lists cover every expert's rows in order, for each tile height.
-    plan = to_np(al.plan)
+    plan = to_np(al.plan).astype(np.int64) & 0xFFFFFFFF
     for b, bm in enumerate((16, 32, 64, 128)):
         cnt, lo = plan[b], plan[4 + b]
-        want = [e | (m << 11) for e in range(E + shared)
-                for m in range((int(off[e + 1] - off[e]) + bm - 1) // bm)]
-        assert cnt == len(want) and list(plan[lo:lo + cnt]) == want, bm
+        want = []
+        for e in range(E + shared):
+            n_e = int(off[e + 1] - off[e])
+            for m in range((n_e + bm - 1) // bm):
+                row0 = int(off[e]) + m * bm
+                want += [e | (m << 11), row0 | (min(bm, n_e - m * bm) << 24)]
+        assert cnt * 2 == len(want) and list(plan[lo:lo + 2 * cnt]) == want, bm
     return al
 
 
@@ -98,7 +102,7 @@ def test_align_is_deterministic(dev):
     assert np.array_equal(pa[:8], pb[:8])
     for i in range(4):          # list entries beyond each count are not written
         lo, n = pa[4 + i], pa[i]
-        assert np.array_equal(pa[lo:lo + n], pb[lo:lo + n])
+        assert np.array_equal(pa[lo:lo + 2 * n], pb[lo:lo + 2 * n])
 
 
 def test_align_plan_size_matches(dev):

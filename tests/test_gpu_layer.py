@@ -88,7 +88,8 @@ def test_prep_layout(dev):
         prep = to_np(ops.prep_weights(d, which, torch.from_numpy(q).to(dev), torch.from_numpy(sf).to(dev)))
         NT, KC = N // 16, K // 128
         codes = prep[:S * N * K // 2].reshape(S, NT, KC, 64, 16)
-        scales = prep[S * N * K // 2:].reshape(S, NT, KC, 64, 2)
+        # scales: [S][tile pairs][chunks][lanes][2 tiles][2 bytes]
+        scales = prep[S * N * K // 2:].reshape(S, NT // 2, KC, 64, 2, 2)
         for e in range(S):
             for nt in range(NT):
                 for lane in range(64):
@@ -99,7 +100,8 @@ def test_prep_layout(dev):
                         row = nt * 16 + n
                     for kc in range(KC):
                         assert np.array_equal(codes[e, nt, kc, lane], q[e, row, kc * 64 + 16 * g: kc * 64 + 16 * g + 16])
-                        assert np.array_equal(scales[e, nt, kc, lane], sf[e, row, kc * 8 + 2 * g: kc * 8 + 2 * g + 2])
+                        assert np.array_equal(scales[e, nt // 2, kc, lane, nt % 2],
+                                              sf[e, row, kc * 8 + 2 * g: kc * 8 + 2 * g + 2])
 
 
 # ---------------------------------------------------------------- stages
