@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_MOE_ABI_VERSION 1
+#define NVFP4_MOE_ABI_VERSION 2
 
 /* Status codes. */
 #define NVFP4_OK 0
@@ -138,10 +138,18 @@ int nvfp4_global_scale(const void* x, int dtype, int64_t batches, int64_t n, flo
  * (taken on the real quotients).  This is the per-token activation
  * quantisation of FlashInfer #2723 ("Why 39 vs 49 tok/s?"), with per-block
  * amax by a wavefront reduction in FP32 ("2. FP32 Amax Computation").
- * Requirements: K % 16 == 0, ldx >= K, ldx % 8 == 0, x 16-byte aligned,
- * q 4-byte aligned, g != NULL, rows_per_g >= 1. */
+ * x_deq (optional, may be NULL): IEEE half [rows][K] receiving the exact
+ * value E2M1[code] * E4M3[scale] of every element (the global scale is not
+ * applied; six significant bits at most and |value| <= 2688, so the half is
+ * exact).  The grouped GEMMs accept this copy in place of the codes: on
+ * gfx950 the FP4 conversion instructions run at a quarter of the VALU rate,
+ * and decoding each activation once here saves decoding it in every
+ * wavefront that reads it.
+ * Requirements: K % 16 == 0, ldx >= K, ldx % 8 == 0, x and x_deq 16-byte
+ * aligned, q 4-byte aligned, g != NULL, rows_per_g >= 1. */
 int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx,
-                   const float* g, int64_t rows_per_g, uint8_t* q, uint8_t* sf, void* stream);
+                   const float* g, int64_t rows_per_g, uint8_t* q, uint8_t* sf, uint16_t* x_deq,
+                   void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Router (runs before the path; not part of the timed layer).               */
@@ -209,11 +217,16 @@ int nvfp4_prep_weights(const nvfp4_moe_dims* dims, int which, const uint8_t* q, 
  * output), gw13 a device array [E+shared], g2 a device scalar chosen by the
  * caller (a static calibration of the intermediate).  Outputs a2_q uint8
  * [P][I/2] and a2_sf uint8 [P][I/16] are in sorted-row order.  a1_q/a1_sf are
- * the canonical [T][H/2] / [T][H/16] activations. */
+ * the canonical [T][H/2] / [T][H/16] activations.
+ * a1_deq (optional): the x_deq output of nvfp4_quantize for a1_q/a1_sf, half
+ * [T][H]; when given, it is read instead of the codes (which may then be
+ * NULL) -- the same values, decoded once.  a2_deq (optional output): half
+ * [P][I], the exact values of the a2 codes (as x_deq), for GEMM2. */
 int grouped_gemm1_swiglu(const nvfp4_moe_dims* dims, const uint8_t* a1_q, const uint8_t* a1_sf,
-                         const float* g1, const int32_t* sorted_pair, const int32_t* expert_offsets,
-                         const int32_t* plan, const uint8_t* w13_prep, const float* gw13,
-                         const float* g2, uint8_t* a2_q, uint8_t* a2_sf, void* stream);
+                         const uint16_t* a1_deq, const float* g1, const int32_t* sorted_pair,
+                         const int32_t* expert_offsets, const int32_t* plan,
+                         const uint8_t* w13_prep, const float* gw13, const float* g2,
+                         uint8_t* a2_q, uint8_t* a2_sf, uint16_t* a2_deq, void* stream);
 
 /* Workspace of the GEMM2 calls: the per-row FP32 down-projection outputs
  * [P][H] that the combine reads. */
@@ -225,9 +238,12 @@ size_t grouped_gemm_workspace_size(const nvfp4_moe_dims* dims);
  * pair with weight 1), summed in FP32 in the order j = 0..topk-1, shared last,
  * rows with inv_pos = -1 skipped.  out is [T][H] bfloat16 (out_dtype
  * NVFP4_BF16, round to nearest even: the bf16-only output of vLLM PR #29242,
- * "Force bf16 only") or float32 (NVFP4_F32, the same sums unrounded). */
+ * "Force bf16 only") or float32 (NVFP4_F32, the same sums unrounded).
+ * a2_deq (optional): the a2_deq output of grouped_gemm1_swiglu, read instead
+ * of a2_q/a2_sf (which may then be NULL). */
 int grouped_gemm2_combine(const nvfp4_moe_dims* dims, const uint8_t* a2_q, const uint8_t* a2_sf,
-                          const float* g2, const int32_t* expert_offsets, const int32_t* inv_pos,
+                          const uint16_t* a2_deq, const float* g2, const int32_t* expert_offsets,
+                          const int32_t* inv_pos,
                           const int32_t* plan, const float* topk_w, const uint8_t* w2_prep,
                           const float* gw2, void* out, int out_dtype, void* ws, size_t ws_bytes,
                           void* stream);

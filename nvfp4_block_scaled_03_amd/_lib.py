@@ -13,7 +13,7 @@ from ctypes import c_char_p, c_int, c_int32, c_int64, c_size_t, c_void_p
 # variant with different tile settings); the default is the in-tree build.
 LIB_PATH = os.environ.get("NVFP4_MOE_LIB") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "libnvfp4moe.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 NVFP4_OK = 0
 NVFP4_EINVAL = -1
@@ -42,7 +42,7 @@ SIGNATURES = {
     "nvfp4_global_scale": (c_int, [c_void_p, c_int, c_int64, c_int64, c_void_p, c_void_p,
                                    c_size_t, c_void_p]),
     "nvfp4_quantize": (c_int, [c_void_p, c_int, c_int64, c_int64, c_int64, c_void_p, c_int64,
-                               c_void_p, c_void_p, c_void_p]),
+                               c_void_p, c_void_p, c_void_p, c_void_p]),
     "moe_route_topk": (c_int, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
     "moe_align_workspace_size": (c_size_t, [_P]),
     "moe_align_plan_size": (c_size_t, [_P]),
@@ -53,10 +53,10 @@ SIGNATURES = {
     "grouped_gemm_workspace_size": (c_size_t, [_P]),
     "grouped_gemm1_swiglu": (c_int, [_P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                                     c_void_p]),
+                                     c_void_p, c_void_p, c_void_p]),
     "grouped_gemm2_combine": (c_int, [_P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int,
-                                      c_void_p, c_size_t, c_void_p]),
+                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_int, c_void_p, c_size_t, c_void_p]),
     "grouped_gemm1_swiglu_w4a16": (c_int, [_P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                            c_void_p, c_void_p, c_void_p]),
     "grouped_gemm2_combine_w4a16": (c_int, [_P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,

@@ -95,7 +95,7 @@ int nvfp4_global_scale(const void* x, int dtype, int64_t batches, int64_t n, flo
 }
 
 int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx, const float* g,
-                   int64_t rows_per_g, uint8_t* q, uint8_t* sf, void* stream) {
+                   int64_t rows_per_g, uint8_t* q, uint8_t* sf, uint16_t* x_deq, void* stream) {
   const char* W = "nvfp4_quantize";
   if (dtype != NVFP4_BF16 && dtype != NVFP4_F32)
     return fail(NVFP4_EINVAL, "%s: EINVAL dtype=%d", W, dtype);
@@ -107,9 +107,10 @@ int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ld
                 (long long)K);
   if (rows == 0) return ok();
   if (!x || !g || !q || !sf) return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
-  if (!aligned(x, 16) || !aligned(q, 4) || !aligned(g, 4))
-    return fail(NVFP4_EINVAL, "%s: EINVAL misaligned pointer (x 16 B, q 4 B)", W);
-  return launched(nvfp4::launch_quantize(x, dtype, rows, K, ldx, g, rows_per_g, q, sf, S(stream)), W);
+  if (!aligned(x, 16) || !aligned(q, 4) || !aligned(g, 4) || !aligned(x_deq, 16))
+    return fail(NVFP4_EINVAL, "%s: EINVAL misaligned pointer (x, x_deq 16 B, q 4 B)", W);
+  return launched(nvfp4::launch_quantize(x, dtype, rows, K, ldx, g, rows_per_g, q, sf, x_deq,
+                                         S(stream)), W);
 }
 
 // ------------------------------------------------------------------ router
@@ -199,14 +200,16 @@ static nvfp4::GemmArgs gemm_args(const nvfp4_moe_dims* d) {
 }
 
 int grouped_gemm1_swiglu(const nvfp4_moe_dims* d, const uint8_t* a1_q, const uint8_t* a1_sf,
-                         const float* g1, const int32_t* sorted_pair, const int32_t* expert_offsets,
-                         const int32_t* plan, const uint8_t* w13_prep, const float* gw13,
-                         const float* g2, uint8_t* a2_q, uint8_t* a2_sf, void* stream) {
+                         const uint16_t* a1_deq, const float* g1, const int32_t* sorted_pair,
+                         const int32_t* expert_offsets, const int32_t* plan,
+                         const uint8_t* w13_prep, const float* gw13, const float* g2,
+                         uint8_t* a2_q, uint8_t* a2_sf, uint16_t* a2_deq, void* stream) {
   const char* W = "grouped_gemm1_swiglu";
   if (int r = check_dims(d, W)) return r;
   if (d->T == 0) return ok();
-  if (!a1_q || !a1_sf || !g1 || !sorted_pair || !expert_offsets || !plan || !w13_prep || !gw13 ||
-      !g2 || !a2_q || !a2_sf || !aligned(a1_q, 16) || !aligned(a1_sf, 2) || !aligned(w13_prep, 16))
+  if ((!a1_deq && (!a1_q || !a1_sf)) || !g1 || !sorted_pair || !expert_offsets || !plan ||
+      !w13_prep || !gw13 || !g2 || !a2_q || !a2_sf || !aligned(a1_q, 16) || !aligned(a1_sf, 2) ||
+      !aligned(a1_deq, 16) || !aligned(a2_deq, 2) || !aligned(w13_prep, 16))
     return gemm_fail_shape(W, d, 2 * d->I, d->H, 0);
   nvfp4::GemmArgs a = gemm_args(d);
   a.offsets = expert_offsets;
@@ -214,12 +217,14 @@ int grouped_gemm1_swiglu(const nvfp4_moe_dims* d, const uint8_t* a1_q, const uin
   a.plan = plan;
   a.a_q = a1_q;
   a.a_sf = a1_sf;
+  a.a_h = a1_deq;
   a.g_a = g1;
   a.w_prep = w13_prep;
   a.g_w = gw13;
   a.g2 = g2;
   a.out_q = a2_q;
   a.out_sf = a2_sf;
+  a.out_h = a2_deq;
   return launched(nvfp4::launch_gemm1(a, true, S(stream)), W);
 }
 
@@ -237,10 +242,10 @@ int grouped_gemm1_swiglu_w4a16(const nvfp4_moe_dims* d, const uint16_t* x,
   a.offsets = expert_offsets;
   a.sorted_pair = sorted_pair;
   a.plan = plan;
-  a.a_bf16 = x;
+  a.a_h = x;
   a.w_prep = w13_prep;
   a.g_w = gw13;
-  a.out_bf16 = a2;
+  a.out_h = a2;
   return launched(nvfp4::launch_gemm1(a, false, S(stream)), W);
 }
 
@@ -263,7 +268,8 @@ static int gemm2_common(const char* W, const nvfp4_moe_dims* d, const int32_t* e
 }
 
 int grouped_gemm2_combine(const nvfp4_moe_dims* d, const uint8_t* a2_q, const uint8_t* a2_sf,
-                          const float* g2, const int32_t* expert_offsets, const int32_t* inv_pos,
+                          const uint16_t* a2_deq, const float* g2, const int32_t* expert_offsets,
+                          const int32_t* inv_pos,
                           const int32_t* plan, const float* topk_w, const uint8_t* w2_prep,
                           const float* gw2, void* out, int out_dtype, void* ws, size_t ws_bytes,
                           void* stream) {
@@ -272,7 +278,8 @@ int grouped_gemm2_combine(const nvfp4_moe_dims* d, const uint8_t* a2_q, const ui
                            out_dtype, ws, ws_bytes))
     return r;
   if (d->T == 0) return ok();
-  if (!a2_q || !a2_sf || !g2 || !aligned(a2_q, 16) || !aligned(a2_sf, 2))
+  if ((!a2_deq && (!a2_q || !a2_sf)) || !g2 || !aligned(a2_q, 16) || !aligned(a2_sf, 2) ||
+      !aligned(a2_deq, 16))
     return gemm_fail_shape(W, d, d->H, d->I, ws_bytes);
   nvfp4::GemmArgs a = gemm_args(d);
   a.offsets = expert_offsets;
@@ -281,6 +288,7 @@ int grouped_gemm2_combine(const nvfp4_moe_dims* d, const uint8_t* a2_q, const ui
   a.topk_w = topk_w;
   a.a_q = a2_q;
   a.a_sf = a2_sf;
+  a.a_h = a2_deq;
   a.g_a = g2;
   a.w_prep = w2_prep;
   a.g_w = gw2;
@@ -306,7 +314,7 @@ int grouped_gemm2_combine_w4a16(const nvfp4_moe_dims* d, const uint16_t* a2,
   a.inv_pos = inv_pos;
   a.plan = plan;
   a.topk_w = topk_w;
-  a.a_bf16 = a2;
+  a.a_h = a2;
   a.w_prep = w2_prep;
   a.g_w = gw2;
   a.d_ws = static_cast<float*>(ws);

@@ -92,16 +92,30 @@ __global__ __launch_bounds__(kThreads) void global_scale_kernel(const T* __restr
   }
 }
 
+// Value of the E2M1 code c (sign in bit 3) times the block scale s, exact
+// in f16 (at most six significant bits, magnitude in [2^-10, 2688]).
+__device__ __forceinline__ uint32_t deq_f16_bits(uint32_t c, float s) {
+  const uint32_t m = c & 7u;
+  const float mag = m < 2 ? 0.5f * (float)m
+                          : __int_as_float((int)(((m >> 1) + 126u) << 23)) * (1.0f + 0.5f * (float)(m & 1u));
+  const float v = (c & 8u) ? -(mag * s) : mag * s;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
 // One thread per 8 elements; the two threads of a 16-element block are
 // adjacent lanes (K % 16 == 0 and the grid starts at an even index), so the
-// block amax is one DPP exchange.
+// block amax is one DPP exchange.  With x_deq, the exact f16 values of the
+// codes (code * block scale, global scale not applied) are written as well:
+// the grouped GEMMs read that copy instead of decoding the codes in every
+// wavefront that uses them.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const T* __restrict__ x, int64_t rows,
                                                             int64_t K, int64_t ldx,
                                                             const float* __restrict__ g,
                                                             int64_t rows_per_g,
                                                             uint8_t* __restrict__ q,
-                                                            uint8_t* __restrict__ sf) {
+                                                            uint8_t* __restrict__ sf,
+                                                            uint16_t* __restrict__ x_deq) {
   const int64_t hb_per_row = K >> 3;
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (i >= rows * hb_per_row) return;  // whole lane pairs leave together
@@ -122,6 +136,13 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const T* __restrict_
   for (int j = 0; j < 8; ++j) word |= e2m1_code(v[j], bd, sc == 0) << (4 * j);
   *reinterpret_cast<uint32_t*>(q + row * (K >> 1) + (c8 >> 1)) = word;
   if ((c8 & 15) == 0) sf[row * (K >> 4) + (c8 >> 4)] = (uint8_t)sc;
+  if (x_deq) {
+    u32x4 d;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      d[j] = deq_f16_bits((word >> (8 * j)) & 15u, s) | (deq_f16_bits((word >> (8 * j + 4)) & 15u, s) << 16);
+    *reinterpret_cast<u32x4*>(x_deq + row * K + c8) = d;
+  }
 }
 
 int64_t amax_blocks(int64_t n) {
@@ -151,15 +172,15 @@ hipError_t launch_global_scale(const void* x, int dtype, int64_t batches, int64_
 
 hipError_t launch_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx,
                            const float* g, int64_t rows_per_g, uint8_t* q, uint8_t* sf,
-                           hipStream_t s) {
+                           uint16_t* x_deq, hipStream_t s) {
   const int64_t threads = rows * (K >> 3);
   const int64_t blocks = (threads + kThreads - 1) / kThreads;
   if (dtype == 0)
     quantize_kernel<uint16_t><<<(unsigned)blocks, kThreads, 0, s>>>(
-        static_cast<const uint16_t*>(x), rows, K, ldx, g, rows_per_g, q, sf);
+        static_cast<const uint16_t*>(x), rows, K, ldx, g, rows_per_g, q, sf, x_deq);
   else
     quantize_kernel<float><<<(unsigned)blocks, kThreads, 0, s>>>(
-        static_cast<const float*>(x), rows, K, ldx, g, rows_per_g, q, sf);
+        static_cast<const float*>(x), rows, K, ldx, g, rows_per_g, q, sf, x_deq);
   return hipGetLastError();
 }
 

@@ -1,23 +1,34 @@
 // Grouped NVFP4 expert GEMMs with fused SwiGLU + requantisation (GEMM1) and
 // the down projection + top-k weighted combine (GEMM2), for gfx950.
 //
-// Contraction strategy: NVFP4 operands are dequantised exactly in registers
-// (code * E4M3 block scale, at most six significant bits) and multiplied on
-// the 16x16x32 f16 (W4A4) or bf16 (W4A16) matrix instructions with FP32
-// accumulation; the FP32 global scales enter as one per-expert alpha in the
-// epilogue (the alpha-pointer-array epilogue with beta = 0 of vLLM PR #29242,
-// review of nvfp4_blockwise_moe_kernel.cu).  The native FP4 instructions of
+// Contraction strategy: NVFP4 operands are dequantised exactly (code * E4M3
+// block scale has at most six significant bits and lies in [2^-10, 2688], so
+// it is exact in f16) and multiplied on the 16x16x32 f16 (W4A4) or bf16
+// (W4A16) matrix instructions with FP32 accumulation; the FP32 global scales
+// enter as one per-expert alpha in the epilogue (the alpha-pointer-array
+// epilogue with beta = 0 of vLLM PR #29242, review of
+// nvfp4_blockwise_moe_kernel.cu).  The native FP4 matrix instructions of
 // gfx950 take power-of-two scales per 32 elements, which cannot carry E4M3
-// scales per 16 exactly; see the design doc for the comparison.
+// scales per 16 exactly.
+//
+// The FP4 conversion instructions of gfx950 issue at a quarter of the rate of
+// plain VALU work, so decoding is the cost to minimise: every weight element
+// is decoded once per wavefront that uses it, and the activations are either
+// decoded once per workgroup (LDS kernel, codes in) or not at all (an exact
+// f16 copy written by their producer: nvfp4_quantize for a1, the GEMM1
+// epilogue for a2).  Activation kinds (template parameter AK):
+//   kActCodes  NVFP4 codes + scales, decoded here
+//   kActF16    the exact f16 dequantised copy of NVFP4 codes
+//   kActBf16   bf16 activations (W4A16)
 //
 // Work decomposition: the alignment plan lists (expert, 16..128-row tile)
-// pairs on the device; a workgroup takes one tile and BN = 4 * WN output
-// columns.  Each wavefront owns WN columns for all BM rows: it streams its
-// weight columns straight from HBM into registers (one coalesced 16-byte load
-// per lane per 16 columns x 128 k, see prep.hip) while the BM x 128 activation
-// chunk is staged once per workgroup in LDS, dequantised, double-buffered.
-// Workgroup ids are remapped so that consecutive tiles land on the same XCD
-// (shared L2 for the expert's weights and the tile's activation rows).
+// pairs on the device.  Short tiles (the decode regime) run on a persistent
+// streaming kernel; taller tiles on a kernel that stages the activation chunk
+// in LDS once per workgroup.  Weights stream from HBM straight into registers
+// in the layout written by prep.hip: one coalesced 16-byte load per lane per
+// 16 columns x 128 k, which is exactly the lane's matrix-instruction operand.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -25,12 +36,6 @@ namespace nvfp4 {
 namespace {
 
 // Tile configuration (compile-time; the defaults are the measured best).
-#ifndef NVFP4_DIRECT_NTW
-#define NVFP4_DIRECT_NTW 2     // 16-column tiles per wavefront, short-tile kernel
-#endif
-#ifndef NVFP4_DIRECT_PFMAX
-#define NVFP4_DIRECT_PFMAX 4   // deepest register prefetch ring (128-k chunks)
-#endif
 #ifndef NVFP4_LIST_MAX
 #define NVFP4_LIST_MAX 2       // tallest tile list used (2: 64 rows, 3: 128 rows)
 #endif
@@ -40,26 +45,41 @@ namespace {
 #ifndef NVFP4_BIG_NW
 #define NVFP4_BIG_NW 4         // wavefronts per workgroup, LDS-staged kernel
 #endif
-#ifndef NVFP4_DIRECT_AF16
-#define NVFP4_DIRECT_AF16 0    // short tiles: stage activations dequantised (f16)
+#ifndef NVFP4_STREAM_NTW
+#define NVFP4_STREAM_NTW 2     // 16-column tiles per work unit, streaming kernel
+#endif
+#ifndef NVFP4_STREAM_PFMAX
+#define NVFP4_STREAM_PFMAX 4   // deepest ring of the streaming kernel (128-k chunks)
 #endif
 
-constexpr int kNW = 4;      // wavefronts per workgroup
+constexpr int kNW = 4;      // wavefronts per workgroup of the streaming kernel
 constexpr int kBK = 128;    // contraction chunk
 constexpr int kLDA = kBK + 8;  // LDS row stride in 16-bit elements (272 bytes)
+// Word 3 of a raw buffer descriptor on gfx9 parts (32-bit data format, no
+// swizzle, no index stride).
+constexpr int kBufferFlags = 0x00020000;
 
+enum Act { kActCodes = 0, kActF16 = 1, kActBf16 = 2 };
 enum Epi { kEpiSwigluFp4 = 0, kEpiSwigluBf16 = 1, kEpiStoreF32 = 2 };
+
+// Load of a value that is the same for the whole wavefront and not written
+// by the running kernel, through the scalar data cache (read-only use).  Its
+// wait uses the scalar counter, so it never drains outstanding vector loads.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* ptr) {
+  return *(const __attribute__((address_space(4))) T*)ptr;
+}
 
 struct KParams {
   int T, topk, I, N, K;
   int n_blocks;
   int list_idx;            // which plan list (tile height)
-  const int32_t* offsets;
+  int64_t a_rows;          // rows of the activation operand (T for GEMM1, P for GEMM2)
   const int32_t* sorted_pair;  // GEMM1: row -> pair; GEMM2: null (row is the A row)
   const int32_t* plan;
-  const uint8_t* a_q;
+  const uint8_t* a_q;      // kActCodes
   const uint8_t* a_sf;
-  const uint16_t* a_bf16;
+  const uint16_t* a_h;     // kActF16 / kActBf16: 16-bit activations [a_rows][K]
   const float* g_a;
   const uint8_t* w_q;      // prepped codes
   const uint8_t* w_sf;     // prepped scales
@@ -67,7 +87,7 @@ struct KParams {
   const float* g2;
   uint8_t* out_q;
   uint8_t* out_sf;
-  uint16_t* out_bf16;
+  uint16_t* out_h;         // GEMM1: bf16 intermediate (W4A16) or optional f16 copy (W4A4)
   float* out_f32;
 };
 
@@ -81,12 +101,19 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
+// Value of an E2M1 magnitude code 0..7: {0, .5, 1, 1.5, 2, 3, 4, 6}.
+__device__ __forceinline__ float e2m1_mag_value(uint32_t m) {
+  const float lo = (float)(m & 1u) * 0.5f;                        // codes 0, 1
+  const float v = __int_as_float((int)(((m >> 1) + 126u) << 23)) * (1.0f + 0.5f * (float)(m & 1u));
+  return m < 2 ? lo : v;                                          // 2^(e-1) * (1 + m/2)
+}
+
 // Epilogue of a wavefront's MT x NTW accumulator tiles (rows row0 + [0, 16 MT),
 // columns n_wave0 + [0, 16 NTW) of the streaming column order).
 template <int EPI, int MT, int NTW>
 __device__ __forceinline__ void epilogue(const KParams& p, f32x4 (&acc)[MT][NTW], int e, int row0,
                                          int nrows, int n_wave0, int lane) {
-  const float alpha = p.g_a ? (*p.g_a) * p.g_w[e] : p.g_w[e];
+  const float alpha = p.g_a ? ld_uniform(p.g_a) * ld_uniform(p.g_w + e) : ld_uniform(p.g_w + e);
   const int ln = lane & 15, lg = lane >> 4;
   if constexpr (EPI == kEpiStoreF32) {
 #pragma unroll
@@ -100,7 +127,7 @@ __device__ __forceinline__ void epilogue(const KParams& p, f32x4 (&acc)[MT][NTW]
             p.out_f32[(int64_t)(row0 + row) * p.N + n_wave0 + 16 * j + ln] = alpha * acc[i][j][r];
         }
   } else {
-    const float g2 = (EPI == kEpiSwigluFp4) ? *p.g2 : 0.0f;
+    const float g2 = (EPI == kEpiSwigluFp4) ? ld_uniform(p.g2) : 0.0f;
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -118,7 +145,8 @@ __device__ __forceinline__ void epilogue(const KParams& p, f32x4 (&acc)[MT][NTW]
           for (int r = 0; r < 4; ++r) {
             const float am = row16_max(fabsf(h[r]));
             const uint32_t sc = e4m3_scale_code(am, g2);
-            const E2M1Bounds bd = e2m1_bounds(e4m3_value(sc), g2);
+            const float sv = e4m3_value(sc);
+            const E2M1Bounds bd = e2m1_bounds(sv, g2);
             const uint32_t code = e2m1_code(h[r], bd, sc == 0);
             const uint32_t other = (uint32_t)dpp_xor1_i((int)code);
             const int row = i * 16 + lg * 4 + r;
@@ -127,6 +155,12 @@ __device__ __forceinline__ void epilogue(const KParams& p, f32x4 (&acc)[MT][NTW]
               if ((ln & 1) == 0)
                 p.out_q[pr * (p.I >> 1) + hb * 8 + (ln >> 1)] = (uint8_t)(code | (other << 4));
               if (ln == 0) p.out_sf[pr * (p.I >> 4) + hb] = (uint8_t)sc;
+              if (p.out_h) {
+                // Exact: six significant bits at most, inside the f16 range.
+                const float dv = e2m1_mag_value(code & 7u) * sv;
+                const _Float16 hv = (_Float16)((code & 8u) ? -dv : dv);
+                p.out_h[pr * p.I + hb * 16 + ln] = __builtin_bit_cast(uint16_t, hv);
+              }
             }
           }
         } else {
@@ -134,48 +168,62 @@ __device__ __forceinline__ void epilogue(const KParams& p, f32x4 (&acc)[MT][NTW]
           for (int r = 0; r < 4; ++r) {
             const int row = i * 16 + lg * 4 + r;
             if (row < nrows)
-              p.out_bf16[(int64_t)(row0 + row) * p.I + hb * 16 + ln] = (uint16_t)f32_to_bf16_bits(h[r]);
+              p.out_h[(int64_t)(row0 + row) * p.I + hb * 16 + ln] = (uint16_t)f32_to_bf16_bits(h[r]);
           }
         }
       }
   }
 }
 
-// Work item of this workgroup: (expert, first row, valid rows, column block).
+// Work item of a workgroup of the LDS kernel: (expert, first row, valid
+// rows, column block).
 struct Tile {
   int e, row0, nrows, nb;
 };
-// Tiles whose work shares data are kept on one XCD (``remap``): the launch
-// order is mapped so that each XCD receives a contiguous range of tiles.
-__device__ __forceinline__ bool decode_tile(const KParams& p, bool remap, Tile& t) {
-  const int ntiles = p.plan[p.list_idx];
+// Tiles whose work shares data are kept on one XCD: the launch order is
+// mapped so that each XCD receives a contiguous range of tiles.
+__device__ __forceinline__ bool decode_tile(const KParams& p, Tile& t) {
+  const int ntiles = ld_uniform(p.plan + p.list_idx);
   const int G = ntiles * p.n_blocks;
   if ((int)blockIdx.x >= G) return false;
-  const int v = remap ? xcd_remap(blockIdx.x, G) : (int)blockIdx.x;
+  const int v = xcd_remap(blockIdx.x, G);
   const int tile = v / p.n_blocks;
   t.nb = v - tile * p.n_blocks;
-  const int* ent = p.plan + p.plan[4 + p.list_idx] + 2 * tile;
-  t.e = ent[0] & 2047;
-  const uint32_t rr = (uint32_t)ent[1];
+  const int* ent = p.plan + ld_uniform(p.plan + 4 + p.list_idx) + 2 * tile;
+  t.e = ld_uniform(ent) & 2047;
+  const uint32_t rr = (uint32_t)ld_uniform(ent + 1);
   t.row0 = (int)(rr & 0xFFFFFFu);
   t.nrows = (int)(rr >> 24);
   return true;
 }
 
-template <bool W4A4, int EPI, int BM, int WN, int NW>
+// Weight fragment of one 16x16x32 step as f16: 8 codes times the block scale
+// of k-steps 0-1 (low half of s2) or 2-3 (high half).
+__device__ __forceinline__ f16x8 weight_f16(uint32_t codes, f16x2 s2, int ks) {
+  return dequant8_f16(codes, ks < 2 ? f16x2_lo(s2) : f16x2_hi(s2));
+}
+
+// ---------------------------------------------------------------------------
+// LDS-staged kernel (tiles of 64 or 128 rows, the prefill regime).  A
+// workgroup takes one tile and BN = NW * WN output columns.  Each wavefront
+// owns WN columns for all BM rows: it streams its weight columns straight from
+// HBM into registers while the BM x 128 activation chunk is staged once per
+// workgroup in LDS (decoded to f16 for codes), double-buffered.
+// ---------------------------------------------------------------------------
+template <int AK, int EPI, int BM, int WN, int NW>
 __global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
   constexpr int MT = BM / 16;
   constexpr int NTW = WN / 16;
   static_assert(NTW % 2 == 0, "scale words cover column tiles in pairs");
   // A staging pieces per chunk: 16-byte pieces of codes (32 elements) for
-  // W4A4, 16-byte pieces of bf16 (8 elements) for W4A16.
-  constexpr int PIECES = W4A4 ? BM * 4 : BM * 16;
+  // kActCodes, 16-byte pieces of 16-bit values (8 elements) otherwise.
+  constexpr int PIECES = AK == kActCodes ? BM * 4 : BM * 16;
   static_assert(PIECES % (NW * kWave) == 0, "staging pieces split evenly over the threads");
   constexpr int PPT = PIECES / (NW * kWave);
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kLDA];
 
   Tile t;
-  if (!decode_tile(p, true, t)) return;
+  if (!decode_tile(p, t)) return;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n_wave0 = (t.nb * NW + wv) * WN;
   const bool wave_on = n_wave0 < p.N;
@@ -190,16 +238,16 @@ __global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
 #pragma unroll
   for (int j = 0; j < PPT; ++j) {
     const int pc = tid + j * NW * kWave;
-    const int r = W4A4 ? (pc >> 2) : (pc >> 4);
-    const int qq = W4A4 ? (pc & 3) : (pc & 15);
+    const int r = AK == kActCodes ? (pc >> 2) : (pc >> 4);
+    const int qq = AK == kActCodes ? (pc & 3) : (pc & 15);
     int src = t.row0 + min(r, t.nrows - 1);
     if (p.sorted_pair) src = pair_token(p.sorted_pair[src], p.T, p.topk);
-    if constexpr (W4A4) {
+    if constexpr (AK == kActCodes) {
       a_src[j] = p.a_q + (int64_t)src * (K >> 1) + qq * 16;
       s_src[j] = p.a_sf + (int64_t)src * (K >> 4) + qq * 2;
       a_dst[j] = r * kLDA + qq * 32;
     } else {
-      a_src[j] = reinterpret_cast<const uint8_t*>(p.a_bf16 + (int64_t)src * K + qq * 8);
+      a_src[j] = reinterpret_cast<const uint8_t*>(p.a_h + (int64_t)src * K + qq * 8);
       s_src[j] = nullptr;
       a_dst[j] = r * kLDA + qq * 8;
     }
@@ -209,7 +257,7 @@ __global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
   auto load_a = [&](int kc) {
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
-      if constexpr (W4A4) {
+      if constexpr (AK == kActCodes) {
         a_reg[j] = *reinterpret_cast<const u32x4*>(a_src[j] + kc * 64);
         a_sreg[j] = *reinterpret_cast<const uint16_t*>(s_src[j] + kc * 8);
       } else {
@@ -221,7 +269,7 @@ __global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
       uint16_t* dst = &As[buf][a_dst[j]];
-      if constexpr (W4A4) {
+      if constexpr (AK == kActCodes) {
         const f16x2 s2 = e4m3x2_to_f16x2(a_sreg[j]);
 #pragma unroll
         for (int w = 0; w < 4; ++w)
@@ -260,7 +308,7 @@ __global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
   auto compute = [&](int buf, const u32x4 (&bq)[NTW], const uint32_t (&bs)[NTW / 2]) {
     if (!wave_on) return;
     const uint16_t* abase = &As[buf][a_lrow * kLDA + a_kq];
-    if constexpr (W4A4) {
+    if constexpr (AK != kActBf16) {
       f16x2 sb2[NTW];
 #pragma unroll
       for (int j = 0; j < NTW; ++j) sb2[j] = e4m3x2_to_f16x2(bs[j >> 1] >> ((j & 1) * 16));
@@ -268,8 +316,7 @@ __global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
       for (int s = 0; s < 4; ++s) {
         f16x8 bf[NTW];
 #pragma unroll
-        for (int j = 0; j < NTW; ++j)
-          bf[j] = dequant8_f16(bq[j][s], s < 2 ? f16x2_lo(sb2[j]) : f16x2_hi(sb2[j]));
+        for (int j = 0; j < NTW; ++j) bf[j] = weight_f16(bq[j][s], sb2[j], s);
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
           const f16x8 af = *reinterpret_cast<const f16x8*>(abase + i * 16 * kLDA + 8 * s);
@@ -338,173 +385,160 @@ __global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
   epilogue<EPI, MT, NTW>(p, acc, t.e, t.row0, t.nrows, n_wave0, lane);
 }
 
-// Main loop for short tiles (16 or 32 rows), the decode regime where the
-// weights are read once and the path is bound by HBM bandwidth.  The tile's
-// activation rows (packed NVFP4 or bf16, all of K) are staged into LDS once,
-// behind a single barrier; after that every wavefront only streams its own
-// weight columns, through a register ring of PF 128-k chunks, so PF chunks of
-// loads are in flight while the matrix instructions consume the oldest one.
-// Activation fragments use the weights' lane layout: lane 16g + m reads the
-// 32 k values [32g, 32g + 32) of row m of a chunk.
-template <bool W4A4, int EPI, int MT, int NTW, int PF>
-__global__ __launch_bounds__(kNW * kWave) void grouped_gemm_direct_kernel(KParams p) {
-  constexpr int BM = MT * 16;
-  extern __shared__ __attribute__((aligned(16))) uint8_t a_lds[];
-  Tile t;
-  // Column blocks of a tile read disjoint weights: no XCD grouping needed.
-  if (!decode_tile(p, false, t)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int n_wave0 = (t.nb * kNW + wv) * (NTW * 16);
-  const bool wave_on = n_wave0 < p.N;
-  const int K = p.K, KC = K / kBK, NT = p.N / 16;
-  const int g = lane >> 4;
+// ---------------------------------------------------------------------------
+// Persistent streaming kernel for short tiles (16 or 32 rows), the decode
+// regime where every weight byte is read once and the time is the weight
+// stream.  Work units are (tile, group of NTW column tiles); wavefront w of
+// W resident ones takes units w, w + W, w + 2W, ... (a fixed, deterministic
+// assignment).  Each wavefront keeps a ring of PF 128-k chunks in flight and
+// the ring does not drain between units: the last round of a unit refills
+// the slots with the first chunks of the wavefront's next unit.  Activation
+// fragments ride in the ring beside the weights, in the weights' lane layout
+// (lane 16g + m holds row m, k in [32g, 32g + 32) of a chunk), so wavefronts
+// share nothing: no LDS, no barriers.
+// ---------------------------------------------------------------------------
+template <int AK, int EPI, int MT, int NTW, int PF>
+__global__ __launch_bounds__(kNW * kWave) void grouped_gemm_stream_kernel(KParams p) {
+  static_assert(NTW % 2 == 0, "scale words cover column tiles in pairs");
+  const int lane = threadIdx.x & 63, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kNW + (threadIdx.x >> 6)));
+  const int W = gridDim.x * kNW;
+  const int K = p.K, KC = K / kBK, NT = p.N / 16, CG = NT / NTW;
+  const int n_units = ld_uniform(p.plan + p.list_idx) * CG;
+  if (wave >= n_units) return;
+  const int* list = p.plan + ld_uniform(p.plan + 4 + p.list_idx);
 
-  const int nt0 = n_wave0 >> 4;
-  const int64_t wbase = ((int64_t)(t.e * NT + nt0) * KC) * kWave + lane;
-  const int64_t sbase = ((int64_t)(t.e * (NT >> 1) + (nt0 >> 1)) * KC) * kWave + lane;
+  // Buffer addressing: a scalar descriptor per operand (per expert for the
+  // weights) plus a 32-bit per-lane offset; every byte range addressed here
+  // is below 2^31 (checked by the launcher).
+  const int64_t wq_expert = (int64_t)NT * KC * 1024;  // code bytes per expert
+  const int64_t ws_expert = (int64_t)(NT >> 1) * KC * 256;
+  const int w_lane = lane * 16, s_lane = lane * 4;
+  const __amdgpu_buffer_rsrc_t a_rsrc = AK == kActCodes
+      ? __builtin_amdgcn_make_buffer_rsrc((void*)p.a_q, (short)0, 0x7FFFFFFF, kBufferFlags)
+      : __builtin_amdgcn_make_buffer_rsrc((void*)p.a_h, (short)0, 0x7FFFFFFF, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t as_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(AK == kActCodes ? p.a_sf : p.w_sf), (short)0, 0x7FFFFFFF, kBufferFlags);
+
+  // Work unit: expert, rows, first column, and the per-lane activation row
+  // offsets (rows past the tile end repeat its last valid row; their results
+  // are never stored).
+  struct Unit {
+    int e, row0, nrows, n0, nt0;
+    int a_off[MT], s_off[MT];
+  };
+  auto unit = [&](int u) {
+    Unit U;
+    const int tile = u / CG, cg = u - tile * CG;
+    U.e = ld_uniform(list + 2 * tile) & 2047;
+    const uint32_t rr = (uint32_t)ld_uniform(list + 2 * tile + 1);
+    U.row0 = (int)(rr & 0xFFFFFFu);
+    U.nrows = (int)(rr >> 24);
+    U.nt0 = cg * NTW;
+    U.n0 = U.nt0 * 16;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      int r = U.row0 + min(i * 16 + (lane & 15), U.nrows - 1);
+      if (p.sorted_pair) {
+        // The 16 pair indices of this m-tile through scalar loads, then each
+        // lane picks its own (a vector gather here would be waited for with
+        // the in-order vector counter, i.e. behind the whole ring).
+        int f = 0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int fq = ld_uniform(p.sorted_pair + U.row0 + min(i * 16 + q, U.nrows - 1));
+          f = (lane & 15) == q ? fq : f;
+        }
+        r = pair_token(f, p.T, p.topk);
+      }
+      U.a_off[i] = AK == kActCodes ? r * (K >> 1) + g * 16 : r * K * 2 + g * 64;
+      U.s_off[i] = r * (K >> 4) + g * 2;
+    }
+    return U;
+  };
+
   u32x4 bq[PF][NTW];
   uint32_t bs[PF][NTW / 2];
-  // bf16 activation fragments ride in the ring too (W4A16: a bf16 tile is 4x
-  // the packed size, too large to stage whole in LDS without costing
-  // occupancy).  Rows past the tile end read a valid row; never stored.
-  constexpr int AR = W4A4 ? 1 : MT;
-  u32x4 ab[PF][AR][W4A4 ? 1 : 4];
-  int64_t arow_g[AR];
+  constexpr int AW = AK == kActCodes ? 1 : 4;  // 16-byte activation words per m-tile and chunk
+  u32x4 aq[PF][MT][AW];
+  uint32_t as[PF][MT];
+  // Refill of ring slot ``slot`` with chunk kc of unit A (sel false) or B
+  // (sel true).  The choice is made with selects, not a branch: the loads
+  // must be unconditional for the hardware load counter to be tracked
+  // exactly (a branch makes the compiler wait for the whole ring).
+  auto load = [&](const Unit& A, const Unit& B, bool sel, int kc, int slot) {
+    const int e = sel ? B.e : A.e, nt0 = sel ? B.nt0 : A.nt0;
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.w_q + e * wq_expert), (short)0, 0x7FFFFFFF, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.w_sf + e * ws_expert), (short)0, 0x7FFFFFFF, kBufferFlags);
 #pragma unroll
-  for (int i = 0; i < AR; ++i) {
-    int src = t.row0 + min(i * 16 + (lane & 15), t.nrows - 1);
-    if (!W4A4 && p.sorted_pair) src = pair_token(p.sorted_pair[src], p.T, p.topk);
-    arow_g[i] = src;
-  }
-  auto load = [&](int kc, int u) {
+    for (int j = 0; j < NTW; ++j)
+      bq[slot][j] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, w_lane, ((nt0 + j) * KC + kc) * 1024, 0));
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const int64_t unit = wbase + ((int64_t)j * KC + kc) * kWave;
-      bq[u][j] = *reinterpret_cast<const u32x4*>(p.w_q + unit * 16);
-    }
+    for (int j = 0; j < NTW / 2; ++j)
+      bs[slot][j] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_lane, (((nt0 >> 1) + j) * KC + kc) * 256, 0);
 #pragma unroll
-    for (int j = 0; j < NTW / 2; ++j) {
-      const int64_t unit = sbase + ((int64_t)j * KC + kc) * kWave;
-      bs[u][j] = *reinterpret_cast<const uint32_t*>(p.w_sf + unit * 4);
-    }
-    if constexpr (!W4A4) {
+    for (int i = 0; i < MT; ++i) {
+      const int ao = sel ? B.a_off[i] : A.a_off[i];
+      if constexpr (AK == kActCodes) {
+        const int so = sel ? B.s_off[i] : A.s_off[i];
+        aq[slot][i][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, ao, kc * 64, 0));
+        as[slot][i] = __builtin_amdgcn_raw_buffer_load_b16(as_rsrc, so, kc * 8, 0);
+      } else {
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4)
-          ab[u][i][s4] = *reinterpret_cast<const u32x4*>(p.a_bf16 + arow_g[i] * K + kc * kBK + g * 32 + s4 * 8);
+        for (int w = 0; w < 4; ++w)
+          aq[slot][i][w] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, ao + w * 16, kc * 256, 0));
+      }
     }
   };
-  // The weight stream does not depend on the activations: start it first,
-  // in slot order (the compiler would otherwise cluster the loads by type,
-  // and every later wait would have to drain the ring).
-  if (wave_on) {
-#pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      load(u, u);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
-  // ---- W4A4: stage the tile's activation rows (rows past the tile end
-  // repeat the last valid row; their results are never stored), packed, or
-  // dequantised to f16 once for all wavefronts (AF16).  Row stride is padded
-  // by 16 bytes so the 16 rows read by one fragment load spread over the
-  // banks.
-  constexpr bool AF16 = W4A4 && NVFP4_DIRECT_AF16;
-  const int row_bytes = K >> 1;
-  const int stride = AF16 ? K * 2 + 16 : row_bytes + 16;
-  const int sf_bytes = K >> 4;
-  uint8_t* a_sf_lds = a_lds + BM * stride;
-  if constexpr (AF16) {
-    const int pieces = K >> 5;  // 32-element pieces per row
-    for (int pc = tid; pc < BM * pieces; pc += kNW * kWave) {
-      const int r = pc / pieces, c = pc - r * pieces;
-      int src = t.row0 + min(r, t.nrows - 1);
-      if (p.sorted_pair) src = pair_token(p.sorted_pair[src], p.T, p.topk);
-      const u32x4 cw = *reinterpret_cast<const u32x4*>(p.a_q + (int64_t)src * row_bytes + c * 16);
-      const f16x2 s2 = e4m3x2_to_f16x2(
-          *reinterpret_cast<const uint16_t*>(p.a_sf + (int64_t)src * sf_bytes + c * 2));
-      uint8_t* dst = a_lds + r * stride + c * 64;
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        *reinterpret_cast<f16x8*>(dst + 16 * w) = dequant8_f16(cw[w], w < 2 ? f16x2_lo(s2) : f16x2_hi(s2));
-    }
-    __syncthreads();
-  } else if constexpr (W4A4) {
-    const int pieces = row_bytes >> 4;  // 16-byte pieces per row
-    for (int pc = tid; pc < BM * pieces; pc += kNW * kWave) {
-      const int r = pc / pieces, c = pc - r * pieces;
-      int src = t.row0 + min(r, t.nrows - 1);
-      if (p.sorted_pair) src = pair_token(p.sorted_pair[src], p.T, p.topk);
-      *reinterpret_cast<u32x4*>(a_lds + r * stride + c * 16) =
-          *reinterpret_cast<const u32x4*>(p.a_q + (int64_t)src * row_bytes + c * 16);
-    }
-    const int spieces = sf_bytes >> 1;  // 2-byte pieces per row
-    for (int pc = tid; pc < BM * spieces; pc += kNW * kWave) {
-      const int r = pc / spieces, c = pc - r * spieces;
-      int src = t.row0 + min(r, t.nrows - 1);
-      if (p.sorted_pair) src = pair_token(p.sorted_pair[src], p.T, p.topk);
-      *reinterpret_cast<uint16_t*>(a_sf_lds + r * sf_bytes + c * 2) =
-          *reinterpret_cast<const uint16_t*>(p.a_sf + (int64_t)src * sf_bytes + c * 2);
-    }
-    __syncthreads();
-  }
-  if (!wave_on) return;  // no barriers below
 
   f32x4 acc[MT][NTW];
+  auto compute = [&](int slot) {
+    if constexpr (AK != kActBf16) {
+      f16x2 sa2[MT], sb2[NTW];
+      if constexpr (AK == kActCodes) {
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int arow = lane & 15;
-  auto compute = [&](int kc, int u) {
-    // Packed activation fragments of this chunk for every m-tile (W4A4), and
-    // the f16 block scales of this chunk ({k-steps 0-1, k-steps 2-3}).
-    u32x4 aq[MT];
-    f16x2 sa2[MT], sb2[NTW];
-    if constexpr (W4A4) {
-#pragma unroll
-      for (int i = 0; i < MT && !AF16; ++i) {
-        aq[i] = *reinterpret_cast<const u32x4*>(a_lds + (i * 16 + arow) * stride + kc * 64 + g * 16);
-        sa2[i] = e4m3x2_to_f16x2(*reinterpret_cast<const uint16_t*>(
-            a_sf_lds + (i * 16 + arow) * sf_bytes + kc * 8 + g * 2));
+        for (int i = 0; i < MT; ++i) sa2[i] = e4m3x2_to_f16x2(as[slot][i]);
       }
 #pragma unroll
-      for (int j = 0; j < NTW; ++j) sb2[j] = e4m3x2_to_f16x2(bs[u][j >> 1] >> ((j & 1) * 16));
-    }
+      for (int j = 0; j < NTW; ++j) sb2[j] = e4m3x2_to_f16x2(bs[slot][j >> 1] >> ((j & 1) * 16));
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int sh = (s < 2 ? 0 : 8);
-      if constexpr (W4A4) {
-        f16x8 bf[NTW], af[MT];
-#pragma unroll
-        for (int j = 0; j < NTW; ++j)
-          bf[j] = dequant8_f16(bq[u][j][s], s < 2 ? f16x2_lo(sb2[j]) : f16x2_hi(sb2[j]));
+      for (int ks = 0; ks < 4; ++ks) {
+        f16x8 af[MT], bf[NTW];
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
-          if constexpr (AF16)
-            af[i] = *reinterpret_cast<const f16x8*>(a_lds + (i * 16 + arow) * stride +
-                                                     (kc * kBK + g * 32 + s * 8) * 2);
+          if constexpr (AK == kActCodes)
+            af[i] = dequant8_f16(aq[slot][i][0][ks], ks < 2 ? f16x2_lo(sa2[i]) : f16x2_hi(sa2[i]));
           else
-            af[i] = dequant8_f16(aq[i][s], s < 2 ? f16x2_lo(sa2[i]) : f16x2_hi(sa2[i]));
+            af[i] = __builtin_bit_cast(f16x8, aq[slot][i][ks]);
         }
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) bf[j] = weight_f16(bq[slot][j][ks], sb2[j], ks);
 #pragma unroll
         for (int i = 0; i < MT; ++i)
 #pragma unroll
           for (int j = 0; j < NTW; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-      } else {
+      }
+    } else {
+      float sb[NTW][2];
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const uint32_t w = bs[slot][j >> 1] >> ((j & 1) * 16);
+        sb[j][0] = e4m3_value(w & 0xFFu);
+        sb[j][1] = e4m3_value((w >> 8) & 0xFFu);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
         bf16x8 bf[NTW];
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-          const uint32_t sb = (bs[u][j >> 1] >> ((j & 1) * 16 + sh)) & 0xFFu;
-          bf[j] = dequant8_bf16(bq[u][j][s], e4m3_value(sb));
-        }
+        for (int j = 0; j < NTW; ++j) bf[j] = dequant8_bf16(bq[slot][j][ks], sb[j][ks >> 1]);
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
-          const bf16x8 af = __builtin_bit_cast(bf16x8, ab[u][i][s]);
+          const bf16x8 af = __builtin_bit_cast(bf16x8, aq[slot][i][ks]);
 #pragma unroll
           for (int j = 0; j < NTW; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0, 0, 0);
@@ -513,35 +547,42 @@ __global__ __launch_bounds__(kNW * kWave) void grouped_gemm_direct_kernel(KParam
     }
   };
 
-  // PF divides KC (chosen by the launcher): the prologue above, a steady
-  // state with unconditional loads, then the drain.  The scheduling fences
-  // pin each refill right behind the compute that frees its slot (left
-  // alone, the scheduler sinks all refills to the end of the loop body and
-  // the ring runs empty).
-  for (int kc0 = PF; kc0 < KC; kc0 += PF) {
+  int u = wave;
+  Unit cur = unit(u);
+  // The unit after the last one is a copy of the current one: its loads
+  // are harmless re-reads, which keeps every load unconditional.
+  bool more = u + W < n_units;
+  Unit nxt = unit(more ? u + W : u);
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      compute(kc0 - PF + u, u);
-      __builtin_amdgcn_sched_barrier(0);
-      load(kc0 + u, u);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  for (int s = 0; s < PF; ++s) {
+    load(cur, cur, false, s, s);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  while (true) {
 #pragma unroll
-  for (int u = 0; u < PF; ++u) compute(KC - PF + u, u);
-  epilogue<EPI, MT, NTW>(p, acc, t.e, t.row0, t.nrows, n_wave0, lane);
-}
-
-// Largest activation tile the short-tile kernel stages (larger ones, e.g. bf16
-// rows with a long K, take the chunked LDS kernel instead).
-constexpr size_t kDirectLdsMax = 96 * 1024;
-
-// LDS bytes of the short-tile kernel: padded packed activation rows + scales
-// (W4A4 only; the bf16 variant keeps its activations in registers).
-size_t direct_lds_bytes(bool w4a4, int BM, int K) {
-  if (!w4a4) return 0;
-  if (NVFP4_DIRECT_AF16) return (size_t)BM * (K * 2 + 16) + (size_t)BM * (K / 16);
-  return (size_t)BM * (K / 2 + 16) + (size_t)BM * (K / 16);
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kc0 = 0; kc0 < KC; kc0 += PF) {
+      const bool last_round = kc0 + PF >= KC;
+#pragma unroll
+      for (int s = 0; s < PF; ++s) {
+        compute(s);
+        __builtin_amdgcn_sched_barrier(0);
+        // PF divides KC, so the next unit's chunk index is s.
+        load(cur, nxt, last_round, last_round ? s : kc0 + PF + s, s);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    epilogue<EPI, MT, NTW>(p, acc, cur.e, cur.row0, cur.nrows, cur.n0, lane);
+    if (!more) break;
+    u += W;
+    cur = nxt;
+    more = u + W < n_units;
+    nxt = unit(more ? u + W : u);
+  }
+  // Let the final (unused) refills land before the wave ends.
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
 // out[t] = sum_j w[t][j] * d[inv_pos[t*k + j]] (+ shared row), FP32, j ascending.
@@ -551,29 +592,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const float* __restrict__ topk_w, int T,
                                                       int topk, int shared, int H, void* out) {
   const int t = blockIdx.x;
-  {
-    const int c = blockIdx.y * 1024 + threadIdx.x * 4;
-    if (c >= H) return;
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < topk; ++j) {
-      const int pos = inv_pos[(int64_t)t * topk + j];
-      if (pos >= 0) {
-        const float w = topk_w[(int64_t)t * topk + j];
-        const f32x4 x = *reinterpret_cast<const f32x4*>(d + (int64_t)pos * H + c);
-        a += w * x;
-      }
+  const int c = blockIdx.y * 1024 + threadIdx.x * 4;
+  if (c >= H) return;
+  f32x4 a = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < topk; ++j) {
+    const int pos = inv_pos[(int64_t)t * topk + j];
+    if (pos >= 0) {
+      const float w = topk_w[(int64_t)t * topk + j];
+      const f32x4 x = *reinterpret_cast<const f32x4*>(d + (int64_t)pos * H + c);
+      a += w * x;
     }
-    if (shared) {
-      const int pos = inv_pos[(int64_t)T * topk + t];
-      if (pos >= 0) a += *reinterpret_cast<const f32x4*>(d + (int64_t)pos * H + c);
-    }
-    if constexpr (BF16) {
-      uint32_t lo = f32_to_bf16_bits(a[0]) | (f32_to_bf16_bits(a[1]) << 16);
-      uint32_t hi = f32_to_bf16_bits(a[2]) | (f32_to_bf16_bits(a[3]) << 16);
-      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + (int64_t)t * H + c) = u32x2{lo, hi};
-    } else {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + (int64_t)t * H + c) = a;
-    }
+  }
+  if (shared) {
+    const int pos = inv_pos[(int64_t)T * topk + t];
+    if (pos >= 0) a += *reinterpret_cast<const f32x4*>(d + (int64_t)pos * H + c);
+  }
+  if constexpr (BF16) {
+    uint32_t lo = f32_to_bf16_bits(a[0]) | (f32_to_bf16_bits(a[1]) << 16);
+    uint32_t hi = f32_to_bf16_bits(a[2]) | (f32_to_bf16_bits(a[3]) << 16);
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + (int64_t)t * H + c) = u32x2{lo, hi};
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + (int64_t)t * H + c) = a;
   }
 }
 
@@ -586,65 +625,71 @@ int pick_list(int64_t P, int slots) {
   return 3;
 }
 
-template <bool W4A4, int EPI, int BM, int WN>
-hipError_t launch_one(KParams kp, int list_len, hipStream_t s) {
+template <int AK, int EPI, int BM, int WN>
+hipError_t launch_lds(KParams kp, int list_len, hipStream_t s) {
   constexpr int NW = NVFP4_BIG_NW;
   kp.n_blocks = (kp.N + NW * WN - 1) / (NW * WN);
   const int64_t G = (int64_t)list_len * kp.n_blocks;
-  const int64_t grid = (G + 7) / 8 * 8;
-  grouped_gemm_kernel<W4A4, EPI, BM, WN, NW><<<(unsigned)grid, NW * kWave, 0, s>>>(kp);
+  const int64_t grid = std::max<int64_t>(8, (G + 7) / 8 * 8);
+  grouped_gemm_kernel<AK, EPI, BM, WN, NW><<<(unsigned)grid, NW * kWave, 0, s>>>(kp);
   return hipGetLastError();
 }
 
-template <bool W4A4, int EPI, int MT, int NTW, int PF>
-hipError_t launch_direct(const KParams& kp, int list_len, hipStream_t s) {
-  const int64_t G = (int64_t)list_len * kp.n_blocks;
-  const int64_t grid = (G + 7) / 8 * 8;
-  const size_t lds = direct_lds_bytes(W4A4, MT * 16, kp.K);
-  auto kern = grouped_gemm_direct_kernel<W4A4, EPI, MT, NTW, PF>;
-  static bool attr_set = false;  // raise the dynamic LDS limit once per instantiation
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)kDirectLdsMax);
+// Persistent launch: as many workgroups as fit on the device at once (the
+// occupancy of this instantiation times the CU count), capped by the work.
+template <int AK, int EPI, int MT, int NTW, int PF>
+hipError_t launch_stream(const KParams& kp, int list_len, hipStream_t s) {
+  auto kern = grouped_gemm_stream_kernel<AK, EPI, MT, NTW, PF>;
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int nb = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(kern),
+                                                                kNW * kWave, 0);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    per_cu = nb > 0 ? nb : 1;
   }
-  kern<<<(unsigned)grid, kNW * kWave, lds, s>>>(kp);
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int64_t units = (int64_t)list_len * ((kp.N / 16) / NTW);
+  const int64_t need = (units + kNW - 1) / kNW;
+  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((int64_t)per_cu * cus, need));
+  kern<<<(unsigned)grid, kNW * kWave, 0, s>>>(kp);
   return hipGetLastError();
 }
 
-// Prefetch depth: the largest of 8, 6, 4, 3, 2, 1 chunks that divides the
-// chunk count (fewer for bf16 activations, whose fragments are 4x larger).
-template <bool W4A4, int EPI, int MT, int NTW>
-hipError_t launch_direct_pf(const KParams& kp, int len, hipStream_t s) {
+// Ring depth of the streaming kernel: the largest allowed depth dividing the
+// chunk count (16-bit activation fragments are 4x larger than codes).
+template <int AK, int EPI, int MT, int NTW>
+hipError_t launch_stream_pf(const KParams& kp, int len, hipStream_t s) {
   const int KC = kp.K / kBK;
-  if (NVFP4_DIRECT_PFMAX >= 8 && W4A4 && KC % 8 == 0)
-    return launch_direct<W4A4, EPI, MT, NTW, 8>(kp, len, s);
-  if (NVFP4_DIRECT_PFMAX >= 6 && W4A4 && KC % 6 == 0)
-    return launch_direct<W4A4, EPI, MT, NTW, 6>(kp, len, s);
-  if (KC % 4 == 0) return launch_direct<W4A4, EPI, MT, NTW, 4>(kp, len, s);
-  if (KC % 3 == 0) return launch_direct<W4A4, EPI, MT, NTW, 3>(kp, len, s);
-  if (KC % 2 == 0) return launch_direct<W4A4, EPI, MT, NTW, 2>(kp, len, s);
-  return launch_direct<W4A4, EPI, MT, NTW, 1>(kp, len, s);
+  if constexpr (NVFP4_STREAM_PFMAX >= 8 && AK == kActCodes) {
+    if (KC % 8 == 0) return launch_stream<AK, EPI, MT, NTW, 8>(kp, len, s);
+  }
+  if constexpr (NVFP4_STREAM_PFMAX >= 4) {
+    if (KC % 4 == 0) return launch_stream<AK, EPI, MT, NTW, 4>(kp, len, s);
+  }
+  if (KC % 3 == 0) return launch_stream<AK, EPI, MT, NTW, 3>(kp, len, s);
+  if (KC % 2 == 0) return launch_stream<AK, EPI, MT, NTW, 2>(kp, len, s);
+  return launch_stream<AK, EPI, MT, NTW, 1>(kp, len, s);
 }
 
-template <bool W4A4, int EPI>
+template <int AK, int EPI>
 hipError_t launch_gemm(KParams kp, const AlignShape& al, hipStream_t s) {
-  const int li = min(pick_list(al.P, al.slots), NVFP4_LIST_MAX);
+  int li = min(pick_list(al.P, al.slots), NVFP4_LIST_MAX);
+  // The streaming kernel addresses with 32-bit buffer offsets.
+  const int64_t a_row_bytes = AK == kActCodes ? kp.K / 2 : 2 * (int64_t)kp.K;
+  const bool offsets_fit = kp.a_rows * a_row_bytes < (int64_t(1) << 31) &&
+                           (int64_t)kp.N * kp.K / 2 < (int64_t(1) << 31);
+  if (li <= 1 && !offsets_fit) li = 2;
   kp.list_idx = li;
-  const int wn = li <= 1 ? 16 * NVFP4_DIRECT_NTW : 64;
-  kp.n_blocks = (kp.N + kNW * wn - 1) / (kNW * wn);
   const int len = (int)al.list_len[li];
-  if (li <= 1 && direct_lds_bytes(W4A4, li == 0 ? 16 : 32, kp.K) > kDirectLdsMax) {
-    kp.list_idx = 2;
-    return launch_one<W4A4, EPI, 64, NVFP4_BIG_WN>(kp, (int)al.list_len[2], s);
-  }
   switch (li) {
-    case 0: return launch_direct_pf<W4A4, EPI, 1, NVFP4_DIRECT_NTW>(kp, len, s);
-    case 1: return launch_direct_pf<W4A4, EPI, 2, NVFP4_DIRECT_NTW>(kp, len, s);
-    case 2: return launch_one<W4A4, EPI, 64, NVFP4_BIG_WN>(kp, len, s);
-    default: return launch_one<W4A4, EPI, 128, NVFP4_BIG_WN>(kp, len, s);
+    case 0: return launch_stream_pf<AK, EPI, 1, NVFP4_STREAM_NTW>(kp, len, s);
+    case 1: return launch_stream_pf<AK, EPI, 2, NVFP4_STREAM_NTW>(kp, len, s);
+    case 2: return launch_lds<AK, EPI, 64, NVFP4_BIG_WN>(kp, len, s);
+    default: return launch_lds<AK, EPI, 128, NVFP4_BIG_WN>(kp, len, s);
   }
 }
 
@@ -653,7 +698,6 @@ KParams base_params(const GemmArgs& a) {
   k.T = a.T;
   k.topk = a.topk;
   k.I = a.I;
-  k.offsets = a.offsets;
   k.plan = a.plan;
   k.g_w = a.g_w;
   return k;
@@ -667,20 +711,24 @@ hipError_t launch_gemm1(const GemmArgs& a, bool w4a4, hipStream_t s) {
   k.N = 2 * a.I;
   k.K = a.H;
   k.sorted_pair = a.sorted_pair;
+  k.a_rows = a.T;
   k.w_q = a.w_prep;
   k.w_sf = a.w_prep + (size_t)al.slots * k.N * (k.K / 2);
   if (w4a4) {
     k.a_q = a.a_q;
     k.a_sf = a.a_sf;
+    k.a_h = a.a_h;
     k.g_a = a.g_a;
     k.g2 = a.g2;
     k.out_q = a.out_q;
     k.out_sf = a.out_sf;
-    return launch_gemm<true, kEpiSwigluFp4>(k, al, s);
+    k.out_h = a.out_h;
+    if (a.a_h) return launch_gemm<kActF16, kEpiSwigluFp4>(k, al, s);
+    return launch_gemm<kActCodes, kEpiSwigluFp4>(k, al, s);
   }
-  k.a_bf16 = a.a_bf16;
-  k.out_bf16 = a.out_bf16;
-  return launch_gemm<false, kEpiSwigluBf16>(k, al, s);
+  k.a_h = a.a_h;
+  k.out_h = a.out_h;
+  return launch_gemm<kActBf16, kEpiSwigluBf16>(k, al, s);
 }
 
 hipError_t launch_gemm2_combine(const GemmArgs& a, bool w4a4, hipStream_t s) {
@@ -689,6 +737,7 @@ hipError_t launch_gemm2_combine(const GemmArgs& a, bool w4a4, hipStream_t s) {
   k.N = a.H;
   k.K = a.I;
   k.sorted_pair = nullptr;
+  k.a_rows = a.P;
   k.w_q = a.w_prep;
   k.w_sf = a.w_prep + (size_t)al.slots * k.N * (k.K / 2);
   k.out_f32 = a.d_ws;
@@ -696,11 +745,13 @@ hipError_t launch_gemm2_combine(const GemmArgs& a, bool w4a4, hipStream_t s) {
   if (w4a4) {
     k.a_q = a.a_q;
     k.a_sf = a.a_sf;
+    k.a_h = a.a_h;
     k.g_a = a.g_a;
-    e = launch_gemm<true, kEpiStoreF32>(k, al, s);
+    e = a.a_h ? launch_gemm<kActF16, kEpiStoreF32>(k, al, s)
+              : launch_gemm<kActCodes, kEpiStoreF32>(k, al, s);
   } else {
-    k.a_bf16 = a.a_bf16;
-    e = launch_gemm<false, kEpiStoreF32>(k, al, s);
+    k.a_h = a.a_h;
+    e = launch_gemm<kActBf16, kEpiStoreF32>(k, al, s);
   }
   if (e != hipSuccess) return e;
   if (a.T == 0) return hipSuccess;

@@ -20,7 +20,7 @@ hipError_t launch_global_scale(const void* x, int dtype, int64_t batches, int64_
                                void* ws, hipStream_t s);
 hipError_t launch_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx,
                            const float* g, int64_t rows_per_g, uint8_t* q, uint8_t* sf,
-                           hipStream_t s);
+                           uint16_t* x_deq, hipStream_t s);
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                              hipStream_t s);
@@ -43,7 +43,7 @@ hipError_t launch_align(const AlignShape& a, const int32_t* topk_ids, int32_t* o
 
 // Weight streaming layout.  For an expert matrix [N][K] (N output columns,
 // K contraction): codes [N/16][K/128][64 lanes][16 B] followed (after all
-// experts' codes) by scales [N/16][K/128][64 lanes][2 B].
+// experts' codes) by scales [N/32][K/128][64 lanes][2 tiles][2 B].
 size_t prep_bytes(int64_t slots, int64_t N, int64_t K);
 hipError_t launch_prep(int64_t slots, int64_t N, int64_t K, int interleave_I, const uint8_t* q,
                        const uint8_t* sf, uint8_t* prep, hipStream_t s);
@@ -61,7 +61,7 @@ struct GemmArgs {
   // operands
   const uint8_t* a_q;
   const uint8_t* a_sf;
-  const uint16_t* a_bf16;
+  const uint16_t* a_h;  // bf16 activations (W4A16) or the f16 dequantised copy (W4A4, optional)
   const float* g_a;     // activation global scale (W4A4) or null
   const uint8_t* w_prep;
   const float* g_w;
@@ -69,7 +69,7 @@ struct GemmArgs {
   const float* g2;
   uint8_t* out_q;
   uint8_t* out_sf;
-  uint16_t* out_bf16;
+  uint16_t* out_h;      // bf16 intermediate (W4A16) or its optional f16 copy (W4A4)
   // GEMM2 outputs
   float* d_ws;
   void* out;

@@ -56,8 +56,10 @@ def global_scale(x: torch.Tensor, batches: int = 1, out: Optional[torch.Tensor] 
 
 
 def quantize(x: torch.Tensor, g: torch.Tensor, rows_per_g: Optional[int] = None,
-             q: Optional[torch.Tensor] = None, sf: Optional[torch.Tensor] = None):
-    """NVFP4-encode the rows of ``x`` [rows, K]: (codes [rows, K/2], scales [rows, K/16])."""
+             q: Optional[torch.Tensor] = None, sf: Optional[torch.Tensor] = None,
+             deq: Optional[torch.Tensor] = None):
+    """NVFP4-encode the rows of ``x`` [rows, K]: (codes [rows, K/2], scales [rows, K/16]).
+    ``deq`` (float16 [rows, K]) optionally receives the exact decoded values."""
     _need_cuda(x, g)
     K = x.shape[-1]
     x2 = x.reshape(-1, K)
@@ -69,7 +71,7 @@ def quantize(x: torch.Tensor, g: torch.Tensor, rows_per_g: Optional[int] = None,
     if sf is None:
         sf = torch.empty(rows, K // 16, dtype=torch.uint8, device=x.device)
     call("nvfp4_quantize", _p(x2), _dtype_code(x2), rows, K, x2.stride(0), _p(g),
-         rows if rows_per_g is None else rows_per_g, _p(q), _p(sf), _stream())
+         rows if rows_per_g is None else rows_per_g, _p(q), _p(sf), _p(deq), _stream())
     return q, sf
 
 
@@ -162,14 +164,18 @@ def quantize_expert_weights(d: Dims, w13: torch.Tensor, w2: torch.Tensor,
 
 
 # ---------------------------------------------------------------- GEMMs
-def gemm1_w4a4(d: Dims, a1_q, a1_sf, g1, al: Alignment, w: ExpertWeights, g2, a2_q=None, a2_sf=None):
+def gemm1_w4a4(d: Dims, a1_q, a1_sf, g1, al: Alignment, w: ExpertWeights, g2, a2_q=None, a2_sf=None,
+               a1_deq=None, a2_deq=None):
+    """GEMM1 + SwiGLU + requantisation.  ``a1_deq`` (the decoded copy from
+    ``quantize``) is read instead of the codes when given; ``a2_deq``
+    optionally receives the decoded copy of a2."""
     P = d.T * d.topk + d.shared * d.T
-    dev = a1_q.device
+    dev = g1.device
     a2_q = a2_q if a2_q is not None else torch.empty(max(P, 1), d.I // 2, dtype=torch.uint8, device=dev)
     a2_sf = a2_sf if a2_sf is not None else torch.empty(max(P, 1), d.I // 16, dtype=torch.uint8, device=dev)
-    call("grouped_gemm1_swiglu", ctypes.byref(d), _p(a1_q), _p(a1_sf), _p(g1), _p(al.sorted_pair),
-         _p(al.offsets), _p(al.plan), _p(w.prep13), _p(w.g13), _p(g2), _p(a2_q), _p(a2_sf),
-         _stream())
+    call("grouped_gemm1_swiglu", ctypes.byref(d), _p(a1_q), _p(a1_sf), _p(a1_deq), _p(g1),
+         _p(al.sorted_pair), _p(al.offsets), _p(al.plan), _p(w.prep13), _p(w.g13), _p(g2),
+         _p(a2_q), _p(a2_sf), _p(a2_deq), _stream())
     return a2_q, a2_sf
 
 
@@ -187,12 +193,12 @@ def gemm_workspace(d: Dims, device) -> torch.Tensor:
 
 
 def gemm2_w4a4(d: Dims, a2_q, a2_sf, g2, al: Alignment, topk_w, w: ExpertWeights,
-               out_dtype=torch.bfloat16, out=None, ws=None):
-    dev = a2_q.device
+               out_dtype=torch.bfloat16, out=None, ws=None, a2_deq=None):
+    dev = g2.device
     out = out if out is not None else torch.empty(d.T, d.H, dtype=out_dtype, device=dev)
     ws = ws if ws is not None else gemm_workspace(d, dev)
-    call("grouped_gemm2_combine", ctypes.byref(d), _p(a2_q), _p(a2_sf), _p(g2), _p(al.offsets),
-         _p(al.inv_pos), _p(al.plan), _p(topk_w), _p(w.prep2), _p(w.g2), _p(out),
+    call("grouped_gemm2_combine", ctypes.byref(d), _p(a2_q), _p(a2_sf), _p(a2_deq), _p(g2),
+         _p(al.offsets), _p(al.inv_pos), _p(al.plan), _p(topk_w), _p(w.prep2), _p(w.g2), _p(out),
          _dtype_code(out), _p(ws), ws.numel() * 4, _stream())
     return out
 
@@ -213,7 +219,12 @@ class MoELayer:
     """One NVFP4 expert layer with all intermediates preallocated, so that a
     call launches kernels only (and can be captured in a HIP graph)."""
 
-    def __init__(self, d: Dims, weights: ExpertWeights, g2: torch.Tensor, device="cuda"):
+    def __init__(self, d: Dims, weights: ExpertWeights, g2: torch.Tensor, device="cuda",
+                 decoded_copies: bool = False):
+        """``decoded_copies``: W4A4 keeps exact f16 copies of a1 and a2 next to
+        their codes and the GEMMs read those instead of decoding the codes.
+        Off by default: on MI355X the 4x larger activation reads cost more
+        than the decoding they save at the measured shapes."""
         self.d = d
         self.w = weights
         self.g2 = g2
@@ -231,15 +242,30 @@ class MoELayer:
         self.a2_q = torch.empty(max(P, 1), d.I // 2, dtype=torch.uint8, device=dev)
         self.a2_sf = torch.empty(max(P, 1), d.I // 16, dtype=torch.uint8, device=dev)
         self.a2_bf16 = torch.empty(max(P, 1), d.I, dtype=torch.bfloat16, device=dev)
+        self.a1_deq = self.a2_deq = None
+        if decoded_copies:
+            self.a1_deq = torch.empty(max(d.T, 1), d.H, dtype=torch.float16, device=dev)
+            self.a2_deq = torch.empty(max(P, 1), d.I, dtype=torch.float16, device=dev)
         self.ws = gemm_workspace(d, dev)
+
+    def _gemm1_w4a4(self, w, s):
+        d = self.d
+        call("grouped_gemm1_swiglu", ctypes.byref(d), _p(self.a1_q), _p(self.a1_sf), _p(self.a1_deq),
+             _p(self.g1), _p(self.al.sorted_pair), _p(self.al.offsets), _p(self.al.plan),
+             _p(w.prep13), _p(w.g13), _p(self.g2), _p(self.a2_q), _p(self.a2_sf), _p(self.a2_deq), s)
+
+    def _gemm2_w4a4(self, w, tw, out, s):
+        d = self.d
+        call("grouped_gemm2_combine", ctypes.byref(d), _p(self.a2_q), _p(self.a2_sf), _p(self.a2_deq),
+             _p(self.g2), _p(self.al.offsets), _p(self.al.inv_pos), _p(self.al.plan),
+             _p(tw), _p(w.prep2), _p(w.g2), _p(out), _dtype_code(out), _p(self.ws),
+             self.ws.numel() * 4, s)
 
     def gemm1(self, variant: str, weights: Optional[ExpertWeights] = None, x=None):
         """GEMM1 alone on the layer's current buffers (for kernel timing)."""
         d, w, s = self.d, weights or self.w, _stream()
         if variant == "w4a4":
-            call("grouped_gemm1_swiglu", ctypes.byref(d), _p(self.a1_q), _p(self.a1_sf),
-                 _p(self.g1), _p(self.al.sorted_pair), _p(self.al.offsets), _p(self.al.plan),
-                 _p(w.prep13), _p(w.g13), _p(self.g2), _p(self.a2_q), _p(self.a2_sf), s)
+            self._gemm1_w4a4(w, s)
         else:
             call("grouped_gemm1_swiglu_w4a16", ctypes.byref(d), _p(x if x is not None else self.x_last),
                  _p(self.al.sorted_pair), _p(self.al.offsets), _p(self.al.plan), _p(w.prep13),
@@ -250,10 +276,7 @@ class MoELayer:
         d, w, s = self.d, weights or self.w, _stream()
         tw = topk_w if topk_w is not None else self.tw_last
         if variant == "w4a4":
-            call("grouped_gemm2_combine", ctypes.byref(d), _p(self.a2_q), _p(self.a2_sf),
-                 _p(self.g2), _p(self.al.offsets), _p(self.al.inv_pos), _p(self.al.plan),
-                 _p(tw), _p(w.prep2), _p(w.g2), _p(out), _dtype_code(out), _p(self.ws),
-                 self.ws.numel() * 4, s)
+            self._gemm2_w4a4(w, tw, out, s)
         else:
             call("grouped_gemm2_combine_w4a16", ctypes.byref(d), _p(self.a2_bf16),
                  _p(self.al.offsets), _p(self.al.inv_pos), _p(self.al.plan), _p(tw),
@@ -273,22 +296,17 @@ class MoELayer:
             call("nvfp4_global_scale", _p(x), NVFP4_BF16, 1, d.T * d.H, _p(self.g1),
                  _p(self.gs_ws), self.gs_ws_bytes, s)
             call("nvfp4_quantize", _p(x), NVFP4_BF16, d.T, d.H, d.H, _p(self.g1), d.T,
-                 _p(self.a1_q), _p(self.a1_sf), s)
+                 _p(self.a1_q), _p(self.a1_sf), _p(self.a1_deq), s)
         call("moe_align", ctypes.byref(d), _p(topk_ids), _p(self.al.offsets),
              _p(self.al.sorted_pair), _p(self.al.inv_pos), _p(self.al.plan),
              _p(self.al.workspace), self.al.workspace.numel(), s)
         if marks:
             marks[0].record()
         if variant == "w4a4":
-            call("grouped_gemm1_swiglu", ctypes.byref(d), _p(self.a1_q), _p(self.a1_sf),
-                 _p(self.g1), _p(self.al.sorted_pair), _p(self.al.offsets), _p(self.al.plan),
-                 _p(w.prep13), _p(w.g13), _p(self.g2), _p(self.a2_q), _p(self.a2_sf), s)
+            self._gemm1_w4a4(w, s)
             if marks:
                 marks[1].record()
-            call("grouped_gemm2_combine", ctypes.byref(d), _p(self.a2_q), _p(self.a2_sf),
-                 _p(self.g2), _p(self.al.offsets), _p(self.al.inv_pos), _p(self.al.plan),
-                 _p(topk_w), _p(w.prep2), _p(w.g2), _p(out), _dtype_code(out), _p(self.ws),
-                 self.ws.numel() * 4, s)
+            self._gemm2_w4a4(w, topk_w, out, s)
         elif variant == "w4a16":
             call("grouped_gemm1_swiglu_w4a16", ctypes.byref(d), _p(x), _p(self.al.sorted_pair),
                  _p(self.al.offsets), _p(self.al.plan), _p(w.prep13), _p(w.g13),

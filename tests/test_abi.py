@@ -76,16 +76,16 @@ def test_dims_rejected(lib, dims, code, frag):
     rc = lib.moe_align(ctypes.byref(d), None, None, None, None, None, None, 0, None)
     assert rc == code
     assert frag in _lib.last_error() and _lib.last_error().startswith("moe_align:")
-    rc = lib.grouped_gemm1_swiglu(ctypes.byref(d), *([None] * 11), None)
+    rc = lib.grouped_gemm1_swiglu(ctypes.byref(d), *([None] * 13), None)
     assert rc == code
 
 
 def test_null_and_enum_errors(lib):
-    assert lib.nvfp4_quantize(None, 7, 1, 16, 16, None, 1, None, None, None) == _lib.NVFP4_EINVAL
+    assert lib.nvfp4_quantize(None, 7, 1, 16, 16, None, 1, None, None, None, None) == _lib.NVFP4_EINVAL
     assert "dtype=7" in _lib.last_error()
-    assert lib.nvfp4_quantize(None, 0, 4, 24, 24, None, 1, None, None, None) == _lib.NVFP4_ESHAPE
-    assert lib.nvfp4_quantize(None, 0, 4, 32, 36, None, 1, None, None, None) == _lib.NVFP4_ESHAPE
-    assert lib.nvfp4_quantize(None, 0, 4, 32, 32, None, 1, None, None, None) == _lib.NVFP4_EINVAL
+    assert lib.nvfp4_quantize(None, 0, 4, 24, 24, None, 1, None, None, None, None) == _lib.NVFP4_ESHAPE
+    assert lib.nvfp4_quantize(None, 0, 4, 32, 36, None, 1, None, None, None, None) == _lib.NVFP4_ESHAPE
+    assert lib.nvfp4_quantize(None, 0, 4, 32, 32, None, 1, None, None, None, None) == _lib.NVFP4_EINVAL
     assert lib.nvfp4_global_scale(None, 0, 1, 12, None, None, 0, None) == _lib.NVFP4_ESHAPE
     assert lib.moe_route_topk(None, 4, 8, 9, None, None, None) == _lib.NVFP4_ESHAPE
     assert lib.moe_route_topk(None, 4, 2048, 4, None, None, None) == _lib.NVFP4_ESHAPE
@@ -95,19 +95,19 @@ def test_null_and_enum_errors(lib):
 
 def test_gemm2_errors_name_the_problem(lib):
     d = _d()
-    rc = lib.grouped_gemm2_combine(ctypes.byref(d), *([None] * 9), None, 0, None, 0, None)
+    rc = lib.grouped_gemm2_combine(ctypes.byref(d), *([None] * 10), None, 0, None, 0, None)
     assert rc == _lib.NVFP4_EWORKSPACE
     msg = _lib.last_error()
     for f in ("num_experts=128", "M=512", "N=2048", "K=768", "workspace_size=0"):
         assert f in msg, msg
-    rc = lib.grouped_gemm2_combine(ctypes.byref(d), *([None] * 9), None, 5, None, 0, None)
+    rc = lib.grouped_gemm2_combine(ctypes.byref(d), *([None] * 10), None, 5, None, 0, None)
     assert rc == _lib.NVFP4_EINVAL and "out_dtype=5" in _lib.last_error()
 
 
 def test_zero_tokens_is_a_noop(lib):
     d = _d(T=0)
-    assert lib.grouped_gemm1_swiglu(ctypes.byref(d), *([None] * 11), None) == _lib.NVFP4_OK
-    assert lib.nvfp4_quantize(None, 0, 0, 32, 32, None, 1, None, None, None) == _lib.NVFP4_OK
+    assert lib.grouped_gemm1_swiglu(ctypes.byref(d), *([None] * 13), None) == _lib.NVFP4_OK
+    assert lib.nvfp4_quantize(None, 0, 0, 32, 32, None, 1, None, None, None, None) == _lib.NVFP4_OK
     assert lib.moe_route_topk(None, 0, 8, 2, None, None, None) == _lib.NVFP4_OK
     assert _lib.last_error() == ""
 

@@ -75,7 +75,8 @@ def test_quantize_activations(dev, name):
     w = moe_inputs.WORKLOADS[name]
     x = moe_inputs.activations(w, device=dev)
     g = ops.global_scale(x)
-    q, sf = ops.quantize(x, g)
+    deq = torch.empty(x.shape, dtype=torch.float16, device=dev)
+    q, sf = ops.quantize(x, g, deq=deq)
     xf = to_np(x).astype(np.float64)
     g_ref = onv.global_scale(xf)
     assert to_np(g)[0] == g_ref
@@ -83,6 +84,8 @@ def test_quantize_activations(dev, name):
     codes, scales = onv.quantize(xf[rows], g_ref)
     assert np.array_equal(to_np(sf)[rows], scales)
     assert np.array_equal(to_np(q)[rows], onv.pack_codes(codes))
+    # The decoded copy is the exact value code * block scale (global scale not applied).
+    assert np.array_equal(to_np(deq)[rows].astype(np.float64), onv.dequantize(codes, scales, 1.0))
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode", "large_e"])
@@ -129,12 +132,15 @@ def test_quantize_ties_and_edges(dev):
     x[2, 16:] = -1e30            # saturating scale
     xt = torch.tensor(x, dtype=torch.float32, device=dev)
     gt = torch.tensor(gs, dtype=torch.float32, device=dev)
-    q, sf = ops.quantize(xt, gt, rows_per_g=1)
-    q, sf = to_np(q), to_np(sf)
+    deq = torch.empty(xt.shape, dtype=torch.float16, device=dev)
+    q, sf = ops.quantize(xt, gt, rows_per_g=1, deq=deq)
+    q, sf, deq = to_np(q), to_np(sf), to_np(deq).astype(np.float64)
     for r in range(len(rows)):
         c, s = onv.quantize(x[r:r + 1], gs[r])
         assert np.array_equal(sf[r:r + 1], s), r
         assert np.array_equal(q[r:r + 1], onv.pack_codes(c)), r
+        # every scale from 0 to the saturating 448 (and every code) decodes exactly in f16
+        assert np.array_equal(deq[r:r + 1], onv.dequantize(c, s, 1.0)), r
 
 
 def test_quantize_strided_rows(dev):
@@ -146,3 +152,29 @@ def test_quantize_strided_rows(dev):
     xf = to_np(x).astype(np.float64)
     c, s = onv.quantize(xf, to_np(g)[0])
     assert np.array_equal(to_np(sf), s) and np.array_equal(to_np(q), onv.pack_codes(c))
+
+
+def test_decoded_copy_covers_every_code_and_scale(dev):
+    """All 16 codes under every one of the 127 non-negative E4M3 scales decode
+    exactly to f16: block b of row r holds scale r and the codes in order."""
+    # Build inputs whose quantisation reproduces a chosen (scale, codes) pair:
+    # with g = 1 the block value code * scale quantises back to itself when
+    # the block's amax is 6 * scale (code 7 is present in every block).
+    vals = []
+    scales = []
+    for sc in range(1, 127):
+        s = onv.E4M3_POS[sc]
+        blk = onv.E2M1_VALUES[[7, 1, 2, 3, 4, 5, 6, 0, 15, 9, 10, 11, 12, 13, 14, 8]] * s
+        vals.append(blk)
+        scales.append(sc)
+    x = np.array(vals, dtype=np.float64)
+    assert np.array_equal(x.astype(np.float32).astype(np.float64), x)
+    g = np.float32(1.0)
+    c_ref, s_ref = onv.quantize(x, g)
+    xt = torch.tensor(x, dtype=torch.float32, device=dev)
+    gt = torch.ones(1, dtype=torch.float32, device=dev)
+    deq = torch.empty(xt.shape, dtype=torch.float16, device=dev)
+    q, sf = ops.quantize(xt, gt, deq=deq)
+    assert np.array_equal(to_np(sf), s_ref)
+    assert np.array_equal(to_np(q), onv.pack_codes(c_ref))
+    assert np.array_equal(to_np(deq).astype(np.float64), onv.dequantize(c_ref, s_ref, 1.0))

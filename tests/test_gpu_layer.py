@@ -115,10 +115,21 @@ def test_gemm1_w4a4_stage(dev, w):
     a1_sf = torch.from_numpy(ref.a1_scales).to(dev)
     g1 = torch.tensor([float(ref.g1)], device=dev)
     g2 = torch.tensor([float(case.g2)], device=dev)
-    a2_q, a2_sf = ops.gemm1_w4a4(case.d, a1_q, a1_sf, g1, al, wq, g2)
     rows = ref.rows
+    # Codes in (decoded in the kernels), then the exact f16 copy in (decoded
+    # once, by the oracle here); both must give a2 to the same bar, and the
+    # a2 copy must be the exact decoding of the a2 codes it accompanies.
+    a2_q, a2_sf = ops.gemm1_w4a4(case.d, a1_q, a1_sf, g1, al, wq, g2)
     chk = check_a2_nvfp4(to_np(a2_q)[rows], to_np(a2_sf)[rows], ref.h, case.g2)
     print(f"{w.name}: a2 exact={chk.exact} flips={chk.flips} of {ref.h.size}")
+    a1_deq = torch.from_numpy(onv.dequantize(ref.a1_codes, ref.a1_scales, 1.0)).to(dev).to(torch.float16)
+    a2_deq = torch.empty(w.pairs, w.I, dtype=torch.float16, device=dev)
+    b2_q, b2_sf = ops.gemm1_w4a4(case.d, None, None, g1, al, wq, g2, a1_deq=a1_deq, a2_deq=a2_deq)
+    chk2 = check_a2_nvfp4(to_np(b2_q)[rows], to_np(b2_sf)[rows], ref.h, case.g2)
+    got_codes = onv.unpack_codes(to_np(b2_q)[rows])
+    assert np.array_equal(to_np(a2_deq)[rows].astype(np.float64),
+                          onv.dequantize(got_codes, to_np(b2_sf)[rows], 1.0))
+    print(f"{w.name} (decoded a1): a2 exact={chk2.exact} flips={chk2.flips} of {ref.h.size}")
 
 
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
@@ -138,6 +149,12 @@ def test_gemm2_w4a4_stage(dev, w):
     got = to_np(out32).astype(np.float64)
     check_layer_out(got, ref.out, f"{w.name} gemm2")
     assert torch.equal(out16, out32.to(torch.bfloat16))
+    # The same a2 as its exact f16 copy (codes not passed).
+    a2_deq = torch.zeros(P, w.I, dtype=torch.float16, device=dev)
+    a2_deq[torch.from_numpy(ref.rows).to(dev)] = torch.from_numpy(
+        onv.dequantize(ref.a2_codes, ref.a2_scales, 1.0)).to(dev).to(torch.float16)
+    outd = ops.gemm2_w4a4(case.d, None, None, g2, al, case.tw, wq, out_dtype=torch.float32, a2_deq=a2_deq)
+    check_layer_out(to_np(outd).astype(np.float64), ref.out, f"{w.name} gemm2 (decoded a2)")
 
 
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
@@ -155,18 +172,18 @@ def test_w4a16_stages(dev, w):
 
 
 # ---------------------------------------------------------------- whole layer
-def _run_layer(case: Case, dev, variant):
+def _run_layer(case: Case, dev, variant, decoded_copies=False):
     g2 = torch.tensor([float(case.g2)], device=dev)
-    layer = ops.MoELayer(case.d, case.wq, g2, device=dev)
+    layer = ops.MoELayer(case.d, case.wq, g2, device=dev, decoded_copies=decoded_copies)
     out32 = layer.forward(case.x, case.ids, case.tw, variant, out_dtype=torch.float32).clone()
     out16 = layer.forward(case.x, case.ids, case.tw, variant, out_dtype=torch.bfloat16).clone()
     torch.cuda.synchronize()
     return layer, out32, out16
 
 
-def _judge_layer(case: Case, dev, variant):
+def _judge_layer(case: Case, dev, variant, decoded_copies=False):
     ref = case.oracle(variant)
-    layer, out32, out16 = _run_layer(case, dev, variant)
+    layer, out32, out16 = _run_layer(case, dev, variant, decoded_copies)
     assert torch.equal(out16, out32.to(torch.bfloat16)), "bf16 output != bf16(f32 output)"
     toks = np.arange(case.w.T) if case.tokens is None else np.asarray(case.tokens)
     rows = ref.rows
@@ -175,7 +192,13 @@ def _judge_layer(case: Case, dev, variant):
         # expected output is then the oracle's down projection of that a2.
         assert np.array_equal(to_np(layer.a1_q), onv.pack_codes(ref.a1_codes))
         assert np.array_equal(to_np(layer.a1_sf), ref.a1_scales)
+        if layer.a1_deq is not None:
+            assert np.array_equal(to_np(layer.a1_deq).astype(np.float64),
+                                  onv.dequantize(ref.a1_codes, ref.a1_scales, 1.0))
         chk = check_a2_nvfp4(to_np(layer.a2_q)[rows], to_np(layer.a2_sf)[rows], ref.h, case.g2)
+        if layer.a2_deq is not None:
+            assert np.array_equal(to_np(layer.a2_deq)[rows].astype(np.float64),
+                                  onv.dequantize(chk.codes, chk.scales, 1.0))
         exp = ref.out if chk.exact else omoe.down_and_combine(
             onv.dequantize(chk.codes, chk.scales, case.g2), rows, ref.sorted_pair, ref.offsets,
             case.tw_np, case.ew, case.w.T, case.w.topk)
@@ -196,15 +219,22 @@ def test_layer_small(dev, w, variant):
     _judge_layer(Case(w, dev), dev, variant)
 
 
-FULL = [("decode", "w4a4", 8), ("decode", "w4a16", 8), ("prefill", "w4a4", 4),
-        ("large_e", "w4a4", 3), ("skew", "w4a4", 4), ("skew", "w4a16", 4)]
+@pytest.mark.parametrize("w", SMALL + [moe_inputs.WORKLOADS["tiny"]], ids=lambda w: w.name)
+def test_layer_small_decoded_copies(dev, w):
+    """W4A4 with the exact f16 activation copies read by the GEMMs."""
+    _judge_layer(Case(w, dev), dev, "w4a4", decoded_copies=True)
 
 
-@pytest.mark.parametrize("name,variant,n_tok", FULL, ids=lambda v: str(v))
-def test_layer_full_size_sampled(dev, name, variant, n_tok):
+FULL = [("decode", "w4a4", 8, False), ("decode", "w4a4", 4, True), ("decode", "w4a16", 8, False),
+        ("prefill", "w4a4", 4, False), ("prefill", "w4a4", 2, True), ("large_e", "w4a4", 3, False),
+        ("skew", "w4a4", 4, False), ("skew", "w4a16", 4, False)]
+
+
+@pytest.mark.parametrize("name,variant,n_tok,decoded", FULL, ids=lambda v: str(v))
+def test_layer_full_size_sampled(dev, name, variant, n_tok, decoded):
     w = moe_inputs.WORKLOADS[name]
     toks = np.sort(np.random.default_rng(w.seed).choice(w.T, n_tok, replace=False))
-    _judge_layer(Case(w, dev, tokens=toks), dev, variant)
+    _judge_layer(Case(w, dev, tokens=toks), dev, variant, decoded)
 
 
 def test_layer_is_deterministic(dev):
