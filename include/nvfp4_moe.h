@@ -14,6 +14,7 @@
  *   nvfp4_global_scale  activations -> g1                    (W4A4 only)
  *   nvfp4_quantize      activations, g1 -> a1 codes + scales (W4A4 only)
  *   moe_align           top-k expert ids -> rows grouped by expert
+ *   (moe_scale_and_align: the first and third steps in one call)
  *   grouped_gemm1_swiglu[_w4a16]   gate/up GEMM, SwiGLU, requantisation
  *   grouped_gemm2_combine[_w4a16]  down GEMM, top-k weighted combine
  *
@@ -188,6 +189,17 @@ size_t moe_align_plan_size(const nvfp4_moe_dims* dims);
 int moe_align(const nvfp4_moe_dims* dims, const int32_t* topk_ids, int32_t* expert_offsets,
               int32_t* sorted_pair, int32_t* inv_pos, int32_t* plan, void* ws, size_t ws_bytes,
               void* stream);
+
+/* The activation global scale and the permutation in one call: the same
+ * results as nvfp4_global_scale(x, NVFP4_BF16, 1, T*H, g1, gs_ws, ...)
+ * followed by moe_align(dims, topk_ids, ...), with the same workspace
+ * contracts.  The two steps are independent, so when the pairs fit one
+ * workgroup (P <= 4096) they share one kernel launch; otherwise they run as
+ * the two launches.  x is bfloat16 [T][H], 16-byte aligned. */
+int moe_scale_and_align(const nvfp4_moe_dims* dims, const uint16_t* x, float* g1, void* gs_ws,
+                        size_t gs_ws_bytes, const int32_t* topk_ids, int32_t* expert_offsets,
+                        int32_t* sorted_pair, int32_t* inv_pos, int32_t* plan, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Weight preparation (offline).                                             */

@@ -48,6 +48,8 @@ SIGNATURES = {
     "moe_align_plan_size": (c_size_t, [_P]),
     "moe_align": (c_int, [_P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                           c_void_p]),
+    "moe_scale_and_align": (c_int, [_P, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, c_void_p,
+                                    c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "nvfp4_prep_weights_size": (c_size_t, [_P, c_int]),
     "nvfp4_prep_weights": (c_int, [_P, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
     "grouped_gemm_workspace_size": (c_size_t, [_P]),

@@ -75,28 +75,97 @@ __device__ int block_exclusive_scan_1024(int v, int* total) {
 
 // One tile-list entry: {expert | m_tile << 11, first row | rows << 24}, so a
 // GEMM workgroup learns its expert, rows and row count from one 8-byte read.
-__device__ __forceinline__ void write_tile(int32_t* dst, int e, int mt, int BM, const int* soff) {
-  const int row0 = soff[e] + mt * BM;
-  const int rows = min(BM, soff[e + 1] - row0);
+// Expert e owns rows [start, start + n).
+__device__ __forceinline__ void write_tile(int32_t* dst, int e, int mt, int BM, int start, int n) {
+  const int row0 = start + mt * BM;
+  const int rows = min(BM, n - mt * BM);
   dst[0] = e | (mt << 11);
   dst[1] = (int32_t)((uint32_t)row0 | ((uint32_t)rows << 24));
 }
 
+// Exclusive scan of V values per thread over 1024 threads (one pass, two
+// barriers); tot[v] receives the sums.
+template <int V>
+__device__ void block_exclusive_scan_1024_v(const int (&v)[V], int (&out)[V], int (&tot)[V]) {
+  __shared__ int wsum[16][V];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) x[i] = v[i];
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int y = __shfl_up(x[i], off);
+      if (lane >= off) x[i] += y;
+    }
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int i = 0; i < V; ++i) wsum[w][i] = x[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    int base = 0, t = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int s = wsum[j][i];
+      base += j < w ? s : 0;
+      t += s;
+    }
+    out[i] = base + x[i] - v[i];
+    tot[i] = t;
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------- scan + plan
+// Writes the four tile lists from the per-expert row counts: thread e (one
+// per expert slot) writes its own tiles of every list.
+__device__ __forceinline__ void write_plan(int32_t* __restrict__ plan, const int (&lo)[4], int e,
+                                           int slots, int off_e, int n_e) {
+  int tiles[4], tstart[4], ntiles[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) tiles[b] = e < slots ? (n_e + kPlanBMs[b] - 1) / kPlanBMs[b] : 0;
+  block_exclusive_scan_1024_v<4>(tiles, tstart, ntiles);
+  if (e == 0) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      plan[b] = ntiles[b];
+      plan[4 + b] = lo[b];
+    }
+  }
+  if (e < slots) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      for (int mt = 0; mt < tiles[b]; ++mt)
+        write_tile(plan + lo[b] + 2 * (tstart[b] + mt), e, mt, kPlanBMs[b], off_e, n_e);
+  }
+}
+
+// Per expert: turn the per-chunk counts into the chunk's first output row
+// (in place), then scan over experts and write offsets and tile lists.
+// The counts of a group of chunks are loaded together (independent loads),
+// so the walk over chunks costs one memory latency per group.
+constexpr int kScanGroup = 16;
 __global__ __launch_bounds__(1024) void align_scan_kernel(AlignP a, int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ plan,
                                                           int4 list_off) {
-  __shared__ int tstart[kMaxExperts + 1];
-  __shared__ int soff[kMaxExperts + 1];
   const int e = threadIdx.x;
   int n_e = 0;
   if (e < a.slots) {
-    for (int c = 0; c < a.nchunks; ++c) {
-      const int64_t i = (int64_t)c * a.slots + e;
-      const int v = counts[i];
-      counts[i] = n_e;  // exclusive prefix over earlier chunks
-      n_e += v;
+    for (int c0 = 0; c0 < a.nchunks; c0 += kScanGroup) {
+      int v[kScanGroup];
+#pragma unroll
+      for (int j = 0; j < kScanGroup; ++j)
+        v[j] = c0 + j < a.nchunks ? counts[(int64_t)(c0 + j) * a.slots + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kScanGroup; ++j) {
+        if (c0 + j < a.nchunks) counts[(int64_t)(c0 + j) * a.slots + e] = n_e;  // exclusive prefix
+        n_e += v[j];
+      }
     }
   }
   int total;
@@ -104,38 +173,10 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(AlignP a, int32_t* __r
   if (e < a.slots) {
     for (int c = 0; c < a.nchunks; ++c) counts[(int64_t)c * a.slots + e] += off_e;
     offsets[e] = off_e;
-    soff[e] = off_e;
   }
-  if (e == 0) {
-    offsets[a.slots] = total;
-    soff[a.slots] = total;
-  }
-
+  if (e == 0) offsets[a.slots] = total;
   const int lo[4] = {list_off.x, list_off.y, list_off.z, list_off.w};
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int BM = kPlanBMs[b];
-    const int tiles = (e < a.slots) ? (n_e + BM - 1) / BM : 0;
-    int ntiles;
-    const int ts = block_exclusive_scan_1024(tiles, &ntiles);
-    if (e < a.slots) tstart[e] = ts;
-    if (e == 0) {
-      tstart[a.slots] = ntiles;
-      plan[b] = ntiles;
-      plan[4 + b] = lo[b];
-    }
-    __syncthreads();
-    for (int slot = threadIdx.x; slot < ntiles; slot += 1024) {
-      // largest expert x with tstart[x] <= slot
-      int l = 0, h = a.slots;  // tstart[l] <= slot < tstart[h]
-      while (h - l > 1) {
-        const int m = (l + h) >> 1;
-        if (tstart[m] <= slot) l = m; else h = m;
-      }
-      write_tile(plan + lo[b] + 2 * slot, l, slot - tstart[l], BM, soff);
-    }
-    __syncthreads();
-  }
+  write_plan(plan, lo, e, a.slots, off_e, n_e);
 }
 
 // ---------------------------------------------------------------- scatter
@@ -188,105 +229,126 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(AlignP a,
 }
 
 // ---------------------------------------------------------------- one workgroup
-// The whole alignment in one launch when P <= 4 * kAlignChunk: histogram,
-// scan, tile lists and the stable scatter, by 1024 threads in rounds of 1024
-// pairs (the in-round order of equal experts comes from wavefront ballots and
-// per-wavefront counts, as in the multi-workgroup path).
-constexpr int kFusedRounds = 4;
+// The whole alignment in one launch when P <= kSmallP (at most 4 pairs per
+// thread).  LDS atomics count the pairs of every expert and hand each pair a
+// slot in its expert's segment, in arbitrary order; after the scan over
+// experts the pair indices are placed there, and each pair's final row is its
+// segment start plus the number of smaller pair indices in the segment -- a
+// stable order that no atomic ordering can change.  Each thread then writes
+// only its own pairs.
+constexpr int kSmallP = 4096;
+constexpr int kSmallPer = kSmallP / 1024;
 
-__global__ __launch_bounds__(1024) void align_fused_kernel(AlignP a, int32_t* __restrict__ offsets,
+__device__ __forceinline__ void align_small_body(const AlignP& a, int32_t* __restrict__ offsets,
+                                                 int32_t* __restrict__ sorted_pair,
+                                                 int32_t* __restrict__ inv_pos,
+                                                 int32_t* __restrict__ plan, int4 list_off) {
+  __shared__ int seg[kSmallP];
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int start[kMaxExperts];
+  const int tid = threadIdx.x;
+  if (tid < a.slots) cnt[tid] = 0;
+  __syncthreads();
+  const int P = (int)a.P;
+  int my_e[kSmallPer], my_slot[kSmallPer];
+#pragma unroll
+  for (int r = 0; r < kSmallPer; ++r) {
+    const int f = tid + 1024 * r;
+    my_e[r] = -1;
+    if (f < P) {
+      bool valid;
+      const int e = expert_of(a, f, valid);
+      if (valid) {
+        my_e[r] = e;
+        my_slot[r] = atomicAdd(&cnt[e], 1);
+      } else {
+        inv_pos[f] = -1;
+      }
+    }
+  }
+  __syncthreads();
+  const int e = tid;
+  const int n_e = e < a.slots ? cnt[e] : 0;
+  int total;
+  const int off_e = block_exclusive_scan_1024(n_e, &total);
+  if (e < a.slots) {
+    offsets[e] = off_e;
+    start[e] = off_e;
+  }
+  if (e == 0) offsets[a.slots] = total;
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kSmallPer; ++r)
+    if (my_e[r] >= 0) seg[start[my_e[r]] + my_slot[r]] = tid + 1024 * r;
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kSmallPer; ++r) {
+    if (my_e[r] < 0) continue;
+    const int f = tid + 1024 * r;
+    const int s0 = start[my_e[r]], n = cnt[my_e[r]];
+    int rank = 0;
+    for (int i = 0; i < n; ++i) rank += seg[s0 + i] < f;
+    sorted_pair[s0 + rank] = f;
+    inv_pos[f] = s0 + rank;
+  }
+  const int lo[4] = {list_off.x, list_off.y, list_off.z, list_off.w};
+  write_plan(plan, lo, e, a.slots, off_e, n_e);
+}
+
+__global__ __launch_bounds__(1024) void align_small_kernel(AlignP a, int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ sorted_pair,
                                                            int32_t* __restrict__ inv_pos,
                                                            int32_t* __restrict__ plan, int4 list_off) {
-  __shared__ int hist[kMaxExperts];
-  __shared__ int running[kMaxExperts];
-  __shared__ int tstart[kMaxExperts + 1];
-  __shared__ int soff[kMaxExperts + 1];
-  __shared__ int wcnt[16][kMaxExperts];
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  if (tid < a.slots) hist[tid] = 0;
-  for (int i = tid; i < 16 * kMaxExperts; i += 1024) (&wcnt[0][0])[i] = 0;
-  __syncthreads();
-  for (int r = 0; r < kFusedRounds; ++r) {
-    const int64_t f = (int64_t)r * 1024 + tid;
-    if (f < a.P) {
-      bool valid;
-      const int e = expert_of(a, f, valid);
-      if (valid) atomicAdd(&hist[e], 1);
-    }
-  }
-  __syncthreads();
-  const int n_e = tid < a.slots ? hist[tid] : 0;
-  int total;
-  const int off_e = block_exclusive_scan_1024(n_e, &total);
-  if (tid < a.slots) {
-    offsets[tid] = off_e;
-    running[tid] = off_e;
-    soff[tid] = off_e;
-  }
-  if (tid == 0) {
-    offsets[a.slots] = total;
-    soff[a.slots] = total;
-  }
+  align_small_body(a, offsets, sorted_pair, inv_pos, plan, list_off);
+}
 
-  const int lo[4] = {list_off.x, list_off.y, list_off.z, list_off.w};
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int BM = kPlanBMs[b];
-    const int tiles = tid < a.slots ? (n_e + BM - 1) / BM : 0;
-    int ntiles;
-    const int ts = block_exclusive_scan_1024(tiles, &ntiles);
-    if (tid < a.slots) tstart[tid] = ts;
-    if (tid == 0) {
-      tstart[a.slots] = ntiles;
-      plan[b] = ntiles;
-      plan[4 + b] = lo[b];
-    }
-    __syncthreads();
-    for (int slot = tid; slot < ntiles; slot += 1024) {
-      int l = 0, h = a.slots;
-      while (h - l > 1) {
-        const int m = (l + h) >> 1;
-        if (tstart[m] <= slot) l = m; else h = m;
-      }
-      write_tile(plan + lo[b] + 2 * slot, l, slot - tstart[l], BM, soff);
-    }
-    __syncthreads();
+// ---------------------------------------------------------------- scale + align
+// The activation global scale and the alignment are independent: one launch
+// runs both.  Workgroups 0 .. nblk-1 reduce max |x| over the bf16 tensor
+// (each folds its maximum into ws[1] and counts itself in ws[0]; the last one
+// writes g and puts both words back to zero, as nvfp4_global_scale does) and
+// workgroup nblk runs the one-workgroup alignment.
+__global__ __launch_bounds__(1024) void scale_align_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                           float* __restrict__ g,
+                                                           uint32_t* __restrict__ ws, int nblk,
+                                                           AlignP a, int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ sorted_pair,
+                                                           int32_t* __restrict__ inv_pos,
+                                                           int32_t* __restrict__ plan, int4 list_off) {
+  if ((int)blockIdx.x == nblk) {
+    align_small_body(a, offsets, sorted_pair, inv_pos, plan, list_off);
+    return;
   }
-
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int r = 0; r < kFusedRounds; ++r) {
-    const int64_t f = (int64_t)r * 1024 + tid;
-    const bool in = f < a.P;
-    bool valid = false;
-    const int e = in ? expert_of(a, f, valid) : 0;
-    valid = valid && in;
-    const int key = valid ? e : 2047;
-    uint64_t same = ~0ull;
+  __shared__ float red[16];
+  const int64_t stride = (int64_t)nblk * 1024 * 8;
+  float m = 0.0f;
+  for (int64_t i = ((int64_t)blockIdx.x * 1024 + threadIdx.x) * 8; i < n; i += stride) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(x + i);
 #pragma unroll
-    for (int bit = 0; bit < 11; ++bit) {
-      const bool bb = (key >> bit) & 1;
-      const uint64_t bal = __ballot(bb);
-      same &= bb ? bal : ~bal;
+    for (int j = 0; j < 4; ++j) {
+      m = fmaxf(m, fabsf(bf16_bits_to_f32(w[j] & 0xFFFFu)));
+      m = fmaxf(m, fabsf(bf16_bits_to_f32(w[j] >> 16)));
     }
-    const int rank = __popcll(same & lt);
-    const int cnt = __popcll(same);
-    if (valid && rank == 0) wcnt[w][e] = cnt;
-    __syncthreads();
-    if (valid) {
-      int pos = running[e] + rank;
-      for (int v = 0; v < w; ++v) pos += wcnt[v][e];
-      sorted_pair[pos] = (int32_t)f;
-      inv_pos[f] = pos;
-    } else if (in) {
-      inv_pos[f] = -1;
-    }
-    __syncthreads();
-    if (valid && rank == 0) {
-      atomicAdd(&running[e], cnt);
-      wcnt[w][e] = 0;
-    }
-    __syncthreads();
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) r = fmaxf(r, red[i]);
+  if (nblk == 1) {
+    *g = global_scale_of_amax(r);
+    return;
+  }
+  __hip_atomic_fetch_max(ws + 1, (uint32_t)__float_as_int(r), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t done = __hip_atomic_fetch_add(ws, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  if (done == (uint32_t)nblk - 1) {
+    const uint32_t bits = __hip_atomic_load(ws + 1, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+    *g = global_scale_of_amax(__int_as_float((int)bits));
+    __hip_atomic_store(ws + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(ws, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -355,6 +417,7 @@ AlignShape align_shape(int T, int topk, int E, int shared) {
   a.topk = topk;
   a.E = E;
   a.shared = shared;
+  a.H = 0;
   a.P = (int64_t)T * topk + (int64_t)shared * T;
   a.slots = E + shared;
   a.nchunks = (int)((a.P + kAlignChunk - 1) / kAlignChunk);
@@ -387,8 +450,8 @@ hipError_t launch_align(const AlignShape& a, const int32_t* topk_ids, int32_t* o
   p.P = a.P;
   int32_t* counts = static_cast<int32_t*>(ws);
   int4 lo0 = make_int4((int)a.list_off[0], (int)a.list_off[1], (int)a.list_off[2], (int)a.list_off[3]);
-  if (a.P <= (int64_t)kFusedRounds * 1024) {
-    align_fused_kernel<<<1, 1024, 0, s>>>(p, offsets, sorted_pair, inv_pos, plan, lo0);
+  if (a.P <= (int64_t)kSmallP) {
+    align_small_kernel<<<1, 1024, 0, s>>>(p, offsets, sorted_pair, inv_pos, plan, lo0);
     return hipGetLastError();
   }
   if (a.nchunks > 0) {
@@ -401,6 +464,32 @@ hipError_t launch_align(const AlignShape& a, const int32_t* topk_ids, int32_t* o
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nchunks == 0) return e;
   align_scatter_kernel<<<a.nchunks, 256, 0, s>>>(p, counts, sorted_pair, inv_pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_and_align(const AlignShape& a, const uint16_t* x, float* g, void* gs_ws,
+                                  const int32_t* topk_ids, int32_t* offsets, int32_t* sorted_pair,
+                                  int32_t* inv_pos, int32_t* plan, void* ws, hipStream_t s) {
+  const int64_t n = (int64_t)a.T * a.H;
+  if (a.P > (int64_t)kSmallP || n == 0) {
+    hipError_t e = launch_global_scale(x, 0, 1, n, g, gs_ws, s);
+    if (e != hipSuccess) return e;
+    return launch_align(a, topk_ids, offsets, sorted_pair, inv_pos, plan, ws, s);
+  }
+  AlignP p;
+  p.ids = topk_ids;
+  p.T = a.T;
+  p.topk = a.topk;
+  p.E = a.E;
+  p.shared = a.shared;
+  p.slots = a.slots;
+  p.nchunks = a.nchunks;
+  p.P = a.P;
+  int nblk = (int)((n + 1024 * 32 - 1) / (1024 * 32));
+  nblk = nblk < 1 ? 1 : (nblk > 256 ? 256 : nblk);
+  const int4 lo = make_int4((int)a.list_off[0], (int)a.list_off[1], (int)a.list_off[2], (int)a.list_off[3]);
+  scale_align_kernel<<<nblk + 1, 1024, 0, s>>>(x, n, g, static_cast<uint32_t*>(gs_ws), nblk, p, offsets,
+                                               sorted_pair, inv_pos, plan, lo);
   return hipGetLastError();
 }
 

@@ -46,12 +46,6 @@ __device__ __forceinline__ float block_max(float m) {
   return r;
 }
 
-__device__ __forceinline__ float scale_of_amax(float amax) {
-  // Correctly rounded FP32 quotient: FP64 division then one rounding to FP32
-  // (53 >= 2 * 24 + 2 makes the double rounding innocuous).
-  return (float)((double)amax / 2688.0);
-}
-
 // One launch per call: grid (nblk, batches).  Every workgroup folds its
 // maximum into ws_max[b] (float bits of a non-negative value order like
 // unsigned integers), then counts itself in ws_cnt[b]; the last workgroup of a
@@ -76,7 +70,7 @@ __global__ __launch_bounds__(kThreads) void global_scale_kernel(const T* __restr
     uint32_t* ws_cnt = ws + 2 * b;
     uint32_t* ws_max = ws + 2 * b + 1;
     if (gridDim.x == 1) {
-      g[b] = scale_of_amax(m);
+      g[b] = global_scale_of_amax(m);
       return;
     }
     __hip_atomic_fetch_max(ws_max, (uint32_t)__float_as_int(m), __ATOMIC_RELAXED,
@@ -85,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void global_scale_kernel(const T* __restr
                                                  __HIP_MEMORY_SCOPE_AGENT);
     if (done == gridDim.x - 1) {
       const uint32_t bits = __hip_atomic_load(ws_max, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-      g[b] = scale_of_amax(__int_as_float((int)bits));
+      g[b] = global_scale_of_amax(__int_as_float((int)bits));
       __hip_atomic_store(ws_max, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(ws_cnt, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }

@@ -194,6 +194,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Global scale g = fl32(amax / 2688): FP64 division then one rounding to FP32
+// (53 >= 2 * 24 + 2 makes the double rounding innocuous).
+__device__ __forceinline__ float global_scale_of_amax(float amax) {
+  return (float)((double)amax / 2688.0);
+}
+
 // Token of pair f: routed pairs are f = t*topk + j, shared pairs f = T*topk + t.
 __device__ __forceinline__ int pair_token(int f, int T, int topk) {
   const int tk = T * topk;

@@ -398,7 +398,7 @@ __global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
 // share nothing: no LDS, no barriers.
 // ---------------------------------------------------------------------------
 template <int AK, int EPI, int MT, int NTW, int PF>
-__global__ __launch_bounds__(kNW * kWave) void grouped_gemm_stream_kernel(KParams p) {
+__device__ __forceinline__ void stream_body(const KParams& p) {
   static_assert(NTW % 2 == 0, "scale words cover column tiles in pairs");
   const int lane = threadIdx.x & 63, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kNW + (threadIdx.x >> 6)));
@@ -585,6 +585,25 @@ __global__ __launch_bounds__(kNW * kWave) void grouped_gemm_stream_kernel(KParam
   __builtin_amdgcn_s_waitcnt(0);
 }
 
+// Register budget: instantiations whose ring fits in 128 registers run 4
+// wavefronts per SIMD (more weight bytes in flight per CU); the others are
+// left to the compiler (a forced budget would spill).
+template <int AK, int MT, int PF>
+constexpr bool stream_fits_four_waves() {
+  return (MT == 1 && (AK == kActCodes || PF <= 3)) || (MT == 2 && AK == kActCodes && PF <= 3);
+}
+
+template <int AK, int EPI, int MT, int NTW, int PF>
+__global__ __launch_bounds__(kNW * kWave) void grouped_gemm_stream_kernel(KParams p) {
+  stream_body<AK, EPI, MT, NTW, PF>(p);
+}
+
+template <int AK, int EPI, int MT, int NTW, int PF>
+__global__ __launch_bounds__(kNW * kWave) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void grouped_gemm_stream4_kernel(KParams p) {
+  stream_body<AK, EPI, MT, NTW, PF>(p);
+}
+
 // out[t] = sum_j w[t][j] * d[inv_pos[t*k + j]] (+ shared row), FP32, j ascending.
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ d,
@@ -636,14 +655,13 @@ hipError_t launch_lds(KParams kp, int list_len, hipStream_t s) {
 }
 
 // Persistent launch: as many workgroups as fit on the device at once (the
-// occupancy of this instantiation times the CU count), capped by the work.
-template <int AK, int EPI, int MT, int NTW, int PF>
-hipError_t launch_stream(const KParams& kp, int list_len, hipStream_t s) {
-  auto kern = grouped_gemm_stream_kernel<AK, EPI, MT, NTW, PF>;
+// occupancy of this kernel times the CU count), capped by the work.
+template <auto KERN>
+hipError_t launch_persistent(const KParams& kp, int64_t units, hipStream_t s) {
   static int per_cu = 0;
   if (per_cu == 0) {
     int nb = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(kern),
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(KERN),
                                                                 kNW * kWave, 0);
     if (e != hipSuccess) return e;
     per_cu = nb > 0 ? nb : 1;
@@ -652,11 +670,19 @@ hipError_t launch_stream(const KParams& kp, int list_len, hipStream_t s) {
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  const int64_t units = (int64_t)list_len * ((kp.N / 16) / NTW);
   const int64_t need = (units + kNW - 1) / kNW;
   const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((int64_t)per_cu * cus, need));
-  kern<<<(unsigned)grid, kNW * kWave, 0, s>>>(kp);
+  KERN<<<(unsigned)grid, kNW * kWave, 0, s>>>(kp);
   return hipGetLastError();
+}
+
+template <int AK, int EPI, int MT, int NTW, int PF>
+hipError_t launch_stream(const KParams& kp, int list_len, hipStream_t s) {
+  const int64_t units = (int64_t)list_len * ((kp.N / 16) / NTW);
+  if constexpr (stream_fits_four_waves<AK, MT, PF>())
+    return launch_persistent<grouped_gemm_stream4_kernel<AK, EPI, MT, NTW, PF>>(kp, units, s);
+  else
+    return launch_persistent<grouped_gemm_stream_kernel<AK, EPI, MT, NTW, PF>>(kp, units, s);
 }
 
 // Ring depth of the streaming kernel: the largest allowed depth dividing the

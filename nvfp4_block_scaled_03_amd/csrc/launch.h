@@ -26,7 +26,7 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
                              hipStream_t s);
 
 struct AlignShape {
-  int T, topk, E, shared;
+  int T, topk, E, shared, H;
   int64_t P;        // pairs
   int slots;        // E + shared
   int nchunks;      // pair chunks of kAlignChunk
@@ -40,6 +40,11 @@ size_t align_plan_ints(const AlignShape& a);
 hipError_t launch_align(const AlignShape& a, const int32_t* topk_ids, int32_t* offsets,
                         int32_t* sorted_pair, int32_t* inv_pos, int32_t* plan, void* ws,
                         hipStream_t s);
+// Activation global scale (bf16 x [T][H]) and alignment in one launch when
+// the pairs fit one workgroup, else the two launches in sequence.
+hipError_t launch_scale_and_align(const AlignShape& a, const uint16_t* x, float* g, void* gs_ws,
+                                  const int32_t* topk_ids, int32_t* offsets, int32_t* sorted_pair,
+                                  int32_t* inv_pos, int32_t* plan, void* ws, hipStream_t s);
 
 // Weight streaming layout.  For an expert matrix [N][K] (N output columns,
 // K contraction): codes [N/16][K/128][64 lanes][16 B] followed (after all

@@ -8,6 +8,7 @@ import torch
 import moe_inputs
 from nvfp4_block_scaled_03_amd import _lib, ops
 from oracle import moe as omoe
+from oracle import nvfp4 as onv
 from oracle import routing as oroute
 
 from parity import device, to_np
@@ -40,10 +41,11 @@ def test_router_ties(dev):
     np.testing.assert_allclose(to_np(wt), rw, rtol=4e-7, atol=0)
 
 
-def _check_align(dev, ids_np, E, shared):
+def _check_align(dev, ids_np, E, shared, al=None):
     T, k = ids_np.shape
     d = ops.dims(T, k, E, 128, 128, shared)
-    al = ops.moe_align(d, torch.from_numpy(ids_np).to(dev))
+    if al is None:
+        al = ops.moe_align(d, torch.from_numpy(ids_np).to(dev))
     off, sp, inv = omoe.align(ids_np, E, shared)
     P = T * k + shared * T
     n_kept = int(off[-1])
@@ -109,3 +111,18 @@ def test_align_plan_size_matches(dev):
     d = ops.dims(64, 8, 128, 2048, 768, 0)
     lib = _lib.load()
     assert lib.moe_align_plan_size(ctypes.byref(d)) // 4 == ops.alloc_alignment(d, dev).plan.numel()
+
+
+@pytest.mark.parametrize("name", ["decode", "large_e", "prefill", "tiny"])
+def test_scale_and_align(dev, name):
+    """One call = global scale + alignment (one launch when P <= 4096, the two
+    launches otherwise): both results bit-exact, the scale workspace left zero."""
+    w = moe_inputs.WORKLOADS[name]
+    x = moe_inputs.activations(w, device=dev)
+    ids, _ = oroute.route_topk(to_np(moe_inputs.router_logits(w, device=dev)), w.topk)
+    d = ops.dims(w.T, w.topk, w.E, w.H, w.I, w.shared)
+    for _ in range(2):
+        g, al, gs_ws = ops.scale_and_align(d, x, torch.from_numpy(ids).to(dev))
+        assert to_np(g)[0] == onv.global_scale(to_np(x).astype(np.float64))
+        _check_align(dev, ids, w.E, w.shared, al=al)
+        assert not gs_ws.any()
