@@ -240,6 +240,12 @@ int grouped_gemm1_swiglu(const nvfp4_moe_dims* dims, const uint8_t* a1_q, const 
                          const uint8_t* w13_prep, const float* gw13, const float* g2,
                          uint8_t* a2_q, uint8_t* a2_sf, uint16_t* a2_deq, void* stream);
 
+/* 1 when, for these dimensions, the W4A4 GEMMs are faster given the exact
+ * f16 activation copies (a1_deq from nvfp4_quantize, a2_deq from GEMM1) than
+ * given the codes alone, else 0 (also 0 for invalid dims).  A performance
+ * hint only: both inputs give the same results. */
+int grouped_gemm_prefers_decoded(const nvfp4_moe_dims* dims);
+
 /* Workspace of the GEMM2 calls: the per-row FP32 down-projection outputs
  * [P][H] that the combine reads. */
 size_t grouped_gemm_workspace_size(const nvfp4_moe_dims* dims);

@@ -52,6 +52,7 @@ SIGNATURES = {
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "nvfp4_prep_weights_size": (c_size_t, [_P, c_int]),
     "nvfp4_prep_weights": (c_int, [_P, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "grouped_gemm_prefers_decoded": (c_int, [_P]),
     "grouped_gemm_workspace_size": (c_size_t, [_P]),
     "grouped_gemm1_swiglu": (c_int, [_P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,

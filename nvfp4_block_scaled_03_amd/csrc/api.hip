@@ -202,6 +202,11 @@ int nvfp4_prep_weights(const nvfp4_moe_dims* d, int which, const uint8_t* q, con
 }
 
 // ------------------------------------------------------------------ GEMMs
+int grouped_gemm_prefers_decoded(const nvfp4_moe_dims* d) {
+  if (check_dims(d, "grouped_gemm_prefers_decoded")) return 0;
+  return nvfp4::prefers_decoded(d->T, d->topk, d->E, d->shared) ? 1 : 0;
+}
+
 size_t grouped_gemm_workspace_size(const nvfp4_moe_dims* d) {
   if (check_dims(d, "grouped_gemm_workspace_size")) return 0;
   return (size_t)pairs(d) * (size_t)d->H * sizeof(float);

@@ -55,24 +55,18 @@ __device__ __forceinline__ float row16_max(float v) {
 // ---------------------------------------------------------------------------
 // Exact rounding decisions.
 //
-// Block scale: s = nearest E4M3 value to q = amax / (6 g), ties to the even
-// code, saturating at 448.  6*g is exact in FP64 and the FP64 quotient is
-// correctly rounded; amax (24 significant bits) and 6*g*m for an E4M3
-// midpoint m (at most 31 bits) are either equal or differ by at least 2^-32
-// relative, far above the 2^-53 rounding of the quotient, so rounding the
-// FP64 quotient decides exactly as the real quotient would.
+// Every decision compares a float |x| (or a block amax) with a real
+// threshold g * M, where g is the FP32 global scale and M a small constant of
+// at most 7 significant bits (6 * an E4M3 midpoint, or t * s for an E2M1
+// boundary t and an E4M3 scale s).  The product g * M is split exactly into
+// p + e with one FMA (p = fl(g M), e = g M - p, exact when g M is far from
+// underflow), which settles the comparison in FP32:
+//   a - gM = (a - p) - e, and a - p is exact when a and p are within a
+//   factor 2 of each other (Sterbenz); otherwise |a - p| > p/2 >> |e| and the
+//   sign of fl(a - p) decides.
+// For an extremely small g (below 2^-80, where the split may underflow) both
+// sides are first multiplied by 2^64, which is exact and changes no decision.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t e4m3_scale_code(float amax, float g) {
-  if (!(amax > 0.0f)) return 0u;
-  const double q = (double)amax / (6.0 * (double)g);
-  if (!(q < 448.0)) return 0x7Eu;                       // saturate (also g == 0)
-  if (q < 0.015625) return (uint32_t)__builtin_rint(q * 512.0);   // subnormal step 2^-9
-  int e2;
-  (void)__builtin_frexp(q, &e2);                         // q = m * 2^e2, m in [0.5, 1)
-  const int e = e2 - 1;                                  // q in [2^e, 2^(e+1)), e in [-6, 8]
-  const double r = __builtin_rint(__builtin_ldexp(q, 3 - e));  // in [8, 16]
-  return (uint32_t)((e + 6) * 8 + (int)r);
-}
 
 // Value of a non-negative E4M3 code 0x00..0x7E.
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
@@ -81,39 +75,90 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
   return __int_as_float((int)(((e + 120u) << 23) | (m << 20)));  // (1 + m/8) * 2^(e-7)
 }
 
-// Largest float <= d (d > 0).
-__device__ __forceinline__ float f32_round_down(double d) {
-  float f = (float)d;
-  if ((double)f > d) f = __int_as_float(__float_as_int(f) - 1);
-  return f;
+// sign(a - g * M) for a >= 0, g > 0, M > 0 (see above).
+__device__ __forceinline__ int cmp_scaled(float a, float g, float M) {
+  const float p = g * M;
+  const float e = __builtin_fmaf(g, M, -p);
+  const float d = a - p;
+  return (d > e) - (d < e);
 }
-// Largest float strictly below the smallest float >= d (d > 0): comparing
-// v > result is the same as v >= d for every float v.
-__device__ __forceinline__ float f32_below_round_up(double d) {
-  float f = (float)d;
-  if ((double)f < d) f = __int_as_float(__float_as_int(f) + 1);
-  return __int_as_float(__float_as_int(f) - 1);
+
+constexpr float kTinyG = 8.271806125530277e-25f;  // 2^-80
+constexpr float kLift = 18446744073709551616.0f;    // 2^64
+
+// Block scale: s = nearest E4M3 value to q = amax / (6 g), ties to the even
+// code, saturating at 448.  A candidate code comes from an approximate FP32
+// quotient (within a few ulps, so at most one code off); exact checks
+// against the midpoints to its two neighbours settle it.  For g < 2^-80
+// both amax and g are first multiplied by 2^64, which is exact and leaves
+// every decision unchanged.
+__device__ __forceinline__ uint32_t e4m3_scale_code(float amax, float g) {
+  if (!(amax > 0.0f)) return 0u;
+  if (g < kTinyG) {
+    amax *= kLift;
+    g *= kLift;
+  }
+  const float q = amax * __builtin_amdgcn_rcpf(6.0f * g);
+  int c;
+  if (!(q < 464.0f)) {
+    c = 0x7E;
+  } else if (q < 0.015625f) {
+    c = (int)__builtin_rintf(q * 512.0f);
+  } else {
+    const int e = __builtin_amdgcn_frexp_expf(q) - 1;     // q in [2^e, 2^(e+1))
+    const float r = __builtin_rintf(__builtin_ldexpf(q, 3 - e));
+    c = min((e + 6) * 8 + (int)r, 0x7E);
+  }
+  int up = 0, down = 0;
+  if (c < 0x7E) {  // beyond the midpoint to c + 1 (ties to the even code)
+    const float M = 3.0f * (e4m3_value((uint32_t)c) + e4m3_value((uint32_t)c + 1u));
+    const int r = cmp_scaled(amax, g, M);
+    up = r > 0 || (r == 0 && ((c + 1) & 1) == 0);
+  }
+  if (c > 0) {     // below the midpoint to c - 1
+    const float M = 3.0f * (e4m3_value((uint32_t)c - 1u) + e4m3_value((uint32_t)c));
+    const int r = cmp_scaled(amax, g, M);
+    down = r < 0 || (r == 0 && (c & 1) == 1);
+  }
+  return (uint32_t)(c + up - down);
 }
 
 // The seven decision boundaries between consecutive E2M1 magnitudes
 // {0, .5, 1, 1.5, 2, 3, 4, 6} for block scale s and global scale g, as
-// floats c[i] such that  magnitude code = #{ i : |x| > c[i] }.
-// The real boundaries are t_i * s * g with t = .25 .75 1.25 1.75 2.5 3.5 5;
-// they have at most 31 significant bits, so they are exact in FP64.  A tie
-// goes to the even code: up at .75, 1.75, 3.5 and down at the others.
+// floats c[i] such that  magnitude code = #{ i : xs * |x| > c[i] }.
+// The real boundaries are b_i = t_i * s * g with t = .25 .75 1.25 1.75 2.5
+// 3.5 5.  A tie goes to the even code: up at .75, 1.75, 3.5 (c = the float
+// below RU(b), so |x| > c <=> |x| >= b) and down at the others (c = RD(b),
+// so |x| > c <=> |x| > b).  With b = p + e split exactly (t * s has at most
+// 7 significant bits): RD(b) = p if e >= 0 else the float below p, and the
+// float below RU(b) = p if e > 0 else the float below p.  For g < 2^-80 the
+// bounds are those of 2^64 g and xs = 2^64 lifts |x| the same way (exact).
 struct E2M1Bounds {
   float c0, c1, c2, c3, c4, c5, c6;
+  float xs;
 };
+__device__ __forceinline__ float bound_rd(float g, float T) {
+  const float p = g * T, e = __builtin_fmaf(g, T, -p);
+  return e >= 0.0f ? p : __int_as_float(__float_as_int(p) - 1);
+}
+__device__ __forceinline__ float bound_below_ru(float g, float T) {
+  const float p = g * T, e = __builtin_fmaf(g, T, -p);
+  return e > 0.0f ? p : __int_as_float(__float_as_int(p) - 1);
+}
 __device__ __forceinline__ E2M1Bounds e2m1_bounds(float s, float g) {
-  const double t = (double)s * (double)g;
   E2M1Bounds b;
-  b.c0 = f32_round_down(0.25 * t);
-  b.c1 = f32_below_round_up(0.75 * t);
-  b.c2 = f32_round_down(1.25 * t);
-  b.c3 = f32_below_round_up(1.75 * t);
-  b.c4 = f32_round_down(2.5 * t);
-  b.c5 = f32_below_round_up(3.5 * t);
-  b.c6 = f32_round_down(5.0 * t);
+  b.xs = 1.0f;
+  if (g < kTinyG) {
+    g *= kLift;
+    b.xs = kLift;
+  }
+  b.c0 = bound_rd(g, 0.25f * s);
+  b.c1 = bound_below_ru(g, 0.75f * s);
+  b.c2 = bound_rd(g, 1.25f * s);
+  b.c3 = bound_below_ru(g, 1.75f * s);
+  b.c4 = bound_rd(g, 2.5f * s);
+  b.c5 = bound_below_ru(g, 3.5f * s);
+  b.c6 = bound_rd(g, 5.0f * s);
   return b;
 }
 // Magnitude code (0..7) of |x| by a three-level search over the bounds.
@@ -128,7 +173,7 @@ __device__ __forceinline__ uint32_t e2m1_mag_code(float a, const E2M1Bounds& b) 
 // Full 4-bit code of x (sign from the IEEE sign bit; s == 0 -> magnitude 0).
 __device__ __forceinline__ uint32_t e2m1_code(float x, const E2M1Bounds& b, bool zero_scale) {
   const uint32_t sign = ((uint32_t)__float_as_int(x) >> 28) & 8u;
-  const uint32_t mag = zero_scale ? 0u : e2m1_mag_code(fabsf(x), b);
+  const uint32_t mag = zero_scale ? 0u : e2m1_mag_code(fabsf(x) * b.xs, b);
   return sign | mag;
 }
 

@@ -48,6 +48,9 @@ namespace {
 #ifndef NVFP4_STREAM_NTW
 #define NVFP4_STREAM_NTW 2     // 16-column tiles per work unit, streaming kernel
 #endif
+#ifndef NVFP4_WIDE_MIN_LIST
+#define NVFP4_WIDE_MIN_LIST 2  // smallest tile list (by mean rows/expert) sent to the wide kernel
+#endif
 #ifndef NVFP4_STREAM_PFMAX
 #define NVFP4_STREAM_PFMAX 4   // deepest ring of the streaming kernel (128-k chunks)
 #endif
@@ -172,6 +175,92 @@ __device__ __forceinline__ void epilogue(const KParams& p, f32x4 (&acc)[MT][NTW]
           }
         }
       }
+  }
+}
+
+// Block-major epilogue of the SwiGLU GEMM1 variants for a wavefront's
+// 16*MT rows x 16*NTW streaming columns (NTW/2 blocks of 16 h columns).  In
+// the matrix-instruction layout a 16-element block of a row is spread over
+// 16 lanes, so every lane would repeat the block's scale and bound
+// computation for each of its values.  Instead the h values go through a
+// wave-private LDS area sh ([16*MT][8*NTW] floats) and come back so that each
+// lane owns whole blocks: one scale decision per block, and the codes, scale
+// bytes and 16-bit copies leave as vector stores.
+template <int EPI, int MT, int NTW>
+__device__ __forceinline__ void epilogue_blocks(const KParams& p, f32x4 (&acc)[MT][NTW], int e,
+                                                int row0, int nrows, int n_wave0, int lane,
+                                                float* __restrict__ sh) {
+  static_assert(EPI != kEpiStoreF32, "SwiGLU epilogues only");
+  constexpr int HC = 8 * NTW;                // h columns of the wave
+  constexpr int BLOCKS = 16 * MT * (HC / 16);
+  static_assert(BLOCKS % kWave == 0, "whole blocks per lane");
+  const float alpha = p.g_a ? ld_uniform(p.g_a) * ld_uniform(p.g_w + e) : ld_uniform(p.g_w + e);
+  const int ln = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int q = 0; q < NTW / 2; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float gate = alpha * acc[i][2 * q][r];
+        const float up = alpha * acc[i][2 * q + 1][r];
+        sh[(i * 16 + lg * 4 + r) * HC + q * 16 + ln] = silu(gate) * up;
+      }
+  // (wave-private area: the wave's own LDS writes are ordered before its reads)
+  const int hb0 = n_wave0 >> 5;                // first 16-column block of h
+  const float g2 = (EPI == kEpiSwigluFp4) ? ld_uniform(p.g2) : 0.0f;
+#pragma unroll
+  for (int j = 0; j < BLOCKS / kWave; ++j) {
+    const int blk = lane + kWave * j;
+    const int row = blk / (HC / 16), hb = blk % (HC / 16);
+    const float* src = sh + row * HC + hb * 16;
+    float v[16];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(src + 4 * w);
+      v[4 * w] = x[0];
+      v[4 * w + 1] = x[1];
+      v[4 * w + 2] = x[2];
+      v[4 * w + 3] = x[3];
+    }
+    if (row >= nrows) continue;
+    const int64_t pr = row0 + row;
+    if constexpr (EPI == kEpiSwigluFp4) {
+      float am = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) am = fmaxf(am, fabsf(v[k]));
+      const uint32_t sc = e4m3_scale_code(am, g2);
+      const float sv = e4m3_value(sc);
+      const E2M1Bounds bd = e2m1_bounds(sv, g2);
+      uint32_t w0 = 0, w1 = 0;
+      uint32_t dh[8];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const uint32_t code = e2m1_code(v[k], bd, sc == 0);
+        if (k < 8) w0 |= code << (4 * k);
+        else w1 |= code << (4 * (k - 8));
+        if (p.out_h) {
+          const float dv = e2m1_mag_value(code & 7u) * sv;   // exact in f16
+          const uint32_t hbits = __builtin_bit_cast(uint16_t, (_Float16)((code & 8u) ? -dv : dv));
+          if (k & 1) dh[k >> 1] |= hbits << 16;
+          else dh[k >> 1] = hbits;
+        }
+      }
+      *reinterpret_cast<u32x2*>(p.out_q + pr * (p.I >> 1) + (hb0 + hb) * 8) = u32x2{w0, w1};
+      p.out_sf[pr * (p.I >> 4) + hb0 + hb] = (uint8_t)sc;
+      if (p.out_h) {
+        uint16_t* dst = p.out_h + pr * p.I + (hb0 + hb) * 16;
+        *reinterpret_cast<u32x4*>(dst) = u32x4{dh[0], dh[1], dh[2], dh[3]};
+        *reinterpret_cast<u32x4*>(dst + 8) = u32x4{dh[4], dh[5], dh[6], dh[7]};
+      }
+    } else {
+      uint32_t bw[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) bw[k] = f32_to_bf16_bits(v[2 * k]) | (f32_to_bf16_bits(v[2 * k + 1]) << 16);
+      uint16_t* dst = p.out_h + pr * p.I + (hb0 + hb) * 16;
+      *reinterpret_cast<u32x4*>(dst) = u32x4{bw[0], bw[1], bw[2], bw[3]};
+      *reinterpret_cast<u32x4*>(dst + 8) = u32x4{bw[4], bw[5], bw[6], bw[7]};
+    }
   }
 }
 
@@ -357,6 +446,8 @@ __global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
   load_b(0, bq0, bs0);
   store_a(0);
   __syncthreads();
+  // Every path back to the loop head passes the full wait (the exit tests
+  // come after it), so the compiler knows no load is pending there.
   for (int kc = 0;; kc += 2) {
     const bool more1 = kc + 1 < KC;
     if (more1) {
@@ -366,9 +457,10 @@ __global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
     __builtin_amdgcn_sched_barrier(0);
     compute(0, bq0, bs0);
     __builtin_amdgcn_sched_barrier(0);
-    if (!more1) break;
-    store_a(1);
+    if (more1) store_a(1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (!more1) break;
     const bool more2 = kc + 2 < KC;
     if (more2) {
       load_a(kc + 2);
@@ -377,12 +469,208 @@ __global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
     __builtin_amdgcn_sched_barrier(0);
     compute(1, bq1, bs1);
     __builtin_amdgcn_sched_barrier(0);
-    if (!more2) break;
-    store_a(0);
+    if (more2) store_a(0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (!more2) break;
   }
   if (!wave_on) return;
   epilogue<EPI, MT, NTW>(p, acc, t.e, t.row0, t.nrows, n_wave0, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Wide kernel for 128-row tiles with 16-bit activations (the exact f16 copy
+// of NVFP4 codes, or bf16 for W4A16): the prefill regime, bound by the
+// matrix instructions and by weight decoding.  A workgroup computes 128 rows
+// x 256 columns; each of its 4 wavefronts owns 64 columns for all 128 rows,
+// so every decoded weight fragment feeds 8 matrix instructions and every
+// activation fragment read from LDS feeds 4.  Activation chunks (128 rows x
+// 128 k) move from memory to LDS with the direct-to-LDS loads of gfx950 (no
+// registers, no VALU), double-buffered; the 16-byte units of a row are
+// XOR-swizzled by the row so that the 16 rows of a fragment read fall in
+// distinct banks.  Weights stream into two register sets used alternately.
+// ---------------------------------------------------------------------------
+constexpr int kWideBM = 128, kWideWN = 64, kWideNW = 4;
+
+template <int AK, int EPI>
+__global__ __launch_bounds__(kWideNW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void grouped_gemm_wide_kernel(KParams p) {
+  static_assert(AK != kActCodes, "the wide kernel takes 16-bit activations");
+  constexpr int MT = kWideBM / 16, NTW = kWideWN / 16, NW = kWideNW;
+  constexpr int ROW_BYTES = kBK * 2;                       // 256
+  constexpr int BUF_BYTES = kWideBM * ROW_BYTES;           // 32 KiB
+  constexpr int LOADS = BUF_BYTES / (NW * kWave * 16);     // direct loads per thread per chunk: 8
+  // Two separate arrays (not one array of two halves): the compiler can then
+  // tell that reads of one buffer do not alias the direct loads filling the
+  // other, and does not drain the loads before every read.
+  __shared__ __attribute__((aligned(16))) uint8_t As0[BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t As1[BUF_BYTES];
+
+  Tile t;
+  if (!decode_tile(p, t)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_wave0 = (t.nb * NW + wv) * kWideWN;
+  const bool wave_on = n_wave0 < p.N;
+  const int K = p.K, KC = K / kBK, NT = p.N / 16;
+
+  // ---- A staging.  Load q of wave wv fills LDS bytes [(wv*LOADS+q) KiB, +1 KiB)
+  // of a buffer: rows 4(wv*LOADS+q) + lane/16, LDS unit lane%16, which holds
+  // source unit (lane%16) ^ (row%16) of the row.  Rows past the tile end
+  // repeat its last valid row (their results are never stored).
+  uint32_t a_off[LOADS];
+  int src[LOADS];
+#pragma unroll
+  for (int q = 0; q < LOADS; ++q) src[q] = t.row0 + min(4 * (wv * LOADS + q) + (lane >> 4), t.nrows - 1);
+  if (p.sorted_pair) {
+    int f[LOADS];  // all gathers in flight together
+#pragma unroll
+    for (int q = 0; q < LOADS; ++q) f[q] = p.sorted_pair[src[q]];
+#pragma unroll
+    for (int q = 0; q < LOADS; ++q) src[q] = pair_token(f[q], p.T, p.topk);
+  }
+#pragma unroll
+  for (int q = 0; q < LOADS; ++q) {
+    const int r = 4 * (wv * LOADS + q) + (lane >> 4);
+    const int unit = (lane & 15) ^ (r & 15);
+    a_off[q] = (uint32_t)src[q] * (uint32_t)(K * 2) + (uint32_t)unit * 16u;
+  }
+  const uint8_t* a_base = reinterpret_cast<const uint8_t*>(p.a_h);
+  // The direct loads are issued as assembly: the compiler treats a
+  // direct-to-LDS load as a pending write that any later LDS read may alias
+  // and drains the load counter before every read, which would serialise the
+  // prefetch of chunk kc + 1 with the compute of chunk kc.  Completion is
+  // awaited explicitly (lds_fill_wait) before the barrier that publishes a
+  // buffer.
+  auto stage_a = [&](int kc, uint8_t* buf) {
+#pragma unroll
+    for (int q = 0; q < LOADS; ++q) {
+      const uint32_t lds = (uint32_t)(uintptr_t)(buf + (wv * LOADS + q) * 1024);
+      const uint32_t voff = a_off[q] + (uint32_t)kc * ROW_BYTES;
+      asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(a_base), "{m0}"(lds) : "memory");
+    }
+  };
+  // (builtin, not assembly: the compiler must see that every load, its own
+  // included, has completed, or it re-waits before reusing load registers)
+  auto lds_fill_wait = [] { __builtin_amdgcn_s_waitcnt(0); };
+
+  // ---- B (weights), two register sets.
+  const int nt0 = n_wave0 >> 4;
+  const int64_t wbase = ((int64_t)(t.e * NT + nt0) * KC) * kWave + lane;
+  const int64_t sbase = ((int64_t)(t.e * (NT >> 1) + (nt0 >> 1)) * KC) * kWave + lane;
+  u32x4 bq0[NTW], bq1[NTW];
+  uint32_t bs0[NTW / 2], bs1[NTW / 2];
+  auto load_b = [&](int kc, u32x4 (&bq)[NTW], uint32_t (&bs)[NTW / 2]) {
+    if (!wave_on) return;
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+      bq[j] = *reinterpret_cast<const u32x4*>(p.w_q + (wbase + ((int64_t)j * KC + kc) * kWave) * 16);
+#pragma unroll
+    for (int j = 0; j < NTW / 2; ++j)
+      bs[j] = *reinterpret_cast<const uint32_t*>(p.w_sf + (sbase + ((int64_t)j * KC + kc) * kWave) * 4);
+  };
+
+  f32x4 acc[MT][NTW];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Fragment read: lane (m = lane%16, g = lane/16) takes row i*16 + m, k in
+  // [32g + 8s, 32g + 8s + 8), i.e. source unit 4g + s, stored at unit
+  // (4g + s) ^ m of the row.
+  const int m = lane & 15, g = lane >> 4;
+  auto compute = [&](const uint8_t* buf, const u32x4 (&bq)[NTW], const uint32_t (&bs)[NTW / 2]) {
+    if (!wave_on) return;
+    const uint8_t* abuf = buf + m * ROW_BYTES;
+    if constexpr (AK == kActF16) {
+      f16x2 sb2[NTW];
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) sb2[j] = e4m3x2_to_f16x2(bs[j >> 1] >> ((j & 1) * 16));
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        f16x8 bf[NTW];
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) bf[j] = weight_f16(bq[j][s], sb2[j], s);
+        const int ucol = ((4 * g + s) ^ m) * 16;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          const f16x8 af = *reinterpret_cast<const f16x8*>(abuf + i * 16 * ROW_BYTES + ucol);
+#pragma unroll
+          for (int j = 0; j < NTW; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[j], acc[i][j], 0, 0, 0);
+        }
+      }
+    } else {
+      float sb[NTW][2];
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const uint32_t w = bs[j >> 1] >> ((j & 1) * 16);
+        sb[j][0] = e4m3_value(w & 0xFFu);
+        sb[j][1] = e4m3_value((w >> 8) & 0xFFu);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bf16x8 bf[NTW];
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) bf[j] = dequant8_bf16(bq[j][s], sb[j][s >> 1]);
+        const int ucol = ((4 * g + s) ^ m) * 16;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          const bf16x8 af = *reinterpret_cast<const bf16x8*>(abuf + i * 16 * ROW_BYTES + ucol);
+#pragma unroll
+          for (int j = 0; j < NTW; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // ---- Pipeline (as in the LDS-staged kernel): chunk kc computes from LDS
+  // buffer kc & 1 and register set kc & 1 while chunk kc + 1 lands; the
+  // direct loads are complete once the vector counter drains, then one
+  // barrier per chunk publishes the buffer.
+  stage_a(0, As0);
+  load_b(0, bq0, bs0);
+  lds_fill_wait();
+  __syncthreads();
+  // Every path back to the loop head passes the full wait (the exit tests
+  // come after it), so the compiler knows no load is pending there and does
+  // not drain the counter before the next refills.
+  for (int kc = 0;; kc += 2) {
+    const bool more1 = kc + 1 < KC;
+    if (more1) {
+      stage_a(kc + 1, As1);
+      load_b(kc + 1, bq1, bs1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(As0, bq0, bs0);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_fill_wait();
+    __syncthreads();
+    if (!more1) break;
+    const bool more2 = kc + 2 < KC;
+    if (more2) {
+      stage_a(kc + 2, As0);
+      load_b(kc + 2, bq0, bs0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(As1, bq1, bs1);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_fill_wait();
+    __syncthreads();
+    if (!more2) break;
+  }
+  if (!wave_on) return;
+  if constexpr (EPI == kEpiStoreF32) {
+    epilogue<EPI, MT, NTW>(p, acc, t.e, t.row0, t.nrows, n_wave0, lane);
+  } else {
+    // The activation buffers are free (the loop ended on a barrier after the
+    // last reads): each wavefront takes 16 KiB of them for the epilogue.
+    static_assert(kWideBM * 8 * NTW * 4 * NW == 2 * BUF_BYTES, "epilogue area = both buffers");
+    float* sh = reinterpret_cast<float*>((wv < 2 ? As0 : As1) + (wv & 1) * (BUF_BYTES / 2));
+    epilogue_blocks<EPI, MT, NTW>(p, acc, t.e, t.row0, t.nrows, n_wave0, lane, sh);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -644,6 +932,15 @@ int pick_list(int64_t P, int slots) {
   return 3;
 }
 
+template <int AK, int EPI>
+hipError_t launch_wide(KParams kp, int list_len, hipStream_t s) {
+  kp.n_blocks = (kp.N + kWideNW * kWideWN - 1) / (kWideNW * kWideWN);
+  const int64_t G = (int64_t)list_len * kp.n_blocks;
+  const int64_t grid = std::max<int64_t>(8, (G + 7) / 8 * 8);
+  grouped_gemm_wide_kernel<AK, EPI><<<(unsigned)grid, kWideNW * kWave, 0, s>>>(kp);
+  return hipGetLastError();
+}
+
 template <int AK, int EPI, int BM, int WN>
 hipError_t launch_lds(KParams kp, int list_len, hipStream_t s) {
   constexpr int NW = NVFP4_BIG_NW;
@@ -709,6 +1006,13 @@ hipError_t launch_gemm(KParams kp, const AlignShape& al, hipStream_t s) {
   const bool offsets_fit = kp.a_rows * a_row_bytes < (int64_t(1) << 31) &&
                            (int64_t)kp.N * kp.K / 2 < (int64_t(1) << 31);
   if (li <= 1 && !offsets_fit) li = 2;
+  // 16-bit activations on tall tiles: the wide kernel (128-row tiles).
+  if constexpr (AK != kActCodes) {
+    if (li >= NVFP4_WIDE_MIN_LIST && offsets_fit) {
+      kp.list_idx = 3;
+      return launch_wide<AK, EPI>(kp, (int)al.list_len[3], s);
+    }
+  }
   kp.list_idx = li;
   const int len = (int)al.list_len[li];
   switch (li) {
@@ -730,6 +1034,11 @@ KParams base_params(const GemmArgs& a) {
 }
 
 }  // namespace
+
+bool prefers_decoded(int T, int topk, int E, int shared) {
+  const AlignShape al = align_shape(T, topk, E, shared);
+  return min(pick_list(al.P, al.slots), 3) >= NVFP4_WIDE_MIN_LIST;
+}
 
 hipError_t launch_gemm1(const GemmArgs& a, bool w4a4, hipStream_t s) {
   const AlignShape al = align_shape(a.T, a.topk, a.E, a.shared);

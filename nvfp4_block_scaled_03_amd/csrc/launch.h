@@ -81,6 +81,9 @@ struct GemmArgs {
   int out_dtype;
 };
 hipError_t launch_gemm1(const GemmArgs& a, bool w4a4, hipStream_t s);
+// Whether the W4A4 GEMMs run faster on the exact f16 activation copies than
+// on the codes for these dimensions (the wide 128-row-tile kernel).
+bool prefers_decoded(int T, int topk, int E, int shared);
 hipError_t launch_gemm2_combine(const GemmArgs& a, bool w4a4, hipStream_t s);
 
 }  // namespace nvfp4

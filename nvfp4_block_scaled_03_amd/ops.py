@@ -233,11 +233,11 @@ class MoELayer:
     call launches kernels only (and can be captured in a HIP graph)."""
 
     def __init__(self, d: Dims, weights: ExpertWeights, g2: torch.Tensor, device="cuda",
-                 decoded_copies: bool = False):
+                 decoded_copies: Optional[bool] = None):
         """``decoded_copies``: W4A4 keeps exact f16 copies of a1 and a2 next to
         their codes and the GEMMs read those instead of decoding the codes.
-        Off by default: on MI355X the 4x larger activation reads cost more
-        than the decoding they save at the measured shapes."""
+        None (default) asks the library which is faster for these dims (the
+        copies pay off for tall tiles, not for decode-sized batches)."""
         self.d = d
         self.w = weights
         self.g2 = g2
@@ -256,6 +256,9 @@ class MoELayer:
         self.a2_sf = torch.empty(max(P, 1), d.I // 16, dtype=torch.uint8, device=dev)
         self.a2_bf16 = torch.empty(max(P, 1), d.I, dtype=torch.bfloat16, device=dev)
         self.a1_deq = self.a2_deq = None
+        if decoded_copies is None:
+            decoded_copies = bool(lib.grouped_gemm_prefers_decoded(ctypes.byref(d)))
+        self.decoded_copies = decoded_copies
         if decoded_copies:
             self.a1_deq = torch.empty(max(d.T, 1), d.H, dtype=torch.float16, device=dev)
             self.a2_deq = torch.empty(max(P, 1), d.I, dtype=torch.float16, device=dev)

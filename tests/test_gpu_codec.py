@@ -178,3 +178,31 @@ def test_decoded_copy_covers_every_code_and_scale(dev):
     assert np.array_equal(to_np(sf), s_ref)
     assert np.array_equal(to_np(q), onv.pack_codes(c_ref))
     assert np.array_equal(to_np(deq).astype(np.float64), onv.dequantize(c_ref, s_ref, 1.0))
+
+
+def test_scale_decisions_at_every_midpoint(dev):
+    """Block amax exactly at 6*g*m for every E4M3 midpoint m, and one float
+    below and above, for global scales of many magnitudes: the FP32 decision
+    path must agree with the oracle's exact-real rounding everywhere."""
+    mids = (onv.E4M3_POS[:-1] + onv.E4M3_POS[1:]) / 2
+    gs = [np.float32(2.0 ** k * f) for k in (-30, -7, -1, 0, 3, 20) for f in (1.0, 1.1, 1.37, 1.9999)]
+    rows, grow = [], []
+    for g in gs:
+        for m in mids:
+            t = np.float32(6.0 * float(g) * float(m))
+            for a in (np.nextafter(t, np.float32(0)), t, np.nextafter(t, np.float32(np.inf))):
+                blk = np.zeros(16)
+                blk[0] = float(a)
+                blk[5] = float(np.float32(float(a) * 0.3))
+                rows.append(blk)
+                grow.append(g)
+    x = np.array(rows)
+    assert np.array_equal(x.astype(np.float32).astype(np.float64), x)
+    xt = torch.tensor(x, dtype=torch.float32, device=dev)
+    gt = torch.tensor(grow, dtype=torch.float32, device=dev)
+    q, sf = ops.quantize(xt, gt, rows_per_g=1)
+    q, sf = to_np(q), to_np(sf)
+    for r in range(len(rows)):
+        c, s = onv.quantize(x[r:r + 1], grow[r])
+        assert sf[r, 0] == s[0, 0], (r, grow[r], x[r, 0])
+        assert np.array_equal(q[r:r + 1], onv.pack_codes(c)), r

@@ -29,6 +29,9 @@ SMALL = [
     Workload("s32", 100, 256, 128, 8, 2, 0, 0.0, 0.02, 0.01, 12),
     Workload("s64", 200, 512, 256, 6, 2, 0, 0.5, 0.02, 0.01, 13),
     Workload("s128", 600, 256, 384, 4, 2, 1, 0.0, 0.02, 0.01, 14),
+    # odd chunk counts (K = 384, 640) and a GEMM2 width (384) that leaves half
+    # of the last 256-column block idle
+    Workload("s128b", 300, 384, 640, 3, 1, 0, 0.0, 0.02, 0.01, 15),
 ]
 
 
@@ -172,7 +175,7 @@ def test_w4a16_stages(dev, w):
 
 
 # ---------------------------------------------------------------- whole layer
-def _run_layer(case: Case, dev, variant, decoded_copies=False):
+def _run_layer(case: Case, dev, variant, decoded_copies=None):
     g2 = torch.tensor([float(case.g2)], device=dev)
     layer = ops.MoELayer(case.d, case.wq, g2, device=dev, decoded_copies=decoded_copies)
     out32 = layer.forward(case.x, case.ids, case.tw, variant, out_dtype=torch.float32).clone()
@@ -181,7 +184,7 @@ def _run_layer(case: Case, dev, variant, decoded_copies=False):
     return layer, out32, out16
 
 
-def _judge_layer(case: Case, dev, variant, decoded_copies=False):
+def _judge_layer(case: Case, dev, variant, decoded_copies=None):
     ref = case.oracle(variant)
     layer, out32, out16 = _run_layer(case, dev, variant, decoded_copies)
     assert torch.equal(out16, out32.to(torch.bfloat16)), "bf16 output != bf16(f32 output)"
@@ -219,15 +222,17 @@ def test_layer_small(dev, w, variant):
     _judge_layer(Case(w, dev), dev, variant)
 
 
+@pytest.mark.parametrize("decoded", [True, False], ids=["decoded", "codes"])
 @pytest.mark.parametrize("w", SMALL + [moe_inputs.WORKLOADS["tiny"]], ids=lambda w: w.name)
-def test_layer_small_decoded_copies(dev, w):
-    """W4A4 with the exact f16 activation copies read by the GEMMs."""
-    _judge_layer(Case(w, dev), dev, "w4a4", decoded_copies=True)
+def test_layer_small_activation_paths(dev, w, decoded):
+    """W4A4 with the GEMMs reading the exact f16 activation copies, and with
+    them decoding the codes themselves."""
+    _judge_layer(Case(w, dev), dev, "w4a4", decoded_copies=decoded)
 
 
-FULL = [("decode", "w4a4", 8, False), ("decode", "w4a4", 4, True), ("decode", "w4a16", 8, False),
-        ("prefill", "w4a4", 4, False), ("prefill", "w4a4", 2, True), ("large_e", "w4a4", 3, False),
-        ("skew", "w4a4", 4, False), ("skew", "w4a16", 4, False)]
+FULL = [("decode", "w4a4", 8, None), ("decode", "w4a4", 4, True), ("decode", "w4a16", 8, None),
+        ("prefill", "w4a4", 4, None), ("prefill", "w4a4", 2, False), ("large_e", "w4a4", 3, None),
+        ("skew", "w4a4", 4, None), ("skew", "w4a16", 4, None)]
 
 
 @pytest.mark.parametrize("name,variant,n_tok,decoded", FULL, ids=lambda v: str(v))
