@@ -188,6 +188,22 @@ def time_gemm1(layer, x, ids, tw, copies, variant, n=50):
     return e0.elapsed_time(e1) / n
 
 
+def measured_traffic(workload: str, variant: str):
+    """HBM bytes per GEMM1 launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when there
+    is none for this workload or the kernel sources changed since it was taken."""
+    from nvfp4_block_scaled_03_amd import profiling
+    if variant != "w4a4":
+        return None
+    path = os.path.join(ROOT, "profiles", f"grouped_gemm1_swiglu_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    t = profiling.read_traffic(path)
+    if t.get("sources_sha256_16") != profiling.sources_hash():
+        return None
+    return int(float(t["bytes_per_launch"]))
+
+
 def measure(w, d, x, ids, tw, wq, g2, a, steps, warmup):
     """Step time, GEMM1 time and the derived figures for one batch shape."""
     P = w.pairs
@@ -207,7 +223,8 @@ def measure(w, d, x, ids, tw, wq, g2, a, steps, warmup):
     if decode_like:
         ach = g1_bytes / (g1_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(w.name, a.variant)}
     else:
         ach = g1_flops / (g1_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_F16_PEAK_TFLOPS,

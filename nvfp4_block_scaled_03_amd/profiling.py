@@ -1,0 +1,176 @@
+"""Programs and summaries for rocprofv3 runs of the hot path.
+
+    python -m nvfp4_block_scaled_03_amd.profiling gemm1 [--workload decode] [--reps 5]
+        Launch GEMM1 (W4A4) of the named layer ``reps`` times, weight copies
+        rotated as in bench.py (the kernel to collect counters for).
+    python -m nvfp4_block_scaled_03_amd.profiling copy [--mib 1024] [--reps 3]
+        A plain device-to-device copy of a known size (counter calibration:
+        FETCH_SIZE / WRITE_SIZE per dispatch against the bytes really moved).
+    python -m nvfp4_block_scaled_03_amd.profiling traffic --fetch F.csv --write W.csv
+        --copy-fetch CF.csv --copy-write CW.csv --mib 1024 --kernel NAME --workload decode
+        --command "..." > profiles/<kernel>_<workload>_traffic.txt
+        Summarise two counter runs of the kernel and two of the copy into the
+        HBM bytes per launch (counter readings scaled by the copy calibration)
+        and record the hash of the kernel sources the counters belong to.
+
+bench.py reads the traffic summary and reports it only while the sources
+still hash to the recorded value (a changed kernel invalidates the counters).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import os
+import re
+import sys
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+# Sources whose change invalidates recorded counters of the GEMM kernels.
+HASHED = ["csrc/gemm.hip", "csrc/common.h", "csrc/launch.h", "csrc/prep.hip"]
+
+
+def sources_hash() -> str:
+    h = hashlib.sha256()
+    for rel in HASHED:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _per_dispatch(path: str, counter: str, name_re: str):
+    """Mean counter value per dispatch (KiB for *_SIZE) of kernels matching name_re."""
+    vals = defaultdict(float)
+    names = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter or not re.search(name_re, r["Kernel_Name"]):
+                continue
+            d = r["Dispatch_Id"]
+            vals[d] += float(r["Counter_Value"])
+            names[d] = r["Kernel_Name"]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for /{name_re}/ in {path}")
+    return sum(vals.values()) / len(vals), len(vals), sorted(set(names.values()))
+
+
+def read_traffic(path: str):
+    """Parse a traffic summary: dict with bytes_per_launch, fetch/write bytes, hash."""
+    out = {}
+    with open(path) as f:
+        for line in f:
+            m = re.match(r"\s*([a-z0-9_]+)\s*=\s*(\S+)", line)
+            if m:
+                out[m.group(1)] = m.group(2)
+    return out
+
+
+def _cmd_gemm1(a):
+    import torch
+    sys.path.insert(0, ROOT)
+    import bench
+    import moe_inputs
+    from nvfp4_block_scaled_03_amd import ops
+    dev = torch.device("cuda:0")
+    w = moe_inputs.WORKLOADS[a.workload]
+    d, x, ids, tw, wq, g2 = bench.build_layer(w, dev)
+    copies = bench.weight_copies(wq, 4)
+    layer = ops.MoELayer(d, wq, g2, device=dev)
+    layer.forward(x, ids, tw, "w4a4")
+    torch.cuda.synchronize()
+    for i in range(a.reps):
+        layer.gemm1("w4a4", copies[i % len(copies)], x)
+    torch.cuda.synchronize()
+    print(f"gemm1 {a.workload}: {a.reps} launches", flush=True)
+
+
+def _cmd_copy(a):
+    import torch
+    n = a.mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(a.reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copy {a.mib} MiB x {a.reps}", flush=True)
+
+
+def _cmd_traffic(a):
+    f_kib, n_f, names = _per_dispatch(a.fetch, "FETCH_SIZE", a.kernel_re)
+    w_kib, n_w, _ = _per_dispatch(a.write, "WRITE_SIZE", a.kernel_re)
+    cf_kib, _, cnames = _per_dispatch(a.copy_fetch, "FETCH_SIZE", a.copy_re)
+    cw_kib, _, _ = _per_dispatch(a.copy_write, "WRITE_SIZE", a.copy_re)
+    moved = float(a.mib << 20)
+    f_scale = moved / (cf_kib * 1024.0)
+    w_scale = moved / (cw_kib * 1024.0)
+    fetch_b = f_kib * 1024.0 * f_scale
+    write_b = w_kib * 1024.0 * w_scale
+    print(f"# HBM traffic of {a.kernel} ({a.workload}), rocprofv3 counter collection")
+    print(f"# command (kernel, per counter): {a.command}")
+    print(f"# calibration: plain copy of {a.mib} MiB (reads {a.mib} MiB, writes {a.mib} MiB)")
+    print(f"# kernels matched: {'; '.join(n[:90] for n in names)}")
+    print(f"# copy kernel: {'; '.join(n[:90] for n in cnames)}")
+    print(f"kernel = {a.kernel}")
+    print(f"workload = {a.workload}")
+    print(f"dispatches_fetch = {n_f}")
+    print(f"dispatches_write = {n_w}")
+    print(f"fetch_size_kib_per_dispatch = {f_kib:.1f}")
+    print(f"write_size_kib_per_dispatch = {w_kib:.1f}")
+    print(f"copy_fetch_size_kib = {cf_kib:.1f}")
+    print(f"copy_write_size_kib = {cw_kib:.1f}")
+    print(f"fetch_scale = {f_scale:.4f}")
+    print(f"write_scale = {w_scale:.4f}")
+    print(f"fetch_bytes_per_launch = {fetch_b:.0f}")
+    print(f"write_bytes_per_launch = {write_b:.0f}")
+    print(f"bytes_per_launch = {fetch_b + write_b:.0f}")
+    print(f"sources_sha256_16 = {sources_hash()}")
+
+
+def _cmd_stats(a):
+    rows = []
+    with open(a.csv) as f:
+        for r in csv.DictReader(f):
+            rows.append((r["Name"], int(r["Calls"]), float(r["TotalDurationNs"]), float(r["AverageNs"]),
+                         float(r["MinNs"]), float(r["MaxNs"])))
+    total = sum(r[2] for r in rows)
+    print(f"# rocprofv3 --kernel-trace --stats summary ({a.title})")
+    print(f"# command: {a.command}")
+    print(f"# {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'share':>6}  kernel")
+    for name, calls, tot, avg, mn, mx in sorted(rows, key=lambda r: -r[2])[:a.top]:
+        short = re.sub(r"\(anonymous namespace\)::", "", name)
+        short = re.sub(r"\(nvfp4::KParams\)|\(.*$", "", short)[:100]
+        print(f"  {calls:6d} {avg / 1e3:9.2f} {mn / 1e3:9.2f} {mx / 1e3:9.2f} {100 * tot / total:5.1f}%  {short}")
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser()
+    sub = p.add_subparsers(dest="cmd", required=True)
+    g = sub.add_parser("gemm1")
+    g.add_argument("--workload", default="decode")
+    g.add_argument("--reps", type=int, default=5)
+    c = sub.add_parser("copy")
+    c.add_argument("--mib", type=int, default=1024)
+    c.add_argument("--reps", type=int, default=3)
+    t = sub.add_parser("traffic")
+    for k in ("fetch", "write", "copy_fetch", "copy_write"):
+        t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
+    t.add_argument("--mib", type=int, default=1024)
+    t.add_argument("--kernel", default="grouped_gemm1_swiglu")
+    t.add_argument("--kernel-re", dest="kernel_re", default=r"grouped_gemm_stream\d?_kernel<0, 0,")
+    t.add_argument("--copy-re", dest="copy_re", default=r"copy|Copy")
+    t.add_argument("--workload", default="decode")
+    t.add_argument("--command", default="")
+    st = sub.add_parser("stats")
+    st.add_argument("--csv", required=True)
+    st.add_argument("--title", default="")
+    st.add_argument("--command", default="")
+    st.add_argument("--top", type=int, default=16)
+    a = p.parse_args(argv)
+    {"gemm1": _cmd_gemm1, "copy": _cmd_copy, "traffic": _cmd_traffic, "stats": _cmd_stats}[a.cmd](a)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,42 @@
+"""Host-side checks of the profiling summaries (CPU only)."""
+import os
+
+from nvfp4_block_scaled_03_amd import profiling
+
+ROOT = os.path.dirname(os.path.dirname(__file__))
+
+
+def test_committed_traffic_summary_parses():
+    path = os.path.join(ROOT, "profiles", "grouped_gemm1_swiglu_decode_traffic.txt")
+    t = profiling.read_traffic(path)
+    for k in ("bytes_per_launch", "fetch_scale", "write_scale", "sources_sha256_16"):
+        assert k in t, k
+    fetch, write = float(t["fetch_bytes_per_launch"]), float(t["write_bytes_per_launch"])
+    assert float(t["bytes_per_launch"]) == round(fetch) + round(write) or \
+        abs(float(t["bytes_per_launch"]) - fetch - write) <= 1
+    assert len(t["sources_sha256_16"]) == 16
+
+
+def test_traffic_summary_from_counter_rows(tmp_path, capsys):
+    def write(name, counter, rows):
+        p = tmp_path / name
+        with open(p, "w") as f:
+            f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+            for d, k, v in rows:
+                f.write(f'{d},"{k}",{counter},{v}\n')
+        return str(p)
+    k = "void nvfp4::grouped_gemm_stream4_kernel<0, 0, 1, 2, 4>(KParams)"
+    # Two dispatches of the kernel, one counter row per XCD piece summed.
+    f = write("f.csv", "FETCH_SIZE", [(1, k, 100.0), (1, k, 28.0), (2, k, 128.0), (3, "other", 9.0)])
+    w = write("w.csv", "WRITE_SIZE", [(1, k, 4.0), (2, k, 4.0)])
+    cf = write("cf.csv", "FETCH_SIZE", [(7, "__amd_rocclr_copyBuffer", 512.0)])
+    cw = write("cw.csv", "WRITE_SIZE", [(7, "__amd_rocclr_copyBuffer", 1024.0)])
+    profiling.main(["traffic", "--fetch", f, "--write", w, "--copy-fetch", cf, "--copy-write", cw,
+                    "--mib", "1", "--copy-re", "rocclr_copyBuffer"])
+    out = tmp_path / "s.txt"
+    out.write_text(capsys.readouterr().out)
+    t = profiling.read_traffic(str(out))
+    assert t["dispatches_fetch"] == "2" and float(t["fetch_scale"]) == 2.0
+    assert float(t["fetch_bytes_per_launch"]) == 128 * 1024 * 2
+    assert float(t["write_bytes_per_launch"]) == 4 * 1024
+    assert t["sources_sha256_16"] == profiling.sources_hash()
