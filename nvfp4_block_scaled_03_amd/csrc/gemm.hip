@@ -51,9 +51,6 @@ namespace {
 #ifndef NVFP4_WIDE_MIN_LIST
 #define NVFP4_WIDE_MIN_LIST 2  // smallest tile list (by mean rows/expert) sent to the wide kernel
 #endif
-#ifndef NVFP4_STREAM_PFMAX
-#define NVFP4_STREAM_PFMAX 4   // deepest ring of the streaming kernel (128-k chunks)
-#endif
 
 constexpr int kNW = 4;      // wavefronts per workgroup of the streaming kernel
 constexpr int kBK = 128;    // contraction chunk
@@ -103,6 +100,10 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// The same with the hardware reciprocal (1 ulp) in place of the division.
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // Value of an E2M1 magnitude code 0..7: {0, .5, 1, 1.5, 2, 3, 4, 6}.
 __device__ __forceinline__ float e2m1_mag_value(uint32_t m) {
@@ -264,6 +265,69 @@ __device__ __forceinline__ void epilogue_blocks(const KParams& p, f32x4 (&acc)[M
   }
 }
 
+// Row-group epilogue of the SwiGLU GEMM1 variants for short tiles (the
+// streaming kernel), where often only a few of the 16 * MT rows are valid.
+// In the matrix-instruction layout every lane holds 4 rows, so all four
+// rounds of per-value work would run whatever the row count.  The h values go
+// through a wave-private LDS area sh ([16*MT][2][8*NTW] floats: alpha-scaled
+// gate and up) and come back with round t holding rows 4t..4t+3 (lane group
+// g takes row 4t + g), so SwiGLU and the requantisation run only for the
+// rounds up to the last valid row.  Each 16-lane row group then decides its
+// block scale with a lane reduction, as in epilogue().
+template <int EPI, int MT, int NTW>
+__device__ __forceinline__ void epilogue_rows(const KParams& p, f32x4 (&acc)[MT][NTW], int e,
+                                              int row0, int nrows, int n_wave0, int lane,
+                                              float* __restrict__ sh) {
+  static_assert(EPI != kEpiStoreF32, "SwiGLU epilogues only");
+  constexpr int HC = 8 * NTW;                // h columns of the wave
+  const float alpha = p.g_a ? ld_uniform(p.g_a) * ld_uniform(p.g_w + e) : ld_uniform(p.g_w + e);
+  const int ln = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int q = 0; q < NTW / 2; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float* dst = sh + (i * 16 + lg * 4 + r) * 2 * HC + q * 16 + ln;
+        dst[0] = alpha * acc[i][2 * q][r];
+        dst[HC] = alpha * acc[i][2 * q + 1][r];
+      }
+  // (wave-private area: the wave's own LDS writes are ordered before its reads)
+  const int hb0 = n_wave0 >> 5;                // first 16-column block of h
+  const float g2 = (EPI == kEpiSwigluFp4) ? ld_uniform(p.g2) : 0.0f;
+  const int rounds = (min(nrows, 16 * MT) + 3) >> 2;
+  for (int t = 0; t < rounds; ++t) {
+    const int row = 4 * t + lg;
+#pragma unroll
+    for (int q = 0; q < NTW / 2; ++q) {
+      const float* src = sh + row * 2 * HC + q * 16 + ln;
+      const float h = silu_fast(src[0]) * src[HC];
+      const int64_t pr = row0 + row;
+      if constexpr (EPI == kEpiSwigluFp4) {
+        const float am = row16_max(fabsf(h));
+        const uint32_t sc = e4m3_scale_code(am, g2);
+        const float sv = e4m3_value(sc);
+        const E2M1Bounds bd = e2m1_bounds(sv, g2);
+        const uint32_t code = e2m1_code(h, bd, sc == 0);
+        const uint32_t other = (uint32_t)dpp_xor1_i((int)code);
+        if (row < nrows) {
+          if ((ln & 1) == 0)
+            p.out_q[pr * (p.I >> 1) + (hb0 + q) * 8 + (ln >> 1)] = (uint8_t)(code | (other << 4));
+          if (ln == 0) p.out_sf[pr * (p.I >> 4) + hb0 + q] = (uint8_t)sc;
+          if (p.out_h) {
+            // Exact: six significant bits at most, inside the f16 range.
+            const float dv = e2m1_mag_value(code & 7u) * sv;
+            const _Float16 hv = (_Float16)((code & 8u) ? -dv : dv);
+            p.out_h[pr * p.I + (hb0 + q) * 16 + ln] = __builtin_bit_cast(uint16_t, hv);
+          }
+        }
+      } else {
+        if (row < nrows) p.out_h[pr * p.I + (hb0 + q) * 16 + ln] = (uint16_t)f32_to_bf16_bits(h);
+      }
+    }
+  }
+}
+
 // Work item of a workgroup of the LDS kernel: (expert, first row, valid
 // rows, column block).
 struct Tile {
@@ -374,7 +438,7 @@ __global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
   // in two register sets used alternately.
   const int nt0 = n_wave0 >> 4;
   const int64_t wbase = ((int64_t)(t.e * NT + nt0) * KC) * kWave + lane;
-  const int64_t sbase = ((int64_t)(t.e * (NT >> 1) + (nt0 >> 1)) * KC) * kWave + lane;
+  const uint8_t* s_expert = p.w_sf + (int64_t)t.e * (NT >> 1) * KC * 256;
   u32x4 bq0[NTW], bq1[NTW];
   uint32_t bs0[NTW / 2], bs1[NTW / 2];
   auto load_b = [&](int kc, u32x4 (&bq)[NTW], uint32_t (&bs)[NTW / 2]) {
@@ -384,7 +448,7 @@ __global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
       bq[j] = *reinterpret_cast<const u32x4*>(p.w_q + (wbase + ((int64_t)j * KC + kc) * kWave) * 16);
 #pragma unroll
     for (int j = 0; j < NTW / 2; ++j)
-      bs[j] = *reinterpret_cast<const uint32_t*>(p.w_sf + (sbase + ((int64_t)j * KC + kc) * kWave) * 4);
+      bs[j] = *reinterpret_cast<const uint32_t*>(s_expert + scale_word_offset((nt0 >> 1) + j, kc, KC, lane));
   };
 
   f32x4 acc[MT][NTW];
@@ -557,7 +621,7 @@ void grouped_gemm_wide_kernel(KParams p) {
   // ---- B (weights), two register sets.
   const int nt0 = n_wave0 >> 4;
   const int64_t wbase = ((int64_t)(t.e * NT + nt0) * KC) * kWave + lane;
-  const int64_t sbase = ((int64_t)(t.e * (NT >> 1) + (nt0 >> 1)) * KC) * kWave + lane;
+  const uint8_t* s_expert = p.w_sf + (int64_t)t.e * (NT >> 1) * KC * 256;
   u32x4 bq0[NTW], bq1[NTW];
   uint32_t bs0[NTW / 2], bs1[NTW / 2];
   auto load_b = [&](int kc, u32x4 (&bq)[NTW], uint32_t (&bs)[NTW / 2]) {
@@ -567,7 +631,7 @@ void grouped_gemm_wide_kernel(KParams p) {
       bq[j] = *reinterpret_cast<const u32x4*>(p.w_q + (wbase + ((int64_t)j * KC + kc) * kWave) * 16);
 #pragma unroll
     for (int j = 0; j < NTW / 2; ++j)
-      bs[j] = *reinterpret_cast<const uint32_t*>(p.w_sf + (sbase + ((int64_t)j * KC + kc) * kWave) * 4);
+      bs[j] = *reinterpret_cast<const uint32_t*>(s_expert + scale_word_offset((nt0 >> 1) + j, kc, KC, lane));
   };
 
   f32x4 acc[MT][NTW];
@@ -682,26 +746,68 @@ void grouped_gemm_wide_kernel(KParams p) {
 // the ring does not drain between units: the last round of a unit refills
 // the slots with the first chunks of the wavefront's next unit.  Activation
 // fragments ride in the ring beside the weights, in the weights' lane layout
-// (lane 16g + m holds row m, k in [32g, 32g + 32) of a chunk), so wavefronts
-// share nothing: no LDS, no barriers.
+// (lane 16g + m holds row m, k in [32g, 32g + 32) of a chunk).
+//
+// NVFP4 codes are decoded by every wavefront that uses them.  16-bit
+// activations (the exact f16 copy, or bf16) need no decoding, and the four
+// wavefronts of a workgroup always work on the same tile (the unit count per
+// tile and the wavefront stride are multiples of four): each loads four of
+// the tile's 16 rows of the chunk (256 contiguous bytes per row, so every
+// load is coalesced), stores them in LDS, and after one barrier all four read
+// their fragments from there.  The LDS fence covers LDS only, so the barrier
+// never waits for the weight ring.
 // ---------------------------------------------------------------------------
+// Scale words of G consecutive chunks (4G contiguous bytes per lane).
+template <int G>
+struct ScaleGroup {
+  uint32_t w[G];
+  __device__ __forceinline__ static ScaleGroup load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    ScaleGroup s;
+    if constexpr (G == 4) {
+      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+      s.w[0] = v[0]; s.w[1] = v[1]; s.w[2] = v[2]; s.w[3] = v[3];
+    } else if constexpr (G == 3) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0);
+      s.w[0] = v[0]; s.w[1] = v[1]; s.w[2] = v[2];
+    } else if constexpr (G == 2) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+      s.w[0] = v[0]; s.w[1] = v[1];
+    } else {
+      s.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    }
+    return s;
+  }
+};
+
 template <int AK, int EPI, int MT, int NTW, int PF>
 __device__ __forceinline__ void stream_body(const KParams& p) {
   static_assert(NTW % 2 == 0, "scale words cover column tiles in pairs");
   const int lane = threadIdx.x & 63, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kNW + (threadIdx.x >> 6)));
-  const int W = gridDim.x * kNW;
   const int K = p.K, KC = K / kBK, NT = p.N / 16, CG = NT / NTW;
   const int n_units = ld_uniform(p.plan + p.list_idx) * CG;
-  if (wave >= n_units) return;
+  if (n_units == 0) return;
+  // The launch covers the largest possible plan; with the actual unit count,
+  // use just enough wavefronts that every one gets the same number of units
+  // (a short last round would leave most of the device idle while it runs).
+  constexpr bool COOP = AK != kActCodes;
+  const int W_launch = gridDim.x * kNW;
+  const int rounds = (n_units + W_launch - 1) / W_launch;
+  int W = (n_units + rounds - 1) / rounds;
+  if constexpr (COOP) W = (W + kNW - 1) / kNW * kNW;   // whole workgroups per tile
+  if (wave >= W) return;
   const int* list = p.plan + ld_uniform(p.plan + 4 + p.list_idx);
+  const int wq = threadIdx.x >> 6;  // COOP: the 32-k step this wavefront loads
 
   // Buffer addressing: a scalar descriptor per operand (per expert for the
   // weights) plus a 32-bit per-lane offset; every byte range addressed here
   // is below 2^31 (checked by the launcher).
   const int64_t wq_expert = (int64_t)NT * KC * 1024;  // code bytes per expert
   const int64_t ws_expert = (int64_t)(NT >> 1) * KC * 256;
-  const int w_lane = lane * 16, s_lane = lane * 4;
+  // The ring holds one group of PF chunks: the weight scales of a tile pair
+  // for the whole group arrive with one load per lane.
+  static_assert(PF >= 1 && PF <= 4, "ring depth = scale group");
+  const int w_lane = lane * 16, s_lane = lane * 4 * PF;
   const __amdgpu_buffer_rsrc_t a_rsrc = AK == kActCodes
       ? __builtin_amdgcn_make_buffer_rsrc((void*)p.a_q, (short)0, 0x7FFFFFFF, kBufferFlags)
       : __builtin_amdgcn_make_buffer_rsrc((void*)p.a_h, (short)0, 0x7FFFFFFF, kBufferFlags);
@@ -724,9 +830,12 @@ __device__ __forceinline__ void stream_body(const KParams& p) {
     U.nrows = (int)(rr >> 24);
     U.nt0 = cg * NTW;
     U.n0 = U.nt0 * 16;
+    // Row of the tile this lane loads: its fragment row, or (COOP) row
+    // 4 * wq + lane / 16 with lane % 16 selecting the 16-byte piece.
+    const int rl = COOP ? 4 * wq + (lane >> 4) : (lane & 15);
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-      int r = U.row0 + min(i * 16 + (lane & 15), U.nrows - 1);
+      int r = U.row0 + min(i * 16 + rl, U.nrows - 1);
       if (p.sorted_pair) {
         // The 16 pair indices of this m-tile through scalar loads, then each
         // lane picks its own (a vector gather here would be waited for with
@@ -735,20 +844,29 @@ __device__ __forceinline__ void stream_body(const KParams& p) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const int fq = ld_uniform(p.sorted_pair + U.row0 + min(i * 16 + q, U.nrows - 1));
-          f = (lane & 15) == q ? fq : f;
+          f = rl == q ? fq : f;
         }
         r = pair_token(f, p.T, p.topk);
       }
-      U.a_off[i] = AK == kActCodes ? r * (K >> 1) + g * 16 : r * K * 2 + g * 64;
+      U.a_off[i] = AK == kActCodes ? r * (K >> 1) + g * 16 : r * K * 2 + (lane & 15) * 16;
       U.s_off[i] = r * (K >> 4) + g * 2;
     }
     return U;
   };
 
   u32x4 bq[PF][NTW];
-  uint32_t bs[PF][NTW / 2];
-  constexpr int AW = AK == kActCodes ? 1 : 4;  // 16-byte activation words per m-tile and chunk
+  // Scale words of the group being computed (bs) and of the next one (bsn,
+  // loaded with the group's first refill).
+  ScaleGroup<PF> bs[NTW / 2], bsn[NTW / 2];
+  // 16-byte activation words per m-tile and chunk held by this wavefront.
+  constexpr int AW = (AK == kActCodes || COOP) ? 1 : 4;
   u32x4 aq[PF][MT][AW];
+  // COOP: [2 buffers][16 MT rows][272 bytes] (a 256-byte chunk row plus 16
+  // bytes of padding, which spreads the fragment reads over all banks), one
+  // buffer per chunk.
+  constexpr int kRowB = 272, kBufB = 16 * MT * kRowB;
+  __shared__ __attribute__((aligned(16))) uint8_t a_lds[COOP ? 2 * kBufB : 16];
+  int abuf = 0;
   uint32_t as[PF][MT];
   // Refill of ring slot ``slot`` with chunk kc of unit A (sel false) or B
   // (sel true).  The choice is made with selects, not a branch: the loads
@@ -764,9 +882,11 @@ __device__ __forceinline__ void stream_body(const KParams& p) {
     for (int j = 0; j < NTW; ++j)
       bq[slot][j] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, w_lane, ((nt0 + j) * KC + kc) * 1024, 0));
+    if (slot == 0) {
 #pragma unroll
-    for (int j = 0; j < NTW / 2; ++j)
-      bs[slot][j] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_lane, (((nt0 >> 1) + j) * KC + kc) * 256, 0);
+      for (int j = 0; j < NTW / 2; ++j)
+        bsn[j] = ScaleGroup<PF>::load(sr, s_lane, (((nt0 >> 1) + j) * (KC / PF) + kc / PF) * 256 * PF);
+    }
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       const int ao = sel ? B.a_off[i] : A.a_off[i];
@@ -776,15 +896,40 @@ __device__ __forceinline__ void stream_body(const KParams& p) {
         as[slot][i] = __builtin_amdgcn_raw_buffer_load_b16(as_rsrc, so, kc * 8, 0);
       } else {
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
+        for (int w = 0; w < AW; ++w)
           aq[slot][i][w] = __builtin_bit_cast(
               u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, ao + w * 16, kc * 256, 0));
       }
     }
   };
+  // COOP: publish this wavefront's k-step of the chunk in slot ``slot`` and
+  // return once all four are readable.  Double-buffered: a buffer is written
+  // again two chunks later, after every wavefront has passed the barrier that
+  // follows its reads (the fence before each barrier completes them).
+  auto share_a = [&](int slot) {
+    uint8_t* buf = a_lds + abuf * kBufB;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+      *reinterpret_cast<u32x4*>(buf + (i * 16 + 4 * wq + (lane >> 4)) * kRowB + (lane & 15) * 16) =
+          aq[slot][i][0];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+  // Fragment of k-step ks: row lane % 16, k in [32 g + 8 ks, 32 g + 8 ks + 8)
+  // (the k order of the weight fragments).
+  auto shared_a = [&](int i, int ks) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(a_lds + abuf * kBufB + (i * 16 + (lane & 15)) * kRowB +
+                                           g * 64 + ks * 16);
+  };
+
+  // SwiGLU epilogues: a wave-private h tile in LDS.
+  __shared__ float h_lds[EPI != kEpiStoreF32 ? kNW * 16 * MT * 16 * NTW : 1];
+  float* const sh = h_lds + (EPI != kEpiStoreF32 ? wq * 16 * MT * 16 * NTW : 0);
 
   f32x4 acc[MT][NTW];
   auto compute = [&](int slot) {
+    if constexpr (COOP) share_a(slot);
     if constexpr (AK != kActBf16) {
       f16x2 sa2[MT], sb2[NTW];
       if constexpr (AK == kActCodes) {
@@ -792,7 +937,7 @@ __device__ __forceinline__ void stream_body(const KParams& p) {
         for (int i = 0; i < MT; ++i) sa2[i] = e4m3x2_to_f16x2(as[slot][i]);
       }
 #pragma unroll
-      for (int j = 0; j < NTW; ++j) sb2[j] = e4m3x2_to_f16x2(bs[slot][j >> 1] >> ((j & 1) * 16));
+      for (int j = 0; j < NTW; ++j) sb2[j] = e4m3x2_to_f16x2(bs[j >> 1].w[slot] >> ((j & 1) * 16));
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         f16x8 af[MT], bf[NTW];
@@ -801,7 +946,7 @@ __device__ __forceinline__ void stream_body(const KParams& p) {
           if constexpr (AK == kActCodes)
             af[i] = dequant8_f16(aq[slot][i][0][ks], ks < 2 ? f16x2_lo(sa2[i]) : f16x2_hi(sa2[i]));
           else
-            af[i] = __builtin_bit_cast(f16x8, aq[slot][i][ks]);
+            af[i] = __builtin_bit_cast(f16x8, shared_a(i, ks));
         }
 #pragma unroll
         for (int j = 0; j < NTW; ++j) bf[j] = weight_f16(bq[slot][j][ks], sb2[j], ks);
@@ -815,7 +960,7 @@ __device__ __forceinline__ void stream_body(const KParams& p) {
       float sb[NTW][2];
 #pragma unroll
       for (int j = 0; j < NTW; ++j) {
-        const uint32_t w = bs[slot][j >> 1] >> ((j & 1) * 16);
+        const uint32_t w = bs[j >> 1].w[slot] >> ((j & 1) * 16);
         sb[j][0] = e4m3_value(w & 0xFFu);
         sb[j][1] = e4m3_value((w >> 8) & 0xFFu);
       }
@@ -826,7 +971,7 @@ __device__ __forceinline__ void stream_body(const KParams& p) {
         for (int j = 0; j < NTW; ++j) bf[j] = dequant8_bf16(bq[slot][j][ks], sb[j][ks >> 1]);
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
-          const bf16x8 af = __builtin_bit_cast(bf16x8, aq[slot][i][ks]);
+          const bf16x8 af = __builtin_bit_cast(bf16x8, shared_a(i, ks));
 #pragma unroll
           for (int j = 0; j < NTW; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0, 0, 0);
@@ -835,17 +980,26 @@ __device__ __forceinline__ void stream_body(const KParams& p) {
     }
   };
 
+  // The unit after a wave's last one points its weight loads at the first
+  // chunks of expert 0's first column tiles, which every wave reads, so those
+  // (unused) refills stay in L2 and every load remains unconditional.
+  auto next_unit = [&](int u_next, bool more) {
+    Unit n = unit(more ? u_next : u_next - W);
+    n.e = more ? n.e : 0;
+    n.nt0 = more ? n.nt0 : 0;
+    return n;
+  };
   int u = wave;
   Unit cur = unit(u);
-  // The unit after the last one is a copy of the current one: its loads
-  // are harmless re-reads, which keeps every load unconditional.
   bool more = u + W < n_units;
-  Unit nxt = unit(more ? u + W : u);
+  Unit nxt = next_unit(u + W, more);
 #pragma unroll
   for (int s = 0; s < PF; ++s) {
     load(cur, cur, false, s, s);
     __builtin_amdgcn_sched_barrier(0);
   }
+#pragma unroll
+  for (int j = 0; j < NTW / 2; ++j) bs[j] = bsn[j];
   while (true) {
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -856,18 +1010,26 @@ __device__ __forceinline__ void stream_body(const KParams& p) {
 #pragma unroll
       for (int s = 0; s < PF; ++s) {
         compute(s);
+        abuf ^= 1;
         __builtin_amdgcn_sched_barrier(0);
         // PF divides KC, so the next unit's chunk index is s.
         load(cur, nxt, last_round, last_round ? s : kc0 + PF + s, s);
         __builtin_amdgcn_sched_barrier(0);
       }
+      // The next group's scales were requested before its weights, so this
+      // waits for nothing that the next compute would not wait for anyway.
+#pragma unroll
+      for (int j = 0; j < NTW / 2; ++j) bs[j] = bsn[j];
     }
-    epilogue<EPI, MT, NTW>(p, acc, cur.e, cur.row0, cur.nrows, cur.n0, lane);
+    if constexpr (EPI == kEpiStoreF32)
+      epilogue<EPI, MT, NTW>(p, acc, cur.e, cur.row0, cur.nrows, cur.n0, lane);
+    else
+      epilogue_rows<EPI, MT, NTW>(p, acc, cur.e, cur.row0, cur.nrows, cur.n0, lane, sh);
     if (!more) break;
     u += W;
     cur = nxt;
     more = u + W < n_units;
-    nxt = unit(more ? u + W : u);
+    nxt = next_unit(u + W, more);
   }
   // Let the final (unused) refills land before the wave ends.
   __builtin_amdgcn_s_waitcnt(0);
@@ -878,7 +1040,7 @@ __device__ __forceinline__ void stream_body(const KParams& p) {
 // left to the compiler (a forced budget would spill).
 template <int AK, int MT, int PF>
 constexpr bool stream_fits_four_waves() {
-  return (MT == 1 && (AK == kActCodes || PF <= 3)) || (MT == 2 && AK == kActCodes && PF <= 3);
+  return MT == 1 || PF <= 3;
 }
 
 template <int AK, int EPI, int MT, int NTW, int PF>
@@ -975,27 +1137,26 @@ hipError_t launch_persistent(const KParams& kp, int64_t units, hipStream_t s) {
 
 template <int AK, int EPI, int MT, int NTW, int PF>
 hipError_t launch_stream(const KParams& kp, int list_len, hipStream_t s) {
-  const int64_t units = (int64_t)list_len * ((kp.N / 16) / NTW);
+  const int64_t cg = (kp.N / 16) / NTW;
+  // 16-bit activations are shared by the workgroup's four wavefronts, which
+  // must all work on one tile: the units per tile come in fours.
+  if (AK != kActCodes && cg % kNW != 0) return hipErrorInvalidValue;
+  const int64_t units = (int64_t)list_len * cg;
   if constexpr (stream_fits_four_waves<AK, MT, PF>())
     return launch_persistent<grouped_gemm_stream4_kernel<AK, EPI, MT, NTW, PF>>(kp, units, s);
   else
     return launch_persistent<grouped_gemm_stream_kernel<AK, EPI, MT, NTW, PF>>(kp, units, s);
 }
 
-// Ring depth of the streaming kernel: the largest allowed depth dividing the
-// chunk count (16-bit activation fragments are 4x larger than codes).
+// Ring depth of the streaming kernel: one scale group of the weights.
 template <int AK, int EPI, int MT, int NTW>
 hipError_t launch_stream_pf(const KParams& kp, int len, hipStream_t s) {
-  const int KC = kp.K / kBK;
-  if constexpr (NVFP4_STREAM_PFMAX >= 8 && AK == kActCodes) {
-    if (KC % 8 == 0) return launch_stream<AK, EPI, MT, NTW, 8>(kp, len, s);
+  switch (scale_group(kp.K / kBK)) {
+    case 4: return launch_stream<AK, EPI, MT, NTW, 4>(kp, len, s);
+    case 3: return launch_stream<AK, EPI, MT, NTW, 3>(kp, len, s);
+    case 2: return launch_stream<AK, EPI, MT, NTW, 2>(kp, len, s);
+    default: return launch_stream<AK, EPI, MT, NTW, 1>(kp, len, s);
   }
-  if constexpr (NVFP4_STREAM_PFMAX >= 4) {
-    if (KC % 4 == 0) return launch_stream<AK, EPI, MT, NTW, 4>(kp, len, s);
-  }
-  if (KC % 3 == 0) return launch_stream<AK, EPI, MT, NTW, 3>(kp, len, s);
-  if (KC % 2 == 0) return launch_stream<AK, EPI, MT, NTW, 2>(kp, len, s);
-  return launch_stream<AK, EPI, MT, NTW, 1>(kp, len, s);
 }
 
 template <int AK, int EPI>

@@ -47,8 +47,19 @@ hipError_t launch_scale_and_align(const AlignShape& a, const uint16_t* x, float*
                                   int32_t* inv_pos, int32_t* plan, void* ws, hipStream_t s);
 
 // Weight streaming layout.  For an expert matrix [N][K] (N output columns,
-// K contraction): codes [N/16][K/128][64 lanes][16 B] followed (after all
-// experts' codes) by scales [N/32][K/128][64 lanes][2 tiles][2 B].
+// K contraction, KC = K/128 chunks): codes [N/16][KC][64 lanes][16 B]
+// followed (after all experts' codes) by scales
+// [N/32][KC/G][64 lanes][G chunks][2 tiles][2 B], G = scale_group(KC): a
+// lane's scale bytes of G consecutive chunks are contiguous (one load).
+__host__ __device__ constexpr int scale_group(int kc) {
+  return kc % 4 == 0 ? 4 : kc % 3 == 0 ? 3 : kc % 2 == 0 ? 2 : 1;
+}
+// Byte offset, inside one expert's scale block, of the 4-byte word of column
+// tile pair tp, chunk kc, lane (the word holds 2 tiles x 2 scale bytes).
+__host__ __device__ constexpr int64_t scale_word_offset(int64_t tp, int kc, int KC, int lane) {
+  const int G = scale_group(KC);
+  return ((tp * (KC / G) + kc / G) * 64 + lane) * (4 * G) + (kc % G) * 4;
+}
 size_t prep_bytes(int64_t slots, int64_t N, int64_t K);
 hipError_t launch_prep(int64_t slots, int64_t N, int64_t K, int interleave_I, const uint8_t* q,
                        const uint8_t* sf, uint8_t* prep, hipStream_t s);

@@ -3,12 +3,14 @@
 // For an expert matrix W [N][K] (canonical NVFP4: codes [N][K/2], scales
 // [N][K/16]) the layout is, per expert:
 //   codes : [N/16 column tiles][K/128 chunks][64 lanes][16 bytes]
-//   scales: [N/32 tile pairs][K/128 chunks][64 lanes][2 tiles][2 bytes]
+//   scales: [N/32 tile pairs][K/128/G chunk groups][64 lanes][G chunks][2 tiles][2 bytes]
 // Lane l = 16*g + n of a (tile, chunk) holds the 32 codes k in
 // [32g, 32g + 32) of the chunk for column n of the tile, in canonical nibble
 // order, and the two scale bytes of those k; the scale bytes of the two
-// tiles of a pair sit side by side, so a lane fetches them with one 4-byte
-// load.  One wavefront therefore reads a
+// tiles of a pair sit side by side, and those of G consecutive chunks
+// (G = 4, 3, 2 or 1, the largest dividing K/128) follow each other, so a lane
+// fetches the scales of a tile pair for G chunks with one load of 4G bytes.
+// One wavefront therefore reads a
 // whole (tile, chunk) with one coalesced 16-byte load per lane, and every
 // lane's bytes are exactly the operand fragment it feeds to the 16x16x32
 // matrix instruction (8 codes per k-step).  All experts' codes come first,
@@ -51,8 +53,8 @@ __global__ __launch_bounds__(256) void prep_kernel(int64_t slots, int64_t N, int
   const u32x4 v = *reinterpret_cast<const u32x4*>(src);
   *reinterpret_cast<u32x4*>(prep + i * 16) = v;
   const uint8_t* ssrc = sf + (e * N + row) * (K / 16) + kc * 8 + 2 * g;
-  const int64_t pair_unit = ((e * (NT / 2) + (nt >> 1)) * KC + kc) * 64 + lane;
-  uint8_t* sdst = prep + slots * N * (K / 2) + pair_unit * 4 + (nt & 1) * 2;
+  uint8_t* sdst = prep + slots * N * (K / 2) + e * (N / 32) * KC * 256 +
+                  scale_word_offset(nt >> 1, (int)kc, (int)KC, (int)lane) + (nt & 1) * 2;
   sdst[0] = ssrc[0];
   sdst[1] = ssrc[1];
 }

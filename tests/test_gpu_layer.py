@@ -81,30 +81,36 @@ def _uploaded_weights(case: Case, dev):
 
 
 # ---------------------------------------------------------------- layout
-def test_prep_layout(dev):
-    S, I, H = 3, 128, 256
+def _scale_group(kc):
+    return next(g for g in (4, 3, 2, 1) if kc % g == 0)
+
+
+@pytest.mark.parametrize("S,I,H", [(3, 128, 256), (2, 384, 512), (1, 768, 2048)])
+def test_prep_layout(dev, S, I, H):
+    """The streaming layout is the documented permutation of the canonical
+    bytes (chunk counts 1, 2, 3, 4 and 16: every scale group size)."""
     d = ops.dims(4, 1, S, H, I, 0)
-    rng = np.random.default_rng(0)
+    rng = np.random.default_rng(S + I)
     for which, N, K in ((13, 2 * I, H), (2, H, I)):
         q = rng.integers(0, 256, (S, N, K // 2), dtype=np.uint8)
         sf = rng.integers(0, 127, (S, N, K // 16), dtype=np.uint8)
         prep = to_np(ops.prep_weights(d, which, torch.from_numpy(q).to(dev), torch.from_numpy(sf).to(dev)))
         NT, KC = N // 16, K // 128
+        G = _scale_group(KC)
         codes = prep[:S * N * K // 2].reshape(S, NT, KC, 64, 16)
-        # scales: [S][tile pairs][chunks][lanes][2 tiles][2 bytes]
-        scales = prep[S * N * K // 2:].reshape(S, NT // 2, KC, 64, 2, 2)
-        for e in range(S):
-            for nt in range(NT):
-                for lane in range(64):
-                    n, g = lane % 16, lane // 16
-                    if which == 13:
-                        row = (I + 16 * (nt // 2) + n) if nt % 2 else (16 * (nt // 2) + n)
-                    else:
-                        row = nt * 16 + n
-                    for kc in range(KC):
-                        assert np.array_equal(codes[e, nt, kc, lane], q[e, row, kc * 64 + 16 * g: kc * 64 + 16 * g + 16])
-                        assert np.array_equal(scales[e, nt // 2, kc, lane, nt % 2],
-                                              sf[e, row, kc * 8 + 2 * g: kc * 8 + 2 * g + 2])
+        # scales: [S][tile pairs][chunk groups][lanes][G chunks][2 tiles][2 bytes]
+        scales = prep[S * N * K // 2:].reshape(S, NT // 2, KC // G, 64, G, 2, 2)
+        nt = np.arange(NT)[:, None]
+        n = np.arange(64)[None, :] % 16
+        g = np.arange(64)[None, :] // 16
+        row = np.where(nt % 2 == 1, I + 16 * (nt // 2) + n, 16 * (nt // 2) + n) if which == 13 \
+            else nt * 16 + n                                   # [NT][64]
+        for kc in range(KC):
+            want_q = q[:, row[..., None], kc * 64 + 16 * g[..., None] + np.arange(16)]
+            assert np.array_equal(codes[:, :, kc], want_q), (which, kc)
+            want_s = sf[:, row[..., None], kc * 8 + 2 * g[..., None] + np.arange(2)]   # [S][NT][64][2]
+            got_s = scales[:, :, kc // G, :, kc % G].transpose(0, 1, 3, 2, 4).reshape(S, NT, 64, 2)
+            assert np.array_equal(got_s, want_s), (which, kc)
 
 
 # ---------------------------------------------------------------- stages
