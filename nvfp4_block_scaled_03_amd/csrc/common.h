@@ -71,8 +71,9 @@ __device__ __forceinline__ float row16_max(float v) {
 // Value of a non-negative E4M3 code 0x00..0x7E.
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
   const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  if (e == 0) return (float)m * 0.001953125f;            // m * 2^-9
-  return __int_as_float((int)(((e + 120u) << 23) | (m << 20)));  // (1 + m/8) * 2^(e-7)
+  const float sub = (float)m * 0.001953125f;                            // m * 2^-9
+  const float nrm = __int_as_float((int)(((e + 120u) << 23) | (m << 20)));  // (1 + m/8) * 2^(e-7)
+  return e == 0 ? sub : nrm;
 }
 
 // sign(a - g * M) for a >= 0, g > 0, M > 0 (see above).

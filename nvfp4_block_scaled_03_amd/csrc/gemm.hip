@@ -99,8 +99,8 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
   return x * q + min(x, r) + idx;
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
-// The same with the hardware reciprocal (1 ulp) in place of the division.
+// silu(z) = z / (1 + e^-z), with the hardware reciprocal (1 ulp) in place of
+// an IEEE division.
 __device__ __forceinline__ float silu_fast(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
@@ -142,7 +142,7 @@ __device__ __forceinline__ void epilogue(const KParams& p, f32x4 (&acc)[MT][NTW]
         for (int r = 0; r < 4; ++r) {
           const float gate = alpha * acc[i][2 * q][r];
           const float up = alpha * acc[i][2 * q + 1][r];
-          h[r] = silu(gate) * up;
+          h[r] = silu_fast(gate) * up;
         }
         if constexpr (EPI == kEpiSwigluFp4) {
 #pragma unroll
@@ -205,7 +205,7 @@ __device__ __forceinline__ void epilogue_blocks(const KParams& p, f32x4 (&acc)[M
       for (int r = 0; r < 4; ++r) {
         const float gate = alpha * acc[i][2 * q][r];
         const float up = alpha * acc[i][2 * q + 1][r];
-        sh[(i * 16 + lg * 4 + r) * HC + q * 16 + ln] = silu(gate) * up;
+        sh[(i * 16 + lg * 4 + r) * HC + q * 16 + ln] = silu_fast(gate) * up;
       }
   // (wave-private area: the wave's own LDS writes are ordered before its reads)
   const int hb0 = n_wave0 >> 5;                // first 16-column block of h
@@ -234,25 +234,21 @@ __device__ __forceinline__ void epilogue_blocks(const KParams& p, f32x4 (&acc)[M
       const float sv = e4m3_value(sc);
       const E2M1Bounds bd = e2m1_bounds(sv, g2);
       uint32_t w0 = 0, w1 = 0;
-      uint32_t dh[8];
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const uint32_t code = e2m1_code(v[k], bd, sc == 0);
         if (k < 8) w0 |= code << (4 * k);
         else w1 |= code << (4 * (k - 8));
-        if (p.out_h) {
-          const float dv = e2m1_mag_value(code & 7u) * sv;   // exact in f16
-          const uint32_t hbits = __builtin_bit_cast(uint16_t, (_Float16)((code & 8u) ? -dv : dv));
-          if (k & 1) dh[k >> 1] |= hbits << 16;
-          else dh[k >> 1] = hbits;
-        }
       }
       *reinterpret_cast<u32x2*>(p.out_q + pr * (p.I >> 1) + (hb0 + hb) * 8) = u32x2{w0, w1};
       p.out_sf[pr * (p.I >> 4) + hb0 + hb] = (uint8_t)sc;
       if (p.out_h) {
+        // The exact f16 decoding of the 16 codes just written (the same
+        // convert + scale multiply as the weights; exact, see dequant8_f16).
+        const f16x2 s2 = f16x2_splat(sv);
         uint16_t* dst = p.out_h + pr * p.I + (hb0 + hb) * 16;
-        *reinterpret_cast<u32x4*>(dst) = u32x4{dh[0], dh[1], dh[2], dh[3]};
-        *reinterpret_cast<u32x4*>(dst + 8) = u32x4{dh[4], dh[5], dh[6], dh[7]};
+        *reinterpret_cast<f16x8*>(dst) = dequant8_f16(w0, s2);
+        *reinterpret_cast<f16x8*>(dst + 8) = dequant8_f16(w1, s2);
       }
     } else {
       uint32_t bw[8];
@@ -482,9 +478,10 @@ __global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
       float sb[NTW][2];
 #pragma unroll
       for (int j = 0; j < NTW; ++j) {
-        const uint32_t w = bs[j >> 1] >> ((j & 1) * 16);
-        sb[j][0] = e4m3_value(w & 0xFFu);
-        sb[j][1] = e4m3_value((w >> 8) & 0xFFu);
+        // (hardware E4M3 -> f16, exact, then f16 -> f32, exact)
+        const f16x2 h = e4m3x2_to_f16x2(bs[j >> 1] >> ((j & 1) * 16));
+        sb[j][0] = (float)h[0];
+        sb[j][1] = (float)h[1];
       }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -546,19 +543,27 @@ __global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
 // Wide kernel for 128-row tiles with 16-bit activations (the exact f16 copy
 // of NVFP4 codes, or bf16 for W4A16): the prefill regime, bound by the
 // matrix instructions and by weight decoding.  A workgroup computes 128 rows
-// x 256 columns; each of its 4 wavefronts owns 64 columns for all 128 rows,
+// x 64 NW columns; each of its NW wavefronts owns 64 columns for all 128 rows,
 // so every decoded weight fragment feeds 8 matrix instructions and every
-// activation fragment read from LDS feeds 4.  Activation chunks (128 rows x
+// activation fragment read from LDS feeds 4; the activation chunk is brought
+// in once for all NW wavefronts.  Activation chunks (128 rows x
 // 128 k) move from memory to LDS with the direct-to-LDS loads of gfx950 (no
 // registers, no VALU), double-buffered; the 16-byte units of a row are
 // XOR-swizzled by the row so that the 16 rows of a fragment read fall in
 // distinct banks.  Weights stream into two register sets used alternately.
 // ---------------------------------------------------------------------------
-constexpr int kWideBM = 128, kWideWN = 64, kWideNW = 4;
+#ifndef NVFP4_WIDE_INTERLEAVE
+#define NVFP4_WIDE_INTERLEAVE 1  // interleave weight decode with matrix instructions
+#endif
+#ifndef NVFP4_WIDE_NW
+#define NVFP4_WIDE_NW 4        // wavefronts per workgroup of the wide kernel (4 or 8)
+#endif
+constexpr int kWideBM = 128, kWideWN = 64, kWideNW = NVFP4_WIDE_NW;
 
 template <int AK, int EPI>
 __global__ __launch_bounds__(kWideNW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void grouped_gemm_wide_kernel(KParams p) {
+  static_assert(kWideNW == 4 || kWideNW == 8, "4 or 8 wavefronts");
   static_assert(AK != kActCodes, "the wide kernel takes 16-bit activations");
   constexpr int MT = kWideBM / 16, NTW = kWideWN / 16, NW = kWideNW;
   constexpr int ROW_BYTES = kBK * 2;                       // 256
@@ -651,41 +656,76 @@ void grouped_gemm_wide_kernel(KParams p) {
       f16x2 sb2[NTW];
 #pragma unroll
       for (int j = 0; j < NTW; ++j) sb2[j] = e4m3x2_to_f16x2(bs[j >> 1] >> ((j & 1) * 16));
+      // Per k-step: all fragment reads first; then column tile by column
+      // tile, the decode of tile j + 1 (8 VALU instructions) is interleaved
+      // with the 8 matrix instructions of tile j, so it issues while the
+      // matrix unit is busy.
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
+        const int ucol = ((4 * g + s) ^ m) * 16;
+        f16x8 af[MT];
+#pragma unroll
+        for (int i = 0; i < MT; ++i) af[i] = *reinterpret_cast<const f16x8*>(abuf + i * 16 * ROW_BYTES + ucol);
+        __builtin_amdgcn_sched_barrier(0);
         f16x8 bf[NTW];
 #pragma unroll
         for (int j = 0; j < NTW; ++j) bf[j] = weight_f16(bq[j][s], sb2[j], s);
-        const int ucol = ((4 * g + s) ^ m) * 16;
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-          const f16x8 af = *reinterpret_cast<const f16x8*>(abuf + i * 16 * ROW_BYTES + ucol);
+        for (int j = 0; j < NTW; ++j)
 #pragma unroll
-          for (int j = 0; j < NTW; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[j], acc[i][j], 0, 0, 0);
-        }
+          for (int i = 0; i < MT; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+#if NVFP4_WIDE_INTERLEAVE
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // decode of tile 0
+#pragma unroll
+        for (int j = 0; j + 1 < NTW; ++j)
+#pragma unroll
+          for (int i = 0; i < MT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix instruction
+            __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // one decode instruction
+          }
+        __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);  // the last tile's
+#endif
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
       float sb[NTW][2];
 #pragma unroll
       for (int j = 0; j < NTW; ++j) {
-        const uint32_t w = bs[j >> 1] >> ((j & 1) * 16);
-        sb[j][0] = e4m3_value(w & 0xFFu);
-        sb[j][1] = e4m3_value((w >> 8) & 0xFFu);
+        // (hardware E4M3 -> f16, exact, then f16 -> f32, exact)
+        const f16x2 h = e4m3x2_to_f16x2(bs[j >> 1] >> ((j & 1) * 16));
+        sb[j][0] = (float)h[0];
+        sb[j][1] = (float)h[1];
       }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
+        const int ucol = ((4 * g + s) ^ m) * 16;
+        bf16x8 af[MT];
+#pragma unroll
+        for (int i = 0; i < MT; ++i) af[i] = *reinterpret_cast<const bf16x8*>(abuf + i * 16 * ROW_BYTES + ucol);
+        __builtin_amdgcn_sched_barrier(0);
         bf16x8 bf[NTW];
 #pragma unroll
         for (int j = 0; j < NTW; ++j) bf[j] = dequant8_bf16(bq[j][s], sb[j][s >> 1]);
-        const int ucol = ((4 * g + s) ^ m) * 16;
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-          const bf16x8 af = *reinterpret_cast<const bf16x8*>(abuf + i * 16 * ROW_BYTES + ucol);
+        for (int j = 0; j < NTW; ++j)
 #pragma unroll
-          for (int j = 0; j < NTW; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0, 0, 0);
-        }
+          for (int i = 0; i < MT; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+#if NVFP4_WIDE_INTERLEAVE
+        // (the bf16 decode of a tile is 16 VALU instructions: two per matrix
+        // instruction of the previous tile)
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+#pragma unroll
+        for (int j = 0; j + 1 < NTW; ++j)
+#pragma unroll
+          for (int i = 0; i < MT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+          }
+        __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);
+#endif
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
@@ -730,10 +770,17 @@ void grouped_gemm_wide_kernel(KParams p) {
     epilogue<EPI, MT, NTW>(p, acc, t.e, t.row0, t.nrows, n_wave0, lane);
   } else {
     // The activation buffers are free (the loop ended on a barrier after the
-    // last reads): each wavefront takes 16 KiB of them for the epilogue.
-    static_assert(kWideBM * 8 * NTW * 4 * NW == 2 * BUF_BYTES, "epilogue area = both buffers");
-    float* sh = reinterpret_cast<float*>((wv < 2 ? As0 : As1) + (wv & 1) * (BUF_BYTES / 2));
-    epilogue_blocks<EPI, MT, NTW>(p, acc, t.e, t.row0, t.nrows, n_wave0, lane, sh);
+    // last reads): each wavefront takes 1/NW of them for the epilogue, which
+    // runs in passes of PM m-tiles (all 8 with 4 wavefronts, 4 with 8).
+    constexpr int WAVE_BYTES = 2 * BUF_BYTES / NW;
+    constexpr int PM = WAVE_BYTES / (16 * 8 * NTW * 4);
+    static_assert(PM >= 1 && MT % PM == 0, "whole m-tiles per pass");
+    uint8_t* const area = (wv < NW / 2 ? As0 : As1) + (wv % (NW / 2)) * WAVE_BYTES;
+    float* sh = reinterpret_cast<float*>(area);
+#pragma unroll
+    for (int pm = 0; pm < MT; pm += PM)
+      epilogue_blocks<EPI, PM, NTW>(p, *reinterpret_cast<f32x4(*)[PM][NTW]>(&acc[pm]), t.e,
+                                    t.row0 + pm * 16, t.nrows - pm * 16, n_wave0, lane, sh);
   }
 }
 
@@ -960,9 +1007,9 @@ __device__ __forceinline__ void stream_body(const KParams& p) {
       float sb[NTW][2];
 #pragma unroll
       for (int j = 0; j < NTW; ++j) {
-        const uint32_t w = bs[j >> 1].w[slot] >> ((j & 1) * 16);
-        sb[j][0] = e4m3_value(w & 0xFFu);
-        sb[j][1] = e4m3_value((w >> 8) & 0xFFu);
+        const f16x2 h = e4m3x2_to_f16x2(bs[j >> 1].w[slot] >> ((j & 1) * 16));
+        sb[j][0] = (float)h[0];
+        sb[j][1] = (float)h[1];
       }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
