@@ -8,7 +8,7 @@
         FETCH_SIZE / WRITE_SIZE per dispatch against the bytes really moved).
     python -m nvfp4_block_scaled_03_amd.profiling traffic --fetch F.csv --write W.csv
         --copy-fetch CF.csv --copy-write CW.csv --mib 1024 --kernel NAME --workload decode
-        --command "..." > profiles/<kernel>_<workload>_traffic.txt
+        [--req R.csv] --command "..." > profiles/<kernel>_<workload>_traffic.txt
         Summarise two counter runs of the kernel and two of the copy into the
         HBM bytes per launch (counter readings scaled by the copy calibration)
         and record the hash of the kernel sources the counters belong to.
@@ -126,6 +126,11 @@ def _cmd_traffic(a):
     print(f"fetch_bytes_per_launch = {fetch_b:.0f}")
     print(f"write_bytes_per_launch = {write_b:.0f}")
     print(f"bytes_per_launch = {fetch_b + write_b:.0f}")
+    if a.req:
+        # Cross-check of the fetch calibration: HBM read requests by size.
+        sizes = {"TCC_EA0_RDREQ_32B_sum": 32, "TCC_EA0_RDREQ_64B_sum": 64, "TCC_EA0_RDREQ_128B_sum": 128}
+        req_b = sum(_per_dispatch(a.req, c, a.kernel_re)[0] * b for c, b in sizes.items())
+        print(f"read_bytes_by_request_size = {req_b:.0f}")
     print(f"sources_sha256_16 = {sources_hash()}")
 
 
@@ -163,6 +168,7 @@ def main(argv=None):
     t.add_argument("--copy-re", dest="copy_re", default=r"copy|Copy")
     t.add_argument("--workload", default="decode")
     t.add_argument("--command", default="")
+    t.add_argument("--req", default="", help="counter CSV of TCC_EA0_RDREQ_{32B,64B,128B}_sum")
     st = sub.add_parser("stats")
     st.add_argument("--csv", required=True)
     st.add_argument("--title", default="")
