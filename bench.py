@@ -143,9 +143,13 @@ def cpu_baseline(w, dev, ids, tw, seconds):
 
 
 def time_steps(layer, x, ids, tw, copies, variant, steps, warmup, mode):
-    """Mean wall time of one layer step (ms) over ``steps`` steps."""
+    """Mean wall time of one layer step (ms) over ``steps`` steps.
+
+    Graph mode captures the steps of all weight copies in one graph, one
+    complete step per copy in sequence, as a model forward captures its
+    consecutive layers; a remainder of steps runs from one-step graphs."""
     out = torch.empty(x.shape[0], layer.d.H, dtype=torch.bfloat16, device=x.device)
-    graphs = []
+    graphs, multi = [], None
     if mode == "graph":
         for wc in copies:
             for _ in range(2):
@@ -155,19 +159,30 @@ def time_steps(layer, x, ids, tw, copies, variant, steps, warmup, mode):
             with torch.cuda.graph(g):
                 layer.forward(x, ids, tw, variant, out=out, weights=wc)
             graphs.append(g)
+        multi = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(multi):
+            for wc in copies:
+                layer.forward(x, ids, tw, variant, out=out, weights=wc)
 
-    def run(i):
+    def run(i0, count):
+        """Steps i0 .. i0 + count - 1; returns how many ran."""
+        if multi is not None and count >= len(copies) and i0 % len(copies) == 0:
+            multi.replay()
+            return len(copies)
         if graphs:
-            graphs[i % len(graphs)].replay()
+            graphs[i0 % len(graphs)].replay()
         else:
-            layer.forward(x, ids, tw, variant, out=out, weights=copies[i % len(copies)])
+            layer.forward(x, ids, tw, variant, out=out, weights=copies[i0 % len(copies)])
+        return 1
 
-    for i in range(warmup):
-        run(i)
+    i = 0
+    while i < warmup:
+        i += run(i, warmup - i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        run(i)
+    i = 0
+    while i < steps:
+        i += run(i, steps - i)
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) * 1e3 / steps
 
@@ -270,7 +285,8 @@ def main():
                  else "nvfp4 weights, bf16 activations, bf16 matrix ops, f32 accumulate",
         "data": "synthetic (seeded), random-init weights",
         "config": {"workload": w.name, **w.describe(), "variant": a.variant, "mode": a.mode,
-                   "experts_touched": m["touched"], "weight_copies": m["copies"]},
+                   "experts_touched": m["touched"], "weight_copies": m["copies"],
+                   "steps_per_graph": m["copies"] if a.mode == "graph" else 1},
         "layer_tflops": m["layer_tflops"], "layer_gbs": m["layer_gbs"],
         "layer_hbm_frac": m["layer_hbm_frac"],
         "roofline": m["roofline"],

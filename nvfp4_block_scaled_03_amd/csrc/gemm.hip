@@ -46,7 +46,10 @@ namespace {
 #define NVFP4_BIG_NW 4         // wavefronts per workgroup, LDS-staged kernel
 #endif
 #ifndef NVFP4_STREAM_NTW
-#define NVFP4_STREAM_NTW 2     // 16-column tiles per work unit, streaming kernel
+#define NVFP4_STREAM_NTW 2     // 16-column tiles per work unit, streaming kernel (GEMM1)
+#endif
+#ifndef NVFP4_STREAM_NTW_DOWN
+#define NVFP4_STREAM_NTW_DOWN 2  // the same for the down projection (GEMM2)
 #endif
 #ifndef NVFP4_WIDE_MIN_LIST
 #define NVFP4_WIDE_MIN_LIST 2  // smallest tile list (by mean rows/expert) sent to the wide kernel
@@ -1208,6 +1211,7 @@ hipError_t launch_stream_pf(const KParams& kp, int len, hipStream_t s) {
 
 template <int AK, int EPI>
 hipError_t launch_gemm(KParams kp, const AlignShape& al, hipStream_t s) {
+  constexpr int kStreamNTW = EPI == kEpiStoreF32 ? NVFP4_STREAM_NTW_DOWN : NVFP4_STREAM_NTW;
   int li = min(pick_list(al.P, al.slots), NVFP4_LIST_MAX);
   // The streaming kernel addresses with 32-bit buffer offsets.
   const int64_t a_row_bytes = AK == kActCodes ? kp.K / 2 : 2 * (int64_t)kp.K;
@@ -1224,8 +1228,8 @@ hipError_t launch_gemm(KParams kp, const AlignShape& al, hipStream_t s) {
   kp.list_idx = li;
   const int len = (int)al.list_len[li];
   switch (li) {
-    case 0: return launch_stream_pf<AK, EPI, 1, NVFP4_STREAM_NTW>(kp, len, s);
-    case 1: return launch_stream_pf<AK, EPI, 2, NVFP4_STREAM_NTW>(kp, len, s);
+    case 0: return launch_stream_pf<AK, EPI, 1, kStreamNTW>(kp, len, s);
+    case 1: return launch_stream_pf<AK, EPI, 2, kStreamNTW>(kp, len, s);
     case 2: return launch_lds<AK, EPI, 64, NVFP4_BIG_WN>(kp, len, s);
     default: return launch_lds<AK, EPI, 128, NVFP4_BIG_WN>(kp, len, s);
   }
