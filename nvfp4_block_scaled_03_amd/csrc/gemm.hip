@@ -1114,13 +1114,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int c = blockIdx.y * 1024 + threadIdx.x * 4;
   if (c >= H) return;
   f32x4 a = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < topk; ++j) {
-    const int pos = inv_pos[(int64_t)t * topk + j];
-    if (pos >= 0) {
-      const float w = topk_w[(int64_t)t * topk + j];
-      const f32x4 x = *reinterpret_cast<const f32x4*>(d + (int64_t)pos * H + c);
-      a += w * x;
+  // Batches of 8 pairs: positions and weights (the same for the whole block)
+  // through scalar loads, then all 8 row loads in flight together, then the
+  // sum in ascending j (selects, not branches, so no load waits on another).
+  constexpr int B = 8;
+  for (int j0 = 0; j0 < topk; j0 += B) {
+    int pos[B];
+    float w[B];
+    f32x4 x[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int j = j0 + b;
+      pos[b] = j < topk ? ld_uniform(inv_pos + (int64_t)t * topk + j) : -1;
+      w[b] = j < topk ? ld_uniform(topk_w + (int64_t)t * topk + j) : 0.0f;
     }
+#pragma unroll
+    for (int b = 0; b < B; ++b) x[b] = *reinterpret_cast<const f32x4*>(d + (int64_t)max(pos[b], 0) * H + c);
+#pragma unroll
+    for (int b = 0; b < B; ++b) a = pos[b] >= 0 ? a + w[b] * x[b] : a;
   }
   if (shared) {
     const int pos = inv_pos[(int64_t)T * topk + t];
