@@ -14,7 +14,8 @@
  *   nvfp4_global_scale  activations -> g1                    (W4A4 only)
  *   nvfp4_quantize      activations, g1 -> a1 codes + scales (W4A4 only)
  *   moe_align           top-k expert ids -> rows grouped by expert
- *   (moe_scale_and_align: the first and third steps in one call)
+ *   (moe_scale_and_align: the first and third steps in one call;
+ *    moe_quantize_and_align: the first three)
  *   grouped_gemm1_swiglu[_w4a16]   gate/up GEMM, SwiGLU, requantisation
  *   grouped_gemm2_combine[_w4a16]  down GEMM, top-k weighted combine
  *
@@ -63,7 +64,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_MOE_ABI_VERSION 2
+#define NVFP4_MOE_ABI_VERSION 3
 
 /* Status codes. */
 #define NVFP4_OK 0
@@ -200,6 +201,23 @@ int moe_scale_and_align(const nvfp4_moe_dims* dims, const uint16_t* x, float* g1
                         size_t gs_ws_bytes, const int32_t* topk_ids, int32_t* expert_offsets,
                         int32_t* sorted_pair, int32_t* inv_pos, int32_t* plan, void* ws,
                         size_t ws_bytes, void* stream);
+
+/* Global scale, quantisation and permutation in one call: the same results,
+ * bit for bit, as moe_scale_and_align(dims, x, g1, gs_ws, ...) followed by
+ * nvfp4_quantize(x, NVFP4_BF16, T, H, H, g1, T, a1_q, a1_sf, a1_deq, ...),
+ * with the same argument contracts (a1_q [T][H/2] 4-byte aligned, a1_sf
+ * [T][H/16], a1_deq optional f16 [T][H] 16-byte aligned).  The three steps of
+ * FlashInfer #2723's activation path ("2. FP32 Amax Computation", the
+ * per-token quantisation of "Why 39 vs 49 tok/s?") and the permutation of
+ * vLLM PR #29242 (get_cutlass_moe_mm_data) need no ordering among
+ * themselves beyond g1 before the codes; for decode-sized activations
+ * (T*H <= 2^18, P <= 4096) they run as one launch in which every quantising
+ * workgroup computes the exact amax itself, otherwise as
+ * moe_scale_and_align then nvfp4_quantize.  Errors as for those calls. */
+int moe_quantize_and_align(const nvfp4_moe_dims* dims, const uint16_t* x, float* g1, void* gs_ws,
+                           size_t gs_ws_bytes, uint8_t* a1_q, uint8_t* a1_sf, uint16_t* a1_deq,
+                           const int32_t* topk_ids, int32_t* expert_offsets, int32_t* sorted_pair,
+                           int32_t* inv_pos, int32_t* plan, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Weight preparation (offline).                                             */

@@ -9,6 +9,7 @@
 // shape is not available to the grouped GEMM).
 #include "common.h"
 #include "launch.h"
+#include "quant.h"
 
 namespace nvfp4 {
 namespace {
@@ -352,6 +353,67 @@ __global__ __launch_bounds__(1024) void scale_align_kernel(const uint16_t* __res
   }
 }
 
+// ---------------------------------------------------------------- quantise + align
+// Activation global scale, NVFP4 quantisation and alignment in one launch,
+// for decode-sized activations.  Workgroups 0 .. nblk-1 each reduce max |x|
+// over the whole tensor (small enough to come from L2; the maximum is exact,
+// so all of them find the same g) and then quantise their share of the
+// 8-element half-blocks; workgroup nblk runs the one-workgroup alignment.
+// No workgroup waits for another.
+constexpr int64_t kFusedQuantMax = int64_t(1) << 18;  // elements of x
+
+__global__ __launch_bounds__(1024) void quant_align_kernel(const uint16_t* __restrict__ x, int64_t T,
+                                                           int64_t H, float* __restrict__ g,
+                                                           uint8_t* __restrict__ q,
+                                                           uint8_t* __restrict__ sf,
+                                                           uint16_t* __restrict__ x_deq, int nblk,
+                                                           AlignP a, int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ sorted_pair,
+                                                           int32_t* __restrict__ inv_pos,
+                                                           int32_t* __restrict__ plan, int4 list_off) {
+  if ((int)blockIdx.x == nblk) {
+    align_small_body(a, offsets, sorted_pair, inv_pos, plan, list_off);
+    return;
+  }
+  __shared__ float red[16];
+  const int64_t n = T * H;
+  float m = 0.0f;
+  // 16 independent loads per trip, one trip at T*H = 2^17 (indices past
+  // the end are clamped to the last 8 elements: re-reading them cannot change
+  // a maximum).  For finite bf16 values, |x| orders like the unsigned 15-bit
+  // pattern, so the maximum is taken on packed 16-bit integers.
+  constexpr int U = 16;
+  u16x2 mm = {0, 0};
+  for (int64_t base = (int64_t)threadIdx.x * 8; base < n; base += U * 1024 * 8) {
+    u32x4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      w[u] = *reinterpret_cast<const u32x4*>(x + min(base + (int64_t)u * 1024 * 8, n - 8));
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        mm = __builtin_elementwise_max(mm, __builtin_bit_cast(u16x2, w[u][j] & 0x7FFF7FFFu));
+  }
+  m = bf16_bits_to_f32(max((uint32_t)mm[0], (uint32_t)mm[1]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) r = fmaxf(r, red[i]);
+  const float gv = global_scale_of_amax(r);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *g = gv;
+  // Half-blocks i (8 elements); both lanes of a block have the same trip
+  // count because n / 8 is even (H is a multiple of 128).
+  const int64_t hb_per_row = H >> 3;
+  for (int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x; i < n / 8; i += (int64_t)nblk * 1024) {
+    const int64_t row = i / hb_per_row;
+    quantize_half_block(x, row, (i - row * hb_per_row) << 3, H, H, gv, q, sf, x_deq);
+  }
+}
+
 // ---------------------------------------------------------------- router
 // One wavefront per token: k rounds of (max logit, lowest id) selection.
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
@@ -490,6 +552,33 @@ hipError_t launch_scale_and_align(const AlignShape& a, const uint16_t* x, float*
   const int4 lo = make_int4((int)a.list_off[0], (int)a.list_off[1], (int)a.list_off[2], (int)a.list_off[3]);
   scale_align_kernel<<<nblk + 1, 1024, 0, s>>>(x, n, g, static_cast<uint32_t*>(gs_ws), nblk, p, offsets,
                                                sorted_pair, inv_pos, plan, lo);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_and_align(const AlignShape& a, const uint16_t* x, float* g, void* gs_ws,
+                                    uint8_t* q, uint8_t* sf, uint16_t* x_deq,
+                                    const int32_t* topk_ids, int32_t* offsets, int32_t* sorted_pair,
+                                    int32_t* inv_pos, int32_t* plan, void* ws, hipStream_t s) {
+  const int64_t n = (int64_t)a.T * a.H;
+  if (a.P > (int64_t)kSmallP || n == 0 || n > kFusedQuantMax) {
+    hipError_t e = launch_scale_and_align(a, x, g, gs_ws, topk_ids, offsets, sorted_pair, inv_pos, plan,
+                                          ws, s);
+    if (e != hipSuccess) return e;
+    return launch_quantize(x, 0, a.T, a.H, a.H, g, a.T, q, sf, x_deq, s);
+  }
+  AlignP p;
+  p.ids = topk_ids;
+  p.T = a.T;
+  p.topk = a.topk;
+  p.E = a.E;
+  p.shared = a.shared;
+  p.slots = a.slots;
+  p.nchunks = a.nchunks;
+  p.P = a.P;
+  const int nblk = (int)((n / 8 + 1023) / 1024);  // 1 .. 32
+  const int4 lo = make_int4((int)a.list_off[0], (int)a.list_off[1], (int)a.list_off[2], (int)a.list_off[3]);
+  quant_align_kernel<<<nblk + 1, 1024, 0, s>>>(x, a.T, a.H, g, q, sf, x_deq, nblk, p, offsets, sorted_pair,
+                                               inv_pos, plan, lo);
   return hipGetLastError();
 }
 

@@ -179,6 +179,35 @@ int moe_scale_and_align(const nvfp4_moe_dims* d, const uint16_t* x, float* g1, v
                                                 inv_pos, plan, ws, S(stream)), W);
 }
 
+int moe_quantize_and_align(const nvfp4_moe_dims* d, const uint16_t* x, float* g1, void* gs_ws,
+                           size_t gs_ws_bytes, uint8_t* a1_q, uint8_t* a1_sf, uint16_t* a1_deq,
+                           const int32_t* topk_ids, int32_t* expert_offsets, int32_t* sorted_pair,
+                           int32_t* inv_pos, int32_t* plan, void* ws, size_t ws_bytes, void* stream) {
+  const char* W = "moe_quantize_and_align";
+  if (int r = check_dims(d, W)) return r;
+  nvfp4::AlignShape a = nvfp4::align_shape(d->T, d->topk, d->E, d->shared);
+  a.H = d->H;
+  if (!expert_offsets || !plan || !g1) return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
+  if (a.P > 0 && (!sorted_pair || !inv_pos || (d->T * d->topk > 0 && !topk_ids) || !x))
+    return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
+  if (d->T > 0 && (!a1_q || !a1_sf)) return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
+  if (!aligned(x, 16) || !aligned(g1, 4) || !aligned(gs_ws, 4) || !aligned(a1_q, 4) ||
+      !aligned(a1_deq, 16))
+    return fail(NVFP4_EINVAL, "%s: EINVAL misaligned x, g1, gs_ws, a1_q or a1_deq", W);
+  const size_t gs_need = nvfp4_global_scale_workspace_size(1, (int64_t)d->T * d->H);
+  if (gs_ws_bytes < gs_need || !gs_ws)
+    return fail(NVFP4_EWORKSPACE, "%s: EWORKSPACE global-scale workspace_size=%zu needed=%zu", W,
+                gs_ws_bytes, gs_need);
+  const size_t need = nvfp4::align_ws_bytes(a);
+  if (ws_bytes < need || (need && !ws))
+    return fail(NVFP4_EWORKSPACE, "%s: EWORKSPACE num_experts=%d M=%lld workspace_size=%zu needed=%zu",
+                W, d->E, (long long)a.P, ws_bytes, need);
+  return launched(nvfp4::launch_quantize_and_align(a, x, g1, gs_ws, a1_q, a1_sf, a1_deq, topk_ids,
+                                                   expert_offsets, sorted_pair, inv_pos, plan, ws,
+                                                   S(stream)),
+                  W);
+}
+
 // ------------------------------------------------------------------ weights
 size_t nvfp4_prep_weights_size(const nvfp4_moe_dims* d, int which) {
   if (check_dims(d, "nvfp4_prep_weights_size") || (which != 13 && which != 2)) return 0;

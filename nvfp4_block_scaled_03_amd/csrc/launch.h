@@ -45,6 +45,13 @@ hipError_t launch_align(const AlignShape& a, const int32_t* topk_ids, int32_t* o
 hipError_t launch_scale_and_align(const AlignShape& a, const uint16_t* x, float* g, void* gs_ws,
                                   const int32_t* topk_ids, int32_t* offsets, int32_t* sorted_pair,
                                   int32_t* inv_pos, int32_t* plan, void* ws, hipStream_t s);
+// Global scale, NVFP4 quantisation (+ optional exact f16 copy) and alignment:
+// one launch when the activations are decode-sized (T * H <= 2^18 and the
+// pairs fit one workgroup), else scale_and_align followed by quantize.
+hipError_t launch_quantize_and_align(const AlignShape& a, const uint16_t* x, float* g, void* gs_ws,
+                                    uint8_t* q, uint8_t* sf, uint16_t* x_deq,
+                                    const int32_t* topk_ids, int32_t* offsets, int32_t* sorted_pair,
+                                    int32_t* inv_pos, int32_t* plan, void* ws, hipStream_t s);
 
 // Weight streaming layout.  For an expert matrix [N][K] (N output columns,
 // K contraction, KC = K/128 chunks): codes [N/16][KC][64 lanes][16 B]

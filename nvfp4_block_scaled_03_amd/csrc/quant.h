@@ -1,0 +1,74 @@
+// Per-lane NVFP4 block quantisation shared by the quantisation kernels.
+//
+// A lane takes 8 consecutive elements of a row; the two lanes of a
+// 16-element block are adjacent (even lane first), so the block amax is one
+// DPP exchange.  Decisions are exact (see common.h): the E4M3 block scale is
+// the nearest value to amax / (6 g), the E2M1 codes the nearest magnitudes
+// to |x| / (s g), ties to the even code.
+#pragma once
+
+#include "common.h"
+
+namespace nvfp4 {
+
+// Load 8 consecutive elements as floats (x is 16-byte aligned at i).
+__device__ __forceinline__ void load8(const uint16_t* x, int64_t i, float v[8]) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(x + i);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = bf16_bits_to_f32(w[j] & 0xFFFFu);
+    v[2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+  }
+}
+__device__ __forceinline__ void load8(const float* x, int64_t i, float v[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(x + i);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(x + i + 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[j] = a[j];
+    v[4 + j] = b[j];
+  }
+}
+
+// Value of the E2M1 code c (sign in bit 3) times the block scale s, exact
+// in f16 (at most six significant bits, magnitude in [2^-10, 2688]).
+__device__ __forceinline__ uint32_t deq_f16_bits(uint32_t c, float s) {
+  const uint32_t m = c & 7u;
+  const float mag = m < 2 ? 0.5f * (float)m
+                          : __int_as_float((int)(((m >> 1) + 126u) << 23)) * (1.0f + 0.5f * (float)(m & 1u));
+  const float v = (c & 8u) ? -(mag * s) : mag * s;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+// Quantise elements [c8, c8 + 8) of row ``row`` (both lanes of the block
+// must call this together).  Writes the 8 codes (4 bytes), the block scale
+// (from the even lane) and, with x_deq, the exact f16 values code * scale.
+template <typename T>
+__device__ __forceinline__ void quantize_half_block(const T* __restrict__ x, int64_t row, int64_t c8,
+                                                    int64_t K, int64_t ldx, float gv,
+                                                    uint8_t* __restrict__ q, uint8_t* __restrict__ sf,
+                                                    uint16_t* __restrict__ x_deq) {
+  float v[8];
+  load8(x, row * ldx + c8, v);
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+  m = fmaxf(m, dpp_xor1(m));
+  const uint32_t sc = e4m3_scale_code(m, gv);
+  const float s = e4m3_value(sc);
+  const E2M1Bounds bd = e2m1_bounds(s, gv);
+  uint32_t word = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) word |= e2m1_code(v[j], bd, sc == 0) << (4 * j);
+  *reinterpret_cast<uint32_t*>(q + row * (K >> 1) + (c8 >> 1)) = word;
+  if ((c8 & 15) == 0) sf[row * (K >> 4) + (c8 >> 4)] = (uint8_t)sc;
+  if (x_deq) {
+    u32x4 d;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      d[j] = deq_f16_bits((word >> (8 * j)) & 15u, s) | (deq_f16_bits((word >> (8 * j + 4)) & 15u, s) << 16);
+    *reinterpret_cast<u32x4*>(x_deq + row * K + c8) = d;
+  }
+}
+
+}  // namespace nvfp4

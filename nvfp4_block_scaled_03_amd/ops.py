@@ -117,6 +117,24 @@ def moe_align(d: Dims, topk_ids: torch.Tensor, al: Optional[Alignment] = None) -
     return al
 
 
+def quantize_and_align(d: Dims, x: torch.Tensor, topk_ids: torch.Tensor, al: Optional[Alignment] = None,
+                       deq: Optional[torch.Tensor] = None):
+    """Global scale, NVFP4 quantisation and moe_align of bf16 ``x`` [T, H] in
+    one call: (g, codes, scales, Alignment); ``deq`` optionally receives the
+    exact f16 values."""
+    _need_cuda(x, topk_ids)
+    al = al or alloc_alignment(d, x.device)
+    g = torch.empty(1, dtype=torch.float32, device=x.device)
+    q = torch.empty(max(d.T, 1), d.H // 2, dtype=torch.uint8, device=x.device)
+    sf = torch.empty(max(d.T, 1), d.H // 16, dtype=torch.uint8, device=x.device)
+    wsb = _lib.load().nvfp4_global_scale_workspace_size(1, d.T * d.H)
+    gs_ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=x.device)
+    call("moe_quantize_and_align", ctypes.byref(d), _p(x.contiguous()), _p(g), _p(gs_ws), wsb,
+         _p(q), _p(sf), _p(deq), _p(topk_ids.contiguous()), _p(al.offsets), _p(al.sorted_pair),
+         _p(al.inv_pos), _p(al.plan), _p(al.workspace), al.workspace.numel(), _stream())
+    return g, q, sf, al
+
+
 def scale_and_align(d: Dims, x: torch.Tensor, topk_ids: torch.Tensor, al: Optional[Alignment] = None):
     """Activation global scale of bf16 ``x`` [T, H] and moe_align in one call: (g, Alignment)."""
     _need_cuda(x, topk_ids)
@@ -309,13 +327,12 @@ class MoELayer:
             out = torch.empty(d.T, d.H, dtype=out_dtype, device=x.device)
         s = _stream()
         if variant == "w4a4":
-            # Activation global scale and the permutation in one launch.
-            call("moe_scale_and_align", ctypes.byref(d), _p(x), _p(self.g1), _p(self.gs_ws),
-                 self.gs_ws_bytes, _p(topk_ids), _p(self.al.offsets), _p(self.al.sorted_pair),
-                 _p(self.al.inv_pos), _p(self.al.plan), _p(self.al.workspace),
-                 self.al.workspace.numel(), s)
-            call("nvfp4_quantize", _p(x), NVFP4_BF16, d.T, d.H, d.H, _p(self.g1), d.T,
-                 _p(self.a1_q), _p(self.a1_sf), _p(self.a1_deq), s)
+            # Activation global scale, quantisation and the permutation (one
+            # launch for decode-sized batches).
+            call("moe_quantize_and_align", ctypes.byref(d), _p(x), _p(self.g1), _p(self.gs_ws),
+                 self.gs_ws_bytes, _p(self.a1_q), _p(self.a1_sf), _p(self.a1_deq), _p(topk_ids),
+                 _p(self.al.offsets), _p(self.al.sorted_pair), _p(self.al.inv_pos), _p(self.al.plan),
+                 _p(self.al.workspace), self.al.workspace.numel(), s)
         else:
             call("moe_align", ctypes.byref(d), _p(topk_ids), _p(self.al.offsets),
                  _p(self.al.sorted_pair), _p(self.al.inv_pos), _p(self.al.plan),

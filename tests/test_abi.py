@@ -112,6 +112,17 @@ def test_zero_tokens_is_a_noop(lib):
     assert _lib.last_error() == ""
 
 
+def test_quantize_and_align_errors(lib):
+    d = _d()
+    # null outputs are rejected before anything is launched
+    args = [None, None, None, 0] + [None] * 9 + [0, None]
+    rc = lib.moe_quantize_and_align(ctypes.byref(d), *args)
+    assert rc == _lib.NVFP4_EINVAL and _lib.last_error().startswith("moe_quantize_and_align:")
+    d = _d(H=2000)
+    rc = lib.moe_quantize_and_align(ctypes.byref(d), *args)
+    assert rc == _lib.NVFP4_ESHAPE and "multiples of 128" in _lib.last_error()
+
+
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(_lib.LibraryNotBuilt):
         old = _lib._lib

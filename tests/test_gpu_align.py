@@ -126,3 +126,28 @@ def test_scale_and_align(dev, name):
         assert to_np(g)[0] == onv.global_scale(to_np(x).astype(np.float64))
         _check_align(dev, ids, w.E, w.shared, al=al)
         assert not gs_ws.any()
+
+
+_LIMIT = moe_inputs.Workload("limit", 128, 2048, 256, 64, 6, 1, 1.1, 0.02, 0.01, 41)  # T*H = 2^18
+
+
+@pytest.mark.parametrize("name", ["decode", "tiny", "limit", "large_e", "prefill"])
+def test_quantize_and_align(dev, name):
+    """One call = global scale + quantisation (+ exact f16 copy) + alignment,
+    bit-exact against the oracle: one launch up to T*H = 2^18 and P = 4096
+    (decode, tiny, limit), the separate launches beyond (large_e, prefill)."""
+    w = _LIMIT if name == "limit" else moe_inputs.WORKLOADS[name]
+    x = moe_inputs.activations(w, device=dev)
+    ids, _ = oroute.route_topk(to_np(moe_inputs.router_logits(w, device=dev)), w.topk)
+    d = ops.dims(w.T, w.topk, w.E, w.H, w.I, w.shared)
+    xf = to_np(x).astype(np.float64)
+    g_ref = onv.global_scale(xf)
+    codes, scales = onv.quantize(xf, g_ref)
+    for _ in range(2):   # the second call must not depend on state the first left
+        deq = torch.empty(w.T, w.H, dtype=torch.float16, device=dev)
+        g, q, sf, al = ops.quantize_and_align(d, x, torch.from_numpy(ids).to(dev), deq=deq)
+        assert to_np(g)[0] == g_ref
+        assert np.array_equal(to_np(q), onv.pack_codes(codes))
+        assert np.array_equal(to_np(sf), scales)
+        assert np.array_equal(to_np(deq).astype(np.float64), onv.dequantize(codes, scales, 1.0))
+        _check_align(dev, ids, w.E, w.shared, al=al)
