@@ -561,10 +561,17 @@ __global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
 #ifndef NVFP4_WIDE_NW
 #define NVFP4_WIDE_NW 4        // wavefronts per workgroup of the wide kernel (4 or 8)
 #endif
-constexpr int kWideBM = 128, kWideWN = 64, kWideNW = NVFP4_WIDE_NW;
+#ifndef NVFP4_WIDE_WN
+#define NVFP4_WIDE_WN 64       // columns per wavefront of the wide kernel (64 or 128)
+#endif
+// Waves per SIMD: 2 with 64 columns per wavefront, 1 with 128 (its 256
+// accumulators take the accumulation registers).
+#define NVFP4_WIDE_WPE (NVFP4_WIDE_WN == 128 ? 1 : 2)
+constexpr int kWideBM = 128, kWideWN = NVFP4_WIDE_WN, kWideNW = NVFP4_WIDE_NW;
 
 template <int AK, int EPI>
-__global__ __launch_bounds__(kWideNW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kWideNW * kWave)
+__attribute__((amdgpu_waves_per_eu(NVFP4_WIDE_WPE, NVFP4_WIDE_WPE)))
 void grouped_gemm_wide_kernel(KParams p) {
   static_assert(kWideNW == 4 || kWideNW == 8, "4 or 8 wavefronts");
   static_assert(AK != kActCodes, "the wide kernel takes 16-bit activations");
