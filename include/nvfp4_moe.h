@@ -166,6 +166,17 @@ int nvfp4_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ld
 int moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t topk, int32_t* ids,
                    float* weights, void* stream);
 
+/* Router and permutation in one call: the same results, bit for bit, as
+ * moe_route_topk(logits, T, E, topk, topk_ids, topk_w) followed by
+ * moe_align(dims, topk_ids, ...), with moe_align's dims, output and
+ * workspace contracts (topk <= 32 for the router).  logits float32 [T][E];
+ * topk_ids int32 [T][topk] and topk_w float32 [T][topk] are written.  The
+ * two steps run as two launches on the stream (the router is a per-token
+ * latency chain; one workgroup doing both measured slower). */
+int moe_route_and_align(const nvfp4_moe_dims* dims, const float* logits, int32_t* topk_ids,
+                        float* topk_w, int32_t* expert_offsets, int32_t* sorted_pair, int32_t* inv_pos,
+                        int32_t* plan, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Permutation by expert.                                                    */
 /* ------------------------------------------------------------------------ */

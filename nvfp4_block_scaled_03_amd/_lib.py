@@ -50,6 +50,8 @@ SIGNATURES = {
                           c_void_p]),
     "moe_scale_and_align": (c_int, [_P, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, c_void_p,
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "moe_route_and_align": (c_int, [_P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                    c_void_p, c_void_p, c_size_t, c_void_p]),
     "moe_quantize_and_align": (c_int, [_P, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, c_void_p,
                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_void_p, c_size_t, c_void_p]),

@@ -416,14 +416,13 @@ __global__ __launch_bounds__(1024) void quant_align_kernel(const uint16_t* __res
 
 // ---------------------------------------------------------------- router
 // One wavefront per token: k rounds of (max logit, lowest id) selection.
-__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
-                                                         int E, int k, int32_t* __restrict__ ids,
-                                                         float* __restrict__ wts) {
-  __shared__ float sel_v[4][32];
-  __shared__ int sel_i[4][32];
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + w;
-  if (t >= T) return;
+// One wavefront routes token t: k rounds of (max logit, lowest id) over the
+// E logits (16 per lane), then the softmax over the selected logits in FP64.
+// sel_v / sel_i: this wavefront's 32-entry LDS scratch.
+__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, int E, int k,
+                                            int32_t* __restrict__ ids, float* __restrict__ wts,
+                                            float* sel_v, int* sel_i, double* sel_e) {
+  const int lane = threadIdx.x & 63;
   const float* z = logits + (int64_t)t * E;
   float v[16];
   uint32_t taken = 0;
@@ -439,36 +438,141 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const bool ok = !((taken >> i) & 1u);
-      if (ok && (v[i] > bv || (v[i] == bv && lane + 64 * i < bi))) {
-        bv = v[i];
-        bi = lane + 64 * i;
-      }
+      const bool better = ok && (v[i] > bv || (v[i] == bv && lane + 64 * i < bi));
+      bv = better ? v[i] : bv;
+      bi = better ? lane + 64 * i : bi;
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       const float ov = __shfl_xor(bv, off);
       const int oi = __shfl_xor(bi, off);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
+      const bool better = ov > bv || (ov == bv && oi < bi);
+      bv = better ? ov : bv;
+      bi = better ? oi : bi;
     }
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     if (lane == 0) {
-      sel_v[w][j] = bv;
-      sel_i[w][j] = bi;
+      sel_v[j] = bv;
+      sel_i[j] = bi;
     }
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  // Each selected exponential once (lane j), then the same sequential sum
+  // in every lane.
+  double mine = 0.0;
   if (lane < k) {
-    const double top = (double)sel_v[w][0];
+    mine = exp((double)sel_v[lane] - (double)sel_v[0]);
+    sel_e[lane] = mine;
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  if (lane < k) {
     double sum = 0.0;
-    for (int j = 0; j < k; ++j) sum += exp((double)sel_v[w][j] - top);
-    const double mine = exp((double)sel_v[w][lane] - top);
-    ids[(int64_t)t * k + lane] = sel_i[w][lane];
+    for (int j = 0; j < k; ++j) sum += sel_e[j];
+    ids[(int64_t)t * k + lane] = sel_i[lane];
     wts[(int64_t)t * k + lane] = (float)(mine / sum);
   }
+  // (the next token of this wavefront rewrites sel_v / sel_i only after all
+  // lanes have read them)
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+// One (value, index) step of the row reduction: keep the larger logit, the
+// lower id on equal logits.
+template <int CTRL>
+__device__ __forceinline__ void route_step(float& bv, int& bi) {
+  const float ov = __int_as_float(dpp_i<CTRL>(__float_as_int(bv)));
+  const int oi = dpp_i<CTRL>(bi);
+  const bool better = ov > bv || (ov == bv && oi < bi);
+  bv = better ? ov : bv;
+  bi = better ? oi : bi;
+}
+
+// The same selection by one 16-lane DPP row per token (E <= 256: logit
+// r + 16 i in lane r), so a wavefront routes 4 tokens at once and each of the
+// k rounds reduces over the row with 4 DPP steps.  Same choices and the same
+// FP64 softmax as route_token.
+__device__ __forceinline__ void route_token16(const float* __restrict__ logits, int t, int E, int k,
+                                              int32_t* __restrict__ ids, float* __restrict__ wts,
+                                              float* sel_v, int* sel_i, double* sel_e) {
+  const int r = threadIdx.x & 15;
+  const float* z = logits + (int64_t)t * E;
+  float v[16];
+  uint32_t taken = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int idx = r + 16 * i;
+    v[i] = idx < E ? z[idx] : -INFINITY;
+    if (idx >= E) taken |= 1u << i;
+  }
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bool ok = !((taken >> i) & 1u);
+      const bool better = ok && (v[i] > bv || (v[i] == bv && r + 16 * i < bi));
+      bv = better ? v[i] : bv;
+      bi = better ? r + 16 * i : bi;
+    }
+    route_step<0xB1>(bv, bi);   // lane ^ 1
+    route_step<0x4E>(bv, bi);   // lane ^ 2
+    route_step<0x141>(bv, bi);  // half-row mirror
+    route_step<0x140>(bv, bi);  // row mirror
+    if ((bi & 15) == r) taken |= 1u << (bi >> 4);
+    if (r == 0) {
+      sel_v[j] = bv;
+      sel_i[j] = bi;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  // Each selected exponential once (lane j % 16), then the same sequential
+  // sum as route_token.
+  for (int jj = r; jj < k; jj += 16) sel_e[jj] = exp((double)sel_v[jj] - (double)sel_v[0]);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  if (r < k) {
+    double sum = 0.0;
+    for (int j = 0; j < k; ++j) sum += sel_e[j];
+    for (int jj = r; jj < k; jj += 16) {
+      ids[(int64_t)t * k + jj] = sel_i[jj];
+      wts[(int64_t)t * k + jj] = (float)(sel_e[jj] / sum);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+}
+
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
+                                                         int E, int k, int32_t* __restrict__ ids,
+                                                         float* __restrict__ wts) {
+  __shared__ float sel_v[4][32];
+  __shared__ int sel_i[4][32];
+  __shared__ double sel_e[4][32];
+  const int w = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + w;
+  if (t >= T) return;
+  route_token(logits, t, E, k, ids, wts, sel_v[w], sel_i[w], sel_e[w]);
+}
+
+// 16 tokens per workgroup, one per 16-lane row (E <= 256).
+__global__ __launch_bounds__(256) void route_topk16_kernel(const float* __restrict__ logits, int T,
+                                                           int E, int k, int32_t* __restrict__ ids,
+                                                           float* __restrict__ wts) {
+  __shared__ float sel_v[16][32];
+  __shared__ int sel_i[16][32];
+  __shared__ double sel_e[16][32];
+  const int g = threadIdx.x >> 4;
+  const int t = blockIdx.x * 16 + g;
+  if (t >= T) return;   // whole rows leave together
+  route_token16(logits, t, E, k, ids, wts, sel_v[g], sel_i[g], sel_e[g]);
 }
 
 }  // namespace
@@ -584,8 +688,24 @@ hipError_t launch_quantize_and_align(const AlignShape& a, const uint16_t* x, flo
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                              hipStream_t s) {
-  route_topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, ids, w);
+  if (E <= 256)
+    route_topk16_kernel<<<(T + 15) / 16, 256, 0, s>>>(logits, T, E, k, ids, w);
+  else
+    route_topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, ids, w);
   return hipGetLastError();
+}
+
+hipError_t launch_route_and_align(const AlignShape& a, const float* logits, int32_t* ids, float* w,
+                                  int32_t* offsets, int32_t* sorted_pair, int32_t* inv_pos,
+                                  int32_t* plan, void* ws, hipStream_t s) {
+  // Two launches: routing is a latency chain per token (k rounds of a
+  // reduction), and one workgroup holding both steps (all tokens on one CU)
+  // measured slower than the router's own grid followed by the alignment.
+  if (a.T > 0) {
+    hipError_t e = launch_route_topk(logits, a.T, a.E, a.topk, ids, w, s);
+    if (e != hipSuccess) return e;
+  }
+  return launch_align(a, ids, offsets, sorted_pair, inv_pos, plan, ws, s);
 }
 
 }  // namespace nvfp4

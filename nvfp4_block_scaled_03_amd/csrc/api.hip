@@ -179,6 +179,26 @@ int moe_scale_and_align(const nvfp4_moe_dims* d, const uint16_t* x, float* g1, v
                                                 inv_pos, plan, ws, S(stream)), W);
 }
 
+int moe_route_and_align(const nvfp4_moe_dims* d, const float* logits, int32_t* topk_ids,
+                        float* topk_w, int32_t* expert_offsets, int32_t* sorted_pair, int32_t* inv_pos,
+                        int32_t* plan, void* ws, size_t ws_bytes, void* stream) {
+  const char* W = "moe_route_and_align";
+  if (int r = check_dims(d, W)) return r;
+  if (d->topk > 32)
+    return fail(NVFP4_ESHAPE, "%s: ESHAPE num_experts=%d topk=%d (router: topk <= 32)", W, d->E, d->topk);
+  nvfp4::AlignShape a = nvfp4::align_shape(d->T, d->topk, d->E, d->shared);
+  if (!expert_offsets || !plan) return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
+  if (a.P > 0 && (!sorted_pair || !inv_pos)) return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
+  if (d->T > 0 && (!logits || !topk_ids || !topk_w)) return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
+  const size_t need = nvfp4::align_ws_bytes(a);
+  if (ws_bytes < need || (need && !ws))
+    return fail(NVFP4_EWORKSPACE, "%s: EWORKSPACE num_experts=%d M=%lld workspace_size=%zu needed=%zu",
+                W, d->E, (long long)a.P, ws_bytes, need);
+  return launched(nvfp4::launch_route_and_align(a, logits, topk_ids, topk_w, expert_offsets, sorted_pair,
+                                                inv_pos, plan, ws, S(stream)),
+                  W);
+}
+
 int moe_quantize_and_align(const nvfp4_moe_dims* d, const uint16_t* x, float* g1, void* gs_ws,
                            size_t gs_ws_bytes, uint8_t* a1_q, uint8_t* a1_sf, uint16_t* a1_deq,
                            const int32_t* topk_ids, int32_t* expert_offsets, int32_t* sorted_pair,

@@ -48,6 +48,10 @@ hipError_t launch_scale_and_align(const AlignShape& a, const uint16_t* x, float*
 // Global scale, NVFP4 quantisation (+ optional exact f16 copy) and alignment:
 // one launch when the activations are decode-sized (T * H <= 2^18 and the
 // pairs fit one workgroup), else scale_and_align followed by quantize.
+// Router then alignment (two launches).
+hipError_t launch_route_and_align(const AlignShape& a, const float* logits, int32_t* ids, float* w,
+                                  int32_t* offsets, int32_t* sorted_pair, int32_t* inv_pos,
+                                  int32_t* plan, void* ws, hipStream_t s);
 hipError_t launch_quantize_and_align(const AlignShape& a, const uint16_t* x, float* g, void* gs_ws,
                                     uint8_t* q, uint8_t* sf, uint16_t* x_deq,
                                     const int32_t* topk_ids, int32_t* offsets, int32_t* sorted_pair,

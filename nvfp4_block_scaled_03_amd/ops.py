@@ -117,6 +117,19 @@ def moe_align(d: Dims, topk_ids: torch.Tensor, al: Optional[Alignment] = None) -
     return al
 
 
+def route_and_align(d: Dims, logits: torch.Tensor, al: Optional[Alignment] = None):
+    """Router (top-k + softmax over the selection) and moe_align in one call:
+    (topk_ids int32 [T, topk], topk_w float32 [T, topk], Alignment)."""
+    _need_cuda(logits)
+    al = al or alloc_alignment(d, logits.device)
+    ids = torch.empty(max(d.T, 1), d.topk, dtype=torch.int32, device=logits.device)
+    wts = torch.empty(max(d.T, 1), d.topk, dtype=torch.float32, device=logits.device)
+    call("moe_route_and_align", ctypes.byref(d), _p(logits.contiguous().float()), _p(ids), _p(wts),
+         _p(al.offsets), _p(al.sorted_pair), _p(al.inv_pos), _p(al.plan), _p(al.workspace),
+         al.workspace.numel(), _stream())
+    return ids[:d.T], wts[:d.T], al
+
+
 def quantize_and_align(d: Dims, x: torch.Tensor, topk_ids: torch.Tensor, al: Optional[Alignment] = None,
                        deq: Optional[torch.Tensor] = None):
     """Global scale, NVFP4 quantisation and moe_align of bf16 ``x`` [T, H] in

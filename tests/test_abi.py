@@ -112,6 +112,16 @@ def test_zero_tokens_is_a_noop(lib):
     assert _lib.last_error() == ""
 
 
+def test_route_and_align_errors(lib):
+    d = _d()
+    args = [None] * 8 + [0, None]
+    rc = lib.moe_route_and_align(ctypes.byref(d), *args)
+    assert rc == _lib.NVFP4_EINVAL and _lib.last_error().startswith("moe_route_and_align:")
+    d = _d(topk=40)
+    rc = lib.moe_route_and_align(ctypes.byref(d), *args)
+    assert rc == _lib.NVFP4_ESHAPE and "topk=40" in _lib.last_error()
+
+
 def test_quantize_and_align_errors(lib):
     d = _d()
     # null outputs are rejected before anything is launched

@@ -151,3 +151,24 @@ def test_quantize_and_align(dev, name):
         assert np.array_equal(to_np(sf), scales)
         assert np.array_equal(to_np(deq).astype(np.float64), onv.dequantize(codes, scales, 1.0))
         _check_align(dev, ids, w.E, w.shared, al=al)
+
+
+@pytest.mark.parametrize("name", ["decode", "tiny", "limit", "large_e", "skew", "ties"])
+def test_route_and_align(dev, name):
+    """One call = router + alignment (the 16-lane router for E <= 256, the
+    wavefront router for large_e's E = 512).  Ids and alignment bit-exact,
+    weights as in the router test."""
+    if name == "ties":
+        z = torch.tensor(np.random.default_rng(5).integers(-2, 3, (100, 40)), dtype=torch.float32, device=dev)
+        T, E, k, shared = 100, 40, 7, 1
+    else:
+        w = _LIMIT if name == "limit" else moe_inputs.WORKLOADS[name]
+        z = moe_inputs.router_logits(w, device=dev)
+        T, E, k, shared = w.T, w.E, w.topk, w.shared
+    d = ops.dims(T, k, E, 128, 128, shared)
+    rid, rw = oroute.route_topk(to_np(z), k)
+    for _ in range(2):
+        ids, wt, al = ops.route_and_align(d, z)
+        assert np.array_equal(to_np(ids), rid)
+        np.testing.assert_allclose(to_np(wt), rw, rtol=4e-7, atol=0)
+        _check_align(dev, rid, E, shared, al=al)
