@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_MOE_ABI_VERSION 3
+#define NVFP4_MOE_ABI_VERSION 4
 
 /* Status codes. */
 #define NVFP4_OK 0
@@ -229,6 +229,33 @@ int moe_quantize_and_align(const nvfp4_moe_dims* dims, const uint16_t* x, float*
                            size_t gs_ws_bytes, uint8_t* a1_q, uint8_t* a1_sf, uint16_t* a1_deq,
                            const int32_t* topk_ids, int32_t* expert_offsets, int32_t* sorted_pair,
                            int32_t* inv_pos, int32_t* plan, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Dense NVFP4 linear layer (the same kernels with one expert).              */
+/* ------------------------------------------------------------------------ */
+/* y [M][N] = x [M][K] W^T for an NVFP4 weight W [N][K] with global scale gw,
+ * the per-GEMM workload the pages time across batch sizes M with NVFP4
+ * activations against bf16 activations and weight dequantisation (unsloth
+ * PR #10417, "Why it matters").  x is bfloat16 [M][K] (16-byte aligned); the
+ * weight is prepared by nvfp4_prep_weights(dims, 2, ...) with dims
+ * {T: any, topk: 1, num_experts: 1, H: N, I: K, shared: 0} (the down
+ * projection's layout of one expert).  N and K are multiples of 128.
+ *   nvfp4_linear:        W4A4.  x gets a dynamic global scale and NVFP4
+ *                        quantisation (as nvfp4_global_scale + nvfp4_quantize),
+ *                        then y = g * gw * (x_hat W_hat^T) with FP32
+ *                        accumulation.
+ *   nvfp4_linear_w4a16:  W4A16.  y = gw * (x W_hat^T).
+ * out: bfloat16 (out_dtype 0, round to nearest even) or float32 (1) [M][N].
+ * ws: nvfp4_linear_workspace_size(M, N, K, w4a4) bytes, 256-byte aligned,
+ * zero-filled before its first use (the library leaves its counter words
+ * zero after every call).  Errors: NVFP4_ESHAPE, NVFP4_EINVAL,
+ * NVFP4_EWORKSPACE (message names M, N, K and the sizes). */
+size_t nvfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K, int w4a4);
+int nvfp4_linear(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w_prep,
+                 const float* gw, void* out, int out_dtype, void* ws, size_t ws_bytes, void* stream);
+int nvfp4_linear_w4a16(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w_prep,
+                       const float* gw, void* out, int out_dtype, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Weight preparation (offline).                                             */

@@ -23,7 +23,7 @@ struct AlignP {
 __device__ __forceinline__ int expert_of(const AlignP& a, int64_t f, bool& valid) {
   const int64_t tk = (int64_t)a.T * a.topk;
   if (f < tk) {
-    const int e = a.ids[f];
+    const int e = a.ids ? a.ids[f] : 0;   // no ids: every pair to expert 0 (dense use)
     valid = e >= 0 && e < a.E;
     return e;
   }

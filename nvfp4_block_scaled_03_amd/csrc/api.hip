@@ -4,6 +4,7 @@
 // message naming the call and the offending values (num_experts, M, N, K and
 // the workspace size for the GEMMs, like the grouped-GEMM initialisation error
 // of vLLM PR #29242, review of nvfp4_blockwise_moe_kernel.cu).
+#include <algorithm>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -226,6 +227,107 @@ int moe_quantize_and_align(const nvfp4_moe_dims* d, const uint16_t* x, float* g1
                                                    expert_offsets, sorted_pair, inv_pos, plan, ws,
                                                    S(stream)),
                   W);
+}
+
+// ------------------------------------------------------------------ dense linear
+namespace {
+// Workspace of nvfp4_linear*: 256-byte aligned sub-buffers in this order.
+struct LinearWs {
+  size_t g, gs, offsets, sorted_pair, inv_pos, plan, align, a_q, a_sf, a_deq, total;
+};
+size_t up256(size_t b) { return (b + 255) & ~size_t(255); }
+bool linear_shape_ok(int64_t M, int64_t N, int64_t K) {
+  return M >= 0 && M <= (int64_t(1) << 24) && N > 0 && K > 0 && N % 128 == 0 && K % 128 == 0 &&
+         N <= (int64_t(1) << 20) && K <= (int64_t(1) << 20);
+}
+LinearWs linear_ws(int64_t M, int64_t N, int64_t K, bool w4a4) {
+  const nvfp4::AlignShape a = nvfp4::align_shape((int)M, 1, 1, 0);
+  LinearWs w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += up256(bytes); return at; };
+  w.g = take(w4a4 ? 4 : 0);
+  w.gs = take(w4a4 ? nvfp4_global_scale_workspace_size(1, std::max<int64_t>(M * K, 8)) : 0);
+  w.offsets = take(2 * sizeof(int32_t));
+  w.sorted_pair = take((size_t)std::max<int64_t>(M, 1) * 4);
+  w.inv_pos = take((size_t)std::max<int64_t>(M, 1) * 4);
+  w.plan = take(nvfp4::align_plan_ints(a) * 4);
+  w.align = take(nvfp4::align_ws_bytes(a));
+  w.a_q = take(w4a4 ? (size_t)M * (K / 2) : 0);
+  w.a_sf = take(w4a4 ? (size_t)M * (K / 16) : 0);
+  w.a_deq = take(w4a4 && nvfp4::prefers_decoded((int)M, 1, 1, 0) ? (size_t)M * K * 2 : 0);
+  w.total = o;
+  return w;
+}
+
+int linear_run(const char* W, bool w4a4, const uint16_t* x, int64_t M, int64_t N, int64_t K,
+               const uint8_t* w_prep, const float* gw, void* out, int out_dtype, void* ws,
+               size_t ws_bytes, void* stream) {
+  if (!linear_shape_ok(M, N, K))
+    return fail(NVFP4_ESHAPE, "%s: ESHAPE M=%lld N=%lld K=%lld (N, K multiples of 128)", W, (long long)M,
+                (long long)N, (long long)K);
+  if (out_dtype != 0 && out_dtype != 1) return fail(NVFP4_EINVAL, "%s: EINVAL out_dtype=%d", W, out_dtype);
+  const LinearWs L = linear_ws(M, N, K, w4a4);
+  if (ws_bytes < L.total || !ws)
+    return fail(NVFP4_EWORKSPACE, "%s: EWORKSPACE num_experts=1 M=%lld N=%lld K=%lld workspace_size=%zu needed=%zu",
+                W, (long long)M, (long long)N, (long long)K, ws_bytes, L.total);
+  if (M == 0) return ok();
+  if (!x || !w_prep || !gw || !out) return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
+  if (!aligned(x, 16) || !aligned(w_prep, 16) || !aligned(ws, 256) || !aligned(out, 16))
+    return fail(NVFP4_EINVAL, "%s: EINVAL x, w_prep and out 16-byte, ws 256-byte aligned", W);
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  nvfp4::AlignShape a = nvfp4::align_shape((int)M, 1, 1, 0);
+  a.H = (int)K;
+  int32_t* offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  int32_t* sp = reinterpret_cast<int32_t*>(b + L.sorted_pair);
+  int32_t* inv = reinterpret_cast<int32_t*>(b + L.inv_pos);
+  int32_t* plan = reinterpret_cast<int32_t*>(b + L.plan);
+  nvfp4::LinearArgs la{};
+  la.M = M;
+  la.N = N;
+  la.K = K;
+  la.w4a4 = w4a4;
+  la.plan = plan;
+  la.w_prep = w_prep;
+  la.g_w = gw;
+  la.out = out;
+  la.out_dtype = out_dtype;
+  hipError_t e;
+  if (w4a4) {
+    float* g = reinterpret_cast<float*>(b + L.g);
+    uint8_t* aq = b + L.a_q;
+    uint8_t* asf = b + L.a_sf;
+    uint16_t* adeq = nvfp4::prefers_decoded((int)M, 1, 1, 0) ? reinterpret_cast<uint16_t*>(b + L.a_deq)
+                                                              : nullptr;
+    e = nvfp4::launch_quantize_and_align(a, x, g, b + L.gs, aq, asf, adeq, nullptr, offsets, sp, inv, plan,
+                                         b + L.align, S(stream));
+    la.g_a = g;
+    la.a_q = aq;
+    la.a_sf = asf;
+    la.a_h = adeq;
+  } else {
+    e = nvfp4::launch_align(a, nullptr, offsets, sp, inv, plan, b + L.align, S(stream));
+    la.a_h = x;
+  }
+  if (e != hipSuccess) return launched(e, W);
+  return launched(nvfp4::launch_linear(la, S(stream)), W);
+}
+}  // namespace
+
+size_t nvfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K, int w4a4) {
+  if (!linear_shape_ok(M, N, K)) return 0;
+  return linear_ws(M, N, K, w4a4 != 0).total;
+}
+
+int nvfp4_linear(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w_prep,
+                 const float* gw, void* out, int out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  return linear_run("nvfp4_linear", true, x, M, N, K, w_prep, gw, out, out_dtype, ws, ws_bytes, stream);
+}
+
+int nvfp4_linear_w4a16(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w_prep,
+                       const float* gw, void* out, int out_dtype, void* ws, size_t ws_bytes,
+                       void* stream) {
+  return linear_run("nvfp4_linear_w4a16", false, x, M, N, K, w_prep, gw, out, out_dtype, ws, ws_bytes,
+                    stream);
 }
 
 // ------------------------------------------------------------------ weights

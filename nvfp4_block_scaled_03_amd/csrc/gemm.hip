@@ -63,7 +63,8 @@ constexpr int kLDA = kBK + 8;  // LDS row stride in 16-bit elements (272 bytes)
 constexpr int kBufferFlags = 0x00020000;
 
 enum Act { kActCodes = 0, kActF16 = 1, kActBf16 = 2 };
-enum Epi { kEpiSwigluFp4 = 0, kEpiSwigluBf16 = 1, kEpiStoreF32 = 2 };
+enum Epi { kEpiSwigluFp4 = 0, kEpiSwigluBf16 = 1, kEpiStoreF32 = 2, kEpiStoreBf16 = 3 };
+constexpr bool swiglu_epi(int e) { return e == kEpiSwigluFp4 || e == kEpiSwigluBf16; }
 
 // Load of a value that is the same for the whole wavefront and not written
 // by the running kernel, through the scalar data cache (read-only use).  Its
@@ -122,7 +123,7 @@ __device__ __forceinline__ void epilogue(const KParams& p, f32x4 (&acc)[MT][NTW]
                                          int nrows, int n_wave0, int lane) {
   const float alpha = p.g_a ? ld_uniform(p.g_a) * ld_uniform(p.g_w + e) : ld_uniform(p.g_w + e);
   const int ln = lane & 15, lg = lane >> 4;
-  if constexpr (EPI == kEpiStoreF32) {
+  if constexpr (EPI == kEpiStoreF32 || EPI == kEpiStoreBf16) {
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -130,8 +131,13 @@ __device__ __forceinline__ void epilogue(const KParams& p, f32x4 (&acc)[MT][NTW]
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = i * 16 + lg * 4 + r;
-          if (row < nrows)
-            p.out_f32[(int64_t)(row0 + row) * p.N + n_wave0 + 16 * j + ln] = alpha * acc[i][j][r];
+          if (row < nrows) {
+            const int64_t o = (int64_t)(row0 + row) * p.N + n_wave0 + 16 * j + ln;
+            if constexpr (EPI == kEpiStoreF32)
+              p.out_f32[o] = alpha * acc[i][j][r];
+            else
+              p.out_h[o] = (uint16_t)f32_to_bf16_bits(alpha * acc[i][j][r]);
+          }
         }
   } else {
     const float g2 = (EPI == kEpiSwigluFp4) ? ld_uniform(p.g2) : 0.0f;
@@ -194,7 +200,7 @@ template <int EPI, int MT, int NTW>
 __device__ __forceinline__ void epilogue_blocks(const KParams& p, f32x4 (&acc)[MT][NTW], int e,
                                                 int row0, int nrows, int n_wave0, int lane,
                                                 float* __restrict__ sh) {
-  static_assert(EPI != kEpiStoreF32, "SwiGLU epilogues only");
+  static_assert(swiglu_epi(EPI), "SwiGLU epilogues only");
   constexpr int HC = 8 * NTW;                // h columns of the wave
   constexpr int BLOCKS = 16 * MT * (HC / 16);
   static_assert(BLOCKS % kWave == 0, "whole blocks per lane");
@@ -277,7 +283,7 @@ template <int EPI, int MT, int NTW>
 __device__ __forceinline__ void epilogue_rows(const KParams& p, f32x4 (&acc)[MT][NTW], int e,
                                               int row0, int nrows, int n_wave0, int lane,
                                               float* __restrict__ sh) {
-  static_assert(EPI != kEpiStoreF32, "SwiGLU epilogues only");
+  static_assert(swiglu_epi(EPI), "SwiGLU epilogues only");
   constexpr int HC = 8 * NTW;                // h columns of the wave
   const float alpha = p.g_a ? ld_uniform(p.g_a) * ld_uniform(p.g_w + e) : ld_uniform(p.g_w + e);
   const int ln = lane & 15, lg = lane >> 4;
@@ -776,7 +782,7 @@ void grouped_gemm_wide_kernel(KParams p) {
     if (!more2) break;
   }
   if (!wave_on) return;
-  if constexpr (EPI == kEpiStoreF32) {
+  if constexpr (!swiglu_epi(EPI)) {
     epilogue<EPI, MT, NTW>(p, acc, t.e, t.row0, t.nrows, n_wave0, lane);
   } else {
     // The activation buffers are free (the loop ended on a barrier after the
@@ -981,8 +987,8 @@ __device__ __forceinline__ void stream_body(const KParams& p) {
   };
 
   // SwiGLU epilogues: a wave-private h tile in LDS.
-  __shared__ float h_lds[EPI != kEpiStoreF32 ? kNW * 16 * MT * 16 * NTW : 1];
-  float* const sh = h_lds + (EPI != kEpiStoreF32 ? wq * 16 * MT * 16 * NTW : 0);
+  __shared__ float h_lds[swiglu_epi(EPI) ? kNW * 16 * MT * 16 * NTW : 1];
+  float* const sh = h_lds + (swiglu_epi(EPI) ? wq * 16 * MT * 16 * NTW : 0);
 
   f32x4 acc[MT][NTW];
   auto compute = [&](int slot) {
@@ -1078,7 +1084,7 @@ __device__ __forceinline__ void stream_body(const KParams& p) {
 #pragma unroll
       for (int j = 0; j < NTW / 2; ++j) bs[j] = bsn[j];
     }
-    if constexpr (EPI == kEpiStoreF32)
+    if constexpr (!swiglu_epi(EPI))
       epilogue<EPI, MT, NTW>(p, acc, cur.e, cur.row0, cur.nrows, cur.n0, lane);
     else
       epilogue_rows<EPI, MT, NTW>(p, acc, cur.e, cur.row0, cur.nrows, cur.n0, lane, sh);
@@ -1229,7 +1235,7 @@ hipError_t launch_stream_pf(const KParams& kp, int len, hipStream_t s) {
 
 template <int AK, int EPI>
 hipError_t launch_gemm(KParams kp, const AlignShape& al, hipStream_t s) {
-  constexpr int kStreamNTW = EPI == kEpiStoreF32 ? NVFP4_STREAM_NTW_DOWN : NVFP4_STREAM_NTW;
+  constexpr int kStreamNTW = swiglu_epi(EPI) ? NVFP4_STREAM_NTW : NVFP4_STREAM_NTW_DOWN;
   int li = min(pick_list(al.P, al.slots), NVFP4_LIST_MAX);
   // The streaming kernel addresses with 32-bit buffer offsets.
   const int64_t a_row_bytes = AK == kActCodes ? kp.K / 2 : 2 * (int64_t)kp.K;
@@ -1294,6 +1300,33 @@ hipError_t launch_gemm1(const GemmArgs& a, bool w4a4, hipStream_t s) {
   k.a_h = a.a_h;
   k.out_h = a.out_h;
   return launch_gemm<kActBf16, kEpiSwigluBf16>(k, al, s);
+}
+
+hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
+  AlignShape al = align_shape((int)a.M, 1, 1, 0);
+  KParams k{};
+  k.T = (int)a.M;
+  k.topk = 1;
+  k.N = (int)a.N;
+  k.K = (int)a.K;
+  k.plan = a.plan;
+  k.sorted_pair = nullptr;   // row m of the output is row m of x
+  k.a_rows = a.M;
+  k.w_q = a.w_prep;
+  k.w_sf = a.w_prep + (size_t)a.N * (a.K / 2);
+  k.g_w = a.g_w;
+  k.g_a = a.g_a;
+  k.a_q = a.a_q;
+  k.a_sf = a.a_sf;
+  k.a_h = a.a_h;
+  const bool f32 = a.out_dtype != 0;
+  if (f32) k.out_f32 = static_cast<float*>(a.out);
+  else k.out_h = static_cast<uint16_t*>(a.out);
+  if (!a.w4a4)
+    return f32 ? launch_gemm<kActBf16, kEpiStoreF32>(k, al, s) : launch_gemm<kActBf16, kEpiStoreBf16>(k, al, s);
+  if (a.a_h)
+    return f32 ? launch_gemm<kActF16, kEpiStoreF32>(k, al, s) : launch_gemm<kActF16, kEpiStoreBf16>(k, al, s);
+  return f32 ? launch_gemm<kActCodes, kEpiStoreF32>(k, al, s) : launch_gemm<kActCodes, kEpiStoreBf16>(k, al, s);
 }
 
 hipError_t launch_gemm2_combine(const GemmArgs& a, bool w4a4, hipStream_t s) {

@@ -108,4 +108,21 @@ hipError_t launch_gemm1(const GemmArgs& a, bool w4a4, hipStream_t s);
 bool prefers_decoded(int T, int topk, int E, int shared);
 hipError_t launch_gemm2_combine(const GemmArgs& a, bool w4a4, hipStream_t s);
 
+// Dense linear y [M][N] = x [M][K] W^T on the grouped-GEMM kernels with one
+// expert (plan from an alignment of M pairs to expert 0).
+struct LinearArgs {
+  int64_t M, N, K;
+  bool w4a4;
+  const int32_t* plan;
+  const uint8_t* w_prep;   // streaming layout of W [N][K] (one expert)
+  const float* g_w;        // weight global scale
+  const float* g_a;        // activation global scale (W4A4) or null
+  const uint8_t* a_q;      // W4A4 codes [M][K/2] + scales, or
+  const uint8_t* a_sf;
+  const uint16_t* a_h;     // the exact f16 copy (W4A4) / bf16 x (W4A16)
+  void* out;
+  int out_dtype;           // 0 bf16, 1 f32
+};
+hipError_t launch_linear(const LinearArgs& a, hipStream_t s);
+
 }  // namespace nvfp4

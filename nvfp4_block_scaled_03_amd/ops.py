@@ -258,6 +258,47 @@ def gemm2_w4a16(d: Dims, a2, al: Alignment, topk_w, w: ExpertWeights, out_dtype=
     return out
 
 
+# ---------------------------------------------------------------- dense linear
+class LinearWeight:
+    """An NVFP4 weight W [N, K] prepared for nvfp4_linear*."""
+
+    def __init__(self, prep: torch.Tensor, g: torch.Tensor, N: int, K: int):
+        self.prep, self.g, self.N, self.K = prep, g, N, K
+
+
+def prepare_linear_weight(w_q: torch.Tensor, w_sf: torch.Tensor, g: torch.Tensor) -> LinearWeight:
+    """From canonical NVFP4 (codes [N, K/2], scales [N, K/16], global scale)."""
+    N, K = w_q.shape[0], w_q.shape[1] * 2
+    d = dims(1, 1, 1, N, K, 0)
+    prep = prep_weights(d, 2, w_q.reshape(1, N, K // 2), w_sf.reshape(1, N, K // 16))
+    return LinearWeight(prep, g.reshape(1).float(), N, K)
+
+
+def quantize_linear_weight(w: torch.Tensor) -> LinearWeight:
+    """FP32 W [N, K] -> global scale, NVFP4 quantisation on the GPU, prep."""
+    g = global_scale(w)
+    q, sf = quantize(w.contiguous().float(), g)
+    return prepare_linear_weight(q, sf, g)
+
+
+def linear_workspace(M: int, N: int, K: int, w4a4: bool, device) -> torch.Tensor:
+    n = _lib.load().nvfp4_linear_workspace_size(M, N, K, int(w4a4))
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def linear(x: torch.Tensor, w: LinearWeight, variant: str = "w4a4", out_dtype=torch.bfloat16,
+           out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y [M, N] = x [M, K] W^T (bf16 x; W4A4 quantises x, W4A16 uses it as is)."""
+    _need_cuda(x)
+    M = x.shape[0]
+    w4a4 = variant == "w4a4"
+    out = out if out is not None else torch.empty(M, w.N, dtype=out_dtype, device=x.device)
+    ws = ws if ws is not None else linear_workspace(M, w.N, w.K, w4a4, x.device)
+    call("nvfp4_linear" if w4a4 else "nvfp4_linear_w4a16", _p(x.contiguous()), M, w.N, w.K, _p(w.prep),
+         _p(w.g), _p(out), _dtype_code(out), _p(ws), ws.numel(), _stream())
+    return out
+
+
 # ---------------------------------------------------------------- the layer
 class MoELayer:
     """One NVFP4 expert layer with all intermediates preallocated, so that a

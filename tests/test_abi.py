@@ -122,6 +122,18 @@ def test_route_and_align_errors(lib):
     assert rc == _lib.NVFP4_ESHAPE and "topk=40" in _lib.last_error()
 
 
+def test_linear_size_and_errors(lib):
+    assert lib.nvfp4_linear_workspace_size(64, 2048, 768, 1) > 64 * 768 // 2
+    assert lib.nvfp4_linear_workspace_size(64, 2048, 768, 0) > 0
+    assert lib.nvfp4_linear_workspace_size(64, 2000, 768, 1) == 0
+    rc = lib.nvfp4_linear(None, 64, 2000, 768, None, None, None, 0, None, 0, None)
+    assert rc == _lib.NVFP4_ESHAPE and "N=2000" in _lib.last_error()
+    rc = lib.nvfp4_linear_w4a16(None, 64, 2048, 768, None, None, None, 0, None, 0, None)
+    assert rc == _lib.NVFP4_EWORKSPACE and "M=64" in _lib.last_error()
+    rc = lib.nvfp4_linear(None, 64, 2048, 768, None, None, None, 7, None, 0, None)
+    assert rc == _lib.NVFP4_EINVAL and "out_dtype=7" in _lib.last_error()
+
+
 def test_quantize_and_align_errors(lib):
     d = _d()
     # null outputs are rejected before anything is launched
