@@ -48,6 +48,7 @@ def parse():
     p.add_argument("--mode", default="graph", choices=["eager", "graph"])
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-linear", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     return p.parse_args()
 
@@ -259,6 +260,56 @@ def measure(w, d, x, ids, tw, wq, g2, a, steps, warmup):
     }
 
 
+LINEAR_N, LINEAR_K = 34816, 5120          # the pages' per-GEMM shape (27B gate_up)
+LINEAR_MS = (1, 16, 64, 256, 1024, 4096)
+
+
+def linear_sweep(dev, copies=3, reps=10):
+    """Dense NVFP4 linear y = x W^T across batch sizes M, W4A4 (quantisation
+    of x included) and W4A16, each timed as ``reps`` calls replayed from one
+    graph with weight copies rotated past the Infinity Cache."""
+    N, K = LINEAR_N, LINEAR_K
+    g = torch.Generator(device=dev).manual_seed(21)
+    w = 0.02 * torch.randn(N, K, generator=g, device=dev)
+    lw = ops.quantize_linear_weight(w)
+    del w
+    ws = [lw] + [ops.LinearWeight(lw.prep.clone(), lw.g.clone(), N, K) for _ in range(copies - 1)]
+    rows = []
+    for M in LINEAR_MS:
+        x = torch.randn(M, K, generator=g, device=dev).to(torch.bfloat16)
+        row = {"M": M}
+        for variant in ("w4a4", "w4a16"):
+            out = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            work = ops.linear_workspace(M, N, K, variant == "w4a4", dev)
+            for i in range(copies):
+                ops.linear(x, ws[i], variant, out=out, ws=work)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(reps):
+                    ops.linear(x, ws[i % copies], variant, out=out, ws=work)
+            graph.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            flops = 2.0 * M * N * K
+            nbytes = N * K * 0.5625 + M * K * 2 + M * N * 2
+            row[f"{variant}_us"] = round(us, 2)
+            row[f"{variant}_tflops"] = round(flops / us / 1e6, 1)
+            row[f"{variant}_gbs"] = round(nbytes / us / 1e3, 1)
+            row[f"{variant}_hbm_frac"] = round(nbytes / us / 1e3 / HBM_PEAK_GBS, 3)
+            row[f"{variant}_mfma_frac"] = round(flops / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 3)
+        row["w4a16_over_w4a4"] = round(row["w4a16_us"] / row["w4a4_us"], 2)
+        rows.append(row)
+    return {"shape": {"N": N, "K": K}, "weight_copies": copies, "calls_per_graph": reps,
+            "w4a4_includes": "global scale + quantisation of x + tile plan + GEMM",
+            "w4a16_includes": "tile plan + GEMM", "rows": rows}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -303,6 +354,9 @@ def main():
         res["prefill"] = {"T": wp.T, "tokens_per_s": round(mp["tokens_per_s"], 1),
                           "ms_per_step": round(mp["ms"], 5), "layer_tflops": mp["layer_tflops"],
                           "layer_mfma_frac": mp["layer_mfma_frac"], "roofline": mp["roofline"]}
+    if a.workload == "decode" and not a.no_linear:
+        log("[bench] dense linear M sweep")
+        res["linear"] = linear_sweep(dev)
     if not a.no_cpu:
         log("[bench] cpu baseline")
         res["cpu_baseline"] = cpu_baseline(w, dev, ids, tw, a.cpu_seconds)

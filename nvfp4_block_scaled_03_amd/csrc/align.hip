@@ -240,10 +240,41 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(AlignP a,
 constexpr int kSmallP = 4096;
 constexpr int kSmallPer = kSmallP / 1024;
 
+// Dense use (no ids, one expert): the identity permutation and the tile
+// lists of one expert with P rows, written directly (no counting, no scans).
+__device__ __forceinline__ void dense_plan_body(const AlignP& a, int32_t* __restrict__ offsets,
+                                                int32_t* __restrict__ sorted_pair,
+                                                int32_t* __restrict__ inv_pos,
+                                                int32_t* __restrict__ plan, int4 list_off) {
+  const int P = (int)a.P, tid = threadIdx.x;
+  for (int f = tid; f < P; f += blockDim.x) {
+    sorted_pair[f] = f;
+    inv_pos[f] = f;
+  }
+  const int lo[4] = {list_off.x, list_off.y, list_off.z, list_off.w};
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int n_t = (P + kPlanBMs[b] - 1) / kPlanBMs[b];
+    for (int mt = tid; mt < n_t; mt += blockDim.x) write_tile(plan + lo[b] + 2 * mt, 0, mt, kPlanBMs[b], 0, P);
+    if (tid == 0) {
+      plan[b] = n_t;
+      plan[4 + b] = lo[b];
+    }
+  }
+  if (tid == 0) {
+    offsets[0] = 0;
+    offsets[1] = P;
+  }
+}
+
 __device__ __forceinline__ void align_small_body(const AlignP& a, int32_t* __restrict__ offsets,
                                                  int32_t* __restrict__ sorted_pair,
                                                  int32_t* __restrict__ inv_pos,
                                                  int32_t* __restrict__ plan, int4 list_off) {
+  if (a.ids == nullptr && a.slots == 1) {
+    dense_plan_body(a, offsets, sorted_pair, inv_pos, plan, list_off);
+    return;
+  }
   __shared__ int seg[kSmallP];
   __shared__ int cnt[kMaxExperts];
   __shared__ int start[kMaxExperts];
