@@ -35,6 +35,7 @@ from nvfp4_block_scaled_03_amd import ops  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense FP16/BF16 matrix peak
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 matrix peak
 INFINITY_CACHE = 256 << 20
 
 
@@ -264,50 +265,69 @@ LINEAR_N, LINEAR_K = 34816, 5120          # the pages' per-GEMM shape (27B gate_
 LINEAR_MS = (1, 16, 64, 256, 1024, 4096)
 
 
+def _graph_us(fn, reps):
+    """Average microseconds of fn(i) for i in range(reps), replayed from one graph."""
+    fn(0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(reps):
+            fn(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
 def linear_sweep(dev, copies=3, reps=10):
-    """Dense NVFP4 linear y = x W^T across batch sizes M, W4A4 (quantisation
-    of x included) and W4A16, each timed as ``reps`` calls replayed from one
-    graph with weight copies rotated past the Infinity Cache."""
+    """Dense linear y = x W^T across batch sizes M: NVFP4 W4A4 (quantisation
+    of x included), NVFP4 W4A16, and OCP MXFP4 (x quantised in the call, the
+    codes fed to the scaled FP4 matrix instruction), each timed as ``reps``
+    calls replayed from one graph with weight copies rotated past the
+    Infinity Cache."""
     N, K = LINEAR_N, LINEAR_K
     g = torch.Generator(device=dev).manual_seed(21)
     w = 0.02 * torch.randn(N, K, generator=g, device=dev)
     lw = ops.quantize_linear_weight(w)
+    mw = ops.quantize_mx_weight(w)
     del w
     ws = [lw] + [ops.LinearWeight(lw.prep.clone(), lw.g.clone(), N, K) for _ in range(copies - 1)]
+    mws = [mw] + [ops.MxLinearWeight(mw.prep.clone(), N, K) for _ in range(copies - 1)]
+    peaks = {"w4a4": MFMA_F16_PEAK_TFLOPS, "w4a16": MFMA_F16_PEAK_TFLOPS, "mxfp4": MFMA_FP4_PEAK_TFLOPS}
+    w_bytes = {"w4a4": N * K * 0.5625, "w4a16": N * K * 0.5625, "mxfp4": N * K * (0.5 + 1 / 32)}
     rows = []
     for M in LINEAR_MS:
         x = torch.randn(M, K, generator=g, device=dev).to(torch.bfloat16)
         row = {"M": M}
-        for variant in ("w4a4", "w4a16"):
+        for variant in ("w4a4", "w4a16", "mxfp4"):
             out = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-            work = ops.linear_workspace(M, N, K, variant == "w4a4", dev)
+            if variant == "mxfp4":
+                work = ops.mx_linear_workspace(M, N, K, dev)
+                fn = lambda i: ops.mx_linear(x, mws[i % copies], out=out, ws=work)
+            else:
+                work = ops.linear_workspace(M, N, K, variant == "w4a4", dev)
+                fn = lambda i: ops.linear(x, ws[i % copies], variant, out=out, ws=work)
             for i in range(copies):
-                ops.linear(x, ws[i], variant, out=out, ws=work)
-            torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                for i in range(reps):
-                    ops.linear(x, ws[i % copies], variant, out=out, ws=work)
-            graph.replay()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            graph.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / reps
+                fn(i)
+            us = _graph_us(fn, reps)
             flops = 2.0 * M * N * K
-            nbytes = N * K * 0.5625 + M * K * 2 + M * N * 2
+            nbytes = w_bytes[variant] + M * K * 2 + M * N * 2
             row[f"{variant}_us"] = round(us, 2)
             row[f"{variant}_tflops"] = round(flops / us / 1e6, 1)
             row[f"{variant}_gbs"] = round(nbytes / us / 1e3, 1)
             row[f"{variant}_hbm_frac"] = round(nbytes / us / 1e3 / HBM_PEAK_GBS, 3)
-            row[f"{variant}_mfma_frac"] = round(flops / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 3)
+            row[f"{variant}_mfma_frac"] = round(flops / us / 1e6 / peaks[variant], 3)
         row["w4a16_over_w4a4"] = round(row["w4a16_us"] / row["w4a4_us"], 2)
         rows.append(row)
     return {"shape": {"N": N, "K": K}, "weight_copies": copies, "calls_per_graph": reps,
             "w4a4_includes": "global scale + quantisation of x + tile plan + GEMM",
-            "w4a16_includes": "tile plan + GEMM", "rows": rows}
+            "w4a16_includes": "tile plan + GEMM",
+            "mxfp4_includes": "MXFP4 quantisation of x + GEMM (mfma_frac against the FP4 peak)",
+            "rows": rows}
 
 
 def main():

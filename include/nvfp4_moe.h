@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_MOE_ABI_VERSION 4
+#define NVFP4_MOE_ABI_VERSION 5
 
 /* Status codes. */
 #define NVFP4_OK 0
@@ -256,6 +256,40 @@ int nvfp4_linear(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8
 int nvfp4_linear_w4a16(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w_prep,
                        const float* gw, void* out, int out_dtype, void* ws, size_t ws_bytes,
                        void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Dense OCP MXFP4 linear layer on the scaled FP4 matrix instruction.        */
+/* ------------------------------------------------------------------------ */
+/* The emulation backend's other block format, OCP MXFP4 on MI3xx (vLLM PR
+ * #35737, summary), built natively: CDNA4's scaled FP4 matrix instruction
+ * takes E2M1 codes with one E8M0 scale per 32 elements of each operand row,
+ * so the codes are multiplied as stored, with no decoding step.
+ * Canonical MXFP4 layout: codes uint8 [rows][K/2] packed as for NVFP4 and
+ * exponent bytes uint8 [rows][K/32] (E8M0: the scale is 2^(byte - 127)).
+ * Quantisation of a block of 32 with largest magnitude amax: byte =
+ * clamp(floor(log2 amax) - 2 + 127, 0, 254), 0 for a block of zeros; each
+ * element is v / 2^(byte - 127) rounded to the nearest E2M1 value (ties to
+ * the even code, above 6 saturating to 6), its sign kept.  No global scale.
+ *
+ * mxfp4_quantize: x [rows][ldx] (dtype 0 bfloat16, 1 float32; 16-byte
+ *   aligned, ldx a multiple of 8, K a multiple of 32, rows * K < 2^31) ->
+ *   q [rows][K/2] (4-byte aligned), ex [rows][K/32].  Bit-exact.
+ * mxfp4_prep_weights: canonical weight W [N][K] (q 16-byte aligned) -> prep
+ *   (mxfp4_prep_weights_size bytes, 16-byte aligned; the same bytes
+ *   permuted).  N, K multiples of 128.
+ * mxfp4_linear: y [M][N] = x_hat W_hat^T with FP32 accumulation, x bfloat16
+ *   [M][K] (16-byte aligned) quantised on the fly into the workspace (ws:
+ *   mxfp4_linear_workspace_size bytes, 256-byte aligned, no initial
+ *   contents needed).  out as nvfp4_linear.  Errors: NVFP4_ESHAPE,
+ *   NVFP4_EINVAL, NVFP4_EWORKSPACE. */
+int mxfp4_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx, uint8_t* q,
+                   uint8_t* ex, void* stream);
+size_t mxfp4_prep_weights_size(int64_t N, int64_t K);
+int mxfp4_prep_weights(int64_t N, int64_t K, const uint8_t* q, const uint8_t* ex, uint8_t* prep,
+                       void* stream);
+size_t mxfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K);
+int mxfp4_linear(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w_prep, void* out,
+                 int out_dtype, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Weight preparation (offline).                                             */

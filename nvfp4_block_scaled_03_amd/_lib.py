@@ -13,7 +13,7 @@ from ctypes import c_char_p, c_int, c_int32, c_int64, c_size_t, c_void_p
 # variant with different tile settings); the default is the in-tree build.
 LIB_PATH = os.environ.get("NVFP4_MOE_LIB") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "libnvfp4moe.so")
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 NVFP4_OK = 0
 NVFP4_EINVAL = -1
@@ -60,6 +60,12 @@ SIGNATURES = {
                              c_void_p, c_size_t, c_void_p]),
     "nvfp4_linear_w4a16": (c_int, [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
                                    c_int, c_void_p, c_size_t, c_void_p]),
+    "mxfp4_quantize": (c_int, [c_void_p, c_int, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
+    "mxfp4_prep_weights_size": (c_size_t, [c_int64, c_int64]),
+    "mxfp4_prep_weights": (c_int, [c_int64, c_int64, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "mxfp4_linear_workspace_size": (c_size_t, [c_int64, c_int64, c_int64]),
+    "mxfp4_linear": (c_int, [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_int, c_void_p,
+                             c_size_t, c_void_p]),
     "nvfp4_prep_weights_size": (c_size_t, [_P, c_int]),
     "nvfp4_prep_weights": (c_int, [_P, c_int, c_void_p, c_void_p, c_void_p, c_void_p]),
     "grouped_gemm_prefers_decoded": (c_int, [_P]),

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libnvfp4moe.so")
 ARCH = "gfx950"
-SOURCES = ["api.hip", "codec.hip", "align.hip", "prep.hip", "gemm.hip"]
+SOURCES = ["api.hip", "codec.hip", "align.hip", "prep.hip", "gemm.hip", "mx.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

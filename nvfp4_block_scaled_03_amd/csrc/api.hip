@@ -330,6 +330,70 @@ int nvfp4_linear_w4a16(const uint16_t* x, int64_t M, int64_t N, int64_t K, const
                     stream);
 }
 
+// ------------------------------------------------------------------ MXFP4
+int mxfp4_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx, uint8_t* q, uint8_t* ex,
+                   void* stream) {
+  const char* W = "mxfp4_quantize";
+  if (dtype != 0 && dtype != 1) return fail(NVFP4_EINVAL, "%s: EINVAL dtype=%d", W, dtype);
+  if (rows < 0 || K <= 0 || K % 32 || ldx < K || ldx % 8)
+    return fail(NVFP4_ESHAPE, "%s: ESHAPE rows=%lld K=%lld ldx=%lld", W, (long long)rows, (long long)K,
+                (long long)ldx);
+  if (rows * K >= (int64_t(1) << 31))
+    return fail(NVFP4_ESHAPE, "%s: ESHAPE rows=%lld K=%lld too large", W, (long long)rows, (long long)K);
+  if (rows == 0) return ok();
+  if (!x || !q || !ex) return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
+  if (!aligned(x, 16) || !aligned(q, 4)) return fail(NVFP4_EINVAL, "%s: EINVAL misaligned x or q", W);
+  return launched(nvfp4::launch_mx_quantize(x, dtype, rows, K, ldx, q, ex, S(stream)), W);
+}
+
+size_t mxfp4_prep_weights_size(int64_t N, int64_t K) {
+  if (!linear_shape_ok(1, N, K)) return 0;
+  return nvfp4::mx_prep_bytes(N, K);
+}
+
+int mxfp4_prep_weights(int64_t N, int64_t K, const uint8_t* q, const uint8_t* ex, uint8_t* prep,
+                       void* stream) {
+  const char* W = "mxfp4_prep_weights";
+  if (!linear_shape_ok(1, N, K))
+    return fail(NVFP4_ESHAPE, "%s: ESHAPE N=%lld K=%lld (multiples of 128)", W, (long long)N, (long long)K);
+  if (!q || !ex || !prep) return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
+  if (!aligned(q, 16) || !aligned(prep, 16))
+    return fail(NVFP4_EINVAL, "%s: EINVAL q and prep must be 16-byte aligned", W);
+  return launched(nvfp4::launch_mx_prep(N, K, q, ex, prep, S(stream)), W);
+}
+
+namespace {
+// Workspace of mxfp4_linear: codes [M][K/2], then exponent bytes [M][K/32].
+size_t mx_ws_codes(int64_t M, int64_t K) { return up256((size_t)M * (K / 2)); }
+}  // namespace
+
+size_t mxfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (!linear_shape_ok(M, N, K)) return 0;
+  return mx_ws_codes(M, K) + up256((size_t)M * (K / 32));
+}
+
+int mxfp4_linear(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w_prep, void* out,
+                 int out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  const char* W = "mxfp4_linear";
+  if (!linear_shape_ok(M, N, K) || M * K >= (int64_t(1) << 31))
+    return fail(NVFP4_ESHAPE, "%s: ESHAPE M=%lld N=%lld K=%lld (N, K multiples of 128)", W, (long long)M,
+                (long long)N, (long long)K);
+  if (out_dtype != 0 && out_dtype != 1) return fail(NVFP4_EINVAL, "%s: EINVAL out_dtype=%d", W, out_dtype);
+  const size_t need = mxfp4_linear_workspace_size(M, N, K);
+  if (ws_bytes < need || (M > 0 && !ws))
+    return fail(NVFP4_EWORKSPACE, "%s: EWORKSPACE M=%lld N=%lld K=%lld workspace_size=%zu needed=%zu", W,
+                (long long)M, (long long)N, (long long)K, ws_bytes, need);
+  if (M == 0) return ok();
+  if (!x || !w_prep || !out) return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
+  if (!aligned(x, 16) || !aligned(w_prep, 16) || !aligned(ws, 256))
+    return fail(NVFP4_EINVAL, "%s: EINVAL x and w_prep 16-byte, ws 256-byte aligned", W);
+  uint8_t* aq = static_cast<uint8_t*>(ws);
+  uint8_t* ae = aq + mx_ws_codes(M, K);
+  hipError_t e = nvfp4::launch_mx_quantize(x, 0, M, K, K, aq, ae, S(stream));
+  if (e != hipSuccess) return launched(e, W);
+  return launched(nvfp4::launch_mx_gemm(aq, ae, M, N, K, w_prep, out, out_dtype, S(stream)), W);
+}
+
 // ------------------------------------------------------------------ weights
 size_t nvfp4_prep_weights_size(const nvfp4_moe_dims* d, int which) {
   if (check_dims(d, "nvfp4_prep_weights_size") || (which != 13 && which != 2)) return 0;

@@ -299,6 +299,61 @@ def linear(x: torch.Tensor, w: LinearWeight, variant: str = "w4a4", out_dtype=to
     return out
 
 
+# ---------------------------------------------------------------- OCP MXFP4
+def mx_quantize(x: torch.Tensor, q: Optional[torch.Tensor] = None, ex: Optional[torch.Tensor] = None):
+    """MXFP4-encode the rows of ``x`` [rows, K]: (codes [rows, K/2], E8M0 bytes [rows, K/32])."""
+    _need_cuda(x)
+    K = x.shape[-1]
+    x2 = x.reshape(-1, K)
+    if x2.stride(-1) != 1:
+        x2 = x2.contiguous()
+    rows = x2.shape[0]
+    q = q if q is not None else torch.empty(rows, K // 2, dtype=torch.uint8, device=x.device)
+    ex = ex if ex is not None else torch.empty(rows, K // 32, dtype=torch.uint8, device=x.device)
+    call("mxfp4_quantize", _p(x2), _dtype_code(x2), rows, K, x2.stride(0), _p(q), _p(ex), _stream())
+    return q, ex
+
+
+class MxLinearWeight:
+    """An MXFP4 weight W [N, K] prepared for mxfp4_linear."""
+
+    def __init__(self, prep: torch.Tensor, N: int, K: int):
+        self.prep, self.N, self.K = prep, N, K
+
+
+def prepare_mx_weight(w_q: torch.Tensor, w_ex: torch.Tensor) -> MxLinearWeight:
+    """From canonical MXFP4 (codes [N, K/2], exponent bytes [N, K/32])."""
+    _need_cuda(w_q, w_ex)
+    N, K = w_q.shape[0], w_q.shape[1] * 2
+    n = _lib.load().mxfp4_prep_weights_size(N, K)
+    prep = torch.empty(max(n, 16), dtype=torch.uint8, device=w_q.device)
+    call("mxfp4_prep_weights", N, K, _p(w_q.contiguous()), _p(w_ex.contiguous()), _p(prep), _stream())
+    return MxLinearWeight(prep, N, K)
+
+
+def quantize_mx_weight(w: torch.Tensor) -> MxLinearWeight:
+    """FP32 or bf16 W [N, K] -> MXFP4 quantisation on the GPU, prep."""
+    q, ex = mx_quantize(w.contiguous())
+    return prepare_mx_weight(q, ex)
+
+
+def mx_linear_workspace(M: int, N: int, K: int, device) -> torch.Tensor:
+    n = _lib.load().mxfp4_linear_workspace_size(M, N, K)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def mx_linear(x: torch.Tensor, w: MxLinearWeight, out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None,
+              ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y [M, N] = Q(x) W^T, x bf16 [M, K] quantised to MXFP4 in the call."""
+    _need_cuda(x)
+    M = x.shape[0]
+    out = out if out is not None else torch.empty(M, w.N, dtype=out_dtype, device=x.device)
+    ws = ws if ws is not None else mx_linear_workspace(M, w.N, w.K, x.device)
+    call("mxfp4_linear", _p(x.contiguous()), M, w.N, w.K, _p(w.prep), _p(out), _dtype_code(out), _p(ws),
+         ws.numel(), _stream())
+    return out
+
+
 # ---------------------------------------------------------------- the layer
 class MoELayer:
     """One NVFP4 expert layer with all intermediates preallocated, so that a

@@ -145,6 +145,23 @@ def test_quantize_and_align_errors(lib):
     assert rc == _lib.NVFP4_ESHAPE and "multiples of 128" in _lib.last_error()
 
 
+def test_mxfp4_sizes_and_errors(lib):
+    assert lib.mxfp4_prep_weights_size(256, 512) == 256 * 256 + 256 * 16
+    assert lib.mxfp4_prep_weights_size(200, 512) == 0
+    assert lib.mxfp4_linear_workspace_size(3, 256, 512) == 768 + 256
+    assert lib.mxfp4_quantize(None, 2, 4, 32, 32, None, None, None) == _lib.NVFP4_EINVAL
+    assert lib.mxfp4_quantize(None, 0, 4, 48, 48, None, None, None) == _lib.NVFP4_ESHAPE
+    assert lib.mxfp4_quantize(None, 0, 4, 32, 36, None, None, None) == _lib.NVFP4_ESHAPE
+    assert lib.mxfp4_quantize(None, 0, 0, 32, 32, None, None, None) == _lib.NVFP4_OK
+    assert lib.mxfp4_quantize(None, 0, 4, 32, 32, None, None, None) == _lib.NVFP4_EINVAL
+    assert lib.mxfp4_prep_weights(256, 100, None, None, None, None) == _lib.NVFP4_ESHAPE
+    rc = lib.mxfp4_linear(None, 8, 256, 512, None, None, 0, None, 0, None)
+    assert rc == _lib.NVFP4_EWORKSPACE and "M=8" in _lib.last_error()
+    rc = lib.mxfp4_linear(None, 8, 256, 512, None, None, 3, None, 0, None)
+    assert rc == _lib.NVFP4_EINVAL and "out_dtype=3" in _lib.last_error()
+    assert lib.mxfp4_linear(None, 0, 256, 512, None, None, 0, None, 0, None) == _lib.NVFP4_OK
+
+
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(_lib.LibraryNotBuilt):
         old = _lib._lib
