@@ -12,6 +12,7 @@
 
 #include "../../include/nvfp4_moe.h"
 #include "launch.h"
+#include "mx.h"
 
 namespace {
 

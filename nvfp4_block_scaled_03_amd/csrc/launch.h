@@ -125,15 +125,4 @@ struct LinearArgs {
 };
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s);
 
-// OCP MXFP4 (E8M0 scale per 32): quantisation (dtype 0 bf16, 1 f32; codes
-// [rows][K/2], scale bytes [rows][K/32]), weight prep and the dense GEMM on
-// the scaled FP4 matrix instruction (out_dtype 0 bf16, 1 f32).
-hipError_t launch_mx_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx, uint8_t* q,
-                              uint8_t* ex, hipStream_t s);
-size_t mx_prep_bytes(int64_t N, int64_t K);
-hipError_t launch_mx_prep(int64_t N, int64_t K, const uint8_t* q, const uint8_t* ex, uint8_t* prep,
-                          hipStream_t s);
-hipError_t launch_mx_gemm(const uint8_t* a_q, const uint8_t* a_e, int64_t M, int64_t N, int64_t K,
-                          const uint8_t* w_prep, void* out, int out_dtype, hipStream_t s);
-
 }  // namespace nvfp4

@@ -8,7 +8,7 @@
 // 2^(floor(log2 amax) - 2), elements rounded to the nearest E2M1 value of
 // v / scale (exact), ties to the even code, saturating at 6.
 #include "common.h"
-#include "launch.h"
+#include "mx.h"
 #include "quant.h"
 
 namespace nvfp4 {
