@@ -16,6 +16,27 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 
+// Split-K configurations by row tiles (MT = 1, 2, 4): column tiles per
+// workgroup and chunks loaded per batch.
+#ifndef NVFP4_MX_NTW1
+#define NVFP4_MX_NTW1 2
+#endif
+#ifndef NVFP4_MX_UB1
+#define NVFP4_MX_UB1 5
+#endif
+#ifndef NVFP4_MX_NTW2
+#define NVFP4_MX_NTW2 4
+#endif
+#ifndef NVFP4_MX_UB2
+#define NVFP4_MX_UB2 2
+#endif
+#ifndef NVFP4_MX_NTW4
+#define NVFP4_MX_NTW4 4
+#endif
+#ifndef NVFP4_MX_UB4
+#define NVFP4_MX_UB4 1
+#endif
+
 // One lane per 8 elements; the 4 lanes of a 32-element block form a DPP
 // quad (K % 32 == 0 and the grid starts at a multiple of 4).
 template <typename T>
@@ -189,6 +210,114 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(const uint8_t* __restrict_
       }
 }
 
+// Few rows (M <= 16 MT): the weight stream decides the time, so the grid is
+// wide and each wavefront keeps many loads in flight.  A workgroup owns NTW
+// column tiles (16 NTW columns); its 4 wavefronts split K into quarters, each
+// loading UB chunks of weights and activations (straight from global memory:
+// the activations are small and stay in L2) before multiplying them, then
+// the quarters are summed through LDS.
+template <int MT, int NTW, int UB, bool F32>
+__global__ __launch_bounds__(256) void mx_gemm_splitk_kernel(const uint8_t* __restrict__ a_q,
+                                                             const uint8_t* __restrict__ a_e, int64_t M,
+                                                             int64_t N, int64_t K,
+                                                             const uint8_t* __restrict__ w_prep,
+                                                             void* __restrict__ out) {
+  __shared__ f32x4 red[3][MT][NTW][64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int fr = lane & 15, fg = lane >> 4;
+  const int64_t KC = K / 128;
+  const int64_t c_lo = KC * wv / 4, c_hi = KC * (wv + 1) / 4;
+  const int64_t nt0 = (int64_t)blockIdx.x * NTW;
+  const uint8_t* w_sc = w_prep + N * (K / 2);
+  const uint8_t* arow[MT];
+  const uint8_t* erow[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int64_t r = min((int64_t)(i * 16 + fr), M - 1);
+    arow[i] = a_q + r * (K / 2) + fg * 16;
+    erow[i] = a_e + r * (K / 32) + fg;
+  }
+  f32x4 acc[MT][NTW];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t c0 = c_lo; c0 < c_hi; c0 += UB) {
+    u32x4 bq[UB][NTW], aq[UB][MT];
+    uint32_t bs[UB][NTW], as[UB][MT];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int64_t kc = min(c0 + u, c_hi - 1);   // a repeated chunk is loaded but not used
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const int64_t unit = ((nt0 + j) * KC + kc) * 64 + lane;
+        bq[u][j] = *reinterpret_cast<const u32x4*>(w_prep + unit * 16);
+        bs[u][j] = w_sc[unit];
+      }
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        aq[u][i] = *reinterpret_cast<const u32x4*>(arow[i] + kc * 64);
+        as[u][i] = erow[i][kc * 4];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      if (c0 + u < c_hi) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          const v8i av = {(int)aq[u][i][0], (int)aq[u][i][1], (int)aq[u][i][2], (int)aq[u][i][3], 0, 0, 0, 0};
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) {
+            const v8i bv = {(int)bq[u][j][0], (int)bq[u][j][1], (int)bq[u][j][2], (int)bq[u][j][3], 0, 0, 0, 0};
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[i][j], 4, 4, 0,
+                                                                        (int)as[u][i], 0, (int)bs[u][j]);
+          }
+        }
+      }
+    }
+  }
+  if (wv > 0) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) red[wv - 1][i][j][lane] = acc[i][j];
+  }
+  __syncthreads();
+  if (wv > 0) return;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      f32x4 v = acc[i][j];
+#pragma unroll
+      for (int w = 0; w < 3; ++w) {
+        const f32x4 o = red[w][i][j][lane];
+        v[0] += o[0];
+        v[1] += o[1];
+        v[2] += o[2];
+        v[3] += o[3];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = i * 16 + fg * 4 + r;
+        if (row < M) {
+          const int64_t o = row * N + (nt0 + j) * 16 + fr;
+          if constexpr (F32) static_cast<float*>(out)[o] = v[r];
+          else static_cast<uint16_t*>(out)[o] = (uint16_t)f32_to_bf16_bits(v[r]);
+        }
+      }
+    }
+}
+
+template <int MT, int NTW, int UB>
+hipError_t launch_mx_splitk(const uint8_t* a_q, const uint8_t* a_e, int64_t M, int64_t N, int64_t K,
+                            const uint8_t* w_prep, void* out, int out_dtype, hipStream_t s) {
+  const dim3 grid((unsigned)(N / (16 * NTW)));
+  if (out_dtype) mx_gemm_splitk_kernel<MT, NTW, UB, true><<<grid, 256, 0, s>>>(a_q, a_e, M, N, K, w_prep, out);
+  else mx_gemm_splitk_kernel<MT, NTW, UB, false><<<grid, 256, 0, s>>>(a_q, a_e, M, N, K, w_prep, out);
+  return hipGetLastError();
+}
+
 template <int MT>
 hipError_t launch_mx_gemm_mt(const uint8_t* a_q, const uint8_t* a_e, int64_t M, int64_t N, int64_t K,
                              const uint8_t* w_prep, void* out, int out_dtype, hipStream_t s) {
@@ -223,8 +352,10 @@ hipError_t launch_mx_prep(int64_t N, int64_t K, const uint8_t* q, const uint8_t*
 
 hipError_t launch_mx_gemm(const uint8_t* a_q, const uint8_t* a_e, int64_t M, int64_t N, int64_t K,
                           const uint8_t* w_prep, void* out, int out_dtype, hipStream_t s) {
-  if (M <= 16) return launch_mx_gemm_mt<1>(a_q, a_e, M, N, K, w_prep, out, out_dtype, s);
-  if (M <= 64) return launch_mx_gemm_mt<4>(a_q, a_e, M, N, K, w_prep, out, out_dtype, s);
+  // N is a multiple of 128, so NTW <= 8 column tiles divide it.
+  if (M <= 16) return launch_mx_splitk<1, NVFP4_MX_NTW1, NVFP4_MX_UB1>(a_q, a_e, M, N, K, w_prep, out, out_dtype, s);
+  if (M <= 32) return launch_mx_splitk<2, NVFP4_MX_NTW2, NVFP4_MX_UB2>(a_q, a_e, M, N, K, w_prep, out, out_dtype, s);
+  if (M <= 64) return launch_mx_splitk<4, NVFP4_MX_NTW4, NVFP4_MX_UB4>(a_q, a_e, M, N, K, w_prep, out, out_dtype, s);
   return launch_mx_gemm_mt<8>(a_q, a_e, M, N, K, w_prep, out, out_dtype, s);
 }
 

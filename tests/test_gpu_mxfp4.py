@@ -110,6 +110,19 @@ def test_linear(dev, M):
     _check(x, lw, ref, _bound(x_hat, omx.dequantize(wc, we), K))
 
 
+@pytest.mark.parametrize("M,N,K", [(3, 128, 128), (20, 256, 384), (40, 128, 640), (100, 128, 256)])
+def test_linear_short_k(dev, M, N, K):
+    """K of 1, 3, 5 and 2 chunks of 128: wavefronts of the split-K kernels with
+    no chunk or uneven shares, and the tiled kernel's odd chunk count."""
+    w = _weight(dev, N, K, 23)
+    wc, we = omx.quantize(to_np(w).astype(np.float64))
+    lw = ops.prepare_mx_weight(torch.from_numpy(onv.pack_codes(wc)).to(dev), torch.from_numpy(we).to(dev))
+    x = _x(dev, M, K, 4)
+    xf = to_np(x).astype(np.float64)
+    ref = omx.linear(xf, wc, we)
+    _check(x, lw, ref, _bound(omx.dequantize(*omx.quantize(xf)), omx.dequantize(wc, we), K))
+
+
 def test_linear_gpu_quantised_weight(dev):
     """The weight quantised on the GPU gives the oracle's codes, so the same result."""
     N, K, M = 256, 512, 33
