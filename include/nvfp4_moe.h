@@ -278,7 +278,8 @@ int nvfp4_linear_w4a16(const uint16_t* x, int64_t M, int64_t N, int64_t K, const
  *   (mxfp4_prep_weights_size bytes, 16-byte aligned; the same bytes
  *   permuted).  N, K multiples of 128.
  * mxfp4_linear: y [M][N] = x_hat W_hat^T with FP32 accumulation, x bfloat16
- *   [M][K] (16-byte aligned) quantised on the fly into the workspace (ws:
+ *   [M][K] (16-byte aligned, M K < 2^31, the prepared weight below 4 GiB)
+ *   quantised on the fly into the workspace (ws:
  *   mxfp4_linear_workspace_size bytes, 256-byte aligned, no initial
  *   contents needed).  out as nvfp4_linear.  Errors: NVFP4_ESHAPE,
  *   NVFP4_EINVAL, NVFP4_EWORKSPACE. */

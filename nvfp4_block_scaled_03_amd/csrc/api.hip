@@ -364,21 +364,23 @@ int mxfp4_prep_weights(int64_t N, int64_t K, const uint8_t* q, const uint8_t* ex
 }
 
 namespace {
-// Workspace of mxfp4_linear: codes [M][K/2], then exponent bytes [M][K/32].
-size_t mx_ws_codes(int64_t M, int64_t K) { return up256((size_t)M * (K / 2)); }
+// Workspace of mxfp4_linear: the activation operand's codes, then its scale
+// words (rows padded to whole tiles).
+size_t mx_ws_codes(int64_t M, int64_t K) { return up256((size_t)nvfp4::mx_rows_pad(M) * (K / 2)); }
 }  // namespace
 
 size_t mxfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
   if (!linear_shape_ok(M, N, K)) return 0;
-  return mx_ws_codes(M, K) + up256((size_t)M * (K / 32));
+  return mx_ws_codes(M, K) + up256((size_t)nvfp4::mx_rows_pad(M) * (K / 32));
 }
 
 int mxfp4_linear(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* w_prep, void* out,
                  int out_dtype, void* ws, size_t ws_bytes, void* stream) {
   const char* W = "mxfp4_linear";
-  if (!linear_shape_ok(M, N, K) || M * K >= (int64_t(1) << 31))
-    return fail(NVFP4_ESHAPE, "%s: ESHAPE M=%lld N=%lld K=%lld (N, K multiples of 128)", W, (long long)M,
-                (long long)N, (long long)K);
+  if (!linear_shape_ok(M, N, K) || nvfp4::mx_rows_pad(M) * K >= (int64_t(1) << 31) ||
+      (N * K / 32) * 17 >= (int64_t(1) << 32))
+    return fail(NVFP4_ESHAPE, "%s: ESHAPE M=%lld N=%lld K=%lld (N, K multiples of 128; M K < 2^31, prepared "
+                "weight < 4 GiB)", W, (long long)M, (long long)N, (long long)K);
   if (out_dtype != 0 && out_dtype != 1) return fail(NVFP4_EINVAL, "%s: EINVAL out_dtype=%d", W, out_dtype);
   const size_t need = mxfp4_linear_workspace_size(M, N, K);
   if (ws_bytes < need || (M > 0 && !ws))
@@ -390,7 +392,7 @@ int mxfp4_linear(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8
     return fail(NVFP4_EINVAL, "%s: EINVAL x and w_prep 16-byte, ws 256-byte aligned", W);
   uint8_t* aq = static_cast<uint8_t*>(ws);
   uint8_t* ae = aq + mx_ws_codes(M, K);
-  hipError_t e = nvfp4::launch_mx_quantize(x, 0, M, K, K, aq, ae, S(stream));
+  hipError_t e = nvfp4::launch_mx_quantize_operand(x, M, K, aq, ae, S(stream));
   if (e != hipSuccess) return launched(e, W);
   return launched(nvfp4::launch_mx_gemm(aq, ae, M, N, K, w_prep, out, out_dtype, S(stream)), W);
 }

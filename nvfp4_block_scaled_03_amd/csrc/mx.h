@@ -10,9 +10,16 @@ namespace nvfp4 {
 // the scaled FP4 matrix instruction (out_dtype 0 bf16, 1 f32).
 hipError_t launch_mx_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx, uint8_t* q,
                               uint8_t* ex, hipStream_t s);
+// The GEMM's activation operand: x bf16 [M][K] quantised into the operand
+// layout (rows padded with zeros to mx_rows_pad(M); codes mx_rows_pad(M) K/2
+// bytes, scales mx_rows_pad(M) K/32 bytes; K % 128 == 0).
+int64_t mx_rows_pad(int64_t M);
+hipError_t launch_mx_quantize_operand(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, uint8_t* ex,
+                                      hipStream_t s);
 size_t mx_prep_bytes(int64_t N, int64_t K);
 hipError_t launch_mx_prep(int64_t N, int64_t K, const uint8_t* q, const uint8_t* ex, uint8_t* prep,
                           hipStream_t s);
+// a_q / a_e: the activation operand from launch_mx_quantize_operand.
 hipError_t launch_mx_gemm(const uint8_t* a_q, const uint8_t* a_e, int64_t M, int64_t N, int64_t K,
                           const uint8_t* w_prep, void* out, int out_dtype, hipStream_t s);
 

@@ -39,17 +39,26 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 
 // One lane per 8 elements; the 4 lanes of a 32-element block form a DPP
 // quad (K % 32 == 0 and the grid starts at a multiple of 4).
-template <typename T>
+//
+// FRAG = false: canonical output (codes [rows][K/2], bytes [rows][K/32]).
+// FRAG = true: the operand layout the GEMM kernels read (K % 128 == 0, rows
+// padded to rows_pad, a multiple of 64, with zeros): codes
+// [rows_pad/16][K/128][64 lanes][16 B] (lane 16 g + m: row 16 t + m of row
+// tile t, k in [32 g, 32 g + 32) of the chunk) and scale words
+// [rows_pad/64][K/128][64 lanes][4 B] (byte t % 4: row tile t of the group),
+// so that one instruction operand is 1 KiB contiguous and the scales of 4
+// row tiles are one 256-byte run.
+template <typename T, bool FRAG>
 __global__ __launch_bounds__(256) void mx_quantize_kernel(const T* __restrict__ x, int64_t rows, int64_t K,
-                                                          int64_t ldx, uint8_t* __restrict__ q,
+                                                          int64_t ldx, int64_t rows_pad, uint8_t* __restrict__ q,
                                                           uint8_t* __restrict__ ex) {
   const int64_t hb_per_row = K >> 3;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= rows * hb_per_row) return;   // whole quads leave together
+  if (i >= (FRAG ? rows_pad : rows) * hb_per_row) return;   // whole quads leave together
   const int64_t row = i / hb_per_row;
   const int64_t c8 = (i - row * hb_per_row) << 3;
-  float v[8];
-  load8(x, row * ldx + c8, v);
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (!FRAG || row < rows) load8(x, row * ldx + c8, v);   // (padding rows: zeros)
   float m = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
@@ -69,14 +78,22 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const T* __restrict__ 
     const uint32_t sign = ((uint32_t)__float_as_int(v[j]) >> 28) & 8u;
     word |= (sign | mag) << (4 * j);
   }
-  *reinterpret_cast<uint32_t*>(q + row * (K >> 1) + (c8 >> 1)) = word;
-  if ((c8 & 31) == 0) ex[row * (K >> 5) + (c8 >> 5)] = (uint8_t)code;
+  if constexpr (FRAG) {
+    const int64_t KC = K >> 7, t = row >> 4, kc = c8 >> 7;
+    const int64_t lane = ((c8 & 127) >> 5) * 16 + (row & 15);
+    *reinterpret_cast<uint32_t*>(q + ((t * KC + kc) * 64 + lane) * 16 + ((c8 & 31) >> 1)) = word;
+    if ((c8 & 31) == 0) ex[((t >> 2) * KC + kc) * 256 + lane * 4 + (t & 3)] = (uint8_t)code;
+  } else {
+    *reinterpret_cast<uint32_t*>(q + row * (K >> 1) + (c8 >> 1)) = word;
+    if ((c8 & 31) == 0) ex[row * (K >> 5) + (c8 >> 5)] = (uint8_t)code;
+  }
 }
 
 // Weight streaming layout: codes [N/16][K/128][64 lanes][16 B] as for NVFP4
 // (lane l = 16g + n: column n of the tile, k in [32g, 32g + 32) of the
-// chunk), then scale bytes [N/16][K/128][64 lanes] (that lane's E8M0 byte):
-// exactly the operand and scale of the lane in the 16x16x128 instruction.
+// chunk: exactly the operand of the lane in the 16x16x128 instruction), then
+// scale words [N/64][K/128][64 lanes][4 B]: byte t of lane l's word is the
+// E8M0 byte of that lane in column tile 4q + t of group q.
 __global__ __launch_bounds__(256) void mx_prep_kernel(int64_t N, int64_t K, const uint8_t* __restrict__ q,
                                                       const uint8_t* __restrict__ ex,
                                                       uint8_t* __restrict__ prep) {
@@ -87,113 +104,160 @@ __global__ __launch_bounds__(256) void mx_prep_kernel(int64_t N, int64_t K, cons
   const int64_t kc = rest % KC, nt = rest / KC;
   const int64_t n = nt * 16 + (lane & 15), g = lane >> 4;
   *reinterpret_cast<u32x4*>(prep + i * 16) = *reinterpret_cast<const u32x4*>(q + n * (K / 2) + kc * 64 + 16 * g);
-  prep[N * (K / 2) + i] = ex[n * (K / 32) + kc * 4 + g];
+  prep[N * (K / 2) + ((nt >> 2) * KC + kc) * 256 + lane * 4 + (nt & 3)] = ex[n * (K / 32) + kc * 4 + g];
 }
 
-// y = x_hat W_hat^T.  Workgroup: 4 wavefronts x 64 columns, 16 MT rows.  The
-// activation chunk (16 MT rows x 128 k: 64 code bytes + 4 scale bytes per
-// row) is staged in LDS, double-buffered (rows 80 bytes apart: the 16 rows of
-// a fragment read hit distinct banks); weights stream into two register sets.
-constexpr int kMxRowB = 80;
-template <int MT, bool F32>
-__global__ __launch_bounds__(256) void mx_gemm_kernel(const uint8_t* __restrict__ a_q,
+// Byte offset, within the scale words, of lane l's E8M0 byte of column tile nt, chunk kc.
+__device__ __forceinline__ int64_t mx_scale_at(int64_t nt, int64_t kc, int64_t KC, int lane) {
+  return ((nt >> 2) * KC + kc) * 256 + lane * 4 + (nt & 3);
+}
+
+// y = x_hat W_hat^T for many rows.  Workgroup: 128 rows x 256 columns, 4
+// wavefronts of 128 x 64 (8 x 4 instruction tiles).  Both operands travel
+// from global memory straight into a ring of D LDS stages (one chunk of 128
+// k each, no registers in between), D - 1 chunks in flight: enough to cover
+// a miss to HBM while the chunks already resident are multiplied.  Each
+// 1 KiB direct load fills one instruction operand in lane order (lane l's 16
+// bytes at 16 l), so every fragment read is a conflict-free read of 16 bytes
+// per lane at 16 l.
+//
+// Stage layout (bytes): activation tiles 8 x 1 KiB (tile i, lane l = 16 g + m:
+// row 16 i + m, codes k in [32 g, 32 g + 32)), activation scale words 4 x 256
+// (wavefront w < 2: row tiles 4 w .. 4 w + 3, lane l's word, byte i % 4),
+// weight tiles 16 x 1 KiB (wavefront w, tile j), weight scale words 4 x 256
+// (wavefront w: lane l's word, byte j for tile j).
+//
+// Tile order: workgroups are dealt to the 8 XCDs in turn (workgroup b runs on
+// XCD b % 8), and each XCD has its own L2.  Workgroup b takes tile
+// (b % 8) * ceil(tiles / 8) + b / 8 of a list that walks groups of GM row
+// tiles column tile by column tile, so the workgroups resident on one XCD
+// share a few weight column tiles and a few activation row tiles.
+#ifndef NVFP4_MX_DEPTH
+#define NVFP4_MX_DEPTH 4
+#endif
+#ifndef NVFP4_MX_GM
+#define NVFP4_MX_GM 8
+#endif
+constexpr int kMxA = 0, kMxAs = 8192, kMxB = kMxAs + 1024, kMxBs = kMxB + 16384, kMxSlot = kMxBs + 1024;
+constexpr int kMxLoads = 8;   // direct loads per wavefront per chunk
+
+// s_waitcnt immediate that waits until at most n vector memory operations
+// are outstanding (the LDS and export counters left at their maxima).
+constexpr int mx_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <int D, bool F32>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void mx_gemm_kernel(const uint8_t* __restrict__ a_q,
                                                       const uint8_t* __restrict__ a_e, int64_t M, int64_t N,
                                                       int64_t K, const uint8_t* __restrict__ w_prep,
                                                       void* __restrict__ out) {
-  constexpr int ROWS = 16 * MT, NTW = 4;
-  __shared__ __attribute__((aligned(16))) uint8_t Aq[2][ROWS * kMxRowB];
-  __shared__ uint32_t Ae[2][ROWS];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int64_t m0 = (int64_t)blockIdx.y * ROWS;
-  const int64_t n_wave0 = (int64_t)blockIdx.x * 256 + wv * 64;
+  static_assert(D >= 2 && (D - 2) * kMxLoads <= 63, "ring depth");
+  constexpr int ROWS = 128, MT = 8, NTW = 4;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[D * kMxSlot];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t TM = (M + ROWS - 1) / ROWS, TN = (N + 255) / 256, tiles = TM * TN;
+  const int64_t per_xcd = (tiles + 7) / 8;
+  const int64_t L = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (L >= tiles) return;
+  const int64_t grp = L / (NVFP4_MX_GM * TN);
+  const int64_t gh = min((int64_t)NVFP4_MX_GM, TM - grp * NVFP4_MX_GM);
+  const int64_t Lg = L - grp * NVFP4_MX_GM * TN;
+  const int64_t tm = grp * NVFP4_MX_GM + Lg % gh, tn = Lg / gh;
+  const int64_t m0 = tm * ROWS;
+  const int64_t n_wave0 = tn * 256 + wv * 64;
   const bool wave_on = n_wave0 < N;
-  const int64_t KC = K / 128;
-  const uint8_t* w_sc = w_prep + N * (K / 2);
+  const int KC = (int)(K / 128);
 
-  // A staging: piece p = 16 bytes of a row (4 per row), scale words by the
-  // first ROWS threads.  Rows past M repeat row M - 1 (never stored).
-  constexpr int PIECES = ROWS * 4, PER = (PIECES + 255) / 256;
-  u32x4 a_reg[PER];
-  uint32_t e_reg = 0;
-  auto load_a = [&](int64_t kc) {
+  // Per-lane 32-bit source offsets of this wavefront's 8 loads (chunk 0);
+  // chunk kc adds kc * (1024, 256, 1024, 256) bytes.  The activations are in
+  // the operand layout with rows padded to whole tiles (zeros past M);
+  // column tiles past N repeat the last one (loaded, never stored).
+  uint32_t va[2];
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int p = tid + 256 * u;
-      if (p < PIECES) {
-        const int64_t r = min(m0 + (p >> 2), M - 1);
-        a_reg[u] = *reinterpret_cast<const u32x4*>(a_q + r * (K / 2) + kc * 64 + (p & 3) * 16);
-      }
-    }
-    if (tid < ROWS) {
-      const int64_t r = min(m0 + tid, M - 1);
-      e_reg = *reinterpret_cast<const uint32_t*>(a_e + r * (K / 32) + kc * 4);
-    }
-  };
-  auto store_a = [&](int buf) {
+  for (int t = 0; t < 2; ++t) va[t] = (uint32_t)((((tm * 8 + 2 * wv + t) * KC) * 64 + lane) * 16);
+  // (the two scale groups of the 8 row tiles, by wavefronts 0 and 1; 2 and 3
+  // load the same words into their own slots, which are not read)
+  const uint32_t ve = (uint32_t)((((tm * 2 + (wv & 1)) * KC) * 64 + lane) * 4);
+  const int64_t nt0 = min(n_wave0, N - 64) / 16;
+  uint32_t vb[NTW];
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int p = tid + 256 * u;
-      if (p < PIECES) *reinterpret_cast<u32x4*>(&Aq[buf][(p >> 2) * kMxRowB + (p & 3) * 16]) = a_reg[u];
-    }
-    if (tid < ROWS) Ae[buf][tid] = e_reg;
-  };
-  u32x4 bq[2][NTW];
-  uint32_t bs[2][NTW];
-  auto load_b = [&](int64_t kc, int set) {
-    if (!wave_on) return;
+  for (int j = 0; j < NTW; ++j) vb[j] = (uint32_t)(((nt0 + j) * KC * 64 + lane) * 16);
+  const uint32_t vbs = (uint32_t)((nt0 >> 2) * KC * 256 + lane * 4);
+  const uint8_t* w_sc = w_prep + N * (K / 2);
+  const uint32_t ring0 = (uint32_t)(uintptr_t)ring;
+
+  // Issue chunk kc (clamped to the last) into ring slot `slot`.  Assembly:
+  // the compiler would otherwise treat each direct load as a pending LDS
+  // write that any later LDS read may alias and wait for all of them before
+  // every fragment read, which would drain the ring.  Completion is awaited
+  // explicitly (vmcnt) before the barrier that publishes a slot.
+  auto issue = [&](int kc, int slot) {
+    kc = min(kc, KC - 1);
+    const uint32_t base = ring0 + (uint32_t)slot * kMxSlot;
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const int64_t unit = ((n_wave0 / 16 + j) * KC + kc) * 64 + lane;
-      bq[set][j] = *reinterpret_cast<const u32x4*>(w_prep + unit * 16);
-      bs[set][j] = w_sc[unit];
-    }
+    for (int t = 0; t < 2; ++t)
+      asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(va[t] + (uint32_t)kc * 1024u), "s"(a_q),
+                   "{m0}"(base + kMxA + (2 * wv + t) * 1024) : "memory");
+    asm volatile("global_load_lds_dword %0, %1" : : "v"(ve + (uint32_t)kc * 256u), "s"(a_e),
+                 "{m0}"(base + kMxAs + wv * 256) : "memory");
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+      asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(vb[j] + (uint32_t)kc * 1024u), "s"(w_prep),
+                   "{m0}"(base + kMxB + (wv * 4 + j) * 1024) : "memory");
+    asm volatile("global_load_lds_dword %0, %1" : : "v"(vbs + (uint32_t)kc * 256u), "s"(w_sc),
+                 "{m0}"(base + kMxBs + wv * 256) : "memory");
   };
+
   f32x4 acc[MT][NTW];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int fr = lane & 15, fg = lane >> 4;
-  auto compute = [&](int buf, int set) {
-    if (!wave_on) return;
+  auto compute = [&](int slot) {
+    const uint8_t* st = ring + slot * kMxSlot;
+    u32x4 b[NTW];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) b[j] = *reinterpret_cast<const u32x4*>(st + kMxB + (wv * 4 + j) * 1024 + lane * 16);
+    const uint32_t bsw = *reinterpret_cast<const uint32_t*>(st + kMxBs + wv * 256 + lane * 4);
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(&Aq[buf][(i * 16 + fr) * kMxRowB + fg * 16]);
-      const int as = (int)((Ae[buf][i * 16 + fr] >> (8 * fg)) & 0xFFu);
+      const u32x4 a = *reinterpret_cast<const u32x4*>(st + kMxA + i * 1024 + lane * 16);
+      const uint32_t aw = *reinterpret_cast<const uint32_t*>(st + kMxAs + (i >> 2) * 256 + lane * 4);
+      const int as = (int)((aw >> (8 * (i & 3))) & 0xFFu);
       const v8i av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
 #pragma unroll
       for (int j = 0; j < NTW; ++j) {
-        const v8i bv = {(int)bq[set][j][0], (int)bq[set][j][1], (int)bq[set][j][2], (int)bq[set][j][3], 0, 0, 0, 0};
+        const v8i bv = {(int)b[j][0], (int)b[j][1], (int)b[j][2], (int)b[j][3], 0, 0, 0, 0};
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[i][j], 4, 4, 0, as, 0,
-                                                                    (int)bs[set][j]);
+                                                                    (int)((bsw >> (8 * j)) & 0xFFu));
       }
     }
   };
 
-  load_a(0);
-  load_b(0, 0);
-  store_a(0);
-  __syncthreads();
-  for (int64_t kc = 0;; kc += 2) {
-    const bool more1 = kc + 1 < KC;
-    if (more1) {
-      load_a(kc + 1);
-      load_b(kc + 1, 1);
+  // Ring: chunk c lives in slot c % D.  At the top of iteration c the
+  // chunks c .. c + D - 2 are in flight (8 loads each, in issue order); once
+  // at most (D - 2) * 8 remain, chunk c has landed.  The barrier then
+  // publishes it and also guarantees that every wavefront has finished
+  // reading slot (c - 1) % D, which is refilled with chunk c + D - 1.
+#pragma unroll
+  for (int c = 0; c < D - 1; ++c) issue(c, c);
+  // (unrolled by D so that every slot index is a constant; compute runs also
+  // on wavefronts past N: a branch around it costs accumulator copies)
+  for (int c0 = 0; c0 < KC; c0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (c0 + d < KC) {
+        __builtin_amdgcn_s_waitcnt(mx_vmcnt((D - 2) * kMxLoads));
+        __syncthreads();
+        issue(c0 + d + D - 1, (d + D - 1) % D);
+        compute(d);
+      }
     }
-    compute(0, 0);
-    if (more1) store_a(1);
-    __syncthreads();
-    if (!more1) break;
-    const bool more2 = kc + 2 < KC;
-    if (more2) {
-      load_a(kc + 2);
-      load_b(kc + 2, 0);
-    }
-    compute(1, 1);
-    if (more2) store_a(0);
-    __syncthreads();
-    if (!more2) break;
   }
+  // Drain the direct loads still in flight (chunks past the end) before the
+  // workgroup's LDS can be handed to another workgroup.
+  __builtin_amdgcn_s_waitcnt(mx_vmcnt(0));
   if (!wave_on) return;
 #pragma unroll
   for (int i = 0; i < MT; ++i)
@@ -229,14 +293,9 @@ __global__ __launch_bounds__(256) void mx_gemm_splitk_kernel(const uint8_t* __re
   const int64_t c_lo = KC * wv / 4, c_hi = KC * (wv + 1) / 4;
   const int64_t nt0 = (int64_t)blockIdx.x * NTW;
   const uint8_t* w_sc = w_prep + N * (K / 2);
-  const uint8_t* arow[MT];
-  const uint8_t* erow[MT];
-#pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    const int64_t r = min((int64_t)(i * 16 + fr), M - 1);
-    arow[i] = a_q + r * (K / 2) + fg * 16;
-    erow[i] = a_e + r * (K / 32) + fg;
-  }
+  // (activations in the operand layout, rows padded with zeros to 64: row
+  // tile i of chunk kc at ((i KC + kc) 64 + lane) 16, its scale byte i of
+  // word (kc 64 + lane))
   f32x4 acc[MT][NTW];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
@@ -252,12 +311,12 @@ __global__ __launch_bounds__(256) void mx_gemm_splitk_kernel(const uint8_t* __re
       for (int j = 0; j < NTW; ++j) {
         const int64_t unit = ((nt0 + j) * KC + kc) * 64 + lane;
         bq[u][j] = *reinterpret_cast<const u32x4*>(w_prep + unit * 16);
-        bs[u][j] = w_sc[unit];
+        bs[u][j] = w_sc[mx_scale_at(nt0 + j, kc, KC, lane)];
       }
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
-        aq[u][i] = *reinterpret_cast<const u32x4*>(arow[i] + kc * 64);
-        as[u][i] = erow[i][kc * 4];
+        aq[u][i] = *reinterpret_cast<const u32x4*>(a_q + ((i * KC + kc) * 64 + lane) * 16);
+        as[u][i] = a_e[(kc * 64 + lane) * 4 + i];
       }
     }
 #pragma unroll
@@ -318,12 +377,12 @@ hipError_t launch_mx_splitk(const uint8_t* a_q, const uint8_t* a_e, int64_t M, i
   return hipGetLastError();
 }
 
-template <int MT>
-hipError_t launch_mx_gemm_mt(const uint8_t* a_q, const uint8_t* a_e, int64_t M, int64_t N, int64_t K,
-                             const uint8_t* w_prep, void* out, int out_dtype, hipStream_t s) {
-  const dim3 grid((unsigned)((N + 255) / 256), (unsigned)((M + 16 * MT - 1) / (16 * MT)));
-  if (out_dtype) mx_gemm_kernel<MT, true><<<grid, 256, 0, s>>>(a_q, a_e, M, N, K, w_prep, out);
-  else mx_gemm_kernel<MT, false><<<grid, 256, 0, s>>>(a_q, a_e, M, N, K, w_prep, out);
+hipError_t launch_mx_gemm_tiled(const uint8_t* a_q, const uint8_t* a_e, int64_t M, int64_t N, int64_t K,
+                                const uint8_t* w_prep, void* out, int out_dtype, hipStream_t s) {
+  const int64_t tiles = ((M + 127) / 128) * ((N + 255) / 256);
+  const unsigned grid = (unsigned)(8 * ((tiles + 7) / 8));
+  if (out_dtype) mx_gemm_kernel<NVFP4_MX_DEPTH, true><<<grid, 256, 0, s>>>(a_q, a_e, M, N, K, w_prep, out);
+  else mx_gemm_kernel<NVFP4_MX_DEPTH, false><<<grid, 256, 0, s>>>(a_q, a_e, M, N, K, w_prep, out);
   return hipGetLastError();
 }
 
@@ -335,9 +394,18 @@ hipError_t launch_mx_quantize(const void* x, int dtype, int64_t rows, int64_t K,
   if (lanes == 0) return hipSuccess;
   const unsigned grid = (unsigned)((lanes + 255) / 256);
   if (dtype == 0)
-    mx_quantize_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), rows, K, ldx, q, ex);
+    mx_quantize_kernel<uint16_t, false><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), rows, K, ldx, rows, q, ex);
   else
-    mx_quantize_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), rows, K, ldx, q, ex);
+    mx_quantize_kernel<float, false><<<grid, 256, 0, s>>>(static_cast<const float*>(x), rows, K, ldx, rows, q, ex);
+  return hipGetLastError();
+}
+
+int64_t mx_rows_pad(int64_t M) { return M <= 0 ? 0 : M <= 64 ? 64 : (M + 127) / 128 * 128; }
+
+hipError_t launch_mx_quantize_operand(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, uint8_t* ex,
+                                      hipStream_t s) {
+  const int64_t lanes = mx_rows_pad(M) * (K / 8);
+  mx_quantize_kernel<uint16_t, true><<<(unsigned)((lanes + 255) / 256), 256, 0, s>>>(x, M, K, K, mx_rows_pad(M), q, ex);
   return hipGetLastError();
 }
 
@@ -356,7 +424,7 @@ hipError_t launch_mx_gemm(const uint8_t* a_q, const uint8_t* a_e, int64_t M, int
   if (M <= 16) return launch_mx_splitk<1, NVFP4_MX_NTW1, NVFP4_MX_UB1>(a_q, a_e, M, N, K, w_prep, out, out_dtype, s);
   if (M <= 32) return launch_mx_splitk<2, NVFP4_MX_NTW2, NVFP4_MX_UB2>(a_q, a_e, M, N, K, w_prep, out, out_dtype, s);
   if (M <= 64) return launch_mx_splitk<4, NVFP4_MX_NTW4, NVFP4_MX_UB4>(a_q, a_e, M, N, K, w_prep, out, out_dtype, s);
-  return launch_mx_gemm_mt<8>(a_q, a_e, M, N, K, w_prep, out, out_dtype, s);
+  return launch_mx_gemm_tiled(a_q, a_e, M, N, K, w_prep, out, out_dtype, s);
 }
 
 }  // namespace nvfp4

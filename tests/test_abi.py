@@ -148,7 +148,8 @@ def test_quantize_and_align_errors(lib):
 def test_mxfp4_sizes_and_errors(lib):
     assert lib.mxfp4_prep_weights_size(256, 512) == 256 * 256 + 256 * 16
     assert lib.mxfp4_prep_weights_size(200, 512) == 0
-    assert lib.mxfp4_linear_workspace_size(3, 256, 512) == 768 + 256
+    assert lib.mxfp4_linear_workspace_size(3, 256, 512) == 64 * 256 + 64 * 16   # rows padded to 64
+    assert lib.mxfp4_linear_workspace_size(130, 256, 512) == 256 * 256 + 256 * 16   # to whole 128-row tiles
     assert lib.mxfp4_quantize(None, 2, 4, 32, 32, None, None, None) == _lib.NVFP4_EINVAL
     assert lib.mxfp4_quantize(None, 0, 4, 48, 48, None, None, None) == _lib.NVFP4_ESHAPE
     assert lib.mxfp4_quantize(None, 0, 4, 32, 36, None, None, None) == _lib.NVFP4_ESHAPE
@@ -160,6 +161,8 @@ def test_mxfp4_sizes_and_errors(lib):
     rc = lib.mxfp4_linear(None, 8, 256, 512, None, None, 3, None, 0, None)
     assert rc == _lib.NVFP4_EINVAL and "out_dtype=3" in _lib.last_error()
     assert lib.mxfp4_linear(None, 0, 256, 512, None, None, 0, None, 0, None) == _lib.NVFP4_OK
+    rc = lib.mxfp4_linear(None, 8, 1 << 20, 1 << 14, None, None, 0, None, 0, None)
+    assert rc == _lib.NVFP4_ESHAPE and "4 GiB" in _lib.last_error()
 
 
 def test_missing_library_fails_loudly(tmp_path):
