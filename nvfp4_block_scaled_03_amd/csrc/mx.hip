@@ -112,20 +112,24 @@ __device__ __forceinline__ int64_t mx_scale_at(int64_t nt, int64_t kc, int64_t K
   return ((nt >> 2) * KC + kc) * 256 + lane * 4 + (nt & 3);
 }
 
-// y = x_hat W_hat^T for many rows.  Workgroup: 128 rows x 256 columns, 4
-// wavefronts of 128 x 64 (8 x 4 instruction tiles).  Both operands travel
-// from global memory straight into a ring of D LDS stages (one chunk of 128
-// k each, no registers in between), D - 1 chunks in flight: enough to cover
-// a miss to HBM while the chunks already resident are multiplied.  Each
-// 1 KiB direct load fills one instruction operand in lane order (lane l's 16
-// bytes at 16 l), so every fragment read is a conflict-free read of 16 bytes
-// per lane at 16 l.
+// y = x_hat W_hat^T for many rows.  Workgroup: 128 WM rows x 256 columns,
+// 4 WM wavefronts of 128 x 64 (8 x 4 instruction tiles; WM = 2 puts two
+// wavefronts on each SIMD and halves the weight bytes per product).  Both
+// operands travel from global memory straight into a ring of D LDS stages
+// (one chunk of 128 k each, no registers in between), D - 1 chunks in
+// flight.  Each 1 KiB direct load fills one instruction operand in lane
+// order (lane l's 16 bytes at 16 l) from 1 KiB of contiguous source (the
+// activation operand layout and the weight streaming layout), so every load
+// uses whole cache lines and every fragment read is conflict-free.
 //
-// Stage layout (bytes): activation tiles 8 x 1 KiB (tile i, lane l = 16 g + m:
-// row 16 i + m, codes k in [32 g, 32 g + 32)), activation scale words 4 x 256
-// (wavefront w < 2: row tiles 4 w .. 4 w + 3, lane l's word, byte i % 4),
-// weight tiles 16 x 1 KiB (wavefront w, tile j), weight scale words 4 x 256
-// (wavefront w: lane l's word, byte j for tile j).
+// Stage layout (bytes): activation tiles 8 WM x 1 KiB (tile i, lane l =
+// 16 g + m: row 16 i + m, codes k in [32 g, 32 g + 32)), activation scale
+// words 4 x 256 (group q: row tiles 4 q .. 4 q + 3, lane l's word, byte
+// i % 4), weight tiles 16 x 1 KiB (column tile j of the workgroup), weight
+// scale words 4 x 256 (group q: column tiles 4 q .. 4 q + 3).
+// Loads per wavefront per chunk: 2 activation tiles, 16 / (4 WM) weight
+// tiles and one run of scale words (WM = 1: the activation groups are
+// loaded twice, into slots that are not read).
 //
 // Tile order: workgroups are dealt to the 8 XCDs in turn (workgroup b runs on
 // XCD b % 8), and each XCD has its own L2.  Workgroup b takes tile
@@ -138,23 +142,28 @@ __device__ __forceinline__ int64_t mx_scale_at(int64_t nt, int64_t kc, int64_t K
 #ifndef NVFP4_MX_GM
 #define NVFP4_MX_GM 8
 #endif
-constexpr int kMxA = 0, kMxAs = 8192, kMxB = kMxAs + 1024, kMxBs = kMxB + 16384, kMxSlot = kMxBs + 1024;
-constexpr int kMxLoads = 8;   // direct loads per wavefront per chunk
+
+template <int WM>
+struct MxRing {
+  static constexpr int A = 0, As = 8192 * WM, B = As + 1024 + 1024 * (WM == 1), Bs = B + 16384, Slot = Bs + 1024;
+  static constexpr int Loads = 2 + 4 / WM + (WM == 1 ? 2 : 1);   // direct loads per wavefront per chunk
+};
 
 // s_waitcnt immediate that waits until at most n vector memory operations
 // are outstanding (the LDS and export counters left at their maxima).
 constexpr int mx_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <int D, bool F32>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void mx_gemm_kernel(const uint8_t* __restrict__ a_q,
-                                                      const uint8_t* __restrict__ a_e, int64_t M, int64_t N,
-                                                      int64_t K, const uint8_t* __restrict__ w_prep,
-                                                      void* __restrict__ out) {
-  static_assert(D >= 2 && (D - 2) * kMxLoads <= 63, "ring depth");
-  constexpr int ROWS = 128, MT = 8, NTW = 4;
-  __shared__ __attribute__((aligned(16))) uint8_t ring[D * kMxSlot];
+template <int WM, int D, bool F32>
+__global__ __launch_bounds__(256 * WM) __attribute__((amdgpu_waves_per_eu(WM, WM))) void mx_gemm_kernel(
+    const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_e, int64_t M, int64_t N, int64_t K,
+    const uint8_t* __restrict__ w_prep, void* __restrict__ out) {
+  using R = MxRing<WM>;
+  static_assert(D >= 2 && (D - 2) * R::Loads <= 63, "ring depth");
+  constexpr int ROWS = 128 * WM, MT = 8, NTW = 4, NBW = 4 / WM;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[D * R::Slot];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv >> 2, wn = wv & 3;
   const int64_t TM = (M + ROWS - 1) / ROWS, TN = (N + 255) / 256, tiles = TM * TN;
   const int64_t per_xcd = (tiles + 7) / 8;
   const int64_t L = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
@@ -164,25 +173,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int64_t Lg = L - grp * NVFP4_MX_GM * TN;
   const int64_t tm = grp * NVFP4_MX_GM + Lg % gh, tn = Lg / gh;
   const int64_t m0 = tm * ROWS;
-  const int64_t n_wave0 = tn * 256 + wv * 64;
+  const int64_t n_wave0 = tn * 256 + wn * 64;
   const bool wave_on = n_wave0 < N;
   const int KC = (int)(K / 128);
 
-  // Per-lane 32-bit source offsets of this wavefront's 8 loads (chunk 0);
-  // chunk kc adds kc * (1024, 256, 1024, 256) bytes.  The activations are in
-  // the operand layout with rows padded to whole tiles (zeros past M);
-  // column tiles past N repeat the last one (loaded, never stored).
+  // Per-lane 32-bit source offsets of this wavefront's loads (chunk 0);
+  // chunk kc adds kc * 1024 (tiles) or kc * 256 (scale words) bytes.  The
+  // activations are in the operand layout with rows padded to whole
+  // workgroup tiles (zeros past M); column tiles past N repeat the last
+  // group of 4 (loaded, never stored).
   uint32_t va[2];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) va[t] = (uint32_t)((((tm * 8 + 2 * wv + t) * KC) * 64 + lane) * 16);
-  // (the two scale groups of the 8 row tiles, by wavefronts 0 and 1; 2 and 3
-  // load the same words into their own slots, which are not read)
-  const uint32_t ve = (uint32_t)((((tm * 2 + (wv & 1)) * KC) * 64 + lane) * 4);
-  const int64_t nt0 = min(n_wave0, N - 64) / 16;
-  uint32_t vb[NTW];
+  for (int t = 0; t < 2; ++t) va[t] = (uint32_t)((((tm * 8 * WM + 2 * wv + t) * KC) * 64 + lane) * 16);
+  uint32_t vb[NBW];
 #pragma unroll
-  for (int j = 0; j < NTW; ++j) vb[j] = (uint32_t)(((nt0 + j) * KC * 64 + lane) * 16);
-  const uint32_t vbs = (uint32_t)((nt0 >> 2) * KC * 256 + lane * 4);
+  for (int t = 0; t < NBW; ++t) {
+    const int jt = wv * NBW + t;                                 // column tile of the workgroup
+    const int64_t nt = min(tn * 16 + jt, N / 16 - 4 + (jt & 3));  // past N: the last group
+    vb[t] = (uint32_t)(((nt * KC) * 64 + lane) * 16);
+  }
+  // scale words: WM = 1: wavefront w loads activation group (w & 1) and
+  // weight group w; WM = 2: wavefronts 0-3 the activation groups, 4-7 the
+  // weight groups.
+  const int64_t nq_last = N / 64 - 1;
+  const int qa = WM == 1 ? (wv & 1) : wv;
+  const int qb = WM == 1 ? wv : wv - 4;
+  const uint32_t vsa = (uint32_t)((((tm * 2 * WM + qa) * KC) * 64 + lane) * 4);
+  const uint32_t vsb = (uint32_t)(((min(tn * 4 + qb, nq_last) * KC) * 64 + lane) * 4);
   const uint8_t* w_sc = w_prep + N * (K / 2);
   const uint32_t ring0 = (uint32_t)(uintptr_t)ring;
 
@@ -193,19 +210,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // explicitly (vmcnt) before the barrier that publishes a slot.
   auto issue = [&](int kc, int slot) {
     kc = min(kc, KC - 1);
-    const uint32_t base = ring0 + (uint32_t)slot * kMxSlot;
+    const uint32_t base = ring0 + (uint32_t)slot * R::Slot;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
       asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(va[t] + (uint32_t)kc * 1024u), "s"(a_q),
-                   "{m0}"(base + kMxA + (2 * wv + t) * 1024) : "memory");
-    asm volatile("global_load_lds_dword %0, %1" : : "v"(ve + (uint32_t)kc * 256u), "s"(a_e),
-                 "{m0}"(base + kMxAs + wv * 256) : "memory");
+                   "{m0}"(base + R::A + (2 * wv + t) * 1024) : "memory");
 #pragma unroll
-    for (int j = 0; j < NTW; ++j)
-      asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(vb[j] + (uint32_t)kc * 1024u), "s"(w_prep),
-                   "{m0}"(base + kMxB + (wv * 4 + j) * 1024) : "memory");
-    asm volatile("global_load_lds_dword %0, %1" : : "v"(vbs + (uint32_t)kc * 256u), "s"(w_sc),
-                 "{m0}"(base + kMxBs + wv * 256) : "memory");
+    for (int t = 0; t < NBW; ++t)
+      asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(vb[t] + (uint32_t)kc * 1024u), "s"(w_prep),
+                   "{m0}"(base + R::B + (wv * NBW + t) * 1024) : "memory");
+    if (WM == 1 || wv < 4)
+      asm volatile("global_load_lds_dword %0, %1" : : "v"(vsa + (uint32_t)kc * 256u), "s"(a_e),
+                   "{m0}"(base + R::As + wv * 256) : "memory");
+    if (WM == 1 || wv >= 4)
+      asm volatile("global_load_lds_dword %0, %1" : : "v"(vsb + (uint32_t)kc * 256u), "s"(w_sc),
+                   "{m0}"(base + R::Bs + qb * 256) : "memory");
   };
 
   f32x4 acc[MT][NTW];
@@ -215,16 +234,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int fr = lane & 15, fg = lane >> 4;
   auto compute = [&](int slot) {
-    const uint8_t* st = ring + slot * kMxSlot;
+    const uint8_t* st = ring + slot * R::Slot;
     u32x4 b[NTW];
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) b[j] = *reinterpret_cast<const u32x4*>(st + kMxB + (wv * 4 + j) * 1024 + lane * 16);
-    const uint32_t bsw = *reinterpret_cast<const uint32_t*>(st + kMxBs + wv * 256 + lane * 4);
+    for (int j = 0; j < NTW; ++j) b[j] = *reinterpret_cast<const u32x4*>(st + R::B + (wn * 4 + j) * 1024 + lane * 16);
+    const uint32_t bsw = *reinterpret_cast<const uint32_t*>(st + R::Bs + wn * 256 + lane * 4);
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(st + kMxA + i * 1024 + lane * 16);
-      const uint32_t aw = *reinterpret_cast<const uint32_t*>(st + kMxAs + (i >> 2) * 256 + lane * 4);
-      const int as = (int)((aw >> (8 * (i & 3))) & 0xFFu);
+      const int ti = wm * 8 + i;
+      const u32x4 a = *reinterpret_cast<const u32x4*>(st + R::A + ti * 1024 + lane * 16);
+      const uint32_t aw = *reinterpret_cast<const uint32_t*>(st + R::As + (ti >> 2) * 256 + lane * 4);
+      const int as = (int)((aw >> (8 * (ti & 3))) & 0xFFu);
       const v8i av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
 #pragma unroll
       for (int j = 0; j < NTW; ++j) {
@@ -236,8 +256,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
 
   // Ring: chunk c lives in slot c % D.  At the top of iteration c the
-  // chunks c .. c + D - 2 are in flight (8 loads each, in issue order); once
-  // at most (D - 2) * 8 remain, chunk c has landed.  The barrier then
+  // chunks c .. c + D - 2 are in flight (Loads each, in issue order); once
+  // at most (D - 2) Loads remain, chunk c has landed.  The barrier then
   // publishes it and also guarantees that every wavefront has finished
   // reading slot (c - 1) % D, which is refilled with chunk c + D - 1.
 #pragma unroll
@@ -248,7 +268,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       if (c0 + d < KC) {
-        __builtin_amdgcn_s_waitcnt(mx_vmcnt((D - 2) * kMxLoads));
+        __builtin_amdgcn_s_waitcnt(mx_vmcnt((D - 2) * R::Loads));
         __syncthreads();
         issue(c0 + d + D - 1, (d + D - 1) % D);
         compute(d);
@@ -259,13 +279,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // workgroup's LDS can be handed to another workgroup.
   __builtin_amdgcn_s_waitcnt(mx_vmcnt(0));
   if (!wave_on) return;
+  const int64_t mw0 = m0 + wm * 128;
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t row = m0 + i * 16 + fg * 4 + r;
+        const int64_t row = mw0 + i * 16 + fg * 4 + r;
         if (row < M) {
           const int64_t o = row * N + n_wave0 + 16 * j + fr;
           if constexpr (F32) static_cast<float*>(out)[o] = acc[i][j][r];
@@ -377,12 +398,13 @@ hipError_t launch_mx_splitk(const uint8_t* a_q, const uint8_t* a_e, int64_t M, i
   return hipGetLastError();
 }
 
-hipError_t launch_mx_gemm_tiled(const uint8_t* a_q, const uint8_t* a_e, int64_t M, int64_t N, int64_t K,
-                                const uint8_t* w_prep, void* out, int out_dtype, hipStream_t s) {
-  const int64_t tiles = ((M + 127) / 128) * ((N + 255) / 256);
+template <int WM>
+hipError_t launch_mx_gemm_ring(const uint8_t* a_q, const uint8_t* a_e, int64_t M, int64_t N, int64_t K,
+                               const uint8_t* w_prep, void* out, int out_dtype, hipStream_t s) {
+  const int64_t tiles = ((M + 128 * WM - 1) / (128 * WM)) * ((N + 255) / 256);
   const unsigned grid = (unsigned)(8 * ((tiles + 7) / 8));
-  if (out_dtype) mx_gemm_kernel<NVFP4_MX_DEPTH, true><<<grid, 256, 0, s>>>(a_q, a_e, M, N, K, w_prep, out);
-  else mx_gemm_kernel<NVFP4_MX_DEPTH, false><<<grid, 256, 0, s>>>(a_q, a_e, M, N, K, w_prep, out);
+  if (out_dtype) mx_gemm_kernel<WM, NVFP4_MX_DEPTH, true><<<grid, 256 * WM, 0, s>>>(a_q, a_e, M, N, K, w_prep, out);
+  else mx_gemm_kernel<WM, NVFP4_MX_DEPTH, false><<<grid, 256 * WM, 0, s>>>(a_q, a_e, M, N, K, w_prep, out);
   return hipGetLastError();
 }
 
@@ -400,7 +422,9 @@ hipError_t launch_mx_quantize(const void* x, int dtype, int64_t rows, int64_t K,
   return hipGetLastError();
 }
 
-int64_t mx_rows_pad(int64_t M) { return M <= 0 ? 0 : M <= 64 ? 64 : (M + 127) / 128 * 128; }
+// Rows of the activation operand: whole tiles of the kernel that runs (64
+// rows for the split-K kernels, 128 or 256 for the ring kernel).
+int64_t mx_rows_pad(int64_t M) { return M <= 0 ? 0 : M <= 64 ? 64 : M <= 128 ? 128 : (M + 255) / 256 * 256; }
 
 hipError_t launch_mx_quantize_operand(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, uint8_t* ex,
                                       hipStream_t s) {
@@ -424,7 +448,9 @@ hipError_t launch_mx_gemm(const uint8_t* a_q, const uint8_t* a_e, int64_t M, int
   if (M <= 16) return launch_mx_splitk<1, NVFP4_MX_NTW1, NVFP4_MX_UB1>(a_q, a_e, M, N, K, w_prep, out, out_dtype, s);
   if (M <= 32) return launch_mx_splitk<2, NVFP4_MX_NTW2, NVFP4_MX_UB2>(a_q, a_e, M, N, K, w_prep, out, out_dtype, s);
   if (M <= 64) return launch_mx_splitk<4, NVFP4_MX_NTW4, NVFP4_MX_UB4>(a_q, a_e, M, N, K, w_prep, out, out_dtype, s);
-  return launch_mx_gemm_tiled(a_q, a_e, M, N, K, w_prep, out, out_dtype, s);
+  // up to 128 rows: one 128-row tile (4 wavefronts); more: 256-row tiles
+  if (M <= 128) return launch_mx_gemm_ring<1>(a_q, a_e, M, N, K, w_prep, out, out_dtype, s);
+  return launch_mx_gemm_ring<2>(a_q, a_e, M, N, K, w_prep, out, out_dtype, s);
 }
 
 }  // namespace nvfp4

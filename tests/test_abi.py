@@ -149,7 +149,8 @@ def test_mxfp4_sizes_and_errors(lib):
     assert lib.mxfp4_prep_weights_size(256, 512) == 256 * 256 + 256 * 16
     assert lib.mxfp4_prep_weights_size(200, 512) == 0
     assert lib.mxfp4_linear_workspace_size(3, 256, 512) == 64 * 256 + 64 * 16   # rows padded to 64
-    assert lib.mxfp4_linear_workspace_size(130, 256, 512) == 256 * 256 + 256 * 16   # to whole 128-row tiles
+    assert lib.mxfp4_linear_workspace_size(100, 256, 512) == 128 * 256 + 128 * 16   # to one 128-row tile
+    assert lib.mxfp4_linear_workspace_size(130, 256, 512) == 256 * 256 + 256 * 16   # to whole 256-row tiles
     assert lib.mxfp4_quantize(None, 2, 4, 32, 32, None, None, None) == _lib.NVFP4_EINVAL
     assert lib.mxfp4_quantize(None, 0, 4, 48, 48, None, None, None) == _lib.NVFP4_ESHAPE
     assert lib.mxfp4_quantize(None, 0, 4, 32, 36, None, None, None) == _lib.NVFP4_ESHAPE

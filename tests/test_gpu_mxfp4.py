@@ -110,10 +110,13 @@ def test_linear(dev, M):
     _check(x, lw, ref, _bound(x_hat, omx.dequantize(wc, we), K))
 
 
-@pytest.mark.parametrize("M,N,K", [(3, 128, 128), (20, 256, 384), (40, 128, 640), (100, 128, 256)])
+@pytest.mark.parametrize("M,N,K", [(3, 128, 128), (20, 256, 384), (40, 128, 640), (100, 128, 256),
+                                   (129, 256, 384), (200, 128, 640)])
 def test_linear_short_k(dev, M, N, K):
-    """K of 1, 3, 5 and 2 chunks of 128: wavefronts of the split-K kernels with
-    no chunk or uneven shares, and the tiled kernel's odd chunk count."""
+    """K of 1 to 5 chunks of 128 (wavefronts of the split-K kernels with no
+    chunk or uneven shares; ring kernels with fewer chunks than ring slots)
+    and both row tilings of the ring kernel (128 and 256 rows) with ragged
+    tails."""
     w = _weight(dev, N, K, 23)
     wc, we = omx.quantize(to_np(w).astype(np.float64))
     lw = ops.prepare_mx_weight(torch.from_numpy(onv.pack_codes(wc)).to(dev), torch.from_numpy(we).to(dev))
