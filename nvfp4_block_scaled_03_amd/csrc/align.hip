@@ -374,13 +374,16 @@ __global__ __launch_bounds__(1024) void scale_align_kernel(const uint16_t* __res
     *g = global_scale_of_amax(r);
     return;
   }
-  __hip_atomic_fetch_max(ws + 1, (uint32_t)__float_as_int(r), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint32_t done = __hip_atomic_fetch_add(ws, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  // (the count waits for the fetch-max's result: see nvfp4_global_scale)
+  const uint32_t old = __hip_atomic_fetch_max(ws + 1, (uint32_t)__float_as_int(r), __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t done = __hip_atomic_fetch_add(ws, 1u + (old >> 31), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
   if (done == (uint32_t)nblk - 1) {
-    const uint32_t bits = __hip_atomic_load(ws + 1, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t bits = __hip_atomic_fetch_max(ws + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *g = global_scale_of_amax(__int_as_float((int)bits));
     __hip_atomic_store(ws + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(ws, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(ws, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -33,38 +33,66 @@ __device__ __forceinline__ float block_max(float m) {
 // unsigned integers), then counts itself in ws_cnt[b]; the last workgroup of a
 // batch computes g[b] and puts both words back to zero, so the workspace is
 // ready for the next call (it must be zero before the first one).
+//
+// Both words are only ever touched by device-scope atomics, which every
+// workgroup performs at the same place, and the count is issued only after
+// the fetch-max has returned (the count's operand depends on its result), so
+// the workgroup that counts last reads the complete maximum.  No workgroup
+// wrote plain data that another reads, so no release/acquire fence is taken:
+// at device scope those write back and invalidate the XCD's L2, and a
+// thousand of them serialised on one counter cost tens of microseconds.
+__device__ __forceinline__ void fold_max_and_count(uint32_t* ws_cnt, uint32_t* ws_max, float m,
+                                                   uint32_t nblk, float* g) {
+  const uint32_t old = __hip_atomic_fetch_max(ws_max, (uint32_t)__float_as_int(m), __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+  // old < 2^31 (bits of a non-negative float), so the increment is 1, but it
+  // cannot be issued before the fetch-max has completed.
+  const uint32_t done = __hip_atomic_fetch_add(ws_cnt, 1u + (old >> 31), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+  if (done == nblk - 1) {
+    const uint32_t bits = __hip_atomic_fetch_max(ws_max, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *g = global_scale_of_amax(__int_as_float((int)bits));
+    __hip_atomic_store(ws_max, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(ws_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Each thread keeps U independent 16-byte loads in flight per trip; with the
+// grid of amax_blocks a bf16 tensor is read in one trip, so the whole tensor
+// is requested at once rather than in latency-bound rounds.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void global_scale_kernel(const T* __restrict__ x, int64_t n,
                                                                 float* __restrict__ g,
                                                                 uint32_t* __restrict__ ws) {
+  constexpr int U = 8;
+  constexpr int E = 16 / sizeof(T);  // elements per load
   const int64_t b = blockIdx.y;
   const T* xb = x + b * n;
-  const int64_t stride = (int64_t)gridDim.x * kThreads * 8;
+  const int64_t stride = (int64_t)gridDim.x * kThreads * E;
   float m = 0.0f;
-  for (int64_t i = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8; i < n; i += stride) {
-    float v[8];
-    load8(xb, i, v);
+  int64_t i = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * E;
+  for (; i + (U - 1) * stride < n; i += U * stride) {
+    float v[U][E];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+    for (int u = 0; u < U; ++u) load_vec(xb, i + u * stride, v[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < E; ++j) m = fmaxf(m, fabsf(v[u][j]));
+  }
+  for (; i < n; i += stride) {
+    float v[E];
+    load_vec(xb, i, v);
+#pragma unroll
+    for (int j = 0; j < E; ++j) m = fmaxf(m, fabsf(v[j]));
   }
   m = block_max(m);
   if (threadIdx.x == 0) {
-    uint32_t* ws_cnt = ws + 2 * b;
-    uint32_t* ws_max = ws + 2 * b + 1;
     if (gridDim.x == 1) {
       g[b] = global_scale_of_amax(m);
       return;
     }
-    __hip_atomic_fetch_max(ws_max, (uint32_t)__float_as_int(m), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t done = __hip_atomic_fetch_add(ws_cnt, 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    if (done == gridDim.x - 1) {
-      const uint32_t bits = __hip_atomic_load(ws_max, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-      g[b] = global_scale_of_amax(__int_as_float((int)bits));
-      __hip_atomic_store(ws_max, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(ws_cnt, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    fold_max_and_count(ws + 2 * b, ws + 2 * b + 1, m, gridDim.x, g + b);
   }
 }
 
@@ -90,8 +118,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const T* __restrict_
 }
 
 int64_t amax_blocks(int64_t n) {
-  // About 32 elements per thread; at most 1024 workgroups per batch.
-  int64_t nb = (n + kThreads * 32 - 1) / (kThreads * 32);
+  // 64 elements per thread (one trip of 8 loads for bf16); at most 1024
+  // workgroups per batch.
+  int64_t nb = (n + kThreads * 64 - 1) / (kThreads * 64);
   return nb < 1 ? 1 : (nb > 1024 ? 1024 : nb);
 }
 

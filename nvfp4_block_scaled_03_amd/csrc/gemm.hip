@@ -28,6 +28,7 @@
 // in the layout written by prep.hip: one coalesced 16-byte load per lane per
 // 16 columns x 128 k, which is exactly the lane's matrix-instruction operand.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -627,9 +628,10 @@ void grouped_gemm_wide_kernel(KParams p) {
   // prefetch of chunk kc + 1 with the compute of chunk kc.  Completion is
   // awaited explicitly (lds_fill_wait) before the barrier that publishes a
   // buffer.
-  auto stage_a = [&](int kc, uint8_t* buf) {
+  auto stage_a = [&, a_base](auto mta, int kc, uint8_t* buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < LOADS; ++q) {
+      if (4 * (wv * LOADS + q) >= 16 * decltype(mta)::value) continue;  // rows no m-tile reads
       const uint32_t lds = (uint32_t)(uintptr_t)(buf + (wv * LOADS + q) * 1024);
       const uint32_t voff = a_off[q] + (uint32_t)kc * ROW_BYTES;
       asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(a_base), "{m0}"(lds) : "memory");
@@ -665,7 +667,8 @@ void grouped_gemm_wide_kernel(KParams p) {
   // [32g + 8s, 32g + 8s + 8), i.e. source unit 4g + s, stored at unit
   // (4g + s) ^ m of the row.
   const int m = lane & 15, g = lane >> 4;
-  auto compute = [&](const uint8_t* buf, const u32x4 (&bq)[NTW], const uint32_t (&bs)[NTW / 2]) {
+  auto compute = [&](auto mta, const uint8_t* buf, const u32x4 (&bq)[NTW], const uint32_t (&bs)[NTW / 2]) __attribute__((always_inline)) {
+    constexpr int MA = decltype(mta)::value;  // m-tiles holding rows of this tile
     if (!wave_on) return;
     const uint8_t* abuf = buf + m * ROW_BYTES;
     if constexpr (AK == kActF16) {
@@ -679,9 +682,9 @@ void grouped_gemm_wide_kernel(KParams p) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int ucol = ((4 * g + s) ^ m) * 16;
-        f16x8 af[MT];
+        f16x8 af[MA];
 #pragma unroll
-        for (int i = 0; i < MT; ++i) af[i] = *reinterpret_cast<const f16x8*>(abuf + i * 16 * ROW_BYTES + ucol);
+        for (int i = 0; i < MA; ++i) af[i] = *reinterpret_cast<const f16x8*>(abuf + i * 16 * ROW_BYTES + ucol);
         __builtin_amdgcn_sched_barrier(0);
         f16x8 bf[NTW];
 #pragma unroll
@@ -689,18 +692,18 @@ void grouped_gemm_wide_kernel(KParams p) {
 #pragma unroll
         for (int j = 0; j < NTW; ++j)
 #pragma unroll
-          for (int i = 0; i < MT; ++i)
+          for (int i = 0; i < MA; ++i)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
 #if NVFP4_WIDE_INTERLEAVE
         __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);   // decode of tile 0
 #pragma unroll
         for (int j = 0; j + 1 < NTW; ++j)
 #pragma unroll
-          for (int i = 0; i < MT; ++i) {
+          for (int i = 0; i < MA; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix instruction
             __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // one decode instruction
           }
-        __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);  // the last tile's
+        __builtin_amdgcn_sched_group_barrier(0x008, MA, 0);  // the last tile's
 #endif
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -716,9 +719,9 @@ void grouped_gemm_wide_kernel(KParams p) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int ucol = ((4 * g + s) ^ m) * 16;
-        bf16x8 af[MT];
+        bf16x8 af[MA];
 #pragma unroll
-        for (int i = 0; i < MT; ++i) af[i] = *reinterpret_cast<const bf16x8*>(abuf + i * 16 * ROW_BYTES + ucol);
+        for (int i = 0; i < MA; ++i) af[i] = *reinterpret_cast<const bf16x8*>(abuf + i * 16 * ROW_BYTES + ucol);
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 bf[NTW];
 #pragma unroll
@@ -726,7 +729,7 @@ void grouped_gemm_wide_kernel(KParams p) {
 #pragma unroll
         for (int j = 0; j < NTW; ++j)
 #pragma unroll
-          for (int i = 0; i < MT; ++i)
+          for (int i = 0; i < MA; ++i)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
 #if NVFP4_WIDE_INTERLEAVE
         // (the bf16 decode of a tile is 16 VALU instructions: two per matrix
@@ -735,11 +738,11 @@ void grouped_gemm_wide_kernel(KParams p) {
 #pragma unroll
         for (int j = 0; j + 1 < NTW; ++j)
 #pragma unroll
-          for (int i = 0; i < MT; ++i) {
+          for (int i = 0; i < MA; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
           }
-        __builtin_amdgcn_sched_group_barrier(0x008, MT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, MA, 0);
 #endif
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -750,37 +753,47 @@ void grouped_gemm_wide_kernel(KParams p) {
   // buffer kc & 1 and register set kc & 1 while chunk kc + 1 lands; the
   // direct loads are complete once the vector counter drains, then one
   // barrier per chunk publishes the buffer.
-  stage_a(0, As0);
-  load_b(0, bq0, bs0);
-  lds_fill_wait();
-  __syncthreads();
-  // Every path back to the loop head passes the full wait (the exit tests
-  // come after it), so the compiler knows no load is pending there and does
-  // not drain the counter before the next refills.
-  for (int kc = 0;; kc += 2) {
-    const bool more1 = kc + 1 < KC;
-    if (more1) {
-      stage_a(kc + 1, As1);
-      load_b(kc + 1, bq1, bs1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    compute(As0, bq0, bs0);
-    __builtin_amdgcn_sched_barrier(0);
+  auto main_loop = [&](auto mta) __attribute__((always_inline)) {
+    stage_a(mta, 0, As0);
+    load_b(0, bq0, bs0);
     lds_fill_wait();
     __syncthreads();
-    if (!more1) break;
-    const bool more2 = kc + 2 < KC;
-    if (more2) {
-      stage_a(kc + 2, As0);
-      load_b(kc + 2, bq0, bs0);
+    // Every path back to the loop head passes the full wait (the exit tests
+    // come after it), so the compiler knows no load is pending there and does
+    // not drain the counter before the next refills.
+    for (int kc = 0;; kc += 2) {
+      const bool more1 = kc + 1 < KC;
+      if (more1) {
+        stage_a(mta, kc + 1, As1);
+        load_b(kc + 1, bq1, bs1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      compute(mta, As0, bq0, bs0);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_fill_wait();
+      __syncthreads();
+      if (!more1) break;
+      const bool more2 = kc + 2 < KC;
+      if (more2) {
+        stage_a(mta, kc + 2, As0);
+        load_b(kc + 2, bq0, bs0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      compute(mta, As1, bq1, bs1);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_fill_wait();
+      __syncthreads();
+      if (!more2) break;
     }
-    __builtin_amdgcn_sched_barrier(0);
-    compute(As1, bq1, bs1);
-    __builtin_amdgcn_sched_barrier(0);
-    lds_fill_wait();
-    __syncthreads();
-    if (!more2) break;
-  }
+  };
+  // The last tile of an expert is usually short: only the m-tiles that hold
+  // its rows are staged and multiplied (the weight stream and decode are the
+  // same for every tile height).  The choice is uniform over the workgroup.
+  const int mt_rows = (t.nrows + 15) >> 4;
+  if (mt_rows > MT / 2) main_loop(std::integral_constant<int, MT>{});
+  else if (mt_rows > MT / 4) main_loop(std::integral_constant<int, MT / 2>{});
+  else if (mt_rows > 1) main_loop(std::integral_constant<int, MT / 4>{});
+  else main_loop(std::integral_constant<int, 1>{});
   if (!wave_on) return;
   if constexpr (!swiglu_epi(EPI)) {
     epilogue<EPI, MT, NTW>(p, acc, t.e, t.row0, t.nrows, n_wave0, lane);

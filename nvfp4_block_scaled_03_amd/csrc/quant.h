@@ -30,6 +30,14 @@ __device__ __forceinline__ void load8(const float* x, int64_t i, float v[8]) {
   }
 }
 
+// One 16-byte load as floats: 8 bf16 or 4 FP32 elements (x + i 16-byte aligned).
+__device__ __forceinline__ void load_vec(const uint16_t* x, int64_t i, float (&v)[8]) { load8(x, i, v); }
+__device__ __forceinline__ void load_vec(const float* x, int64_t i, float (&v)[4]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(x + i);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = a[j];
+}
+
 // Value of the E2M1 code c (sign in bit 3) times the block scale s, exact
 // in f16 (at most six significant bits, magnitude in [2^-10, 2688]).
 __device__ __forceinline__ uint32_t deq_f16_bits(uint32_t c, float s) {
