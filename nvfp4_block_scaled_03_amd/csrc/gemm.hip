@@ -189,6 +189,54 @@ __device__ __forceinline__ void epilogue(const KParams& p, f32x4 (&acc)[MT][NTW]
   }
 }
 
+// Row-major store epilogue (FP32 or bf16 output) of a wavefront's MT x NTW
+// accumulator tiles through a wave-private LDS area sh of 16 x (16 NTW + 4)
+// floats.  In the matrix-instruction layout a lane holds four rows of one
+// column, so direct stores write 4 bytes per lane; here each 16-row m-tile
+// is turned around in LDS and leaves as 16-byte (FP32) or 8-byte (bf16)
+// stores of four consecutive columns, a wavefront writing whole rows.
+template <int EPI, int MT, int NTW>
+__device__ __forceinline__ void epilogue_rowmajor(const KParams& p, f32x4 (&acc)[MT][NTW], int e,
+                                                  int row0, int nrows, int n_wave0, int lane,
+                                                  float* sh) {
+  static_assert(EPI == kEpiStoreF32 || EPI == kEpiStoreBf16, "plain stores only");
+  constexpr int W = 16 * NTW;       // columns of the wavefront
+  constexpr int SW = W + 4;         // LDS row stride in floats
+  constexpr int LPR = W / 4;        // lanes per row (four columns each)
+  constexpr int RPP = 64 / LPR;     // rows per pass
+  const float alpha = p.g_a ? ld_uniform(p.g_a) * ld_uniform(p.g_w + e) : ld_uniform(p.g_w + e);
+  const int ln = lane & 15, lg = lane >> 4;
+  const int rr = lane / LPR, c4 = (lane % LPR) * 4;
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    if (i * 16 >= nrows) break;     // (uniform)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sh[(lg * 4 + r) * SW + 16 * j + ln] = alpha * acc[i][j][r];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+    for (int ps = 0; ps < 16 / RPP; ++ps) {
+      const int row = i * 16 + ps * RPP + rr;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(sh + (ps * RPP + rr) * SW + c4);
+      if (row < nrows) {
+        const int64_t o = (int64_t)(row0 + row) * p.N + n_wave0 + c4;
+        if constexpr (EPI == kEpiStoreF32) {
+          *reinterpret_cast<f32x4*>(p.out_f32 + o) = v;
+        } else {
+          const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+          const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+          *reinterpret_cast<u32x2*>(p.out_h + o) = u32x2{lo, hi};
+        }
+      }
+    }
+    // (the next m-tile rewrites sh only after every lane has read it)
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
 // Block-major epilogue of the SwiGLU GEMM1 variants for a wavefront's
 // 16*MT rows x 16*NTW streaming columns (NTW/2 blocks of 16 h columns).  In
 // the matrix-instruction layout a 16-element block of a row is spread over
@@ -795,17 +843,18 @@ void grouped_gemm_wide_kernel(KParams p) {
   else if (mt_rows > 1) main_loop(std::integral_constant<int, MT / 4>{});
   else main_loop(std::integral_constant<int, 1>{});
   if (!wave_on) return;
+  // The activation buffers are free (the loop ended on a barrier after the
+  // last reads): each wavefront takes 1/NW of them for its epilogue.
+  constexpr int WAVE_BYTES = 2 * BUF_BYTES / NW;
+  uint8_t* const area = (wv < NW / 2 ? As0 : As1) + (wv % (NW / 2)) * WAVE_BYTES;
+  float* sh = reinterpret_cast<float*>(area);
   if constexpr (!swiglu_epi(EPI)) {
-    epilogue<EPI, MT, NTW>(p, acc, t.e, t.row0, t.nrows, n_wave0, lane);
+    static_assert(16 * (16 * NTW + 4) * 4 <= WAVE_BYTES, "one m-tile fits the wave's area");
+    epilogue_rowmajor<EPI, MT, NTW>(p, acc, t.e, t.row0, t.nrows, n_wave0, lane, sh);
   } else {
-    // The activation buffers are free (the loop ended on a barrier after the
-    // last reads): each wavefront takes 1/NW of them for the epilogue, which
-    // runs in passes of PM m-tiles (all 8 with 4 wavefronts, 4 with 8).
-    constexpr int WAVE_BYTES = 2 * BUF_BYTES / NW;
+    // SwiGLU: passes of PM m-tiles (all 8 with 4 wavefronts, 4 with 8).
     constexpr int PM = WAVE_BYTES / (16 * 8 * NTW * 4);
     static_assert(PM >= 1 && MT % PM == 0, "whole m-tiles per pass");
-    uint8_t* const area = (wv < NW / 2 ? As0 : As1) + (wv % (NW / 2)) * WAVE_BYTES;
-    float* sh = reinterpret_cast<float*>(area);
 #pragma unroll
     for (int pm = 0; pm < MT; pm += PM)
       epilogue_blocks<EPI, PM, NTW>(p, *reinterpret_cast<f32x4(*)[PM][NTW]>(&acc[pm]), t.e,
