@@ -32,11 +32,12 @@ __device__ __forceinline__ int expert_of(const AlignP& a, int64_t f, bool& valid
 }
 
 // ---------------------------------------------------------------- counts
-__global__ __launch_bounds__(256) void align_count_kernel(AlignP a, int32_t* __restrict__ counts) {
+// Expert histogram of one chunk of kAlignChunk pairs (256 threads).
+__device__ __forceinline__ void count_chunk(const AlignP& a, int32_t* __restrict__ counts, int chunk) {
   __shared__ int hist[kMaxExperts];
   for (int e = threadIdx.x; e < a.slots; e += 256) hist[e] = 0;
   __syncthreads();
-  const int64_t f0 = (int64_t)blockIdx.x * kAlignChunk;
+  const int64_t f0 = (int64_t)chunk * kAlignChunk;
   for (int r = 0; r < kAlignChunk / 256; ++r) {
     const int64_t f = f0 + r * 256 + threadIdx.x;
     if (f < a.P) {
@@ -47,7 +48,11 @@ __global__ __launch_bounds__(256) void align_count_kernel(AlignP a, int32_t* __r
   }
   __syncthreads();
   for (int e = threadIdx.x; e < a.slots; e += 256)
-    counts[(int64_t)blockIdx.x * a.slots + e] = hist[e];
+    counts[(int64_t)chunk * a.slots + e] = hist[e];
+}
+
+__global__ __launch_bounds__(256) void align_count_kernel(AlignP a, int32_t* __restrict__ counts) {
+  count_chunk(a, counts, blockIdx.x);
 }
 
 // Exclusive scan over 1024 threads; returns the thread's prefix, *total gets the sum.
@@ -147,13 +152,12 @@ __device__ __forceinline__ void write_plan(int32_t* __restrict__ plan, const int
 
 // Per expert: turn the per-chunk counts into the chunk's first output row
 // (in place), then scan over experts and write offsets and tile lists.
-// The counts of a group of chunks are loaded together (independent loads),
-// so the walk over chunks costs one memory latency per group.
+// Both walks over the chunks load a group of chunks together (independent
+// loads), so each costs one memory latency per group.
 constexpr int kScanGroup = 16;
-__global__ __launch_bounds__(1024) void align_scan_kernel(AlignP a, int32_t* __restrict__ counts,
-                                                          int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ plan,
-                                                          int4 list_off) {
+__device__ __forceinline__ void scan_body(const AlignP& a, int32_t* __restrict__ counts,
+                                          int32_t* __restrict__ offsets, int32_t* __restrict__ plan,
+                                          int4 list_off) {
   const int e = threadIdx.x;
   int n_e = 0;
   if (e < a.slots) {
@@ -172,12 +176,27 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(AlignP a, int32_t* __r
   int total;
   const int off_e = block_exclusive_scan_1024(n_e, &total);
   if (e < a.slots) {
-    for (int c = 0; c < a.nchunks; ++c) counts[(int64_t)c * a.slots + e] += off_e;
+    for (int c0 = 0; c0 < a.nchunks; c0 += kScanGroup) {
+      int v[kScanGroup];
+#pragma unroll
+      for (int j = 0; j < kScanGroup; ++j)
+        v[j] = c0 + j < a.nchunks ? counts[(int64_t)(c0 + j) * a.slots + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kScanGroup; ++j)
+        if (c0 + j < a.nchunks) counts[(int64_t)(c0 + j) * a.slots + e] = v[j] + off_e;
+    }
     offsets[e] = off_e;
   }
   if (e == 0) offsets[a.slots] = total;
   const int lo[4] = {list_off.x, list_off.y, list_off.z, list_off.w};
   write_plan(plan, lo, e, a.slots, off_e, n_e);
+}
+
+__global__ __launch_bounds__(1024) void align_scan_kernel(AlignP a, int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ plan,
+                                                          int4 list_off) {
+  scan_body(a, counts, offsets, plan, list_off);
 }
 
 // ---------------------------------------------------------------- scatter

@@ -13,9 +13,11 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kScaleThreads = 1024;  // global-scale workgroups
 
+template <int NT>
 __device__ __forceinline__ float block_max(float m) {
-  __shared__ float red[kThreads / kWave];
+  __shared__ float red[NT / kWave];
   // Reduce within the wave.
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -24,7 +26,7 @@ __device__ __forceinline__ float block_max(float m) {
   __syncthreads();
   float r = red[0];
 #pragma unroll
-  for (int i = 1; i < kThreads / kWave; ++i) r = fmaxf(r, red[i]);
+  for (int i = 1; i < NT / kWave; ++i) r = fmaxf(r, red[i]);
   return r;
 }
 
@@ -34,43 +36,20 @@ __device__ __forceinline__ float block_max(float m) {
 // batch computes g[b] and puts both words back to zero, so the workspace is
 // ready for the next call (it must be zero before the first one).
 //
-// Both words are only ever touched by device-scope atomics, which every
-// workgroup performs at the same place, and the count is issued only after
-// the fetch-max has returned (the count's operand depends on its result), so
-// the workgroup that counts last reads the complete maximum.  No workgroup
-// wrote plain data that another reads, so no release/acquire fence is taken:
-// at device scope those write back and invalidate the XCD's L2, and a
-// thousand of them serialised on one counter cost tens of microseconds.
-__device__ __forceinline__ void fold_max_and_count(uint32_t* ws_cnt, uint32_t* ws_max, float m,
-                                                   uint32_t nblk, float* g) {
-  const uint32_t old = __hip_atomic_fetch_max(ws_max, (uint32_t)__float_as_int(m), __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-  // old < 2^31 (bits of a non-negative float), so the increment is 1, but it
-  // cannot be issued before the fetch-max has completed.
-  const uint32_t done = __hip_atomic_fetch_add(ws_cnt, 1u + (old >> 31), __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-  if (done == nblk - 1) {
-    const uint32_t bits = __hip_atomic_fetch_max(ws_max, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *g = global_scale_of_amax(__int_as_float((int)bits));
-    __hip_atomic_store(ws_max, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(ws_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
 // Each thread keeps U independent 16-byte loads in flight per trip; with the
 // grid of amax_blocks a bf16 tensor is read in one trip, so the whole tensor
 // is requested at once rather than in latency-bound rounds.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void global_scale_kernel(const T* __restrict__ x, int64_t n,
+__global__ __launch_bounds__(kScaleThreads) void global_scale_kernel(const T* __restrict__ x, int64_t n,
                                                                 float* __restrict__ g,
                                                                 uint32_t* __restrict__ ws) {
   constexpr int U = 8;
   constexpr int E = 16 / sizeof(T);  // elements per load
   const int64_t b = blockIdx.y;
   const T* xb = x + b * n;
-  const int64_t stride = (int64_t)gridDim.x * kThreads * E;
+  const int64_t stride = (int64_t)gridDim.x * kScaleThreads * E;
   float m = 0.0f;
-  int64_t i = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * E;
+  int64_t i = ((int64_t)blockIdx.x * kScaleThreads + threadIdx.x) * E;
   for (; i + (U - 1) * stride < n; i += U * stride) {
     float v[U][E];
 #pragma unroll
@@ -86,7 +65,7 @@ __global__ __launch_bounds__(kThreads) void global_scale_kernel(const T* __restr
 #pragma unroll
     for (int j = 0; j < E; ++j) m = fmaxf(m, fabsf(v[j]));
   }
-  m = block_max(m);
+  m = block_max<kScaleThreads>(m);
   if (threadIdx.x == 0) {
     if (gridDim.x == 1) {
       g[b] = global_scale_of_amax(m);
@@ -118,10 +97,12 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const T* __restrict_
 }
 
 int64_t amax_blocks(int64_t n) {
-  // 64 elements per thread (one trip of 8 loads for bf16); at most 1024
-  // workgroups per batch.
-  int64_t nb = (n + kThreads * 64 - 1) / (kThreads * 64);
-  return nb < 1 ? 1 : (nb > 1024 ? 1024 : nb);
+  // 64 elements per thread (one trip of 8 loads for bf16), at most 128
+  // workgroups per batch: the workgroups meet in two atomics on one address
+  // each, and those serialise (measured on a 16.7 MB tensor: 512 workgroups
+  // 17 us, 256 of a quarter the threads 11.5 us).
+  int64_t nb = (n + kScaleThreads * 64 - 1) / (kScaleThreads * 64);
+  return nb < 1 ? 1 : (nb > 128 ? 128 : nb);
 }
 
 }  // namespace
@@ -137,9 +118,9 @@ hipError_t launch_global_scale(const void* x, int dtype, int64_t batches, int64_
   dim3 grid((unsigned)nb, (unsigned)batches);
   uint32_t* w = static_cast<uint32_t*>(ws);
   if (dtype == 0)
-    global_scale_kernel<uint16_t><<<grid, kThreads, 0, s>>>(static_cast<const uint16_t*>(x), n, g, w);
+    global_scale_kernel<uint16_t><<<grid, kScaleThreads, 0, s>>>(static_cast<const uint16_t*>(x), n, g, w);
   else
-    global_scale_kernel<float><<<grid, kThreads, 0, s>>>(static_cast<const float*>(x), n, g, w);
+    global_scale_kernel<float><<<grid, kScaleThreads, 0, s>>>(static_cast<const float*>(x), n, g, w);
   return hipGetLastError();
 }
 

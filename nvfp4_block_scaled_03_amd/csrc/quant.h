@@ -30,6 +30,35 @@ __device__ __forceinline__ void load8(const float* x, int64_t i, float v[8]) {
   }
 }
 
+// Cross-workgroup step of a global scale: workgroup maxima are folded into
+// ws_max (float bits of a non-negative value order like unsigned integers)
+// and counted in ws_cnt; the last of nblk workgroups writes g and puts both
+// words back to zero, so the workspace is ready for the next call (it must be
+// zero before the first one).
+//
+// Both words are only ever touched by device-scope atomics, which every
+// workgroup performs at the same place, and the count is issued only after
+// the fetch-max has returned (the count's operand depends on its result), so
+// the workgroup that counts last reads the complete maximum.  No workgroup
+// wrote plain data that another reads, so no release/acquire fence is taken:
+// at device scope those write back and invalidate the XCD's L2, and a
+// thousand of them serialised on one counter cost tens of microseconds.
+__device__ __forceinline__ void fold_max_and_count(uint32_t* ws_cnt, uint32_t* ws_max, float m,
+                                                   uint32_t nblk, float* g) {
+  const uint32_t old = __hip_atomic_fetch_max(ws_max, (uint32_t)__float_as_int(m), __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+  // old < 2^31 (bits of a non-negative float), so the increment is 1, but it
+  // cannot be issued before the fetch-max has completed.
+  const uint32_t done = __hip_atomic_fetch_add(ws_cnt, 1u + (old >> 31), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+  if (done == nblk - 1) {
+    const uint32_t bits = __hip_atomic_fetch_max(ws_max, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *g = global_scale_of_amax(__int_as_float((int)bits));
+    __hip_atomic_store(ws_max, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(ws_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // One 16-byte load as floats: 8 bf16 or 4 FP32 elements (x + i 16-byte aligned).
 __device__ __forceinline__ void load_vec(const uint16_t* x, int64_t i, float (&v)[8]) { load8(x, i, v); }
 __device__ __forceinline__ void load_vec(const float* x, int64_t i, float (&v)[4]) {
@@ -51,13 +80,11 @@ __device__ __forceinline__ uint32_t deq_f16_bits(uint32_t c, float s) {
 // Quantise elements [c8, c8 + 8) of row ``row`` (both lanes of the block
 // must call this together).  Writes the 8 codes (4 bytes), the block scale
 // (from the even lane) and, with x_deq, the exact f16 values code * scale.
-template <typename T>
-__device__ __forceinline__ void quantize_half_block(const T* __restrict__ x, int64_t row, int64_t c8,
-                                                    int64_t K, int64_t ldx, float gv,
-                                                    uint8_t* __restrict__ q, uint8_t* __restrict__ sf,
-                                                    uint16_t* __restrict__ x_deq) {
-  float v[8];
-  load8(x, row * ldx + c8, v);
+// quantize_half_block on 8 values already loaded.
+__device__ __forceinline__ void quantize_half_block_values(const float (&v)[8], int64_t row, int64_t c8,
+                                                           int64_t K, float gv, uint8_t* __restrict__ q,
+                                                           uint8_t* __restrict__ sf,
+                                                           uint16_t* __restrict__ x_deq) {
   float m = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
@@ -77,6 +104,16 @@ __device__ __forceinline__ void quantize_half_block(const T* __restrict__ x, int
       d[j] = deq_f16_bits((word >> (8 * j)) & 15u, s) | (deq_f16_bits((word >> (8 * j + 4)) & 15u, s) << 16);
     *reinterpret_cast<u32x4*>(x_deq + row * K + c8) = d;
   }
+}
+
+template <typename T>
+__device__ __forceinline__ void quantize_half_block(const T* __restrict__ x, int64_t row, int64_t c8,
+                                                    int64_t K, int64_t ldx, float gv,
+                                                    uint8_t* __restrict__ q, uint8_t* __restrict__ sf,
+                                                    uint16_t* __restrict__ x_deq) {
+  float v[8];
+  load8(x, row * ldx + c8, v);
+  quantize_half_block_values(v, row, c8, K, gv, q, sf, x_deq);
 }
 
 }  // namespace nvfp4

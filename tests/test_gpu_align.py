@@ -113,7 +113,7 @@ def test_align_plan_size_matches(dev):
     assert lib.moe_align_plan_size(ctypes.byref(d)) // 4 == ops.alloc_alignment(d, dev).plan.numel()
 
 
-@pytest.mark.parametrize("name", ["decode", "large_e", "prefill", "tiny"])
+@pytest.mark.parametrize("name", ["decode", "large_e", "prefill", "skew", "tiny"])
 def test_scale_and_align(dev, name):
     """One call = global scale + alignment (one launch when P <= 4096, the two
     launches otherwise): both results bit-exact, the scale workspace left zero."""
@@ -131,11 +131,13 @@ def test_scale_and_align(dev, name):
 _LIMIT = moe_inputs.Workload("limit", 128, 2048, 256, 64, 6, 1, 1.1, 0.02, 0.01, 41)  # T*H = 2^18
 
 
-@pytest.mark.parametrize("name", ["decode", "tiny", "limit", "large_e", "prefill"])
+@pytest.mark.parametrize("name", ["decode", "tiny", "limit", "large_e", "prefill", "skew"])
 def test_quantize_and_align(dev, name):
     """One call = global scale + quantisation (+ exact f16 copy) + alignment,
     bit-exact against the oracle: one launch up to T*H = 2^18 and P = 4096
-    (decode, tiny, limit), the separate launches beyond (large_e, prefill)."""
+    (decode, tiny, limit); the scale+align launch then quantisation beyond
+    (large_e); for P > 4096 the scale beside the counts, the quantisation
+    beside the scan, then the scatter (prefill: 32 chunks of pairs, skew: 64)."""
     w = _LIMIT if name == "limit" else moe_inputs.WORKLOADS[name]
     x = moe_inputs.activations(w, device=dev)
     ids, _ = oroute.route_topk(to_np(moe_inputs.router_logits(w, device=dev)), w.topk)
