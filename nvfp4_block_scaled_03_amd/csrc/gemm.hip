@@ -245,12 +245,19 @@ __device__ __forceinline__ void epilogue_rowmajor(const KParams& p, f32x4 (&acc)
 // wave-private LDS area sh ([16*MT][8*NTW] floats) and come back so that each
 // lane owns whole blocks: one scale decision per block, and the codes, scale
 // bytes and 16-bit copies leave as vector stores.
+// Row stride (floats) of the h tile in LDS: 8 NTW columns plus 4 floats of
+// padding, so that the four 4-row groups of a store and the 64-byte-apart
+// block reads fall in different banks.
+template <int NTW>
+constexpr int kBlocksStride = 8 * NTW + 4;
+
 template <int EPI, int MT, int NTW>
 __device__ __forceinline__ void epilogue_blocks(const KParams& p, f32x4 (&acc)[MT][NTW], int e,
                                                 int row0, int nrows, int n_wave0, int lane,
                                                 float* __restrict__ sh) {
   static_assert(swiglu_epi(EPI), "SwiGLU epilogues only");
   constexpr int HC = 8 * NTW;                // h columns of the wave
+  constexpr int SH = kBlocksStride<NTW>;     // LDS row stride (floats)
   constexpr int BLOCKS = 16 * MT * (HC / 16);
   static_assert(BLOCKS % kWave == 0, "whole blocks per lane");
   const float alpha = p.g_a ? ld_uniform(p.g_a) * ld_uniform(p.g_w + e) : ld_uniform(p.g_w + e);
@@ -263,7 +270,7 @@ __device__ __forceinline__ void epilogue_blocks(const KParams& p, f32x4 (&acc)[M
       for (int r = 0; r < 4; ++r) {
         const float gate = alpha * acc[i][2 * q][r];
         const float up = alpha * acc[i][2 * q + 1][r];
-        sh[(i * 16 + lg * 4 + r) * HC + q * 16 + ln] = silu_fast(gate) * up;
+        sh[(i * 16 + lg * 4 + r) * SH + q * 16 + ln] = silu_fast(gate) * up;
       }
   // (wave-private area: the wave's own LDS writes are ordered before its reads)
   const int hb0 = n_wave0 >> 5;                // first 16-column block of h
@@ -272,7 +279,7 @@ __device__ __forceinline__ void epilogue_blocks(const KParams& p, f32x4 (&acc)[M
   for (int j = 0; j < BLOCKS / kWave; ++j) {
     const int blk = lane + kWave * j;
     const int row = blk / (HC / 16), hb = blk % (HC / 16);
-    const float* src = sh + row * HC + hb * 16;
+    const float* src = sh + row * SH + hb * 16;
     float v[16];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -852,8 +859,9 @@ void grouped_gemm_wide_kernel(KParams p) {
     static_assert(16 * (16 * NTW + 4) * 4 <= WAVE_BYTES, "one m-tile fits the wave's area");
     epilogue_rowmajor<EPI, MT, NTW>(p, acc, t.e, t.row0, t.nrows, n_wave0, lane, sh);
   } else {
-    // SwiGLU: passes of PM m-tiles (all 8 with 4 wavefronts, 4 with 8).
-    constexpr int PM = WAVE_BYTES / (16 * 8 * NTW * 4);
+    // SwiGLU: passes of PM m-tiles (4 with 4 wavefronts, 2 with 8).
+    constexpr int PMF = WAVE_BYTES / (16 * kBlocksStride<NTW> * 4);
+    constexpr int PM = PMF >= 8 ? 8 : PMF >= 4 ? 4 : PMF >= 2 ? 2 : 1;
     static_assert(PM >= 1 && MT % PM == 0, "whole m-tiles per pass");
 #pragma unroll
     for (int pm = 0; pm < MT; pm += PM)

@@ -6,6 +6,11 @@
     python -m nvfp4_block_scaled_03_amd.profiling copy [--mib 1024] [--reps 3]
         A plain device-to-device copy of a known size (counter calibration:
         FETCH_SIZE / WRITE_SIZE per dispatch against the bytes really moved).
+    python -m nvfp4_block_scaled_03_amd.profiling counters --csv A.csv [B.csv ...]
+        --kernel-re RE --title T --command C > profiles/<kernel>_<workload>_counters.txt
+        Mean value per dispatch of every counter collected for the kernels
+        matching RE, and the matrix-unit and VALU busy fractions derived
+        from them (rocprofv3's MfmaUtil and VALUBusy formulas).
     python -m nvfp4_block_scaled_03_amd.profiling traffic --fetch F.csv --write W.csv
         --copy-fetch CF.csv --copy-write CW.csv --mib 1024 --kernel NAME --workload decode
         [--req R.csv] --command "..." > profiles/<kernel>_<workload>_traffic.txt
@@ -150,6 +155,43 @@ def _cmd_stats(a):
         print(f"  {calls:6d} {avg / 1e3:9.2f} {mn / 1e3:9.2f} {mx / 1e3:9.2f} {100 * tot / total:5.1f}%  {short}")
 
 
+def _cmd_counters(a):
+    vals = defaultdict(lambda: defaultdict(float))
+    names = set()
+    for path in a.csv:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if not re.search(a.kernel_re, r["Kernel_Name"]):
+                    continue
+                vals[r["Counter_Name"]][(path, r["Dispatch_Id"])] += float(r["Counter_Value"])
+                names.add(re.sub(r"\(.*$", "", r["Kernel_Name"]))
+    if not vals:
+        raise SystemExit(f"no counter rows for /{a.kernel_re}/")
+    mean = {c: sum(d.values()) / len(d) for c, d in vals.items()}
+    print(f"# rocprofv3 counters per dispatch ({a.title})")
+    print(f"# command: {a.command}")
+    print(f"# kernels matched: {', '.join(sorted(names))[:160]}")
+    for c in sorted(mean):
+        print(f"{c} = {mean[c]:.6g}   # {len(vals[c])} dispatches")
+    gui = mean.get("GRBM_GUI_ACTIVE")
+    if gui:
+        # rocprofv3's derived metrics (its counter list): MfmaUtil =
+        # sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max(GRBM_GUI_ACTIVE) * SIMD_NUM),
+        # VALUBusy = sum(SQ_ACTIVE_INST_VALU) / CU_NUM / max(GRBM_GUI_ACTIVE).
+        # The CSV holds each counter summed over its dimensions, so the
+        # per-XCC maximum of GRBM_GUI_ACTIVE is taken as the sum over the 8
+        # XCCs / 8.  MI355X: 256 CUs, 1024 SIMDs.
+        cycles = gui / 8.0
+        print(f"gui_cycles_per_xcc = {cycles:.6g}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+            print(f"mfma_util = {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (cycles * 1024):.4f}")
+        if "SQ_ACTIVE_INST_VALU" in mean:
+            print(f"valu_busy = {mean['SQ_ACTIVE_INST_VALU'] / 256 / cycles:.4f}")
+        if "SQ_LDS_BANK_CONFLICT" in mean:
+            print(f"lds_bank_conflict_cycles_per_cu_over_gui = "
+                  f"{mean['SQ_LDS_BANK_CONFLICT'] / 256 / cycles:.4f}")
+
+
 def main(argv=None):
     p = argparse.ArgumentParser()
     sub = p.add_subparsers(dest="cmd", required=True)
@@ -169,13 +211,19 @@ def main(argv=None):
     t.add_argument("--workload", default="decode")
     t.add_argument("--command", default="")
     t.add_argument("--req", default="", help="counter CSV of TCC_EA0_RDREQ_{32B,64B,128B}_sum")
+    co = sub.add_parser("counters")
+    co.add_argument("--csv", nargs="+", required=True)
+    co.add_argument("--kernel-re", dest="kernel_re", required=True)
+    co.add_argument("--title", default="")
+    co.add_argument("--command", default="")
     st = sub.add_parser("stats")
     st.add_argument("--csv", required=True)
     st.add_argument("--title", default="")
     st.add_argument("--command", default="")
     st.add_argument("--top", type=int, default=16)
     a = p.parse_args(argv)
-    {"gemm1": _cmd_gemm1, "copy": _cmd_copy, "traffic": _cmd_traffic, "stats": _cmd_stats}[a.cmd](a)
+    {"gemm1": _cmd_gemm1, "copy": _cmd_copy, "traffic": _cmd_traffic, "stats": _cmd_stats,
+     "counters": _cmd_counters}[a.cmd](a)
 
 
 if __name__ == "__main__":

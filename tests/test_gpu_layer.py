@@ -253,3 +253,44 @@ def test_layer_is_deterministic(dev):
     _, a, _ = _run_layer(case, dev, "w4a4")
     _, b, _ = _run_layer(case, dev, "w4a4")
     assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- ragged tiles
+# Rows per expert chosen so that the last 128-row tile of the experts falls in
+# every class of active 16-row groups of the wide kernel (1, 2, 4 and 8 groups,
+# each at both ends of its range), plus an empty expert; top-1 routing in a
+# seeded order, so the tokens of an expert are scattered over the batch.
+RAGGED_COUNTS = [1, 16, 17, 32, 33, 64, 65, 128, 129, 0, 200, 255, 256, 257, 300]
+
+
+class RoutedCase(Case):
+    """Case with routing given by expert row counts instead of router logits."""
+
+    def __init__(self, counts, dev, H=256, I=128, seed=71):
+        E = len(counts)
+        w = Workload("ragged", int(sum(counts)), H, I, E, 1, 0, 0.0, 0.02, 0.01, seed)
+        ids = np.repeat(np.arange(E, dtype=np.int32), counts)
+        ids = ids[np.random.default_rng(seed).permutation(ids.size)].reshape(-1, 1)
+        self.w = w
+        self.d = ops.dims(w.T, w.topk, w.E, w.H, w.I, w.shared)
+        self.x = moe_inputs.activations(w, device=dev)
+        self.ids_np, self.tw_np = ids, np.ones((w.T, 1), dtype=np.float32)
+        self.ids = torch.from_numpy(self.ids_np).to(dev)
+        self.tw = torch.from_numpy(self.tw_np).to(dev)
+        self.w13 = moe_inputs.expert_weights(w, 13, device=dev)
+        self.w2 = moe_inputs.expert_weights(w, 2, device=dev)
+        self.ew = omoe.ExpertWeights(lambda e: to_np(self.w13[e]), lambda e: to_np(self.w2[e]))
+        self.xf = to_np(self.x).astype(np.float64)
+        self.tokens = None
+        self.g2 = omoe.calibrate_g2(self.xf, ids, self.ew, w.E, w.I, w.shared)
+        self.wq = ops.quantize_expert_weights(self.d, self.w13, self.w2, keep_canonical=False)
+
+
+@pytest.mark.parametrize("variant", ["w4a4", "w4a16"])
+def test_layer_ragged_tile_heights(dev, variant):
+    """Every token of a layer whose experts end in tiles of every height class
+    of the 128-row kernel (mean rows per expert > 96 selects it; W4A4 with
+    the exact f16 activation copies it reads)."""
+    case = RoutedCase(RAGGED_COUNTS, dev)
+    assert case.w.pairs / case.w.E > 96
+    _judge_layer(case, dev, variant, decoded_copies=True if variant == "w4a4" else None)
