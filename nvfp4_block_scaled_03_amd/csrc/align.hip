@@ -7,6 +7,8 @@
 // also writes the tile lists the grouped GEMMs read, so per-expert problem
 // sizes never leave the device (vLLM PR #29242, debug trace: the host problem
 // shape is not available to the grouped GEMM).
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 #include "quant.h"
@@ -129,24 +131,25 @@ __device__ void block_exclusive_scan_1024_v(const int (&v)[V], int (&out)[V], in
 // ---------------------------------------------------------------- scan + plan
 // Writes the four tile lists from the per-expert row counts: thread e (one
 // per expert slot) writes its own tiles of every list.
-__device__ __forceinline__ void write_plan(int32_t* __restrict__ plan, const int (&lo)[4], int e,
+__device__ __forceinline__ void write_plan(int32_t* __restrict__ plan, const PlanOffs& lo, int e,
                                            int slots, int off_e, int n_e) {
-  int tiles[4], tstart[4], ntiles[4];
+  int tiles[kPlanLists], tstart[kPlanLists], ntiles[kPlanLists];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) tiles[b] = e < slots ? (n_e + kPlanBMs[b] - 1) / kPlanBMs[b] : 0;
-  block_exclusive_scan_1024_v<4>(tiles, tstart, ntiles);
+  for (int b = 0; b < kPlanLists; ++b)
+    tiles[b] = (e < slots && plan_list_has(b, n_e)) ? (n_e + kPlanBMs[b] - 1) / kPlanBMs[b] : 0;
+  block_exclusive_scan_1024_v<kPlanLists>(tiles, tstart, ntiles);
   if (e == 0) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b = 0; b < kPlanLists; ++b) {
       plan[b] = ntiles[b];
-      plan[4 + b] = lo[b];
+      plan[kPlanLists + b] = lo.v[b];
     }
   }
   if (e < slots) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < kPlanLists; ++b)
       for (int mt = 0; mt < tiles[b]; ++mt)
-        write_tile(plan + lo[b] + 2 * (tstart[b] + mt), e, mt, kPlanBMs[b], off_e, n_e);
+        write_tile(plan + lo.v[b] + 2 * (tstart[b] + mt), e, mt, kPlanBMs[b], off_e, n_e);
   }
 }
 
@@ -157,7 +160,7 @@ __device__ __forceinline__ void write_plan(int32_t* __restrict__ plan, const int
 constexpr int kScanGroup = 16;
 __device__ __forceinline__ void scan_body(const AlignP& a, int32_t* __restrict__ counts,
                                           int32_t* __restrict__ offsets, int32_t* __restrict__ plan,
-                                          int4 list_off) {
+                                          PlanOffs list_off) {
   const int e = threadIdx.x;
   int n_e = 0;
   if (e < a.slots) {
@@ -188,14 +191,13 @@ __device__ __forceinline__ void scan_body(const AlignP& a, int32_t* __restrict__
     offsets[e] = off_e;
   }
   if (e == 0) offsets[a.slots] = total;
-  const int lo[4] = {list_off.x, list_off.y, list_off.z, list_off.w};
-  write_plan(plan, lo, e, a.slots, off_e, n_e);
+  write_plan(plan, list_off, e, a.slots, off_e, n_e);
 }
 
 __global__ __launch_bounds__(1024) void align_scan_kernel(AlignP a, int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ plan,
-                                                          int4 list_off) {
+                                                          PlanOffs list_off) {
   scan_body(a, counts, offsets, plan, list_off);
 }
 
@@ -264,20 +266,20 @@ constexpr int kSmallPer = kSmallP / 1024;
 __device__ __forceinline__ void dense_plan_body(const AlignP& a, int32_t* __restrict__ offsets,
                                                 int32_t* __restrict__ sorted_pair,
                                                 int32_t* __restrict__ inv_pos,
-                                                int32_t* __restrict__ plan, int4 list_off) {
+                                                int32_t* __restrict__ plan, PlanOffs list_off) {
   const int P = (int)a.P, tid = threadIdx.x;
   for (int f = tid; f < P; f += blockDim.x) {
     sorted_pair[f] = f;
     inv_pos[f] = f;
   }
-  const int lo[4] = {list_off.x, list_off.y, list_off.z, list_off.w};
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int n_t = (P + kPlanBMs[b] - 1) / kPlanBMs[b];
-    for (int mt = tid; mt < n_t; mt += blockDim.x) write_tile(plan + lo[b] + 2 * mt, 0, mt, kPlanBMs[b], 0, P);
+  for (int b = 0; b < kPlanLists; ++b) {
+    const int n_t = plan_list_has(b, P) ? (P + kPlanBMs[b] - 1) / kPlanBMs[b] : 0;
+    for (int mt = tid; mt < n_t; mt += blockDim.x)
+      write_tile(plan + list_off.v[b] + 2 * mt, 0, mt, kPlanBMs[b], 0, P);
     if (tid == 0) {
       plan[b] = n_t;
-      plan[4 + b] = lo[b];
+      plan[kPlanLists + b] = list_off.v[b];
     }
   }
   if (tid == 0) {
@@ -289,7 +291,7 @@ __device__ __forceinline__ void dense_plan_body(const AlignP& a, int32_t* __rest
 __device__ __forceinline__ void align_small_body(const AlignP& a, int32_t* __restrict__ offsets,
                                                  int32_t* __restrict__ sorted_pair,
                                                  int32_t* __restrict__ inv_pos,
-                                                 int32_t* __restrict__ plan, int4 list_off) {
+                                                 int32_t* __restrict__ plan, PlanOffs list_off) {
   if (a.ids == nullptr && a.slots == 1) {
     dense_plan_body(a, offsets, sorted_pair, inv_pos, plan, list_off);
     return;
@@ -342,14 +344,13 @@ __device__ __forceinline__ void align_small_body(const AlignP& a, int32_t* __res
     sorted_pair[s0 + rank] = f;
     inv_pos[f] = s0 + rank;
   }
-  const int lo[4] = {list_off.x, list_off.y, list_off.z, list_off.w};
-  write_plan(plan, lo, e, a.slots, off_e, n_e);
+  write_plan(plan, list_off, e, a.slots, off_e, n_e);
 }
 
 __global__ __launch_bounds__(1024) void align_small_kernel(AlignP a, int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ sorted_pair,
                                                            int32_t* __restrict__ inv_pos,
-                                                           int32_t* __restrict__ plan, int4 list_off) {
+                                                           int32_t* __restrict__ plan, PlanOffs list_off) {
   align_small_body(a, offsets, sorted_pair, inv_pos, plan, list_off);
 }
 
@@ -365,7 +366,7 @@ __global__ __launch_bounds__(1024) void scale_align_kernel(const uint16_t* __res
                                                            AlignP a, int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ sorted_pair,
                                                            int32_t* __restrict__ inv_pos,
-                                                           int32_t* __restrict__ plan, int4 list_off) {
+                                                           int32_t* __restrict__ plan, PlanOffs list_off) {
   if ((int)blockIdx.x == nblk) {
     align_small_body(a, offsets, sorted_pair, inv_pos, plan, list_off);
     return;
@@ -423,7 +424,7 @@ __global__ __launch_bounds__(1024) void quant_align_kernel(const uint16_t* __res
                                                            AlignP a, int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ sorted_pair,
                                                            int32_t* __restrict__ inv_pos,
-                                                           int32_t* __restrict__ plan, int4 list_off) {
+                                                           int32_t* __restrict__ plan, PlanOffs list_off) {
   if ((int)blockIdx.x == nblk) {
     align_small_body(a, offsets, sorted_pair, inv_pos, plan, list_off);
     return;
@@ -641,9 +642,12 @@ AlignShape align_shape(int T, int topk, int E, int shared) {
   a.slots = E + shared;
   a.nchunks = (int)((a.P + kAlignChunk - 1) / kAlignChunk);
   int64_t off = kPlanHeader;
-  for (int b = 0; b < 4; ++b) {
+  for (int b = 0; b < kPlanLists; ++b) {
     a.list_off[b] = off;
-    a.list_len[b] = (a.P + kPlanBMs[b] - 1) / kPlanBMs[b] + a.slots;
+    // Every expert adds at most one partial tile; list 5 holds only experts
+    // with more than kSplitRows rows, of which there are at most P / (kSplitRows + 1).
+    const int64_t experts = b == 5 ? std::min<int64_t>(a.slots, a.P / (kSplitRows + 1)) : a.slots;
+    a.list_len[b] = (a.P + kPlanBMs[b] - 1) / kPlanBMs[b] + experts;
     off += 2 * a.list_len[b];
   }
   return a;
@@ -653,7 +657,15 @@ size_t align_ws_bytes(const AlignShape& a) {
   return (size_t)a.nchunks * (size_t)a.slots * sizeof(int32_t);
 }
 
-size_t align_plan_ints(const AlignShape& a) { return (size_t)(a.list_off[3] + 2 * a.list_len[3]); }
+size_t align_plan_ints(const AlignShape& a) {
+  return (size_t)(a.list_off[kPlanLists - 1] + 2 * a.list_len[kPlanLists - 1]);
+}
+
+PlanOffs plan_offsets(const AlignShape& a) {
+  PlanOffs o;
+  for (int b = 0; b < kPlanLists; ++b) o.v[b] = (int)a.list_off[b];
+  return o;
+}
 
 hipError_t launch_align(const AlignShape& a, const int32_t* topk_ids, int32_t* offsets,
                         int32_t* sorted_pair, int32_t* inv_pos, int32_t* plan, void* ws,
@@ -668,7 +680,7 @@ hipError_t launch_align(const AlignShape& a, const int32_t* topk_ids, int32_t* o
   p.nchunks = a.nchunks;
   p.P = a.P;
   int32_t* counts = static_cast<int32_t*>(ws);
-  int4 lo0 = make_int4((int)a.list_off[0], (int)a.list_off[1], (int)a.list_off[2], (int)a.list_off[3]);
+  const PlanOffs lo0 = plan_offsets(a);
   if (a.P <= (int64_t)kSmallP) {
     align_small_kernel<<<1, 1024, 0, s>>>(p, offsets, sorted_pair, inv_pos, plan, lo0);
     return hipGetLastError();
@@ -678,7 +690,7 @@ hipError_t launch_align(const AlignShape& a, const int32_t* topk_ids, int32_t* o
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  int4 lo = make_int4((int)a.list_off[0], (int)a.list_off[1], (int)a.list_off[2], (int)a.list_off[3]);
+  const PlanOffs lo = plan_offsets(a);
   align_scan_kernel<<<1, 1024, 0, s>>>(p, counts, offsets, plan, lo);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nchunks == 0) return e;
@@ -706,7 +718,7 @@ hipError_t launch_scale_and_align(const AlignShape& a, const uint16_t* x, float*
   p.P = a.P;
   int nblk = (int)((n + 1024 * 32 - 1) / (1024 * 32));
   nblk = nblk < 1 ? 1 : (nblk > 256 ? 256 : nblk);
-  const int4 lo = make_int4((int)a.list_off[0], (int)a.list_off[1], (int)a.list_off[2], (int)a.list_off[3]);
+  const PlanOffs lo = plan_offsets(a);
   scale_align_kernel<<<nblk + 1, 1024, 0, s>>>(x, n, g, static_cast<uint32_t*>(gs_ws), nblk, p, offsets,
                                                sorted_pair, inv_pos, plan, lo);
   return hipGetLastError();
@@ -733,7 +745,7 @@ hipError_t launch_quantize_and_align(const AlignShape& a, const uint16_t* x, flo
   p.nchunks = a.nchunks;
   p.P = a.P;
   const int nblk = (int)((n / 8 + 1023) / 1024);  // 1 .. 32
-  const int4 lo = make_int4((int)a.list_off[0], (int)a.list_off[1], (int)a.list_off[2], (int)a.list_off[3]);
+  const PlanOffs lo = plan_offsets(a);
   quant_align_kernel<<<nblk + 1, 1024, 0, s>>>(x, a.T, a.H, g, q, sf, x_deq, nblk, p, offsets, sorted_pair,
                                                inv_pos, plan, lo);
   return hipGetLastError();

@@ -403,7 +403,7 @@ __device__ __forceinline__ bool decode_tile(const KParams& p, Tile& t) {
   const int v = xcd_remap(blockIdx.x, G);
   const int tile = v / p.n_blocks;
   t.nb = v - tile * p.n_blocks;
-  const int* ent = p.plan + ld_uniform(p.plan + 4 + p.list_idx) + 2 * tile;
+  const int* ent = p.plan + ld_uniform(p.plan + kPlanLists + p.list_idx) + 2 * tile;
   t.e = ld_uniform(ent) & 2047;
   const uint32_t rr = (uint32_t)ld_uniform(ent + 1);
   t.row0 = (int)(rr & 0xFFFFFFu);
@@ -929,7 +929,7 @@ __device__ __forceinline__ void stream_body(const KParams& p) {
   int W = (n_units + rounds - 1) / rounds;
   if constexpr (COOP) W = (W + kNW - 1) / kNW * kNW;   // whole workgroups per tile
   if (wave >= W) return;
-  const int* list = p.plan + ld_uniform(p.plan + 4 + p.list_idx);
+  const int* list = p.plan + ld_uniform(p.plan + kPlanLists + p.list_idx);
   const int wq = threadIdx.x >> 6;  // COOP: the 32-k step this wavefront loads
 
   // Buffer addressing: a scalar descriptor per operand (per expert for the
@@ -1238,6 +1238,13 @@ int pick_list(int64_t P, int slots) {
   return 3;
 }
 
+// Whether short experts and tall ones run on different kernels: short tiles
+// on average (the streaming regime) while one expert may still hold more
+// than 64 rows (T > 64, or a shared expert, which takes every token).
+bool split_experts(const AlignShape& al) {
+  return pick_list(al.P, al.slots) <= 1 && (al.T > 64 || (al.shared && al.T > kSplitRows));
+}
+
 template <int AK, int EPI>
 hipError_t launch_wide(KParams kp, int list_len, hipStream_t s) {
   kp.n_blocks = (kp.N + kWideNW * kWideWN - 1) / (kWideNW * kWideWN);
@@ -1312,11 +1319,22 @@ hipError_t launch_gemm(KParams kp, const AlignShape& al, hipStream_t s) {
   const bool offsets_fit = kp.a_rows * a_row_bytes < (int64_t(1) << 31) &&
                            (int64_t)kp.N * kp.K / 2 < (int64_t(1) << 31);
   if (li <= 1 && !offsets_fit) li = 2;
-  // 16-bit activations on tall tiles: the wide kernel (128-row tiles).
   if constexpr (AK != kActCodes) {
+    // 16-bit activations on tall tiles: the wide kernel (128-row tiles).
     if (li >= NVFP4_WIDE_MIN_LIST && offsets_fit) {
       kp.list_idx = 3;
       return launch_wide<AK, EPI>(kp, (int)al.list_len[3], s);
+    }
+    // Short tiles on average, but some experts may hold many rows: the
+    // streaming kernel would read their weights once per 16-row tile, so
+    // those experts (list 5) go to the wide kernel and the rest (list 4) to
+    // the streaming kernel.  Two launches writing disjoint rows.
+    if (split_experts(al) && offsets_fit) {
+      kp.list_idx = 4;
+      hipError_t e = launch_stream_pf<AK, EPI, 1, kStreamNTW>(kp, (int)al.list_len[4], s);
+      if (e != hipSuccess) return e;
+      kp.list_idx = 5;
+      return launch_wide<AK, EPI>(kp, (int)al.list_len[5], s);
     }
   }
   kp.list_idx = li;
@@ -1343,7 +1361,7 @@ KParams base_params(const GemmArgs& a) {
 
 bool prefers_decoded(int T, int topk, int E, int shared) {
   const AlignShape al = align_shape(T, topk, E, shared);
-  return min(pick_list(al.P, al.slots), 3) >= NVFP4_WIDE_MIN_LIST;
+  return min(pick_list(al.P, al.slots), 3) >= NVFP4_WIDE_MIN_LIST || split_experts(al);
 }
 
 hipError_t launch_gemm1(const GemmArgs& a, bool w4a4, hipStream_t s) {

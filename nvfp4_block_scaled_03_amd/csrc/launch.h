@@ -8,11 +8,25 @@
 
 namespace nvfp4 {
 
-// Tile heights the alignment plan lists, in this order.  Plan layout (int32):
-// counts[4], list offsets[4], then per list 2 ints per tile
-// {expert | m_tile << 11, first row | rows << 24}, expert-major.
-constexpr int kPlanBMs[4] = {16, 32, 64, 128};
-constexpr int kPlanHeader = 8;
+// Tile lists of the alignment plan, in this order: lists 0-3 cover every
+// expert with tiles of 16, 32, 64 and 128 rows; list 4 covers only the
+// experts with at most kSplitRows rows (16-row tiles) and list 5 only those
+// with more (128-row tiles), so that a batch whose experts differ widely in
+// rows can run its short experts on the streaming kernel and its tall ones
+// on the 128-row kernel.  Plan layout (int32): counts[6], list offsets[6],
+// then per list 2 ints per tile {expert | m_tile << 11, first row | rows << 24},
+// expert-major.
+constexpr int kPlanLists = 6;
+constexpr int kPlanBMs[kPlanLists] = {16, 32, 64, 128, 16, 128};
+constexpr int kSplitRows = 32;
+constexpr int kPlanHeader = 2 * kPlanLists;
+struct PlanOffs {
+  int v[kPlanLists];
+};
+// Whether list b holds the tiles of an expert with n rows.
+__host__ __device__ constexpr bool plan_list_has(int b, int n) {
+  return b < 4 ? true : (b == 4 ? n <= kSplitRows : n > kSplitRows);
+}
 constexpr int kMaxExperts = 1024;
 
 size_t global_scale_ws_bytes(int64_t batches, int64_t n);
@@ -30,8 +44,8 @@ struct AlignShape {
   int64_t P;        // pairs
   int slots;        // E + shared
   int nchunks;      // pair chunks of kAlignChunk
-  int64_t list_off[4];
-  int64_t list_len[4];
+  int64_t list_off[kPlanLists];
+  int64_t list_len[kPlanLists];
 };
 constexpr int kAlignChunk = 1024;
 AlignShape align_shape(int T, int topk, int E, int shared);

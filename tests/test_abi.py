@@ -54,7 +54,11 @@ def test_size_queries(lib):
     assert lib.nvfp4_prep_weights_size(ctypes.byref(d), 5) == 0
     assert lib.moe_align_workspace_size(ctypes.byref(d)) == 1 * 128 * 4
     plan = lib.moe_align_plan_size(ctypes.byref(d))
-    assert plan == 4 * (8 + sum(2 * ((P + bm - 1) // bm + 128) for bm in (16, 32, 64, 128)))
+    # six tile lists (heights 16, 32, 64, 128; then 16 and 128 for the experts
+    # with at most / more than 32 rows), each with room for one partial tile
+    # per expert that can appear in it
+    lens = [(P + bm - 1) // bm + 128 for bm in (16, 32, 64, 128, 16)] + [(P + 127) // 128 + min(128, P // 33)]
+    assert plan == 4 * (12 + sum(2 * n for n in lens))
     assert lib.nvfp4_global_scale_workspace_size(1, 64 * 2048) == 8
     assert lib.nvfp4_global_scale_workspace_size(4, 1 << 22) == 4 * 8
     ds = _d(T=256, topk=10, E=512, H=4096, I=1024, shared=1)

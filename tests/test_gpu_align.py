@@ -52,13 +52,18 @@ def _check_align(dev, ids_np, E, shared, al=None):
     assert np.array_equal(to_np(al.offsets), off)
     assert np.array_equal(to_np(al.sorted_pair)[:n_kept], sp)
     assert np.array_equal(to_np(al.inv_pos)[:P], inv)
-    # The tile lists cover every expert's rows in order, for each tile height.
+    # The tile lists cover every expert's rows in order, for each tile height
+    # (lists 0-3), and for the experts with at most / more than 32 rows in
+    # 16- / 128-row tiles (lists 4, 5).
     plan = to_np(al.plan).astype(np.int64) & 0xFFFFFFFF
-    for b, bm in enumerate((16, 32, 64, 128)):
-        cnt, lo = plan[b], plan[4 + b]
+    lists = [(16, None), (32, None), (64, None), (128, None), (16, True), (128, False)]
+    for b, (bm, short) in enumerate(lists):
+        cnt, lo = plan[b], plan[6 + b]
         want = []
         for e in range(E + shared):
             n_e = int(off[e + 1] - off[e])
+            if short is not None and (n_e <= 32) != short:
+                continue
             for m in range((n_e + bm - 1) // bm):
                 row0 = int(off[e]) + m * bm
                 want += [e | (m << 11), row0 | (min(bm, n_e - m * bm) << 24)]
@@ -101,9 +106,9 @@ def test_align_is_deterministic(dev):
     b = ops.moe_align(d, t)
     assert torch.equal(a.sorted_pair, b.sorted_pair) and torch.equal(a.inv_pos, b.inv_pos)
     pa, pb = to_np(a.plan), to_np(b.plan)
-    assert np.array_equal(pa[:8], pb[:8])
-    for i in range(4):          # list entries beyond each count are not written
-        lo, n = pa[4 + i], pa[i]
+    assert np.array_equal(pa[:12], pb[:12])      # 6 counts, 6 list offsets
+    for i in range(6):          # list entries beyond each count are not written
+        lo, n = pa[6 + i], pa[i]
         assert np.array_equal(pa[lo:lo + 2 * n], pb[lo:lo + 2 * n])
 
 

@@ -238,6 +238,7 @@ def test_layer_small_activation_paths(dev, w, decoded):
 
 FULL = [("decode", "w4a4", 8, None), ("decode", "w4a4", 4, True), ("decode", "w4a16", 8, None),
         ("prefill", "w4a4", 4, None), ("prefill", "w4a4", 2, False), ("large_e", "w4a4", 3, None),
+        ("large_e", "w4a16", 3, None), ("large_e", "w4a4", 2, False),
         ("skew", "w4a4", 4, None), ("skew", "w4a16", 4, None)]
 
 
@@ -293,4 +294,17 @@ def test_layer_ragged_tile_heights(dev, variant):
     the exact f16 activation copies it reads)."""
     case = RoutedCase(RAGGED_COUNTS, dev)
     assert case.w.pairs / case.w.E > 96
+    _judge_layer(case, dev, variant, decoded_copies=True if variant == "w4a4" else None)
+
+
+# Short experts on average (mean 13.7 rows: the streaming regime) but some
+# experts hold up to 200 rows: the experts with more than 32 rows run on the
+# 128-row kernel, the others on the streaming kernel.
+SPLIT_COUNTS = [200, 100, 40, 33, 32, 17, 16, 15, 8, 5, 4, 3, 2, 1, 0, 1] + [3] * 24
+
+
+@pytest.mark.parametrize("variant", ["w4a4", "w4a16"])
+def test_layer_split_short_and_tall_experts(dev, variant):
+    case = RoutedCase(SPLIT_COUNTS, dev, seed=72)
+    assert case.w.pairs / case.w.E <= 16 and case.w.T > 64
     _judge_layer(case, dev, variant, decoded_copies=True if variant == "w4a4" else None)
