@@ -129,28 +129,39 @@ __device__ void block_exclusive_scan_1024_v(const int (&v)[V], int (&out)[V], in
 }
 
 // ---------------------------------------------------------------- scan + plan
-// Writes the four tile lists from the per-expert row counts: thread e (one
+// Writes the six tile lists from the per-expert row counts: thread e (one
 // per expert slot) writes its own tiles of every list.
-__device__ __forceinline__ void write_plan(int32_t* __restrict__ plan, const PlanOffs& lo, int e,
-                                           int slots, int off_e, int n_e) {
-  int tiles[kPlanLists], tstart[kPlanLists], ntiles[kPlanLists];
+// (in two groups of three lists, which keeps the register use of the
+// 1024-thread kernels that call it below their limit)
+template <int B0>
+__device__ __forceinline__ void write_plan_group(int32_t* __restrict__ plan, const PlanOffs& lo, int e,
+                                                 int slots, int off_e, int n_e) {
+  constexpr int V = 3;
+  int tiles[V], tstart[V], ntiles[V];
 #pragma unroll
-  for (int b = 0; b < kPlanLists; ++b)
-    tiles[b] = (e < slots && plan_list_has(b, n_e)) ? (n_e + kPlanBMs[b] - 1) / kPlanBMs[b] : 0;
-  block_exclusive_scan_1024_v<kPlanLists>(tiles, tstart, ntiles);
+  for (int b = 0; b < V; ++b)
+    tiles[b] = (e < slots && plan_list_has(B0 + b, n_e)) ? (n_e + kPlanBMs[B0 + b] - 1) / kPlanBMs[B0 + b] : 0;
+  block_exclusive_scan_1024_v<V>(tiles, tstart, ntiles);
   if (e == 0) {
 #pragma unroll
-    for (int b = 0; b < kPlanLists; ++b) {
-      plan[b] = ntiles[b];
-      plan[kPlanLists + b] = lo.v[b];
+    for (int b = 0; b < V; ++b) {
+      plan[B0 + b] = ntiles[b];
+      plan[kPlanLists + B0 + b] = lo.v[B0 + b];
     }
   }
   if (e < slots) {
 #pragma unroll
-    for (int b = 0; b < kPlanLists; ++b)
+    for (int b = 0; b < V; ++b)
       for (int mt = 0; mt < tiles[b]; ++mt)
-        write_tile(plan + lo.v[b] + 2 * (tstart[b] + mt), e, mt, kPlanBMs[b], off_e, n_e);
+        write_tile(plan + lo.v[B0 + b] + 2 * (tstart[b] + mt), e, mt, kPlanBMs[B0 + b], off_e, n_e);
   }
+}
+
+__device__ __forceinline__ void write_plan(int32_t* __restrict__ plan, const PlanOffs& lo, int e,
+                                           int slots, int off_e, int n_e) {
+  static_assert(kPlanLists == 6, "two groups of three lists");
+  write_plan_group<0>(plan, lo, e, slots, off_e, n_e);
+  write_plan_group<3>(plan, lo, e, slots, off_e, n_e);
 }
 
 // Per expert: turn the per-chunk counts into the chunk's first output row
@@ -296,14 +307,15 @@ __device__ __forceinline__ void align_small_body(const AlignP& a, int32_t* __res
     dense_plan_body(a, offsets, sorted_pair, inv_pos, plan, list_off);
     return;
   }
-  __shared__ int seg[kSmallP];
   __shared__ int cnt[kMaxExperts];
-  __shared__ int start[kMaxExperts];
+  __shared__ int running[kMaxExperts];
+  __shared__ int wcnt[16][kMaxExperts];   // pairs of an expert per wavefront, current round
   const int tid = threadIdx.x;
-  if (tid < a.slots) cnt[tid] = 0;
-  __syncthreads();
   const int P = (int)a.P;
-  int my_e[kSmallPer], my_slot[kSmallPer];
+  for (int x = tid; x < a.slots; x += 1024) cnt[x] = 0;
+  for (int x = tid; x < 16 * kMaxExperts; x += 1024) (&wcnt[0][0])[x] = 0;
+  __syncthreads();
+  int my_e[kSmallPer];
 #pragma unroll
   for (int r = 0; r < kSmallPer; ++r) {
     const int f = tid + 1024 * r;
@@ -313,7 +325,7 @@ __device__ __forceinline__ void align_small_body(const AlignP& a, int32_t* __res
       const int e = expert_of(a, f, valid);
       if (valid) {
         my_e[r] = e;
-        my_slot[r] = atomicAdd(&cnt[e], 1);
+        atomicAdd(&cnt[e], 1);
       } else {
         inv_pos[f] = -1;
       }
@@ -326,23 +338,46 @@ __device__ __forceinline__ void align_small_body(const AlignP& a, int32_t* __res
   const int off_e = block_exclusive_scan_1024(n_e, &total);
   if (e < a.slots) {
     offsets[e] = off_e;
-    start[e] = off_e;
+    running[e] = off_e;
   }
   if (e == 0) offsets[a.slots] = total;
   __syncthreads();
-#pragma unroll
-  for (int r = 0; r < kSmallPer; ++r)
-    if (my_e[r] >= 0) seg[start[my_e[r]] + my_slot[r]] = tid + 1024 * r;
-  __syncthreads();
+  // Stable order without comparisons: in round r the 1024 pairs
+  // f = 1024 r + tid are in increasing order, so a pair's row is its
+  // expert's rows of the earlier rounds (running), plus those of the earlier
+  // wavefronts of this round (wcnt), plus the lower lanes of its own
+  // wavefront with the same expert (an 11-bit ballot match).
+  const int w = tid >> 6, lane = tid & 63;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int r = 0; r < kSmallPer; ++r) {
-    if (my_e[r] < 0) continue;
-    const int f = tid + 1024 * r;
-    const int s0 = start[my_e[r]], n = cnt[my_e[r]];
-    int rank = 0;
-    for (int i = 0; i < n; ++i) rank += seg[s0 + i] < f;
-    sorted_pair[s0 + rank] = f;
-    inv_pos[f] = s0 + rank;
+    const int ex = my_e[r];
+    const bool valid = ex >= 0;
+    const int key = valid ? ex : 2047;
+    uint64_t same = ~0ull;
+#pragma unroll
+    for (int bit = 0; bit < 11; ++bit) {
+      const bool bb = (key >> bit) & 1;
+      const uint64_t bal = __ballot(bb);
+      same &= bb ? bal : ~bal;
+    }
+    const int rank = __popcll(same & lt);
+    const int cw = __popcll(same);
+    if (valid && rank == 0) wcnt[w][ex] = cw;
+    __syncthreads();
+    if (valid) {
+      int pos = running[ex] + rank;
+      for (int v = 0; v < w; ++v) pos += wcnt[v][ex];
+      const int f = tid + 1024 * r;
+      sorted_pair[pos] = f;
+      inv_pos[f] = pos;
+    }
+    __syncthreads();
+    if (valid && rank == 0) {
+      atomicAdd(&running[ex], cw);
+      wcnt[w][ex] = 0;
+    }
+    __syncthreads();
   }
   write_plan(plan, list_off, e, a.slots, off_e, n_e);
 }
