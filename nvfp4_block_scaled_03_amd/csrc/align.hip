@@ -313,7 +313,7 @@ __device__ __forceinline__ void align_small_body(const AlignP& a, int32_t* __res
   const int tid = threadIdx.x;
   const int P = (int)a.P;
   for (int x = tid; x < a.slots; x += 1024) cnt[x] = 0;
-  for (int x = tid; x < 16 * kMaxExperts; x += 1024) (&wcnt[0][0])[x] = 0;
+  for (int x = tid; x < 16 * a.slots; x += 1024) wcnt[x / a.slots][x % a.slots] = 0;
   __syncthreads();
   int my_e[kSmallPer];
 #pragma unroll
@@ -351,6 +351,7 @@ __device__ __forceinline__ void align_small_body(const AlignP& a, int32_t* __res
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int r = 0; r < kSmallPer; ++r) {
+    if (1024 * r >= P) break;  // (uniform: rounds past the last pair)
     const int ex = my_e[r];
     const bool valid = ex >= 0;
     const int key = valid ? ex : 2047;
