@@ -410,7 +410,22 @@ __global__ __launch_bounds__(1024) void scale_align_kernel(const uint16_t* __res
   __shared__ float red[16];
   const int64_t stride = (int64_t)nblk * 1024 * 8;
   float m = 0.0f;
-  for (int64_t i = ((int64_t)blockIdx.x * 1024 + threadIdx.x) * 8; i < n; i += stride) {
+  // U independent loads per trip (the grid gives each thread about 4).
+  constexpr int U = 4;
+  int64_t i = ((int64_t)blockIdx.x * 1024 + threadIdx.x) * 8;
+  for (; i + (U - 1) * stride < n; i += U * stride) {
+    u32x4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = *reinterpret_cast<const u32x4*>(x + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        m = fmaxf(m, fabsf(bf16_bits_to_f32(w[u][j] & 0xFFFFu)));
+        m = fmaxf(m, fabsf(bf16_bits_to_f32(w[u][j] >> 16)));
+      }
+  }
+  for (; i < n; i += stride) {
     const u32x4 w = *reinterpret_cast<const u32x4*>(x + i);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -430,17 +445,7 @@ __global__ __launch_bounds__(1024) void scale_align_kernel(const uint16_t* __res
     *g = global_scale_of_amax(r);
     return;
   }
-  // (the count waits for the fetch-max's result: see nvfp4_global_scale)
-  const uint32_t old = __hip_atomic_fetch_max(ws + 1, (uint32_t)__float_as_int(r), __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-  const uint32_t done = __hip_atomic_fetch_add(ws, 1u + (old >> 31), __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-  if (done == (uint32_t)nblk - 1) {
-    const uint32_t bits = __hip_atomic_fetch_max(ws + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *g = global_scale_of_amax(__int_as_float((int)bits));
-    __hip_atomic_store(ws + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(ws, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  fold_max_and_count(ws, ws + 1, r, (uint32_t)nblk, g);
 }
 
 // ---------------------------------------------------------------- quantise + align

@@ -655,6 +655,25 @@ void grouped_gemm_wide_kernel(KParams p) {
   const bool wave_on = n_wave0 < p.N;
   const int K = p.K, KC = K / kBK, NT = p.N / 16;
 
+  // ---- B (weights), two register sets.
+  const int nt0 = n_wave0 >> 4;
+  const int64_t wbase = ((int64_t)(t.e * NT + nt0) * KC) * kWave + lane;
+  const uint8_t* s_expert = p.w_sf + (int64_t)t.e * (NT >> 1) * KC * 256;
+  u32x4 bq0[NTW], bq1[NTW];
+  uint32_t bs0[NTW / 2], bs1[NTW / 2];
+  auto load_b = [&](int kc, u32x4 (&bq)[NTW], uint32_t (&bs)[NTW / 2]) {
+    if (!wave_on) return;
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+      bq[j] = *reinterpret_cast<const u32x4*>(p.w_q + (wbase + ((int64_t)j * KC + kc) * kWave) * 16);
+#pragma unroll
+    for (int j = 0; j < NTW / 2; ++j)
+      bs[j] = *reinterpret_cast<const uint32_t*>(s_expert + scale_word_offset((nt0 >> 1) + j, kc, KC, lane));
+  };
+  // The weights of chunk 0 do not depend on the activation rows: they are
+  // requested first, so their latency overlaps the sorted-pair gather.
+  load_b(0, bq0, bs0);
+
   // ---- A staging.  Load q of wave wv fills LDS bytes [(wv*LOADS+q) KiB, +1 KiB)
   // of a buffer: rows 4(wv*LOADS+q) + lane/16, LDS unit lane%16, which holds
   // source unit (lane%16) ^ (row%16) of the row.  Rows past the tile end
@@ -695,22 +714,6 @@ void grouped_gemm_wide_kernel(KParams p) {
   // (builtin, not assembly: the compiler must see that every load, its own
   // included, has completed, or it re-waits before reusing load registers)
   auto lds_fill_wait = [] { __builtin_amdgcn_s_waitcnt(0); };
-
-  // ---- B (weights), two register sets.
-  const int nt0 = n_wave0 >> 4;
-  const int64_t wbase = ((int64_t)(t.e * NT + nt0) * KC) * kWave + lane;
-  const uint8_t* s_expert = p.w_sf + (int64_t)t.e * (NT >> 1) * KC * 256;
-  u32x4 bq0[NTW], bq1[NTW];
-  uint32_t bs0[NTW / 2], bs1[NTW / 2];
-  auto load_b = [&](int kc, u32x4 (&bq)[NTW], uint32_t (&bs)[NTW / 2]) {
-    if (!wave_on) return;
-#pragma unroll
-    for (int j = 0; j < NTW; ++j)
-      bq[j] = *reinterpret_cast<const u32x4*>(p.w_q + (wbase + ((int64_t)j * KC + kc) * kWave) * 16);
-#pragma unroll
-    for (int j = 0; j < NTW / 2; ++j)
-      bs[j] = *reinterpret_cast<const uint32_t*>(s_expert + scale_word_offset((nt0 >> 1) + j, kc, KC, lane));
-  };
 
   f32x4 acc[MT][NTW];
 #pragma unroll
@@ -810,7 +813,6 @@ void grouped_gemm_wide_kernel(KParams p) {
   // barrier per chunk publishes the buffer.
   auto main_loop = [&](auto mta) __attribute__((always_inline)) {
     stage_a(mta, 0, As0);
-    load_b(0, bq0, bs0);
     lds_fill_wait();
     __syncthreads();
     // Every path back to the loop head passes the full wait (the exit tests
