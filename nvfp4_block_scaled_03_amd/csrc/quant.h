@@ -67,20 +67,10 @@ __device__ __forceinline__ void load_vec(const float* x, int64_t i, float (&v)[4
   for (int j = 0; j < 4; ++j) v[j] = a[j];
 }
 
-// Value of the E2M1 code c (sign in bit 3) times the block scale s, exact
-// in f16 (at most six significant bits, magnitude in [2^-10, 2688]).
-__device__ __forceinline__ uint32_t deq_f16_bits(uint32_t c, float s) {
-  const uint32_t m = c & 7u;
-  const float mag = m < 2 ? 0.5f * (float)m
-                          : __int_as_float((int)(((m >> 1) + 126u) << 23)) * (1.0f + 0.5f * (float)(m & 1u));
-  const float v = (c & 8u) ? -(mag * s) : mag * s;
-  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v);
-}
-
-// Quantise elements [c8, c8 + 8) of row ``row`` (both lanes of the block
-// must call this together).  Writes the 8 codes (4 bytes), the block scale
-// (from the even lane) and, with x_deq, the exact f16 values code * scale.
-// quantize_half_block on 8 values already loaded.
+// Quantise the 8 values v of elements [c8, c8 + 8) of row ``row`` (both
+// lanes of the block must call this together).  Writes the 8 codes (4
+// bytes), the block scale (from the even lane) and, with x_deq, the exact
+// f16 values code * scale.
 __device__ __forceinline__ void quantize_half_block_values(const float (&v)[8], int64_t row, int64_t c8,
                                                            int64_t K, float gv, uint8_t* __restrict__ q,
                                                            uint8_t* __restrict__ sf,
@@ -97,15 +87,13 @@ __device__ __forceinline__ void quantize_half_block_values(const float (&v)[8], 
   for (int j = 0; j < 8; ++j) word |= e2m1_code(v[j], bd, sc == 0) << (4 * j);
   *reinterpret_cast<uint32_t*>(q + row * (K >> 1) + (c8 >> 1)) = word;
   if ((c8 & 15) == 0) sf[row * (K >> 4) + (c8 >> 4)] = (uint8_t)sc;
-  if (x_deq) {
-    u32x4 d;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      d[j] = deq_f16_bits((word >> (8 * j)) & 15u, s) | (deq_f16_bits((word >> (8 * j + 4)) & 15u, s) << 16);
-    *reinterpret_cast<u32x4*>(x_deq + row * K + c8) = d;
-  }
+  // The exact f16 values code * scale (at most six significant bits, in
+  // [2^-10, 2688]): the hardware FP4 convert, then one packed multiply by the
+  // scale per pair.
+  if (x_deq) *reinterpret_cast<f16x8*>(x_deq + row * K + c8) = dequant8_f16(word, f16x2_splat(s));
 }
 
+// The same, loading the 8 elements from x.
 template <typename T>
 __device__ __forceinline__ void quantize_half_block(const T* __restrict__ x, int64_t row, int64_t c8,
                                                     int64_t K, int64_t ldx, float gv,
