@@ -164,6 +164,44 @@ __device__ __forceinline__ void write_plan(int32_t* __restrict__ plan, const Pla
   write_plan_group<3>(plan, lo, e, slots, off_e, n_e);
 }
 
+// The same for the one-workgroup alignment (P <= kSmallP), where one scan
+// of four values serves the expert offsets and all six lists: the
+// per-expert tile counts travel two per int (16 bits each: a list holds at
+// most P / 16 + slots <= 1280 tiles, so no half-sum carries into the other
+// half).  plan_counts_small packs the counts; write_plan_small writes the
+// header and the expert's tiles from the scan of the packed counts.
+__device__ __forceinline__ void plan_counts_small(int e, int slots, int n_e, int (&packed)[3]) {
+  int tiles[kPlanLists];
+#pragma unroll
+  for (int b = 0; b < kPlanLists; ++b)
+    tiles[b] = (e < slots && plan_list_has(b, n_e)) ? (n_e + kPlanBMs[b] - 1) / kPlanBMs[b] : 0;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) packed[i] = tiles[2 * i] | (tiles[2 * i + 1] << 16);
+}
+
+__device__ __forceinline__ void write_plan_small(int32_t* __restrict__ plan, const PlanOffs& lo, int e,
+                                                 int slots, int off_e, int n_e, const int (&pstart)[3],
+                                                 const int (&ptot)[3]) {
+  static_assert(kPlanLists == 6, "three ints of two 16-bit counts");
+  if (e == 0) {
+#pragma unroll
+    for (int b = 0; b < kPlanLists; ++b) {
+      plan[b] = (ptot[b >> 1] >> (16 * (b & 1))) & 0xFFFF;
+      plan[kPlanLists + b] = lo.v[b];
+    }
+  }
+  if (e < slots) {
+#pragma unroll
+    for (int b = 0; b < kPlanLists; ++b) {
+      if (!plan_list_has(b, n_e)) continue;
+      const int t0 = (pstart[b >> 1] >> (16 * (b & 1))) & 0xFFFF;
+      const int nt = (n_e + kPlanBMs[b] - 1) / kPlanBMs[b];
+      for (int mt = 0; mt < nt; ++mt)
+        write_tile(plan + lo.v[b] + 2 * (t0 + mt), e, mt, kPlanBMs[b], off_e, n_e);
+    }
+  }
+}
+
 // Per expert: turn the per-chunk counts into the chunk's first output row
 // (in place), then scan over experts and write offsets and tile lists.
 // Both walks over the chunks load a group of chunks together (independent
@@ -334,8 +372,13 @@ __device__ __forceinline__ void align_small_body(const AlignP& a, int32_t* __res
   __syncthreads();
   const int e = tid;
   const int n_e = e < a.slots ? cnt[e] : 0;
-  int total;
-  const int off_e = block_exclusive_scan_1024(n_e, &total);
+  int pk[3];
+  plan_counts_small(e, a.slots, n_e, pk);
+  const int sv[4] = {n_e, pk[0], pk[1], pk[2]};
+  int sx[4], st[4];
+  block_exclusive_scan_1024_v<4>(sv, sx, st);
+  const int off_e = sx[0], total = st[0];
+  write_plan_small(plan, list_off, e, a.slots, off_e, n_e, {sx[1], sx[2], sx[3]}, {st[1], st[2], st[3]});
   if (e < a.slots) {
     offsets[e] = off_e;
     running[e] = off_e;
@@ -380,7 +423,6 @@ __device__ __forceinline__ void align_small_body(const AlignP& a, int32_t* __res
     }
     __syncthreads();
   }
-  write_plan(plan, list_off, e, a.slots, off_e, n_e);
 }
 
 __global__ __launch_bounds__(1024) void align_small_kernel(AlignP a, int32_t* __restrict__ offsets,
