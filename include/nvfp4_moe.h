@@ -333,8 +333,12 @@ int grouped_gemm1_swiglu(const nvfp4_moe_dims* dims, const uint8_t* a1_q, const 
 
 /* 1 when, for these dimensions, the W4A4 GEMMs are faster given the exact
  * f16 activation copies (a1_deq from nvfp4_quantize, a2_deq from GEMM1) than
- * given the codes alone, else 0 (also 0 for invalid dims).  A performance
- * hint only: both inputs give the same results. */
+ * given the codes alone, else 0 (also 0 for invalid dims): tall tiles on
+ * average, or short ones on average while some expert may still exceed 64
+ * rows (T > 64 or a shared expert) -- then, given the copies, the GEMMs run
+ * the experts with more than 32 rows on the 128-row kernel and the rest on
+ * the streaming kernel.  A performance hint only: both inputs give the same
+ * results. */
 int grouped_gemm_prefers_decoded(const nvfp4_moe_dims* dims);
 
 /* Workspace of the GEMM2 calls: the per-row FP32 down-projection outputs
