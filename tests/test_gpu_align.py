@@ -87,6 +87,28 @@ def test_align_shapes(dev, T, k, E, shared):
     _check_align(dev, ids, E, shared)
 
 
+@pytest.mark.parametrize("case", ["one_expert", "two_hot", "full_slots"])
+def test_align_skewed_one_workgroup(dev, case):
+    """The one-workgroup alignment (P <= 4096) at its limits: every pair to
+    one expert (4096 rows in one segment), two experts sharing all pairs in
+    alternation, and 1023 experts + a shared one (1024 slots, P = 4095),
+    each against the oracle's stable grouping and the six tile lists."""
+    rng = np.random.default_rng(5)
+    if case == "one_expert":
+        ids = np.zeros((4096, 1), dtype=np.int32)
+        E, shared = 3, 0
+    elif case == "two_hot":
+        ids = np.stack([np.arange(2048) % 2, 1 - np.arange(2048) % 2], axis=1).astype(np.int32)
+        E, shared = 64, 0
+    else:
+        ids = rng.integers(0, 1023, (455, 8)).astype(np.int32)
+        ids[:, 0] = 7          # one hot expert next to many cold ones
+        E, shared = 1023, 1
+    T, k = ids.shape
+    assert T * k + shared * T <= 4096
+    _check_align(dev, ids, E, shared)
+
+
 def test_align_drops_invalid_ids(dev):
     rng = np.random.default_rng(3)
     ids = rng.integers(0, 12, (700, 4)).astype(np.int32)
