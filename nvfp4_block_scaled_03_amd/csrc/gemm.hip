@@ -1231,6 +1231,115 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Dense linear layer for at most 16 rows (the decode shape of a dense
+// layer): one workgroup per 2 column tiles (32 columns), its 4 wavefronts
+// splitting K into quarters, each loading UB chunks (weights, activation
+// codes or bf16 values, scales) before decoding and multiplying them;
+// the partial sums meet in LDS in a fixed order.  Four times the wavefronts
+// of a persistent pass over (tile, 32-column) units, which at N = 34816
+// leaves most of the device idle for a single 16-row tile.
+// ---------------------------------------------------------------------------
+template <int AK, bool F32, int UB>
+__global__ __launch_bounds__(4 * kWave) void linear_splitk_kernel(KParams p) {
+  constexpr int NTW = 2;
+  static_assert(AK != kActF16, "codes or bf16 activations");
+  __shared__ f32x4 red[3][NTW][kWave];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  const int M = p.T, N = p.N, K = p.K, KC = K / kBK, NT = N / 16;
+  const int c_lo = KC * wv / 4, c_hi = KC * (wv + 1) / 4;
+  const int nt0 = blockIdx.x * NTW;
+  const int row = min(m, M - 1);   // rows past M repeat the last one (never stored)
+  f32x4 acc[NTW];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c0 = c_lo; c0 < c_hi; c0 += UB) {
+    u32x4 bq[UB][NTW];
+    uint32_t bs[UB];
+    u32x4 aq[UB][AK == kActCodes ? 1 : 4];
+    uint32_t as[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int kc = min(c0 + u, c_hi - 1);   // a repeated chunk is loaded but not used
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+        bq[u][j] = *reinterpret_cast<const u32x4*>(p.w_q + ((int64_t)((nt0 + j) * KC + kc) * kWave + lane) * 16);
+      bs[u] = *reinterpret_cast<const uint32_t*>(p.w_sf + scale_word_offset(nt0 >> 1, kc, KC, lane));
+      if constexpr (AK == kActCodes) {
+        aq[u][0] = *reinterpret_cast<const u32x4*>(p.a_q + (int64_t)row * (K / 2) + kc * 64 + g * 16);
+        as[u] = *reinterpret_cast<const uint16_t*>(p.a_sf + (int64_t)row * (K / 16) + kc * 8 + g * 2);
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          aq[u][w] = *reinterpret_cast<const u32x4*>(p.a_h + (int64_t)row * K + kc * kBK + g * 32 + w * 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      if (c0 + u >= c_hi) continue;
+      if constexpr (AK == kActCodes) {
+        const f16x2 sa2 = e4m3x2_to_f16x2(as[u]);
+        f16x2 sb2[NTW];
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) sb2[j] = e4m3x2_to_f16x2(bs[u] >> (j * 16));
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const f16x8 af = dequant8_f16(aq[u][0][ks], ks < 2 ? f16x2_lo(sa2) : f16x2_hi(sa2));
+#pragma unroll
+          for (int j = 0; j < NTW; ++j)
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, weight_f16(bq[u][j][ks], sb2[j], ks), acc[j], 0, 0, 0);
+        }
+      } else {
+        float sb[NTW][2];
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+          const f16x2 h = e4m3x2_to_f16x2(bs[u] >> (j * 16));
+          sb[j][0] = (float)h[0];
+          sb[j][1] = (float)h[1];
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 af = __builtin_bit_cast(bf16x8, aq[u][ks]);
+#pragma unroll
+          for (int j = 0; j < NTW; ++j)
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, dequant8_bf16(bq[u][j][ks], sb[j][ks >> 1]),
+                                                             acc[j], 0, 0, 0);
+        }
+      }
+    }
+  }
+  if (wv > 0) {
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) red[wv - 1][j][lane] = acc[j];
+  }
+  __syncthreads();
+  if (wv > 0) return;
+  const float alpha = p.g_a ? ld_uniform(p.g_a) * ld_uniform(p.g_w) : ld_uniform(p.g_w);
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) {
+    f32x4 v = acc[j];
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+      const f32x4 o = red[w][j][lane];
+      v[0] += o[0];
+      v[1] += o[1];
+      v[2] += o[2];
+      v[3] += o[3];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int rr = g * 4 + r;
+      if (rr < M) {
+        const int64_t o = (int64_t)rr * N + (nt0 + j) * 16 + m;
+        if constexpr (F32) p.out_f32[o] = alpha * v[r];
+        else p.out_h[o] = (uint16_t)f32_to_bf16_bits(alpha * v[r]);
+      }
+    }
+  }
+  (void)NT;
+}
+
 // Tile height from the mean rows per expert (host side, from dims only).
 int pick_list(int64_t P, int slots) {
   const int64_t avg = P / (slots > 0 ? slots : 1);
@@ -1412,6 +1521,23 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
   const bool f32 = a.out_dtype != 0;
   if (f32) k.out_f32 = static_cast<float*>(a.out);
   else k.out_h = static_cast<uint16_t*>(a.out);
+  // Few rows from codes (at most 16) or bf16 (at most 4): K split over the
+  // 4 wavefronts of a workgroup per 32 columns (N is a multiple of 128).
+  // Measured at N = 34816, K = 5120: M = 1 W4A4 33.0 -> 30.3 us, W4A16
+  // 35.7 -> 31.8 us, M = 16 W4A4 41.0 -> 39.7 us; W4A16 at M = 16 is faster
+  // on the streaming kernel (35.7 against 47.1 us: its bf16 rows are 4x the
+  // bytes of codes).
+  if (a.M >= 1 && ((a.w4a4 && !a.a_h && a.M <= 16) || (!a.w4a4 && a.M <= 4))) {
+    const dim3 grid((unsigned)(a.N / 32));
+    if (a.w4a4) {
+      if (f32) linear_splitk_kernel<kActCodes, true, 4><<<grid, 4 * kWave, 0, s>>>(k);
+      else linear_splitk_kernel<kActCodes, false, 4><<<grid, 4 * kWave, 0, s>>>(k);
+    } else {
+      if (f32) linear_splitk_kernel<kActBf16, true, 4><<<grid, 4 * kWave, 0, s>>>(k);
+      else linear_splitk_kernel<kActBf16, false, 4><<<grid, 4 * kWave, 0, s>>>(k);
+    }
+    return hipGetLastError();
+  }
   if (!a.w4a4)
     return f32 ? launch_gemm<kActBf16, kEpiStoreF32>(k, al, s) : launch_gemm<kActBf16, kEpiStoreBf16>(k, al, s);
   if (a.a_h)

@@ -52,7 +52,7 @@ def _check(dev, x, lw, variant, ref, bound):
 
 
 @pytest.mark.parametrize("variant", ["w4a4", "w4a16"])
-@pytest.mark.parametrize("M", [1, 16, 64, 256, 300, 1024, 4096])
+@pytest.mark.parametrize("M", [1, 5, 13, 16, 17, 64, 256, 300, 1024, 4096])
 def test_linear_full(dev, M, variant):
     N, K = 1024, 768
     w = _weight(dev, N, K, 11)
