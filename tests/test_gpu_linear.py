@@ -98,3 +98,25 @@ def test_linear_pages_shape_sampled(dev, M, variant):
     y32 = to_np(ops.linear(x, lw, variant, out_dtype=torch.float32))[np.ix_(rows, cols)]
     err = np.abs(y32.astype(np.float64) - ref)
     assert (err <= _bound(x_hat, w_hat, K)).all()
+
+
+@pytest.mark.parametrize("variant", ["w4a4", "w4a16"])
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 256), (7, 384), (2, 640)])
+def test_linear_few_rows_short_k(dev, M, K, variant):
+    """Few rows with 1 to 5 chunks of K, so that some wavefronts of the
+    split-K kernel get no chunk at all and the others uneven shares."""
+    N = 256
+    w = _weight(dev, N, K, 13)
+    lw = ops.quantize_linear_weight(w)
+    x = _x(dev, M, K, 200 + K)
+    xf = to_np(x).astype(np.float64)
+    wc, ws, gw = olin.quantize_weight(to_np(w))
+    w_hat = onv.dequantize(wc, ws, gw)
+    if variant == "w4a4":
+        ref = olin.linear_w4a4(xf, wc, ws, gw)
+        g = onv.global_scale(xf)
+        x_hat = onv.dequantize(*onv.quantize(xf, g), g)
+    else:
+        ref = olin.linear_w4a16(xf, wc, ws, gw)
+        x_hat = xf
+    _check(dev, x, lw, variant, ref, _bound(x_hat, w_hat, K))
