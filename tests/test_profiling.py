@@ -40,3 +40,23 @@ def test_traffic_summary_from_counter_rows(tmp_path, capsys):
     assert float(t["fetch_bytes_per_launch"]) == 128 * 1024 * 2
     assert float(t["write_bytes_per_launch"]) == 4 * 1024
     assert t["sources_sha256_16"] == profiling.sources_hash()
+
+
+def test_counters_summary_derived_fractions(tmp_path, capsys):
+    """rocprofv3's MfmaUtil / VALUBusy formulas on synthetic rows: the per-XCC
+    GUI cycles are the 8-XCC sum / 8, MFMA busy is per SIMD (1024), VALU
+    active per CU (256)."""
+    p = tmp_path / "c.csv"
+    k = "void nvfp4::grouped_gemm_wide_kernel<1, 0>(KParams)"
+    rows = [(1, "GRBM_GUI_ACTIVE", 8 * 1000.0), (1, "SQ_VALU_MFMA_BUSY_CYCLES", 0.5 * 1000 * 1024),
+            (1, "SQ_ACTIVE_INST_VALU", 0.25 * 1000 * 256), (2, "GRBM_GUI_ACTIVE", 8 * 1000.0),
+            (2, "SQ_VALU_MFMA_BUSY_CYCLES", 0.5 * 1000 * 1024), (2, "SQ_ACTIVE_INST_VALU", 0.25 * 1000 * 256)]
+    with open(p, "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for d, c, v in rows:
+            f.write(f'{d},"{k}",{c},{v}\n')
+    profiling.main(["counters", "--csv", str(p), "--kernel-re", "wide_kernel<1, 0>"])
+    out = capsys.readouterr().out
+    vals = dict(l.split(" = ")[0:2] for l in out.splitlines() if " = " in l and not l.startswith("#"))
+    assert float(vals["mfma_util"].split()[0]) == 0.5
+    assert float(vals["valu_busy"].split()[0]) == 0.25
