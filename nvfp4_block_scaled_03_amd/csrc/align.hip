@@ -91,6 +91,34 @@ __device__ __forceinline__ void write_tile(int32_t* dst, int e, int mt, int BM, 
   dst[1] = (int32_t)((uint32_t)row0 | ((uint32_t)rows << 24));
 }
 
+// Tiles [0, nt) of expert e (rows [start, start + n), height BM) at
+// plan[pos + 2 mt].  A lane whose expert has at most kOwnTiles tiles writes
+// them itself; the tiles of a larger expert (skewed routing gives one expert
+// thousands of rows, hundreds of tiles per list) are written by all 64 lanes
+// of its wavefront, one such expert at a time, instead of by one lane in
+// series.  Every lane of the wavefront must call this (wave-wide ballot).
+// Measured on the Zipf-1.3 layer (P = 65536): the scan took 51.8 us with
+// every expert written by its own lane, 19.1 us with this at 8 tiles; a
+// threshold that uniform routing reaches (16 tiles at 256 rows per expert)
+// serialises whole wavefronts, so it stays above that.
+constexpr int kOwnTiles = 32;
+__device__ __forceinline__ void write_tiles(int32_t* __restrict__ plan, int pos, int nt, int e, int BM,
+                                            int start, int n) {
+  const bool own = nt <= kOwnTiles;
+  if (own)
+    for (int mt = 0; mt < nt; ++mt) write_tile(plan + pos + 2 * mt, e, mt, BM, start, n);
+  uint64_t heavy = __ballot(!own);
+  const int lane = threadIdx.x & 63;
+  while (heavy) {
+    const int src = __builtin_ctzll(heavy);
+    heavy &= heavy - 1;
+    const int pos_s = __builtin_amdgcn_readlane(pos, src), nt_s = __builtin_amdgcn_readlane(nt, src);
+    const int e_s = __builtin_amdgcn_readlane(e, src), start_s = __builtin_amdgcn_readlane(start, src);
+    const int n_s = __builtin_amdgcn_readlane(n, src);
+    for (int mt = lane; mt < nt_s; mt += 64) write_tile(plan + pos_s + 2 * mt, e_s, mt, BM, start_s, n_s);
+  }
+}
+
 // Exclusive scan of V values per thread over 1024 threads (one pass, two
 // barriers); tot[v] receives the sums.
 template <int V>
@@ -149,12 +177,9 @@ __device__ __forceinline__ void write_plan_group(int32_t* __restrict__ plan, con
       plan[kPlanLists + B0 + b] = lo.v[B0 + b];
     }
   }
-  if (e < slots) {
 #pragma unroll
-    for (int b = 0; b < V; ++b)
-      for (int mt = 0; mt < tiles[b]; ++mt)
-        write_tile(plan + lo.v[B0 + b] + 2 * (tstart[b] + mt), e, mt, kPlanBMs[B0 + b], off_e, n_e);
-  }
+  for (int b = 0; b < V; ++b)   // tiles[b] is 0 for e >= slots
+    write_tiles(plan, lo.v[B0 + b] + 2 * tstart[b], tiles[b], e, kPlanBMs[B0 + b], off_e, n_e);
 }
 
 __device__ __forceinline__ void write_plan(int32_t* __restrict__ plan, const PlanOffs& lo, int e,
@@ -190,29 +215,40 @@ __device__ __forceinline__ void write_plan_small(int32_t* __restrict__ plan, con
       plan[kPlanLists + b] = lo.v[b];
     }
   }
-  if (e < slots) {
 #pragma unroll
-    for (int b = 0; b < kPlanLists; ++b) {
-      if (!plan_list_has(b, n_e)) continue;
-      const int t0 = (pstart[b >> 1] >> (16 * (b & 1))) & 0xFFFF;
-      const int nt = (n_e + kPlanBMs[b] - 1) / kPlanBMs[b];
-      for (int mt = 0; mt < nt; ++mt)
-        write_tile(plan + lo.v[b] + 2 * (t0 + mt), e, mt, kPlanBMs[b], off_e, n_e);
-    }
+  for (int b = 0; b < kPlanLists; ++b) {
+    const int t0 = (pstart[b >> 1] >> (16 * (b & 1))) & 0xFFFF;
+    const int nt = (e < slots && plan_list_has(b, n_e)) ? (n_e + kPlanBMs[b] - 1) / kPlanBMs[b] : 0;
+    write_tiles(plan, lo.v[b] + 2 * t0, nt, e, kPlanBMs[b], off_e, n_e);
   }
 }
 
 // Per expert: turn the per-chunk counts into the chunk's first output row
 // (in place), then scan over experts and write offsets and tile lists.
-// Both walks over the chunks load a group of chunks together (independent
-// loads), so each costs one memory latency per group.
+// Up to kScanRegChunks chunks (P <= 65536) every count is loaded at once and
+// the per-expert prefixes stay in registers until the expert offset is
+// known: one memory latency in all.  Beyond that both walks over the chunks
+// load a group of chunks together (independent loads), so each costs one
+// memory latency per group.
 constexpr int kScanGroup = 16;
+constexpr int kScanRegChunks = 64;
 __device__ __forceinline__ void scan_body(const AlignP& a, int32_t* __restrict__ counts,
                                           int32_t* __restrict__ offsets, int32_t* __restrict__ plan,
                                           PlanOffs list_off) {
   const int e = threadIdx.x;
+  const bool in_regs = a.nchunks <= kScanRegChunks;
   int n_e = 0;
-  if (e < a.slots) {
+  int pre[kScanRegChunks];
+  if (e < a.slots && in_regs) {
+#pragma unroll
+    for (int j = 0; j < kScanRegChunks; ++j) pre[j] = j < a.nchunks ? counts[(int64_t)j * a.slots + e] : 0;
+#pragma unroll
+    for (int j = 0; j < kScanRegChunks; ++j) {
+      const int v = pre[j];
+      pre[j] = n_e;  // exclusive prefix
+      n_e += v;
+    }
+  } else if (e < a.slots) {
     for (int c0 = 0; c0 < a.nchunks; c0 += kScanGroup) {
       int v[kScanGroup];
 #pragma unroll
@@ -227,7 +263,12 @@ __device__ __forceinline__ void scan_body(const AlignP& a, int32_t* __restrict__
   }
   int total;
   const int off_e = block_exclusive_scan_1024(n_e, &total);
-  if (e < a.slots) {
+  if (e < a.slots && in_regs) {
+#pragma unroll
+    for (int j = 0; j < kScanRegChunks; ++j)
+      if (j < a.nchunks) counts[(int64_t)j * a.slots + e] = pre[j] + off_e;
+    offsets[e] = off_e;
+  } else if (e < a.slots) {
     for (int c0 = 0; c0 < a.nchunks; c0 += kScanGroup) {
       int v[kScanGroup];
 #pragma unroll

@@ -78,8 +78,12 @@ def test_align_workloads(dev, name):
     _check_align(dev, ids, w.E, w.shared)
 
 
+# Pair counts across the alignment paths: one workgroup (P <= 4096), chunk
+# scans with the per-expert prefixes in registers (up to 64 chunks of 1024
+# pairs) and chunk scans in groups (65 and 80 chunks).
 @pytest.mark.parametrize("T,k,E,shared", [(1, 1, 1, 0), (1023, 1, 4, 0), (128, 3, 3, 1),
-                                          (1025, 1, 1000, 0), (5000, 3, 17, 1), (7, 2, 1023, 1)])
+                                          (1025, 1, 1000, 0), (5000, 3, 17, 1), (7, 2, 1023, 1),
+                                          (8193, 8, 128, 0), (9000, 8, 64, 1)])
 def test_align_shapes(dev, T, k, E, shared):
     rng = np.random.default_rng(T + k + E)
     z = rng.standard_normal((T, E)).astype(np.float32)
