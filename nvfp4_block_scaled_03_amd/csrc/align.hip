@@ -97,10 +97,8 @@ __device__ __forceinline__ void write_tile(int32_t* dst, int e, int mt, int BM, 
 // thousands of rows, hundreds of tiles per list) are written by all 64 lanes
 // of its wavefront, one such expert at a time, instead of by one lane in
 // series.  Every lane of the wavefront must call this (wave-wide ballot).
-// Measured on the Zipf-1.3 layer (P = 65536): the scan took 51.8 us with
-// every expert written by its own lane, 19.1 us with this at 8 tiles; a
-// threshold that uniform routing reaches (16 tiles at 256 rows per expert)
-// serialises whole wavefronts, so it stays above that.
+// A threshold that even routing reaches would serialise whole wavefronts,
+// so it sits above the tiles of an evenly shared P <= 4096.
 constexpr int kOwnTiles = 32;
 __device__ __forceinline__ void write_tiles(int32_t* __restrict__ plan, int pos, int nt, int e, int BM,
                                             int start, int n) {
@@ -157,14 +155,23 @@ __device__ void block_exclusive_scan_1024_v(const int (&v)[V], int (&out)[V], in
 }
 
 // ---------------------------------------------------------------- scan + plan
-// Writes the six tile lists from the per-expert row counts: thread e (one
-// per expert slot) writes its own tiles of every list.
-// (in two groups of three lists, which keeps the register use of the
-// 1024-thread kernels that call it below their limit)
+// Writes the six tile lists from the per-expert row counts (thread e = expert
+// slot e), in two groups of three lists, which keeps the register use of the
+// 1024-thread kernel below its limit.  When no expert has more than
+// kOwnTiles tiles in these lists, each lane writes its own expert's tiles.
+// Otherwise the tiles of a list are shared out over all 1024 threads (tile t
+// to thread t mod 1024), each finding the expert of its tile by binary
+// search over the experts' first tiles in LDS, so the time does not depend
+// on how the rows are spread over the experts.  Measured with 65536 pairs:
+// Zipf-1.3 routing (one expert with about 8100 rows) 51.8 us with a lane per
+// expert, 17.4 us shared out; even routing (32768 pairs, 16 tiles per
+// expert at most) 10.1 us with a lane per expert, 12.1 us shared out.
 template <int B0>
 __device__ __forceinline__ void write_plan_group(int32_t* __restrict__ plan, const PlanOffs& lo, int e,
                                                  int slots, int off_e, int n_e) {
   constexpr int V = 3;
+  __shared__ int first[V][kMaxExperts];   // first tile of expert e in each list
+  __shared__ int e_start[kMaxExperts], e_rows[kMaxExperts];
   int tiles[V], tstart[V], ntiles[V];
 #pragma unroll
   for (int b = 0; b < V; ++b)
@@ -177,9 +184,38 @@ __device__ __forceinline__ void write_plan_group(int32_t* __restrict__ plan, con
       plan[kPlanLists + B0 + b] = lo.v[B0 + b];
     }
   }
+  int heavy = 0;
 #pragma unroll
-  for (int b = 0; b < V; ++b)   // tiles[b] is 0 for e >= slots
-    write_tiles(plan, lo.v[B0 + b] + 2 * tstart[b], tiles[b], e, kPlanBMs[B0 + b], off_e, n_e);
+  for (int b = 0; b < V; ++b) heavy |= tiles[b] > kOwnTiles;
+  if (!__syncthreads_or(heavy)) {   // block-uniform
+#pragma unroll
+    for (int b = 0; b < V; ++b)   // tiles[b] is 0 for e >= slots
+      for (int mt = 0; mt < tiles[b]; ++mt)
+        write_tile(plan + lo.v[B0 + b] + 2 * (tstart[b] + mt), e, mt, kPlanBMs[B0 + b], off_e, n_e);
+    return;
+  }
+  if (e < slots) {
+#pragma unroll
+    for (int b = 0; b < V; ++b) first[b][e] = tstart[b];
+    e_start[e] = off_e;
+    e_rows[e] = n_e;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < V; ++b) {
+    for (int t = threadIdx.x; t < ntiles[b]; t += 1024) {
+      // The last expert whose first tile is <= t owns tile t (an expert
+      // with no tile here shares its first index with the next expert).
+      int l = 0, h = slots - 1;
+      while (l < h) {
+        const int mid = (l + h + 1) >> 1;
+        if (first[b][mid] <= t) l = mid;
+        else h = mid - 1;
+      }
+      write_tile(plan + lo.v[B0 + b] + 2 * t, l, t - first[b][l], kPlanBMs[B0 + b], e_start[l], e_rows[l]);
+    }
+  }
+  __syncthreads();
 }
 
 __device__ __forceinline__ void write_plan(int32_t* __restrict__ plan, const PlanOffs& lo, int e,
