@@ -428,7 +428,9 @@ __device__ __forceinline__ void align_small_body(const AlignP& a, int32_t* __res
   const int tid = threadIdx.x;
   const int P = (int)a.P;
   for (int x = tid; x < a.slots; x += 1024) cnt[x] = 0;
-  for (int x = tid; x < 16 * a.slots; x += 1024) wcnt[x / a.slots][x % a.slots] = 0;
+#pragma unroll
+  for (int v = 0; v < 16; ++v)
+    for (int x = tid; x < a.slots; x += 1024) wcnt[v][x] = 0;
   __syncthreads();
   int my_e[kSmallPer];
 #pragma unroll
