@@ -623,10 +623,13 @@ __global__ __launch_bounds__(1024) void quant_align_kernel(const uint16_t* __res
   if (blockIdx.x == 0 && threadIdx.x == 0) *g = gv;
   // Half-blocks i (8 elements); both lanes of a block have the same trip
   // count because n / 8 is even (H is a multiple of 128).
-  const int64_t hb_per_row = H >> 3;
-  for (int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x; i < n / 8; i += (int64_t)nblk * 1024) {
-    const int64_t row = i / hb_per_row;
-    quantize_half_block(x, row, (i - row * hb_per_row) << 3, H, H, gv, q, sf, x_deq);
+  // 32-bit index arithmetic (n <= kFusedQuantMax): the row division is the
+  // costliest step of the loop in 64 bits.
+  static_assert(kFusedQuantMax / 8 < (int64_t(1) << 31), "half-block indices fit 32 bits");
+  const uint32_t hb_per_row = (uint32_t)(H >> 3), n_hb = (uint32_t)(n / 8);
+  for (uint32_t i = blockIdx.x * 1024u + threadIdx.x; i < n_hb; i += (uint32_t)nblk * 1024u) {
+    const uint32_t row = i / hb_per_row;
+    quantize_half_block(x, (int64_t)row, (int64_t)(i - row * hb_per_row) << 3, H, H, gv, q, sf, x_deq);
   }
 }
 
