@@ -52,7 +52,12 @@
  *   from moe_align and are trusted, as the per-group shapes of the grouped
  *   GEMM in vLLM PR #29242 (debug trace) are device-resident and unchecked.
  * - Inputs must be finite; NaN or Inf inputs give unspecified (but in-bounds)
- *   results.  T == 0 is a no-op that still validates the other arguments.
+ *   results, with one guarantee: a NaN takes no part in any maximum (the
+ *   global and the per-block amax ignore it), on every dispatch path, so the
+ *   fused and unfused activation paths agree bit for bit on every input.
+ * - T == 0: the layer calls (moe_*, grouped_gemm*) check dims and return
+ *   NVFP4_OK without launching or writing anything; their pointers may then
+ *   be NULL.  rows == 0 / M == 0 is the same no-op for the row-wise calls.
  */
 #ifndef NVFP4_MOE_H
 #define NVFP4_MOE_H

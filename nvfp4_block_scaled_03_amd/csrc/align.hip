@@ -542,16 +542,16 @@ __global__ __launch_bounds__(1024) void scale_align_kernel(const uint16_t* __res
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        m = fmaxf(m, fabsf(bf16_bits_to_f32(w[u][j] & 0xFFFFu)));
-        m = fmaxf(m, fabsf(bf16_bits_to_f32(w[u][j] >> 16)));
+        m = fmaxf(m, amax_input(bf16_bits_to_f32(w[u][j] & 0xFFFFu)));
+        m = fmaxf(m, amax_input(bf16_bits_to_f32(w[u][j] >> 16)));
       }
   }
   for (; i < n; i += stride) {
     const u32x4 w = *reinterpret_cast<const u32x4*>(x + i);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      m = fmaxf(m, fabsf(bf16_bits_to_f32(w[j] & 0xFFFFu)));
-      m = fmaxf(m, fabsf(bf16_bits_to_f32(w[j] >> 16)));
+      m = fmaxf(m, amax_input(bf16_bits_to_f32(w[j] & 0xFFFFu)));
+      m = fmaxf(m, amax_input(bf16_bits_to_f32(w[j] >> 16)));
     }
   }
 #pragma unroll
@@ -596,8 +596,11 @@ __global__ __launch_bounds__(1024) void quant_align_kernel(const uint16_t* __res
   float m = 0.0f;
   // 16 independent loads per trip, one trip at T*H = 2^17 (indices past
   // the end are clamped to the last 8 elements: re-reading them cannot change
-  // a maximum).  For finite bf16 values, |x| orders like the unsigned 15-bit
-  // pattern, so the maximum is taken on packed 16-bit integers.
+  // a maximum).  For bf16 values that are not NaN, |x| orders like the
+  // unsigned 15-bit pattern, so the maximum is taken on packed 16-bit
+  // integers.  NaN patterns (above 0x7F80) are cleared first, so that a NaN
+  // takes no part in the maximum, as in fmaxf of the unfused reduction: the
+  // two dispatch paths give the same g for every input.
   constexpr int U = 16;
   u16x2 mm = {0, 0};
   for (int64_t base = (int64_t)threadIdx.x * 8; base < n; base += U * 1024 * 8) {
@@ -608,8 +611,13 @@ __global__ __launch_bounds__(1024) void quant_align_kernel(const uint16_t* __res
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        mm = __builtin_elementwise_max(mm, __builtin_bit_cast(u16x2, w[u][j] & 0x7FFF7FFFu));
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t mag = w[u][j] & 0x7FFF7FFFu;
+        // Bit 15 of a half is set by the addition exactly when that half
+        // exceeds 0x7F80 (no carry crosses halves: each stays below 2^16).
+        const uint32_t nan = ((mag + 0x007F007Fu) & 0x80008000u) >> 15;
+        mm = __builtin_elementwise_max(mm, __builtin_bit_cast(u16x2, mag & ~(nan * 0xFFFFu)));
+      }
   }
   m = bf16_bits_to_f32(max((uint32_t)mm[0], (uint32_t)mm[1]));
 #pragma unroll

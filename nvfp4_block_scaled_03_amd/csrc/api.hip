@@ -144,6 +144,7 @@ int moe_align(const nvfp4_moe_dims* d, const int32_t* topk_ids, int32_t* expert_
               void* stream) {
   const char* W = "moe_align";
   if (int r = check_dims(d, W)) return r;
+  if (d->T == 0) return ok();
   const nvfp4::AlignShape a = nvfp4::align_shape(d->T, d->topk, d->E, d->shared);
   if (!expert_offsets || !plan) return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
   if (a.P > 0 && (!sorted_pair || !inv_pos || (d->T * d->topk > 0 && !topk_ids)))
@@ -162,6 +163,7 @@ int moe_scale_and_align(const nvfp4_moe_dims* d, const uint16_t* x, float* g1, v
                         size_t ws_bytes, void* stream) {
   const char* W = "moe_scale_and_align";
   if (int r = check_dims(d, W)) return r;
+  if (d->T == 0) return ok();
   nvfp4::AlignShape a = nvfp4::align_shape(d->T, d->topk, d->E, d->shared);
   a.H = d->H;
   if (!expert_offsets || !plan || !g1) return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
@@ -186,6 +188,7 @@ int moe_route_and_align(const nvfp4_moe_dims* d, const float* logits, int32_t* t
                         int32_t* plan, void* ws, size_t ws_bytes, void* stream) {
   const char* W = "moe_route_and_align";
   if (int r = check_dims(d, W)) return r;
+  if (d->T == 0) return ok();
   if (d->topk > 32)
     return fail(NVFP4_ESHAPE, "%s: ESHAPE num_experts=%d topk=%d (router: topk <= 32)", W, d->E, d->topk);
   nvfp4::AlignShape a = nvfp4::align_shape(d->T, d->topk, d->E, d->shared);
@@ -207,6 +210,7 @@ int moe_quantize_and_align(const nvfp4_moe_dims* d, const uint16_t* x, float* g1
                            int32_t* inv_pos, int32_t* plan, void* ws, size_t ws_bytes, void* stream) {
   const char* W = "moe_quantize_and_align";
   if (int r = check_dims(d, W)) return r;
+  if (d->T == 0) return ok();
   nvfp4::AlignShape a = nvfp4::align_shape(d->T, d->topk, d->E, d->shared);
   a.H = d->H;
   if (!expert_offsets || !plan || !g1) return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);

@@ -57,13 +57,13 @@ __global__ __launch_bounds__(kScaleThreads) void global_scale_kernel(const T* __
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int j = 0; j < E; ++j) m = fmaxf(m, fabsf(v[u][j]));
+      for (int j = 0; j < E; ++j) m = fmaxf(m, amax_input(v[u][j]));
   }
   for (; i < n; i += stride) {
     float v[E];
     load_vec(xb, i, v);
 #pragma unroll
-    for (int j = 0; j < E; ++j) m = fmaxf(m, fabsf(v[j]));
+    for (int j = 0; j < E; ++j) m = fmaxf(m, amax_input(v[j]));
   }
   m = block_max<kScaleThreads>(m);
   if (threadIdx.x == 0) {
@@ -129,6 +129,7 @@ hipError_t launch_quantize(const void* x, int dtype, int64_t rows, int64_t K, in
                            uint16_t* x_deq, hipStream_t s) {
   const int64_t threads = rows * (K >> 3);
   const int64_t blocks = (threads + kThreads - 1) / kThreads;
+  if (blocks == 0) return hipSuccess;
   if (dtype == 0)
     quantize_kernel<uint16_t><<<(unsigned)blocks, kThreads, 0, s>>>(
         static_cast<const uint16_t*>(x), rows, K, ldx, g, rows_per_g, q, sf, x_deq);

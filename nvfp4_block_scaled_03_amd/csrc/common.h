@@ -59,14 +59,19 @@ __device__ __forceinline__ float row16_max(float v) {
 // Every decision compares a float |x| (or a block amax) with a real
 // threshold g * M, where g is the FP32 global scale and M a small constant of
 // at most 7 significant bits (6 * an E4M3 midpoint, or t * s for an E2M1
-// boundary t and an E4M3 scale s).  The product g * M is split exactly into
-// p + e with one FMA (p = fl(g M), e = g M - p, exact when g M is far from
-// underflow), which settles the comparison in FP32:
-//   a - gM = (a - p) - e, and a - p is exact when a and p are within a
-//   factor 2 of each other (Sterbenz); otherwise |a - p| > p/2 >> |e| and the
-//   sign of fl(a - p) decides.
+// boundary t and an E4M3 scale s).
+//  - Block scale: fma(-g, M, a) rounds the exact a - g M once, and a
+//    correctly rounded value has the sign of the exact one (it is zero only
+//    when the exact value is, as a - g M is a multiple of a far larger power
+//    of two than the smallest subnormal), so its sign is the decision.
+//  - E2M1 bounds: the product g * M is split exactly into p + e with one FMA
+//    (p = fl(g M), e = g M - p), which gives the floats just below and above
+//    the real boundary.
 // For an extremely small g (below 2^-80, where the split may underflow) both
 // sides are first multiplied by 2^64, which is exact and changes no decision.
+// (An earlier form took sign((a - p) - e); the compiler's contraction of
+// a - g*M into an FMA made it return "equal" when g M lies exactly halfway
+// between two floats.  The one-FMA form leaves nothing to contract.)
 // ---------------------------------------------------------------------------
 
 // Value of a non-negative E4M3 code 0x00..0x7E.
@@ -79,11 +84,16 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
 
 // sign(a - g * M) for a >= 0, g > 0, M > 0 (see above).
 __device__ __forceinline__ int cmp_scaled(float a, float g, float M) {
-  const float p = g * M;
-  const float e = __builtin_fmaf(g, M, -p);
-  const float d = a - p;
-  return (d > e) - (d < e);
+  const float d = __builtin_fmaf(-g, M, a);
+  return (d > 0.0f) - (d < 0.0f);
 }
+
+// |v| as an input to a maximum that must ignore NaN.  In IEEE mode the
+// hardware maximum returns the other operand for a quiet NaN but a quiet NaN
+// for a signalling one, which would drop the maximum gathered so far; the
+// input is therefore quietened first (canonicalisation), so any NaN, quiet or
+// signalling, takes no part in the maximum.
+__device__ __forceinline__ float amax_input(float v) { return fabsf(__builtin_canonicalizef(v)); }
 
 constexpr float kTinyG = 8.271806125530277e-25f;  // 2^-80
 constexpr float kLift = 18446744073709551616.0f;    // 2^64

@@ -1378,19 +1378,18 @@ hipError_t launch_lds(KParams kp, int list_len, hipStream_t s) {
 }
 
 // Persistent launch: as many workgroups as fit on the device at once (the
-// occupancy of this kernel times the CU count), capped by the work.
+// occupancy of this kernel times the CU count), capped by the work.  Both
+// figures are queried on every call (host-side lookups), so nothing is kept
+// between calls and each device answers for itself.
 template <auto KERN>
 hipError_t launch_persistent(const KParams& kp, int64_t units, hipStream_t s) {
-  static int per_cu = 0;
-  if (per_cu == 0) {
-    int nb = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(KERN),
-                                                                kNW * kWave, 0);
-    if (e != hipSuccess) return e;
-    per_cu = nb > 0 ? nb : 1;
-  }
+  int nb = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(KERN),
+                                                              kNW * kWave, 0);
+  if (e != hipSuccess) return e;
+  const int per_cu = nb > 0 ? nb : 1;
   int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
+  e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   const int64_t need = (units + kNW - 1) / kNW;

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const T* __restrict__ 
   if (!FRAG || row < rows) load8(x, row * ldx + c8, v);   // (padding rows: zeros)
   float m = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+  for (int j = 0; j < 8; ++j) m = fmaxf(m, amax_input(v[j]));
   m = fmaxf(m, dpp_xor1(m));
   m = fmaxf(m, dpp_xor2(m));
   // floor(log2 m) = frexp exponent - 1 (m = f * 2^E, f in [0.5, 1)).

@@ -77,7 +77,7 @@ __device__ __forceinline__ void quantize_half_block_values(const float (&v)[8], 
                                                            uint16_t* __restrict__ x_deq) {
   float m = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+  for (int j = 0; j < 8; ++j) m = fmaxf(m, amax_input(v[j]));
   m = fmaxf(m, dpp_xor1(m));
   const uint32_t sc = e4m3_scale_code(m, gv);
   const float s = e4m3_value(sc);

@@ -108,12 +108,28 @@ def test_gemm2_errors_name_the_problem(lib):
     assert rc == _lib.NVFP4_EINVAL and "out_dtype=5" in _lib.last_error()
 
 
-def test_zero_tokens_is_a_noop(lib):
-    d = _d(T=0)
-    assert lib.grouped_gemm1_swiglu(ctypes.byref(d), *([None] * 13), None) == _lib.NVFP4_OK
+@pytest.mark.parametrize("shared", [0, 1])
+def test_zero_tokens_is_a_noop(lib, shared):
+    """T == 0: every layer call checks dims and returns OK without launching
+    (no stream is touched, so NULL pointers are fine) -- also the fused
+    activation + permutation calls."""
+    d = _d(T=0, shared=shared)
+    r = ctypes.byref(d)
+    assert lib.grouped_gemm1_swiglu(r, *([None] * 13), None) == _lib.NVFP4_OK
+    assert lib.grouped_gemm1_swiglu_w4a16(r, *([None] * 7), None) == _lib.NVFP4_OK
+    assert lib.grouped_gemm2_combine(r, *([None] * 10), None, 0, None, 0, None) == _lib.NVFP4_OK
+    assert lib.grouped_gemm2_combine_w4a16(r, *([None] * 7), None, 0, None, 0, None) == _lib.NVFP4_OK
+    assert lib.moe_align(r, *([None] * 6), 0, None) == _lib.NVFP4_OK
+    assert lib.moe_scale_and_align(r, *([None] * 3), 0, *([None] * 6), 0, None) == _lib.NVFP4_OK
+    assert lib.moe_route_and_align(r, *([None] * 8), 0, None) == _lib.NVFP4_OK
+    assert lib.moe_quantize_and_align(r, None, None, None, 0, *([None] * 9), 0, None) == _lib.NVFP4_OK
     assert lib.nvfp4_quantize(None, 0, 0, 32, 32, None, 1, None, None, None, None) == _lib.NVFP4_OK
     assert lib.moe_route_topk(None, 0, 8, 2, None, None, None) == _lib.NVFP4_OK
     assert _lib.last_error() == ""
+    # bad dims are still rejected at T == 0
+    bad = _d(T=0, H=100)
+    assert lib.moe_quantize_and_align(ctypes.byref(bad), None, None, None, 0, *([None] * 9), 0,
+                                      None) == _lib.NVFP4_ESHAPE
 
 
 def test_route_and_align_errors(lib):

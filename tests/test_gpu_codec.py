@@ -9,6 +9,7 @@ import moe_inputs
 from nvfp4_block_scaled_03_amd import ops
 from oracle import nvfp4 as onv
 
+import ties
 from parity import device, to_np
 
 pytestmark = pytest.mark.gpu
@@ -80,7 +81,7 @@ def test_quantize_activations(dev, name):
     xf = to_np(x).astype(np.float64)
     g_ref = onv.global_scale(xf)
     assert to_np(g)[0] == g_ref
-    rows = np.arange(w.T) if w.T <= 1024 else np.random.default_rng(0).choice(w.T, 1024, replace=False)
+    rows = np.arange(w.T)          # every row, prefill and skew included
     codes, scales = onv.quantize(xf[rows], g_ref)
     assert np.array_equal(to_np(sf)[rows], scales)
     assert np.array_equal(to_np(q)[rows], onv.pack_codes(codes))
@@ -206,3 +207,60 @@ def test_scale_decisions_at_every_midpoint(dev):
         c, s = onv.quantize(x[r:r + 1], grow[r])
         assert sf[r, 0] == s[0, 0], (r, grow[r], x[r, 0])
         assert np.array_equal(q[r:r + 1], onv.pack_codes(c)), r
+
+
+@pytest.mark.parametrize("T", [64, 4096])
+def test_nan_takes_no_part_in_the_amax(dev, T):
+    """A NaN (quiet and signalling bf16 patterns) takes no part in the global
+    or the block amax on either dispatch path of the activation step: the
+    fused decode-sized kernel (T = 64) and the separate scale and quantise
+    launches (T = 4096) give g1 = the oracle's scale of x with the NaNs set
+    to 0, the oracle's codes and scales on every block without a NaN, and the
+    two paths agree bit for bit on every byte."""
+    H = 2048
+    gen = torch.Generator(device=dev).manual_seed(T)
+    x = torch.randn(T, H, generator=gen, device=dev).to(torch.bfloat16)
+    bits = x.view(torch.int16)
+    nan_at = [(1, 5, 0x7FC0), (T - 1, H - 1, 0x7F81), (T // 2, 100, 0xFFC1)]   # quiet, signalling, negative
+    for r, c, pat in nan_at:
+        bits[r, c] = pat if pat < 0x8000 else pat - 0x10000
+    x[3, 7] = 100.0                                      # the finite maximum
+    xf = to_np(x).astype(np.float64)
+    assert np.isnan(xf).sum() == 3
+    x0 = np.where(np.isnan(xf), 0.0, xf)
+    g_ref = onv.global_scale(x0)
+    codes, scales = onv.quantize(x0, g_ref)
+    d = ops.dims(T, 1, 1, H, 128, 0)
+    ids = torch.zeros(T, 1, dtype=torch.int32, device=dev)
+    # fused path (one launch when T * H <= 2^18) or its two-launch form
+    g_f, q_f, sf_f, _ = ops.quantize_and_align(d, x, ids)
+    # the separate calls
+    g_s = ops.global_scale(x)
+    q_s, sf_s = ops.quantize(x, g_s)
+    torch.cuda.synchronize()
+    assert to_np(g_f)[0] == g_ref and to_np(g_s)[0] == g_ref
+    assert np.array_equal(to_np(q_f), to_np(q_s)) and np.array_equal(to_np(sf_f), to_np(sf_s))
+    # every block scale is that of the block without its NaN; every code but
+    # the NaN elements' own is the oracle's
+    assert np.array_equal(to_np(sf_s), scales)
+    got_c = onv.unpack_codes(to_np(q_s))
+    nan_el = np.isnan(xf)
+    assert np.array_equal(got_c[~nan_el], codes[~nan_el])
+
+
+def test_decisions_at_product_ties(dev):
+    """Block amaxes and elements next to thresholds g * M that fall exactly
+    halfway between two floats, for every E4M3 midpoint and every E2M1
+    boundary: the case where comparing fl(a - g M) with the product's
+    rounding error returns "equal" although a is strictly above."""
+    x, grow = ties.product_tie_blocks(np.random.default_rng(31))
+    xt = torch.tensor(x, dtype=torch.float32, device=dev)
+    gt = torch.tensor(grow, dtype=torch.float32, device=dev)
+    q, sf = ops.quantize(xt, gt, rows_per_g=1)
+    q, sf = to_np(q), to_np(sf)
+    n_bad = 0
+    for r in range(x.shape[0]):
+        cc, ss = onv.quantize(x[r:r + 1], grow[r])
+        n_bad += int(sf[r, 0] != ss[0, 0]) + int(not np.array_equal(q[r:r + 1], onv.pack_codes(cc)))
+    assert n_bad == 0, f"{n_bad} of {x.shape[0]} tie blocks decided differently"
+    print(f"product-tie blocks: {x.shape[0]}")
