@@ -5,18 +5,22 @@ garbage while the dense FP4 GEMM was right.  This module therefore restates the
 layer without any grouping, permutation or batching: for each token, for each
 of its experts, one dense matrix-vector product per projection, accumulated in
 FP64 in the order of the token's expert list.  ``tests`` compare it with the
-grouped ``oracle.moe.layer`` on small workloads.
+grouped ``oracle.moe.layer`` on small workloads.  The activation comes from
+torch (``torch.nn.functional.silu`` in FP64), not from ``oracle.moe``, so a
+mistake in either implementation of the SwiGLU step shows as a mismatch.
 """
 from __future__ import annotations
 
 import numpy as np
+import torch
 
 from . import nvfp4
 
 
 def _silu(z):
-    with np.errstate(over="ignore"):
-        return z / (1.0 + np.exp(-z))
+    """silu through torch's own FP64 CPU kernel (z * sigmoid(z)), a second,
+    independent implementation of the activation next to ``moe.silu``."""
+    return torch.nn.functional.silu(torch.from_numpy(np.asarray(z, dtype=np.float64))).numpy()
 
 
 def layer_per_token(x, topk_ids, topk_w, w13_hat, w2_hat, I: int, variant: str = "w4a4",

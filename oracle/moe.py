@@ -121,6 +121,10 @@ class ExpertWeights:
         codes, scales, g = self.quantized(which, e)
         return nvfp4.dequantize(codes, scales, g)
 
+    def drop(self, which: int, e: int) -> None:
+        """Forget the quantisation of one matrix (to bound host memory)."""
+        self._cache.pop((which, int(e)), None)
+
 
 def silu(z):
     z = np.asarray(z, dtype=np.float64)
@@ -131,6 +135,23 @@ def silu(z):
 def swiglu(c, I: int):
     """h = silu(gate) * up for c = [gate | up] along the last axis."""
     return silu(c[..., :I]) * c[..., I:]
+
+
+def expert_h(x_hat, tok, weights: "ExpertWeights", e: int, I: int) -> np.ndarray:
+    """FP64 SwiGLU intermediate of expert slot e for the rows of tokens ``tok``:
+    h = swiglu(x_hat[tok] W13_e^T)."""
+    return swiglu(np.asarray(x_hat)[np.asarray(tok)] @ weights.dequantized(13, e).T, I)
+
+
+def activations_hat(x, variant: str):
+    """(g1, codes, scales, x_hat): the dequantised W4A4 activations, or x
+    itself for W4A16 (g1, codes, scales None)."""
+    x = np.asarray(x, dtype=np.float64)
+    if variant == "w4a4":
+        g1 = nvfp4.global_scale(x)
+        codes, scales = nvfp4.quantize(x, g1)
+        return g1, codes, scales, nvfp4.dequantize(codes, scales, g1)
+    return None, None, None, x
 
 
 # --------------------------------------------------------------------------
@@ -151,16 +172,21 @@ class LayerResult:
     a2_scales: Optional[np.ndarray]  # uint8 [len(rows), I/16] (W4A4)
     a2_bf16: Optional[np.ndarray]   # FP64 [len(rows), I] bfloat16 values (W4A16)
     d: np.ndarray                  # FP64 [len(rows), H] down-projection output per row
+    g2: Optional[np.float32] = None  # intermediate global scale used (W4A4)
 
 
 def layer(x, topk_ids, topk_w, weights: ExpertWeights, n_routed: int, I: int,
-          variant: str = "w4a4", g2=None, shared: int = 0, tokens=None) -> LayerResult:
+          variant: str = "w4a4", g2=None, shared: int = 0, tokens=None,
+          calibrate: bool = False) -> LayerResult:
     """One mixture-of-experts expert layer.
 
     x: [T, H] bf16 values (any float dtype holding them); topk_ids int [T, k];
     topk_w float32 [T, k]; g2: FP32 intermediate global scale (W4A4 only).
     ``tokens`` restricts the computation to the pairs of those tokens (the
-    activation global scale is still taken over all of x).
+    activation global scale is still taken over all of x).  ``calibrate``
+    (W4A4): take g2 = fl32(max |h| / 2688) over the computed pairs (the value
+    ``calibrate_g2`` returns for the same tokens) instead of the argument; the
+    result's ``g2`` field holds the value used.
     """
     if variant not in ("w4a4", "w4a16"):
         raise ValueError(variant)
@@ -168,16 +194,12 @@ def layer(x, topk_ids, topk_w, weights: ExpertWeights, n_routed: int, I: int,
     T, H = x.shape
     k = np.asarray(topk_ids).shape[1]
     offsets, sorted_pair, inv_pos = align(topk_ids, n_routed, shared)
-    if variant == "w4a4":
-        g1 = nvfp4.global_scale(x)
-        a1_codes, a1_scales = nvfp4.quantize(x, g1)
-        x_hat = nvfp4.dequantize(a1_codes, a1_scales, g1)
-    else:
-        g1, a1_codes, a1_scales = None, None, None
-        x_hat = x
+    g1, a1_codes, a1_scales, x_hat = activations_hat(x, variant)
     keep_tok = np.ones(T, dtype=bool) if tokens is None else np.isin(np.arange(T), tokens)
     out = np.zeros((T, H), dtype=np.float64)
     rows_all, h_all, a2c_all, a2s_all, a2b_all, d_all = [], [], [], [], [], []
+    # GEMM1 + SwiGLU of every expert first (g2 may depend on all of them).
+    stage1 = []
     for e in range(len(offsets) - 1):
         rows = np.arange(offsets[e], offsets[e + 1])
         tok, wgt = pair_token_weight(sorted_pair[rows], T, k, topk_w)
@@ -185,8 +207,11 @@ def layer(x, topk_ids, topk_w, weights: ExpertWeights, n_routed: int, I: int,
         rows, tok, wgt = rows[sel], tok[sel], wgt[sel]
         if rows.size == 0:
             continue
-        c = x_hat[tok] @ weights.dequantized(13, e).T
-        h = swiglu(c, I)
+        stage1.append((e, rows, tok, wgt, expert_h(x_hat, tok, weights, e, I)))
+    if calibrate and variant == "w4a4":
+        amax = max((float(np.abs(h).max()) for *_, h in stage1), default=0.0)
+        g2 = np.float32(amax / (nvfp4.E2M1_MAX * nvfp4.E4M3_MAX))
+    for e, rows, tok, wgt, h in stage1:
         if variant == "w4a4":
             a2c, a2s = nvfp4.quantize(h, g2)
             h_hat = nvfp4.dequantize(a2c, a2s, g2)
@@ -206,7 +231,7 @@ def layer(x, topk_ids, topk_w, weights: ExpertWeights, n_routed: int, I: int,
 
     return LayerResult(
         out=out, offsets=offsets, sorted_pair=sorted_pair, inv_pos=inv_pos,
-        g1=g1, a1_codes=a1_codes, a1_scales=a1_scales,
+        g1=g1, a1_codes=a1_codes, a1_scales=a1_scales, g2=g2,
         rows=np.concatenate(rows_all) if rows_all else np.zeros(0, dtype=np.int64),
         h=cat(h_all, I),
         a2_codes=cat(a2c_all, I).astype(np.uint8) if variant == "w4a4" else None,
@@ -242,8 +267,7 @@ def calibrate_g2(x, topk_ids, weights: ExpertWeights, n_routed: int, I: int,
     x = np.asarray(x, dtype=np.float64)
     T = x.shape[0]
     k = np.asarray(topk_ids).shape[1]
-    g1 = nvfp4.global_scale(x)
-    x_hat = nvfp4.dequantize(*nvfp4.quantize(x, g1), g1)
+    x_hat = activations_hat(x, "w4a4")[3]
     offsets, sorted_pair, _ = align(topk_ids, n_routed, shared)
     keep_tok = np.ones(T, dtype=bool) if tokens is None else np.isin(np.arange(T), tokens)
     amax = 0.0
@@ -253,6 +277,5 @@ def calibrate_g2(x, topk_ids, weights: ExpertWeights, n_routed: int, I: int,
         tok = tok[keep_tok[tok]]
         if tok.size == 0:
             continue
-        h = swiglu(x_hat[tok] @ weights.dequantized(13, e).T, I)
-        amax = max(amax, float(np.abs(h).max()))
+        amax = max(amax, float(np.abs(expert_h(x_hat, tok, weights, e, I)).max()))
     return np.float32(amax / (nvfp4.E2M1_MAX * nvfp4.E4M3_MAX))

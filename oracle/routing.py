@@ -26,10 +26,33 @@ def route_topk(logits, k: int) -> tuple[np.ndarray, np.ndarray]:
         raise ValueError("need 1 <= k <= E")
     order = np.argsort(-z, axis=1, kind="stable")      # stable: lower id first on ties
     ids = order[:, :k]
-    sel = np.take_along_axis(z, ids, axis=1)
-    ex = np.exp(sel - sel[:, :1])                      # sel[:, 0] is the row maximum
-    w = ex / ex.sum(axis=1, keepdims=True)
+    w = selected_weights_f64(np.take_along_axis(z, ids, axis=1))
     return ids.astype(np.int32), w.astype(np.float32)
+
+
+def selected_weights_f64(sel) -> np.ndarray:
+    """FP64 softmax over the selected logits [T, k] (column 0 the largest):
+    exp(z_j - z_0) / sum_i exp(z_i - z_0), the sum taken in the order
+    i = 0, 1, ..., k-1 (the order fixes the FP64 rounding of the sum)."""
+    sel = np.asarray(sel, dtype=np.float64)
+    ex = np.exp(sel - sel[:, :1])
+    s = ex[:, 0].copy()
+    for j in range(1, ex.shape[1]):
+        s = s + ex[:, j]
+    return ex / s[:, None]
+
+
+def fp32_rounding_near_tie(v, rel: float = 2.0 ** -40) -> np.ndarray:
+    """True where the FP64 value v lies within ``rel`` (relative) of a point
+    halfway between two neighbouring FP32 numbers: there, an FP64 result that
+    differs from this one by a few FP64 ulps (another exp implementation) may
+    round to the other FP32 neighbour.  For normal FP32 magnitudes only."""
+    v = np.abs(np.asarray(v, dtype=np.float64))
+    m, e = np.frexp(v)                       # v = m * 2^e, 0.5 <= m < 1
+    ulp = np.ldexp(1.0, e - 24)              # FP32 spacing at v
+    lo = np.floor(v / ulp) * ulp             # FP32 neighbour below (exact)
+    mid = lo + 0.5 * ulp
+    return (v > 0) & (np.abs(v - mid) <= rel * v)
 
 
 def route_two_step(logits, k: int) -> tuple[np.ndarray, np.ndarray]:

@@ -1,4 +1,8 @@
 """Pins for the routing, permutation and layer oracle (CPU only)."""
+import math
+from decimal import Decimal, localcontext
+from fractions import Fraction
+
 import numpy as np
 import pytest
 import torch
@@ -38,6 +42,98 @@ def test_route_weights_descending_and_top1():
     assert np.all(np.diff(w, axis=1) <= 0)
     ids1, w1 = routing.route_topk(z, 1)
     assert np.all(w1 == 1.0) and np.array_equal(ids1[:, 0], np.argmax(z, 1))
+
+
+def test_route_weights_sum_in_expert_order():
+    """The FP64 sum of the selected exponentials runs j = 0, 1, ..., k-1 (the
+    order the GPU router uses), checked against a plain Python loop."""
+    rng = np.random.default_rng(12)
+    z = rng.standard_normal((200, 64)).astype(np.float32) * 3
+    ids, w = routing.route_topk(z, 10)
+    for t in range(200):
+        sel = [float(z[t, e]) for e in ids[t]]
+        ex = [math.exp(v - sel[0]) for v in sel]
+        tot = 0.0
+        for v in ex:
+            tot += v
+        assert [np.float32(v / tot) for v in ex] == list(w[t])
+
+
+def test_fp32_near_tie_flag_against_fractions():
+    """fp32_rounding_near_tie flags exactly the values within rel of a point
+    halfway between FP32 neighbours (exact rational distances)."""
+    rng = np.random.default_rng(13)
+    v = rng.uniform(0.01, 1.0, 3000)
+    # values placed at known distances from FP32 midpoints
+    f32 = rng.uniform(0.05, 0.9, 300).astype(np.float32).astype(np.float64)
+    ulp = np.ldexp(1.0, np.frexp(f32)[1] - 24)
+    mid = f32 + 0.5 * ulp
+    rel = 2.0 ** -40
+    placed = np.concatenate([mid, mid * (1 + 0.5 * rel), mid * (1 - 0.5 * rel),
+                             mid * (1 + 3 * rel), mid * (1 - 3 * rel)])
+    v = np.concatenate([v, placed])
+    got = routing.fp32_rounding_near_tie(v, rel)
+    for x, flag in zip(v, got):
+        fx = Fraction(float(x))
+        # FP32 neighbours of x by exact search: below = largest FP32 <= x
+        lo = Fraction(float(np.float32(x)))
+        if lo > fx:
+            lo = Fraction(float(np.nextafter(np.float32(x), np.float32(0))))
+        hi = Fraction(float(np.nextafter(np.float32(float(lo)), np.float32(2))))
+        m = (lo + hi) / 2
+        want = abs(fx - m) <= Fraction(rel) * fx
+        assert bool(flag) == want, (x, flag)
+    assert got[3000:3900].all() and not got[3900:].any()
+
+
+# ---------------------------------------------------------------- SwiGLU
+def _silu_exact(z: float) -> Decimal:
+    """silu(z) = z / (1 + e^-z) evaluated with 60 significant decimal digits."""
+    with localcontext() as ctx:
+        ctx.prec = 60
+        dz = Decimal(float(z))
+        return dz / (1 + (-dz).exp())
+
+
+SILU_GRID = np.concatenate([
+    np.array([0.0, -0.0, 1e-300, -1e-300, 5e-324, 2.0 ** -30, -2.0 ** -30, 0.5, -0.5, 1.0, -1.0,
+              3.0, -3.0, 20.0, -20.0, 36.0, -36.0, 88.0, -88.0, 700.0, -700.0, 709.0, -709.0,
+              1e4, 1e300]),
+    np.random.default_rng(14).standard_normal(2000) * np.exp(np.random.default_rng(15).uniform(-8, 6, 2000)),
+])
+
+
+def test_silu_against_exact_decimal():
+    """moe.silu within 4 ulps of the 60-digit value on a grid that includes
+    tiny, huge and large-negative arguments (where exp(-z) is far above 1)."""
+    got = moe.silu(SILU_GRID)
+    for z, v in zip(SILU_GRID, got):
+        ref = float(_silu_exact(z))
+        assert math.copysign(1.0, v) == math.copysign(1.0, ref) or ref == 0.0
+        assert abs(v - ref) <= 4 * np.spacing(abs(ref)), (z, v, ref)
+
+
+def test_silu_against_torch():
+    """The same grid through torch's FP64 silu (z * sigmoid(z))."""
+    ref = torch.nn.functional.silu(torch.from_numpy(SILU_GRID)).numpy()
+    assert np.allclose(moe.silu(SILU_GRID), ref, rtol=1e-14, atol=0)
+    big = np.array([-745.0, -1000.0, -1e300])      # true values underflow to -0 or a subnormal
+    assert np.all(np.abs(moe.silu(big)) <= 1e-320)
+
+
+def test_swiglu_gate_then_up_against_exact_decimal():
+    """h = silu(first half) * second half, element by element at 60 digits;
+    swapping the halves or dropping a factor fails."""
+    rng = np.random.default_rng(16)
+    I = 48
+    c = rng.standard_normal((5, 2 * I)) * 4
+    h = moe.swiglu(c, I)
+    for r in range(5):
+        for i in range(I):
+            want = _silu_exact(c[r, i]) * Decimal(float(c[r, I + i]))
+            assert abs(h[r, i] - float(want)) <= 8 * np.spacing(abs(float(want))) + 1e-300
+    swapped = moe.silu(c[:, I:]) * c[:, :I]
+    assert not np.allclose(h, swapped)
 
 
 # ---------------------------------------------------------------- permutation
@@ -126,7 +222,9 @@ def test_layer_shared_expert_equals_per_token():
 
 
 def _dense_mlp(x_hat, W13, W2, I, variant, g2):
-    h = moe.silu(x_hat @ W13[:I].T) * (x_hat @ W13[I:].T)
+    # silu from torch: these special cases must not lean on moe.silu itself
+    gate = torch.from_numpy(x_hat @ W13[:I].T)
+    h = torch.nn.functional.silu(gate).numpy() * (x_hat @ W13[I:].T)
     if variant == "w4a4":
         h = nvfp4.dequantize(*nvfp4.quantize(h, g2), g2)
     else:
@@ -217,3 +315,19 @@ def test_pair_token_weight():
     tw = np.array([[0.25, 0.75], [0.5, 0.5]], dtype=np.float32)
     tok, wt = moe.pair_token_weight(np.array([0, 1, 3, 4, 5]), 2, 2, tw)
     assert list(tok) == [0, 0, 1, 0, 1] and list(wt) == [0.25, 0.75, 0.5, 1.0, 1.0]
+
+
+def test_layer_calibrate_inline_matches_two_pass():
+    """layer(calibrate=True) takes g2 = fl32(max |h| / 2688) over the computed
+    pairs: the value calibrate_g2 gives, and then the same layer."""
+    w = moe_inputs.WORKLOADS["tiny"]
+    x, ids, tw, w13, w2 = _tiny_inputs(w)
+    ew = moe.ExpertWeights.from_arrays(w13, w2)
+    for toks in (None, [0, 3, 9]):
+        g2 = moe.calibrate_g2(x, ids, ew, w.E, w.I, tokens=toks)
+        a = moe.layer(x, ids, tw, ew, w.E, w.I, g2=g2, tokens=toks)
+        b = moe.layer(x, ids, tw, ew, w.E, w.I, calibrate=True, tokens=toks)
+        assert b.g2 == g2
+        assert np.array_equal(a.out, b.out) and np.array_equal(a.a2_codes, b.a2_codes)
+        # g2 is the global scale of h itself
+        assert b.g2 == nvfp4.global_scale(b.h)

@@ -270,3 +270,95 @@ def test_near_tie_mask_flags_ties():
     x[0, 0] = 7.125                      # scale tie (see golden B5)
     ef, bf = nvfp4.near_tie_mask(x, g)
     assert bf[0, 0]
+
+
+# ---------------------------------------------------------------- near ties (exact)
+def _near_tie_brute(row, g, rel, abs_tol):
+    """Flags of one 16-element block with exact rationals: the block is
+    flagged when its amax lies within rel * b + abs_tol of a boundary b = 6 g m
+    (m halfway between neighbouring E4M3 values); an element when |x| lies that
+    close to a boundary t s g (t halfway between neighbouring E2M1
+    magnitudes, s the block's scale)."""
+    g = Fraction(float(np.float32(g)))
+    rel, abs_tol = Fraction(rel), Fraction(abs_tol)
+    vals = [Fraction(float(v)) for v in row]
+    amax = max(abs(v) for v in vals)
+    e4 = [Fraction(float(v)) for v in nvfp4.E4M3_POS]
+    e2 = [Fraction(float(v)) for v in nvfp4.E2M1_MAGS]
+
+    def close(a, b):
+        return abs(a - b) <= rel * b + abs_tol
+
+    block = any(close(amax, 6 * g * (e4[i] + e4[i + 1]) / 2) for i in range(len(e4) - 1))
+    s = Fraction(float(nvfp4.E4M3_POS[nvfp4.block_scales(np.asarray(row)[None, :], float(g))[0, 0]]))
+    elem = [s > 0 and any(close(abs(v), s * g * (e2[i] + e2[i + 1]) / 2) for i in range(7))
+            for v in vals]
+    return elem, block
+
+
+def _placed_blocks(rng, g, rel, abs_tol):
+    """Blocks with elements and maxima put at chosen distances from their
+    rounding boundaries: inside the band (should flag), just outside it (should
+    not), exactly on it, and random values in between."""
+    out = []
+    e4m = nvfp4._midpoints(nvfp4.E4M3_POS)
+    e2m = nvfp4._midpoints(nvfp4.E2M1_MAGS)
+    for f in (0.0, 0.5, -0.5, 0.9, -0.9, 1.2, -1.2, 3.0, -3.0):
+        for _ in range(6):
+            s_code = int(rng.integers(0x20, 0x60))
+            s = nvfp4.E4M3_POS[s_code]
+            row = rng.uniform(-6, 6, 16) * s * g
+            row[0] = 6 * s * g                             # amax sits at the scale itself
+            t = e2m[int(rng.integers(0, 7))] * s * g
+            row[1 + int(rng.integers(0, 15))] = t * (1 + f * rel) + (f * abs_tol if abs_tol else 0.0)
+            out.append(row)
+            b = 6 * g * e4m[int(rng.integers(0x18, 0x70))]
+            row2 = rng.uniform(-1, 1, 16) * b / 2
+            row2[int(rng.integers(0, 16))] = b * (1 + f * rel) + (f * abs_tol if abs_tol else 0.0)
+            out.append(row2)
+    return np.array(out)
+
+
+@pytest.mark.parametrize("rel,abs_tol", [(2.0 ** -12, 0.0), (2.0 ** -12, 2.0 ** -16), (2.0 ** -8, 0.0)])
+def test_near_tie_mask_against_fractions(rel, abs_tol):
+    """near_tie_mask equals the exact-rational definition on random blocks
+    and on blocks built around the boundaries, so that neither a missed nor an
+    over-broad flag (which would quietly loosen the parity bar) gets through."""
+    rng = np.random.default_rng(int(1 / rel) + int(abs_tol * 1e6))
+    g = np.float32(0.0371)
+    rnd = rng.standard_normal((120, 16)) * np.exp(rng.uniform(-3, 3, (120, 1)))
+    x = np.concatenate([rnd, _placed_blocks(rng, float(g), rel, abs_tol)])
+    ef, bf = nvfp4.near_tie_mask(x, g, rel, abs_tol=abs_tol)
+    n_flag = 0
+    for r in range(x.shape[0]):
+        elem, block = _near_tie_brute(x[r], g, rel, abs_tol)
+        assert bool(bf[r, 0]) == block, (r, x[r])
+        assert list(ef[r].astype(bool)) == elem, (r, x[r])
+        n_flag += sum(elem)
+    # the placed values land on both sides of the band
+    assert 0 < n_flag < x.size // 4
+
+
+def test_quantize_at_product_ties_against_fractions():
+    """The oracle's decisions next to thresholds g * M that lie exactly
+    halfway between two floats, against the exact-rational definition."""
+    import ties
+    x, gs = ties.product_tie_blocks(np.random.default_rng(31))
+    e4 = [Fraction(float(v)) for v in nvfp4.E4M3_POS]
+    e2 = [Fraction(float(v)) for v in nvfp4.E2M1_MAGS]
+
+    def nearest(v, grid):          # ties to the even index, saturating
+        best = min(range(len(grid)), key=lambda i: (abs(grid[i] - v), i % 2))
+        return best
+
+    for r in range(x.shape[0]):
+        g = Fraction(float(np.float32(gs[r])))
+        codes, sc = nvfp4.quantize(x[r:r + 1], gs[r])
+        amax = max(abs(Fraction(float(v))) for v in x[r])
+        s_idx = nearest(amax / (6 * g), e4) if amax > 0 else 0
+        assert sc[0, 0] == s_idx, r
+        s = e4[s_idx]
+        for k in range(16):
+            v = Fraction(float(x[r, k]))
+            m = nearest(abs(v) / (s * g), e2) if s > 0 else 0
+            assert codes[0, k] == (m | (8 if x[r, k] < 0 or (x[r, k] == 0 and np.signbit(x[r, k])) else 0)), (r, k)
