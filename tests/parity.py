@@ -55,27 +55,71 @@ def check_layer_out(got, ref, what=""):
     return rf, ma / r if r else 0.0
 
 
+# Observed near-tie rates of every a2 judged in this session (reported by
+# conftest.py at the end of the run).
+RATES: list = []
+
+
 class A2Check:
     """Result of judging a GPU-requantised NVFP4 intermediate."""
 
-    def __init__(self, codes, scales, exact, flips):
+    def __init__(self, codes, scales, exact, flips, code_rate=0.0, scale_rate=0.0):
         self.codes = codes      # admissible codes (the GPU's, once validated)
         self.scales = scales
         self.exact = exact      # bool: bit-identical to the oracle's own rounding
         self.flips = flips      # number of differing codes/scales
+        self.code_rate = code_rate    # differing element codes / elements
+        self.scale_rate = scale_rate  # differing block scales / blocks
 
 
-def check_a2_nvfp4(gpu_q: np.ndarray, gpu_sf: np.ndarray, h: np.ndarray, g2, max_rate=1e-4,
-                   rel=2.0 ** -12) -> A2Check:
+# The error model behind both checks.  The GPU's h = silu(alpha c_gate) *
+# (alpha c_up) comes from FP32 accumulation of exact products (f16 x f16
+# fragments, or bf16) over the contraction, then an FP32 alpha multiply, the
+# hardware exp and reciprocal in silu, and one FP32 product.  Its distance to
+# the FP64 h is a few FP32 ulps of |h| (the epilogue) plus the accumulation
+# error, which scales with the partial sums rather than with h and is
+# therefore absolute: about 2^-24 times the magnitudes the sums pass through,
+# i.e. of the order of 2^-24 * sqrt(K) * rms(h) for K-long sums of
+# random-signed terms.  So an element is "near a tie" when it lies within
+# REL * |b| + ABS_FRAC * rms(h) of a rounding boundary b:
+#   REL = 2^-12 (NVFP4 codes and scales; 2^12 FP32 ulps, far above the
+#         epilogue's few), ABS_FRAC = 2^-16 (2^8 times 2^-24, covering
+#         sqrt(K) up to 256 with margin).
+# For the bf16 intermediate every value is within a few ulps of some bf16
+# boundary at that resolution, so there the admissible set is the bf16
+# rounding of any value within BF16_REL * |h| + ABS_FRAC * rms(h) of h
+# (BF16_REL = 2^-19, 32 FP32 ulps).
+REL = 2.0 ** -12
+ABS_FRAC = 2.0 ** -16
+BF16_REL = 2.0 ** -19
+# Rate bounds.  A flip needs h within the error of a boundary: about
+# 2 * err / spacing of the grid, with err a few FP32 ulps of |h| (the
+# epilogue's exp, reciprocal and products) in the common case.  NVFP4 codes
+# (spacing about a third of the value) give ~1e-6 and the bound is 1e-4;
+# bf16 (spacing 2^-8 of the value) gives ~1e-4 and the bound is 1e-3.
+# Observed on MI355X over every workload: 0 NVFP4 code or scale flips,
+# bf16 differences 0 to 2.7e-4 of the elements (all inside the band).
+NVFP4_MAX_RATE = 1e-4
+BF16_MAX_RATE = 1e-3
+
+
+def _record(what, kind, n_diff, n_total, flagged):
+    RATES.append({"what": what, "kind": kind, "diff": int(n_diff), "total": int(n_total),
+                  "rate": float(n_diff) / max(1, int(n_total)), "flagged": int(flagged)})
+
+
+def check_a2_nvfp4(gpu_q: np.ndarray, gpu_sf: np.ndarray, h: np.ndarray, g2, max_rate=NVFP4_MAX_RATE,
+                   rel=REL, what="") -> A2Check:
     """Judge GPU a2 bytes (rows x I/2, rows x I/16) against the oracle's FP64 h.
 
-    Exact everywhere except where the oracle flags a near tie (within ``rel``
-    of a rounding midpoint of a block scale or of an element code); there the
-    GPU may hold the neighbouring code, and element codes of a block whose
-    scale flipped must equal the oracle's encoding of h with that scale."""
+    Exact everywhere except where the oracle flags a near tie (within
+    rel * |b| + 2^-16 * rms(h) of a rounding boundary b of a block scale or
+    an element code); there the GPU may hold the neighbouring code, and
+    element codes of a block whose scale flipped must equal the oracle's
+    encoding of h with that scale."""
     ref_codes, ref_sf = onv.quantize(h, g2)
     got_codes = onv.unpack_codes(gpu_q)
-    elem_flag, block_flag = onv.near_tie_mask(h, g2, rel, abs_tol=2.0 ** -16 * rms(h))
+    elem_flag, block_flag = onv.near_tie_mask(h, g2, rel, abs_tol=ABS_FRAC * rms(h))
     sf_diff = gpu_sf != ref_sf
     bad_sf = sf_diff & ~(block_flag & (np.abs(gpu_sf.astype(int) - ref_sf.astype(int)) == 1))
     assert not bad_sf.any(), f"block scales differ outside near ties at {np.argwhere(bad_sf)[:5]}"
@@ -90,30 +134,35 @@ def check_a2_nvfp4(gpu_q: np.ndarray, gpu_sf: np.ndarray, h: np.ndarray, g2, max
     bad = cd & ~ok_flip
     assert not bad.any(), (f"codes differ outside near ties: {bad.sum()} at {np.argwhere(bad)[:5]} "
                            f"got {got_codes[bad][:5]} want {exp_codes[bad][:5]}")
-    flips = int(cd.sum()) + int(sf_diff.sum())
+    n_cd, n_sf = int(cd.sum()), int(sf_diff.sum())
+    flips = n_cd + n_sf
+    _record(what, "nvfp4 codes", n_cd, h.size, elem_flag.sum())
+    _record(what, "nvfp4 scales", n_sf, gpu_sf.size, block_flag.sum())
     assert flips <= max(2, max_rate * h.size), \
-        f"too many near-tie flips: {int(cd.sum())} codes, {int(sf_diff.sum())} scales of {h.size}"
+        f"too many near-tie flips: {n_cd} codes, {n_sf} scales of {h.size}"
     exact = bool(np.array_equal(got_codes, ref_codes) and np.array_equal(gpu_sf, ref_sf))
-    return A2Check(got_codes, gpu_sf.copy(), exact, flips)
+    return A2Check(got_codes, gpu_sf.copy(), exact, flips, n_cd / max(1, h.size),
+                   n_sf / max(1, gpu_sf.size))
 
 
-def check_a2_bf16(gpu_bits: np.ndarray, h: np.ndarray, max_rate=5e-3) -> np.ndarray:
+def check_a2_bf16(gpu_bits: np.ndarray, h: np.ndarray, max_rate=BF16_MAX_RATE, what="") -> np.ndarray:
     """GPU bf16 a2 vs the oracle's FP64 h.
 
-    The GPU's h carries FP32 accumulation error, which is absolute (about
-    2^-24 of the accumulated magnitudes), so a small h may be off by more than
-    a bf16 ulp of itself.  Admissible: the bf16 rounding (nearest even) of any
-    value within delta = 2^-16 * rms(h) of h.  Exact bf16(h) elsewhere; the
-    rate of differences is bounded.  Returns the GPU values as FP64."""
+    Admissible: the bf16 rounding (nearest even) of any value within
+    delta = 2^-19 |h| + 2^-16 rms(h) of h (the error model above).  Exact
+    bf16(h) elsewhere; the rate of differences is bounded.  Returns the GPU
+    values as FP64."""
     got = (gpu_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     ref = onv.round_to_bf16(h)
     diff = got != ref
+    n_diff = int(diff.sum())
     if diff.any():
         hv, gv = h[diff], got[diff]
-        delta = 2.0 ** -16 * rms(h)
+        delta = BF16_REL * np.abs(hv) + ABS_FRAC * rms(h)
         lo = onv.round_to_bf16(hv - delta)
         hi = onv.round_to_bf16(hv + delta)
         ok = (gv >= lo) & (gv <= hi)
         assert ok.all(), f"bf16 a2 outside the admissible roundings: got {gv[~ok][:5]} h {hv[~ok][:5]}"
-    assert diff.sum() <= max(2, max_rate * h.size), f"too many bf16 differences: {diff.sum()}"
+    _record(what, "bf16", n_diff, h.size, n_diff)
+    assert n_diff <= max(2, max_rate * h.size), f"too many bf16 differences: {n_diff} of {h.size}"
     return got

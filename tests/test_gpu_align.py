@@ -21,6 +21,24 @@ def dev():
     return device()
 
 
+def check_router_weights(got, z, ids):
+    """Router weights bit for bit.  Both sides take the softmax over the
+    selected logits in FP64 (the sum in selection order) and round once to
+    FP32; only the exp implementations differ, by an FP64 ulp or two, which
+    can move the FP32 rounding only where the FP64 quotient lies within
+    2^-40 of a point halfway between FP32 neighbours.  Such positions (the
+    oracle flags them; expected none) may differ by one FP32 ulp."""
+    sel = np.take_along_axis(np.asarray(z, dtype=np.float32).astype(np.float64), ids.astype(np.int64), axis=1)
+    w64 = oroute.selected_weights_f64(sel)
+    want = w64.astype(np.float32)
+    flag = oroute.fp32_rounding_near_tie(w64)
+    diff = got != want
+    assert not (diff & ~flag).any(), f"router weights differ at {np.argwhere(diff & ~flag)[:5]}"
+    ulp = np.abs(got.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+    assert (ulp[diff] <= 1).all()
+    print(f"router weights: {diff.sum()} of {got.size} differ, {flag.sum()} flagged near ties")
+
+
 @pytest.mark.parametrize("name", moe_inputs.ORDER)
 def test_router(dev, name):
     w = moe_inputs.WORKLOADS[name]
@@ -28,7 +46,7 @@ def test_router(dev, name):
     ids, wt = ops.route_topk(z, w.topk)
     rid, rw = oroute.route_topk(to_np(z), w.topk)
     assert np.array_equal(to_np(ids), rid)
-    np.testing.assert_allclose(to_np(wt), rw, rtol=4e-7, atol=0)
+    check_router_weights(to_np(wt), to_np(z), rid)
 
 
 def test_router_ties(dev):
@@ -38,7 +56,7 @@ def test_router_ties(dev):
     ids, wt = ops.route_topk(z, 7)
     rid, rw = oroute.route_topk(to_np(z), 7)
     assert np.array_equal(to_np(ids), rid)
-    np.testing.assert_allclose(to_np(wt), rw, rtol=4e-7, atol=0)
+    check_router_weights(to_np(wt), to_np(z), rid)
 
 
 def _check_align(dev, ids_np, E, shared, al=None):
@@ -203,5 +221,5 @@ def test_route_and_align(dev, name):
     for _ in range(2):
         ids, wt, al = ops.route_and_align(d, z)
         assert np.array_equal(to_np(ids), rid)
-        np.testing.assert_allclose(to_np(wt), rw, rtol=4e-7, atol=0)
+        check_router_weights(to_np(wt), to_np(z), rid)
         _check_align(dev, rid, E, shared, al=al)
