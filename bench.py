@@ -1,7 +1,8 @@
 """Benchmark of the NVFP4 MoE expert layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
-                    [--variant w4a4|w4a16] [--mode graph|eager] [--no-cpu]
+                    [--variant w4a4|w4a16] [--mode graph|eager] [--no-configs]
+                    [--no-linear] [--no-cpu]
 
 A step is one pass of the whole layer path on one batch: global activation
 scale, activation quantisation, permutation by expert, grouped GEMM1 with
@@ -11,9 +12,15 @@ prepared weights) are resident in HBM before timing starts; routing and weight
 preparation are outside the step.  Several copies of the weights are rotated
 between steps so the 256 MB Infinity Cache cannot serve repeats.
 
-Prints one JSON line: throughput in tokens/s, the dominant kernel's roofline
-figures measured with HIP events inside the timed region, and the CPU oracle's
-throughput on a bounded sample of the same workload.
+Prints one JSON line.  ``value`` is the tokens/s of the headline workload
+(decode: T = 64, H = 2048, I = 768, E = 128, top-8) over exactly K timed
+steps.  ``configs`` holds every workload and variant (tiny, decode W4A16,
+prefill, large_e, skew in both variants), each with its step time over K
+steps, the median over >= 100 graph replays after >= 10 warm-up replays, the
+per-stage breakdown, and the roofline figures of its dominant kernel (GEMM1)
+measured with HIP events on the launch stream inside the timed region.
+``cpu_baseline`` is the FP64 oracle timed on the host cores on a bounded
+sample.
 """
 from __future__ import annotations
 
@@ -21,6 +28,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -32,11 +40,13 @@ sys.path.insert(0, ROOT)
 
 import moe_inputs  # noqa: E402
 from nvfp4_block_scaled_03_amd import ops  # noqa: E402
+from nvfp4_block_scaled_03_amd.profiling import build_layer, weight_copies  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense FP16/BF16 matrix peak
 MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 matrix peak
 INFINITY_CACHE = 256 << 20
+REPLAYS, REPLAY_WARMUP = 100, 10
 
 
 def parse():
@@ -47,10 +57,10 @@ def parse():
     p.add_argument("--workload", default="decode", choices=moe_inputs.ORDER)
     p.add_argument("--variant", default="w4a4", choices=["w4a4", "w4a16"])
     p.add_argument("--mode", default="graph", choices=["eager", "graph"])
-    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-configs", action="store_true", help="skip the other workloads")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-linear", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
     return p.parse_args()
 
 
@@ -58,116 +68,105 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_layer(w, dev):
-    d = ops.dims(w.T, w.topk, w.E, w.H, w.I, w.shared)
-    x = moe_inputs.activations(w, device=dev)
-    logits = moe_inputs.router_logits(w, device=dev)
-    ids, tw = ops.route_topk(logits, w.topk)
-    # Quantise the weights expert-group by expert-group to bound FP32 memory.
-    S = w.n_experts
-    chunk = max(1, min(S, (8 << 30) // (4 * 3 * w.I * w.H)))
-    parts = []
-    for s0 in range(0, S, chunk):
-        sel = range(s0, min(S, s0 + chunk))
-        sub = ops.dims(w.T, w.topk, len(sel), w.H, w.I, 0)
-        w13 = moe_inputs.expert_weights(w, 13, device=dev, experts=sel)
-        w2 = moe_inputs.expert_weights(w, 2, device=dev, experts=sel)
-        g13 = ops.global_scale(w13, batches=len(sel))
-        q13, sf13 = ops.quantize(w13.reshape(-1, w.H), g13, rows_per_g=2 * w.I)
-        g2w = ops.global_scale(w2, batches=len(sel))
-        q2, sf2 = ops.quantize(w2.reshape(-1, w.I), g2w, rows_per_g=w.H)
-        parts.append((q13.view(len(sel), 2 * w.I, -1), sf13.view(len(sel), 2 * w.I, -1), g13,
-                      q2.view(len(sel), w.H, -1), sf2.view(len(sel), w.H, -1), g2w))
-        del w13, w2, sub
-    cat = [torch.cat([p[i] for p in parts]) for i in range(6)]
-    del parts
-    prep13 = ops.prep_weights(d, 13, cat[0], cat[1])
-    prep2 = ops.prep_weights(d, 2, cat[3], cat[4])
-    empty = torch.empty(0, dtype=torch.uint8, device=dev)
-    wq = ops.ExpertWeights(empty, empty, cat[2], empty, empty, cat[5], prep13, prep2)
-    del cat
-    g2 = ops.calibrate_g2(d, x, ids, wq)
-    torch.cuda.synchronize()
-    return d, x, ids, tw, wq, g2
+def dtype_label(variant):
+    return ("nvfp4 codes, f16 matrix ops, f32 accumulate" if variant == "w4a4"
+            else "nvfp4 weights, bf16 activations, bf16 matrix ops, f32 accumulate")
 
 
-def weight_copies(wq, n):
-    out = [wq]
-    for _ in range(n - 1):
-        out.append(ops.ExpertWeights(wq.q13, wq.sf13, wq.g13.clone(), wq.q2, wq.sf2, wq.g2.clone(),
-                                     wq.prep13.clone(), wq.prep2.clone()))
-    return out
-
-
-def cpu_baseline(w, dev, ids, tw, seconds):
-    """The FP64 oracle on a bounded sample of the workload's tokens (host cores)."""
+# ---------------------------------------------------------------- CPU oracle
+def _oracle_inputs(w, dev, n_tok):
+    """Host copies of the sample: x, routing (the oracle's own router on the
+    same logits), and expert weights fetched on demand."""
     from oracle import moe as omoe
-    try:
-        import threadpoolctl
-        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) \
-            if threadpoolctl.threadpool_info() else 1
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
-    n_tok = min(w.T, 16)
-    toks = np.arange(n_tok)
+    from oracle import routing as oroute
     x = moe_inputs.activations(w, device=dev).float().cpu().numpy().astype(np.float64)
-    ids_np, tw_np = ids.cpu().numpy(), tw.cpu().numpy()
-    cache13, cache2 = {}, {}
+    ids, tw = oroute.route_topk(moe_inputs.router_logits(w, device=dev).cpu().numpy(), w.topk)
+    cache = {}
 
-    def src13(e):
-        if e not in cache13:
-            cache13[e] = moe_inputs.expert_weight(w, 13, e, device=dev).cpu().numpy()
-        return cache13[e]
+    def src(which):
+        def get(e):
+            if (which, e) not in cache:
+                cache[(which, e)] = moe_inputs.expert_weight(w, which, e, device=dev).cpu().numpy()
+            return cache[(which, e)]
+        return get
 
-    def src2(e):
-        if e not in cache2:
-            cache2[e] = moe_inputs.expert_weight(w, 2, e, device=dev).cpu().numpy()
-        return cache2[e]
-
-    ew = omoe.ExpertWeights(src13, src2)
-    # Offline weight quantisation is outside the timed scope, as on the GPU.
-    used = set(int(e) for e in ids_np[:n_tok].reshape(-1)) | ({w.E} if w.shared else set())
-    for e in used:
+    ew = omoe.ExpertWeights(src(13), src(2))
+    used = set(int(e) for e in ids[:n_tok].reshape(-1)) | ({w.E} if w.shared else set())
+    for e in used:              # offline weight quantisation: outside the timed scope, as on the GPU
         ew.quantized(13, e)
         ew.quantized(2, e)
-    g2 = np.float32(1e-3)
+    toks = np.arange(n_tok)
+    g2 = omoe.calibrate_g2(x, ids, ew, w.E, w.I, w.shared, tokens=toks)
+    return x, ids, tw, ew, toks, g2
+
+
+def _time_oracle(w, x, ids, tw, ew, toks, g2, seconds, max_reps=1000):
+    from oracle import moe as omoe
     reps, t0 = 0, time.perf_counter()
     while True:
-        omoe.layer(x, ids_np, tw_np, ew, w.E, w.I, variant="w4a4", g2=g2, shared=w.shared,
-                   tokens=toks)
+        omoe.layer(x, ids, tw, ew, w.E, w.I, variant="w4a4", g2=g2, shared=w.shared, tokens=toks)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= seconds or reps >= 1000:
-            break
-    return {"value": n_tok * reps / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n_tok} of {w.T} tokens of the {w.name} layer, W4A4, FP64 NumPy, "
-                      f"{reps} repetitions in {el:.1f} s (weight quantisation excluded)"}
+        if el >= seconds or reps >= max_reps:
+            return reps, el
 
 
-def time_steps(layer, x, ids, tw, copies, variant, steps, warmup, mode):
-    """Mean wall time of one layer step (ms) over ``steps`` steps.
+def cpu_baseline(w, dev, seconds):
+    """The FP64 oracle (W4A4, same scope as the GPU step: global scale,
+    quantisation, alignment, both GEMMs with SwiGLU and requantisation,
+    combine) on a bounded sample of the workload's tokens, with every BLAS
+    thread the process may use; then single-threaded on the tiny and decode
+    layers."""
+    import threadpoolctl
+    info = threadpoolctl.threadpool_info()
+    threads = max((i.get("num_threads", 1) for i in info), default=1)
+    affinity = len(os.sched_getaffinity(0))
+    n_tok = min(w.T, 16)
+    x, ids, tw, ew, toks, g2 = _oracle_inputs(w, dev, n_tok)
+    reps, el = _time_oracle(w, x, ids, tw, ew, toks, g2, seconds)
+    flops = 6.0 * w.H * w.I * (n_tok * w.topk + (n_tok if w.shared else 0))
+    res = {"value": n_tok * reps / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{n_tok} of {w.T} tokens of the {w.name} layer, W4A4, FP64 NumPy, "
+                     f"{reps} repetitions in {el:.1f} s (weight quantisation excluded)",
+           "gflops": round(flops * reps / el / 1e9, 2),
+           "affinity_cores": affinity, "blas_threads": int(threads), "single_thread": []}
+    with threadpoolctl.threadpool_limits(1):
+        for name, n1, sec in (("tiny", 16, 3.0), ("decode", 4, 6.0)):
+            w1 = moe_inputs.WORKLOADS[name]
+            xi, idi, twi, ewi, ti, g2i = _oracle_inputs(w1, dev, n1)
+            r1, e1 = _time_oracle(w1, xi, idi, twi, ewi, ti, g2i, sec)
+            res["single_thread"].append({"workload": name, "tokens": n1, "reps": r1, "seconds": round(e1, 2),
+                                         "tokens_per_s": round(n1 * r1 / e1, 3)})
+    return res
 
-    Graph mode captures the steps of all weight copies in one graph, one
-    complete step per copy in sequence, as a model forward captures its
-    consecutive layers; a remainder of steps runs from one-step graphs."""
-    out = torch.empty(x.shape[0], layer.d.H, dtype=torch.bfloat16, device=x.device)
-    graphs, multi = [], None
-    if mode == "graph":
+
+# ---------------------------------------------------------------- GPU timing
+def make_graphs(layer, x, ids, tw, copies, variant, out):
+    """One graph per weight copy (a single step) and one graph holding one step
+    per copy in sequence, as a model forward captures its consecutive layers."""
+    graphs = []
+    for wc in copies:
+        for _ in range(2):
+            layer.forward(x, ids, tw, variant, out=out, weights=wc)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layer.forward(x, ids, tw, variant, out=out, weights=wc)
+        graphs.append(g)
+    multi = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(multi):
         for wc in copies:
-            for _ in range(2):
-                layer.forward(x, ids, tw, variant, out=out, weights=wc)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                layer.forward(x, ids, tw, variant, out=out, weights=wc)
-            graphs.append(g)
-        multi = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(multi):
-            for wc in copies:
-                layer.forward(x, ids, tw, variant, out=out, weights=wc)
+            layer.forward(x, ids, tw, variant, out=out, weights=wc)
+    return graphs, multi
+
+
+def time_steps(layer, x, ids, tw, copies, variant, steps, warmup, mode, graphs=None, multi=None):
+    """Mean wall time of one layer step (ms) over exactly ``steps`` steps
+    (synchronised on both sides); graph mode replays the multi-step graph and
+    the one-step graphs for a remainder."""
+    out = torch.empty(x.shape[0], layer.d.H, dtype=torch.bfloat16, device=x.device)
 
     def run(i0, count):
-        """Steps i0 .. i0 + count - 1; returns how many ran."""
         if multi is not None and count >= len(copies) and i0 % len(copies) == 0:
             multi.replay()
             return len(copies)
@@ -187,6 +186,40 @@ def time_steps(layer, x, ids, tw, copies, variant, steps, warmup, mode):
         i += run(i, steps - i)
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def replay_median(multi, n_copies, replays=REPLAYS, warmup=REPLAY_WARMUP):
+    """Median (and spread) of the per-step time over ``replays`` replays of
+    the multi-step graph, each bracketed by events on the current stream."""
+    for _ in range(warmup):
+        multi.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(replays + 1)]
+    ev[0].record()
+    for i in range(replays):
+        multi.replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) / n_copies for i in range(replays))
+    return {"replays": replays, "warmup_replays": warmup, "median_ms": round(statistics.median(per), 5),
+            "p10_ms": round(per[replays // 10], 5), "p90_ms": round(per[(9 * replays) // 10], 5)}
+
+
+def breakdown(layer, x, ids, tw, copies, variant, n=20):
+    """Mean per-stage time (ms) of eager steps: front end (scale, quantise,
+    align; W4A16: align), GEMM1, GEMM2 + combine; events on the launch stream."""
+    out = torch.empty(x.shape[0], layer.d.H, dtype=torch.bfloat16, device=x.device)
+    tot = np.zeros(3)
+    for i in range(n + 3):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record()
+        layer.forward(x, ids, tw, variant, out=out, weights=copies[i % len(copies)], marks=ev[1:])
+        torch.cuda.synchronize()
+        if i >= 3:
+            tot += [ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]), ev[2].elapsed_time(ev[3])]
+    t = tot / n
+    return {"front_ms": round(t[0], 5), "gemm1_ms": round(t[1], 5), "gemm2_combine_ms": round(t[2], 5),
+            "eager_step_ms": round(float(t.sum()), 5)}
 
 
 def time_gemm1(layer, x, ids, tw, copies, variant, n=50):
@@ -210,9 +243,8 @@ def measured_traffic(workload: str, variant: str):
     (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when there
     is none for this workload or the kernel sources changed since it was taken."""
     from nvfp4_block_scaled_03_amd import profiling
-    if variant != "w4a4":
-        return None
-    path = os.path.join(ROOT, "profiles", f"grouped_gemm1_swiglu_{workload}_traffic.txt")
+    suffix = "" if variant == "w4a4" else "_w4a16"
+    path = os.path.join(ROOT, "profiles", f"grouped_gemm1_swiglu{suffix}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     t = profiling.read_traffic(path)
@@ -221,8 +253,9 @@ def measured_traffic(workload: str, variant: str):
     return int(float(t["bytes_per_launch"]))
 
 
-def measure(w, d, x, ids, tw, wq, g2, a, steps, warmup):
-    """Step time, GEMM1 time and the derived figures for one batch shape."""
+def measure(w, d, x, ids, tw, wq, g2, variant, steps, warmup, mode):
+    """Step time (mean over ``steps``), replay median, breakdown and GEMM1
+    roofline for one workload and variant."""
     P = w.pairs
     al = ops.moe_align(d, ids)
     rows_per_expert = np.diff(al.offsets.cpu().numpy())
@@ -232,35 +265,53 @@ def measure(w, d, x, ids, tw, wq, g2, a, steps, warmup):
     n_copies = max(1, math.ceil(4 * INFINITY_CACHE / max(1, touched * (wbytes13 + wbytes2))))
     copies = weight_copies(wq, min(n_copies, 8))
     layer = ops.MoELayer(d, wq, g2, device=x.device)
-    ms = time_steps(layer, x, ids, tw, copies, a.variant, steps, warmup, a.mode)
-    g1_ms = time_gemm1(layer, x, ids, tw, copies, a.variant)
+    out = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=x.device)
+    graphs = multi = None
+    if mode == "graph":
+        graphs, multi = make_graphs(layer, x, ids, tw, copies, variant, out)
+    ms = time_steps(layer, x, ids, tw, copies, variant, steps, warmup, mode, graphs, multi)
+    rep = replay_median(multi, len(copies)) if multi is not None else None
+    bd = breakdown(layer, x, ids, tw, copies, variant)
+    g1_ms = time_gemm1(layer, x, ids, tw, copies, variant)
     g1_flops = 2.0 * P * (2 * w.I) * w.H
-    g1_bytes = touched * wbytes13 + w.T * (w.H // 2 + w.H // 16) + P * (w.I // 2 + w.I // 16)
+    a1_bytes = w.T * (w.H // 2 + w.H // 16) if variant == "w4a4" else w.T * w.H * 2
+    a2_bytes = P * (w.I // 2 + w.I // 16) if variant == "w4a4" else P * w.I * 2
+    g1_bytes = touched * wbytes13 + a1_bytes + a2_bytes
     decode_like = P / max(1, w.n_experts) < 64
     if decode_like:
         ach = g1_bytes / (g1_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(w.name, a.variant)}
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name, variant)}
     else:
         ach = g1_flops / (g1_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
-    roof.update({"kernel": "grouped_gemm1_swiglu" + ("" if a.variant == "w4a4" else "_w4a16"),
+    roof.update({"kernel": "grouped_gemm1_swiglu" + ("" if variant == "w4a4" else "_w4a16"),
                  "kernel_ms": round(g1_ms, 5), "algorithmic_bytes": int(g1_bytes),
                  "algorithmic_flops": g1_flops})
     layer_flops = moe_inputs.flops(w)
     layer_bytes = moe_inputs.touched_bytes(w, rows_per_expert)
-    return {
-        "ms": ms, "tokens_per_s": w.T / (ms * 1e-3), "touched": touched,
-        "copies": len(copies), "roofline": roof,
+    med = rep["median_ms"] if rep else ms
+    rec = {
+        "workload": w.name, **w.describe(), "variant": variant, "mode": mode,
+        "experts_touched": touched, "weight_copies": len(copies),
+        "steps": steps, "ms_per_step": round(ms, 5), "tokens_per_s": round(w.T / (ms * 1e-3), 1),
         "layer_tflops": round(layer_flops / (ms * 1e-3) / 1e12, 2),
         "layer_gbs": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
         "layer_hbm_frac": round(layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "layer_mfma_frac": round(layer_flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+        "median_tokens_per_s": round(w.T / (med * 1e-3), 1),
+        "breakdown": bd, "roofline": roof,
     }
+    if rep:
+        rec["replay"] = rep
+    del graphs, multi, layer, copies
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
 
 
+# ---------------------------------------------------------------- dense linear
 LINEAR_N, LINEAR_K = 34816, 5120          # the pages' per-GEMM shape (27B gate_up)
 LINEAR_MS = (1, 16, 64, 256, 1024, 4096)
 
@@ -330,56 +381,74 @@ def linear_sweep(dev, copies=3, reps=10):
             "rows": rows}
 
 
+# ---------------------------------------------------------------- main
+# The other workloads and variants reported next to the headline line (the
+# five workload shapes; large_e and skew in both variants).  Prefill reuses
+# the decode layer's weights (the same expert shape).
+OTHER_CONFIGS = [("decode", "w4a16"), ("tiny", "w4a4"), ("prefill", "w4a4"), ("prefill", "w4a16"),
+                 ("large_e", "w4a4"), ("large_e", "w4a16"), ("skew", "w4a4"), ("skew", "w4a16")]
+
+
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark measures one GPU; --gpus must be 1 (no second GPU is used)"}))
         sys.exit(2)
     dev = torch.device("cuda:0")
     w = moe_inputs.WORKLOADS[a.workload]
     log(f"[bench] building {w.name} layer ({a.variant}, {a.mode})")
-    d, x, ids, tw, wq, g2 = build_layer(w, dev)
+    built = {w.name: build_layer(w, dev)}
+    d, x, ids, tw, wq, g2 = built[w.name]
     log(f"[bench] timing {a.steps} steps")
-    m = measure(w, d, x, ids, tw, wq, g2, a, a.steps, a.warmup)
+    m = measure(w, d, x, ids, tw, wq, g2, a.variant, a.steps, a.warmup, a.mode)
     res = {
         "metric": "NVFP4 MoE layer tokens/s (30B-A3B expert shape)",
-        "value": round(m["tokens_per_s"], 1),
+        "value": m["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": round(m["ms"], 5),
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4 codes, f16 matrix ops, f32 accumulate" if a.variant == "w4a4"
-                 else "nvfp4 weights, bf16 activations, bf16 matrix ops, f32 accumulate",
+        "dtype": dtype_label(a.variant),
         "data": "synthetic (seeded), random-init weights",
         "config": {"workload": w.name, **w.describe(), "variant": a.variant, "mode": a.mode,
-                   "experts_touched": m["touched"], "weight_copies": m["copies"],
-                   "steps_per_graph": m["copies"] if a.mode == "graph" else 1},
+                   "experts_touched": m["experts_touched"], "weight_copies": m["weight_copies"],
+                   "steps_per_graph": m["weight_copies"] if a.mode == "graph" else 1},
         "layer_tflops": m["layer_tflops"], "layer_gbs": m["layer_gbs"],
         "layer_hbm_frac": m["layer_hbm_frac"],
         "roofline": m["roofline"],
+        "replay": m.get("replay"), "breakdown": m["breakdown"],
     }
-    if a.workload == "decode" and not a.no_prefill:
-        # The prefill-shaped batch (T = 4096) on the same layer weights.
-        wp = moe_inputs.WORKLOADS["prefill"]
-        log("[bench] prefill batch on the same layer")
-        dp = ops.dims(wp.T, wp.topk, wp.E, wp.H, wp.I, wp.shared)
-        xp = moe_inputs.activations(wp, device=dev)
-        idp, twp = ops.route_topk(moe_inputs.router_logits(wp, device=dev), wp.topk)
-        g2p = ops.calibrate_g2(dp, xp, idp, wq)
-        mp = measure(wp, dp, xp, idp, twp, wq, g2p, a, max(5, a.steps // 4), max(2, a.warmup // 2))
-        res["prefill"] = {"T": wp.T, "tokens_per_s": round(mp["tokens_per_s"], 1),
-                          "ms_per_step": round(mp["ms"], 5), "layer_tflops": mp["layer_tflops"],
-                          "layer_mfma_frac": mp["layer_mfma_frac"], "roofline": mp["roofline"]}
-    if a.workload == "decode" and not a.no_linear:
+    if not a.no_configs:
+        res["configs"] = {}
+        for name, variant in OTHER_CONFIGS:
+            if name == a.workload and variant == a.variant:
+                continue
+            wc = moe_inputs.WORKLOADS[name]
+            if name not in built:
+                # drop layers no later config uses (bounded device memory)
+                for k in [k for k in built if k not in ("decode",) and k != name]:
+                    del built[k]
+                torch.cuda.empty_cache()
+                reuse = built["decode"][4] if name == "prefill" and "decode" in built else None
+                log(f"[bench] building {name} layer")
+                built[name] = build_layer(wc, dev, weights=reuse)
+            dc, xc, idc, twc, wqc, g2c = built[name]
+            log(f"[bench] {name} {variant}")
+            steps = max(5, a.steps // 2)
+            res["configs"][f"{name}_{variant}"] = measure(wc, dc, xc, idc, twc, wqc, g2c, variant, steps,
+                                                          max(3, a.warmup // 2), a.mode)
+    built.clear()
+    torch.cuda.empty_cache()
+    if not a.no_linear:
         log("[bench] dense linear M sweep")
         res["linear"] = linear_sweep(dev)
     if not a.no_cpu:
         log("[bench] cpu baseline")
-        res["cpu_baseline"] = cpu_baseline(w, dev, ids, tw, a.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(w, dev, a.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

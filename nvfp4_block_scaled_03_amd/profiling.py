@@ -1,8 +1,13 @@
 """Programs and summaries for rocprofv3 runs of the hot path.
 
-    python -m nvfp4_block_scaled_03_amd.profiling gemm1 [--workload decode] [--reps 5]
-        Launch GEMM1 (W4A4) of the named layer ``reps`` times, weight copies
-        rotated as in bench.py (the kernel to collect counters for).
+    python -m nvfp4_block_scaled_03_amd.profiling gemm1|gemm2 [--workload decode]
+            [--variant w4a4] [--reps 5]
+        Launch GEMM1 (or GEMM2 + combine) of the named layer ``reps`` times,
+        weight copies rotated as in bench.py (the kernel to collect counters
+        for).
+    python -m nvfp4_block_scaled_03_amd.profiling layer [--workload decode]
+            [--variant w4a4] [--steps 20]
+        Eager passes of the whole layer (the program of a kernel trace).
     python -m nvfp4_block_scaled_03_amd.profiling copy [--mib 1024] [--reps 3]
         A plain device-to-device copy of a known size (counter calibration:
         FETCH_SIZE / WRITE_SIZE per dispatch against the bytes really moved).
@@ -20,6 +25,8 @@
 
 bench.py reads the traffic summary and reports it only while the sources
 still hash to the recorded value (a changed kernel invalidates the counters).
+``build_layer`` and ``weight_copies`` build the benchmark's layers (bench.py
+and the profiling programs above share them).
 """
 from __future__ import annotations
 
@@ -72,23 +79,103 @@ def read_traffic(path: str):
     return out
 
 
-def _cmd_gemm1(a):
+def build_layer(w, dev, weights=None):
+    """Inputs and prepared NVFP4 weights of workload ``w`` on device ``dev``:
+    (dims, x, topk_ids, topk_w, ExpertWeights, g2).  Routing by the library's
+    router; weights quantised and prepared by the library, expert group by
+    expert group (bounded FP32 memory); g2 calibrated from the layer's own
+    W4A16 intermediate.  ``weights`` reuses prepared weights of the same
+    expert shape instead of building new ones."""
     import torch
-    sys.path.insert(0, ROOT)
-    import bench
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    import moe_inputs
+    from nvfp4_block_scaled_03_amd import ops
+    d = ops.dims(w.T, w.topk, w.E, w.H, w.I, w.shared)
+    x = moe_inputs.activations(w, device=dev)
+    logits = moe_inputs.router_logits(w, device=dev)
+    ids, tw = ops.route_topk(logits, w.topk)
+    if weights is None:
+        S = w.n_experts
+        chunk = max(1, min(S, (8 << 30) // (4 * 3 * w.I * w.H)))
+        parts = []
+        for s0 in range(0, S, chunk):
+            sel = range(s0, min(S, s0 + chunk))
+            w13 = moe_inputs.expert_weights(w, 13, device=dev, experts=sel)
+            w2 = moe_inputs.expert_weights(w, 2, device=dev, experts=sel)
+            g13 = ops.global_scale(w13, batches=len(sel))
+            q13, sf13 = ops.quantize(w13.reshape(-1, w.H), g13, rows_per_g=2 * w.I)
+            g2w = ops.global_scale(w2, batches=len(sel))
+            q2, sf2 = ops.quantize(w2.reshape(-1, w.I), g2w, rows_per_g=w.H)
+            parts.append((q13.view(len(sel), 2 * w.I, -1), sf13.view(len(sel), 2 * w.I, -1), g13,
+                          q2.view(len(sel), w.H, -1), sf2.view(len(sel), w.H, -1), g2w))
+            del w13, w2
+        cat = [torch.cat([p[i] for p in parts]) for i in range(6)]
+        del parts
+        prep13 = ops.prep_weights(d, 13, cat[0], cat[1])
+        prep2 = ops.prep_weights(d, 2, cat[3], cat[4])
+        empty = torch.empty(0, dtype=torch.uint8, device=dev)
+        weights = ops.ExpertWeights(empty, empty, cat[2], empty, empty, cat[5], prep13, prep2)
+        del cat
+    g2 = ops.calibrate_g2(d, x, ids, weights)
+    torch.cuda.synchronize()
+    return d, x, ids, tw, weights, g2
+
+
+def weight_copies(wq, n):
+    """``n`` independent copies of the prepared weights (the first is ``wq``),
+    rotated between steps so that the Infinity Cache cannot serve repeats."""
+    from nvfp4_block_scaled_03_amd import ops
+    out = [wq]
+    for _ in range(n - 1):
+        out.append(ops.ExpertWeights(wq.q13, wq.sf13, wq.g13.clone(), wq.q2, wq.sf2, wq.g2.clone(),
+                                     wq.prep13.clone(), wq.prep2.clone()))
+    return out
+
+
+def _cmd_gemm(a):
+    """Launch one GEMM of the named layer ``reps`` times (weight copies
+    rotated), after one full layer pass has filled its inputs."""
+    import torch
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
     import moe_inputs
     from nvfp4_block_scaled_03_amd import ops
     dev = torch.device("cuda:0")
     w = moe_inputs.WORKLOADS[a.workload]
-    d, x, ids, tw, wq, g2 = bench.build_layer(w, dev)
-    copies = bench.weight_copies(wq, 4)
+    d, x, ids, tw, wq, g2 = build_layer(w, dev)
+    copies = weight_copies(wq, 4)
     layer = ops.MoELayer(d, wq, g2, device=dev)
-    layer.forward(x, ids, tw, "w4a4")
+    out = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev)
+    layer.forward(x, ids, tw, a.variant, out=out)
     torch.cuda.synchronize()
     for i in range(a.reps):
-        layer.gemm1("w4a4", copies[i % len(copies)], x)
+        if a.cmd == "gemm1":
+            layer.gemm1(a.variant, copies[i % len(copies)], x)
+        else:
+            layer.gemm2(a.variant, out, copies[i % len(copies)], tw)
     torch.cuda.synchronize()
-    print(f"gemm1 {a.workload}: {a.reps} launches", flush=True)
+    print(f"{a.cmd} {a.workload} {a.variant}: {a.reps} launches", flush=True)
+
+
+def _cmd_layer(a):
+    """``steps`` eager layer passes of the named workload (weight copies
+    rotated): the program behind the kernel-trace summaries."""
+    import torch
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    import moe_inputs
+    from nvfp4_block_scaled_03_amd import ops
+    dev = torch.device("cuda:0")
+    w = moe_inputs.WORKLOADS[a.workload]
+    d, x, ids, tw, wq, g2 = build_layer(w, dev)
+    copies = weight_copies(wq, 4)
+    layer = ops.MoELayer(d, wq, g2, device=dev)
+    out = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev)
+    for i in range(a.steps):
+        layer.forward(x, ids, tw, a.variant, out=out, weights=copies[i % len(copies)])
+    torch.cuda.synchronize()
+    print(f"layer {a.workload} {a.variant}: {a.steps} steps", flush=True)
 
 
 def _cmd_copy(a):
@@ -195,9 +282,15 @@ def _cmd_counters(a):
 def main(argv=None):
     p = argparse.ArgumentParser()
     sub = p.add_subparsers(dest="cmd", required=True)
-    g = sub.add_parser("gemm1")
-    g.add_argument("--workload", default="decode")
-    g.add_argument("--reps", type=int, default=5)
+    for name in ("gemm1", "gemm2"):
+        g = sub.add_parser(name)
+        g.add_argument("--workload", default="decode")
+        g.add_argument("--variant", default="w4a4", choices=["w4a4", "w4a16"])
+        g.add_argument("--reps", type=int, default=5)
+    ly = sub.add_parser("layer")
+    ly.add_argument("--workload", default="decode")
+    ly.add_argument("--variant", default="w4a4", choices=["w4a4", "w4a16"])
+    ly.add_argument("--steps", type=int, default=20)
     c = sub.add_parser("copy")
     c.add_argument("--mib", type=int, default=1024)
     c.add_argument("--reps", type=int, default=3)
@@ -222,8 +315,8 @@ def main(argv=None):
     st.add_argument("--command", default="")
     st.add_argument("--top", type=int, default=16)
     a = p.parse_args(argv)
-    {"gemm1": _cmd_gemm1, "copy": _cmd_copy, "traffic": _cmd_traffic, "stats": _cmd_stats,
-     "counters": _cmd_counters}[a.cmd](a)
+    {"gemm1": _cmd_gemm, "gemm2": _cmd_gemm, "layer": _cmd_layer, "copy": _cmd_copy,
+     "traffic": _cmd_traffic, "stats": _cmd_stats, "counters": _cmd_counters}[a.cmd](a)
 
 
 if __name__ == "__main__":
