@@ -26,7 +26,10 @@
  *   NULL is the null stream).  The library never synchronises, never
  *   allocates or frees device memory, and keeps no state between calls: all
  *   scratch memory is a caller-owned workspace sized by the *_size queries.
- *   Calls that touch the same buffers must be ordered by the caller.
+ *   (One exception, for callers that cannot allocate:
+ *   grouped_gemm2_combine_noalloc keeps its scratch in a static device array
+ *   per GPU; see its declaration.)  Calls that touch the same buffers must be
+ *   ordered by the caller.
  * - The caller owns every buffer.  Nothing is retained after a call returns.
  * - bfloat16 buffers are passed as uint16_t*.
  * - Canonical NVFP4 layout (the layout bit-exactness is judged on): a matrix
@@ -69,7 +72,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_MOE_ABI_VERSION 5
+#define NVFP4_MOE_ABI_VERSION 6
 
 /* Status codes. */
 #define NVFP4_OK 0
@@ -383,6 +386,33 @@ int grouped_gemm2_combine_w4a16(const nvfp4_moe_dims* dims, const uint16_t* a2,
                                 const int32_t* plan, const float* topk_w, const uint8_t* w2_prep,
                                 const float* gw2, void* out, int out_dtype, void* ws,
                                 size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* GEMM2 + combine without allocation.                                       */
+/* ------------------------------------------------------------------------ */
+/* For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same computation and results, bit for bit, as
+ * grouped_gemm2_combine with the same arguments, except that the per-row
+ * FP32 down-projection outputs live in a static scratch array inside the
+ * library (one per GPU, held until the process ends) instead of a
+ * caller-owned workspace.  Limit: P * H * 4 bytes <=
+ * grouped_gemm2_combine_noalloc_max_bytes() (48 MiB: P * H <= 12,582,912,
+ * e.g. every decode-shaped batch of this header's examples, T * topk up to
+ * 6144 rows at H = 2048); larger shapes return NVFP4_EWORKSPACE with the
+ * needed and available sizes.  The call allocates and frees nothing; on its
+ * first call on a device it looks up that device's copy of the array
+ * (hipGetSymbolAddress).  Every call on a GPU shares that GPU's array, which
+ * keeps the last call's contents (nothing in it needs clearing: each call
+ * writes every row it reads): calls that overlap on one GPU (concurrent
+ * streams, or threads on one device) race and must be serialised by the
+ * caller. */
+size_t grouped_gemm2_combine_noalloc_max_bytes(void);
+int grouped_gemm2_combine_noalloc(const nvfp4_moe_dims* dims, const uint8_t* a2_q, const uint8_t* a2_sf,
+                                  const uint16_t* a2_deq, const float* g2, const int32_t* expert_offsets,
+                                  const int32_t* inv_pos, const int32_t* plan, const float* topk_w,
+                                  const uint8_t* w2_prep, const float* gw2, void* out, int out_dtype,
+                                  void* stream);
 
 #ifdef __cplusplus
 }

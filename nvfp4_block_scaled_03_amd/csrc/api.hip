@@ -8,6 +8,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/nvfp4_moe.h"
@@ -573,6 +574,69 @@ int grouped_gemm2_combine_w4a16(const nvfp4_moe_dims* d, const uint16_t* a2,
   a.out = out;
   a.out_dtype = out_dtype;
   return launched(nvfp4::launch_gemm2_combine(a, false, S(stream)), W);
+}
+
+// ------------------------------------------------------------------ GEMM2 without allocation
+namespace {
+// Scratch of grouped_gemm2_combine_noalloc: the per-row FP32 down-projection
+// outputs [P][H] that the combine reads, in a file-scope device array (every
+// GPU the library runs on holds its own copy until the process ends).  In
+// host code the array's name is only a stand-in for the symbol: the device
+// address comes from hipGetSymbolAddress, once per device, and only that
+// address is passed to kernels.
+constexpr size_t kNoAllocScratchBytes = size_t(48) << 20;
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(const char* W, float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(NVFP4_ELAUNCH, "%s: ELAUNCH hipGetDevice: %s", W, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(NVFP4_EINVAL, "%s: EINVAL device %d beyond the %d supported", W, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(NVFP4_ELAUNCH, "%s: ELAUNCH hipGetSymbolAddress(scratch): %s", W, hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return NVFP4_OK;
+}
+}  // namespace
+
+size_t grouped_gemm2_combine_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+int grouped_gemm2_combine_noalloc(const nvfp4_moe_dims* d, const uint8_t* a2_q, const uint8_t* a2_sf,
+                                  const uint16_t* a2_deq, const float* g2, const int32_t* expert_offsets,
+                                  const int32_t* inv_pos, const int32_t* plan, const float* topk_w,
+                                  const uint8_t* w2_prep, const float* gw2, void* out, int out_dtype,
+                                  void* stream) {
+  const char* W = "grouped_gemm2_combine_noalloc";
+  if (int r = check_dims(d, W)) return r;
+  const size_t need = grouped_gemm_workspace_size(d);
+  if (need > kNoAllocScratchBytes)
+    return fail(NVFP4_EWORKSPACE, "%s: EWORKSPACE num_experts=%d M=%lld N=%d K=%d needs %zu bytes of "
+                "scratch; the static scratch holds %zu (P * H <= %zu)", W, d->E + d->shared,
+                (long long)pairs(d), d->H, d->I, need, kNoAllocScratchBytes,
+                kNoAllocScratchBytes / sizeof(float));
+  if (d->T == 0) return ok();
+  float* ws = nullptr;
+  if (int r = scratch_of_current_device(W, &ws)) return r;
+  const int r = grouped_gemm2_combine(d, a2_q, a2_sf, a2_deq, g2, expert_offsets, inv_pos, plan, topk_w,
+                                      w2_prep, gw2, out, out_dtype, ws, kNoAllocScratchBytes, stream);
+  if (r != NVFP4_OK) {
+    // name this entry point in the message of the shared path
+    std::string m = g_err;
+    const std::string from = "grouped_gemm2_combine:";
+    if (m.compare(0, from.size(), from) == 0) m = std::string(W) + ":" + m.substr(from.size());
+    g_err = m;
+  }
+  return r;
 }
 
 }  // extern "C"

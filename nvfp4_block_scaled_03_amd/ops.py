@@ -247,6 +247,16 @@ def gemm2_w4a4(d: Dims, a2_q, a2_sf, g2, al: Alignment, topk_w, w: ExpertWeights
     return out
 
 
+def gemm2_w4a4_noalloc(d: Dims, a2_q, a2_sf, g2, al: Alignment, topk_w, w: ExpertWeights,
+                       out: torch.Tensor, a2_deq=None):
+    """grouped_gemm2_combine_noalloc: GEMM2 + combine with the library's
+    static scratch instead of a workspace (``out`` is caller-allocated)."""
+    call("grouped_gemm2_combine_noalloc", ctypes.byref(d), _p(a2_q), _p(a2_sf), _p(a2_deq), _p(g2),
+         _p(al.offsets), _p(al.inv_pos), _p(al.plan), _p(topk_w), _p(w.prep2), _p(w.g2), _p(out),
+         _dtype_code(out), _stream())
+    return out
+
+
 def gemm2_w4a16(d: Dims, a2, al: Alignment, topk_w, w: ExpertWeights, out_dtype=torch.bfloat16,
                 out=None, ws=None):
     dev = a2.device
