@@ -56,3 +56,32 @@ def layer_per_token(x, topk_ids, topk_w, w13_hat, w2_hat, I: int, variant: str =
         if shared_w13 is not None:
             out[t] += mlp(x_hat[t], shared_w13, shared_w2)
     return out
+
+
+def mx_layer_per_token(x, topk_ids, topk_w, w13_hat, w2_hat, I: int, shared_w13=None,
+                       shared_w2=None) -> np.ndarray:
+    """The OCP MXFP4 layer token by token (dense products, FP64, the token's
+    experts in list order); the activation and intermediate are MXFP4
+    quantise-dequantised per token row."""
+    from . import mxfp4
+    x = np.asarray(x, dtype=np.float64)
+    T, H = x.shape
+    ids = np.asarray(topk_ids)
+    wts = np.asarray(topk_w, dtype=np.float64)
+    x_hat = mxfp4.dequantize(*mxfp4.quantize(x))
+    out = np.zeros((T, H))
+
+    def mlp(xv, W13, W2):
+        gate = np.array([np.dot(W13[i], xv) for i in range(I)])
+        up = np.array([np.dot(W13[I + i], xv) for i in range(I)])
+        h = _silu(gate) * up
+        h = mxfp4.dequantize(*mxfp4.quantize(h[None, :]))[0]
+        return np.array([np.dot(W2[r], h) for r in range(H)])
+
+    for t in range(T):
+        for j in range(ids.shape[1]):
+            e = int(ids[t, j])
+            out[t] += wts[t, j] * mlp(x_hat[t], w13_hat[e], w2_hat[e])
+        if shared_w13 is not None:
+            out[t] += mlp(x_hat[t], shared_w13, shared_w2)
+    return out

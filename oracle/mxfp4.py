@@ -71,3 +71,122 @@ def linear(x, w_codes, w_exps) -> np.ndarray:
     """y [M, N] = Q(x) Q(W)^T, x [M, K] quantised to MXFP4 on the fly."""
     xc, xe = quantize(x)
     return dequantize(xc, xe) @ dequantize(w_codes, w_exps).T
+
+
+# --------------------------------------------------------------------------
+# The mixture-of-experts layer in OCP MXFP4.
+# --------------------------------------------------------------------------
+# The emulation backend's OCP MX path runs the MoE experts of MXFP4 models
+# (vLLM PR #35737, "Purpose": TritonExperts for OCP MX emulation).  The
+# reading taken: the NVFP4 layer (oracle.moe.layer, W4A4) with MXFP4 in place
+# of NVFP4 for the activations, the expert weights and the intermediate; all
+# block scales are computed from the tensor itself (dynamic), and since an
+# E8M0 scale spans the whole FP32 range there is no global scale and nothing
+# to calibrate.
+
+
+class MxExpertWeights:
+    """MXFP4 expert weights, quantised on demand from FP32.
+
+    ``src13(e)`` returns the FP32 [2I, H] gate/up weight of expert slot e and
+    ``src2(e)`` the FP32 [H, I] down weight (blocks of 32 along the
+    contraction dimension)."""
+
+    def __init__(self, src13, src2):
+        self._src = {13: src13, 2: src2}
+        self._cache: dict = {}
+
+    @classmethod
+    def from_arrays(cls, w13, w2):
+        w13 = np.asarray(w13, dtype=np.float32)
+        w2 = np.asarray(w2, dtype=np.float32)
+        return cls(lambda e: w13[e], lambda e: w2[e])
+
+    def quantized(self, which: int, e: int):
+        """(codes uint8 [N, K], exponent bytes uint8 [N, K/32])."""
+        key = (which, int(e))
+        if key not in self._cache:
+            self._cache[key] = quantize(np.asarray(self._src[which](int(e)), dtype=np.float32))
+        return self._cache[key]
+
+    def dequantized(self, which: int, e: int) -> np.ndarray:
+        return dequantize(*self.quantized(which, e))
+
+
+def layer(x, topk_ids, topk_w, weights: MxExpertWeights, n_routed: int, I: int, shared: int = 0,
+          tokens=None):
+    """One MXFP4 expert layer (FP64).  Returns a dict with out [T, H], the
+    alignment (offsets, sorted_pair, inv_pos), a1 codes/exponents, the sorted
+    rows computed, h (pre-requantisation), a2 codes/exponents and d."""
+    from . import moe
+    x = np.asarray(x, dtype=np.float64)
+    T, H = x.shape
+    k = np.asarray(topk_ids).shape[1]
+    offsets, sorted_pair, inv_pos = moe.align(topk_ids, n_routed, shared)
+    a1c, a1e = quantize(x)
+    x_hat = dequantize(a1c, a1e)
+    keep = np.ones(T, dtype=bool) if tokens is None else np.isin(np.arange(T), tokens)
+    out = np.zeros((T, H))
+    rows_all, h_all, c_all, e_all, d_all = [], [], [], [], []
+    for e in range(len(offsets) - 1):
+        rows = np.arange(offsets[e], offsets[e + 1])
+        tok, wgt = moe.pair_token_weight(sorted_pair[rows], T, k, topk_w)
+        sel = keep[tok]
+        rows, tok, wgt = rows[sel], tok[sel], wgt[sel]
+        if rows.size == 0:
+            continue
+        h = moe.swiglu(x_hat[tok] @ weights.dequantized(13, e).T, I)
+        a2c, a2e = quantize(h)
+        d = dequantize(a2c, a2e) @ weights.dequantized(2, e).T
+        np.add.at(out, tok, wgt[:, None] * d)
+        rows_all.append(rows)
+        h_all.append(h)
+        c_all.append(a2c)
+        e_all.append(a2e)
+        d_all.append(d)
+
+    def cat(lst, width, dtype=np.float64):
+        return np.concatenate(lst) if lst else np.zeros((0, width), dtype=dtype)
+
+    return {"out": out, "offsets": offsets, "sorted_pair": sorted_pair, "inv_pos": inv_pos,
+            "a1_codes": a1c, "a1_exps": a1e,
+            "rows": np.concatenate(rows_all) if rows_all else np.zeros(0, dtype=np.int64),
+            "h": cat(h_all, I), "a2_codes": cat(c_all, I, np.uint8).astype(np.uint8),
+            "a2_exps": cat(e_all, I // BLOCK, np.uint8).astype(np.uint8), "d": cat(d_all, H)}
+
+
+def down_and_combine(a2_hat, rows, sorted_pair, offsets, topk_w, weights: MxExpertWeights,
+                     T: int, k: int) -> np.ndarray:
+    """The layer's second half from given dequantised intermediate rows."""
+    from . import moe
+    rows = np.asarray(rows, dtype=np.int64)
+    H = weights.dequantized(2, 0).shape[0]
+    out = np.zeros((T, H))
+    expert_of_row = np.searchsorted(offsets, rows, side="right") - 1
+    for e in np.unique(expert_of_row):
+        sel = expert_of_row == e
+        tok, wgt = moe.pair_token_weight(sorted_pair[rows[sel]], T, k, topk_w)
+        np.add.at(out, tok, wgt[:, None] * (a2_hat[sel] @ weights.dequantized(2, int(e)).T))
+    return out
+
+
+def near_tie_mask(x, rel: float = 2.0 ** -12, abs_tol: float = 0.0):
+    """Flags (element_mask [..., K], block_mask [..., K/32]) where an input
+    carrying accumulation error may legitimately round the other way: a block
+    whose amax lies within rel * b + abs_tol of a power of two b (where
+    floor(log2 amax), hence the exponent byte, changes), an element whose |x|
+    lies that close to t * X for an E2M1 midpoint t and the block scale X."""
+    x = np.asarray(x, dtype=np.float64)
+    K = x.shape[-1]
+    blocks = np.abs(x.reshape(*x.shape[:-1], K // BLOCK, BLOCK))
+    amax = blocks.max(axis=-1)
+    _, fe = np.frexp(np.where(amax > 0, amax, 1.0))
+    lo = np.ldexp(1.0, fe - 1)                     # power of two at or below amax
+    hi = 2.0 * lo
+    d = np.minimum(np.abs(amax - lo) - rel * lo, np.abs(hi - amax) - rel * hi)
+    block_flag = (amax > 0) & (d <= abs_tol)
+    X = np.ldexp(1.0, block_exponents(x).astype(np.int64) - E8M0_BIAS)[..., None, None]
+    b2 = X * nvfp4._midpoints(nvfp4.E2M1_MAGS)     # [..., K/32, 1, 7]
+    de = np.min(np.abs(blocks[..., None] - b2) - rel * b2, axis=-1)
+    elem_flag = (de <= abs_tol).reshape(x.shape)
+    return elem_flag, block_flag

@@ -166,3 +166,33 @@ def check_a2_bf16(gpu_bits: np.ndarray, h: np.ndarray, max_rate=BF16_MAX_RATE, w
     _record(what, "bf16", n_diff, h.size, n_diff)
     assert n_diff <= max(2, max_rate * h.size), f"too many bf16 differences: {n_diff} of {h.size}"
     return got
+
+
+def check_a2_mx(gpu_q: np.ndarray, gpu_e: np.ndarray, h: np.ndarray, max_rate=NVFP4_MAX_RATE, rel=REL,
+                what="") -> A2Check:
+    """GPU MXFP4 a2 bytes (rows x I/2 codes, rows x I/32 exponents) against
+    the oracle's FP64 h, on the same terms as check_a2_nvfp4: exact except
+    at positions the oracle flags as near ties (an exponent byte off by one
+    where the block amax lies next to a power of two; a neighbouring element
+    code where |h| lies next to a rounding boundary)."""
+    from oracle import mxfp4 as omx
+    ref_codes, ref_e = omx.quantize(h)
+    got_codes = onv.unpack_codes(gpu_q)
+    elem_flag, block_flag = omx.near_tie_mask(h, rel, abs_tol=ABS_FRAC * rms(h))
+    e_diff = gpu_e != ref_e
+    bad_e = e_diff & ~(block_flag & (np.abs(gpu_e.astype(int) - ref_e.astype(int)) == 1))
+    assert not bad_e.any(), f"exponent bytes differ outside near ties at {np.argwhere(bad_e)[:5]}"
+    exp_codes = omx.encode(h, gpu_e)
+    zero_mag = ((got_codes & 7) == 0) & ((exp_codes & 7) == 0)
+    cd = (got_codes != exp_codes) & ~zero_mag
+    mag_step = np.abs((got_codes & 7).astype(int) - (exp_codes & 7).astype(int))
+    same_sign = (got_codes & 8) == (exp_codes & 8)
+    bad = cd & ~(elem_flag & (mag_step <= 1) & same_sign)
+    assert not bad.any(), (f"codes differ outside near ties: {bad.sum()} at {np.argwhere(bad)[:5]} "
+                           f"got {got_codes[bad][:5]} want {exp_codes[bad][:5]}")
+    n_cd, n_e = int(cd.sum()), int(e_diff.sum())
+    _record(what, "mxfp4 codes", n_cd, h.size, elem_flag.sum())
+    _record(what, "mxfp4 exponents", n_e, gpu_e.size, block_flag.sum())
+    assert n_cd + n_e <= max(2, max_rate * h.size), f"too many near-tie flips: {n_cd} codes, {n_e} exponents"
+    exact = bool(np.array_equal(got_codes, ref_codes) and np.array_equal(gpu_e, ref_e))
+    return A2Check(got_codes, gpu_e.copy(), exact, n_cd + n_e, n_cd / max(1, h.size), n_e / max(1, gpu_e.size))
