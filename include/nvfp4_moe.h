@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_MOE_ABI_VERSION 6
+#define NVFP4_MOE_ABI_VERSION 7
 
 /* Status codes. */
 #define NVFP4_OK 0
@@ -385,6 +385,43 @@ int grouped_gemm2_combine_w4a16(const nvfp4_moe_dims* dims, const uint16_t* a2,
                                 const int32_t* expert_offsets, const int32_t* inv_pos,
                                 const int32_t* plan, const float* topk_w, const uint8_t* w2_prep,
                                 const float* gw2, void* out, int out_dtype, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Mixture-of-experts layer in OCP MXFP4 (grouped GEMMs on the scaled FP4      */
+/* matrix instruction).                                                       */
+/* ------------------------------------------------------------------------ */
+/* The emulation backend's OCP MX path runs the experts of MXFP4 models (vLLM
+ * PR #35737, "Purpose"); here the same layer as the NVFP4 W4A4 path with
+ * MXFP4 (E2M1 codes, one E8M0 exponent byte per 32 elements, no global scale,
+ * the rules of mxfp4_quantize) for the activations, the expert weights and
+ * the intermediate.  The block scales are powers of two per 32, exactly what
+ * CDNA4's scaled FP4 matrix instruction takes, so codes are multiplied as
+ * stored.  The layer:
+ *   mxfp4_quantize(x)                 a1: codes [T][H/2], exponents [T][H/32]
+ *   moe_align(dims, topk_ids, ...)    the permutation and tile plan
+ *   grouped_gemm1_swiglu_mxfp4        per row p of expert e (token t):
+ *                                     h = silu(c[0:I]) * c[I:2I],
+ *                                     c = a1_hat[t] . w13_hat[e]^T (FP32),
+ *                                     a2 row p = MXFP4(h) (block scale from h)
+ *   grouped_gemm2_combine_mxfp4       d[p] = a2_hat[p] . w2_hat[e]^T, then
+ *                                     out as grouped_gemm2_combine.
+ * Expert weights (canonical MXFP4, q [S][N][K/2], ex [S][N][K/32], S = E +
+ * shared; which = 13: [2I][H] rows [0, I) gate, [I, 2I) up; which = 2:
+ * [H][I]) are rearranged offline by mxfp4_prep_expert_weights into prep
+ * (mxfp4_prep_expert_weights_size bytes, 16-byte aligned, opaque).
+ * a1_q/a2_q must be 16-byte and a1_e/a2_e 4-byte aligned; T*H/2, P*I/2 and
+ * I*H must stay below 2^31 (ESHAPE otherwise).  ws: grouped_gemm_workspace_size
+ * bytes (the FP32 rows the combine reads). */
+size_t mxfp4_prep_expert_weights_size(const nvfp4_moe_dims* dims, int which);
+int mxfp4_prep_expert_weights(const nvfp4_moe_dims* dims, int which, const uint8_t* q, const uint8_t* ex,
+                              uint8_t* prep, void* stream);
+int grouped_gemm1_swiglu_mxfp4(const nvfp4_moe_dims* dims, const uint8_t* a1_q, const uint8_t* a1_e,
+                               const int32_t* sorted_pair, const int32_t* expert_offsets, const int32_t* plan,
+                               const uint8_t* w13_prep, uint8_t* a2_q, uint8_t* a2_e, void* stream);
+int grouped_gemm2_combine_mxfp4(const nvfp4_moe_dims* dims, const uint8_t* a2_q, const uint8_t* a2_e,
+                                const int32_t* expert_offsets, const int32_t* inv_pos, const int32_t* plan,
+                                const float* topk_w, const uint8_t* w2_prep, void* out, int out_dtype, void* ws,
                                 size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */

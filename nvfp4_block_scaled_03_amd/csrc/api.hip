@@ -505,7 +505,7 @@ int grouped_gemm1_swiglu_w4a16(const nvfp4_moe_dims* d, const uint16_t* x,
 static int gemm2_common(const char* W, const nvfp4_moe_dims* d, const int32_t* expert_offsets,
                         const int32_t* inv_pos, const int32_t* plan, const float* topk_w,
                         const uint8_t* w2_prep, const float* gw2, void* out, int out_dtype,
-                        void* ws, size_t ws_bytes) {
+                        void* ws, size_t ws_bytes, bool need_gw = true) {
   if (int r = check_dims(d, W)) return r;
   if (out_dtype != NVFP4_BF16 && out_dtype != NVFP4_F32)
     return fail(NVFP4_EINVAL, "%s: EINVAL out_dtype=%d", W, out_dtype);
@@ -514,7 +514,7 @@ static int gemm2_common(const char* W, const nvfp4_moe_dims* d, const int32_t* e
   if (ws_bytes < need || !ws)
     return fail(NVFP4_EWORKSPACE, "%s: EWORKSPACE num_experts=%d M=%lld N=%d K=%d workspace_size=%zu "
                 "needed=%zu", W, d->E + d->shared, (long long)pairs(d), d->H, d->I, ws_bytes, need);
-  if (!expert_offsets || !inv_pos || !plan || !topk_w || !w2_prep || !gw2 || !out ||
+  if (!expert_offsets || !inv_pos || !plan || !topk_w || !w2_prep || (need_gw && !gw2) || !out ||
       !aligned(w2_prep, 16) || !aligned(ws, 16) || !aligned(out, out_dtype == NVFP4_F32 ? 16 : 8))
     return gemm_fail_shape(W, d, d->H, d->I, ws_bytes);
   return NVFP4_OK;
@@ -574,6 +574,96 @@ int grouped_gemm2_combine_w4a16(const nvfp4_moe_dims* d, const uint16_t* a2,
   a.out = out;
   a.out_dtype = out_dtype;
   return launched(nvfp4::launch_gemm2_combine(a, false, S(stream)), W);
+}
+
+// ------------------------------------------------------------------ MXFP4 layer
+size_t mxfp4_prep_expert_weights_size(const nvfp4_moe_dims* d, int which) {
+  if (check_dims(d, "mxfp4_prep_expert_weights_size") || (which != 13 && which != 2)) return 0;
+  const int64_t slots = d->E + d->shared;
+  return which == 13 ? nvfp4::mx_expert_prep_bytes(slots, 2 * (int64_t)d->I, d->H)
+                     : nvfp4::mx_expert_prep_bytes(slots, d->H, d->I);
+}
+
+int mxfp4_prep_expert_weights(const nvfp4_moe_dims* d, int which, const uint8_t* q, const uint8_t* ex,
+                              uint8_t* prep, void* stream) {
+  const char* W = "mxfp4_prep_expert_weights";
+  if (int r = check_dims(d, W)) return r;
+  if (which != 13 && which != 2) return fail(NVFP4_EINVAL, "%s: EINVAL which=%d (13 or 2)", W, which);
+  if (!q || !ex || !prep) return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
+  if (!aligned(q, 16) || !aligned(prep, 16))
+    return fail(NVFP4_EINVAL, "%s: EINVAL q and prep must be 16-byte aligned", W);
+  const int64_t slots = d->E + d->shared;
+  const int64_t N = which == 13 ? 2 * (int64_t)d->I : d->H;
+  const int64_t K = which == 13 ? d->H : d->I;
+  return launched(nvfp4::launch_mx_expert_prep(slots, N, K, which == 13 ? d->I : 0, q, ex, prep, S(stream)), W);
+}
+
+namespace {
+nvfp4::MxGemmArgs mx_args(const nvfp4_moe_dims* d) {
+  nvfp4::MxGemmArgs a{};
+  a.T = d->T;
+  a.topk = d->topk;
+  a.E = d->E;
+  a.shared = d->shared;
+  a.H = d->H;
+  a.I = d->I;
+  return a;
+}
+// Byte offsets of the activation operands travel as 32-bit values.
+bool mx_offsets_fit(const nvfp4_moe_dims* d) {
+  const int64_t P = pairs(d);
+  return (int64_t)d->T * d->H / 2 < (int64_t(1) << 31) && P * d->I / 2 < (int64_t(1) << 31) &&
+         (int64_t)2 * d->I * d->H / 2 < (int64_t(1) << 31);
+}
+}  // namespace
+
+int grouped_gemm1_swiglu_mxfp4(const nvfp4_moe_dims* d, const uint8_t* a1_q, const uint8_t* a1_e,
+                               const int32_t* sorted_pair, const int32_t* expert_offsets, const int32_t* plan,
+                               const uint8_t* w13_prep, uint8_t* a2_q, uint8_t* a2_e, void* stream) {
+  const char* W = "grouped_gemm1_swiglu_mxfp4";
+  if (int r = check_dims(d, W)) return r;
+  if (!mx_offsets_fit(d))
+    return fail(NVFP4_ESHAPE, "%s: ESHAPE num_experts=%d M=%lld N=%d K=%d (operand offsets must fit 31 bits)", W,
+                d->E + d->shared, (long long)pairs(d), 2 * d->I, d->H);
+  if (d->T == 0) return ok();
+  if (!a1_q || !a1_e || !sorted_pair || !expert_offsets || !plan || !w13_prep || !a2_q || !a2_e ||
+      !aligned(a1_q, 16) || !aligned(a1_e, 4) || !aligned(w13_prep, 16))
+    return gemm_fail_shape(W, d, 2 * d->I, d->H, 0);
+  nvfp4::MxGemmArgs a = mx_args(d);
+  a.sorted_pair = sorted_pair;
+  a.plan = plan;
+  a.a_q = a1_q;
+  a.a_e = a1_e;
+  a.w_prep = w13_prep;
+  a.out_q = a2_q;
+  a.out_e = a2_e;
+  return launched(nvfp4::launch_mx_gemm1_swiglu(a, S(stream)), W);
+}
+
+int grouped_gemm2_combine_mxfp4(const nvfp4_moe_dims* d, const uint8_t* a2_q, const uint8_t* a2_e,
+                                const int32_t* expert_offsets, const int32_t* inv_pos, const int32_t* plan,
+                                const float* topk_w, const uint8_t* w2_prep, void* out, int out_dtype, void* ws,
+                                size_t ws_bytes, void* stream) {
+  const char* W = "grouped_gemm2_combine_mxfp4";
+  if (int r = gemm2_common(W, d, expert_offsets, inv_pos, plan, topk_w, w2_prep, nullptr, out, out_dtype, ws,
+                           ws_bytes, false))
+    return r;
+  if (!mx_offsets_fit(d))
+    return fail(NVFP4_ESHAPE, "%s: ESHAPE num_experts=%d M=%lld N=%d K=%d (operand offsets must fit 31 bits)", W,
+                d->E + d->shared, (long long)pairs(d), d->H, d->I);
+  if (d->T == 0) return ok();
+  if (!a2_q || !a2_e || !aligned(a2_q, 16) || !aligned(a2_e, 4)) return gemm_fail_shape(W, d, d->H, d->I, ws_bytes);
+  nvfp4::MxGemmArgs a = mx_args(d);
+  a.inv_pos = inv_pos;
+  a.plan = plan;
+  a.topk_w = topk_w;
+  a.a_q = a2_q;
+  a.a_e = a2_e;
+  a.w_prep = w2_prep;
+  a.d_ws = static_cast<float*>(ws);
+  a.out = out;
+  a.out_dtype = out_dtype;
+  return launched(nvfp4::launch_mx_gemm2_combine(a, S(stream)), W);
 }
 
 // ------------------------------------------------------------------ GEMM2 without allocation

@@ -257,6 +257,20 @@ __device__ __forceinline__ float global_scale_of_amax(float amax) {
   return (float)((double)amax / 2688.0);
 }
 
+// Load of a value that is the same for the whole wavefront and not written
+// by the running kernel, through the scalar data cache (read-only use).  Its
+// wait uses the scalar counter, so it never drains outstanding vector loads.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* ptr) {
+  return *(const __attribute__((address_space(4))) T*)ptr;
+}
+
+// silu(z) = z / (1 + e^-z), with the hardware reciprocal (1 ulp) in place of
+// an IEEE division.
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
 // Token of pair f: routed pairs are f = t*topk + j, shared pairs f = T*topk + t.
 __device__ __forceinline__ int pair_token(int f, int T, int topk) {
   const int tk = T * topk;

@@ -67,13 +67,6 @@ enum Act { kActCodes = 0, kActF16 = 1, kActBf16 = 2 };
 enum Epi { kEpiSwigluFp4 = 0, kEpiSwigluBf16 = 1, kEpiStoreF32 = 2, kEpiStoreBf16 = 3 };
 constexpr bool swiglu_epi(int e) { return e == kEpiSwigluFp4 || e == kEpiSwigluBf16; }
 
-// Load of a value that is the same for the whole wavefront and not written
-// by the running kernel, through the scalar data cache (read-only use).  Its
-// wait uses the scalar counter, so it never drains outstanding vector loads.
-template <typename T>
-__device__ __forceinline__ T ld_uniform(const T* ptr) {
-  return *(const __attribute__((address_space(4))) T*)ptr;
-}
 
 struct KParams {
   int T, topk, I, N, K;
@@ -104,11 +97,6 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
   return x * q + min(x, r) + idx;
 }
 
-// silu(z) = z / (1 + e^-z), with the hardware reciprocal (1 ulp) in place of
-// an IEEE division.
-__device__ __forceinline__ float silu_fast(float z) {
-  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
-}
 
 // Value of an E2M1 magnitude code 0..7: {0, .5, 1, 1.5, 2, 3, 4, 6}.
 __device__ __forceinline__ float e2m1_mag_value(uint32_t m) {
@@ -1342,14 +1330,6 @@ __global__ __launch_bounds__(4 * kWave) void linear_splitk_kernel(KParams p) {
   (void)NT;
 }
 
-// Tile height from the mean rows per expert (host side, from dims only).
-int pick_list(int64_t P, int slots) {
-  const int64_t avg = P / (slots > 0 ? slots : 1);
-  if (avg <= 16) return 0;
-  if (avg <= 40) return 1;
-  if (avg <= 96) return 2;
-  return 3;
-}
 
 // Whether short experts and tall ones run on different kernels: short tiles
 // on average (the streaming regime) while one expert may still hold more
@@ -1471,6 +1451,15 @@ KParams base_params(const GemmArgs& a) {
 
 }  // namespace
 
+// Tile height from the mean rows per expert (host side, from dims only).
+int pick_list(int64_t P, int slots) {
+  const int64_t avg = P / (slots > 0 ? slots : 1);
+  if (avg <= 16) return 0;
+  if (avg <= 40) return 1;
+  if (avg <= 96) return 2;
+  return 3;
+}
+
 bool prefers_decoded(int T, int topk, int E, int shared) {
   const AlignShape al = align_shape(T, topk, E, shared);
   return min(pick_list(al.P, al.slots), 3) >= NVFP4_WIDE_MIN_LIST || split_experts(al);
@@ -1546,6 +1535,17 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
   return f32 ? launch_gemm<kActCodes, kEpiStoreF32>(k, al, s) : launch_gemm<kActCodes, kEpiStoreBf16>(k, al, s);
 }
 
+hipError_t launch_combine(const float* d, const int32_t* inv_pos, const float* topk_w, int T, int topk,
+                          int shared, int H, void* out, int out_dtype, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const dim3 cgrid(T, (H + 1023) / 1024);
+  if (out_dtype == 0)
+    combine_kernel<true><<<cgrid, 256, 0, s>>>(d, inv_pos, topk_w, T, topk, shared, H, out);
+  else
+    combine_kernel<false><<<cgrid, 256, 0, s>>>(d, inv_pos, topk_w, T, topk, shared, H, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm2_combine(const GemmArgs& a, bool w4a4, hipStream_t s) {
   const AlignShape al = align_shape(a.T, a.topk, a.E, a.shared);
   KParams k = base_params(a);
@@ -1569,13 +1569,7 @@ hipError_t launch_gemm2_combine(const GemmArgs& a, bool w4a4, hipStream_t s) {
     e = launch_gemm<kActBf16, kEpiStoreF32>(k, al, s);
   }
   if (e != hipSuccess) return e;
-  if (a.T == 0) return hipSuccess;
-  const dim3 cgrid(a.T, (a.H + 1023) / 1024);
-  if (a.out_dtype == 0)
-    combine_kernel<true><<<cgrid, 256, 0, s>>>(a.d_ws, a.inv_pos, a.topk_w, a.T, a.topk, a.shared, a.H, a.out);
-  else
-    combine_kernel<false><<<cgrid, 256, 0, s>>>(a.d_ws, a.inv_pos, a.topk_w, a.T, a.topk, a.shared, a.H, a.out);
-  return hipGetLastError();
+  return launch_combine(a.d_ws, a.inv_pos, a.topk_w, a.T, a.topk, a.shared, a.H, a.out, a.out_dtype, s);
 }
 
 }  // namespace nvfp4

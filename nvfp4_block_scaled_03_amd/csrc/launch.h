@@ -121,6 +121,12 @@ hipError_t launch_gemm1(const GemmArgs& a, bool w4a4, hipStream_t s);
 // on the codes for these dimensions (the wide 128-row-tile kernel).
 bool prefers_decoded(int T, int topk, int E, int shared);
 hipError_t launch_gemm2_combine(const GemmArgs& a, bool w4a4, hipStream_t s);
+// out[t] = sum_j topk_w[t][j] * d[inv_pos[t*topk + j]] (+ the shared row),
+// FP32 in j order, rows with inv_pos < 0 skipped; out bf16 (0) or f32 (1).
+hipError_t launch_combine(const float* d, const int32_t* inv_pos, const float* topk_w, int T, int topk,
+                          int shared, int H, void* out, int out_dtype, hipStream_t s);
+// Tile list (0..3: 16, 32, 64, 128 rows) chosen from the mean rows per expert.
+int pick_list(int64_t P, int slots);
 
 // Dense linear y [M][N] = x [M][K] W^T on the grouped-GEMM kernels with one
 // expert (plan from an alignment of M pairs to expert 0).

@@ -23,4 +23,30 @@ hipError_t launch_mx_prep(int64_t N, int64_t K, const uint8_t* q, const uint8_t*
 hipError_t launch_mx_gemm(const uint8_t* a_q, const uint8_t* a_e, int64_t M, int64_t N, int64_t K,
                           const uint8_t* w_prep, void* out, int out_dtype, hipStream_t s);
 
+// Mixture-of-experts layer in MXFP4: expert weights prepared per slot
+// (interleave_I = I for the gate/up weights: column tiles alternate gate and
+// up), GEMM1 with SwiGLU and MXFP4 requantisation of h, GEMM2 into the FP32
+// per-row workspace followed by the combine.  Activations in the canonical
+// MXFP4 layout (codes [rows][K/2], exponent bytes [rows][K/32]).
+size_t mx_expert_prep_bytes(int64_t slots, int64_t N, int64_t K);
+hipError_t launch_mx_expert_prep(int64_t slots, int64_t N, int64_t K, int interleave_I, const uint8_t* q,
+                                 const uint8_t* ex, uint8_t* prep, hipStream_t s);
+struct MxGemmArgs {
+  int T, topk, E, shared, H, I;
+  const int32_t* sorted_pair;   // GEMM1
+  const int32_t* inv_pos;       // combine
+  const int32_t* plan;
+  const float* topk_w;
+  const uint8_t* a_q;           // a1 (GEMM1) or a2 (GEMM2) codes
+  const uint8_t* a_e;           // and exponent bytes
+  const uint8_t* w_prep;
+  uint8_t* out_q;               // GEMM1: a2
+  uint8_t* out_e;
+  float* d_ws;                  // GEMM2: FP32 [P][H]
+  void* out;
+  int out_dtype;
+};
+hipError_t launch_mx_gemm1_swiglu(const MxGemmArgs& a, hipStream_t s);
+hipError_t launch_mx_gemm2_combine(const MxGemmArgs& a, hipStream_t s);
+
 }  // namespace nvfp4

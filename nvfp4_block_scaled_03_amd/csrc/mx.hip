@@ -7,7 +7,10 @@
 // the emulation backend's other format, vLLM PR #35737): scale
 // 2^(floor(log2 amax) - 2), elements rounded to the nearest E2M1 value of
 // v / scale (exact), ties to the even code, saturating at 6.
+#include <algorithm>
+
 #include "common.h"
+#include "launch.h"
 #include "mx.h"
 #include "quant.h"
 
@@ -408,6 +411,253 @@ hipError_t launch_mx_gemm_ring(const uint8_t* a_q, const uint8_t* a_e, int64_t M
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Mixture-of-experts layer in OCP MXFP4 (the emulation backend's other block
+// format, vLLM PR #35737, "Purpose"): grouped GEMMs on the scaled FP4 matrix
+// instruction, tiles from the alignment plan of moe_align.
+//
+// Expert weights: one dense prepared matrix per expert slot (codes
+// [N/16][K/128][64 lanes][16 B], then scale words [N/64][K/128][64 lanes]
+// [4 B]), experts one after the other.  For the gate/up weights the column
+// tiles alternate gate and up: tile 2 q holds gate rows [16 q, 16 q + 16),
+// tile 2 q + 1 the matching up rows, so that a wavefront's 64 columns are the
+// gate and up halves of 32 columns of h -- one MX block of the intermediate.
+__global__ __launch_bounds__(256) void mx_expert_prep_kernel(int64_t N, int64_t K, int interleave_I,
+                                                             const uint8_t* __restrict__ q,
+                                                             const uint8_t* __restrict__ ex,
+                                                             uint8_t* __restrict__ prep) {
+  const int64_t KC = K / 128, NT = N / 16, e = blockIdx.y;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= NT * KC * 64) return;
+  const int64_t lane = i & 63, rest = i >> 6;
+  const int64_t kc = rest % KC, nt = rest / KC;
+  const int64_t tile_row = interleave_I ? ((nt & 1) ? interleave_I + 16 * (nt >> 1) : 16 * (nt >> 1)) : nt * 16;
+  const int64_t n = tile_row + (lane & 15), g = lane >> 4;
+  const uint8_t* qe = q + e * N * (K / 2);
+  const uint8_t* xe = ex + e * N * (K / 32);
+  uint8_t* pe = prep + e * (N * (K / 2) + N * (K / 32));
+  *reinterpret_cast<u32x4*>(pe + i * 16) = *reinterpret_cast<const u32x4*>(qe + n * (K / 2) + kc * 64 + 16 * g);
+  pe[N * (K / 2) + ((nt >> 2) * KC + kc) * 256 + lane * 4 + (nt & 3)] = xe[n * (K / 32) + kc * 4 + g];
+}
+
+enum MxEpi { kMxSwiglu = 0, kMxStoreF32 = 1 };
+
+struct MxMoeParams {
+  int T, topk, N, K, I, list_idx, n_blocks;
+  const int32_t* plan;
+  const int32_t* sorted_pair;   // GEMM1: row -> pair (activation row = its token); GEMM2: null
+  const uint8_t* a_q;           // canonical codes [rows][K/2]
+  const uint8_t* a_e;           // canonical exponent bytes [rows][K/32]
+  const uint8_t* w_prep;        // experts' prepared weights
+  int64_t w_expert_bytes;
+  uint8_t* out_q;               // GEMM1: a2 codes [P][I/2]
+  uint8_t* out_e;               // GEMM1: a2 exponent bytes [P][I/32]
+  float* out_f32;               // GEMM2: d [P][N]
+};
+
+// Stage of the LDS ring: MT activation tiles (1 KiB: lane 16 g + m holds row
+// m's codes k in [32 g, 32 g + 32) of the chunk), MT words runs (256 B:
+// lane l's 4 exponent bytes of row l % 16 for the chunk's 4 blocks), 16
+// weight tiles (1 KiB each, the streaming layout) and 4 weight scale runs.
+template <int MT>
+struct MxMoeRing {
+  static constexpr int A = 0, Ae = 1024 * MT, B = Ae + 256 * MT, Bs = B + 16384, Slot = Bs + 1024;
+  static constexpr int D = MT == 4 ? 3 : 4;                       // stages (LDS: 2 workgroups per CU up to MT 4)
+  // activation tiles issued by wavefront w: w, w + 4, ... (< MT)
+  static constexpr int a_per_wave(int w) { return MT >= 4 ? MT / 4 : (w < MT ? 1 : 0); }
+  static constexpr int loads(int w) { return 2 * a_per_wave(w) + 4 + 1; }
+};
+
+template <int MT, int EPI>
+__global__ __launch_bounds__(256) void grouped_mx_kernel(MxMoeParams p) {
+  using R = MxMoeRing<MT>;
+  constexpr int D = R::D, NTW = 4;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[D * R::Slot];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Tile of the plan list (consecutive work items on one XCD).
+  const int ntiles = ld_uniform(p.plan + p.list_idx);
+  const int G = ntiles * p.n_blocks;
+  if ((int)blockIdx.x >= G) return;
+  int v;
+  {
+    const int q = G >> 3, r = G & 7, x = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    v = x * q + min(x, r) + idx;
+  }
+  const int tile = v / p.n_blocks, nb = v - tile * p.n_blocks;
+  const int* ent = p.plan + ld_uniform(p.plan + kPlanLists + p.list_idx) + 2 * tile;
+  const int e = ld_uniform(ent) & 2047;
+  const uint32_t rr = (uint32_t)ld_uniform(ent + 1);
+  const int row0 = (int)(rr & 0xFFFFFFu), nrows = (int)(rr >> 24);
+  const int K = p.K, KC = K / 128, N = p.N, NT = N / 16;
+  const int nt_wave = nb * 16 + wv * 4;                 // first column tile of this wavefront
+  const bool wave_on = nt_wave * 16 < N;
+  const int m = lane & 15, g = lane >> 4;
+
+  // Per-lane source offsets (chunk 0).  Rows past the tile end repeat its
+  // last valid row (loaded, never stored); column tiles past N repeat the
+  // last group of four.
+  constexpr int AW = MT >= 4 ? MT / 4 : 1;
+  uint32_t va[AW], vae[AW];
+#pragma unroll
+  for (int u = 0; u < AW; ++u) {
+    const int i = MT >= 4 ? wv + 4 * u : wv;            // activation tile this lane loads
+    int r = row0 + min(16 * min(i, MT - 1) + m, nrows - 1);
+    if (p.sorted_pair) r = pair_token(p.sorted_pair[r], p.T, p.topk);
+    va[u] = (uint32_t)r * (uint32_t)(K / 2) + (uint32_t)(16 * g);
+    vae[u] = (uint32_t)r * (uint32_t)(K / 32);
+  }
+  const uint8_t* wq = p.w_prep + (int64_t)e * p.w_expert_bytes;
+  const uint8_t* ws = wq + (int64_t)N * (K / 2);
+  uint32_t vb[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    const int nt = min(nt_wave + t, NT - 4 + t);
+    vb[t] = (uint32_t)((nt * KC) * 64 + lane) * 16u;
+  }
+  const uint32_t vbs = (uint32_t)((min(nt_wave, NT - 4) / 4 * KC) * 64 + lane) * 4u;
+  const uint32_t ring0 = (uint32_t)(uintptr_t)ring;
+
+  // Issue chunk kc (clamped to the last) into ring slot `slot`: direct loads
+  // (assembly, see mx_gemm_kernel), awaited with explicit vmcnt waits.
+  auto issue = [&](int kc, int slot) {
+    kc = min(kc, KC - 1);
+    const uint32_t base = ring0 + (uint32_t)slot * R::Slot;
+    if (R::a_per_wave(wv) > 0) {
+#pragma unroll
+      for (int u = 0; u < AW; ++u) {
+        const int i = MT >= 4 ? wv + 4 * u : wv;
+        asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(va[u] + (uint32_t)kc * 64u), "s"(p.a_q),
+                     "{m0}"(base + R::A + i * 1024) : "memory");
+        asm volatile("global_load_lds_dword %0, %1" : : "v"(vae[u] + (uint32_t)kc * 4u), "s"(p.a_e),
+                     "{m0}"(base + R::Ae + i * 256) : "memory");
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+      asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(vb[t] + (uint32_t)kc * 1024u), "s"(wq),
+                   "{m0}"(base + R::B + (wv * NTW + t) * 1024) : "memory");
+    asm volatile("global_load_lds_dword %0, %1" : : "v"(vbs + (uint32_t)kc * 256u), "s"(ws),
+                 "{m0}"(base + R::Bs + wv * 256) : "memory");
+  };
+
+  f32x4 acc[MT][NTW];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int slot) {
+    const uint8_t* st = ring + slot * R::Slot;
+    u32x4 b[NTW];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) b[j] = *reinterpret_cast<const u32x4*>(st + R::B + (wv * NTW + j) * 1024 + lane * 16);
+    const uint32_t bsw = *reinterpret_cast<const uint32_t*>(st + R::Bs + wv * 256 + lane * 4);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(st + R::A + i * 1024 + lane * 16);
+      // lane l holds the 4 exponent bytes of row l % 16; its operand's block is g
+      const uint32_t aw = *reinterpret_cast<const uint32_t*>(st + R::Ae + i * 256 + lane * 4);
+      const int as = (int)((aw >> (8 * g)) & 0xFFu);
+      const v8i av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const v8i bv = {(int)b[j][0], (int)b[j][1], (int)b[j][2], (int)b[j][3], 0, 0, 0, 0};
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[i][j], 4, 4, 0, as, 0,
+                                                                    (int)((bsw >> (8 * j)) & 0xFFu));
+      }
+    }
+  };
+  auto wait_ring = [&]() {
+    // at most (D - 2) chunks' loads of this wavefront still in flight
+    if (R::a_per_wave(wv) > 0) __builtin_amdgcn_s_waitcnt(mx_vmcnt((D - 2) * R::loads(0)));
+    else __builtin_amdgcn_s_waitcnt(mx_vmcnt((D - 2) * R::loads(3)));
+  };
+#pragma unroll
+  for (int c = 0; c < D - 1; ++c) issue(c, c);
+  for (int c0 = 0; c0 < KC; c0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (c0 + d < KC) {
+        wait_ring();
+        __syncthreads();
+        issue(c0 + d + D - 1, (d + D - 1) % D);
+        compute(d);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(mx_vmcnt(0));
+  if (!wave_on) return;
+
+  const int fr = lane & 15, fg = lane >> 4;
+  if constexpr (EPI == kMxStoreF32) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = i * 16 + fg * 4 + r;
+          if (row < nrows)
+            p.out_f32[(int64_t)(row0 + row) * N + (nt_wave + j) * 16 + fr] = acc[i][j][r];
+        }
+  } else {
+    // Tiles (gate, up, gate, up): h columns 32 w + fr and 32 w + 16 + fr of
+    // MX block w; a row's 32 values sit on the 16 lanes of one DPP row.
+    const int w = nt_wave >> 2;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float h0 = silu_fast(acc[i][0][r]) * acc[i][1][r];
+        const float h1 = silu_fast(acc[i][2][r]) * acc[i][3][r];
+        const float am = row16_max(fmaxf(fabsf(h0), fabsf(h1)));
+        // floor(log2 am) - 2 + 127, clamped (E8M0); 0 for an all-zero block
+        const int code = am > 0.0f ? min(max(__builtin_amdgcn_frexp_expf(am) - 1 - 2 + 127, 0), 254) : 0;
+        const int sh = 127 - code;
+        uint32_t c[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float hv = u == 0 ? h0 : h1;
+          const float a = fabsf(__builtin_ldexpf(hv, sh));   // exact: a power-of-two scaling
+          const uint32_t mag = (uint32_t)(a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+                               (a >= 3.5f) + (a > 5.0f);
+          c[u] = (((uint32_t)__float_as_int(hv) >> 28) & 8u) | mag;
+        }
+        const uint32_t o0 = (uint32_t)dpp_xor1_i((int)c[0]), o1 = (uint32_t)dpp_xor1_i((int)c[1]);
+        const int row = i * 16 + fg * 4 + r;
+        if (row < nrows) {
+          const int64_t pr = row0 + row;
+          if ((fr & 1) == 0) {
+            p.out_q[pr * (p.I >> 1) + (32 * w + fr) / 2] = (uint8_t)(c[0] | (o0 << 4));
+            p.out_q[pr * (p.I >> 1) + (32 * w + 16 + fr) / 2] = (uint8_t)(c[1] | (o1 << 4));
+          }
+          if (fr == 0) p.out_e[pr * (p.I >> 5) + w] = (uint8_t)code;
+        }
+      }
+  }
+}
+
+template <int MT, int EPI>
+hipError_t launch_grouped_mx_t(MxMoeParams p, int64_t list_len, hipStream_t s) {
+  const int64_t G = list_len * p.n_blocks;
+  const unsigned grid = (unsigned)std::max<int64_t>(8, (G + 7) / 8 * 8);
+  grouped_mx_kernel<MT, EPI><<<grid, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_grouped_mx(MxMoeParams p, const AlignShape& al, hipStream_t s) {
+  const int li = pick_list(al.P, al.slots);
+  p.list_idx = li;
+  p.n_blocks = (p.N + 255) / 256;
+  switch (li) {
+    case 0: return launch_grouped_mx_t<1, EPI>(p, al.list_len[0], s);
+    case 1: return launch_grouped_mx_t<2, EPI>(p, al.list_len[1], s);
+    case 2: return launch_grouped_mx_t<4, EPI>(p, al.list_len[2], s);
+    default: return launch_grouped_mx_t<8, EPI>(p, al.list_len[3], s);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_mx_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx, uint8_t* q,
@@ -451,6 +701,61 @@ hipError_t launch_mx_gemm(const uint8_t* a_q, const uint8_t* a_e, int64_t M, int
   // up to 128 rows: one 128-row tile (4 wavefronts); more: 256-row tiles
   if (M <= 128) return launch_mx_gemm_ring<1>(a_q, a_e, M, N, K, w_prep, out, out_dtype, s);
   return launch_mx_gemm_ring<2>(a_q, a_e, M, N, K, w_prep, out, out_dtype, s);
+}
+
+}  // namespace nvfp4
+
+namespace nvfp4 {
+
+size_t mx_expert_prep_bytes(int64_t slots, int64_t N, int64_t K) {
+  return (size_t)slots * (size_t)(N * (K / 2) + N * (K / 32));
+}
+
+hipError_t launch_mx_expert_prep(int64_t slots, int64_t N, int64_t K, int interleave_I, const uint8_t* q,
+                                 const uint8_t* ex, uint8_t* prep, hipStream_t s) {
+  const int64_t pieces = (N / 16) * (K / 128) * 64;
+  const dim3 grid((unsigned)((pieces + 255) / 256), (unsigned)slots);
+  mx_expert_prep_kernel<<<grid, 256, 0, s>>>(N, K, interleave_I, q, ex, prep);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_gemm1_swiglu(const MxGemmArgs& a, hipStream_t s) {
+  const AlignShape al = align_shape(a.T, a.topk, a.E, a.shared);
+  MxMoeParams p{};
+  p.T = a.T;
+  p.topk = a.topk;
+  p.N = 2 * a.I;
+  p.K = a.H;
+  p.I = a.I;
+  p.plan = a.plan;
+  p.sorted_pair = a.sorted_pair;
+  p.a_q = a.a_q;
+  p.a_e = a.a_e;
+  p.w_prep = a.w_prep;
+  p.w_expert_bytes = (int64_t)p.N * (p.K / 2) + (int64_t)p.N * (p.K / 32);
+  p.out_q = a.out_q;
+  p.out_e = a.out_e;
+  return launch_grouped_mx<kMxSwiglu>(p, al, s);
+}
+
+hipError_t launch_mx_gemm2_combine(const MxGemmArgs& a, hipStream_t s) {
+  const AlignShape al = align_shape(a.T, a.topk, a.E, a.shared);
+  MxMoeParams p{};
+  p.T = a.T;
+  p.topk = a.topk;
+  p.N = a.H;
+  p.K = a.I;
+  p.I = a.I;
+  p.plan = a.plan;
+  p.sorted_pair = nullptr;                // a2 rows are in sorted order
+  p.a_q = a.a_q;
+  p.a_e = a.a_e;
+  p.w_prep = a.w_prep;
+  p.w_expert_bytes = (int64_t)p.N * (p.K / 2) + (int64_t)p.N * (p.K / 32);
+  p.out_f32 = a.d_ws;
+  hipError_t e = launch_grouped_mx<kMxStoreF32>(p, al, s);
+  if (e != hipSuccess) return e;
+  return launch_combine(a.d_ws, a.inv_pos, a.topk_w, a.T, a.topk, a.shared, a.H, a.out, a.out_dtype, s);
 }
 
 }  // namespace nvfp4

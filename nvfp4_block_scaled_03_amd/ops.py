@@ -364,6 +364,83 @@ def mx_linear(x: torch.Tensor, w: MxLinearWeight, out_dtype=torch.bfloat16, out:
     return out
 
 
+# ---------------------------------------------------------------- MXFP4 layer
+@dataclasses.dataclass
+class MxExpertWeights:
+    """OCP MXFP4 expert weights prepared for the grouped MXFP4 GEMMs."""
+    prep13: torch.Tensor
+    prep2: torch.Tensor
+
+
+def prep_mx_expert_weights(d: Dims, which: int, q: torch.Tensor, ex: torch.Tensor) -> torch.Tensor:
+    _need_cuda(q, ex)
+    n = _lib.load().mxfp4_prep_expert_weights_size(ctypes.byref(d), which)
+    prep = torch.empty(n, dtype=torch.uint8, device=q.device)
+    call("mxfp4_prep_expert_weights", ctypes.byref(d), which, _p(q.contiguous()), _p(ex.contiguous()),
+         _p(prep), _stream())
+    return prep
+
+
+def quantize_mx_expert_weights(d: Dims, w13: torch.Tensor, w2: torch.Tensor) -> MxExpertWeights:
+    """FP32 expert weights (w13 [S, 2I, H], w2 [S, H, I]) -> MXFP4 on the GPU -> prep."""
+    S = d.E + d.shared
+    # mxfp4_quantize takes fewer than 2^31 elements per call: expert groups
+    per = max(1, ((1 << 31) - 1) // (2 * d.I * d.H))
+    q13 = torch.empty(S * 2 * d.I, d.H // 2, dtype=torch.uint8, device=w13.device)
+    e13 = torch.empty(S * 2 * d.I, d.H // 32, dtype=torch.uint8, device=w13.device)
+    q2 = torch.empty(S * d.H, d.I // 2, dtype=torch.uint8, device=w13.device)
+    e2 = torch.empty(S * d.H, d.I // 32, dtype=torch.uint8, device=w13.device)
+    for s0 in range(0, S, per):
+        s1 = min(S, s0 + per)
+        mx_quantize(w13[s0:s1].reshape(-1, d.H), q=q13[s0 * 2 * d.I:s1 * 2 * d.I], ex=e13[s0 * 2 * d.I:s1 * 2 * d.I])
+        mx_quantize(w2[s0:s1].reshape(-1, d.I), q=q2[s0 * d.H:s1 * d.H], ex=e2[s0 * d.H:s1 * d.H])
+    return MxExpertWeights(prep_mx_expert_weights(d, 13, q13, e13), prep_mx_expert_weights(d, 2, q2, e2))
+
+
+class MxMoELayer:
+    """One OCP MXFP4 expert layer with its intermediates preallocated (a call
+    launches kernels only): mxfp4_quantize, moe_align,
+    grouped_gemm1_swiglu_mxfp4, grouped_gemm2_combine_mxfp4."""
+
+    def __init__(self, d: Dims, weights: MxExpertWeights, device="cuda"):
+        self.d, self.w = d, weights
+        dev = torch.device(device)
+        P = d.T * d.topk + d.shared * d.T
+        self.a1_q = torch.empty(max(d.T, 1), d.H // 2, dtype=torch.uint8, device=dev)
+        self.a1_e = torch.empty(max(d.T, 1), d.H // 32, dtype=torch.uint8, device=dev)
+        self.al = alloc_alignment(d, dev)
+        self.a2_q = torch.empty(max(P, 1), d.I // 2, dtype=torch.uint8, device=dev)
+        self.a2_e = torch.empty(max(P, 1), d.I // 32, dtype=torch.uint8, device=dev)
+        self.ws = gemm_workspace(d, dev)
+
+    def forward(self, x, topk_ids, topk_w, out=None, out_dtype=torch.bfloat16, weights=None, marks=None):
+        d, w, s = self.d, weights or self.w, _stream()
+        if out is None:
+            out = torch.empty(d.T, d.H, dtype=out_dtype, device=x.device)
+        call("mxfp4_quantize", _p(x), NVFP4_BF16, d.T, d.H, d.H, _p(self.a1_q), _p(self.a1_e), s)
+        call("moe_align", ctypes.byref(d), _p(topk_ids), _p(self.al.offsets), _p(self.al.sorted_pair),
+             _p(self.al.inv_pos), _p(self.al.plan), _p(self.al.workspace), self.al.workspace.numel(), s)
+        if marks:
+            marks[0].record()
+        call("grouped_gemm1_swiglu_mxfp4", ctypes.byref(d), _p(self.a1_q), _p(self.a1_e),
+             _p(self.al.sorted_pair), _p(self.al.offsets), _p(self.al.plan), _p(w.prep13),
+             _p(self.a2_q), _p(self.a2_e), s)
+        if marks:
+            marks[1].record()
+        call("grouped_gemm2_combine_mxfp4", ctypes.byref(d), _p(self.a2_q), _p(self.a2_e),
+             _p(self.al.offsets), _p(self.al.inv_pos), _p(self.al.plan), _p(topk_w), _p(w.prep2),
+             _p(out), _dtype_code(out), _p(self.ws), self.ws.numel() * 4, s)
+        if marks:
+            marks[2].record()
+        return out
+
+    def gemm1(self, weights=None):
+        d, w = self.d, weights or self.w
+        call("grouped_gemm1_swiglu_mxfp4", ctypes.byref(d), _p(self.a1_q), _p(self.a1_e),
+             _p(self.al.sorted_pair), _p(self.al.offsets), _p(self.al.plan), _p(w.prep13),
+             _p(self.a2_q), _p(self.a2_e), _stream())
+
+
 # ---------------------------------------------------------------- the layer
 class MoELayer:
     """One NVFP4 expert layer with all intermediates preallocated, so that a

@@ -1,0 +1,123 @@
+"""GPU parity of the OCP MXFP4 expert layer (grouped GEMMs on the scaled FP4
+matrix instruction) against the MXFP4 oracle (oracle/mxfp4.py): the
+activation codes and exponents bit for bit, the requantised intermediate
+exact except at oracle-flagged near ties, and the output within the layer
+gate of the staged oracle (its down projection of the GPU's own a2)."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs
+from moe_inputs import Workload
+from nvfp4_block_scaled_03_amd import ops
+from oracle import moe as omoe
+from oracle import mxfp4 as omx
+from oracle import nvfp4 as onv
+from oracle import routing as oroute
+
+from parity import check_a2_mx, check_layer_out, device, relf, to_np
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    Workload("mx16", 40, 256, 256, 8, 2, 0, 0.0, 0.02, 0.01, 111),
+    Workload("mx32", 100, 256, 128, 8, 2, 0, 0.0, 0.02, 0.01, 112),
+    Workload("mx64", 200, 512, 256, 6, 2, 0, 0.5, 0.02, 0.01, 113),
+    Workload("mx128", 600, 256, 384, 4, 2, 1, 0.0, 0.02, 0.01, 114),
+    # odd chunk counts (K = 384, 640) and a GEMM2 width (384) that leaves half
+    # of the last 256-column block idle
+    Workload("mx128b", 300, 384, 640, 3, 1, 0, 0.0, 0.02, 0.01, 115),
+]
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return device()
+
+
+class MxCase:
+    def __init__(self, w: Workload, dev, tokens=None):
+        self.w = w
+        self.d = ops.dims(w.T, w.topk, w.E, w.H, w.I, w.shared)
+        self.x = moe_inputs.activations(w, device=dev)
+        ids, tw = oroute.route_topk(to_np(moe_inputs.router_logits(w, device=dev)), w.topk)
+        self.ids_np, self.tw_np = ids, tw
+        self.ids = torch.from_numpy(ids).to(dev)
+        self.tw = torch.from_numpy(tw).to(dev)
+        self.w13 = moe_inputs.expert_weights(w, 13, device=dev)
+        self.w2 = moe_inputs.expert_weights(w, 2, device=dev)
+        self.ew = omx.MxExpertWeights(lambda e: to_np(self.w13[e]), lambda e: to_np(self.w2[e]))
+        self.xf = to_np(self.x).astype(np.float64)
+        self.tokens = tokens
+        print(f"  mx oracle {w.name}", flush=True)
+        self.ref = omx.layer(self.xf, ids, tw, self.ew, w.E, w.I, shared=w.shared, tokens=tokens)
+        self.wq = ops.quantize_mx_expert_weights(self.d, self.w13, self.w2)
+
+
+def _judge(case: MxCase, dev):
+    w, ref = case.w, case.ref
+    layer = ops.MxMoELayer(case.d, case.wq, device=dev)
+    out32 = layer.forward(case.x, case.ids, case.tw, out_dtype=torch.float32).clone()
+    out16 = layer.forward(case.x, case.ids, case.tw, out_dtype=torch.bfloat16).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(out16, out32.to(torch.bfloat16)), "bf16 output != bf16(f32 output)"
+    assert np.array_equal(onv.unpack_codes(to_np(layer.a1_q)), ref["a1_codes"])
+    assert np.array_equal(to_np(layer.a1_e), ref["a1_exps"])
+    rows = ref["rows"]
+    chk = check_a2_mx(to_np(layer.a2_q)[rows], to_np(layer.a2_e)[rows], ref["h"], what=f"{w.name} mx")
+    exp = ref["out"] if chk.exact else omx.down_and_combine(
+        omx.dequantize(chk.codes, chk.scales), rows, ref["sorted_pair"], ref["offsets"], case.tw_np, case.ew,
+        w.T, w.topk)
+    toks = np.arange(w.T) if case.tokens is None else np.asarray(case.tokens)
+    got = to_np(out32).astype(np.float64)[toks]
+    rf, ma = check_layer_out(got, exp[toks], f"{w.name} mxfp4")
+    e2e = relf(got, ref["out"][toks])
+    assert e2e <= 2e-3, f"end-to-end rel-F {e2e:.2e}"
+    print(f"{w.name} mxfp4: relF {rf:.2e} maxabs/rms {ma:.2e} (vs own-a2 oracle {e2e:.2e})")
+    return layer
+
+
+@pytest.mark.parametrize("w", SMALL + [moe_inputs.WORKLOADS["tiny"]], ids=lambda w: w.name)
+def test_mx_layer_small(dev, w):
+    _judge(MxCase(w, dev), dev)
+
+
+def test_mx_expert_weights_are_the_oracle_codes(dev):
+    """The GPU-quantised expert weights, read back through the layer's
+    GEMMs, are the oracle's: a one-expert layer whose activations are one-hot
+    rows reproduces columns of W13 (checked through h = silu(gate) * up for
+    gate = up = the weight values, compared at a2's precision) -- here simply
+    the canonical codes of every expert against the oracle's quantisation."""
+    w = Workload("mxw", 8, 256, 128, 5, 1, 1, 0.0, 0.02, 0.01, 117)
+    S = w.n_experts
+    w13 = moe_inputs.expert_weights(w, 13, device=dev)
+    q, e = ops.mx_quantize(w13.reshape(S * 2 * w.I, w.H))
+    c_ref, e_ref = omx.quantize(to_np(w13).reshape(S * 2 * w.I, w.H))
+    assert np.array_equal(onv.unpack_codes(to_np(q)), c_ref) and np.array_equal(to_np(e), e_ref)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["decode", "large_e"])
+def test_mx_layer_full_size_every_token(dev, name):
+    print(f"mx full-size {name}", flush=True)
+    _judge(MxCase(moe_inputs.WORKLOADS[name], dev), dev)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["prefill", "skew"])
+def test_mx_layer_full_size_hot_expert(dev, name):
+    """Sampled tokens end to end, and every a2 row of the hottest and the
+    last non-empty expert."""
+    print(f"mx full-size {name}", flush=True)
+    w = moe_inputs.WORKLOADS[name]
+    toks = np.sort(np.random.default_rng(w.seed + 7).choice(w.T, 12, replace=False))
+    case = MxCase(w, dev, tokens=toks)
+    layer = _judge(case, dev)
+    off, sp = case.ref["offsets"], case.ref["sorted_pair"]
+    counts = np.diff(off)
+    x_hat = omx.dequantize(case.ref["a1_codes"], case.ref["a1_exps"])
+    for e in sorted({int(np.argmax(counts)), int(np.nonzero(counts)[0][-1])}):
+        rows = np.arange(off[e], off[e + 1])
+        tok, _ = omoe.pair_token_weight(sp[rows], w.T, w.topk, case.tw_np)
+        h = omoe.swiglu(x_hat[tok] @ case.ew.dequantized(13, e).T, w.I)
+        check_a2_mx(to_np(layer.a2_q)[rows], to_np(layer.a2_e)[rows], h, what=f"{name} mx expert rows")
