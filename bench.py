@@ -1,13 +1,14 @@
 """Benchmark of the NVFP4 MoE expert layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
-                    [--variant w4a4|w4a16] [--mode graph|eager] [--no-configs]
+                    [--variant w4a4|w4a16|mxfp4] [--mode graph|eager] [--no-configs]
                     [--no-linear] [--no-cpu]
 
 A step is one pass of the whole layer path on one batch: global activation
 scale, activation quantisation, permutation by expert, grouped GEMM1 with
 SwiGLU and requantisation, grouped GEMM2 with the top-k weighted combine
-(W4A16: permutation and the two GEMMs).  Inputs (activations, routing,
+(W4A16: permutation and the two GEMMs; MXFP4: block-scale quantisation,
+permutation, the two GEMMs on the scaled FP4 matrix instruction).  Inputs (activations, routing,
 prepared weights) are resident in HBM before timing starts; routing and weight
 preparation are outside the step.  Several copies of the weights are rotated
 between steps so the 256 MB Infinity Cache cannot serve repeats.
@@ -15,7 +16,8 @@ between steps so the 256 MB Infinity Cache cannot serve repeats.
 Prints one JSON line.  ``value`` is the tokens/s of the headline workload
 (decode: T = 64, H = 2048, I = 768, E = 128, top-8) over exactly K timed
 steps.  ``configs`` holds every workload and variant (tiny, decode W4A16,
-prefill, large_e, skew in both variants), each with its step time over K
+prefill, large_e, skew in both NVFP4 variants; decode, prefill and large_e in
+OCP MXFP4), each with its step time over K
 steps, the median over >= 100 graph replays after >= 10 warm-up replays, the
 per-stage breakdown, and the roofline figures of its dominant kernel (GEMM1)
 measured with HIP events on the launch stream inside the timed region.
@@ -40,7 +42,8 @@ sys.path.insert(0, ROOT)
 
 import moe_inputs  # noqa: E402
 from nvfp4_block_scaled_03_amd import ops  # noqa: E402
-from nvfp4_block_scaled_03_amd.profiling import build_layer, weight_copies  # noqa: E402
+from nvfp4_block_scaled_03_amd.profiling import (MxStep, build_layer, build_mx_weights,  # noqa: E402
+                                                  mx_weight_copies, weight_copies)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense FP16/BF16 matrix peak
@@ -55,7 +58,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode", choices=moe_inputs.ORDER)
-    p.add_argument("--variant", default="w4a4", choices=["w4a4", "w4a16"])
+    p.add_argument("--variant", default="w4a4", choices=["w4a4", "w4a16", "mxfp4"])
     p.add_argument("--mode", default="graph", choices=["eager", "graph"])
     p.add_argument("--no-configs", action="store_true", help="skip the other workloads")
     p.add_argument("--no-cpu", action="store_true")
@@ -69,8 +72,19 @@ def log(*a):
 
 
 def dtype_label(variant):
-    return ("nvfp4 codes, f16 matrix ops, f32 accumulate" if variant == "w4a4"
-            else "nvfp4 weights, bf16 activations, bf16 matrix ops, f32 accumulate")
+    return {"w4a4": "nvfp4 codes, f16 matrix ops, f32 accumulate",
+            "w4a16": "nvfp4 weights, bf16 activations, bf16 matrix ops, f32 accumulate",
+            "mxfp4": "mxfp4 codes (E8M0 block scales), fp4 matrix ops, f32 accumulate"}[variant]
+
+
+# Bytes per element of an operand held in each variant's format (codes and
+# block scales, or bf16), and the matrix-unit peak its GEMMs run against.
+def elem_bytes(variant):
+    return {"w4a4": 0.5 + 1 / 16, "w4a16": 2.0, "mxfp4": 0.5 + 1 / 32}[variant]
+
+
+def matrix_peak(variant):
+    return MFMA_FP4_PEAK_TFLOPS if variant == "mxfp4" else MFMA_F16_PEAK_TFLOPS
 
 
 # ---------------------------------------------------------------- CPU oracle
@@ -253,18 +267,25 @@ def measured_traffic(workload: str, variant: str):
     return int(float(t["bytes_per_launch"]))
 
 
-def measure(w, d, x, ids, tw, wq, g2, variant, steps, warmup, mode):
+def measure(w, built, variant, steps, warmup, mode, mx_weights=None):
     """Step time (mean over ``steps``), replay median, breakdown and GEMM1
-    roofline for one workload and variant."""
+    roofline for one workload and variant (``mx_weights``: the prepared MXFP4
+    weights, variant mxfp4)."""
+    d, x, ids, tw, wq, g2 = built
     P = w.pairs
     al = ops.moe_align(d, ids)
     rows_per_expert = np.diff(al.offsets.cpu().numpy())
     touched = int((rows_per_expert > 0).sum())
-    wbytes13 = (2 * w.I * w.H) // 2 + (2 * w.I * w.H) // 16
-    wbytes2 = (w.I * w.H) // 2 + (w.I * w.H) // 16
-    n_copies = max(1, math.ceil(4 * INFINITY_CACHE / max(1, touched * (wbytes13 + wbytes2))))
-    copies = weight_copies(wq, min(n_copies, 8))
-    layer = ops.MoELayer(d, wq, g2, device=x.device)
+    block = 32 if variant == "mxfp4" else 16
+    wbytes13 = (2 * w.I * w.H) // 2 + (2 * w.I * w.H) // block
+    wbytes2 = (w.I * w.H) // 2 + (w.I * w.H) // block
+    n_copies = min(8, max(1, math.ceil(4 * INFINITY_CACHE / max(1, touched * (wbytes13 + wbytes2)))))
+    if variant == "mxfp4":
+        copies = mx_weight_copies(mx_weights, n_copies)
+        layer = MxStep(d, mx_weights, x.device)
+    else:
+        copies = weight_copies(wq, n_copies)
+        layer = ops.MoELayer(d, wq, g2, device=x.device)
     out = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=x.device)
     graphs = multi = None
     if mode == "graph":
@@ -274,9 +295,9 @@ def measure(w, d, x, ids, tw, wq, g2, variant, steps, warmup, mode):
     bd = breakdown(layer, x, ids, tw, copies, variant)
     g1_ms = time_gemm1(layer, x, ids, tw, copies, variant)
     g1_flops = 2.0 * P * (2 * w.I) * w.H
-    a1_bytes = w.T * (w.H // 2 + w.H // 16) if variant == "w4a4" else w.T * w.H * 2
-    a2_bytes = P * (w.I // 2 + w.I // 16) if variant == "w4a4" else P * w.I * 2
-    g1_bytes = touched * wbytes13 + a1_bytes + a2_bytes
+    eb = elem_bytes(variant)
+    g1_bytes = int(touched * wbytes13 + w.T * w.H * eb + P * w.I * eb)
+    peak = matrix_peak(variant)
     decode_like = P / max(1, w.n_experts) < 64
     if decode_like:
         ach = g1_bytes / (g1_ms * 1e-3) / 1e9
@@ -284,13 +305,13 @@ def measure(w, d, x, ids, tw, wq, g2, variant, steps, warmup, mode):
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name, variant)}
     else:
         ach = g1_flops / (g1_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_F16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
-    roof.update({"kernel": "grouped_gemm1_swiglu" + ("" if variant == "w4a4" else "_w4a16"),
-                 "kernel_ms": round(g1_ms, 5), "algorithmic_bytes": int(g1_bytes),
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None}
+    roof.update({"kernel": "grouped_gemm1_swiglu" + {"w4a4": "", "w4a16": "_w4a16", "mxfp4": "_mxfp4"}[variant],
+                 "kernel_ms": round(g1_ms, 5), "algorithmic_bytes": g1_bytes,
                  "algorithmic_flops": g1_flops})
     layer_flops = moe_inputs.flops(w)
-    layer_bytes = moe_inputs.touched_bytes(w, rows_per_expert)
+    layer_bytes = moe_inputs.touched_bytes(w, rows_per_expert, block)
     med = rep["median_ms"] if rep else ms
     rec = {
         "workload": w.name, **w.describe(), "variant": variant, "mode": mode,
@@ -299,7 +320,7 @@ def measure(w, d, x, ids, tw, wq, g2, variant, steps, warmup, mode):
         "layer_tflops": round(layer_flops / (ms * 1e-3) / 1e12, 2),
         "layer_gbs": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
         "layer_hbm_frac": round(layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "layer_mfma_frac": round(layer_flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+        "layer_mfma_frac": round(layer_flops / (ms * 1e-3) / 1e12 / peak, 4),
         "median_tokens_per_s": round(w.T / (med * 1e-3), 1),
         "breakdown": bd, "roofline": roof,
     }
@@ -383,10 +404,11 @@ def linear_sweep(dev, copies=3, reps=10):
 
 # ---------------------------------------------------------------- main
 # The other workloads and variants reported next to the headline line (the
-# five workload shapes; large_e and skew in both variants).  Prefill reuses
-# the decode layer's weights (the same expert shape).
-OTHER_CONFIGS = [("decode", "w4a16"), ("tiny", "w4a4"), ("prefill", "w4a4"), ("prefill", "w4a16"),
-                 ("large_e", "w4a4"), ("large_e", "w4a16"), ("skew", "w4a4"), ("skew", "w4a16")]
+# five workload shapes in both NVFP4 variants, three of them in MXFP4).
+# Prefill reuses the decode layer's weights (the same expert shape).
+OTHER_CONFIGS = [("decode", "w4a16"), ("decode", "mxfp4"), ("tiny", "w4a4"), ("prefill", "w4a4"),
+                 ("prefill", "w4a16"), ("prefill", "mxfp4"), ("large_e", "w4a4"), ("large_e", "w4a16"),
+                 ("large_e", "mxfp4"), ("skew", "w4a4"), ("skew", "w4a16")]
 
 
 def main():
@@ -398,9 +420,18 @@ def main():
     w = moe_inputs.WORKLOADS[a.workload]
     log(f"[bench] building {w.name} layer ({a.variant}, {a.mode})")
     built = {w.name: build_layer(w, dev)}
-    d, x, ids, tw, wq, g2 = built[w.name]
+    mx = {}                     # prepared MXFP4 weights per workload (prefill shares decode's)
+
+    def mx_weights(name):
+        key = "decode" if name == "prefill" else name
+        if key not in mx:
+            log(f"[bench] building {key} MXFP4 weights")
+            mx[key] = build_mx_weights(moe_inputs.WORKLOADS[key], dev)
+        return mx[key]
+
     log(f"[bench] timing {a.steps} steps")
-    m = measure(w, d, x, ids, tw, wq, g2, a.variant, a.steps, a.warmup, a.mode)
+    m = measure(w, built[w.name], a.variant, a.steps, a.warmup, a.mode,
+                mx_weights(w.name) if a.variant == "mxfp4" else None)
     res = {
         "metric": "NVFP4 MoE layer tokens/s (30B-A3B expert shape)",
         "value": m["tokens_per_s"],
@@ -432,16 +463,18 @@ def main():
                 # drop layers no later config uses (bounded device memory)
                 for k in [k for k in built if k not in ("decode",) and k != name]:
                     del built[k]
+                    mx.pop(k, None)
                 torch.cuda.empty_cache()
                 reuse = built["decode"][4] if name == "prefill" and "decode" in built else None
                 log(f"[bench] building {name} layer")
                 built[name] = build_layer(wc, dev, weights=reuse)
-            dc, xc, idc, twc, wqc, g2c = built[name]
             log(f"[bench] {name} {variant}")
             steps = max(5, a.steps // 2)
-            res["configs"][f"{name}_{variant}"] = measure(wc, dc, xc, idc, twc, wqc, g2c, variant, steps,
-                                                          max(3, a.warmup // 2), a.mode)
+            res["configs"][f"{name}_{variant}"] = measure(
+                wc, built[name], variant, steps, max(3, a.warmup // 2), a.mode,
+                mx_weights(name) if variant == "mxfp4" else None)
     built.clear()
+    mx.clear()
     torch.cuda.empty_cache()
     if not a.no_linear:
         log("[bench] dense linear M sweep")

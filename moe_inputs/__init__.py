@@ -151,10 +151,12 @@ def flops(w: Workload) -> float:
     return 2.0 * w.pairs * (2 * w.I * w.H + w.H * w.I)
 
 
-def touched_bytes(w: Workload, rows_per_expert) -> float:
+def touched_bytes(w: Workload, rows_per_expert, block: int = 16) -> float:
     """Algorithmic HBM bytes of one layer pass: weights of the experts that
-    receive at least one row, plus bf16 x and out and the routing arrays."""
-    per_expert = (3 * w.I * w.H) // 2 + (3 * w.I * w.H) // 16
+    receive at least one row (4-bit codes and one scale byte per ``block``
+    elements: 16 for NVFP4, 32 for MXFP4), plus bf16 x and out and the routing
+    arrays."""
+    per_expert = (3 * w.I * w.H) // 2 + (3 * w.I * w.H) // block
     touched = sum(1 for n in rows_per_expert if n > 0)
     return touched * per_expert + 2 * 2 * w.T * w.H + 2 * 4 * w.T * w.topk
 

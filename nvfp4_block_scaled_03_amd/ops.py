@@ -440,6 +440,12 @@ class MxMoELayer:
              _p(self.al.sorted_pair), _p(self.al.offsets), _p(self.al.plan), _p(w.prep13),
              _p(self.a2_q), _p(self.a2_e), _stream())
 
+    def gemm2(self, out, topk_w, weights=None):
+        d, w = self.d, weights or self.w
+        call("grouped_gemm2_combine_mxfp4", ctypes.byref(d), _p(self.a2_q), _p(self.a2_e),
+             _p(self.al.offsets), _p(self.al.inv_pos), _p(self.al.plan), _p(topk_w), _p(w.prep2),
+             _p(out), _dtype_code(out), _p(self.ws), self.ws.numel() * 4, _stream())
+
 
 # ---------------------------------------------------------------- the layer
 class MoELayer:

@@ -133,6 +133,73 @@ def weight_copies(wq, n):
     return out
 
 
+def build_mx_weights(w, dev):
+    """OCP MXFP4 expert weights of workload ``w`` (the same FP32 source
+    weights as build_layer), quantised and prepared by the library expert
+    group by expert group (bounded FP32 memory, under 2^31 elements a call)."""
+    import torch
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    import moe_inputs
+    from nvfp4_block_scaled_03_amd import ops
+    d = ops.dims(w.T, w.topk, w.E, w.H, w.I, w.shared)
+    S, I, H = w.n_experts, w.I, w.H
+    chunk = max(1, min(S, (8 << 30) // (4 * 3 * I * H), ((1 << 31) - 1) // (2 * I * H)))
+    u8 = dict(dtype=torch.uint8, device=dev)
+    q13, e13 = torch.empty(S * 2 * I, H // 2, **u8), torch.empty(S * 2 * I, H // 32, **u8)
+    q2, e2 = torch.empty(S * H, I // 2, **u8), torch.empty(S * H, I // 32, **u8)
+    for s0 in range(0, S, chunk):
+        s1 = min(S, s0 + chunk)
+        sel = range(s0, s1)
+        w13 = moe_inputs.expert_weights(w, 13, device=dev, experts=sel)
+        ops.mx_quantize(w13.reshape(-1, H), q=q13[s0 * 2 * I:s1 * 2 * I], ex=e13[s0 * 2 * I:s1 * 2 * I])
+        del w13
+        w2 = moe_inputs.expert_weights(w, 2, device=dev, experts=sel)
+        ops.mx_quantize(w2.reshape(-1, I), q=q2[s0 * H:s1 * H], ex=e2[s0 * H:s1 * H])
+        del w2
+    wq = ops.MxExpertWeights(ops.prep_mx_expert_weights(d, 13, q13, e13),
+                             ops.prep_mx_expert_weights(d, 2, q2, e2))
+    torch.cuda.synchronize()
+    return wq
+
+
+def mx_weight_copies(wq, n):
+    """``n`` independent copies of prepared MXFP4 expert weights."""
+    from nvfp4_block_scaled_03_amd import ops
+    return [wq] + [ops.MxExpertWeights(wq.prep13.clone(), wq.prep2.clone()) for _ in range(n - 1)]
+
+
+class MxStep:
+    """The MXFP4 layer behind the calls of ops.MoELayer (forward, gemm1,
+    gemm2 with a variant argument), so that timing and profiling code drives
+    both layers alike."""
+
+    def __init__(self, d, weights, dev):
+        from nvfp4_block_scaled_03_amd import ops
+        self.d = d
+        self.layer = ops.MxMoELayer(d, weights, device=dev)
+
+    def forward(self, x, ids, tw, variant, out=None, weights=None, marks=None):
+        return self.layer.forward(x, ids, tw, out=out, weights=weights, marks=marks)
+
+    def gemm1(self, variant, weights, x):
+        self.layer.gemm1(weights)
+
+    def gemm2(self, variant, out, weights, tw):
+        self.layer.gemm2(out, tw, weights)
+
+
+def make_layer(w, dev, variant, built=None):
+    """(layer, weight copies, dims, x, ids, tw) of workload ``w`` for one
+    variant; the NVFP4 variants share one build, mxfp4 builds its weights."""
+    from nvfp4_block_scaled_03_amd import ops
+    d, x, ids, tw, wq, g2 = built if built is not None else build_layer(w, dev)
+    if variant == "mxfp4":
+        mq = build_mx_weights(w, dev)
+        return MxStep(d, mq, dev), mx_weight_copies(mq, 4), d, x, ids, tw
+    return ops.MoELayer(d, wq, g2, device=dev), weight_copies(wq, 4), d, x, ids, tw
+
+
 def _cmd_gemm(a):
     """Launch one GEMM of the named layer ``reps`` times (weight copies
     rotated), after one full layer pass has filled its inputs."""
@@ -140,12 +207,9 @@ def _cmd_gemm(a):
     if ROOT not in sys.path:
         sys.path.insert(0, ROOT)
     import moe_inputs
-    from nvfp4_block_scaled_03_amd import ops
     dev = torch.device("cuda:0")
     w = moe_inputs.WORKLOADS[a.workload]
-    d, x, ids, tw, wq, g2 = build_layer(w, dev)
-    copies = weight_copies(wq, 4)
-    layer = ops.MoELayer(d, wq, g2, device=dev)
+    layer, copies, d, x, ids, tw = make_layer(w, dev, a.variant)
     out = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev)
     layer.forward(x, ids, tw, a.variant, out=out)
     torch.cuda.synchronize()
@@ -165,12 +229,9 @@ def _cmd_layer(a):
     if ROOT not in sys.path:
         sys.path.insert(0, ROOT)
     import moe_inputs
-    from nvfp4_block_scaled_03_amd import ops
     dev = torch.device("cuda:0")
     w = moe_inputs.WORKLOADS[a.workload]
-    d, x, ids, tw, wq, g2 = build_layer(w, dev)
-    copies = weight_copies(wq, 4)
-    layer = ops.MoELayer(d, wq, g2, device=dev)
+    layer, copies, d, x, ids, tw = make_layer(w, dev, a.variant)
     out = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=dev)
     for i in range(a.steps):
         layer.forward(x, ids, tw, a.variant, out=out, weights=copies[i % len(copies)])
@@ -285,11 +346,11 @@ def main(argv=None):
     for name in ("gemm1", "gemm2"):
         g = sub.add_parser(name)
         g.add_argument("--workload", default="decode")
-        g.add_argument("--variant", default="w4a4", choices=["w4a4", "w4a16"])
+        g.add_argument("--variant", default="w4a4", choices=["w4a4", "w4a16", "mxfp4"])
         g.add_argument("--reps", type=int, default=5)
     ly = sub.add_parser("layer")
     ly.add_argument("--workload", default="decode")
-    ly.add_argument("--variant", default="w4a4", choices=["w4a4", "w4a16"])
+    ly.add_argument("--variant", default="w4a4", choices=["w4a4", "w4a16", "mxfp4"])
     ly.add_argument("--steps", type=int, default=20)
     c = sub.add_parser("copy")
     c.add_argument("--mib", type=int, default=1024)
