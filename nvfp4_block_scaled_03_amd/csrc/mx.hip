@@ -468,6 +468,64 @@ struct MxMoeRing {
   static constexpr int loads(int w) { return 2 * a_per_wave(w) + 4 + 1; }
 };
 
+// Epilogue of one wavefront (64 columns: column tiles nt_wave .. nt_wave + 3)
+// for the row groups i < MTA of its accumulators.
+//   kMxStoreF32: FP32 rows of the down projection into the workspace.
+//   kMxSwiglu: the tiles are (gate, up, gate, up): h columns 32 w + fr and
+//   32 w + 16 + fr of MX block w; a row's 32 values sit on the 16 lanes of
+//   one DPP row, so the block amax is a row maximum, the exponent byte is
+//   frexp(amax) - 3 + 127 (clamped; 0 for an all-zero block) and each code is
+//   7 threshold comparisons of the exactly scaled value.
+template <int MTA, int MTACC, int EPI>
+__device__ __forceinline__ void mx_epilogue(const MxMoeParams& p, const f32x4 (&acc)[MTACC][4], int row0,
+                                            int nrows, int nt_wave, int lane) {
+  const int N = p.N;
+  const int fr = lane & 15, fg = lane >> 4;
+  if constexpr (EPI == kMxStoreF32) {
+#pragma unroll
+    for (int i = 0; i < MTA; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = i * 16 + fg * 4 + r;
+          if (row < nrows)
+            p.out_f32[(int64_t)(row0 + row) * N + (nt_wave + j) * 16 + fr] = acc[i][j][r];
+        }
+  } else {
+    const int w = nt_wave >> 2;
+#pragma unroll
+    for (int i = 0; i < MTA; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float h0 = silu_fast(acc[i][0][r]) * acc[i][1][r];
+        const float h1 = silu_fast(acc[i][2][r]) * acc[i][3][r];
+        const float am = row16_max(fmaxf(fabsf(h0), fabsf(h1)));
+        const int code = am > 0.0f ? min(max(__builtin_amdgcn_frexp_expf(am) - 1 - 2 + 127, 0), 254) : 0;
+        const int sh = 127 - code;
+        uint32_t c[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float hv = u == 0 ? h0 : h1;
+          const float a = fabsf(__builtin_ldexpf(hv, sh));   // exact: a power-of-two scaling
+          const uint32_t mag = (uint32_t)(a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+                               (a >= 3.5f) + (a > 5.0f);
+          c[u] = (((uint32_t)__float_as_int(hv) >> 28) & 8u) | mag;
+        }
+        const uint32_t o0 = (uint32_t)dpp_xor1_i((int)c[0]), o1 = (uint32_t)dpp_xor1_i((int)c[1]);
+        const int row = i * 16 + fg * 4 + r;
+        if (row < nrows) {
+          const int64_t pr = row0 + row;
+          if ((fr & 1) == 0) {
+            p.out_q[pr * (p.I >> 1) + (32 * w + fr) / 2] = (uint8_t)(c[0] | (o0 << 4));
+            p.out_q[pr * (p.I >> 1) + (32 * w + 16 + fr) / 2] = (uint8_t)(c[1] | (o1 << 4));
+          }
+          if (fr == 0) p.out_e[pr * (p.I >> 5) + w] = (uint8_t)code;
+        }
+      }
+  }
+}
+
 template <int MT, int EPI>
 __global__ __launch_bounds__(256) void grouped_mx_kernel(MxMoeParams p) {
   using R = MxMoeRing<MT>;
@@ -588,53 +646,212 @@ __global__ __launch_bounds__(256) void grouped_mx_kernel(MxMoeParams p) {
   __builtin_amdgcn_s_waitcnt(mx_vmcnt(0));
   if (!wave_on) return;
 
-  const int fr = lane & 15, fg = lane >> 4;
-  if constexpr (EPI == kMxStoreF32) {
+  mx_epilogue<MT, MT, EPI>(p, acc, row0, nrows, nt_wave, lane);
+}
+
+// Tall tiles (the 64- and 128-row plan lists) run on a kernel built for two
+// workgroups per CU, i.e. two wavefronts per SIMD: one wavefront per SIMD
+// leaves every LDS read latency and every barrier exposed, and with 16 chunks
+// per tile (K = 2048; 6 for the down projection) a workgroup's ring fill and
+// drain are not hidden by another one.  Each wavefront owns 64 columns, so
+// no wavefront shares another's weights: they stream from memory straight
+// into registers (the streaming layout is the instruction operand, one
+// 16-byte load per lane per column tile and chunk) through a ring of three
+// chunks.  The activation tile is shared by the four wavefronts: its rows
+// are gathered into registers two chunks ahead and written to one of two
+// LDS buffers one chunk ahead of use; exponent words are kept as
+// [row][tile] so that one 16-byte read gives a lane the bytes of 4 tiles.
+// Every load is an ordinary one, so the compiler's own waits are exact.
+// The main loop is instantiated for 8, 4, 2 and 1 active 16-row groups: a
+// ragged last tile stages and multiplies only the groups that hold rows.
+constexpr int kMxTallRing = 3;   // weight chunks in registers
+
+// KCT > 0: the chunk loop fully unrolled for K = 128 KCT (straight-line code,
+// so the compiler's waits are exact; in a loop its analysis merges the
+// header's incoming states and falls back to draining every load).  KCT = 0:
+// any K, as a loop.
+template <int MTA, int EPI, int KCT>
+__device__ __forceinline__ void mx_tall_body(const MxMoeParams& p, uint8_t (*sa)[8 * 1024], uint32_t (*se)[16 * 8],
+                                             int e, int row0, int nrows, int nb) {
+  constexpr int NTW = 4, AW = MTA >= 4 ? MTA / 4 : 1, RB = kMxTallRing;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int K = p.K, KC = KCT > 0 ? KCT : K / 128, N = p.N, NT = N / 16;
+  const int nt_wave = nb * 16 + wv * 4;
+  const bool wave_on = nt_wave * 16 < N;
+  const int m = lane & 15, g = lane >> 4;
+  const bool a_on = MTA >= 4 || wv < MTA;         // this wavefront stages activation tiles
+
+  // Activation tile i = wv + 4 u (u < AW): lane 16 g + m loads row m, bytes
+  // [16 g, 16 g + 16) of the chunk's 64; rows past the tile end repeat its
+  // last row (loaded, never stored).  Each lane also loads the exponent word
+  // (4 blocks of the chunk) of row m of tile wv + 4 min(g, AW - 1).
+  uint32_t va[AW];
+  int tok[AW];
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int j = 0; j < NTW; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = i * 16 + fg * 4 + r;
-          if (row < nrows)
-            p.out_f32[(int64_t)(row0 + row) * N + (nt_wave + j) * 16 + fr] = acc[i][j][r];
-        }
-  } else {
-    // Tiles (gate, up, gate, up): h columns 32 w + fr and 32 w + 16 + fr of
-    // MX block w; a row's 32 values sit on the 16 lanes of one DPP row.
-    const int w = nt_wave >> 2;
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float h0 = silu_fast(acc[i][0][r]) * acc[i][1][r];
-        const float h1 = silu_fast(acc[i][2][r]) * acc[i][3][r];
-        const float am = row16_max(fmaxf(fabsf(h0), fabsf(h1)));
-        // floor(log2 am) - 2 + 127, clamped (E8M0); 0 for an all-zero block
-        const int code = am > 0.0f ? min(max(__builtin_amdgcn_frexp_expf(am) - 1 - 2 + 127, 0), 254) : 0;
-        const int sh = 127 - code;
-        uint32_t c[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const float hv = u == 0 ? h0 : h1;
-          const float a = fabsf(__builtin_ldexpf(hv, sh));   // exact: a power-of-two scaling
-          const uint32_t mag = (uint32_t)(a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
-                               (a >= 3.5f) + (a > 5.0f);
-          c[u] = (((uint32_t)__float_as_int(hv) >> 28) & 8u) | mag;
-        }
-        const uint32_t o0 = (uint32_t)dpp_xor1_i((int)c[0]), o1 = (uint32_t)dpp_xor1_i((int)c[1]);
-        const int row = i * 16 + fg * 4 + r;
-        if (row < nrows) {
-          const int64_t pr = row0 + row;
-          if ((fr & 1) == 0) {
-            p.out_q[pr * (p.I >> 1) + (32 * w + fr) / 2] = (uint8_t)(c[0] | (o0 << 4));
-            p.out_q[pr * (p.I >> 1) + (32 * w + 16 + fr) / 2] = (uint8_t)(c[1] | (o1 << 4));
-          }
-          if (fr == 0) p.out_e[pr * (p.I >> 5) + w] = (uint8_t)code;
-        }
-      }
+  for (int u = 0; u < AW; ++u) {
+    const int i = MTA >= 4 ? wv + 4 * u : min(wv, MTA - 1);
+    int r = row0 + min(16 * i + m, nrows - 1);
+    if (p.sorted_pair) r = pair_token(p.sorted_pair[r], p.T, p.topk);
+    tok[u] = r;
+    va[u] = (uint32_t)r * (uint32_t)(K / 2) + (uint32_t)(16 * g);
   }
+  const int ge = min(g, AW - 1);
+  const uint32_t vae = (uint32_t)tok[ge] * (uint32_t)(K / 32);
+  const int ie = MTA >= 4 ? wv + 4 * ge : min(wv, MTA - 1);   // tile of this lane's exponent word
+
+  const uint8_t* wq = p.w_prep + (int64_t)e * p.w_expert_bytes;
+  const uint8_t* ws = wq + (int64_t)N * (K / 2);
+  uint32_t vb[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    const int nt = min(nt_wave + t, NT - 4 + t);
+    vb[t] = (uint32_t)((nt * KC) * 64 + lane) * 16u;
+  }
+  const uint32_t vbs = (uint32_t)((min(nt_wave, NT - 4) / 4 * KC) * 64 + lane) * 4u;
+
+  u32x4 rb[RB][NTW];
+  uint32_t rbs[RB];
+  u32x4 ra[AW];
+  uint32_t rae;
+  // Loads past the last chunk repeat it (unconditional, so every wait is
+  // the same in every iteration).
+  auto load_b = [&](int kc, u32x4 (&b)[NTW], uint32_t& bs) __attribute__((always_inline)) {
+    kc = min(kc, KC - 1);
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) b[t] = *reinterpret_cast<const u32x4*>(wq + (vb[t] + (uint32_t)kc * 1024u));
+    bs = *reinterpret_cast<const uint32_t*>(ws + (vbs + (uint32_t)kc * 256u));
+  };
+  auto load_a = [&](int kc, u32x4 (&a)[AW], uint32_t& ae) __attribute__((always_inline)) {
+    if (!a_on) return;
+    kc = min(kc, KC - 1);
+#pragma unroll
+    for (int u = 0; u < AW; ++u) a[u] = *reinterpret_cast<const u32x4*>(p.a_q + (va[u] + (uint32_t)kc * 64u));
+    ae = *reinterpret_cast<const uint32_t*>(p.a_e + (vae + (uint32_t)kc * 4u));
+  };
+  auto store_a = [&](int buf, const u32x4 (&a)[AW], uint32_t ae) __attribute__((always_inline)) {
+    if (!a_on) return;
+#pragma unroll
+    for (int u = 0; u < AW; ++u) {
+      const int i = MTA >= 4 ? wv + 4 * u : wv;
+      *reinterpret_cast<u32x4*>(sa[buf] + i * 1024 + lane * 16) = a[u];
+    }
+    // lanes g >= AW hold the word of lane (m, AW - 1) and store the same
+    // value to the same place (no branch, so the waits stay exact)
+    se[buf][m * 8 + ie] = ae;
+  };
+
+  f32x4 acc[MTA][NTW];
+#pragma unroll
+  for (int i = 0; i < MTA; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf, const u32x4 (&b)[NTW], uint32_t bsw) __attribute__((always_inline)) {
+    // exponent bytes of row m for tiles 0..7, byte g of word i
+    const u32x4 ew0 = *reinterpret_cast<const u32x4*>(&se[buf][m * 8]);
+    u32x4 ew1 = ew0;
+    if constexpr (MTA > 4) ew1 = *reinterpret_cast<const u32x4*>(&se[buf][m * 8 + 4]);
+    // One fragment read ahead of the matrix instructions that use it (the
+    // scheduler is fenced so that it does not hoist all MTA reads and their
+    // registers to the top).
+    u32x4 an = *reinterpret_cast<const u32x4*>(sa[buf] + lane * 16);
+#pragma unroll
+    for (int i = 0; i < MTA; ++i) {
+      const u32x4 a = an;
+      if (i + 1 < MTA) an = *reinterpret_cast<const u32x4*>(sa[buf] + (i + 1) * 1024 + lane * 16);
+      const uint32_t aw = i < 4 ? ew0[i & 3] : ew1[i & 3];
+      const int as = (int)((aw >> (8 * g)) & 0xFFu);
+      const v8i av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const v8i bv = {(int)b[j][0], (int)b[j][1], (int)b[j][2], (int)b[j][3], 0, 0, 0, 0};
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[i][j], 4, 4, 0, as, 0,
+                                                                    (int)((bsw >> (8 * j)) & 0xFFu));
+      }
+      asm volatile("" ::: "memory");   // keeps the next read from being hoisted further
+    }
+  };
+
+  // Prologue: activations of chunk 0 into buffer 0, chunk 1 into the
+  // registers, weights of chunks 0..RB-1.
+  load_a(0, ra, rae);
+  store_a(0, ra, rae);
+  load_a(1, ra, rae);
+#pragma unroll
+  for (int c = 0; c < RB; ++c) load_b(c, rb[c], rbs[c]);
+  __syncthreads();
+
+  // Iteration c: buffer c % 2 holds chunk c and rb[c % RB] its weights; ra
+  // holds chunk c + 1.  Per iteration the loads go out activations first,
+  // then weights, so that the wait before the activation store (loads
+  // complete in order) does not also wait for the weights issued with it.
+  auto step = [&](int c, int d) __attribute__((always_inline)) {
+    compute(d & 1, rb[d % RB], rbs[d % RB]);
+    // The matrix instructions touch no memory: without this the compiler
+    // sinks all of them past the barriers to the end of the unrolled body
+    // and spills the fragments they read.  An empty statement that reads
+    // and writes the accumulators keeps each chunk's instructions here.
+#pragma unroll
+    for (int i = 0; i < MTA; ++i)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) asm volatile("" : "+v"(acc[i][j]));
+    store_a((d + 1) & 1, ra, rae);
+    load_a(c + 2, ra, rae);
+    load_b(c + RB, rb[d % RB], rbs[d % RB]);
+    __syncthreads();
+  };
+  if constexpr (KCT > 0) {
+#pragma unroll
+    for (int c = 0; c < KCT; ++c) step(c, c);
+  } else {
+    constexpr int U = 6;   // lcm(2, RB)
+    static_assert(U % RB == 0 && U % 2 == 0, "unroll covers both rings");
+    for (int c0 = 0; c0 < KC; c0 += U) {
+#pragma unroll
+      for (int d = 0; d < U; ++d)
+        if (c0 + d < KC) step(c0 + d, d);
+    }
+  }
+  if (!wave_on) return;
+  mx_epilogue<MTA, MTA, EPI>(p, acc, row0, nrows, nt_wave, lane);
+}
+
+// The contraction lengths of the expert shapes get straight-line bodies.
+template <int MTA, int EPI>
+__device__ __forceinline__ void mx_tall_groups(const MxMoeParams& p, uint8_t (*sa)[8 * 1024],
+                                               uint32_t (*se)[16 * 8], int e, int row0, int nrows, int nb) {
+  switch (p.K) {
+    case 768: mx_tall_body<MTA, EPI, 6>(p, sa, se, e, row0, nrows, nb); break;
+    case 1024: mx_tall_body<MTA, EPI, 8>(p, sa, se, e, row0, nrows, nb); break;
+    case 2048: mx_tall_body<MTA, EPI, 16>(p, sa, se, e, row0, nrows, nb); break;
+    case 4096: mx_tall_body<MTA, EPI, 32>(p, sa, se, e, row0, nrows, nb); break;
+    default: mx_tall_body<MTA, EPI, 0>(p, sa, se, e, row0, nrows, nb); break;
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void grouped_mx_tall_kernel(MxMoeParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t sa[2][8 * 1024];
+  __shared__ __attribute__((aligned(16))) uint32_t se[2][16 * 8];
+  const int ntiles = ld_uniform(p.plan + p.list_idx);
+  const int G = ntiles * p.n_blocks;
+  if ((int)blockIdx.x >= G) return;
+  int v;
+  {
+    const int q = G >> 3, r = G & 7, x = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    v = x * q + min(x, r) + idx;
+  }
+  const int tile = v / p.n_blocks, nb = v - tile * p.n_blocks;
+  const int* ent = p.plan + ld_uniform(p.plan + kPlanLists + p.list_idx) + 2 * tile;
+  const int e = ld_uniform(ent) & 2047;
+  const uint32_t rr = (uint32_t)ld_uniform(ent + 1);
+  const int row0 = (int)(rr & 0xFFFFFFu), nrows = (int)(rr >> 24);
+  const int groups = (nrows + 15) >> 4;
+  if (groups > 4) mx_tall_groups<8, EPI>(p, sa, se, e, row0, nrows, nb);
+  else if (groups > 2) mx_tall_groups<4, EPI>(p, sa, se, e, row0, nrows, nb);
+  else if (groups > 1) mx_tall_groups<2, EPI>(p, sa, se, e, row0, nrows, nb);
+  else mx_tall_groups<1, EPI>(p, sa, se, e, row0, nrows, nb);
 }
 
 template <int MT, int EPI>
@@ -653,8 +870,12 @@ hipError_t launch_grouped_mx(MxMoeParams p, const AlignShape& al, hipStream_t s)
   switch (li) {
     case 0: return launch_grouped_mx_t<1, EPI>(p, al.list_len[0], s);
     case 1: return launch_grouped_mx_t<2, EPI>(p, al.list_len[1], s);
-    case 2: return launch_grouped_mx_t<4, EPI>(p, al.list_len[2], s);
-    default: return launch_grouped_mx_t<8, EPI>(p, al.list_len[3], s);
+    default: {
+      const int64_t G = al.list_len[li] * p.n_blocks;
+      const unsigned grid = (unsigned)std::max<int64_t>(8, (G + 7) / 8 * 8);
+      grouped_mx_tall_kernel<EPI><<<grid, 256, 0, s>>>(p);
+      return hipGetLastError();
+    }
   }
 }
 
