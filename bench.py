@@ -252,19 +252,21 @@ def time_gemm1(layer, x, ids, tw, copies, variant, n=50):
     return e0.elapsed_time(e1) / n
 
 
-def measured_traffic(workload: str, variant: str):
-    """HBM bytes per GEMM1 launch from the committed rocprofv3 counter summary
-    (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None when there
-    is none for this workload or the kernel sources changed since it was taken."""
+def measured_traffic(workload: str, variant: str, kernel: str = "grouped_gemm1_swiglu"):
+    """HBM bytes per call of ``kernel`` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None
+    when there is none for this workload and variant or the kernel sources
+    changed since it was taken."""
     from nvfp4_block_scaled_03_amd import profiling
-    suffix = "" if variant == "w4a4" else "_w4a16"
-    path = os.path.join(ROOT, "profiles", f"grouped_gemm1_swiglu{suffix}_{workload}_traffic.txt")
+    suffix = {"w4a4": "", "w4a16": "_w4a16", "mxfp4": "_mxfp4"}[variant]
+    path = os.path.join(ROOT, "profiles", f"{kernel}{suffix}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     t = profiling.read_traffic(path)
-    if t.get("sources_sha256_16") != profiling.sources_hash():
+    family = "mxfp4" if variant == "mxfp4" else "nvfp4"
+    if t.get("sources_sha256_16") != profiling.sources_hash(family):
         return None
-    return int(float(t["bytes_per_launch"]))
+    return int(float(t["bytes_per_call"]))
 
 
 def measure(w, built, variant, steps, warmup, mode, mx_weights=None):

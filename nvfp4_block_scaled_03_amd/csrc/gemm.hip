@@ -1331,13 +1331,6 @@ __global__ __launch_bounds__(4 * kWave) void linear_splitk_kernel(KParams p) {
 }
 
 
-// Whether short experts and tall ones run on different kernels: short tiles
-// on average (the streaming regime) while one expert may still hold more
-// than 64 rows (T > 64, or a shared expert, which takes every token).
-bool split_experts(const AlignShape& al) {
-  return pick_list(al.P, al.slots) <= 1 && (al.T > 64 || (al.shared && al.T > kSplitRows));
-}
-
 template <int AK, int EPI>
 hipError_t launch_wide(KParams kp, int list_len, hipStream_t s) {
   kp.n_blocks = (kp.N + kWideNW * kWideWN - 1) / (kWideNW * kWideWN);
@@ -1458,6 +1451,10 @@ int pick_list(int64_t P, int slots) {
   if (avg <= 40) return 1;
   if (avg <= 96) return 2;
   return 3;
+}
+
+bool split_experts(const AlignShape& al) {
+  return pick_list(al.P, al.slots) <= 1 && (al.T > 64 || (al.shared && al.T > kSplitRows));
 }
 
 bool prefers_decoded(int T, int topk, int E, int shared) {

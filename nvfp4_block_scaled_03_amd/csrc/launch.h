@@ -127,6 +127,11 @@ hipError_t launch_combine(const float* d, const int32_t* inv_pos, const float* t
                           int shared, int H, void* out, int out_dtype, hipStream_t s);
 // Tile list (0..3: 16, 32, 64, 128 rows) chosen from the mean rows per expert.
 int pick_list(int64_t P, int slots);
+// Whether short experts and tall ones run on different kernels (lists 4 and
+// 5): short tiles on average (the streaming regime) while one expert may
+// still hold more than 64 rows (T > 64, or a shared expert, which takes
+// every token).
+bool split_experts(const AlignShape& al);
 
 // Dense linear y [M][N] = x [M][K] W^T on the grouped-GEMM kernels with one
 // expert (plan from an alignment of M pairs to expert 0).

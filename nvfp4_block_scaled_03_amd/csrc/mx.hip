@@ -863,19 +863,31 @@ hipError_t launch_grouped_mx_t(MxMoeParams p, int64_t list_len, hipStream_t s) {
 }
 
 template <int EPI>
+hipError_t launch_grouped_mx_tall(MxMoeParams p, int64_t list_len, hipStream_t s) {
+  const int64_t G = list_len * p.n_blocks;
+  const unsigned grid = (unsigned)std::max<int64_t>(8, (G + 7) / 8 * 8);
+  grouped_mx_tall_kernel<EPI><<<grid, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+template <int EPI>
 hipError_t launch_grouped_mx(MxMoeParams p, const AlignShape& al, hipStream_t s) {
+  p.n_blocks = (p.N + 255) / 256;
+  if (split_experts(al)) {
+    // short experts on 16-row tiles, the tall ones (a shared expert) on the
+    // tall-tile kernel, which reads their weights once per 128 rows
+    p.list_idx = 4;
+    const hipError_t e = launch_grouped_mx_t<1, EPI>(p, al.list_len[4], s);
+    if (e != hipSuccess) return e;
+    p.list_idx = 5;
+    return launch_grouped_mx_tall<EPI>(p, al.list_len[5], s);
+  }
   const int li = pick_list(al.P, al.slots);
   p.list_idx = li;
-  p.n_blocks = (p.N + 255) / 256;
   switch (li) {
     case 0: return launch_grouped_mx_t<1, EPI>(p, al.list_len[0], s);
     case 1: return launch_grouped_mx_t<2, EPI>(p, al.list_len[1], s);
-    default: {
-      const int64_t G = al.list_len[li] * p.n_blocks;
-      const unsigned grid = (unsigned)std::max<int64_t>(8, (G + 7) / 8 * 8);
-      grouped_mx_tall_kernel<EPI><<<grid, 256, 0, s>>>(p);
-      return hipGetLastError();
-    }
+    default: return launch_grouped_mx_tall<EPI>(p, al.list_len[li], s);
   }
 }
 

@@ -40,13 +40,15 @@ from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-# Sources whose change invalidates recorded counters of the GEMM kernels.
-HASHED = ["csrc/gemm.hip", "csrc/common.h", "csrc/launch.h", "csrc/prep.hip"]
+# Sources whose change invalidates recorded counters of the GEMM kernels, by
+# kernel family (the NVFP4 GEMMs, the MXFP4 GEMMs).
+HASHED = {"nvfp4": ["csrc/gemm.hip", "csrc/common.h", "csrc/launch.h", "csrc/prep.hip"],
+          "mxfp4": ["csrc/mx.hip", "csrc/mx.h", "csrc/common.h", "csrc/launch.h"]}
 
 
-def sources_hash() -> str:
+def sources_hash(family: str = "nvfp4") -> str:
     h = hashlib.sha256()
-    for rel in HASHED:
+    for rel in HASHED[family]:
         with open(os.path.join(PKG, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -69,7 +71,7 @@ def _per_dispatch(path: str, counter: str, name_re: str):
 
 
 def read_traffic(path: str):
-    """Parse a traffic summary: dict with bytes_per_launch, fetch/write bytes, hash."""
+    """Parse a traffic summary: dict with bytes_per_call, fetch/write bytes, hash."""
     out = {}
     with open(path) as f:
         for line in f:
@@ -252,8 +254,12 @@ def _cmd_copy(a):
 
 
 def _cmd_traffic(a):
+    # A call of some GEMMs is several launches (short and tall experts):
+    # per-call figures are per-dispatch means times launches per call.
     f_kib, n_f, names = _per_dispatch(a.fetch, "FETCH_SIZE", a.kernel_re)
     w_kib, n_w, _ = _per_dispatch(a.write, "WRITE_SIZE", a.kernel_re)
+    f_kib *= a.launches_per_call
+    w_kib *= a.launches_per_call
     cf_kib, _, cnames = _per_dispatch(a.copy_fetch, "FETCH_SIZE", a.copy_re)
     cw_kib, _, _ = _per_dispatch(a.copy_write, "WRITE_SIZE", a.copy_re)
     moved = float(a.mib << 20)
@@ -270,21 +276,23 @@ def _cmd_traffic(a):
     print(f"workload = {a.workload}")
     print(f"dispatches_fetch = {n_f}")
     print(f"dispatches_write = {n_w}")
-    print(f"fetch_size_kib_per_dispatch = {f_kib:.1f}")
-    print(f"write_size_kib_per_dispatch = {w_kib:.1f}")
+    print(f"launches_per_call = {a.launches_per_call}")
+    print(f"fetch_size_kib_per_call = {f_kib:.1f}")
+    print(f"write_size_kib_per_call = {w_kib:.1f}")
     print(f"copy_fetch_size_kib = {cf_kib:.1f}")
     print(f"copy_write_size_kib = {cw_kib:.1f}")
     print(f"fetch_scale = {f_scale:.4f}")
     print(f"write_scale = {w_scale:.4f}")
-    print(f"fetch_bytes_per_launch = {fetch_b:.0f}")
-    print(f"write_bytes_per_launch = {write_b:.0f}")
-    print(f"bytes_per_launch = {fetch_b + write_b:.0f}")
+    print(f"fetch_bytes_per_call = {fetch_b:.0f}")
+    print(f"write_bytes_per_call = {write_b:.0f}")
+    print(f"bytes_per_call = {fetch_b + write_b:.0f}")
     if a.req:
         # Cross-check of the fetch calibration: HBM read requests by size.
         sizes = {"TCC_EA0_RDREQ_32B_sum": 32, "TCC_EA0_RDREQ_64B_sum": 64, "TCC_EA0_RDREQ_128B_sum": 128}
         req_b = sum(_per_dispatch(a.req, c, a.kernel_re)[0] * b for c, b in sizes.items())
         print(f"read_bytes_by_request_size = {req_b:.0f}")
-    print(f"sources_sha256_16 = {sources_hash()}")
+    print(f"family = {a.family}")
+    print(f"sources_sha256_16 = {sources_hash(a.family)}")
 
 
 def _cmd_stats(a):
@@ -365,6 +373,8 @@ def main(argv=None):
     t.add_argument("--workload", default="decode")
     t.add_argument("--command", default="")
     t.add_argument("--req", default="", help="counter CSV of TCC_EA0_RDREQ_{32B,64B,128B}_sum")
+    t.add_argument("--family", default="nvfp4", choices=sorted(HASHED))
+    t.add_argument("--launches-per-call", dest="launches_per_call", type=int, default=1)
     co = sub.add_parser("counters")
     co.add_argument("--csv", nargs="+", required=True)
     co.add_argument("--kernel-re", dest="kernel_re", required=True)

@@ -9,11 +9,11 @@ ROOT = os.path.dirname(os.path.dirname(__file__))
 def test_committed_traffic_summary_parses():
     path = os.path.join(ROOT, "profiles", "grouped_gemm1_swiglu_decode_traffic.txt")
     t = profiling.read_traffic(path)
-    for k in ("bytes_per_launch", "fetch_scale", "write_scale", "sources_sha256_16"):
+    for k in ("bytes_per_call", "fetch_scale", "write_scale", "sources_sha256_16"):
         assert k in t, k
-    fetch, write = float(t["fetch_bytes_per_launch"]), float(t["write_bytes_per_launch"])
-    assert float(t["bytes_per_launch"]) == round(fetch) + round(write) or \
-        abs(float(t["bytes_per_launch"]) - fetch - write) <= 1
+    fetch, write = float(t["fetch_bytes_per_call"]), float(t["write_bytes_per_call"])
+    assert float(t["bytes_per_call"]) == round(fetch) + round(write) or \
+        abs(float(t["bytes_per_call"]) - fetch - write) <= 1
     assert len(t["sources_sha256_16"]) == 16
 
 
@@ -37,8 +37,8 @@ def test_traffic_summary_from_counter_rows(tmp_path, capsys):
     out.write_text(capsys.readouterr().out)
     t = profiling.read_traffic(str(out))
     assert t["dispatches_fetch"] == "2" and float(t["fetch_scale"]) == 2.0
-    assert float(t["fetch_bytes_per_launch"]) == 128 * 1024 * 2
-    assert float(t["write_bytes_per_launch"]) == 4 * 1024
+    assert float(t["fetch_bytes_per_call"]) == 128 * 1024 * 2
+    assert float(t["write_bytes_per_call"]) == 4 * 1024
     assert t["sources_sha256_16"] == profiling.sources_hash()
 
 
