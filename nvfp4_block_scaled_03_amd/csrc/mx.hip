@@ -526,6 +526,56 @@ __device__ __forceinline__ void mx_epilogue(const MxMoeParams& p, const f32x4 (&
   }
 }
 
+// SwiGLU epilogue through a wave-private LDS tile (the tall-tile kernel,
+// whose activation buffers are free once its last chunk is done): h of one
+// 16-row group (16 rows x 32 columns, one MX block per row) is written in the
+// accumulator layout and read back so that lane 4 row + q owns columns
+// [8 q, 8 q + 8) of its row.  The block amax is then a local maximum and two
+// quad exchanges, and each lane stores its 8 codes as one 32-bit word (16
+// contiguous bytes per row) instead of single bytes.  Same decisions as
+// mx_epilogue: the maximum is exact and the per-value rule is the same.
+template <int MTA, int MTACC>
+__device__ __forceinline__ void mx_epilogue_swiglu_lds(const MxMoeParams& p, const f32x4 (&acc)[MTACC][4],
+                                                       int row0, int nrows, int nt_wave, int lane,
+                                                       float* __restrict__ tile) {
+  constexpr int LD = 36;   // row stride in floats: the 4 row groups of a write fall in distinct banks
+  const int fr = lane & 15, fg = lane >> 4;
+  const int w = nt_wave >> 2;
+  const int rr = lane >> 2, q = lane & 3;
+#pragma unroll
+  for (int i = 0; i < MTA; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      tile[(fg * 4 + r) * LD + fr] = silu_fast(acc[i][0][r]) * acc[i][1][r];
+      tile[(fg * 4 + r) * LD + 16 + fr] = silu_fast(acc[i][2][r]) * acc[i][3][r];
+    }
+    const f32x4 v0 = *reinterpret_cast<const f32x4*>(tile + rr * LD + 8 * q);
+    const f32x4 v1 = *reinterpret_cast<const f32x4*>(tile + rr * LD + 8 * q + 4);
+    const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    float am = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(v[j]));
+    am = fmaxf(am, dpp_xor1(am));
+    am = fmaxf(am, dpp_xor2(am));
+    const int code = am > 0.0f ? min(max(__builtin_amdgcn_frexp_expf(am) - 1 - 2 + 127, 0), 254) : 0;
+    const int sh = 127 - code;
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float a = fabsf(__builtin_ldexpf(v[j], sh));   // exact: a power-of-two scaling
+      const uint32_t mag = (uint32_t)(a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+                           (a >= 3.5f) + (a > 5.0f);
+      word |= ((((uint32_t)__float_as_int(v[j]) >> 28) & 8u) | mag) << (4 * j);
+    }
+    const int row = i * 16 + rr;
+    if (row < nrows) {
+      const int64_t pr = row0 + row;
+      *reinterpret_cast<uint32_t*>(p.out_q + pr * (p.I >> 1) + 16 * w + 4 * q) = word;
+      if (q == 0) p.out_e[pr * (p.I >> 5) + w] = (uint8_t)code;
+    }
+  }
+}
+
 template <int MT, int EPI>
 __global__ __launch_bounds__(256) void grouped_mx_kernel(MxMoeParams p) {
   using R = MxMoeRing<MT>;
@@ -813,7 +863,11 @@ __device__ __forceinline__ void mx_tall_body(const MxMoeParams& p, uint8_t (*sa)
     }
   }
   if (!wave_on) return;
-  mx_epilogue<MTA, MTA, EPI>(p, acc, row0, nrows, nt_wave, lane);
+  if constexpr (EPI == kMxSwiglu)
+    mx_epilogue_swiglu_lds<MTA, MTA>(p, acc, row0, nrows, nt_wave, lane,
+                                     reinterpret_cast<float*>(&sa[0][0]) + wv * 16 * 36);
+  else
+    mx_epilogue<MTA, MTA, EPI>(p, acc, row0, nrows, nt_wave, lane);
 }
 
 // The contraction lengths of the expert shapes get straight-line bodies.
