@@ -101,3 +101,38 @@ def test_layer_writes_stay_inside_buffers(dev, w):
                 assert torch.equal(out, want), f"{w.name} {variant} decoded={decoded} {dt}"
             del layer, ref_layer
     torch.cuda.empty_cache()
+
+
+def _guard_mx_layer(layer: ops.MxMoELayer, g: Guarded):
+    for name in ("a1_q", "a1_e", "a2_q", "a2_e", "ws"):
+        setattr(layer, name, g.make(getattr(layer, name)))
+    al = layer.al
+    layer.al = ops.Alignment(offsets=g.make(al.offsets), sorted_pair=g.make(al.sorted_pair),
+                             inv_pos=g.make(al.inv_pos), plan=g.make(al.plan),
+                             workspace=g.make(al.workspace))
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_mx_layer_writes_stay_inside_buffers(dev, w):
+    """The OCP MXFP4 layer on the same shapes: every buffer between guard
+    bands, and the output equal to that of the same layer on ordinary
+    allocations."""
+    print(f"mx guards {w.name}", flush=True)
+    d = ops.dims(w.T, w.topk, w.E, w.H, w.I, w.shared)
+    x = moe_inputs.activations(w, device=dev)
+    ids, tw = ops.route_topk(moe_inputs.router_logits(w, device=dev), w.topk)
+    wq = ops.quantize_mx_expert_weights(d, moe_inputs.expert_weights(w, 13, device=dev),
+                                        moe_inputs.expert_weights(w, 2, device=dev))
+    torch.cuda.empty_cache()
+    ref = ops.MxMoELayer(d, wq, device=dev).forward(x, ids, tw, out_dtype=torch.float32).clone()
+    g = Guarded(dev)
+    layer = ops.MxMoELayer(d, wq, device=dev)
+    _guard_mx_layer(layer, g)
+    for dt in (torch.float32, torch.bfloat16):
+        out = g.make(torch.empty(w.T, w.H, dtype=dt, device=dev))
+        layer.forward(x, ids, tw, out=out)
+        g.check(f"{w.name} mxfp4 out={dt}")
+        want = ref if dt == torch.float32 else ref.to(torch.bfloat16)
+        assert torch.equal(out, want), f"{w.name} mxfp4 {dt}"
+    del layer, wq
+    torch.cuda.empty_cache()
