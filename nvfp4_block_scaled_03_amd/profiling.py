@@ -299,11 +299,15 @@ def _cmd_stats(a):
     rows = []
     with open(a.csv) as f:
         for r in csv.DictReader(f):
+            if a.exclude_re and re.search(a.exclude_re, r["Name"]):
+                continue
             rows.append((r["Name"], int(r["Calls"]), float(r["TotalDurationNs"]), float(r["AverageNs"]),
                          float(r["MinNs"]), float(r["MaxNs"])))
     total = sum(r[2] for r in rows)
     print(f"# rocprofv3 --kernel-trace --stats summary ({a.title})")
     print(f"# command: {a.command}")
+    if a.exclude_re:
+        print(f"# kernels matching /{a.exclude_re}/ left out (input and weight preparation)")
     print(f"# {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'share':>6}  kernel")
     for name, calls, tot, avg, mn, mx in sorted(rows, key=lambda r: -r[2])[:a.top]:
         short = re.sub(r"\(anonymous namespace\)::", "", name)
@@ -385,6 +389,7 @@ def main(argv=None):
     st.add_argument("--title", default="")
     st.add_argument("--command", default="")
     st.add_argument("--top", type=int, default=16)
+    st.add_argument("--exclude-re", dest="exclude_re", default="")
     a = p.parse_args(argv)
     {"gemm1": _cmd_gemm, "gemm2": _cmd_gemm, "layer": _cmd_layer, "copy": _cmd_copy,
      "traffic": _cmd_traffic, "stats": _cmd_stats, "counters": _cmd_counters}[a.cmd](a)
