@@ -8,19 +8,21 @@ A step is one pass of the whole layer path on one batch: global activation
 scale, activation quantisation, permutation by expert, grouped GEMM1 with
 SwiGLU and requantisation, grouped GEMM2 with the top-k weighted combine
 (W4A16: permutation and the two GEMMs; MXFP4: block-scale quantisation,
-permutation, the two GEMMs on the scaled FP4 matrix instruction).  Inputs (activations, routing,
-prepared weights) are resident in HBM before timing starts; routing and weight
-preparation are outside the step.  Several copies of the weights are rotated
+permutation, the two GEMMs on the scaled FP4 matrix instruction).  Inputs
+(activations, routing, prepared weights) are resident in HBM before timing
+starts; routing and weight preparation are outside the step.  Several copies of the weights are rotated
 between steps so the 256 MB Infinity Cache cannot serve repeats.
 
 Prints one JSON line.  ``value`` is the tokens/s of the headline workload
 (decode: T = 64, H = 2048, I = 768, E = 128, top-8) over exactly K timed
-steps.  ``configs`` holds every workload and variant (tiny, decode W4A16,
-prefill, large_e, skew in both NVFP4 variants; decode, prefill and large_e in
-OCP MXFP4), each with its step time over K
-steps, the median over >= 100 graph replays after >= 10 warm-up replays, the
-per-stage breakdown, and the roofline figures of its dominant kernel (GEMM1)
-measured with HIP events on the launch stream inside the timed region.
+steps, after W warm-up steps; the K steps are one replay of a graph holding
+K steps (default K = 200, W = 400: the device's clocks settle under
+sustained load).  ``configs`` holds every other workload and variant (tiny,
+decode W4A16, prefill, large_e, skew in both NVFP4 variants; decode, prefill
+and large_e in OCP MXFP4; K/4 steps after W/4), each with its mean step, the
+per-step median over 100 replays of its timed graph after 10 warm-up
+replays, the per-stage breakdown, and the roofline figures of its dominant
+kernel (GEMM1) measured with HIP events on the launch stream.
 ``cpu_baseline`` is the FP64 oracle timed on the host cores on a bounded
 sample.
 """
@@ -55,8 +57,10 @@ REPLAYS, REPLAY_WARMUP = 100, 10
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    # Defaults: enough warm-up (two replays of the timed graph) for the
+    # device's clocks to settle under sustained load before timing.
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=400)
     p.add_argument("--workload", default="decode", choices=moe_inputs.ORDER)
     p.add_argument("--variant", default="w4a4", choices=["w4a4", "w4a16", "mxfp4"])
     p.add_argument("--mode", default="graph", choices=["eager", "graph"])
@@ -155,9 +159,11 @@ def cpu_baseline(w, dev, seconds):
 
 
 # ---------------------------------------------------------------- GPU timing
-def make_graphs(layer, x, ids, tw, copies, variant, out):
-    """One graph per weight copy (a single step) and one graph holding one step
-    per copy in sequence, as a model forward captures its consecutive layers."""
+def make_graphs(layer, x, ids, tw, copies, variant, out, per_graph):
+    """One graph per weight copy (a single step) and one graph holding
+    ``per_graph`` steps in sequence, cycling through the weight copies, as a
+    model forward captures its consecutive layers in one graph (each replay
+    boundary leaves the GPU idle for several microseconds)."""
     graphs = []
     for wc in copies:
         for _ in range(2):
@@ -169,21 +175,42 @@ def make_graphs(layer, x, ids, tw, copies, variant, out):
         graphs.append(g)
     multi = torch.cuda.CUDAGraph()
     with torch.cuda.graph(multi):
-        for wc in copies:
-            layer.forward(x, ids, tw, variant, out=out, weights=wc)
+        for i in range(per_graph):
+            layer.forward(x, ids, tw, variant, out=out, weights=copies[i % len(copies)])
     return graphs, multi
 
 
-def time_steps(layer, x, ids, tw, copies, variant, steps, warmup, mode, graphs=None, multi=None):
+def upload_graph(g) -> bool:
+    """Upload an instantiated graph's executable to the device before its
+    first launch (hipGraphUpload), so that the timed replay does not pay the
+    one-time upload of a few hundred kernel nodes.  Uses the HIP runtime
+    already loaded in the process; returns False (nothing done) if that
+    cannot be found or the call fails."""
+    import ctypes
+    try:
+        path = next(line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line)
+        hip = ctypes.CDLL(path)
+        hip.hipGraphUpload.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipGraphUpload.restype = ctypes.c_int
+        rc = hip.hipGraphUpload(ctypes.c_void_p(g.raw_cuda_graph_exec()),
+                                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        return rc == 0
+    except (StopIteration, OSError, AttributeError, RuntimeError):
+        return False
+
+
+def time_steps(layer, x, ids, tw, copies, variant, steps, warmup, mode, graphs=None, multi=None,
+               per_graph=0):
     """Mean wall time of one layer step (ms) over exactly ``steps`` steps
     (synchronised on both sides); graph mode replays the multi-step graph and
     the one-step graphs for a remainder."""
     out = torch.empty(x.shape[0], layer.d.H, dtype=torch.bfloat16, device=x.device)
 
     def run(i0, count):
-        if multi is not None and count >= len(copies) and i0 % len(copies) == 0:
+        if multi is not None and count >= per_graph and i0 % len(copies) == 0:
             multi.replay()
-            return len(copies)
+            return per_graph
         if graphs:
             graphs[i0 % len(graphs)].replay()
         else:
@@ -202,7 +229,7 @@ def time_steps(layer, x, ids, tw, copies, variant, steps, warmup, mode, graphs=N
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
-def replay_median(multi, n_copies, replays=REPLAYS, warmup=REPLAY_WARMUP):
+def replay_median(multi, per_graph, replays=REPLAYS, warmup=REPLAY_WARMUP):
     """Median (and spread) of the per-step time over ``replays`` replays of
     the multi-step graph, each bracketed by events on the current stream."""
     for _ in range(warmup):
@@ -214,7 +241,7 @@ def replay_median(multi, n_copies, replays=REPLAYS, warmup=REPLAY_WARMUP):
         multi.replay()
         ev[i + 1].record()
     torch.cuda.synchronize()
-    per = sorted(ev[i].elapsed_time(ev[i + 1]) / n_copies for i in range(replays))
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) / per_graph for i in range(replays))
     return {"replays": replays, "warmup_replays": warmup, "median_ms": round(statistics.median(per), 5),
             "p10_ms": round(per[replays // 10], 5), "p90_ms": round(per[(9 * replays) // 10], 5)}
 
@@ -290,10 +317,14 @@ def measure(w, built, variant, steps, warmup, mode, mx_weights=None):
         layer = ops.MoELayer(d, wq, g2, device=x.device)
     out = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=x.device)
     graphs = multi = None
+    # The timed steps are one replay of a graph of that many steps.
+    per_graph = max(steps, len(copies))
+    uploaded = False
     if mode == "graph":
-        graphs, multi = make_graphs(layer, x, ids, tw, copies, variant, out)
-    ms = time_steps(layer, x, ids, tw, copies, variant, steps, warmup, mode, graphs, multi)
-    rep = replay_median(multi, len(copies)) if multi is not None else None
+        graphs, multi = make_graphs(layer, x, ids, tw, copies, variant, out, per_graph)
+        uploaded = upload_graph(multi)
+    ms = time_steps(layer, x, ids, tw, copies, variant, steps, warmup, mode, graphs, multi, per_graph)
+    rep = replay_median(multi, per_graph) if multi is not None else None
     bd = breakdown(layer, x, ids, tw, copies, variant)
     g1_ms = time_gemm1(layer, x, ids, tw, copies, variant)
     g1_flops = 2.0 * P * (2 * w.I) * w.H
@@ -318,6 +349,7 @@ def measure(w, built, variant, steps, warmup, mode, mx_weights=None):
     rec = {
         "workload": w.name, **w.describe(), "variant": variant, "mode": mode,
         "experts_touched": touched, "weight_copies": len(copies),
+        "steps_per_graph": per_graph if mode == "graph" else 1, "graph_uploaded": uploaded,
         "steps": steps, "ms_per_step": round(ms, 5), "tokens_per_s": round(w.T / (ms * 1e-3), 1),
         "layer_tflops": round(layer_flops / (ms * 1e-3) / 1e12, 2),
         "layer_gbs": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
@@ -449,7 +481,7 @@ def main():
         "data": "synthetic (seeded), random-init weights",
         "config": {"workload": w.name, **w.describe(), "variant": a.variant, "mode": a.mode,
                    "experts_touched": m["experts_touched"], "weight_copies": m["weight_copies"],
-                   "steps_per_graph": m["weight_copies"] if a.mode == "graph" else 1},
+                   "steps_per_graph": m["steps_per_graph"], "graph_uploaded": m["graph_uploaded"]},
         "layer_tflops": m["layer_tflops"], "layer_gbs": m["layer_gbs"],
         "layer_hbm_frac": m["layer_hbm_frac"],
         "roofline": m["roofline"],
@@ -471,9 +503,9 @@ def main():
                 log(f"[bench] building {name} layer")
                 built[name] = build_layer(wc, dev, weights=reuse)
             log(f"[bench] {name} {variant}")
-            steps = max(5, a.steps // 2)
+            steps = max(5, a.steps // 4)
             res["configs"][f"{name}_{variant}"] = measure(
-                wc, built[name], variant, steps, max(3, a.warmup // 2), a.mode,
+                wc, built[name], variant, steps, max(3, a.warmup // 4), a.mode,
                 mx_weights(name) if variant == "mxfp4" else None)
     built.clear()
     mx.clear()
