@@ -627,7 +627,8 @@ int grouped_gemm1_swiglu_mxfp4(const nvfp4_moe_dims* d, const uint8_t* a1_q, con
                 d->E + d->shared, (long long)pairs(d), 2 * d->I, d->H);
   if (d->T == 0) return ok();
   if (!a1_q || !a1_e || !sorted_pair || !expert_offsets || !plan || !w13_prep || !a2_q || !a2_e ||
-      !aligned(a1_q, 16) || !aligned(a1_e, 4) || !aligned(w13_prep, 16))
+      !aligned(a1_q, 16) || !aligned(a1_e, 4) || !aligned(w13_prep, 16) || !aligned(a2_q, 16) ||
+      !aligned(a2_e, 4))
     return gemm_fail_shape(W, d, 2 * d->I, d->H, 0);
   nvfp4::MxGemmArgs a = mx_args(d);
   a.sorted_pair = sorted_pair;

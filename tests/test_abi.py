@@ -125,6 +125,8 @@ def test_zero_tokens_is_a_noop(lib, shared):
     assert lib.moe_quantize_and_align(r, None, None, None, 0, *([None] * 9), 0, None) == _lib.NVFP4_OK
     assert lib.nvfp4_quantize(None, 0, 0, 32, 32, None, 1, None, None, None, None) == _lib.NVFP4_OK
     assert lib.moe_route_topk(None, 0, 8, 2, None, None, None) == _lib.NVFP4_OK
+    assert lib.grouped_gemm1_swiglu_mxfp4(r, *([None] * 8), None) == _lib.NVFP4_OK
+    assert lib.grouped_gemm2_combine_mxfp4(r, *([None] * 7), None, 0, None, 0, None) == _lib.NVFP4_OK
     assert _lib.last_error() == ""
     # bad dims are still rejected at T == 0
     bad = _d(T=0, H=100)
@@ -194,3 +196,26 @@ def test_missing_library_fails_loudly(tmp_path):
             _lib.load(str(tmp_path / "nope.so"))
         finally:
             _lib._lib = old
+
+
+def test_mx_layer_errors(lib):
+    """The MXFP4 layer calls validate before launching: missing or misaligned
+    operands are rejected with the GEMM's shape in the message, prep needs
+    MX-sized blocks, and the 2^31 operand-offset limit is checked."""
+    d = _d()
+    r = ctypes.byref(d)
+    assert lib.mxfp4_prep_expert_weights_size(r, 13) > 0
+    assert lib.mxfp4_prep_expert_weights_size(r, 7) == 0
+    assert lib.grouped_gemm1_swiglu_mxfp4(r, *([None] * 8), None) == _lib.NVFP4_EINVAL
+    assert "grouped_gemm1_swiglu_mxfp4" in _lib.last_error()
+    # every pointer present but a2 codes misaligned
+    p = [ctypes.c_void_p(256)] * 8
+    p[6] = ctypes.c_void_p(256 + 4)
+    assert lib.grouped_gemm1_swiglu_mxfp4(r, *p, None) == _lib.NVFP4_EINVAL
+    # GEMM2: the workspace size is checked first, then the operands
+    assert lib.grouped_gemm2_combine_mxfp4(r, *([None] * 7), None, 0, None, 0, None) == _lib.NVFP4_EWORKSPACE
+    ws = lib.grouped_gemm_workspace_size(r)
+    assert lib.grouped_gemm2_combine_mxfp4(r, *([None] * 7), None, 0, ctypes.c_void_p(256), ws,
+                                           None) == _lib.NVFP4_EINVAL
+    big = _d(T=1 << 17, H=1 << 15)
+    assert lib.grouped_gemm1_swiglu_mxfp4(ctypes.byref(big), *([None] * 8), None) == _lib.NVFP4_ESHAPE
