@@ -438,11 +438,12 @@ def linear_sweep(dev, copies=3, reps=10):
 
 # ---------------------------------------------------------------- main
 # The other workloads and variants reported next to the headline line (the
-# five workload shapes in both NVFP4 variants, three of them in MXFP4).
+# five workload shapes in both NVFP4 variants, three of them in MXFP4, and one
+# GPU's share of the prefill layer under 8-way expert parallelism).
 # Prefill reuses the decode layer's weights (the same expert shape).
 OTHER_CONFIGS = [("decode", "w4a16"), ("decode", "mxfp4"), ("tiny", "w4a4"), ("prefill", "w4a4"),
                  ("prefill", "w4a16"), ("prefill", "mxfp4"), ("large_e", "w4a4"), ("large_e", "w4a16"),
-                 ("large_e", "mxfp4"), ("skew", "w4a4"), ("skew", "w4a16")]
+                 ("large_e", "mxfp4"), ("skew", "w4a4"), ("skew", "w4a16"), ("ep8_share", "w4a4")]
 
 
 def main():

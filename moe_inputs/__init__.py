@@ -15,6 +15,8 @@ Workloads (shapes and value distributions):
 * ``large_e``  T=256,  H=4096, I=1024, E=512 + 1 shared expert, top-10,
                Zipf(1.1)-skewed logits, sigma 0.015
 * ``skew``     T=8192, H=2048, I=768,  E=128, top-8, Zipf(1.3)-skewed logits
+* ``ep8_share`` T=512, H=2048, I=768, E=16, top-8 (one GPU's share of
+               ``prefill`` under 8-way expert parallelism)
 
 The expert shapes follow the 30B-A3B mixture-of-experts model the pages serve
 (vLLM PR #29242, "Test Plan"), and the 512-routed + 1-shared, top-10 layout is
@@ -82,9 +84,13 @@ WORKLOADS = {
     "prefill": Workload("prefill", 4096, 2048, 768, 128, 8, 0, 0.0, 0.02, 0.01, 1002),
     "large_e": Workload("large_e", 256, 4096, 1024, 512, 10, 1, 1.1, 0.015, 0.01, 1003),
     "skew": Workload("skew", 8192, 2048, 768, 128, 8, 0, 1.3, 0.02, 0.01, 1004),
+    # One GPU's share of the prefill layer under 8-way expert parallelism:
+    # 16 of the 128 experts with the 4096 pairs routed to them (about 256
+    # rows each), as 512 tokens routed top-8 over 16 experts.
+    "ep8_share": Workload("ep8_share", 512, 2048, 768, 16, 8, 0, 0.0, 0.02, 0.01, 1005),
 }
 
-ORDER = ["tiny", "decode", "prefill", "large_e", "skew"]
+ORDER = ["tiny", "decode", "prefill", "large_e", "skew", "ep8_share"]
 
 
 def _gen(device, seed: int) -> torch.Generator:
