@@ -36,11 +36,16 @@ def dev():
 
 
 class MxCase:
-    def __init__(self, w: Workload, dev, tokens=None):
+    def __init__(self, w: Workload, dev, tokens=None, routing=None):
+        """``routing``: (ids [T, k] int32, weights [T, k] f32) given directly
+        instead of the router's choice on the workload's logits."""
         self.w = w
         self.d = ops.dims(w.T, w.topk, w.E, w.H, w.I, w.shared)
         self.x = moe_inputs.activations(w, device=dev)
-        ids, tw = oroute.route_topk(to_np(moe_inputs.router_logits(w, device=dev)), w.topk)
+        if routing is None:
+            ids, tw = oroute.route_topk(to_np(moe_inputs.router_logits(w, device=dev)), w.topk)
+        else:
+            ids, tw = routing
         self.ids_np, self.tw_np = ids, tw
         self.ids = torch.from_numpy(ids).to(dev)
         self.tw = torch.from_numpy(tw).to(dev)
@@ -121,3 +126,37 @@ def test_mx_layer_full_size_hot_expert(dev, name):
         tok, _ = omoe.pair_token_weight(sp[rows], w.T, w.topk, case.tw_np)
         h = omoe.swiglu(x_hat[tok] @ case.ew.dequantized(13, e).T, w.I)
         check_a2_mx(to_np(layer.a2_q)[rows], to_np(layer.a2_e)[rows], h, what=f"{name} mx expert rows")
+
+
+# Routing by expert row counts (top-1, weight 1, the tokens of an expert
+# scattered over the batch) at the expert shape (H = 2048, I = 768), so that
+# the tall-tile kernel runs its straight-line bodies for K = 2048 (GEMM1) and
+# K = 768 (GEMM2).
+RAGGED_COUNTS = [1, 16, 17, 32, 33, 64, 65, 128, 129, 0, 200, 255, 256, 257, 300]
+SPLIT_COUNTS = [200, 100, 40, 33, 32, 17, 16, 15, 8, 5, 4, 3, 2, 1, 0, 1] + [3] * 24
+
+
+def _routed(counts, name, seed, dev):
+    w = Workload(name, int(sum(counts)), 2048, 768, len(counts), 1, 0, 0.0, 0.02, 0.01, seed)
+    ids = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    ids = ids[np.random.default_rng(seed).permutation(ids.size)].reshape(-1, 1)
+    return MxCase(w, dev, routing=(ids, np.ones((w.T, 1), dtype=np.float32)))
+
+
+@pytest.mark.timeout(600)
+def test_mx_layer_ragged_tile_heights(dev):
+    """Every token of a layer whose experts end in 128-row tiles of every
+    class of active 16-row groups (1, 2, 4, 8 at both ends of each range)
+    plus an empty expert: the tall-tile kernel's four instantiations."""
+    case = _routed(RAGGED_COUNTS, "mx_ragged", 81, dev)
+    assert case.w.pairs / case.w.E > 96
+    _judge(case, dev)
+
+
+@pytest.mark.timeout(600)
+def test_mx_layer_split_short_and_tall_experts(dev):
+    """Short experts on average (the 16-row kernel) with a few tall ones
+    (more than 32 rows: the tall-tile kernel, a second launch)."""
+    case = _routed(SPLIT_COUNTS, "mx_split", 82, dev)
+    assert case.w.pairs / case.w.E <= 16 and case.w.T > 64
+    _judge(case, dev)
