@@ -1180,7 +1180,16 @@ void grouped_gemm_stream4_kernel(KParams p) {
 }
 
 // out[t] = sum_j w[t][j] * d[inv_pos[t*k + j]] (+ shared row), FP32, j ascending.
-template <bool BF16>
+// NT: read the rows with non-temporal loads (for workspaces larger than the
+// caches; a small workspace, still cached from GEMM2, is read faster with
+// ordinary loads).
+template <bool BF16, bool NT>
+__device__ __forceinline__ f32x4 load_row4(const float* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  else return *reinterpret_cast<const f32x4*>(p);
+}
+
+template <bool BF16, bool NT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ d,
                                                       const int32_t* __restrict__ inv_pos,
                                                       const float* __restrict__ topk_w, int T,
@@ -1192,9 +1201,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   // Batches of 8 pairs: positions and weights (the same for the whole block)
   // through scalar loads, then all 8 row loads in flight together, then the
   // sum in ascending j (selects, not branches, so no load waits on another).
-  // Each row is read exactly once: non-temporal loads keep the streamed rows
-  // from displacing other data in the caches (Zipf-skewed prefill: the
-  // combine 127 -> 97 us).
   constexpr int B = 8;
   for (int j0 = 0; j0 < topk; j0 += B) {
     int pos[B];
@@ -1207,14 +1213,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       w[b] = j < topk ? ld_uniform(topk_w + (int64_t)t * topk + j) : 0.0f;
     }
 #pragma unroll
-    for (int b = 0; b < B; ++b)
-      x[b] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(d + (int64_t)max(pos[b], 0) * H + c));
+    for (int b = 0; b < B; ++b) x[b] = load_row4<BF16, NT>(d + (int64_t)max(pos[b], 0) * H + c);
 #pragma unroll
     for (int b = 0; b < B; ++b) a = pos[b] >= 0 ? a + w[b] * x[b] : a;
   }
   if (shared) {
     const int pos = inv_pos[(int64_t)T * topk + t];
-    if (pos >= 0) a += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(d + (int64_t)pos * H + c));
+    if (pos >= 0) a += load_row4<BF16, NT>(d + (int64_t)pos * H + c);
   }
   if constexpr (BF16) {
     uint32_t lo = f32_to_bf16_bits(a[0]) | (f32_to_bf16_bits(a[1]) << 16);
@@ -1540,10 +1545,18 @@ hipError_t launch_combine(const float* d, const int32_t* inv_pos, const float* t
                           int shared, int H, void* out, int out_dtype, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const dim3 cgrid(T, (H + 1023) / 1024);
-  if (out_dtype == 0)
-    combine_kernel<true><<<cgrid, 256, 0, s>>>(d, inv_pos, topk_w, T, topk, shared, H, out);
-  else
-    combine_kernel<false><<<cgrid, 256, 0, s>>>(d, inv_pos, topk_w, T, topk, shared, H, out);
+  // Non-temporal reads once the workspace exceeds half the 256 MB Infinity
+  // Cache (measured: Zipf-skewed prefill, 537 MB, 127 -> 93 us; even
+  // prefill, 268 MB, 53 -> 51 us; the 512-expert layer's 46 MB, 9.8 ->
+  // 11.7 us, so small workspaces keep ordinary loads).
+  const bool nt = (int64_t)T * (topk + shared) * H * 4 > (int64_t(128) << 20);
+  if (out_dtype == 0) {
+    if (nt) combine_kernel<true, true><<<cgrid, 256, 0, s>>>(d, inv_pos, topk_w, T, topk, shared, H, out);
+    else combine_kernel<true, false><<<cgrid, 256, 0, s>>>(d, inv_pos, topk_w, T, topk, shared, H, out);
+  } else {
+    if (nt) combine_kernel<false, true><<<cgrid, 256, 0, s>>>(d, inv_pos, topk_w, T, topk, shared, H, out);
+    else combine_kernel<false, false><<<cgrid, 256, 0, s>>>(d, inv_pos, topk_w, T, topk, shared, H, out);
+  }
   return hipGetLastError();
 }
 
