@@ -328,21 +328,24 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(AlignP a, int32_t* __r
 }
 
 // ---------------------------------------------------------------- scatter
-__global__ __launch_bounds__(256) void align_scatter_kernel(AlignP a,
-                                                            const int32_t* __restrict__ bases,
-                                                            int32_t* __restrict__ sorted_pair,
-                                                            int32_t* __restrict__ inv_pos) {
+// Places the pairs of one chunk: each pair's row is its expert's base for
+// the chunk plus its rank among the chunk's earlier pairs of that expert
+// (wavefront ballots within a round of 256, LDS counts across wavefronts and
+// rounds), so the order is stable and no atomic decides a position.
+__device__ __forceinline__ void scatter_chunk(const AlignP& a, const int32_t* __restrict__ bases,
+                                              int32_t* __restrict__ sorted_pair,
+                                              int32_t* __restrict__ inv_pos, int chunk) {
   __shared__ int running[kMaxExperts];
   __shared__ int wcnt[4][kMaxExperts];
   for (int e = threadIdx.x; e < a.slots; e += 256) {
-    running[e] = bases[(int64_t)blockIdx.x * a.slots + e];
+    running[e] = bases[(int64_t)chunk * a.slots + e];
     wcnt[0][e] = wcnt[1][e] = wcnt[2][e] = wcnt[3][e] = 0;
   }
   __syncthreads();
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int r = 0; r < kAlignChunk / 256; ++r) {
-    const int64_t f = (int64_t)blockIdx.x * kAlignChunk + r * 256 + threadIdx.x;
+    const int64_t f = (int64_t)chunk * kAlignChunk + r * 256 + threadIdx.x;
     const bool in = f < a.P;
     bool valid = false;
     int e = in ? expert_of(a, f, valid) : 0;
@@ -374,6 +377,13 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(AlignP a,
     }
     __syncthreads();
   }
+}
+
+__global__ __launch_bounds__(256) void align_scatter_kernel(AlignP a,
+                                                            const int32_t* __restrict__ bases,
+                                                            int32_t* __restrict__ sorted_pair,
+                                                            int32_t* __restrict__ inv_pos) {
+  scatter_chunk(a, bases, sorted_pair, inv_pos, blockIdx.x);
 }
 
 // ---------------------------------------------------------------- one workgroup
@@ -567,6 +577,111 @@ __global__ __launch_bounds__(1024) void scale_align_kernel(const uint16_t* __res
     return;
   }
   fold_max_and_count(ws, ws + 1, r, (uint32_t)nblk, g);
+}
+
+// ---------------------------------------------------------------- large batches
+// Global scale, quantisation and alignment when the pairs exceed one
+// workgroup's alignment (P > kSmallP): three launches instead of the five
+// of the separate steps (scale, count, scan, scatter, quantise), and no
+// cross-workgroup atomics.
+//   1. scale_count_kernel: workgroups [0, nb) each store max |x| over their
+//      share of the tensor in partial[b]; workgroups [nb, nb + nchunks) each
+//      count the experts of one pair chunk.
+//   2. scan_scale_kernel: the one-workgroup scan (chunk bases, offsets, tile
+//      lists), which also takes the maximum of the nb partial maxima and
+//      writes g.
+//   3. scatter_quant_kernel: workgroups [0, nchunks) place the pairs of one
+//      chunk; the others quantise x with g, one lane per 8 elements.
+// A maximum is exact in any grouping, so g is bit for bit the one of the
+// single-launch reduction (nvfp4_global_scale).
+constexpr int kScalePartials = 1024;  // most workgroups of the fused global scale
+constexpr int kScaleThreads = 256;
+constexpr int kScaleLoads = 8;   // 16-byte loads per thread and trip
+
+__global__ __launch_bounds__(kScaleThreads) void scale_count_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                                    int nb, float* __restrict__ partial,
+                                                                    AlignP a, int32_t* __restrict__ counts) {
+  if ((int)blockIdx.x >= nb) {
+    count_chunk(a, counts, (int)blockIdx.x - nb);
+    return;
+  }
+  __shared__ float red[kScaleThreads / 64];
+  constexpr int U = kScaleLoads;
+  const int64_t stride = (int64_t)nb * kScaleThreads * 8;
+  float m = 0.0f;
+  int64_t i = ((int64_t)blockIdx.x * kScaleThreads + threadIdx.x) * 8;
+  for (; i + (U - 1) * stride < n; i += U * stride) {
+    u32x4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = *reinterpret_cast<const u32x4*>(x + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        m = fmaxf(m, amax_input(bf16_bits_to_f32(w[u][j] & 0xFFFFu)));
+        m = fmaxf(m, amax_input(bf16_bits_to_f32(w[u][j] >> 16)));
+      }
+  }
+  for (; i < n; i += stride) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(x + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m = fmaxf(m, amax_input(bf16_bits_to_f32(w[j] & 0xFFFFu)));
+      m = fmaxf(m, amax_input(bf16_bits_to_f32(w[j] >> 16)));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+#pragma unroll
+    for (int k = 1; k < kScaleThreads / 64; ++k) r = fmaxf(r, red[k]);
+    partial[blockIdx.x] = r;
+  }
+}
+
+__global__ __launch_bounds__(1024) void scan_scale_kernel(AlignP a, int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ plan, PlanOffs list_off,
+                                                          const float* __restrict__ partial, int nb,
+                                                          float* __restrict__ g) {
+  // (requested first, so its latency overlaps the scan's own loads)
+  float m = (int)threadIdx.x < nb ? partial[threadIdx.x] : 0.0f;
+  scan_body(a, counts, offsets, plan, list_off);
+  __shared__ float red[16];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+#pragma unroll
+    for (int k = 1; k < 16; ++k) r = fmaxf(r, red[k]);
+    *g = global_scale_of_amax(r);
+  }
+}
+
+__global__ __launch_bounds__(256) void scatter_quant_kernel(AlignP a, const int32_t* __restrict__ bases,
+                                                            int32_t* __restrict__ sorted_pair,
+                                                            int32_t* __restrict__ inv_pos,
+                                                            const uint16_t* __restrict__ x, uint32_t n_hb,
+                                                            uint32_t hb_per_row, int64_t H,
+                                                            const float* __restrict__ g,
+                                                            uint8_t* __restrict__ q, uint8_t* __restrict__ sf,
+                                                            uint16_t* __restrict__ x_deq) {
+  if ((int)blockIdx.x < a.nchunks) {
+    scatter_chunk(a, bases, sorted_pair, inv_pos, blockIdx.x);
+    return;
+  }
+  // Half-block i (8 elements); both lanes of a block leave together (H is a
+  // multiple of 16).  32-bit indices: n_hb < 2^31 (checked by the launcher).
+  const uint32_t i = ((uint32_t)blockIdx.x - (uint32_t)a.nchunks) * 256u + threadIdx.x;
+  if (i >= n_hb) return;
+  const uint32_t row = i / hb_per_row;
+  quantize_half_block(x, (int64_t)row, (int64_t)(i - row * hb_per_row) << 3, H, H, ld_uniform(g), q, sf,
+                      x_deq);
 }
 
 // ---------------------------------------------------------------- quantise + align
@@ -827,7 +942,10 @@ AlignShape align_shape(int T, int topk, int E, int shared) {
 }
 
 size_t align_ws_bytes(const AlignShape& a) {
-  return (size_t)a.nchunks * (size_t)a.slots * sizeof(int32_t);
+  // per-chunk expert counts, then (batches past one workgroup's alignment)
+  // the partial maxima of the fused global scale
+  const size_t part = a.P > (int64_t)kSmallP ? (size_t)kScalePartials * sizeof(float) : 0;
+  return (size_t)a.nchunks * (size_t)a.slots * sizeof(int32_t) + part;
 }
 
 size_t align_plan_ints(const AlignShape& a) {
@@ -902,6 +1020,33 @@ hipError_t launch_quantize_and_align(const AlignShape& a, const uint16_t* x, flo
                                     const int32_t* topk_ids, int32_t* offsets, int32_t* sorted_pair,
                                     int32_t* inv_pos, int32_t* plan, void* ws, hipStream_t s) {
   const int64_t n = (int64_t)a.T * a.H;
+  if (a.P > (int64_t)kSmallP && n > 0 && n / 8 < (int64_t(1) << 31)) {
+    AlignP p;
+    p.ids = topk_ids;
+    p.T = a.T;
+    p.topk = a.topk;
+    p.E = a.E;
+    p.shared = a.shared;
+    p.slots = a.slots;
+    p.nchunks = a.nchunks;
+    p.P = a.P;
+    int32_t* counts = static_cast<int32_t*>(ws);
+    float* partial = reinterpret_cast<float*>(counts + (int64_t)a.nchunks * a.slots);
+    // one trip of kScaleLoads loads per thread when the tensor allows
+    const int64_t per_blk = (int64_t)kScaleThreads * 8 * kScaleLoads;
+    const int nb = (int)std::min<int64_t>(kScalePartials, std::max<int64_t>(1, (n + per_blk - 1) / per_blk));
+    scale_count_kernel<<<nb + a.nchunks, kScaleThreads, 0, s>>>(x, n, nb, partial, p, counts);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    scan_scale_kernel<<<1, 1024, 0, s>>>(p, counts, offsets, plan, plan_offsets(a), partial, nb, g);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n_hb = n / 8;
+    const int64_t qblocks = (n_hb + 255) / 256;
+    scatter_quant_kernel<<<(unsigned)(a.nchunks + qblocks), 256, 0, s>>>(
+        p, counts, sorted_pair, inv_pos, x, (uint32_t)n_hb, (uint32_t)(a.H >> 3), a.H, g, q, sf, x_deq);
+    return hipGetLastError();
+  }
   if (a.P > (int64_t)kSmallP || n == 0 || n > kFusedQuantMax) {
     hipError_t e = launch_scale_and_align(a, x, g, gs_ws, topk_ids, offsets, sorted_pair, inv_pos, plan,
                                           ws, s);

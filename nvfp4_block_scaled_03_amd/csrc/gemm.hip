@@ -617,15 +617,19 @@ __global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
 // Waves per SIMD: 2 with 64 columns per wavefront, 1 with 128 (its 256
 // accumulators take the accumulation registers).
 #define NVFP4_WIDE_WPE (NVFP4_WIDE_WN == 128 ? 1 : 2)
+#ifndef NVFP4_TALL_WN
+#define NVFP4_TALL_WN 64       // columns per wavefront of the wide kernel for the tall experts of a split layer
+#endif
 constexpr int kWideBM = 128, kWideWN = NVFP4_WIDE_WN, kWideNW = NVFP4_WIDE_NW;
 
-template <int AK, int EPI>
+template <int AK, int EPI, int WN>
 __global__ __launch_bounds__(kWideNW * kWave)
 __attribute__((amdgpu_waves_per_eu(NVFP4_WIDE_WPE, NVFP4_WIDE_WPE)))
 void grouped_gemm_wide_kernel(KParams p) {
   static_assert(kWideNW == 4 || kWideNW == 8, "4 or 8 wavefronts");
   static_assert(AK != kActCodes, "the wide kernel takes 16-bit activations");
-  constexpr int MT = kWideBM / 16, NTW = kWideWN / 16, NW = kWideNW;
+  static_assert(WN == 32 || WN == 64 || WN == 128, "whole tile pairs per wavefront");
+  constexpr int MT = kWideBM / 16, NTW = WN / 16, NW = kWideNW;
   constexpr int ROW_BYTES = kBK * 2;                       // 256
   constexpr int BUF_BYTES = kWideBM * ROW_BYTES;           // 32 KiB
   constexpr int LOADS = BUF_BYTES / (NW * kWave * 16);     // direct loads per thread per chunk: 8
@@ -639,7 +643,7 @@ void grouped_gemm_wide_kernel(KParams p) {
   if (!decode_tile(p, t)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n_wave0 = (t.nb * NW + wv) * kWideWN;
+  const int n_wave0 = (t.nb * NW + wv) * WN;
   const bool wave_on = n_wave0 < p.N;
   const int K = p.K, KC = K / kBK, NT = p.N / 16;
 
@@ -1340,12 +1344,12 @@ __global__ __launch_bounds__(4 * kWave) void linear_splitk_kernel(KParams p) {
 }
 
 
-template <int AK, int EPI>
+template <int AK, int EPI, int WN = kWideWN>
 hipError_t launch_wide(KParams kp, int list_len, hipStream_t s) {
-  kp.n_blocks = (kp.N + kWideNW * kWideWN - 1) / (kWideNW * kWideWN);
+  kp.n_blocks = (kp.N + kWideNW * WN - 1) / (kWideNW * WN);
   const int64_t G = (int64_t)list_len * kp.n_blocks;
   const int64_t grid = std::max<int64_t>(8, (G + 7) / 8 * 8);
-  grouped_gemm_wide_kernel<AK, EPI><<<(unsigned)grid, kWideNW * kWave, 0, s>>>(kp);
+  grouped_gemm_wide_kernel<AK, EPI, WN><<<(unsigned)grid, kWideNW * kWave, 0, s>>>(kp);
   return hipGetLastError();
 }
 
@@ -1428,7 +1432,7 @@ hipError_t launch_gemm(KParams kp, const AlignShape& al, hipStream_t s) {
       hipError_t e = launch_stream_pf<AK, EPI, 1, kStreamNTW>(kp, (int)al.list_len[4], s);
       if (e != hipSuccess) return e;
       kp.list_idx = 5;
-      return launch_wide<AK, EPI>(kp, (int)al.list_len[5], s);
+      return launch_wide<AK, EPI, NVFP4_TALL_WN>(kp, (int)al.list_len[5], s);
     }
   }
   kp.list_idx = li;

@@ -180,14 +180,22 @@ def test_scale_and_align(dev, name):
 _LIMIT = moe_inputs.Workload("limit", 128, 2048, 256, 64, 6, 1, 1.1, 0.02, 0.01, 41)  # T*H = 2^18
 
 
-@pytest.mark.parametrize("name", ["decode", "tiny", "limit", "large_e", "prefill", "skew"])
+# 10240 tokens: past the 1024 partial maxima of one load trip each (a
+# second, partial trip per thread) and past the 64 chunks whose counts the
+# scan keeps in registers.
+_BIG = moe_inputs.Workload("big", 10240, 2048, 256, 128, 8, 0, 0.0, 0.02, 0.01, 43)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["decode", "tiny", "limit", "large_e", "prefill", "skew", "big"])
 def test_quantize_and_align(dev, name):
     """One call = global scale + quantisation (+ exact f16 copy) + alignment,
     bit-exact against the oracle: one launch up to T*H = 2^18 and P = 4096
     (decode, tiny, limit); the scale+align launch then quantisation beyond
-    (large_e); for P > 4096 the scale beside the counts, the quantisation
-    beside the scan, then the scatter (prefill: 32 chunks of pairs, skew: 64)."""
-    w = _LIMIT if name == "limit" else moe_inputs.WORKLOADS[name]
+    (large_e); for P > 4096 three launches -- partial maxima beside the
+    chunk counts, the scan (which also finishes g), then the scatter beside
+    the quantisation (prefill: 32 chunks of pairs, skew: 64, big: 80)."""
+    w = {"limit": _LIMIT, "big": _BIG}.get(name) or moe_inputs.WORKLOADS[name]
     x = moe_inputs.activations(w, device=dev)
     ids, _ = oroute.route_topk(to_np(moe_inputs.router_logits(w, device=dev)), w.topk)
     d = ops.dims(w.T, w.topk, w.E, w.H, w.I, w.shared)

@@ -209,14 +209,15 @@ def test_scale_decisions_at_every_midpoint(dev):
         assert np.array_equal(q[r:r + 1], onv.pack_codes(c)), r
 
 
-@pytest.mark.parametrize("T", [64, 4096])
+@pytest.mark.parametrize("T", [64, 4096, 8192])
 def test_nan_takes_no_part_in_the_amax(dev, T):
     """A NaN (quiet and signalling bf16 patterns) takes no part in the global
-    or the block amax on either dispatch path of the activation step: the
-    fused decode-sized kernel (T = 64) and the separate scale and quantise
-    launches (T = 4096) give g1 = the oracle's scale of x with the NaNs set
-    to 0, the oracle's codes and scales on every block without a NaN, and the
-    two paths agree bit for bit on every byte."""
+    or the block amax on any dispatch path of the activation step: the
+    fused decode-sized kernel (T = 64), the scale+align launch then the
+    quantisation (T = 4096, P = 4096) and the three-launch form with partial
+    maxima (T = 8192, P > 4096) give g1 = the oracle's scale of x with the
+    NaNs set to 0, the oracle's codes and scales on every block without a
+    NaN, and agree bit for bit with the separate calls on every byte."""
     H = 2048
     gen = torch.Generator(device=dev).manual_seed(T)
     x = torch.randn(T, H, generator=gen, device=dev).to(torch.bfloat16)
