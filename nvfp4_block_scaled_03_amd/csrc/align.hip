@@ -154,79 +154,9 @@ __device__ void block_exclusive_scan_1024_v(const int (&v)[V], int (&out)[V], in
   __syncthreads();
 }
 
-// ---------------------------------------------------------------- scan + plan
-// Writes the six tile lists from the per-expert row counts (thread e = expert
-// slot e), in two groups of three lists, which keeps the register use of the
-// 1024-thread kernel below its limit.  When no expert has more than
-// kOwnTiles tiles in these lists, each lane writes its own expert's tiles.
-// Otherwise the tiles of a list are shared out over all 1024 threads (tile t
-// to thread t mod 1024), each finding the expert of its tile by binary
-// search over the experts' first tiles in LDS, so the time does not depend
-// on how the rows are spread over the experts.  Measured with 65536 pairs:
-// Zipf-1.3 routing (one expert with about 8100 rows) 51.8 us with a lane per
-// expert, 17.4 us shared out; even routing (32768 pairs, 16 tiles per
-// expert at most) 10.1 us with a lane per expert, 12.1 us shared out.
-template <int B0>
-__device__ __forceinline__ void write_plan_group(int32_t* __restrict__ plan, const PlanOffs& lo, int e,
-                                                 int slots, int off_e, int n_e) {
-  constexpr int V = 3;
-  __shared__ int first[V][kMaxExperts];   // first tile of expert e in each list
-  __shared__ int e_start[kMaxExperts], e_rows[kMaxExperts];
-  int tiles[V], tstart[V], ntiles[V];
-#pragma unroll
-  for (int b = 0; b < V; ++b)
-    tiles[b] = (e < slots && plan_list_has(B0 + b, n_e)) ? (n_e + kPlanBMs[B0 + b] - 1) / kPlanBMs[B0 + b] : 0;
-  block_exclusive_scan_1024_v<V>(tiles, tstart, ntiles);
-  if (e == 0) {
-#pragma unroll
-    for (int b = 0; b < V; ++b) {
-      plan[B0 + b] = ntiles[b];
-      plan[kPlanLists + B0 + b] = lo.v[B0 + b];
-    }
-  }
-  int heavy = 0;
-#pragma unroll
-  for (int b = 0; b < V; ++b) heavy |= tiles[b] > kOwnTiles;
-  if (!__syncthreads_or(heavy)) {   // block-uniform
-#pragma unroll
-    for (int b = 0; b < V; ++b)   // tiles[b] is 0 for e >= slots
-      for (int mt = 0; mt < tiles[b]; ++mt)
-        write_tile(plan + lo.v[B0 + b] + 2 * (tstart[b] + mt), e, mt, kPlanBMs[B0 + b], off_e, n_e);
-    return;
-  }
-  if (e < slots) {
-#pragma unroll
-    for (int b = 0; b < V; ++b) first[b][e] = tstart[b];
-    e_start[e] = off_e;
-    e_rows[e] = n_e;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int b = 0; b < V; ++b) {
-    for (int t = threadIdx.x; t < ntiles[b]; t += 1024) {
-      // The last expert whose first tile is <= t owns tile t (an expert
-      // with no tile here shares its first index with the next expert).
-      int l = 0, h = slots - 1;
-      while (l < h) {
-        const int mid = (l + h + 1) >> 1;
-        if (first[b][mid] <= t) l = mid;
-        else h = mid - 1;
-      }
-      write_tile(plan + lo.v[B0 + b] + 2 * t, l, t - first[b][l], kPlanBMs[B0 + b], e_start[l], e_rows[l]);
-    }
-  }
-  __syncthreads();
-}
-
-__device__ __forceinline__ void write_plan(int32_t* __restrict__ plan, const PlanOffs& lo, int e,
-                                           int slots, int off_e, int n_e) {
-  static_assert(kPlanLists == 6, "two groups of three lists");
-  write_plan_group<0>(plan, lo, e, slots, off_e, n_e);
-  write_plan_group<3>(plan, lo, e, slots, off_e, n_e);
-}
-
-// The same for the one-workgroup alignment (P <= kSmallP), where one scan
-// of four values serves the expert offsets and all six lists: the
+// ---------------------------------------------------------------- plan (one workgroup)
+// The tile lists in the one-workgroup alignment (P <= kSmallP), where one
+// scan of four values serves the expert offsets and all six lists: the
 // per-expert tile counts travel two per int (16 bits each: a list holds at
 // most P / 16 + slots <= 1280 tiles, so no half-sum carries into the other
 // half).  plan_counts_small packs the counts; write_plan_small writes the
@@ -260,7 +190,7 @@ __device__ __forceinline__ void write_plan_small(int32_t* __restrict__ plan, con
 }
 
 // Per expert: turn the per-chunk counts into the chunk's first output row
-// (in place), then scan over experts and write offsets and tile lists.
+// (in place), then scan over experts and write the offsets.
 // Up to kScanRegChunks chunks (P <= 65536) every count is loaded at once and
 // the per-expert prefixes stay in registers until the expert offset is
 // known: one memory latency in all.  Beyond that both walks over the chunks
@@ -269,8 +199,7 @@ __device__ __forceinline__ void write_plan_small(int32_t* __restrict__ plan, con
 constexpr int kScanGroup = 16;
 constexpr int kScanRegChunks = 64;
 __device__ __forceinline__ void scan_body(const AlignP& a, int32_t* __restrict__ counts,
-                                          int32_t* __restrict__ offsets, int32_t* __restrict__ plan,
-                                          PlanOffs list_off) {
+                                          int32_t* __restrict__ offsets) {
   const int e = threadIdx.x;
   const bool in_regs = a.nchunks <= kScanRegChunks;
   int n_e = 0;
@@ -317,14 +246,12 @@ __device__ __forceinline__ void scan_body(const AlignP& a, int32_t* __restrict__
     offsets[e] = off_e;
   }
   if (e == 0) offsets[a.slots] = total;
-  write_plan(plan, list_off, e, a.slots, off_e, n_e);
 }
 
+// (the tile lists are written by the scatter launch)
 __global__ __launch_bounds__(1024) void align_scan_kernel(AlignP a, int32_t* __restrict__ counts,
-                                                          int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ plan,
-                                                          PlanOffs list_off) {
-  scan_body(a, counts, offsets, plan, list_off);
+                                                          int32_t* __restrict__ offsets) {
+  scan_body(a, counts, offsets);
 }
 
 // ---------------------------------------------------------------- scatter
@@ -332,11 +259,13 @@ __global__ __launch_bounds__(1024) void align_scan_kernel(AlignP a, int32_t* __r
 // the chunk plus its rank among the chunk's earlier pairs of that expert
 // (wavefront ballots within a round of 256, LDS counts across wavefronts and
 // rounds), so the order is stable and no atomic decides a position.
+// lds: 5 kMaxExperts ints.
+constexpr int kScatterLds = 5 * kMaxExperts;
 __device__ __forceinline__ void scatter_chunk(const AlignP& a, const int32_t* __restrict__ bases,
                                               int32_t* __restrict__ sorted_pair,
-                                              int32_t* __restrict__ inv_pos, int chunk) {
-  __shared__ int running[kMaxExperts];
-  __shared__ int wcnt[4][kMaxExperts];
+                                              int32_t* __restrict__ inv_pos, int chunk, int* lds) {
+  int* const running = lds;
+  int (*const wcnt)[kMaxExperts] = reinterpret_cast<int (*)[kMaxExperts]>(lds + kMaxExperts);
   for (int e = threadIdx.x; e < a.slots; e += 256) {
     running[e] = bases[(int64_t)chunk * a.slots + e];
     wcnt[0][e] = wcnt[1][e] = wcnt[2][e] = wcnt[3][e] = 0;
@@ -383,7 +312,75 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(AlignP a,
                                                             const int32_t* __restrict__ bases,
                                                             int32_t* __restrict__ sorted_pair,
                                                             int32_t* __restrict__ inv_pos) {
-  scatter_chunk(a, bases, sorted_pair, inv_pos, blockIdx.x);
+  __shared__ int lds[kScatterLds];
+  scatter_chunk(a, bases, sorted_pair, inv_pos, blockIdx.x, lds);
+}
+
+// ---------------------------------------------------------------- tile lists
+// List b of the plan from the expert offsets, by one workgroup of 256
+// threads: per-expert tile counts (thread t takes experts [4t, 4t + 4)),
+// their exclusive scan, then tile t to thread t mod 256, which finds its
+// expert by binary search over the experts' first tiles in LDS, so the time
+// does not depend on how the rows are spread over the experts.  Tiles come
+// out expert-major (the order of the oracle's lists).  lds: 3 kMaxExperts ints.
+constexpr int kListEPT = kMaxExperts / 256;
+__device__ __forceinline__ void write_list(int b, const int32_t* __restrict__ offsets, int slots,
+                                           int32_t* __restrict__ plan, int list_off, int* lds) {
+  int* const first = lds;
+  int* const e_start = lds + kMaxExperts;
+  int* const e_rows = lds + 2 * kMaxExperts;
+  __shared__ int wsum[4];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, BM = kPlanBMs[b];
+  int nt[kListEPT], st[kListEPT], nr[kListEPT];
+  int sum = 0;
+#pragma unroll
+  for (int k = 0; k < kListEPT; ++k) {
+    const int e = t * kListEPT + k;
+    st[k] = e < slots ? offsets[e] : 0;
+    nr[k] = e < slots ? offsets[e + 1] - st[k] : 0;
+    nt[k] = (e < slots && plan_list_has(b, nr[k])) ? (nr[k] + BM - 1) / BM : 0;
+    sum += nt[k];
+  }
+  int x = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int run = x - sum, total = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    run += i < w ? wsum[i] : 0;
+    total += wsum[i];
+  }
+#pragma unroll
+  for (int k = 0; k < kListEPT; ++k) {
+    const int e = t * kListEPT + k;
+    if (e < slots) {
+      first[e] = run;
+      e_start[e] = st[k];
+      e_rows[e] = nr[k];
+    }
+    run += nt[k];
+  }
+  if (t == 0) {
+    plan[b] = total;
+    plan[kPlanLists + b] = list_off;
+  }
+  __syncthreads();
+  for (int tt = t; tt < total; tt += 256) {
+    // The last expert whose first tile is <= tt owns tile tt (an expert
+    // with no tile here shares its first index with the next expert).
+    int l = 0, h = slots - 1;
+    while (l < h) {
+      const int mid = (l + h + 1) >> 1;
+      if (first[mid] <= tt) l = mid;
+      else h = mid - 1;
+    }
+    write_tile(plan + list_off + 2 * tt, l, tt - first[l], BM, e_start[l], e_rows[l]);
+  }
 }
 
 // ---------------------------------------------------------------- one workgroup
@@ -587,11 +584,12 @@ __global__ __launch_bounds__(1024) void scale_align_kernel(const uint16_t* __res
 //   1. scale_count_kernel: workgroups [0, nb) each store max |x| over their
 //      share of the tensor in partial[b]; workgroups [nb, nb + nchunks) each
 //      count the experts of one pair chunk.
-//   2. scan_scale_kernel: the one-workgroup scan (chunk bases, offsets, tile
-//      lists), which also takes the maximum of the nb partial maxima and
+//   2. scan_scale_kernel: the one-workgroup scan (chunk bases and expert
+//      offsets), which also takes the maximum of the nb partial maxima and
 //      writes g.
-//   3. scatter_quant_kernel: workgroups [0, nchunks) place the pairs of one
-//      chunk; the others quantise x with g, one lane per 8 elements.
+//   3. scatter_plan_quant_kernel: workgroups [0, nchunks) place the pairs
+//      of one chunk, the next six write one tile list each, the others
+//      quantise x with g, one lane per 8 elements.
 // A maximum is exact in any grouping, so g is bit for bit the one of the
 // single-launch reduction (nvfp4_global_scale).
 constexpr int kScalePartials = 1024;  // most workgroups of the fused global scale
@@ -644,12 +642,11 @@ __global__ __launch_bounds__(kScaleThreads) void scale_count_kernel(const uint16
 
 __global__ __launch_bounds__(1024) void scan_scale_kernel(AlignP a, int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ plan, PlanOffs list_off,
                                                           const float* __restrict__ partial, int nb,
                                                           float* __restrict__ g) {
   // (requested first, so its latency overlaps the scan's own loads)
   float m = (int)threadIdx.x < nb ? partial[threadIdx.x] : 0.0f;
-  scan_body(a, counts, offsets, plan, list_off);
+  scan_body(a, counts, offsets);
   __shared__ float red[16];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -663,25 +660,50 @@ __global__ __launch_bounds__(1024) void scan_scale_kernel(AlignP a, int32_t* __r
   }
 }
 
-__global__ __launch_bounds__(256) void scatter_quant_kernel(AlignP a, const int32_t* __restrict__ bases,
-                                                            int32_t* __restrict__ sorted_pair,
-                                                            int32_t* __restrict__ inv_pos,
-                                                            const uint16_t* __restrict__ x, uint32_t n_hb,
-                                                            uint32_t hb_per_row, int64_t H,
-                                                            const float* __restrict__ g,
-                                                            uint8_t* __restrict__ q, uint8_t* __restrict__ sf,
-                                                            uint16_t* __restrict__ x_deq) {
-  if ((int)blockIdx.x < a.nchunks) {
-    scatter_chunk(a, bases, sorted_pair, inv_pos, blockIdx.x);
+#ifndef NVFP4_QUANT_U
+#define NVFP4_QUANT_U 1
+#endif
+constexpr int kQuantU = NVFP4_QUANT_U;  // half-blocks per lane of the quantisation
+
+// Workgroups [0, nchunks): the pairs of one chunk; the next kPlanLists: one
+// tile list each; the rest (if x): quantisation of x with g, one lane per 8
+// elements (kQuantU half-blocks per lane).  The roles share one LDS area.
+__global__ __launch_bounds__(256) void scatter_plan_quant_kernel(
+    AlignP a, const int32_t* __restrict__ bases, int32_t* __restrict__ sorted_pair,
+    int32_t* __restrict__ inv_pos, const int32_t* __restrict__ offsets, int32_t* __restrict__ plan,
+    PlanOffs list_off, const uint16_t* __restrict__ x, uint32_t n_hb, uint32_t hb_per_row, int64_t H,
+    const float* __restrict__ g, uint8_t* __restrict__ q, uint8_t* __restrict__ sf,
+    uint16_t* __restrict__ x_deq) {
+  __shared__ int lds[kScatterLds];
+  const int blk = (int)blockIdx.x;
+  if (blk < a.nchunks) {
+    scatter_chunk(a, bases, sorted_pair, inv_pos, blk, lds);
     return;
   }
-  // Half-block i (8 elements); both lanes of a block leave together (H is a
-  // multiple of 16).  32-bit indices: n_hb < 2^31 (checked by the launcher).
-  const uint32_t i = ((uint32_t)blockIdx.x - (uint32_t)a.nchunks) * 256u + threadIdx.x;
-  if (i >= n_hb) return;
-  const uint32_t row = i / hb_per_row;
-  quantize_half_block(x, (int64_t)row, (int64_t)(i - row * hb_per_row) << 3, H, H, ld_uniform(g), q, sf,
-                      x_deq);
+  if (blk < a.nchunks + kPlanLists) {
+    const int b = blk - a.nchunks;
+    write_list(b, offsets, a.slots, plan, list_off.v[b], lds);
+    return;
+  }
+  // Half-blocks i0 + 256 u (8 elements each) for u < kQuantU: all loads are
+  // issued before any is used.  Both lanes of a block take the same branches
+  // (256 u is even and so is n_hb).  32-bit indices: n_hb < 2^31 (checked by
+  // the launcher).
+  const uint32_t i0 = ((uint32_t)blk - (uint32_t)(a.nchunks + kPlanLists)) * (256u * kQuantU) + threadIdx.x;
+  float v[kQuantU][8];
+#pragma unroll
+  for (int u = 0; u < kQuantU; ++u) {
+    const uint32_t i = min(i0 + 256u * u, n_hb - 1);
+    load8(x, (int64_t)i * 8, v[u]);
+  }
+  const float gv = ld_uniform(g);
+#pragma unroll
+  for (int u = 0; u < kQuantU; ++u) {
+    const uint32_t i = i0 + 256u * u;
+    if (i >= n_hb) break;
+    const uint32_t row = i / hb_per_row;
+    quantize_half_block_values(v[u], (int64_t)row, (int64_t)(i - row * hb_per_row) << 3, H, gv, q, sf, x_deq);
+  }
 }
 
 // ---------------------------------------------------------------- quantise + align
@@ -982,10 +1004,12 @@ hipError_t launch_align(const AlignShape& a, const int32_t* topk_ids, int32_t* o
     if (e != hipSuccess) return e;
   }
   const PlanOffs lo = plan_offsets(a);
-  align_scan_kernel<<<1, 1024, 0, s>>>(p, counts, offsets, plan, lo);
+  align_scan_kernel<<<1, 1024, 0, s>>>(p, counts, offsets);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.nchunks == 0) return e;
-  align_scatter_kernel<<<a.nchunks, 256, 0, s>>>(p, counts, sorted_pair, inv_pos);
+  if (e != hipSuccess) return e;
+  // the pair scatter beside the six tile lists
+  scatter_plan_quant_kernel<<<a.nchunks + kPlanLists, 256, 0, s>>>(
+      p, counts, sorted_pair, inv_pos, offsets, plan, lo, nullptr, 0u, 1u, 0, nullptr, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -1038,13 +1062,14 @@ hipError_t launch_quantize_and_align(const AlignShape& a, const uint16_t* x, flo
     scale_count_kernel<<<nb + a.nchunks, kScaleThreads, 0, s>>>(x, n, nb, partial, p, counts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    scan_scale_kernel<<<1, 1024, 0, s>>>(p, counts, offsets, plan, plan_offsets(a), partial, nb, g);
+    scan_scale_kernel<<<1, 1024, 0, s>>>(p, counts, offsets, partial, nb, g);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n_hb = n / 8;
-    const int64_t qblocks = (n_hb + 255) / 256;
-    scatter_quant_kernel<<<(unsigned)(a.nchunks + qblocks), 256, 0, s>>>(
-        p, counts, sorted_pair, inv_pos, x, (uint32_t)n_hb, (uint32_t)(a.H >> 3), a.H, g, q, sf, x_deq);
+    const int64_t qblocks = (n_hb + 256 * kQuantU - 1) / (256 * kQuantU);
+    scatter_plan_quant_kernel<<<(unsigned)(a.nchunks + kPlanLists + qblocks), 256, 0, s>>>(
+        p, counts, sorted_pair, inv_pos, offsets, plan, plan_offsets(a), x, (uint32_t)n_hb,
+        (uint32_t)(a.H >> 3), a.H, g, q, sf, x_deq);
     return hipGetLastError();
   }
   if (a.P > (int64_t)kSmallP || n == 0 || n > kFusedQuantMax) {
