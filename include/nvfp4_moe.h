@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_MOE_ABI_VERSION 7
+#define NVFP4_MOE_ABI_VERSION 8
 
 /* Status codes. */
 #define NVFP4_OK 0
@@ -404,6 +404,8 @@ int grouped_gemm2_combine_w4a16(const nvfp4_moe_dims* dims, const uint16_t* a2,
  * stored.  The layer:
  *   mxfp4_quantize(x)                 a1: codes [T][H/2], exponents [T][H/32]
  *   moe_align(dims, topk_ids, ...)    the permutation and tile plan
+ *                                     (both in one call:
+ *                                     moe_mxfp4_quantize_and_align)
  *   grouped_gemm1_swiglu_mxfp4        per row p of expert e (token t):
  *                                     h = silu(c[0:I]) * c[I:2I],
  *                                     c = a1_hat[t] . w13_hat[e]^T (FP32),
@@ -427,6 +429,18 @@ int grouped_gemm2_combine_mxfp4(const nvfp4_moe_dims* dims, const uint8_t* a2_q,
                                 const int32_t* expert_offsets, const int32_t* inv_pos, const int32_t* plan,
                                 const float* topk_w, const uint8_t* w2_prep, void* out, int out_dtype, void* ws,
                                 size_t ws_bytes, void* stream);
+/* The layer's first two steps in one call: the same results, bit for bit,
+ * as mxfp4_quantize(x, NVFP4_BF16, T, H, H, a1_q, a1_e, ...) followed by
+ * moe_align(dims, topk_ids, ...), with those calls' argument contracts (x
+ * bfloat16 [T][H] 16-byte aligned, a1_q [T][H/2] 4-byte aligned, a1_e
+ * [T][H/32]; ws: moe_align_workspace_size(dims) bytes).  MXFP4 has no global
+ * scale, so the two steps are independent: when the pairs fit one workgroup
+ * (P <= 4096) they share one launch; otherwise the quantisation runs beside
+ * the pair scatter, after the count and scan launches.  Errors: as for
+ * those calls, and NVFP4_ESHAPE when T*H >= 2^31. */
+int moe_mxfp4_quantize_and_align(const nvfp4_moe_dims* dims, const uint16_t* x, uint8_t* a1_q, uint8_t* a1_e,
+                                 const int32_t* topk_ids, int32_t* expert_offsets, int32_t* sorted_pair,
+                                 int32_t* inv_pos, int32_t* plan, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* GEMM2 + combine without allocation.                                       */

@@ -13,7 +13,7 @@ from ctypes import c_char_p, c_int, c_int32, c_int64, c_size_t, c_void_p
 # variant with different tile settings); the default is the in-tree build.
 LIB_PATH = os.environ.get("NVFP4_MOE_LIB") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "libnvfp4moe.so")
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 NVFP4_OK = 0
 NVFP4_EINVAL = -1
@@ -87,6 +87,8 @@ SIGNATURES = {
                                            c_void_p, c_void_p, c_void_p]),
     "grouped_gemm2_combine_mxfp4": (c_int, [_P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                             c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
+    "moe_mxfp4_quantize_and_align": (c_int, [_P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                             c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "grouped_gemm2_combine_noalloc_max_bytes": (c_size_t, []),
     "grouped_gemm2_combine_noalloc": (c_int, [_P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,

@@ -666,8 +666,11 @@ __global__ __launch_bounds__(1024) void scan_scale_kernel(AlignP a, int32_t* __r
 constexpr int kQuantU = NVFP4_QUANT_U;  // half-blocks per lane of the quantisation
 
 // Workgroups [0, nchunks): the pairs of one chunk; the next kPlanLists: one
-// tile list each; the rest (if x): quantisation of x with g, one lane per 8
-// elements (kQuantU half-blocks per lane).  The roles share one LDS area.
+// tile list each; the rest (if x): quantisation of x, one lane per 8
+// elements (kQuantU half-blocks per lane) -- NVFP4 with g (q codes, sf E4M3
+// scales, optional x_deq), or (MX) OCP MXFP4 (q codes, sf E8M0 bytes).  The
+// roles share one LDS area.
+template <bool MX>
 __global__ __launch_bounds__(256) void scatter_plan_quant_kernel(
     AlignP a, const int32_t* __restrict__ bases, int32_t* __restrict__ sorted_pair,
     int32_t* __restrict__ inv_pos, const int32_t* __restrict__ offsets, int32_t* __restrict__ plan,
@@ -686,9 +689,9 @@ __global__ __launch_bounds__(256) void scatter_plan_quant_kernel(
     return;
   }
   // Half-blocks i0 + 256 u (8 elements each) for u < kQuantU: all loads are
-  // issued before any is used.  Both lanes of a block take the same branches
-  // (256 u is even and so is n_hb).  32-bit indices: n_hb < 2^31 (checked by
-  // the launcher).
+  // issued before any is used.  The lanes of a block take the same branches
+  // (256 u and n_hb are multiples of 4).  32-bit indices: n_hb < 2^31
+  // (checked by the launcher).
   const uint32_t i0 = ((uint32_t)blk - (uint32_t)(a.nchunks + kPlanLists)) * (256u * kQuantU) + threadIdx.x;
   float v[kQuantU][8];
 #pragma unroll
@@ -696,13 +699,40 @@ __global__ __launch_bounds__(256) void scatter_plan_quant_kernel(
     const uint32_t i = min(i0 + 256u * u, n_hb - 1);
     load8(x, (int64_t)i * 8, v[u]);
   }
-  const float gv = ld_uniform(g);
+  const float gv = MX ? 0.0f : ld_uniform(g);
 #pragma unroll
   for (int u = 0; u < kQuantU; ++u) {
     const uint32_t i = i0 + 256u * u;
     if (i >= n_hb) break;
     const uint32_t row = i / hb_per_row;
-    quantize_half_block_values(v[u], (int64_t)row, (int64_t)(i - row * hb_per_row) << 3, H, gv, q, sf, x_deq);
+    const int64_t c8 = (int64_t)(i - row * hb_per_row) << 3;
+    if constexpr (MX)
+      mx_quantize8_canonical(v[u], (int64_t)row, c8, H, q, sf);
+    else
+      quantize_half_block_values(v[u], (int64_t)row, c8, H, gv, q, sf, x_deq);
+  }
+}
+
+// OCP MXFP4 quantisation and alignment in one launch when the pairs fit one
+// workgroup: workgroups 0 .. nblk-1 quantise (grid-strided; the four lanes
+// of a 32-element block stay together), workgroup nblk runs the
+// one-workgroup alignment.  The two are independent (no global scale).
+__global__ __launch_bounds__(1024) void mx_quant_align_kernel(const uint16_t* __restrict__ x, uint32_t n_hb,
+                                                              uint32_t hb_per_row, int64_t H,
+                                                              uint8_t* __restrict__ q, uint8_t* __restrict__ ex,
+                                                              int nblk, AlignP a, int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ sorted_pair,
+                                                              int32_t* __restrict__ inv_pos,
+                                                              int32_t* __restrict__ plan, PlanOffs list_off) {
+  if ((int)blockIdx.x == nblk) {
+    align_small_body(a, offsets, sorted_pair, inv_pos, plan, list_off);
+    return;
+  }
+  for (uint32_t i = blockIdx.x * 1024u + threadIdx.x; i < n_hb; i += (uint32_t)nblk * 1024u) {
+    float v[8];
+    load8(x, (int64_t)i * 8, v);
+    const uint32_t row = i / hb_per_row;
+    mx_quantize8_canonical(v, (int64_t)row, (int64_t)(i - row * hb_per_row) << 3, H, q, ex);
   }
 }
 
@@ -1008,7 +1038,7 @@ hipError_t launch_align(const AlignShape& a, const int32_t* topk_ids, int32_t* o
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // the pair scatter beside the six tile lists
-  scatter_plan_quant_kernel<<<a.nchunks + kPlanLists, 256, 0, s>>>(
+  scatter_plan_quant_kernel<false><<<a.nchunks + kPlanLists, 256, 0, s>>>(
       p, counts, sorted_pair, inv_pos, offsets, plan, lo, nullptr, 0u, 1u, 0, nullptr, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
@@ -1067,7 +1097,7 @@ hipError_t launch_quantize_and_align(const AlignShape& a, const uint16_t* x, flo
     if (e != hipSuccess) return e;
     const int64_t n_hb = n / 8;
     const int64_t qblocks = (n_hb + 256 * kQuantU - 1) / (256 * kQuantU);
-    scatter_plan_quant_kernel<<<(unsigned)(a.nchunks + kPlanLists + qblocks), 256, 0, s>>>(
+    scatter_plan_quant_kernel<false><<<(unsigned)(a.nchunks + kPlanLists + qblocks), 256, 0, s>>>(
         p, counts, sorted_pair, inv_pos, offsets, plan, plan_offsets(a), x, (uint32_t)n_hb,
         (uint32_t)(a.H >> 3), a.H, g, q, sf, x_deq);
     return hipGetLastError();
@@ -1091,6 +1121,40 @@ hipError_t launch_quantize_and_align(const AlignShape& a, const uint16_t* x, flo
   const PlanOffs lo = plan_offsets(a);
   quant_align_kernel<<<nblk + 1, 1024, 0, s>>>(x, a.T, a.H, g, q, sf, x_deq, nblk, p, offsets, sorted_pair,
                                                inv_pos, plan, lo);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quantize_and_align(const AlignShape& a, const uint16_t* x, uint8_t* q, uint8_t* ex,
+                                       const int32_t* topk_ids, int32_t* offsets, int32_t* sorted_pair,
+                                       int32_t* inv_pos, int32_t* plan, void* ws, hipStream_t s) {
+  AlignP p;
+  p.ids = topk_ids;
+  p.T = a.T;
+  p.topk = a.topk;
+  p.E = a.E;
+  p.shared = a.shared;
+  p.slots = a.slots;
+  p.nchunks = a.nchunks;
+  p.P = a.P;
+  const int64_t n_hb = (int64_t)a.T * a.H / 8;
+  const PlanOffs lo = plan_offsets(a);
+  if (a.P <= (int64_t)kSmallP) {
+    const int nblk = (int)std::min<int64_t>(256, std::max<int64_t>(1, (n_hb + 1023) / 1024));
+    mx_quant_align_kernel<<<nblk + 1, 1024, 0, s>>>(x, (uint32_t)n_hb, (uint32_t)(a.H >> 3), a.H, q, ex, nblk, p,
+                                                     offsets, sorted_pair, inv_pos, plan, lo);
+    return hipGetLastError();
+  }
+  int32_t* counts = static_cast<int32_t*>(ws);
+  align_count_kernel<<<a.nchunks, 256, 0, s>>>(p, counts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  align_scan_kernel<<<1, 1024, 0, s>>>(p, counts, offsets);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t qblocks = (n_hb + 256 * kQuantU - 1) / (256 * kQuantU);
+  scatter_plan_quant_kernel<true><<<(unsigned)(a.nchunks + kPlanLists + qblocks), 256, 0, s>>>(
+      p, counts, sorted_pair, inv_pos, offsets, plan, lo, x, (uint32_t)n_hb, (uint32_t)(a.H >> 3), a.H, nullptr,
+      q, ex, nullptr);
   return hipGetLastError();
 }
 

@@ -235,6 +235,30 @@ int moe_quantize_and_align(const nvfp4_moe_dims* d, const uint16_t* x, float* g1
                   W);
 }
 
+int moe_mxfp4_quantize_and_align(const nvfp4_moe_dims* d, const uint16_t* x, uint8_t* a1_q, uint8_t* a1_e,
+                                 const int32_t* topk_ids, int32_t* expert_offsets, int32_t* sorted_pair,
+                                 int32_t* inv_pos, int32_t* plan, void* ws, size_t ws_bytes, void* stream) {
+  const char* W = "moe_mxfp4_quantize_and_align";
+  if (int r = check_dims(d, W)) return r;
+  if ((int64_t)d->T * d->H >= (int64_t(1) << 31))
+    return fail(NVFP4_ESHAPE, "%s: ESHAPE T=%d H=%d too large", W, d->T, d->H);
+  if (d->T == 0) return ok();
+  nvfp4::AlignShape a = nvfp4::align_shape(d->T, d->topk, d->E, d->shared);
+  a.H = d->H;
+  if (!expert_offsets || !plan || !x || !a1_q || !a1_e) return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
+  if (a.P > 0 && (!sorted_pair || !inv_pos || (d->T * d->topk > 0 && !topk_ids)))
+    return fail(NVFP4_EINVAL, "%s: EINVAL null pointer", W);
+  if (!aligned(x, 16) || !aligned(a1_q, 4))
+    return fail(NVFP4_EINVAL, "%s: EINVAL misaligned x or a1_q", W);
+  const size_t need = nvfp4::align_ws_bytes(a);
+  if (ws_bytes < need || (need && !ws))
+    return fail(NVFP4_EWORKSPACE, "%s: EWORKSPACE num_experts=%d M=%lld workspace_size=%zu needed=%zu",
+                W, d->E, (long long)a.P, ws_bytes, need);
+  return launched(nvfp4::launch_mx_quantize_and_align(a, x, a1_q, a1_e, topk_ids, expert_offsets, sorted_pair,
+                                                      inv_pos, plan, ws, S(stream)),
+                  W);
+}
+
 // ------------------------------------------------------------------ dense linear
 namespace {
 // Workspace of nvfp4_linear*: 256-byte aligned sub-buffers in this order.

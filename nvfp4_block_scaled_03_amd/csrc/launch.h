@@ -56,6 +56,12 @@ hipError_t launch_align(const AlignShape& a, const int32_t* topk_ids, int32_t* o
                         hipStream_t s);
 // Activation global scale (bf16 x [T][H]) and alignment in one launch when
 // the pairs fit one workgroup, else the two launches in sequence.
+// OCP MXFP4 quantisation of bf16 x [T][H] (canonical q, ex) and the
+// alignment: one launch when the pairs fit one workgroup, else the count and
+// scan launches then the scatter beside the quantisation.
+hipError_t launch_mx_quantize_and_align(const AlignShape& a, const uint16_t* x, uint8_t* q, uint8_t* ex,
+                                       const int32_t* topk_ids, int32_t* offsets, int32_t* sorted_pair,
+                                       int32_t* inv_pos, int32_t* plan, void* ws, hipStream_t s);
 hipError_t launch_scale_and_align(const AlignShape& a, const uint16_t* x, float* g, void* gs_ws,
                                   const int32_t* topk_ids, int32_t* offsets, int32_t* sorted_pair,
                                   int32_t* inv_pos, int32_t* plan, void* ws, hipStream_t s);

@@ -62,25 +62,8 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const T* __restrict__ 
   const int64_t c8 = (i - row * hb_per_row) << 3;
   float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (!FRAG || row < rows) load8(x, row * ldx + c8, v);   // (padding rows: zeros)
-  float m = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) m = fmaxf(m, amax_input(v[j]));
-  m = fmaxf(m, dpp_xor1(m));
-  m = fmaxf(m, dpp_xor2(m));
-  // floor(log2 m) = frexp exponent - 1 (m = f * 2^E, f in [0.5, 1)).
-  const int code = m > 0.0f ? min(max(__builtin_amdgcn_frexp_expf(m) - 1 - 2 + 127, 0), 254) : 0;
-  const int sh = 127 - code;   // v / scale = v * 2^sh, exact
-  uint32_t word = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float a = fabsf(__builtin_ldexpf(v[j], sh));
-    // nearest of {0,.5,1,1.5,2,3,4,6}; ties to the even code (up at .75,
-    // 1.75, 3.5; down at .25, 1.25, 2.5, 5); above 6 saturates
-    const uint32_t mag = (uint32_t)(a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
-                         (a >= 3.5f) + (a > 5.0f);
-    const uint32_t sign = ((uint32_t)__float_as_int(v[j]) >> 28) & 8u;
-    word |= (sign | mag) << (4 * j);
-  }
+  int code;
+  const uint32_t word = mx_encode8(v, code);
   if constexpr (FRAG) {
     const int64_t KC = K >> 7, t = row >> 4, kc = c8 >> 7;
     const int64_t lane = ((c8 & 127) >> 5) * 16 + (row & 15);

@@ -104,4 +104,44 @@ __device__ __forceinline__ void quantize_half_block(const T* __restrict__ x, int
   quantize_half_block_values(v, row, c8, K, gv, q, sf, x_deq);
 }
 
+// OCP MXFP4 encoding of 8 consecutive elements of a row by one lane; the
+// four lanes of a 32-element block are a DPP quad (the block maximum is two
+// exchanges), so all four must call this together.  Returns the 8 codes
+// (element j in nibble j) and sets ebyte to the block's E8M0 byte:
+// floor(log2 amax) - 2 + 127 clamped to [0, 254] (0 for an all-zero block);
+// each code is the nearest E2M1 value to v / 2^(ebyte - 127), ties to the
+// even code, above 6 saturating, the sign kept.
+__device__ __forceinline__ uint32_t mx_encode8(const float (&v)[8], int& ebyte) {
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = fmaxf(m, amax_input(v[j]));
+  m = fmaxf(m, dpp_xor1(m));
+  m = fmaxf(m, dpp_xor2(m));
+  // floor(log2 m) = frexp exponent - 1 (m = f * 2^E, f in [0.5, 1)).
+  ebyte = m > 0.0f ? min(max(__builtin_amdgcn_frexp_expf(m) - 1 - 2 + 127, 0), 254) : 0;
+  const int sh = 127 - ebyte;   // v / scale = v * 2^sh, exact
+  uint32_t word = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float a = fabsf(__builtin_ldexpf(v[j], sh));
+    // nearest of {0,.5,1,1.5,2,3,4,6}; ties to the even code (up at .75,
+    // 1.75, 3.5; down at .25, 1.25, 2.5, 5); above 6 saturates
+    const uint32_t mag = (uint32_t)(a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+                         (a >= 3.5f) + (a > 5.0f);
+    const uint32_t sign = ((uint32_t)__float_as_int(v[j]) >> 28) & 8u;
+    word |= (sign | mag) << (4 * j);
+  }
+  return word;
+}
+
+// The same with the canonical stores: q [rows][K/2] gets the 8 codes, ex
+// [rows][K/32] the exponent byte (from the first lane of the block).
+__device__ __forceinline__ void mx_quantize8_canonical(const float (&v)[8], int64_t row, int64_t c8, int64_t K,
+                                                       uint8_t* __restrict__ q, uint8_t* __restrict__ ex) {
+  int ebyte;
+  const uint32_t word = mx_encode8(v, ebyte);
+  *reinterpret_cast<uint32_t*>(q + row * (K >> 1) + (c8 >> 1)) = word;
+  if ((c8 & 31) == 0) ex[row * (K >> 5) + (c8 >> 5)] = (uint8_t)ebyte;
+}
+
 }  // namespace nvfp4

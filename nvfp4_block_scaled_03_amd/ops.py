@@ -148,6 +148,19 @@ def quantize_and_align(d: Dims, x: torch.Tensor, topk_ids: torch.Tensor, al: Opt
     return g, q, sf, al
 
 
+def mx_quantize_and_align(d: Dims, x: torch.Tensor, topk_ids: torch.Tensor, al: Optional[Alignment] = None):
+    """OCP MXFP4 quantisation and moe_align of bf16 ``x`` [T, H] in one call:
+    (codes [T, H/2], E8M0 bytes [T, H/32], Alignment)."""
+    _need_cuda(x, topk_ids)
+    al = al or alloc_alignment(d, x.device)
+    q = torch.empty(max(d.T, 1), d.H // 2, dtype=torch.uint8, device=x.device)
+    ex = torch.empty(max(d.T, 1), d.H // 32, dtype=torch.uint8, device=x.device)
+    call("moe_mxfp4_quantize_and_align", ctypes.byref(d), _p(x.contiguous()), _p(q), _p(ex),
+         _p(topk_ids.contiguous()), _p(al.offsets), _p(al.sorted_pair), _p(al.inv_pos), _p(al.plan),
+         _p(al.workspace), al.workspace.numel(), _stream())
+    return q, ex, al
+
+
 def scale_and_align(d: Dims, x: torch.Tensor, topk_ids: torch.Tensor, al: Optional[Alignment] = None):
     """Activation global scale of bf16 ``x`` [T, H] and moe_align in one call: (g, Alignment)."""
     _need_cuda(x, topk_ids)
@@ -417,9 +430,9 @@ class MxMoELayer:
         d, w, s = self.d, weights or self.w, _stream()
         if out is None:
             out = torch.empty(d.T, d.H, dtype=out_dtype, device=x.device)
-        call("mxfp4_quantize", _p(x), NVFP4_BF16, d.T, d.H, d.H, _p(self.a1_q), _p(self.a1_e), s)
-        call("moe_align", ctypes.byref(d), _p(topk_ids), _p(self.al.offsets), _p(self.al.sorted_pair),
-             _p(self.al.inv_pos), _p(self.al.plan), _p(self.al.workspace), self.al.workspace.numel(), s)
+        call("moe_mxfp4_quantize_and_align", ctypes.byref(d), _p(x), _p(self.a1_q), _p(self.a1_e), _p(topk_ids),
+             _p(self.al.offsets), _p(self.al.sorted_pair), _p(self.al.inv_pos), _p(self.al.plan),
+             _p(self.al.workspace), self.al.workspace.numel(), s)
         if marks:
             marks[0].record()
         call("grouped_gemm1_swiglu_mxfp4", ctypes.byref(d), _p(self.a1_q), _p(self.a1_e),

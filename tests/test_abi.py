@@ -53,6 +53,10 @@ def test_size_queries(lib):
     assert lib.nvfp4_prep_weights_size(ctypes.byref(d), 2) == 128 * 2048 * (384 + 48)
     assert lib.nvfp4_prep_weights_size(ctypes.byref(d), 5) == 0
     assert lib.moe_align_workspace_size(ctypes.byref(d)) == 1 * 128 * 4
+    # past 4096 pairs: per-chunk expert counts, then 1024 partial maxima of
+    # the fused global scale
+    d4k = _d(T=4096)
+    assert lib.moe_align_workspace_size(ctypes.byref(d4k)) == 32 * 128 * 4 + 1024 * 4
     plan = lib.moe_align_plan_size(ctypes.byref(d))
     # six tile lists (heights 16, 32, 64, 128; then 16 and 128 for the experts
     # with at most / more than 32 rows), each with room for one partial tile
@@ -123,6 +127,7 @@ def test_zero_tokens_is_a_noop(lib, shared):
     assert lib.moe_scale_and_align(r, *([None] * 3), 0, *([None] * 6), 0, None) == _lib.NVFP4_OK
     assert lib.moe_route_and_align(r, *([None] * 8), 0, None) == _lib.NVFP4_OK
     assert lib.moe_quantize_and_align(r, None, None, None, 0, *([None] * 9), 0, None) == _lib.NVFP4_OK
+    assert lib.moe_mxfp4_quantize_and_align(r, *([None] * 8), None, 0, None) == _lib.NVFP4_OK
     assert lib.nvfp4_quantize(None, 0, 0, 32, 32, None, 1, None, None, None, None) == _lib.NVFP4_OK
     assert lib.moe_route_topk(None, 0, 8, 2, None, None, None) == _lib.NVFP4_OK
     assert lib.grouped_gemm1_swiglu_mxfp4(r, *([None] * 8), None) == _lib.NVFP4_OK
@@ -165,6 +170,32 @@ def test_quantize_and_align_errors(lib):
     d = _d(H=2000)
     rc = lib.moe_quantize_and_align(ctypes.byref(d), *args)
     assert rc == _lib.NVFP4_ESHAPE and "multiples of 128" in _lib.last_error()
+
+
+def test_mx_quantize_and_align_errors(lib):
+    """Validation before any launch: null operands, misaligned x or codes,
+    a workspace below moe_align_workspace_size, bad dims, T*H >= 2^31."""
+    d = _d()
+    r = ctypes.byref(d)
+    assert lib.moe_mxfp4_quantize_and_align(r, *([None] * 8), None, 0, None) == _lib.NVFP4_EINVAL
+    assert _lib.last_error().startswith("moe_mxfp4_quantize_and_align:")
+    ok = [ctypes.c_void_p(256)] * 8
+    ws = lib.moe_align_workspace_size(r)
+    bad_x = list(ok)
+    bad_x[0] = ctypes.c_void_p(256 + 8)
+    assert lib.moe_mxfp4_quantize_and_align(r, *bad_x, ctypes.c_void_p(256), ws, None) == _lib.NVFP4_EINVAL
+    assert "misaligned" in _lib.last_error()
+    bad_q = list(ok)
+    bad_q[1] = ctypes.c_void_p(256 + 2)
+    assert lib.moe_mxfp4_quantize_and_align(r, *bad_q, ctypes.c_void_p(256), ws, None) == _lib.NVFP4_EINVAL
+    rc = lib.moe_mxfp4_quantize_and_align(r, *ok, ctypes.c_void_p(256), ws - 4, None)
+    assert rc == _lib.NVFP4_EWORKSPACE and "workspace_size" in _lib.last_error()
+    dh = _d(H=2000)
+    rc = lib.moe_mxfp4_quantize_and_align(ctypes.byref(dh), *ok, ctypes.c_void_p(256), ws, None)
+    assert rc == _lib.NVFP4_ESHAPE and "multiples of 128" in _lib.last_error()
+    big = _d(T=1 << 16, H=1 << 15)
+    rc = lib.moe_mxfp4_quantize_and_align(ctypes.byref(big), *ok, ctypes.c_void_p(256), 1 << 30, None)
+    assert rc == _lib.NVFP4_ESHAPE and "too large" in _lib.last_error()
 
 
 def test_mxfp4_sizes_and_errors(lib):

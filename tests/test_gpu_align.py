@@ -8,6 +8,7 @@ import torch
 import moe_inputs
 from nvfp4_block_scaled_03_amd import _lib, ops
 from oracle import moe as omoe
+from oracle import mxfp4 as omx
 from oracle import nvfp4 as onv
 from oracle import routing as oroute
 
@@ -209,6 +210,25 @@ def test_quantize_and_align(dev, name):
         assert np.array_equal(to_np(q), onv.pack_codes(codes))
         assert np.array_equal(to_np(sf), scales)
         assert np.array_equal(to_np(deq).astype(np.float64), onv.dequantize(codes, scales, 1.0))
+        _check_align(dev, ids, w.E, w.shared, al=al)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["decode", "tiny", "limit", "large_e", "prefill", "skew", "big"])
+def test_mx_quantize_and_align(dev, name):
+    """One call = OCP MXFP4 quantisation + alignment, bit-exact against the
+    oracle: one launch up to P = 4096 (decode, tiny, limit, large_e), the
+    quantisation beside the pair scatter and tile lists beyond (prefill,
+    skew, big); twice, so that the second call cannot lean on the first."""
+    w = {"limit": _LIMIT, "big": _BIG}.get(name) or moe_inputs.WORKLOADS[name]
+    x = moe_inputs.activations(w, device=dev)
+    ids, _ = oroute.route_topk(to_np(moe_inputs.router_logits(w, device=dev)), w.topk)
+    d = ops.dims(w.T, w.topk, w.E, w.H, w.I, w.shared)
+    codes, exps = omx.quantize(to_np(x).astype(np.float64))
+    for _ in range(2):
+        q, ex, al = ops.mx_quantize_and_align(d, x, torch.from_numpy(ids).to(dev))
+        assert np.array_equal(onv.unpack_codes(to_np(q)), codes)
+        assert np.array_equal(to_np(ex), exps)
         _check_align(dev, ids, w.E, w.shared, al=al)
 
 
