@@ -509,6 +509,44 @@ __device__ __forceinline__ void mx_epilogue(const MxMoeParams& p, const f32x4 (&
   }
 }
 
+// FP32 row store of the down projection through a wave-private LDS tile
+// (the tall-tile kernel): each 16-row group is turned around in two halves
+// of 8 rows (8 x 68 floats), so that a lane stores 4 consecutive columns
+// and the wavefront writes 256 contiguous bytes per row, instead of the
+// 64-byte row pieces of the accumulator layout.
+template <int MTA>
+__device__ __forceinline__ void mx_epilogue_f32_lds(const MxMoeParams& p, const f32x4 (&acc)[MTA][4], int row0,
+                                                    int nrows, int nt_wave, int lane, float* __restrict__ tile) {
+  constexpr int LD = 68;   // row stride in floats: the two row quads of a write fall in distinct banks
+  const int fr = lane & 15, fg = lane >> 4;
+  const int rr = lane >> 4, c4 = (lane & 15) * 4;
+  const int64_t N = p.N;
+#pragma unroll
+  for (int i = 0; i < MTA; ++i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if ((fg >> 1) == h) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) tile[((fg & 1) * 4 + r) * LD + j * 16 + fr] = acc[i][j][r];
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+      for (int ps = 0; ps < 2; ++ps) {
+        const int rl = ps * 4 + rr;
+        const int row = i * 16 + 8 * h + rl;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(tile + rl * LD + c4);
+        if (row < nrows) *reinterpret_cast<f32x4*>(p.out_f32 + (int64_t)(row0 + row) * N + nt_wave * 16 + c4) = v;
+      }
+      // (the next half rewrites the tile only after every lane has read it)
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+}
+
 // SwiGLU epilogue through a wave-private LDS tile (the tall-tile kernel,
 // whose activation buffers are free once its last chunk is done): h of one
 // 16-row group (16 rows x 32 columns, one MX block per row) is written in the
@@ -850,7 +888,7 @@ __device__ __forceinline__ void mx_tall_body(const MxMoeParams& p, uint8_t (*sa)
     mx_epilogue_swiglu_lds<MTA, MTA>(p, acc, row0, nrows, nt_wave, lane,
                                      reinterpret_cast<float*>(&sa[0][0]) + wv * 16 * 36);
   else
-    mx_epilogue<MTA, MTA, EPI>(p, acc, row0, nrows, nt_wave, lane);
+    mx_epilogue_f32_lds<MTA>(p, acc, row0, nrows, nt_wave, lane, reinterpret_cast<float*>(&sa[0][0]) + wv * 8 * 68);
 }
 
 // The contraction lengths of the expert shapes get straight-line bodies.
