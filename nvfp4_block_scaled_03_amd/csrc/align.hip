@@ -660,17 +660,12 @@ __global__ __launch_bounds__(1024) void scan_scale_kernel(AlignP a, int32_t* __r
   }
 }
 
-#ifndef NVFP4_QUANT_U
-#define NVFP4_QUANT_U 1
-#endif
-constexpr int kQuantU = NVFP4_QUANT_U;  // half-blocks per lane of the quantisation
-
 // Workgroups [0, nchunks): the pairs of one chunk; the next kPlanLists: one
-// tile list each; the rest (if x): quantisation of x, one lane per 8
-// elements (kQuantU half-blocks per lane) -- NVFP4 with g (q codes, sf E4M3
-// scales, optional x_deq), or (MX) OCP MXFP4 (q codes, sf E8M0 bytes).  The
-// roles share one LDS area.
-template <bool MX>
+// tile list each; the rest (if x): quantisation of x -- NVFP4 with g (q
+// codes, sf E4M3 scales, optional x_deq), one lane per 16-element block
+// (BLOCK) or per 8 elements, or (MX) OCP MXFP4, one lane per 8 elements (q
+// codes, sf E8M0 bytes).  The roles share one LDS area.
+template <bool MX, bool BLOCK>
 __global__ __launch_bounds__(256) void scatter_plan_quant_kernel(
     AlignP a, const int32_t* __restrict__ bases, int32_t* __restrict__ sorted_pair,
     int32_t* __restrict__ inv_pos, const int32_t* __restrict__ offsets, int32_t* __restrict__ plan,
@@ -688,28 +683,26 @@ __global__ __launch_bounds__(256) void scatter_plan_quant_kernel(
     write_list(b, offsets, a.slots, plan, list_off.v[b], lds);
     return;
   }
-  // Half-blocks i0 + 256 u (8 elements each) for u < kQuantU: all loads are
-  // issued before any is used.  The lanes of a block take the same branches
-  // (256 u and n_hb are multiples of 4).  32-bit indices: n_hb < 2^31
-  // (checked by the launcher).
-  const uint32_t i0 = ((uint32_t)blk - (uint32_t)(a.nchunks + kPlanLists)) * (256u * kQuantU) + threadIdx.x;
-  float v[kQuantU][8];
-#pragma unroll
-  for (int u = 0; u < kQuantU; ++u) {
-    const uint32_t i = min(i0 + 256u * u, n_hb - 1);
-    load8(x, (int64_t)i * 8, v[u]);
-  }
-  const float gv = MX ? 0.0f : ld_uniform(g);
-#pragma unroll
-  for (int u = 0; u < kQuantU; ++u) {
-    const uint32_t i = i0 + 256u * u;
-    if (i >= n_hb) break;
+  const uint32_t i = ((uint32_t)blk - (uint32_t)(a.nchunks + kPlanLists)) * 256u + threadIdx.x;
+  if constexpr (!MX && BLOCK) {
+    // NVFP4, block i (16 elements) per lane.  32-bit indices: n_hb < 2^31
+    // (checked by the launcher).
+    const uint32_t b_per_row = hb_per_row >> 1;
+    if (i >= (n_hb >> 1)) return;
+    const uint32_t row = i / b_per_row;
+    quantize_block(x, (int64_t)row, (int64_t)(i - row * b_per_row) << 4, H, H, ld_uniform(g), q, sf, x_deq);
+  } else {
+    // Half-block i (8 elements); the lanes of a block (2 for NVFP4, 4 for
+    // MXFP4) take the same branch (n_hb is a multiple of 4).
+    if (i >= n_hb) return;
+    float v[8];
+    load8(x, (int64_t)i * 8, v);
     const uint32_t row = i / hb_per_row;
     const int64_t c8 = (int64_t)(i - row * hb_per_row) << 3;
     if constexpr (MX)
-      mx_quantize8_canonical(v[u], (int64_t)row, c8, H, q, sf);
+      mx_quantize8_canonical(v, (int64_t)row, c8, H, q, sf);
     else
-      quantize_half_block_values(v[u], (int64_t)row, c8, H, gv, q, sf, x_deq);
+      quantize_half_block_values(v, (int64_t)row, c8, H, ld_uniform(g), q, sf, x_deq);
   }
 }
 
@@ -804,7 +797,9 @@ __global__ __launch_bounds__(1024) void quant_align_kernel(const uint16_t* __res
   const uint32_t hb_per_row = (uint32_t)(H >> 3), n_hb = (uint32_t)(n / 8);
   for (uint32_t i = blockIdx.x * 1024u + threadIdx.x; i < n_hb; i += (uint32_t)nblk * 1024u) {
     const uint32_t row = i / hb_per_row;
-    quantize_half_block(x, (int64_t)row, (int64_t)(i - row * hb_per_row) << 3, H, H, gv, q, sf, x_deq);
+    float v[8];
+    load8(x, (int64_t)i * 8, v);
+    quantize_half_block_values(v, (int64_t)row, (int64_t)(i - row * hb_per_row) << 3, H, gv, q, sf, x_deq);
   }
 }
 
@@ -1038,7 +1033,7 @@ hipError_t launch_align(const AlignShape& a, const int32_t* topk_ids, int32_t* o
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // the pair scatter beside the six tile lists
-  scatter_plan_quant_kernel<false><<<a.nchunks + kPlanLists, 256, 0, s>>>(
+  scatter_plan_quant_kernel<false, false><<<a.nchunks + kPlanLists, 256, 0, s>>>(
       p, counts, sorted_pair, inv_pos, offsets, plan, lo, nullptr, 0u, 1u, 0, nullptr, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
@@ -1096,10 +1091,19 @@ hipError_t launch_quantize_and_align(const AlignShape& a, const uint16_t* x, flo
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n_hb = n / 8;
-    const int64_t qblocks = (n_hb + 256 * kQuantU - 1) / (256 * kQuantU);
-    scatter_plan_quant_kernel<false><<<(unsigned)(a.nchunks + kPlanLists + qblocks), 256, 0, s>>>(
-        p, counts, sorted_pair, inv_pos, offsets, plan, plan_offsets(a), x, (uint32_t)n_hb,
-        (uint32_t)(a.H >> 3), a.H, g, q, sf, x_deq);
+    // a lane per 16-element block from 2^18 blocks, else per 8 elements
+    // (as nvfp4_quantize)
+    const bool block = n_hb / 2 >= (int64_t(1) << 18);
+    const int64_t qblocks = ((block ? n_hb / 2 : n_hb) + 255) / 256;
+    const unsigned grid = (unsigned)(a.nchunks + kPlanLists + qblocks);
+    if (block)
+      scatter_plan_quant_kernel<false, true><<<grid, 256, 0, s>>>(p, counts, sorted_pair, inv_pos, offsets, plan,
+                                                                  plan_offsets(a), x, (uint32_t)n_hb,
+                                                                  (uint32_t)(a.H >> 3), a.H, g, q, sf, x_deq);
+    else
+      scatter_plan_quant_kernel<false, false><<<grid, 256, 0, s>>>(p, counts, sorted_pair, inv_pos, offsets, plan,
+                                                                   plan_offsets(a), x, (uint32_t)n_hb,
+                                                                   (uint32_t)(a.H >> 3), a.H, g, q, sf, x_deq);
     return hipGetLastError();
   }
   if (a.P > (int64_t)kSmallP || n == 0 || n > kFusedQuantMax) {
@@ -1151,8 +1155,8 @@ hipError_t launch_mx_quantize_and_align(const AlignShape& a, const uint16_t* x, 
   align_scan_kernel<<<1, 1024, 0, s>>>(p, counts, offsets);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t qblocks = (n_hb + 256 * kQuantU - 1) / (256 * kQuantU);
-  scatter_plan_quant_kernel<true><<<(unsigned)(a.nchunks + kPlanLists + qblocks), 256, 0, s>>>(
+  const int64_t qblocks = (n_hb + 255) / 256;   // one lane per 8 elements
+  scatter_plan_quant_kernel<true, false><<<(unsigned)(a.nchunks + kPlanLists + qblocks), 256, 0, s>>>(
       p, counts, sorted_pair, inv_pos, offsets, plan, lo, x, (uint32_t)n_hb, (uint32_t)(a.H >> 3), a.H, nullptr,
       q, ex, nullptr);
   return hipGetLastError();

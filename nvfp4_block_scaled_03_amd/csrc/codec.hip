@@ -75,13 +75,18 @@ __global__ __launch_bounds__(kScaleThreads) void global_scale_kernel(const T* __
   }
 }
 
-// One thread per 8 elements; the two threads of a 16-element block are
-// adjacent lanes (K % 16 == 0 and the grid starts at an even index), so the
-// block amax is one DPP exchange.  With x_deq, the exact f16 values of the
-// codes (code * block scale, global scale not applied) are written as well:
-// the grouped GEMMs read that copy instead of decoding the codes in every
-// wavefront that uses them.
-template <typename T>
+// One thread per 16-element block (BLOCK) or per 8 elements, the two
+// threads of a block adjacent lanes that share its amax by one DPP exchange
+// (K % 16 == 0 and the grid starts at an even index).  A lane per block takes
+// the scale decision once per block; half a block per lane gives twice the
+// lanes, which pays below about 2^18 blocks (the 512-expert layer's 65536
+// blocks: 1 us faster; prefill's 524288: 2 us slower).  With x_deq, the exact
+// f16 values of the codes (code * block scale, global scale not applied) are
+// written as well: the grouped GEMMs read that copy instead of decoding the
+// codes in every wavefront that uses them.
+constexpr int64_t kBlockLaneMin = int64_t(1) << 18;   // blocks from which a lane takes a whole block
+
+template <typename T, bool BLOCK>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const T* __restrict__ x, int64_t rows,
                                                             int64_t K, int64_t ldx,
                                                             const float* __restrict__ g,
@@ -89,11 +94,18 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const T* __restrict_
                                                             uint8_t* __restrict__ q,
                                                             uint8_t* __restrict__ sf,
                                                             uint16_t* __restrict__ x_deq) {
-  const int64_t hb_per_row = K >> 3;
+  const int64_t per_row = K >> (BLOCK ? 4 : 3);
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= rows * hb_per_row) return;  // whole lane pairs leave together
-  const int64_t row = i / hb_per_row;
-  quantize_half_block(x, row, (i - row * hb_per_row) << 3, K, ldx, g[row / rows_per_g], q, sf, x_deq);
+  if (i >= rows * per_row) return;  // (half blocks: whole lane pairs leave together)
+  const int64_t row = i / per_row;
+  const int64_t c = (i - row * per_row) << (BLOCK ? 4 : 3);
+  if constexpr (BLOCK) {
+    quantize_block(x, row, c, K, ldx, g[row / rows_per_g], q, sf, x_deq);
+  } else {
+    float v[8];
+    load8(x, row * ldx + c, v);
+    quantize_half_block_values(v, row, c, K, g[row / rows_per_g], q, sf, x_deq);
+  }
 }
 
 int64_t amax_blocks(int64_t n) {
@@ -127,15 +139,20 @@ hipError_t launch_global_scale(const void* x, int dtype, int64_t batches, int64_
 hipError_t launch_quantize(const void* x, int dtype, int64_t rows, int64_t K, int64_t ldx,
                            const float* g, int64_t rows_per_g, uint8_t* q, uint8_t* sf,
                            uint16_t* x_deq, hipStream_t s) {
-  const int64_t threads = rows * (K >> 3);
+  const bool block = rows * (K >> 4) >= kBlockLaneMin;
+  const int64_t threads = rows * (K >> (block ? 4 : 3));
   const int64_t blocks = (threads + kThreads - 1) / kThreads;
   if (blocks == 0) return hipSuccess;
-  if (dtype == 0)
-    quantize_kernel<uint16_t><<<(unsigned)blocks, kThreads, 0, s>>>(
-        static_cast<const uint16_t*>(x), rows, K, ldx, g, rows_per_g, q, sf, x_deq);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const float* xf = static_cast<const float*>(x);
+  if (dtype == 0 && block)
+    quantize_kernel<uint16_t, true><<<(unsigned)blocks, kThreads, 0, s>>>(xb, rows, K, ldx, g, rows_per_g, q, sf, x_deq);
+  else if (dtype == 0)
+    quantize_kernel<uint16_t, false><<<(unsigned)blocks, kThreads, 0, s>>>(xb, rows, K, ldx, g, rows_per_g, q, sf, x_deq);
+  else if (block)
+    quantize_kernel<float, true><<<(unsigned)blocks, kThreads, 0, s>>>(xf, rows, K, ldx, g, rows_per_g, q, sf, x_deq);
   else
-    quantize_kernel<float><<<(unsigned)blocks, kThreads, 0, s>>>(
-        static_cast<const float*>(x), rows, K, ldx, g, rows_per_g, q, sf, x_deq);
+    quantize_kernel<float, false><<<(unsigned)blocks, kThreads, 0, s>>>(xf, rows, K, ldx, g, rows_per_g, q, sf, x_deq);
   return hipGetLastError();
 }
 

@@ -99,10 +99,13 @@ def test_align_workloads(dev, name):
 
 # Pair counts across the alignment paths: one workgroup (P <= 4096), chunk
 # scans with the per-expert prefixes in registers (up to 64 chunks of 1024
-# pairs) and chunk scans in groups (65 and 80 chunks).
+# pairs) and chunk scans in groups (65 and 80 chunks); past one workgroup
+# with 1001 and 1024 expert slots (the tile-list writers' four experts per
+# thread, up to the last slot).
 @pytest.mark.parametrize("T,k,E,shared", [(1, 1, 1, 0), (1023, 1, 4, 0), (128, 3, 3, 1),
                                           (1025, 1, 1000, 0), (5000, 3, 17, 1), (7, 2, 1023, 1),
-                                          (8193, 8, 128, 0), (9000, 8, 64, 1)])
+                                          (8193, 8, 128, 0), (9000, 8, 64, 1), (6000, 2, 1000, 1),
+                                          (4500, 1, 1023, 1)])
 def test_align_shapes(dev, T, k, E, shared):
     rng = np.random.default_rng(T + k + E)
     z = rng.standard_normal((T, E)).astype(np.float32)
@@ -185,18 +188,21 @@ _LIMIT = moe_inputs.Workload("limit", 128, 2048, 256, 64, 6, 1, 1.1, 0.02, 0.01,
 # second, partial trip per thread) and past the 64 chunks whose counts the
 # scan keeps in registers.
 _BIG = moe_inputs.Workload("big", 10240, 2048, 256, 128, 8, 0, 0.0, 0.02, 0.01, 43)
+# 1024 tokens: past one workgroup's pairs but below 2^18 blocks, where the
+# fused quantisation takes a lane per 8 elements instead of per block.
+_MID = moe_inputs.Workload("mid", 1024, 2048, 256, 64, 8, 0, 0.0, 0.02, 0.01, 44)
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["decode", "tiny", "limit", "large_e", "prefill", "skew", "big"])
+@pytest.mark.parametrize("name", ["decode", "tiny", "limit", "large_e", "mid", "prefill", "skew", "big"])
 def test_quantize_and_align(dev, name):
     """One call = global scale + quantisation (+ exact f16 copy) + alignment,
     bit-exact against the oracle: one launch up to T*H = 2^18 and P = 4096
     (decode, tiny, limit); the scale+align launch then quantisation beyond
     (large_e); for P > 4096 three launches -- partial maxima beside the
     chunk counts, the scan (which also finishes g), then the scatter beside
-    the quantisation (prefill: 32 chunks of pairs, skew: 64, big: 80)."""
-    w = {"limit": _LIMIT, "big": _BIG}.get(name) or moe_inputs.WORKLOADS[name]
+    the quantisation (mid: 8 chunks of pairs, prefill: 32, skew: 64, big: 80)."""
+    w = {"limit": _LIMIT, "big": _BIG, "mid": _MID}.get(name) or moe_inputs.WORKLOADS[name]
     x = moe_inputs.activations(w, device=dev)
     ids, _ = oroute.route_topk(to_np(moe_inputs.router_logits(w, device=dev)), w.topk)
     d = ops.dims(w.T, w.topk, w.E, w.H, w.I, w.shared)
@@ -214,13 +220,13 @@ def test_quantize_and_align(dev, name):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["decode", "tiny", "limit", "large_e", "prefill", "skew", "big"])
+@pytest.mark.parametrize("name", ["decode", "tiny", "limit", "large_e", "mid", "prefill", "skew", "big"])
 def test_mx_quantize_and_align(dev, name):
     """One call = OCP MXFP4 quantisation + alignment, bit-exact against the
     oracle: one launch up to P = 4096 (decode, tiny, limit, large_e), the
     quantisation beside the pair scatter and tile lists beyond (prefill,
     skew, big); twice, so that the second call cannot lean on the first."""
-    w = {"limit": _LIMIT, "big": _BIG}.get(name) or moe_inputs.WORKLOADS[name]
+    w = {"limit": _LIMIT, "big": _BIG, "mid": _MID}.get(name) or moe_inputs.WORKLOADS[name]
     x = moe_inputs.activations(w, device=dev)
     ids, _ = oroute.route_topk(to_np(moe_inputs.router_logits(w, device=dev)), w.topk)
     d = ops.dims(w.T, w.topk, w.E, w.H, w.I, w.shared)
