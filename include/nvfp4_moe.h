@@ -231,12 +231,13 @@ int moe_scale_and_align(const nvfp4_moe_dims* dims, const uint16_t* x, float* g1
  * vLLM PR #29242 (get_cutlass_moe_mm_data) need no ordering among
  * themselves beyond g1 before the codes; for decode-sized activations
  * (T*H <= 2^18, P <= 4096) they run as one launch in which every quantising
- * workgroup computes the exact amax itself; for P > 4096 as three launches
- * (per-workgroup maxima of |x| beside the expert counts; the scan, which
- * also reduces the maxima to g1; the pair scatter beside the quantisation),
- * which keep their partial maxima in ws and leave gs_ws untouched;
- * otherwise as moe_scale_and_align then nvfp4_quantize.  Errors as for
- * those calls. */
+ * workgroup computes the exact amax itself; beyond that (P > 4096 or
+ * T*H > 2^18) as three launches (per-workgroup maxima of |x| beside the
+ * expert counts; the scan, which also reduces the maxima to g1; the pair
+ * scatter and tile lists beside the quantisation), which keep their partial
+ * maxima in ws and leave gs_ws untouched; dense use (no ids, one expert, P
+ * <= 4096) as moe_scale_and_align then nvfp4_quantize.  Errors as for those
+ * calls. */
 int moe_quantize_and_align(const nvfp4_moe_dims* dims, const uint16_t* x, float* g1, void* gs_ws,
                            size_t gs_ws_bytes, uint8_t* a1_q, uint8_t* a1_sf, uint16_t* a1_deq,
                            const int32_t* topk_ids, int32_t* expert_offsets, int32_t* sorted_pair,

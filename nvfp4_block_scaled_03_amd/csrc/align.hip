@@ -989,10 +989,9 @@ AlignShape align_shape(int T, int topk, int E, int shared) {
 }
 
 size_t align_ws_bytes(const AlignShape& a) {
-  // per-chunk expert counts, then (batches past one workgroup's alignment)
-  // the partial maxima of the fused global scale
-  const size_t part = a.P > (int64_t)kSmallP ? (size_t)kScalePartials * sizeof(float) : 0;
-  return (size_t)a.nchunks * (size_t)a.slots * sizeof(int32_t) + part;
+  // per-chunk expert counts, then the partial maxima of the fused global
+  // scale (moe_quantize_and_align beyond one launch)
+  return (size_t)a.nchunks * (size_t)a.slots * sizeof(int32_t) + (size_t)kScalePartials * sizeof(float);
 }
 
 size_t align_plan_ints(const AlignShape& a) {
@@ -1069,7 +1068,13 @@ hipError_t launch_quantize_and_align(const AlignShape& a, const uint16_t* x, flo
                                     const int32_t* topk_ids, int32_t* offsets, int32_t* sorted_pair,
                                     int32_t* inv_pos, int32_t* plan, void* ws, hipStream_t s) {
   const int64_t n = (int64_t)a.T * a.H;
-  if (a.P > (int64_t)kSmallP && n > 0 && n / 8 < (int64_t(1) << 31)) {
+  // Beyond the single fused launch (P > kSmallP or T*H > kFusedQuantMax):
+  // three launches (at the 512-expert layer's 2816 pairs and 2^20 elements,
+  // 2 us faster than the global scale + one-workgroup alignment launch
+  // followed by the quantisation).  Dense use (no ids, one expert) keeps the
+  // alignment's direct identity plan when it fits one workgroup.
+  const bool dense = topk_ids == nullptr && a.slots == 1;
+  if ((a.P > (int64_t)kSmallP || (n > kFusedQuantMax && !dense)) && n > 0 && n / 8 < (int64_t(1) << 31)) {
     AlignP p;
     p.ids = topk_ids;
     p.T = a.T;

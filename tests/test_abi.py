@@ -52,9 +52,9 @@ def test_size_queries(lib):
     assert lib.nvfp4_prep_weights_size(ctypes.byref(d), 13) == 128 * 1536 * (1024 + 128)
     assert lib.nvfp4_prep_weights_size(ctypes.byref(d), 2) == 128 * 2048 * (384 + 48)
     assert lib.nvfp4_prep_weights_size(ctypes.byref(d), 5) == 0
-    assert lib.moe_align_workspace_size(ctypes.byref(d)) == 1 * 128 * 4
-    # past 4096 pairs: per-chunk expert counts, then 1024 partial maxima of
-    # the fused global scale
+    # per-chunk expert counts, then 1024 partial maxima of the fused global
+    # scale
+    assert lib.moe_align_workspace_size(ctypes.byref(d)) == 1 * 128 * 4 + 1024 * 4
     d4k = _d(T=4096)
     assert lib.moe_align_workspace_size(ctypes.byref(d4k)) == 32 * 128 * 4 + 1024 * 4
     plan = lib.moe_align_plan_size(ctypes.byref(d))

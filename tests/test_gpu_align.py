@@ -198,10 +198,11 @@ _MID = moe_inputs.Workload("mid", 1024, 2048, 256, 64, 8, 0, 0.0, 0.02, 0.01, 44
 def test_quantize_and_align(dev, name):
     """One call = global scale + quantisation (+ exact f16 copy) + alignment,
     bit-exact against the oracle: one launch up to T*H = 2^18 and P = 4096
-    (decode, tiny, limit); the scale+align launch then quantisation beyond
-    (large_e); for P > 4096 three launches -- partial maxima beside the
-    chunk counts, the scan (which also finishes g), then the scatter beside
-    the quantisation (mid: 8 chunks of pairs, prefill: 32, skew: 64, big: 80)."""
+    (decode, tiny, limit); beyond, three launches -- partial maxima beside
+    the chunk counts, the scan (which also finishes g), then the scatter
+    and tile lists beside the quantisation (large_e: 3 chunks of pairs, mid:
+    8, prefill: 32, skew: 64, big: 80).  (Dense use, no ids, takes the
+    scale+align launch then the quantisation: test_gpu_linear.)"""
     w = {"limit": _LIMIT, "big": _BIG, "mid": _MID}.get(name) or moe_inputs.WORKLOADS[name]
     x = moe_inputs.activations(w, device=dev)
     ids, _ = oroute.route_topk(to_np(moe_inputs.router_logits(w, device=dev)), w.topk)

@@ -213,11 +213,12 @@ def test_scale_decisions_at_every_midpoint(dev):
 def test_nan_takes_no_part_in_the_amax(dev, T):
     """A NaN (quiet and signalling bf16 patterns) takes no part in the global
     or the block amax on any dispatch path of the activation step: the
-    fused decode-sized kernel (T = 64), the scale+align launch then the
-    quantisation (T = 4096, P = 4096) and the three-launch form with partial
-    maxima (T = 8192, P > 4096) give g1 = the oracle's scale of x with the
-    NaNs set to 0, the oracle's codes and scales on every block without a
-    NaN, and agree bit for bit with the separate calls on every byte."""
+    fused decode-sized kernel (T = 64) and the three-launch form with
+    partial maxima (T = 4096 with P = 4096; T = 8192, P > 4096, with a lane
+    per 16-element block) give g1 = the oracle's scale of x with the NaNs
+    set to 0, the oracle's codes and scales on every block without a NaN,
+    and agree bit for bit with the separate calls (nvfp4_global_scale, then
+    nvfp4_quantize) on every byte."""
     H = 2048
     gen = torch.Generator(device=dev).manual_seed(T)
     x = torch.randn(T, H, generator=gen, device=dev).to(torch.bfloat16)
