@@ -338,8 +338,10 @@ def measure(w, built, variant, steps, warmup, mode, mx_weights=None):
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name, variant)}
     else:
         ach = g1_flops / (g1_ms * 1e-3) / 1e12
+        # (traffic: the HBM bytes the matrix-bound kernel moved, for the
+        # record; its roofline is the matrix peak)
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": measured_traffic(w.name, variant)}
     roof.update({"kernel": "grouped_gemm1_swiglu" + {"w4a4": "", "w4a16": "_w4a16", "mxfp4": "_mxfp4"}[variant],
                  "kernel_ms": round(g1_ms, 5), "algorithmic_bytes": g1_bytes,
                  "algorithmic_flops": g1_flops})
