@@ -308,14 +308,6 @@ __device__ __forceinline__ void scatter_chunk(const AlignP& a, const int32_t* __
   }
 }
 
-__global__ __launch_bounds__(256) void align_scatter_kernel(AlignP a,
-                                                            const int32_t* __restrict__ bases,
-                                                            int32_t* __restrict__ sorted_pair,
-                                                            int32_t* __restrict__ inv_pos) {
-  __shared__ int lds[kScatterLds];
-  scatter_chunk(a, bases, sorted_pair, inv_pos, blockIdx.x, lds);
-}
-
 // ---------------------------------------------------------------- tile lists
 // List b of the plan from the expert offsets, by one workgroup of 256
 // threads: per-expert tile counts (thread t takes experts [4t, 4t + 4)),
