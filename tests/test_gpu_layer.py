@@ -338,6 +338,29 @@ def test_layer_full_size_hot_and_last_experts(dev, name, variant, decoded):
     _judge_layer(case, dev, variant, decoded, run=run)
 
 
+# The largest batch the tests run through the whole layer: 32768 tokens,
+# 262144 pairs (256 chunks of pairs, past the scan's register path), about
+# 2100 tiles of 128 rows per GEMM, a 2 GiB FP32 workspace (the combine's
+# non-temporal path) and activation offsets up to 2^27.
+_MAX_ROWS = Workload("max_rows", 32768, 2048, 768, 128, 8, 0, 0.0, 0.02, 0.01, 1007)
+
+
+@pytest.mark.timeout(900)
+def test_layer_max_rows_sampled(dev):
+    """The W4A4 layer at 32768 tokens: a1 bit for bit over every token, a2
+    and the output at the first, the last and 10 sampled tokens."""
+    print("max-rows layer", flush=True)
+    _CASE.clear()
+    torch.cuda.empty_cache()
+    w = _MAX_ROWS
+    rng = np.random.default_rng(w.seed)
+    toks = np.unique(np.concatenate([[0, w.T - 1], rng.choice(w.T, 10, replace=False)]))
+    case = Case(w, dev, tokens=toks)
+    _judge_layer(case, dev, "w4a4")
+    del case
+    torch.cuda.empty_cache()
+
+
 def test_layer_is_deterministic(dev):
     case = Case(moe_inputs.WORKLOADS["decode"], dev, tokens=[0])
     _, a, _ = _run_layer(case, dev, "w4a4")
