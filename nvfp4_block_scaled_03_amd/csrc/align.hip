@@ -569,9 +569,9 @@ __global__ __launch_bounds__(1024) void scale_align_kernel(const uint16_t* __res
 }
 
 // ---------------------------------------------------------------- large batches
-// Global scale, quantisation and alignment when the pairs exceed one
-// workgroup's alignment (P > kSmallP): three launches instead of the five
-// of the separate steps (scale, count, scan, scatter, quantise), and no
+// Global scale, quantisation and alignment beyond the single fused launch
+// (P > kSmallP, or T*H > kFusedQuantMax): three launches instead of the
+// five of the separate steps (scale, count, scan, scatter, quantise), and no
 // cross-workgroup atomics.
 //   1. scale_count_kernel: workgroups [0, nb) each store max |x| over their
 //      share of the tensor in partial[b]; workgroups [nb, nb + nchunks) each
@@ -581,7 +581,7 @@ __global__ __launch_bounds__(1024) void scale_align_kernel(const uint16_t* __res
 //      writes g.
 //   3. scatter_plan_quant_kernel: workgroups [0, nchunks) place the pairs
 //      of one chunk, the next six write one tile list each, the others
-//      quantise x with g, one lane per 8 elements.
+//      quantise x with g.
 // A maximum is exact in any grouping, so g is bit for bit the one of the
 // single-launch reduction (nvfp4_global_scale).
 constexpr int kScalePartials = 1024;  // most workgroups of the fused global scale
