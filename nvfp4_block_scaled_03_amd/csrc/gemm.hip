@@ -620,6 +620,10 @@ __global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
 #ifndef NVFP4_TALL_WN
 #define NVFP4_TALL_WN 64       // columns per wavefront of the wide kernel for the tall experts of a split layer
 #endif
+#ifndef NVFP4_TALL_WN_UP
+#define NVFP4_TALL_WN_UP 32    // the same for the gate/up projection (twice the workgroups: its column
+                               // blocks alone do not fill the device)
+#endif
 constexpr int kWideBM = 128, kWideWN = NVFP4_WIDE_WN, kWideNW = NVFP4_WIDE_NW;
 
 template <int AK, int EPI, int WN>
@@ -1432,7 +1436,7 @@ hipError_t launch_gemm(KParams kp, const AlignShape& al, hipStream_t s) {
       hipError_t e = launch_stream_pf<AK, EPI, 1, kStreamNTW>(kp, (int)al.list_len[4], s);
       if (e != hipSuccess) return e;
       kp.list_idx = 5;
-      return launch_wide<AK, EPI, NVFP4_TALL_WN>(kp, (int)al.list_len[5], s);
+      return launch_wide<AK, EPI, swiglu_epi(EPI) ? NVFP4_TALL_WN_UP : NVFP4_TALL_WN>(kp, (int)al.list_len[5], s);
     }
   }
   kp.list_idx = li;
