@@ -620,9 +620,13 @@ __global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
 #ifndef NVFP4_TALL_WN
 #define NVFP4_TALL_WN 64       // columns per wavefront of the wide kernel for the tall experts of a split layer
 #endif
-#ifndef NVFP4_TALL_WN_UP
-#define NVFP4_TALL_WN_UP 32    // the same for the gate/up projection (twice the workgroups: its column
-                               // blocks alone do not fill the device)
+// The gate/up projection with f16 activations takes 32 columns per wavefront
+// (twice the workgroups) where 64 would leave CU slots empty: on the tall
+// experts of a split layer, and on 128-row tiles when the launch's bound on
+// workgroups at 64 columns is at most NVFP4_SMALL_WIDE_GRID (the device
+// holds 512 of them, two per CU).
+#ifndef NVFP4_SMALL_WIDE_GRID
+#define NVFP4_SMALL_WIDE_GRID 400
 #endif
 constexpr int kWideBM = 128, kWideWN = NVFP4_WIDE_WN, kWideNW = NVFP4_WIDE_NW;
 
@@ -1423,8 +1427,13 @@ hipError_t launch_gemm(KParams kp, const AlignShape& al, hipStream_t s) {
   if (li <= 1 && !offsets_fit) li = 2;
   if constexpr (AK != kActCodes) {
     // 16-bit activations on tall tiles: the wide kernel (128-row tiles).
+    constexpr bool kUp32 = swiglu_epi(EPI) && AK == kActF16;
     if (li >= NVFP4_WIDE_MIN_LIST && offsets_fit) {
       kp.list_idx = 3;
+      if constexpr (kUp32) {
+        if (al.list_len[3] * ((kp.N + 255) / 256) <= NVFP4_SMALL_WIDE_GRID)
+          return launch_wide<AK, EPI, 32>(kp, (int)al.list_len[3], s);
+      }
       return launch_wide<AK, EPI>(kp, (int)al.list_len[3], s);
     }
     // Short tiles on average, but some experts may hold many rows: the
@@ -1436,7 +1445,7 @@ hipError_t launch_gemm(KParams kp, const AlignShape& al, hipStream_t s) {
       hipError_t e = launch_stream_pf<AK, EPI, 1, kStreamNTW>(kp, (int)al.list_len[4], s);
       if (e != hipSuccess) return e;
       kp.list_idx = 5;
-      return launch_wide<AK, EPI, swiglu_epi(EPI) ? NVFP4_TALL_WN_UP : NVFP4_TALL_WN>(kp, (int)al.list_len[5], s);
+      return launch_wide<AK, EPI, kUp32 ? 32 : NVFP4_TALL_WN>(kp, (int)al.list_len[5], s);
     }
   }
   kp.list_idx = li;
