@@ -620,11 +620,11 @@ __global__ __launch_bounds__(NW * kWave) void grouped_gemm_kernel(KParams p) {
 #ifndef NVFP4_TALL_WN
 #define NVFP4_TALL_WN 64       // columns per wavefront of the wide kernel for the tall experts of a split layer
 #endif
-// The gate/up projection with f16 activations takes 32 columns per wavefront
-// (twice the workgroups) where 64 would leave CU slots empty: on the tall
-// experts of a split layer, and on 128-row tiles when the launch's bound on
-// workgroups at 64 columns is at most NVFP4_SMALL_WIDE_GRID (the device
-// holds 512 of them, two per CU).
+// With f16 activations the wide kernel takes 32 columns per wavefront (twice
+// the workgroups) where 64 would leave CU slots empty: both projections on
+// 128-row tiles when the launch's bound on workgroups at 64 columns is at
+// most NVFP4_SMALL_WIDE_GRID (the device holds 512 of them, two per CU), and
+// the gate/up projection on the tall experts of a split layer.
 #ifndef NVFP4_SMALL_WIDE_GRID
 #define NVFP4_SMALL_WIDE_GRID 400
 #endif
@@ -1430,7 +1430,7 @@ hipError_t launch_gemm(KParams kp, const AlignShape& al, hipStream_t s) {
     constexpr bool kUp32 = swiglu_epi(EPI) && AK == kActF16;
     if (li >= NVFP4_WIDE_MIN_LIST && offsets_fit) {
       kp.list_idx = 3;
-      if constexpr (kUp32) {
+      if constexpr (AK == kActF16) {
         if (al.list_len[3] * ((kp.N + 255) / 256) <= NVFP4_SMALL_WIDE_GRID)
           return launch_wide<AK, EPI, 32>(kp, (int)al.list_len[3], s);
       }
