@@ -411,3 +411,27 @@ def test_layer_split_short_and_tall_experts(dev, variant):
     case = RoutedCase(SPLIT_COUNTS, dev, seed=72)
     assert case.w.pairs / case.w.E <= 16 and case.w.T > 64
     _judge_layer(case, dev, variant, decoded_copies=True if variant == "w4a4" else None)
+
+
+# The largest expert count the boundary takes: 1023 routed experts and a
+# shared one (1024 slots).  Short experts on average and the shared expert
+# tall, so plan entries and prepared weights of nearly every slot are in
+# play, the split launches run (W4A4 with f16 copies, W4A16), or the 16-row
+# streaming kernel takes every tile (W4A4 from the codes), and the combine
+# adds the shared row of every token.
+MAX_EXPERTS = Workload("max_experts", 300, 128, 128, 1023, 4, 1, 0.0, 0.02, 0.01, 1011)
+
+
+@pytest.fixture(scope="module")
+def max_experts_case(dev):
+    return Case(MAX_EXPERTS, dev)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("variant,decoded", [("w4a4", True), ("w4a4", False), ("w4a16", None)],
+                         ids=["w4a4-f16-copies", "w4a4-codes", "w4a16"])
+def test_layer_max_experts(dev, max_experts_case, variant, decoded):
+    case = max_experts_case
+    assert case.w.E + case.w.shared == 1024
+    _judge_layer(case, dev, variant, decoded_copies=decoded)
+

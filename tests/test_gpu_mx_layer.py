@@ -160,3 +160,13 @@ def test_mx_layer_split_short_and_tall_experts(dev):
     case = _routed(SPLIT_COUNTS, "mx_split", 82, dev)
     assert case.w.pairs / case.w.E <= 16 and case.w.T > 64
     _judge(case, dev)
+
+
+@pytest.mark.timeout(600)
+def test_mx_layer_max_experts(dev):
+    """1023 routed experts and a shared one (1024 slots, the boundary's
+    limit): short experts on the 16-row kernel, the shared expert on the
+    tall-tile kernel, every token's shared row in the combine."""
+    w = Workload("mx_max_experts", 300, 128, 128, 1023, 4, 1, 0.0, 0.02, 0.01, 1012)
+    _judge(MxCase(w, dev), dev)
+
