@@ -435,3 +435,17 @@ def test_layer_max_experts(dev, max_experts_case, variant, decoded):
     assert case.w.E + case.w.shared == 1024
     _judge_layer(case, dev, variant, decoded_copies=decoded)
 
+
+# Batch-one decode and a three-token batch: every tile holds a single row,
+# the front end runs one quantising workgroup, the combine one or three
+# tokens.
+FEW_TOKENS = [Workload("one_token", 1, 256, 128, 128, 8, 0, 0.0, 0.02, 0.01, 1021),
+              Workload("three_tokens", 3, 256, 128, 64, 6, 1, 0.0, 0.02, 0.01, 1022)]
+
+
+@pytest.mark.parametrize("variant,decoded", [("w4a4", True), ("w4a4", False), ("w4a16", None)],
+                         ids=["w4a4-f16-copies", "w4a4-codes", "w4a16"])
+@pytest.mark.parametrize("w", FEW_TOKENS, ids=lambda w: w.name)
+def test_layer_few_tokens(dev, w, variant, decoded):
+    _judge_layer(Case(w, dev), dev, variant, decoded_copies=decoded)
+

@@ -170,3 +170,9 @@ def test_mx_layer_max_experts(dev):
     w = Workload("mx_max_experts", 300, 128, 128, 1023, 4, 1, 0.0, 0.02, 0.01, 1012)
     _judge(MxCase(w, dev), dev)
 
+
+@pytest.mark.parametrize("T,E,k,shared", [(1, 128, 8, 0), (3, 64, 6, 1)], ids=["one_token", "three_tokens"])
+def test_mx_layer_few_tokens(dev, T, E, k, shared):
+    """Batch-one decode and a three-token batch (single-row tiles)."""
+    _judge(MxCase(Workload(f"mx_{T}_tokens", T, 256, 128, E, k, shared, 0.0, 0.02, 0.01, 1030 + T), dev), dev)
+
