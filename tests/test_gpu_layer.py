@@ -449,3 +449,28 @@ FEW_TOKENS = [Workload("one_token", 1, 256, 128, 128, 8, 0, 0.0, 0.02, 0.01, 102
 def test_layer_few_tokens(dev, w, variant, decoded):
     _judge_layer(Case(w, dev), dev, variant, decoded_copies=decoded)
 
+
+@pytest.mark.parametrize("variant,decoded", [("w4a4", True), ("w4a4", False), ("w4a16", None)],
+                         ids=["w4a4-f16-copies", "w4a4-codes", "w4a16"])
+@pytest.mark.parametrize("T", [40, 1100], ids=["one_launch_front", "three_launch_front"])
+def test_layer_zero_activations(dev, T, variant, decoded):
+    """All-zero activations (the oracle's result is pinned to exact zeros on
+    the CPU): g1 = 0, zero codes, scales and f16 copy, and an exactly zero
+    output.  1100 tokens x 256 take the three-launch front end."""
+    w = Workload("zeros", T, 256, 128, 16, 2, 1, 0.0, 0.02, 0.01, 1041)
+    d = ops.dims(w.T, w.topk, w.E, w.H, w.I, w.shared)
+    wq = ops.quantize_expert_weights(d, moe_inputs.expert_weights(w, 13, device=dev),
+                                     moe_inputs.expert_weights(w, 2, device=dev), keep_canonical=False)
+    ids, tw = oroute.route_topk(to_np(moe_inputs.router_logits(w, device=dev)), w.topk)
+    layer = ops.MoELayer(d, wq, torch.tensor([0.003], device=dev), device=dev, decoded_copies=decoded)
+    x0 = torch.zeros(w.T, w.H, dtype=torch.bfloat16, device=dev)
+    out = layer.forward(x0, torch.from_numpy(ids).to(dev), torch.from_numpy(tw).to(dev), variant,
+                        out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert not out.any(), "nonzero output for zero activations"
+    if variant == "w4a4":
+        assert float(layer.g1.item()) == 0.0
+        assert not layer.a1_q.any() and not layer.a1_sf.any()
+        if layer.a1_deq is not None:
+            assert not layer.a1_deq.any()
+

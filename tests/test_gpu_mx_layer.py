@@ -176,3 +176,23 @@ def test_mx_layer_few_tokens(dev, T, E, k, shared):
     """Batch-one decode and a three-token batch (single-row tiles)."""
     _judge(MxCase(Workload(f"mx_{T}_tokens", T, 256, 128, E, k, shared, 0.0, 0.02, 0.01, 1030 + T), dev), dev)
 
+
+@pytest.mark.parametrize("T", [40, 1100], ids=["one_launch_front", "three_launch_front"])
+def test_mx_layer_zero_activations(dev, T):
+    """All-zero activations: codes and exponent bytes as the oracle encodes
+    a zero tensor, and an exactly zero output."""
+    w = Workload("mx_zeros", T, 256, 128, 16, 2, 1, 0.0, 0.02, 0.01, 1042)
+    d = ops.dims(w.T, w.topk, w.E, w.H, w.I, w.shared)
+    wq = ops.quantize_mx_expert_weights(d, moe_inputs.expert_weights(w, 13, device=dev),
+                                        moe_inputs.expert_weights(w, 2, device=dev))
+    ids, tw = oroute.route_topk(to_np(moe_inputs.router_logits(w, device=dev)), w.topk)
+    layer = ops.MxMoELayer(d, wq, device=dev)
+    x0 = torch.zeros(w.T, w.H, dtype=torch.bfloat16, device=dev)
+    out = layer.forward(x0, torch.from_numpy(ids).to(dev), torch.from_numpy(tw).to(dev),
+                        out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert not out.any(), "nonzero output for zero activations"
+    codes, exps = omx.quantize(np.zeros((w.T, w.H)))
+    assert np.array_equal(onv.unpack_codes(to_np(layer.a1_q)), codes)
+    assert np.array_equal(to_np(layer.a1_e), exps)
+

@@ -331,3 +331,20 @@ def test_layer_calibrate_inline_matches_two_pass():
         assert np.array_equal(a.out, b.out) and np.array_equal(a.a2_codes, b.a2_codes)
         # g2 is the global scale of h itself
         assert b.g2 == nvfp4.global_scale(b.h)
+
+
+@pytest.mark.parametrize("variant", ["w4a4", "w4a16"])
+def test_zero_activations_give_zero(variant):
+    """All-zero activations: g1 = 0, every code and block scale 0, and (as
+    SwiGLU(0) = 0) a zero intermediate and a zero output, whatever g2."""
+    w = moe_inputs.Workload("zeros", 12, 128, 64, 6, 2, 1, 0.0, 0.02, 0.01, 45)
+    x = np.zeros((w.T, w.H))
+    ids, tw = routing.route_topk(moe_inputs.router_logits(w).numpy(), 2)
+    ew = moe.ExpertWeights.from_arrays(moe_inputs.expert_weights(w, 13).numpy(),
+                                       moe_inputs.expert_weights(w, 2).numpy())
+    res = moe.layer(x, ids, tw, ew, w.E, w.I, variant=variant, g2=np.float32(0.003), shared=1)
+    if variant == "w4a4":
+        assert nvfp4.global_scale(x) == 0.0
+        assert not res.a1_codes.any() and not res.a1_scales.any()
+    assert not np.asarray(res.out).any()
+
