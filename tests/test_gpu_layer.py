@@ -474,3 +474,42 @@ def test_layer_zero_activations(dev, T, variant, decoded):
         if layer.a1_deq is not None:
             assert not layer.a1_deq.any()
 
+
+def _drop_ids(ids, E, frac, seed):
+    """Replace a fraction of the expert ids by ones outside [0, E) (-1, E
+    itself, which is the shared slot's index, and E + 100): such pairs are
+    dropped, as an expert-parallel share drops the experts it does not own."""
+    rng = np.random.default_rng(seed)
+    bad = rng.choice(np.array([-1, E, E + 100], dtype=np.int32), ids.shape)
+    return np.where(rng.random(ids.shape) < frac, bad, ids).astype(np.int32)
+
+
+class DroppedCase(Case):
+    def __init__(self, w: Workload, dev, frac, seed):
+        self.w = w
+        self.d = ops.dims(w.T, w.topk, w.E, w.H, w.I, w.shared)
+        self.x = moe_inputs.activations(w, device=dev)
+        ids, tw = oroute.route_topk(to_np(moe_inputs.router_logits(w, device=dev)), w.topk)
+        self._setup(w, dev, _drop_ids(ids, w.E, frac, seed), tw, None)
+
+
+DROPPED = [Workload("dropped_decode", 64, 256, 128, 32, 4, 1, 0.0, 0.02, 0.01, 1051),
+           Workload("dropped_big", 1100, 256, 128, 16, 2, 0, 0.0, 0.02, 0.01, 1052)]
+
+
+@pytest.mark.parametrize("variant,decoded", [("w4a4", True), ("w4a4", False), ("w4a16", None)],
+                         ids=["w4a4-f16-copies", "w4a4-codes", "w4a16"])
+@pytest.mark.parametrize("w", DROPPED, ids=lambda w: w.name)
+def test_layer_dropped_pairs(dev, w, variant, decoded):
+    """Half of the routed pairs carry ids outside [0, E): they get no row,
+    their inverse position is -1, and the combine leaves them out (a token
+    may keep only its shared row, or nothing)."""
+    case = DroppedCase(w, dev, 0.5, w.seed)
+    al = ops.moe_align(case.d, case.ids)
+    off, sp, inv = omoe.align(case.ids_np, w.E, w.shared)
+    assert off[-1] < w.pairs
+    assert np.array_equal(to_np(al.offsets), off)
+    assert np.array_equal(to_np(al.sorted_pair)[:off[-1]], sp)
+    assert np.array_equal(to_np(al.inv_pos), inv)
+    _judge_layer(case, dev, variant, decoded_copies=decoded)
+

@@ -196,3 +196,15 @@ def test_mx_layer_zero_activations(dev, T):
     assert np.array_equal(onv.unpack_codes(to_np(layer.a1_q)), codes)
     assert np.array_equal(to_np(layer.a1_e), exps)
 
+
+@pytest.mark.parametrize("T,E,k,shared", [(64, 32, 4, 1), (1100, 16, 2, 0)], ids=["decode_like", "three_launch_front"])
+def test_mx_layer_dropped_pairs(dev, T, E, k, shared):
+    """Half of the routed pairs carry ids outside [0, E) (-1, E, E + 100):
+    dropped, as an expert-parallel share drops the experts it does not own."""
+    w = Workload(f"mx_dropped_{T}", T, 256, 128, E, k, shared, 0.0, 0.02, 0.01, 1060 + T)
+    ids, tw = oroute.route_topk(to_np(moe_inputs.router_logits(w, device=dev)), w.topk)
+    rng = np.random.default_rng(w.seed)
+    bad = rng.choice(np.array([-1, E, E + 100], dtype=np.int32), ids.shape)
+    ids = np.where(rng.random(ids.shape) < 0.5, bad, ids).astype(np.int32)
+    _judge(MxCase(w, dev, routing=(ids, tw)), dev)
+
