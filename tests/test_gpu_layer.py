@@ -513,3 +513,26 @@ def test_layer_dropped_pairs(dev, w, variant, decoded):
     assert np.array_equal(to_np(al.inv_pos), inv)
     _judge_layer(case, dev, variant, decoded_copies=decoded)
 
+
+# 262144 pairs with I = 4096: the down projection's 16-bit activation rows
+# span 2^31 bytes, past the 32-bit buffer offsets of the streaming and wide
+# kernels, so it runs on the LDS-staged kernel with 64-bit addressing (f16
+# copy or bf16), while the 4-bit codes still fit.
+_WIDE_OFFSETS = Workload("wide_offsets", 32768, 128, 4096, 8, 8, 0, 0.0, 0.02, 0.01, 1071)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("variant,decoded", [("w4a4", True), ("w4a4", False), ("w4a16", None)],
+                         ids=["w4a4-f16-copies", "w4a4-codes", "w4a16"])
+def test_layer_wide_offsets_sampled(dev, variant, decoded):
+    w = _WIDE_OFFSETS
+    assert w.pairs * w.I * 2 >= 2 ** 31
+    _CASE.clear()
+    torch.cuda.empty_cache()
+    rng = np.random.default_rng(w.seed)
+    toks = np.unique(np.concatenate([[0, w.T - 1], rng.choice(w.T, 10, replace=False)]))
+    case = Case(w, dev, tokens=toks)
+    _judge_layer(case, dev, variant, decoded_copies=decoded)
+    del case
+    torch.cuda.empty_cache()
+
