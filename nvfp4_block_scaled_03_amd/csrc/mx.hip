@@ -736,6 +736,7 @@ __global__ __launch_bounds__(256) void grouped_mx_kernel(MxMoeParams p) {
 // The main loop is instantiated for 8, 4, 2 and 1 active 16-row groups: a
 // ragged last tile stages and multiplies only the groups that hold rows.
 constexpr int kMxTallRing = 3;   // weight chunks in registers
+constexpr int kMxTallBufs = 4;   // activation chunk buffers in LDS
 
 // KCT > 0: the chunk loop fully unrolled for K = 128 KCT (straight-line code,
 // so the compiler's waits are exact; in a loop its analysis merges the
@@ -785,6 +786,55 @@ __device__ __forceinline__ void mx_tall_body(const MxMoeParams& p, uint8_t (*sa)
   uint32_t rbs[RB];
   u32x4 ra[AW];
   uint32_t rae;
+  // Whole-cache-line gathers (straight-line bodies): two chunks per load, lane
+  // l taking row (l >> 3) + 8 h of its tile, bytes [16 (l & 3), +16) of chunk
+  // kc0 + ((l >> 2) & 1), i.e. 128 contiguous bytes per row.
+  constexpr bool PAIR = KCT > 0;
+  const int half = (lane >> 2) & 1;
+  uint32_t vrow[AW][2];
+#pragma unroll
+  for (int u = 0; u < AW; ++u) {
+    const int i = MTA >= 4 ? wv + 4 * u : min(wv, MTA - 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int r = row0 + min(16 * i + (lane >> 3) + 8 * h, nrows - 1);
+      if (p.sorted_pair) r = pair_token(p.sorted_pair[r], p.T, p.topk);
+      vrow[u][h] = (uint32_t)r * (uint32_t)(K / 2) + (uint32_t)(16 * (lane & 3));
+    }
+  }
+  u32x4 rp[AW][2];
+  auto load_pair = [&](int kc0) __attribute__((always_inline)) {
+    if (!a_on) return;
+    const int c = min(kc0 + half, KC - 1);
+#pragma unroll
+    for (int u = 0; u < AW; ++u)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) rp[u][h] = *reinterpret_cast<const u32x4*>(p.a_q + (vrow[u][h] + (uint32_t)c * 64u));
+  };
+  auto store_pair = [&](int kc0) __attribute__((always_inline)) {
+    if (!a_on) return;
+    uint8_t* const base = half ? sa[(kc0 + 1) % kMxTallBufs] : sa[kc0 % kMxTallBufs];
+#pragma unroll
+    for (int u = 0; u < AW; ++u) {
+      const int i = MTA >= 4 ? wv + 4 * u : wv;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // fragment slot of (row, g) in a chunk of parity q: 16 g + (row ^ (2 g + q)),
+        // so that the 8 lanes of one row piece land in distinct banks
+        const int g4 = lane & 3, row = (lane >> 3) + 8 * h;
+        *reinterpret_cast<u32x4*>(base + i * 1024 + (16 * g4 + (row ^ (2 * g4 + half))) * 16) = rp[u][h];
+      }
+    }
+  };
+  auto load_e = [&](int kc) __attribute__((always_inline)) {
+    if (!a_on) return;
+    kc = min(kc, KC - 1);
+    rae = *reinterpret_cast<const uint32_t*>(p.a_e + (vae + (uint32_t)kc * 4u));
+  };
+  auto store_e = [&](int buf) __attribute__((always_inline)) {
+    if (!a_on) return;
+    se[buf][m * 8 + ie] = rae;
+  };
   // Loads past the last chunk repeat it (unconditional, so every wait is
   // the same in every iteration).
   auto load_b = [&](int kc, u32x4 (&b)[NTW], uint32_t& bs) __attribute__((always_inline)) {
@@ -817,7 +867,9 @@ __device__ __forceinline__ void mx_tall_body(const MxMoeParams& p, uint8_t (*sa)
   for (int i = 0; i < MTA; ++i)
 #pragma unroll
     for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int buf, const u32x4 (&b)[NTW], uint32_t bsw) __attribute__((always_inline)) {
+  auto compute = [&](int buf, const u32x4 (&b)[NTW], uint32_t bsw, int par) __attribute__((always_inline)) {
+    // this lane's fragment slot (the pair gathers store swizzled by chunk parity)
+    const int slot = PAIR ? 16 * g + (m ^ (2 * g + par)) : lane;
     // exponent bytes of row m for tiles 0..7, byte g of word i
     const u32x4 ew0 = *reinterpret_cast<const u32x4*>(&se[buf][m * 8]);
     u32x4 ew1 = ew0;
@@ -825,11 +877,11 @@ __device__ __forceinline__ void mx_tall_body(const MxMoeParams& p, uint8_t (*sa)
     // One fragment read ahead of the matrix instructions that use it (the
     // scheduler is fenced so that it does not hoist all MTA reads and their
     // registers to the top).
-    u32x4 an = *reinterpret_cast<const u32x4*>(sa[buf] + lane * 16);
+    u32x4 an = *reinterpret_cast<const u32x4*>(sa[buf] + slot * 16);
 #pragma unroll
     for (int i = 0; i < MTA; ++i) {
       const u32x4 a = an;
-      if (i + 1 < MTA) an = *reinterpret_cast<const u32x4*>(sa[buf] + (i + 1) * 1024 + lane * 16);
+      if (i + 1 < MTA) an = *reinterpret_cast<const u32x4*>(sa[buf] + (i + 1) * 1024 + slot * 16);
       const uint32_t aw = i < 4 ? ew0[i & 3] : ew1[i & 3];
       const int as = (int)((aw >> (8 * g)) & 0xFFu);
       const v8i av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
@@ -845,9 +897,17 @@ __device__ __forceinline__ void mx_tall_body(const MxMoeParams& p, uint8_t (*sa)
 
   // Prologue: activations of chunk 0 into buffer 0, chunk 1 into the
   // registers, weights of chunks 0..RB-1.
-  load_a(0, ra, rae);
-  store_a(0, ra, rae);
-  load_a(1, ra, rae);
+  if constexpr (PAIR) {
+    load_pair(0);
+    store_pair(0);
+    load_e(0);
+    store_e(0);
+    load_e(1);
+  } else {
+    load_a(0, ra, rae);
+    store_a(0, ra, rae);
+    load_a(1, ra, rae);
+  }
 #pragma unroll
   for (int c = 0; c < RB; ++c) load_b(c, rb[c], rbs[c]);
   __syncthreads();
@@ -857,7 +917,7 @@ __device__ __forceinline__ void mx_tall_body(const MxMoeParams& p, uint8_t (*sa)
   // then weights, so that the wait before the activation store (loads
   // complete in order) does not also wait for the weights issued with it.
   auto step = [&](int c, int d) __attribute__((always_inline)) {
-    compute(d & 1, rb[d % RB], rbs[d % RB]);
+    compute(PAIR ? d % kMxTallBufs : d & 1, rb[d % RB], rbs[d % RB], d & 1);
     // The matrix instructions touch no memory: without this the compiler
     // sinks all of them past the barriers to the end of the unrolled body
     // and spills the fragments they read.  An empty statement that reads
@@ -866,8 +926,15 @@ __device__ __forceinline__ void mx_tall_body(const MxMoeParams& p, uint8_t (*sa)
     for (int i = 0; i < MTA; ++i)
 #pragma unroll
       for (int j = 0; j < NTW; ++j) asm volatile("" : "+v"(acc[i][j]));
-    store_a((d + 1) & 1, ra, rae);
-    load_a(c + 2, ra, rae);
+    if constexpr (PAIR) {
+      store_e((d + 1) % kMxTallBufs);
+      if (d & 1) store_pair(c + 1);
+      load_e(c + 2);
+      if (!(d & 1)) load_pair(c + 2);
+    } else {
+      store_a((d + 1) & 1, ra, rae);
+      load_a(c + 2, ra, rae);
+    }
     load_b(c + RB, rb[d % RB], rbs[d % RB]);
     __syncthreads();
   };
@@ -907,8 +974,8 @@ __device__ __forceinline__ void mx_tall_groups(const MxMoeParams& p, uint8_t (*s
 template <int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void grouped_mx_tall_kernel(MxMoeParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t sa[2][8 * 1024];
-  __shared__ __attribute__((aligned(16))) uint32_t se[2][16 * 8];
+  __shared__ __attribute__((aligned(16))) uint8_t sa[kMxTallBufs][8 * 1024];
+  __shared__ __attribute__((aligned(16))) uint32_t se[kMxTallBufs][16 * 8];
   const int ntiles = ld_uniform(p.plan + p.list_idx);
   const int G = ntiles * p.n_blocks;
   if ((int)blockIdx.x >= G) return;
