@@ -728,9 +728,11 @@ __global__ __launch_bounds__(256) void grouped_mx_kernel(MxMoeParams p) {
 // no wavefront shares another's weights: they stream from memory straight
 // into registers (the streaming layout is the instruction operand, one
 // 16-byte load per lane per column tile and chunk) through a ring of three
-// chunks.  The activation tile is shared by the four wavefronts: its rows
-// are gathered into registers two chunks ahead and written to one of two
-// LDS buffers one chunk ahead of use; exponent words are kept as
+// chunks.  The activation tile is shared by the four wavefronts: in the
+// straight-line bodies its rows are gathered two chunks per load (128-byte
+// row pieces) into registers and written to four LDS chunk buffers, each at
+// least one chunk ahead of use; the looped body gathers one chunk two
+// chunks ahead into two buffers.  Exponent words are kept as
 // [row][tile] so that one 16-byte read gives a lane the bytes of 4 tiles.
 // Every load is an ordinary one, so the compiler's own waits are exact.
 // The main loop is instantiated for 8, 4, 2 and 1 active 16-row groups: a
