@@ -22,7 +22,10 @@ decode W4A16, prefill, large_e, skew in both NVFP4 variants; decode, prefill
 and large_e in OCP MXFP4; K/4 steps after W/4), each with its mean step, the
 per-step median over 100 replays of its timed graph after 10 warm-up
 replays, the per-stage breakdown, and the roofline figures of its dominant
-kernel (GEMM1) measured with HIP events on the launch stream.
+kernel (GEMM1) measured with HIP events on the launch stream.  Layers whose
+GEMMs run in two parts (the 512-expert layer: short experts and tall ones)
+run the tall experts' part on a second stream inside the captured graph
+(``"streams": 2``); the kernel figures time each GEMM whole on one stream.
 ``cpu_baseline`` is the FP64 oracle timed on the host cores on a bounded
 sample.
 """
@@ -309,12 +312,17 @@ def measure(w, built, variant, steps, warmup, mode, mx_weights=None):
     wbytes13 = (2 * w.I * w.H) // 2 + (2 * w.I * w.H) // block
     wbytes2 = (w.I * w.H) // 2 + (w.I * w.H) // block
     n_copies = min(8, max(1, math.ceil(4 * INFINITY_CACHE / max(1, touched * (wbytes13 + wbytes2)))))
+    # Layers whose GEMMs run in two parts (short and tall experts) overlap
+    # them on a second stream.
+    side = torch.cuda.Stream()
     if variant == "mxfp4":
         copies = mx_weight_copies(mx_weights, n_copies)
-        layer = MxStep(d, mx_weights, x.device)
+        layer = MxStep(d, mx_weights, x.device, side_stream=side)
     else:
         copies = weight_copies(wq, n_copies)
-        layer = ops.MoELayer(d, wq, g2, device=x.device)
+        layer = ops.MoELayer(d, wq, g2, device=x.device, side_stream=side)
+    inner = layer.layer if variant == "mxfp4" else layer
+    streams = 2 if inner.side is not None and (variant != "w4a4" or inner.decoded_copies) else 1
     out = torch.empty(w.T, w.H, dtype=torch.bfloat16, device=x.device)
     graphs = multi = None
     # The timed steps are one replay of a graph of that many steps.
@@ -351,7 +359,7 @@ def measure(w, built, variant, steps, warmup, mode, mx_weights=None):
     rec = {
         "workload": w.name, **w.describe(), "variant": variant, "mode": mode,
         "experts_touched": touched, "weight_copies": len(copies),
-        "steps_per_graph": per_graph if mode == "graph" else 1, "graph_uploaded": uploaded,
+        "steps_per_graph": per_graph if mode == "graph" else 1, "graph_uploaded": uploaded, "streams": streams,
         "steps": steps, "ms_per_step": round(ms, 5), "tokens_per_s": round(w.T / (ms * 1e-3), 1),
         "layer_tflops": round(layer_flops / (ms * 1e-3) / 1e12, 2),
         "layer_gbs": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
@@ -484,7 +492,8 @@ def main():
         "data": "synthetic (seeded), random-init weights",
         "config": {"workload": w.name, **w.describe(), "variant": a.variant, "mode": a.mode,
                    "experts_touched": m["experts_touched"], "weight_copies": m["weight_copies"],
-                   "steps_per_graph": m["steps_per_graph"], "graph_uploaded": m["graph_uploaded"]},
+                   "steps_per_graph": m["steps_per_graph"], "graph_uploaded": m["graph_uploaded"],
+                   "streams": m["streams"]},
         "layer_tflops": m["layer_tflops"], "layer_gbs": m["layer_gbs"],
         "layer_hbm_frac": m["layer_hbm_frac"],
         "roofline": m["roofline"],

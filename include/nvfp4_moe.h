@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define NVFP4_MOE_ABI_VERSION 8
+#define NVFP4_MOE_ABI_VERSION 9
 
 /* Status codes. */
 #define NVFP4_OK 0
@@ -442,6 +442,57 @@ int grouped_gemm2_combine_mxfp4(const nvfp4_moe_dims* dims, const uint8_t* a2_q,
 int moe_mxfp4_quantize_and_align(const nvfp4_moe_dims* dims, const uint16_t* x, uint8_t* a1_q, uint8_t* a1_e,
                                  const int32_t* topk_ids, int32_t* expert_offsets, int32_t* sorted_pair,
                                  int32_t* inv_pos, int32_t* plan, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* The grouped GEMMs in two parts, for two streams.                          */
+/* ------------------------------------------------------------------------ */
+/* A scheduling interface, not an operation of its own (the pages define
+ * none): when the pairs are few per expert on average but some expert may
+ * still hold more than 64 rows (the 512-expert layer with a shared expert of
+ * FlashInfer #2723, "Model"), the GEMMs run the short experts and the tall
+ * ones as separate launches that write disjoint rows.  A caller with a second
+ * stream can run the two side by side:
+ *   part 1 (short experts) and part 2 (tall experts) of GEMM1, then of GEMM2,
+ *   each part's GEMM2 after the same part's GEMM1 (it reads only the a2 rows
+ *   that part wrote), and part 3 (the combine) after both parts' GEMM2.
+ * Each *_part call takes the arguments of the call it is named after, plus
+ * part: 0 = the whole call (the same as the call itself), 1 = the short
+ * experts' rows, 2 = the tall experts' rows, 3 (GEMM2 calls only) = the
+ * combine alone.  Parts 1 and 2 write the same values, bit for bit, as part 0
+ * writes to those rows; for dimensions that do not run in two parts (see
+ * grouped_gemm_runs_in_parts, and W4A4 without the f16 activation copies),
+ * part 1 is the whole GEMM and part 2 launches nothing.  Errors: those of the
+ * named call, and NVFP4_EINVAL for a part outside 0..2 (GEMM1) or 0..3 (GEMM2).
+ * The library creates no stream or event: ordering the parts is the caller's
+ * (events between its streams). */
+
+/* 1 when these dimensions run the grouped GEMMs in two parts (then a second
+ * stream can overlap them), else 0 (also 0 for invalid dims). */
+int grouped_gemm_runs_in_parts(const nvfp4_moe_dims* dims);
+int grouped_gemm1_swiglu_part(const nvfp4_moe_dims* dims, const uint8_t* a1_q, const uint8_t* a1_sf,
+                              const uint16_t* a1_deq, const float* g1, const int32_t* sorted_pair,
+                              const int32_t* expert_offsets, const int32_t* plan, const uint8_t* w13_prep,
+                              const float* gw13, const float* g2, uint8_t* a2_q, uint8_t* a2_sf,
+                              uint16_t* a2_deq, int part, void* stream);
+int grouped_gemm2_combine_part(const nvfp4_moe_dims* dims, const uint8_t* a2_q, const uint8_t* a2_sf,
+                               const uint16_t* a2_deq, const float* g2, const int32_t* expert_offsets,
+                               const int32_t* inv_pos, const int32_t* plan, const float* topk_w,
+                               const uint8_t* w2_prep, const float* gw2, void* out, int out_dtype, void* ws,
+                               size_t ws_bytes, int part, void* stream);
+int grouped_gemm1_swiglu_w4a16_part(const nvfp4_moe_dims* dims, const uint16_t* x, const int32_t* sorted_pair,
+                                    const int32_t* expert_offsets, const int32_t* plan, const uint8_t* w13_prep,
+                                    const float* gw13, uint16_t* a2, int part, void* stream);
+int grouped_gemm2_combine_w4a16_part(const nvfp4_moe_dims* dims, const uint16_t* a2, const int32_t* expert_offsets,
+                                     const int32_t* inv_pos, const int32_t* plan, const float* topk_w,
+                                     const uint8_t* w2_prep, const float* gw2, void* out, int out_dtype, void* ws,
+                                     size_t ws_bytes, int part, void* stream);
+int grouped_gemm1_swiglu_mxfp4_part(const nvfp4_moe_dims* dims, const uint8_t* a1_q, const uint8_t* a1_e,
+                                    const int32_t* sorted_pair, const int32_t* expert_offsets, const int32_t* plan,
+                                    const uint8_t* w13_prep, uint8_t* a2_q, uint8_t* a2_e, int part, void* stream);
+int grouped_gemm2_combine_mxfp4_part(const nvfp4_moe_dims* dims, const uint8_t* a2_q, const uint8_t* a2_e,
+                                     const int32_t* expert_offsets, const int32_t* inv_pos, const int32_t* plan,
+                                     const float* topk_w, const uint8_t* w2_prep, void* out, int out_dtype,
+                                     void* ws, size_t ws_bytes, int part, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* GEMM2 + combine without allocation.                                       */

@@ -13,7 +13,7 @@ from ctypes import c_char_p, c_int, c_int32, c_int64, c_size_t, c_void_p
 # variant with different tile settings); the default is the in-tree build.
 LIB_PATH = os.environ.get("NVFP4_MOE_LIB") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "libnvfp4moe.so")
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 NVFP4_OK = 0
 NVFP4_EINVAL = -1
@@ -93,7 +93,13 @@ SIGNATURES = {
     "grouped_gemm2_combine_noalloc": (c_int, [_P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                               c_void_p, c_int, c_void_p]),
+    "grouped_gemm_runs_in_parts": (c_int, [_P]),
 }
+# The *_part calls: the named call's arguments with int part before the stream.
+for _name in ("grouped_gemm1_swiglu", "grouped_gemm2_combine", "grouped_gemm1_swiglu_w4a16",
+              "grouped_gemm2_combine_w4a16", "grouped_gemm1_swiglu_mxfp4", "grouped_gemm2_combine_mxfp4"):
+    _res, _args = SIGNATURES[_name]
+    SIGNATURES[_name + "_part"] = (_res, _args[:-1] + [c_int, c_void_p])
 
 
 class LibraryNotBuilt(RuntimeError):

@@ -454,6 +454,11 @@ int grouped_gemm_prefers_decoded(const nvfp4_moe_dims* d) {
   return nvfp4::prefers_decoded(d->T, d->topk, d->E, d->shared) ? 1 : 0;
 }
 
+int grouped_gemm_runs_in_parts(const nvfp4_moe_dims* d) {
+  if (check_dims(d, "grouped_gemm_runs_in_parts")) return 0;
+  return nvfp4::split_experts(nvfp4::align_shape(d->T, d->topk, d->E, d->shared)) ? 1 : 0;
+}
+
 size_t grouped_gemm_workspace_size(const nvfp4_moe_dims* d) {
   if (check_dims(d, "grouped_gemm_workspace_size")) return 0;
   return (size_t)pairs(d) * (size_t)d->H * sizeof(float);
@@ -476,12 +481,12 @@ static nvfp4::GemmArgs gemm_args(const nvfp4_moe_dims* d) {
   return a;
 }
 
-int grouped_gemm1_swiglu(const nvfp4_moe_dims* d, const uint8_t* a1_q, const uint8_t* a1_sf,
-                         const uint16_t* a1_deq, const float* g1, const int32_t* sorted_pair,
-                         const int32_t* expert_offsets, const int32_t* plan,
-                         const uint8_t* w13_prep, const float* gw13, const float* g2,
-                         uint8_t* a2_q, uint8_t* a2_sf, uint16_t* a2_deq, void* stream) {
-  const char* W = "grouped_gemm1_swiglu";
+static int grouped_gemm1_swiglu_impl(const char* W, int part, const nvfp4_moe_dims* d, const uint8_t* a1_q,
+                                     const uint8_t* a1_sf, const uint16_t* a1_deq, const float* g1,
+                                     const int32_t* sorted_pair, const int32_t* expert_offsets,
+                                     const int32_t* plan, const uint8_t* w13_prep, const float* gw13,
+                                     const float* g2, uint8_t* a2_q, uint8_t* a2_sf, uint16_t* a2_deq,
+                                     void* stream) {
   if (int r = check_dims(d, W)) return r;
   if (d->T == 0) return ok();
   if ((!a1_deq && (!a1_q || !a1_sf)) || !g1 || !sorted_pair || !expert_offsets || !plan ||
@@ -502,14 +507,36 @@ int grouped_gemm1_swiglu(const nvfp4_moe_dims* d, const uint8_t* a1_q, const uin
   a.out_q = a2_q;
   a.out_sf = a2_sf;
   a.out_h = a2_deq;
+  a.part = part;
   return launched(nvfp4::launch_gemm1(a, true, S(stream)), W);
 }
 
-int grouped_gemm1_swiglu_w4a16(const nvfp4_moe_dims* d, const uint16_t* x,
-                               const int32_t* sorted_pair, const int32_t* expert_offsets,
-                               const int32_t* plan, const uint8_t* w13_prep, const float* gw13,
-                               uint16_t* a2, void* stream) {
-  const char* W = "grouped_gemm1_swiglu_w4a16";
+int grouped_gemm1_swiglu(const nvfp4_moe_dims* d, const uint8_t* a1_q, const uint8_t* a1_sf,
+                         const uint16_t* a1_deq, const float* g1, const int32_t* sorted_pair,
+                         const int32_t* expert_offsets, const int32_t* plan, const uint8_t* w13_prep,
+                         const float* gw13, const float* g2, uint8_t* a2_q, uint8_t* a2_sf, uint16_t* a2_deq,
+                         void* stream) {
+  return grouped_gemm1_swiglu_impl("grouped_gemm1_swiglu", nvfp4::kPartAll, d, a1_q, a1_sf, a1_deq, g1,
+                                   sorted_pair, expert_offsets, plan, w13_prep, gw13, g2, a2_q, a2_sf, a2_deq,
+                                   stream);
+}
+
+int grouped_gemm1_swiglu_part(const nvfp4_moe_dims* d, const uint8_t* a1_q, const uint8_t* a1_sf,
+                              const uint16_t* a1_deq, const float* g1, const int32_t* sorted_pair,
+                              const int32_t* expert_offsets, const int32_t* plan, const uint8_t* w13_prep,
+                              const float* gw13, const float* g2, uint8_t* a2_q, uint8_t* a2_sf,
+                              uint16_t* a2_deq, int part, void* stream) {
+  if (part < 0 || part > 2)
+    return fail(NVFP4_EINVAL, "%s: EINVAL part=%d (0..2)", "grouped_gemm1_swiglu_part", part);
+  return grouped_gemm1_swiglu_impl("grouped_gemm1_swiglu_part", part, d, a1_q, a1_sf, a1_deq, g1, sorted_pair,
+                                   expert_offsets, plan, w13_prep, gw13, g2, a2_q, a2_sf, a2_deq, stream);
+}
+
+static int grouped_gemm1_swiglu_w4a16_impl(const char* W, int part, const nvfp4_moe_dims* d,
+                                           const uint16_t* x, const int32_t* sorted_pair,
+                                           const int32_t* expert_offsets, const int32_t* plan,
+                                           const uint8_t* w13_prep, const float* gw13, uint16_t* a2,
+                                           void* stream) {
   if (int r = check_dims(d, W)) return r;
   if (d->T == 0) return ok();
   if (!x || !sorted_pair || !expert_offsets || !plan || !w13_prep || !gw13 || !a2 ||
@@ -523,7 +550,25 @@ int grouped_gemm1_swiglu_w4a16(const nvfp4_moe_dims* d, const uint16_t* x,
   a.w_prep = w13_prep;
   a.g_w = gw13;
   a.out_h = a2;
+  a.part = part;
   return launched(nvfp4::launch_gemm1(a, false, S(stream)), W);
+}
+
+int grouped_gemm1_swiglu_w4a16(const nvfp4_moe_dims* d, const uint16_t* x, const int32_t* sorted_pair,
+                               const int32_t* expert_offsets, const int32_t* plan, const uint8_t* w13_prep,
+                               const float* gw13, uint16_t* a2, void* stream) {
+  return grouped_gemm1_swiglu_w4a16_impl("grouped_gemm1_swiglu_w4a16", nvfp4::kPartAll, d, x, sorted_pair,
+                                         expert_offsets, plan, w13_prep, gw13, a2, stream);
+}
+
+int grouped_gemm1_swiglu_w4a16_part(const nvfp4_moe_dims* d, const uint16_t* x, const int32_t* sorted_pair,
+                                    const int32_t* expert_offsets, const int32_t* plan,
+                                    const uint8_t* w13_prep, const float* gw13, uint16_t* a2, int part,
+                                    void* stream) {
+  if (part < 0 || part > 2)
+    return fail(NVFP4_EINVAL, "%s: EINVAL part=%d (0..2)", "grouped_gemm1_swiglu_w4a16_part", part);
+  return grouped_gemm1_swiglu_w4a16_impl("grouped_gemm1_swiglu_w4a16_part", part, d, x, sorted_pair,
+                                         expert_offsets, plan, w13_prep, gw13, a2, stream);
 }
 
 static int gemm2_common(const char* W, const nvfp4_moe_dims* d, const int32_t* expert_offsets,
@@ -544,13 +589,12 @@ static int gemm2_common(const char* W, const nvfp4_moe_dims* d, const int32_t* e
   return NVFP4_OK;
 }
 
-int grouped_gemm2_combine(const nvfp4_moe_dims* d, const uint8_t* a2_q, const uint8_t* a2_sf,
-                          const uint16_t* a2_deq, const float* g2, const int32_t* expert_offsets,
-                          const int32_t* inv_pos,
-                          const int32_t* plan, const float* topk_w, const uint8_t* w2_prep,
-                          const float* gw2, void* out, int out_dtype, void* ws, size_t ws_bytes,
-                          void* stream) {
-  const char* W = "grouped_gemm2_combine";
+static int grouped_gemm2_combine_impl(const char* W, int part, const nvfp4_moe_dims* d, const uint8_t* a2_q,
+                                      const uint8_t* a2_sf, const uint16_t* a2_deq, const float* g2,
+                                      const int32_t* expert_offsets, const int32_t* inv_pos,
+                                      const int32_t* plan, const float* topk_w, const uint8_t* w2_prep,
+                                      const float* gw2, void* out, int out_dtype, void* ws, size_t ws_bytes,
+                                      void* stream) {
   if (int r = gemm2_common(W, d, expert_offsets, inv_pos, plan, topk_w, w2_prep, gw2, out,
                            out_dtype, ws, ws_bytes))
     return r;
@@ -572,15 +616,37 @@ int grouped_gemm2_combine(const nvfp4_moe_dims* d, const uint8_t* a2_q, const ui
   a.d_ws = static_cast<float*>(ws);
   a.out = out;
   a.out_dtype = out_dtype;
+  a.part = part;
   return launched(nvfp4::launch_gemm2_combine(a, true, S(stream)), W);
 }
 
-int grouped_gemm2_combine_w4a16(const nvfp4_moe_dims* d, const uint16_t* a2,
-                                const int32_t* expert_offsets, const int32_t* inv_pos,
-                                const int32_t* plan, const float* topk_w, const uint8_t* w2_prep,
-                                const float* gw2, void* out, int out_dtype, void* ws,
-                                size_t ws_bytes, void* stream) {
-  const char* W = "grouped_gemm2_combine_w4a16";
+int grouped_gemm2_combine(const nvfp4_moe_dims* d, const uint8_t* a2_q, const uint8_t* a2_sf,
+                          const uint16_t* a2_deq, const float* g2, const int32_t* expert_offsets,
+                          const int32_t* inv_pos, const int32_t* plan, const float* topk_w,
+                          const uint8_t* w2_prep, const float* gw2, void* out, int out_dtype, void* ws,
+                          size_t ws_bytes, void* stream) {
+  return grouped_gemm2_combine_impl("grouped_gemm2_combine", nvfp4::kPartAll, d, a2_q, a2_sf, a2_deq, g2,
+                                    expert_offsets, inv_pos, plan, topk_w, w2_prep, gw2, out, out_dtype, ws,
+                                    ws_bytes, stream);
+}
+
+int grouped_gemm2_combine_part(const nvfp4_moe_dims* d, const uint8_t* a2_q, const uint8_t* a2_sf,
+                               const uint16_t* a2_deq, const float* g2, const int32_t* expert_offsets,
+                               const int32_t* inv_pos, const int32_t* plan, const float* topk_w,
+                               const uint8_t* w2_prep, const float* gw2, void* out, int out_dtype, void* ws,
+                               size_t ws_bytes, int part, void* stream) {
+  if (part < 0 || part > 3)
+    return fail(NVFP4_EINVAL, "%s: EINVAL part=%d (0..3)", "grouped_gemm2_combine_part", part);
+  return grouped_gemm2_combine_impl("grouped_gemm2_combine_part", part, d, a2_q, a2_sf, a2_deq, g2,
+                                    expert_offsets, inv_pos, plan, topk_w, w2_prep, gw2, out, out_dtype, ws,
+                                    ws_bytes, stream);
+}
+
+static int grouped_gemm2_combine_w4a16_impl(const char* W, int part, const nvfp4_moe_dims* d,
+                                            const uint16_t* a2, const int32_t* expert_offsets,
+                                            const int32_t* inv_pos, const int32_t* plan, const float* topk_w,
+                                            const uint8_t* w2_prep, const float* gw2, void* out,
+                                            int out_dtype, void* ws, size_t ws_bytes, void* stream) {
   if (int r = gemm2_common(W, d, expert_offsets, inv_pos, plan, topk_w, w2_prep, gw2, out,
                            out_dtype, ws, ws_bytes))
     return r;
@@ -597,7 +663,29 @@ int grouped_gemm2_combine_w4a16(const nvfp4_moe_dims* d, const uint16_t* a2,
   a.d_ws = static_cast<float*>(ws);
   a.out = out;
   a.out_dtype = out_dtype;
+  a.part = part;
   return launched(nvfp4::launch_gemm2_combine(a, false, S(stream)), W);
+}
+
+int grouped_gemm2_combine_w4a16(const nvfp4_moe_dims* d, const uint16_t* a2, const int32_t* expert_offsets,
+                                const int32_t* inv_pos, const int32_t* plan, const float* topk_w,
+                                const uint8_t* w2_prep, const float* gw2, void* out, int out_dtype, void* ws,
+                                size_t ws_bytes, void* stream) {
+  return grouped_gemm2_combine_w4a16_impl("grouped_gemm2_combine_w4a16", nvfp4::kPartAll, d, a2,
+                                          expert_offsets, inv_pos, plan, topk_w, w2_prep, gw2, out, out_dtype,
+                                          ws, ws_bytes, stream);
+}
+
+int grouped_gemm2_combine_w4a16_part(const nvfp4_moe_dims* d, const uint16_t* a2,
+                                     const int32_t* expert_offsets, const int32_t* inv_pos,
+                                     const int32_t* plan, const float* topk_w, const uint8_t* w2_prep,
+                                     const float* gw2, void* out, int out_dtype, void* ws, size_t ws_bytes,
+                                     int part, void* stream) {
+  if (part < 0 || part > 3)
+    return fail(NVFP4_EINVAL, "%s: EINVAL part=%d (0..3)", "grouped_gemm2_combine_w4a16_part", part);
+  return grouped_gemm2_combine_w4a16_impl("grouped_gemm2_combine_w4a16_part", part, d, a2, expert_offsets,
+                                          inv_pos, plan, topk_w, w2_prep, gw2, out, out_dtype, ws, ws_bytes,
+                                          stream);
 }
 
 // ------------------------------------------------------------------ MXFP4 layer
@@ -641,10 +729,11 @@ bool mx_offsets_fit(const nvfp4_moe_dims* d) {
 }
 }  // namespace
 
-int grouped_gemm1_swiglu_mxfp4(const nvfp4_moe_dims* d, const uint8_t* a1_q, const uint8_t* a1_e,
-                               const int32_t* sorted_pair, const int32_t* expert_offsets, const int32_t* plan,
-                               const uint8_t* w13_prep, uint8_t* a2_q, uint8_t* a2_e, void* stream) {
-  const char* W = "grouped_gemm1_swiglu_mxfp4";
+static int grouped_gemm1_swiglu_mxfp4_impl(const char* W, int part, const nvfp4_moe_dims* d,
+                                           const uint8_t* a1_q, const uint8_t* a1_e,
+                                           const int32_t* sorted_pair, const int32_t* expert_offsets,
+                                           const int32_t* plan, const uint8_t* w13_prep, uint8_t* a2_q,
+                                           uint8_t* a2_e, void* stream) {
   if (int r = check_dims(d, W)) return r;
   if (!mx_offsets_fit(d))
     return fail(NVFP4_ESHAPE, "%s: ESHAPE num_experts=%d M=%lld N=%d K=%d (operand offsets must fit 31 bits)", W,
@@ -662,14 +751,33 @@ int grouped_gemm1_swiglu_mxfp4(const nvfp4_moe_dims* d, const uint8_t* a1_q, con
   a.w_prep = w13_prep;
   a.out_q = a2_q;
   a.out_e = a2_e;
+  a.part = part;
   return launched(nvfp4::launch_mx_gemm1_swiglu(a, S(stream)), W);
 }
 
-int grouped_gemm2_combine_mxfp4(const nvfp4_moe_dims* d, const uint8_t* a2_q, const uint8_t* a2_e,
-                                const int32_t* expert_offsets, const int32_t* inv_pos, const int32_t* plan,
-                                const float* topk_w, const uint8_t* w2_prep, void* out, int out_dtype, void* ws,
-                                size_t ws_bytes, void* stream) {
-  const char* W = "grouped_gemm2_combine_mxfp4";
+int grouped_gemm1_swiglu_mxfp4(const nvfp4_moe_dims* d, const uint8_t* a1_q, const uint8_t* a1_e,
+                               const int32_t* sorted_pair, const int32_t* expert_offsets, const int32_t* plan,
+                               const uint8_t* w13_prep, uint8_t* a2_q, uint8_t* a2_e, void* stream) {
+  return grouped_gemm1_swiglu_mxfp4_impl("grouped_gemm1_swiglu_mxfp4", nvfp4::kPartAll, d, a1_q, a1_e,
+                                         sorted_pair, expert_offsets, plan, w13_prep, a2_q, a2_e, stream);
+}
+
+int grouped_gemm1_swiglu_mxfp4_part(const nvfp4_moe_dims* d, const uint8_t* a1_q, const uint8_t* a1_e,
+                                    const int32_t* sorted_pair, const int32_t* expert_offsets,
+                                    const int32_t* plan, const uint8_t* w13_prep, uint8_t* a2_q,
+                                    uint8_t* a2_e, int part, void* stream) {
+  if (part < 0 || part > 2)
+    return fail(NVFP4_EINVAL, "%s: EINVAL part=%d (0..2)", "grouped_gemm1_swiglu_mxfp4_part", part);
+  return grouped_gemm1_swiglu_mxfp4_impl("grouped_gemm1_swiglu_mxfp4_part", part, d, a1_q, a1_e, sorted_pair,
+                                         expert_offsets, plan, w13_prep, a2_q, a2_e, stream);
+}
+
+static int grouped_gemm2_combine_mxfp4_impl(const char* W, int part, const nvfp4_moe_dims* d,
+                                            const uint8_t* a2_q, const uint8_t* a2_e,
+                                            const int32_t* expert_offsets, const int32_t* inv_pos,
+                                            const int32_t* plan, const float* topk_w, const uint8_t* w2_prep,
+                                            void* out, int out_dtype, void* ws, size_t ws_bytes,
+                                            void* stream) {
   if (int r = gemm2_common(W, d, expert_offsets, inv_pos, plan, topk_w, w2_prep, nullptr, out, out_dtype, ws,
                            ws_bytes, false))
     return r;
@@ -688,7 +796,29 @@ int grouped_gemm2_combine_mxfp4(const nvfp4_moe_dims* d, const uint8_t* a2_q, co
   a.d_ws = static_cast<float*>(ws);
   a.out = out;
   a.out_dtype = out_dtype;
+  a.part = part;
   return launched(nvfp4::launch_mx_gemm2_combine(a, S(stream)), W);
+}
+
+int grouped_gemm2_combine_mxfp4(const nvfp4_moe_dims* d, const uint8_t* a2_q, const uint8_t* a2_e,
+                                const int32_t* expert_offsets, const int32_t* inv_pos, const int32_t* plan,
+                                const float* topk_w, const uint8_t* w2_prep, void* out, int out_dtype,
+                                void* ws, size_t ws_bytes, void* stream) {
+  return grouped_gemm2_combine_mxfp4_impl("grouped_gemm2_combine_mxfp4", nvfp4::kPartAll, d, a2_q, a2_e,
+                                          expert_offsets, inv_pos, plan, topk_w, w2_prep, out, out_dtype, ws,
+                                          ws_bytes, stream);
+}
+
+int grouped_gemm2_combine_mxfp4_part(const nvfp4_moe_dims* d, const uint8_t* a2_q, const uint8_t* a2_e,
+                                     const int32_t* expert_offsets, const int32_t* inv_pos,
+                                     const int32_t* plan, const float* topk_w, const uint8_t* w2_prep,
+                                     void* out, int out_dtype, void* ws, size_t ws_bytes, int part,
+                                     void* stream) {
+  if (part < 0 || part > 3)
+    return fail(NVFP4_EINVAL, "%s: EINVAL part=%d (0..3)", "grouped_gemm2_combine_mxfp4_part", part);
+  return grouped_gemm2_combine_mxfp4_impl("grouped_gemm2_combine_mxfp4_part", part, d, a2_q, a2_e,
+                                          expert_offsets, inv_pos, plan, topk_w, w2_prep, out, out_dtype, ws,
+                                          ws_bytes, stream);
 }
 
 // ------------------------------------------------------------------ GEMM2 without allocation

@@ -1416,8 +1416,11 @@ hipError_t launch_stream_pf(const KParams& kp, int len, hipStream_t s) {
   }
 }
 
+// part (kPart*): kPartShort and kPartTall launch one list each of a split
+// layer; a layer that is not split runs whole under kPartShort and not at
+// all under kPartTall, so the two always add up to kPartAll.
 template <int AK, int EPI>
-hipError_t launch_gemm(KParams kp, const AlignShape& al, hipStream_t s) {
+hipError_t launch_gemm(KParams kp, const AlignShape& al, hipStream_t s, int part) {
   constexpr int kStreamNTW = swiglu_epi(EPI) ? NVFP4_STREAM_NTW : NVFP4_STREAM_NTW_DOWN;
   int li = min(pick_list(al.P, al.slots), NVFP4_LIST_MAX);
   // The streaming kernel addresses with 32-bit buffer offsets.
@@ -1429,6 +1432,7 @@ hipError_t launch_gemm(KParams kp, const AlignShape& al, hipStream_t s) {
     // 16-bit activations on tall tiles: the wide kernel (128-row tiles).
     constexpr bool kUp32 = swiglu_epi(EPI) && AK == kActF16;
     if (li >= NVFP4_WIDE_MIN_LIST && offsets_fit) {
+      if (part == kPartTall) return hipSuccess;
       kp.list_idx = 3;
       if constexpr (AK == kActF16) {
         if (al.list_len[3] * ((kp.N + 255) / 256) <= NVFP4_SMALL_WIDE_GRID)
@@ -1441,13 +1445,16 @@ hipError_t launch_gemm(KParams kp, const AlignShape& al, hipStream_t s) {
     // those experts (list 5) go to the wide kernel and the rest (list 4) to
     // the streaming kernel.  Two launches writing disjoint rows.
     if (split_experts(al) && offsets_fit) {
-      kp.list_idx = 4;
-      hipError_t e = launch_stream_pf<AK, EPI, 1, kStreamNTW>(kp, (int)al.list_len[4], s);
-      if (e != hipSuccess) return e;
+      if (part != kPartTall) {
+        kp.list_idx = 4;
+        const hipError_t e = launch_stream_pf<AK, EPI, 1, kStreamNTW>(kp, (int)al.list_len[4], s);
+        if (e != hipSuccess || part == kPartShort) return e;
+      }
       kp.list_idx = 5;
       return launch_wide<AK, EPI, kUp32 ? 32 : NVFP4_TALL_WN>(kp, (int)al.list_len[5], s);
     }
   }
+  if (part == kPartTall) return hipSuccess;
   kp.list_idx = li;
   const int len = (int)al.list_len[li];
   switch (li) {
@@ -1506,12 +1513,12 @@ hipError_t launch_gemm1(const GemmArgs& a, bool w4a4, hipStream_t s) {
     k.out_q = a.out_q;
     k.out_sf = a.out_sf;
     k.out_h = a.out_h;
-    if (a.a_h) return launch_gemm<kActF16, kEpiSwigluFp4>(k, al, s);
-    return launch_gemm<kActCodes, kEpiSwigluFp4>(k, al, s);
+    if (a.a_h) return launch_gemm<kActF16, kEpiSwigluFp4>(k, al, s, a.part);
+    return launch_gemm<kActCodes, kEpiSwigluFp4>(k, al, s, a.part);
   }
   k.a_h = a.a_h;
   k.out_h = a.out_h;
-  return launch_gemm<kActBf16, kEpiSwigluBf16>(k, al, s);
+  return launch_gemm<kActBf16, kEpiSwigluBf16>(k, al, s, a.part);
 }
 
 hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
@@ -1552,10 +1559,13 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   if (!a.w4a4)
-    return f32 ? launch_gemm<kActBf16, kEpiStoreF32>(k, al, s) : launch_gemm<kActBf16, kEpiStoreBf16>(k, al, s);
+    return f32 ? launch_gemm<kActBf16, kEpiStoreF32>(k, al, s, kPartAll)
+               : launch_gemm<kActBf16, kEpiStoreBf16>(k, al, s, kPartAll);
   if (a.a_h)
-    return f32 ? launch_gemm<kActF16, kEpiStoreF32>(k, al, s) : launch_gemm<kActF16, kEpiStoreBf16>(k, al, s);
-  return f32 ? launch_gemm<kActCodes, kEpiStoreF32>(k, al, s) : launch_gemm<kActCodes, kEpiStoreBf16>(k, al, s);
+    return f32 ? launch_gemm<kActF16, kEpiStoreF32>(k, al, s, kPartAll)
+               : launch_gemm<kActF16, kEpiStoreBf16>(k, al, s, kPartAll);
+  return f32 ? launch_gemm<kActCodes, kEpiStoreF32>(k, al, s, kPartAll)
+             : launch_gemm<kActCodes, kEpiStoreBf16>(k, al, s, kPartAll);
 }
 
 hipError_t launch_combine(const float* d, const int32_t* inv_pos, const float* topk_w, int T, int topk,
@@ -1587,19 +1597,23 @@ hipError_t launch_gemm2_combine(const GemmArgs& a, bool w4a4, hipStream_t s) {
   k.w_q = a.w_prep;
   k.w_sf = a.w_prep + (size_t)al.slots * k.N * (k.K / 2);
   k.out_f32 = a.d_ws;
-  hipError_t e;
-  if (w4a4) {
-    k.a_q = a.a_q;
-    k.a_sf = a.a_sf;
-    k.a_h = a.a_h;
-    k.g_a = a.g_a;
-    e = a.a_h ? launch_gemm<kActF16, kEpiStoreF32>(k, al, s)
-              : launch_gemm<kActCodes, kEpiStoreF32>(k, al, s);
-  } else {
-    k.a_h = a.a_h;
-    e = launch_gemm<kActBf16, kEpiStoreF32>(k, al, s);
+  hipError_t e = hipSuccess;
+  if (a.part != kPartCombine) {
+    if (w4a4) {
+      k.a_q = a.a_q;
+      k.a_sf = a.a_sf;
+      k.a_h = a.a_h;
+      k.g_a = a.g_a;
+      e = a.a_h ? launch_gemm<kActF16, kEpiStoreF32>(k, al, s, a.part)
+                : launch_gemm<kActCodes, kEpiStoreF32>(k, al, s, a.part);
+    } else {
+      k.a_h = a.a_h;
+      e = launch_gemm<kActBf16, kEpiStoreF32>(k, al, s, a.part);
+    }
   }
-  if (e != hipSuccess) return e;
+  // The combine needs every row of d: it follows the whole GEMM, or runs
+  // alone once both lists are done.
+  if (e != hipSuccess || (a.part != kPartAll && a.part != kPartCombine)) return e;
   return launch_combine(a.d_ws, a.inv_pos, a.topk_w, a.T, a.topk, a.shared, a.H, a.out, a.out_dtype, s);
 }
 

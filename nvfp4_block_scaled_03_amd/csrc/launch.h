@@ -121,7 +121,12 @@ struct GemmArgs {
   float* d_ws;
   void* out;
   int out_dtype;
+  // Which share of the work a call launches (kPart*): all of it, the
+  // short-expert list or the tall-expert list of a split layer, or the
+  // combine alone.
+  int part;
 };
+constexpr int kPartAll = 0, kPartShort = 1, kPartTall = 2, kPartCombine = 3;
 hipError_t launch_gemm1(const GemmArgs& a, bool w4a4, hipStream_t s);
 // Whether the W4A4 GEMMs run faster on the exact f16 activation copies than
 // on the codes for these dimensions (the wide 128-row-tile kernel).

@@ -45,6 +45,7 @@ struct MxGemmArgs {
   float* d_ws;                  // GEMM2: FP32 [P][H]
   void* out;
   int out_dtype;
+  int part;                     // share of the work, as GemmArgs::part
 };
 hipError_t launch_mx_gemm1_swiglu(const MxGemmArgs& a, hipStream_t s);
 hipError_t launch_mx_gemm2_combine(const MxGemmArgs& a, hipStream_t s);

@@ -1014,18 +1014,23 @@ hipError_t launch_grouped_mx_tall(MxMoeParams p, int64_t list_len, hipStream_t s
   return hipGetLastError();
 }
 
+// part (kPart*): the short- or the tall-expert list of a split layer; a layer
+// that is not split runs whole under kPartShort and not at all under kPartTall.
 template <int EPI>
-hipError_t launch_grouped_mx(MxMoeParams p, const AlignShape& al, hipStream_t s) {
+hipError_t launch_grouped_mx(MxMoeParams p, const AlignShape& al, hipStream_t s, int part) {
   p.n_blocks = (p.N + 255) / 256;
   if (split_experts(al)) {
     // short experts on 16-row tiles, the tall ones (a shared expert) on the
     // tall-tile kernel, which reads their weights once per 128 rows
-    p.list_idx = 4;
-    const hipError_t e = launch_grouped_mx_t<1, EPI>(p, al.list_len[4], s);
-    if (e != hipSuccess) return e;
+    if (part != kPartTall) {
+      p.list_idx = 4;
+      const hipError_t e = launch_grouped_mx_t<1, EPI>(p, al.list_len[4], s);
+      if (e != hipSuccess || part == kPartShort) return e;
+    }
     p.list_idx = 5;
     return launch_grouped_mx_tall<EPI>(p, al.list_len[5], s);
   }
+  if (part == kPartTall) return hipSuccess;
   const int li = pick_list(al.P, al.slots);
   p.list_idx = li;
   switch (li) {
@@ -1112,7 +1117,7 @@ hipError_t launch_mx_gemm1_swiglu(const MxGemmArgs& a, hipStream_t s) {
   p.w_expert_bytes = (int64_t)p.N * (p.K / 2) + (int64_t)p.N * (p.K / 32);
   p.out_q = a.out_q;
   p.out_e = a.out_e;
-  return launch_grouped_mx<kMxSwiglu>(p, al, s);
+  return launch_grouped_mx<kMxSwiglu>(p, al, s, a.part);
 }
 
 hipError_t launch_mx_gemm2_combine(const MxGemmArgs& a, hipStream_t s) {
@@ -1130,8 +1135,8 @@ hipError_t launch_mx_gemm2_combine(const MxGemmArgs& a, hipStream_t s) {
   p.w_prep = a.w_prep;
   p.w_expert_bytes = (int64_t)p.N * (p.K / 2) + (int64_t)p.N * (p.K / 32);
   p.out_f32 = a.d_ws;
-  hipError_t e = launch_grouped_mx<kMxStoreF32>(p, al, s);
-  if (e != hipSuccess) return e;
+  const hipError_t e = a.part == kPartCombine ? hipSuccess : launch_grouped_mx<kMxStoreF32>(p, al, s, a.part);
+  if (e != hipSuccess || (a.part != kPartAll && a.part != kPartCombine)) return e;
   return launch_combine(a.d_ws, a.inv_pos, a.topk_w, a.T, a.topk, a.shared, a.H, a.out, a.out_dtype, s);
 }
 

@@ -410,14 +410,57 @@ def quantize_mx_expert_weights(d: Dims, w13: torch.Tensor, w2: torch.Tensor) -> 
     return MxExpertWeights(prep_mx_expert_weights(d, 13, q13, e13), prep_mx_expert_weights(d, 2, q2, e2))
 
 
+PART_ALL, PART_SHORT, PART_TALL, PART_COMBINE = 0, 1, 2, 3
+
+
+def _side_stream_if_parts(d: Dims, side_stream):
+    """The side stream to use, or None when these dims run the GEMMs whole."""
+    if side_stream is None or not _lib.load().grouped_gemm_runs_in_parts(ctypes.byref(d)):
+        return None
+    return side_stream
+
+
+def _run_gemms(side, gemm1, gemm2, marks=None):
+    """GEMM1 then GEMM2 + combine of one layer; ``gemm1(part, stream)`` and
+    ``gemm2(part, stream)`` launch one part.  With a side stream, the tall
+    experts' part of both GEMMs runs there (each part's GEMM2 reads only the
+    rows its GEMM1 wrote) while the short experts' part runs on the current
+    stream, which then waits for the side stream and runs the combine.  The
+    events make the fork and the join part of a captured graph too."""
+    main = torch.cuda.current_stream()
+    s = ctypes.c_void_p(main.cuda_stream)
+    if side is None:
+        gemm1(PART_ALL, s)
+        if marks:
+            marks[1].record()
+        gemm2(PART_ALL, s)
+    else:
+        side.wait_stream(main)
+        ss = ctypes.c_void_p(side.cuda_stream)
+        gemm1(PART_TALL, ss)
+        gemm2(PART_TALL, ss)
+        gemm1(PART_SHORT, s)
+        if marks:
+            marks[1].record()
+        gemm2(PART_SHORT, s)
+        main.wait_stream(side)
+        gemm2(PART_COMBINE, s)
+    if marks:
+        marks[2].record()
+
+
 class MxMoELayer:
     """One OCP MXFP4 expert layer with its intermediates preallocated (a call
     launches kernels only): mxfp4_quantize, moe_align,
     grouped_gemm1_swiglu_mxfp4, grouped_gemm2_combine_mxfp4."""
 
-    def __init__(self, d: Dims, weights: MxExpertWeights, device="cuda"):
+    def __init__(self, d: Dims, weights: MxExpertWeights, device="cuda", side_stream=None):
+        """``side_stream``: a second stream for layers that run their GEMMs
+        in two parts (``grouped_gemm_runs_in_parts``): the tall experts' part
+        then runs on it beside the short experts' part."""
         self.d, self.w = d, weights
         dev = torch.device(device)
+        self.side = _side_stream_if_parts(d, side_stream)
         P = d.T * d.topk + d.shared * d.T
         self.a1_q = torch.empty(max(d.T, 1), d.H // 2, dtype=torch.uint8, device=dev)
         self.a1_e = torch.empty(max(d.T, 1), d.H // 32, dtype=torch.uint8, device=dev)
@@ -435,16 +478,15 @@ class MxMoELayer:
              _p(self.al.workspace), self.al.workspace.numel(), s)
         if marks:
             marks[0].record()
-        call("grouped_gemm1_swiglu_mxfp4", ctypes.byref(d), _p(self.a1_q), _p(self.a1_e),
-             _p(self.al.sorted_pair), _p(self.al.offsets), _p(self.al.plan), _p(w.prep13),
-             _p(self.a2_q), _p(self.a2_e), s)
-        if marks:
-            marks[1].record()
-        call("grouped_gemm2_combine_mxfp4", ctypes.byref(d), _p(self.a2_q), _p(self.a2_e),
-             _p(self.al.offsets), _p(self.al.inv_pos), _p(self.al.plan), _p(topk_w), _p(w.prep2),
-             _p(out), _dtype_code(out), _p(self.ws), self.ws.numel() * 4, s)
-        if marks:
-            marks[2].record()
+        g1 = lambda part, st: call(
+            "grouped_gemm1_swiglu_mxfp4_part", ctypes.byref(d), _p(self.a1_q), _p(self.a1_e),
+            _p(self.al.sorted_pair), _p(self.al.offsets), _p(self.al.plan), _p(w.prep13),
+            _p(self.a2_q), _p(self.a2_e), part, st)
+        g2 = lambda part, st: call(
+            "grouped_gemm2_combine_mxfp4_part", ctypes.byref(d), _p(self.a2_q), _p(self.a2_e),
+            _p(self.al.offsets), _p(self.al.inv_pos), _p(self.al.plan), _p(topk_w), _p(w.prep2),
+            _p(out), _dtype_code(out), _p(self.ws), self.ws.numel() * 4, part, st)
+        _run_gemms(self.side, g1, g2, marks)
         return out
 
     def gemm1(self, weights=None):
@@ -466,11 +508,12 @@ class MoELayer:
     call launches kernels only (and can be captured in a HIP graph)."""
 
     def __init__(self, d: Dims, weights: ExpertWeights, g2: torch.Tensor, device="cuda",
-                 decoded_copies: Optional[bool] = None):
+                 decoded_copies: Optional[bool] = None, side_stream=None):
         """``decoded_copies``: W4A4 keeps exact f16 copies of a1 and a2 next to
         their codes and the GEMMs read those instead of decoding the codes.
         None (default) asks the library which is faster for these dims (the
-        copies pay off for tall tiles, not for decode-sized batches)."""
+        copies pay off for tall tiles, not for decode-sized batches).
+        ``side_stream``: as for MxMoELayer (W4A4 splits only with the copies)."""
         self.d = d
         self.w = weights
         self.g2 = g2
@@ -496,6 +539,7 @@ class MoELayer:
             self.a1_deq = torch.empty(max(d.T, 1), d.H, dtype=torch.float16, device=dev)
             self.a2_deq = torch.empty(max(P, 1), d.I, dtype=torch.float16, device=dev)
         self.ws = gemm_workspace(d, dev)
+        self.side = _side_stream_if_parts(d, side_stream)
 
     def _gemm1_w4a4(self, w, s):
         d = self.d
@@ -555,24 +599,30 @@ class MoELayer:
         if marks:
             marks[0].record()
         if variant == "w4a4":
-            self._gemm1_w4a4(w, s)
-            if marks:
-                marks[1].record()
-            self._gemm2_w4a4(w, topk_w, out, s)
+            g1 = lambda part, st: call(
+                "grouped_gemm1_swiglu_part", ctypes.byref(d), _p(self.a1_q), _p(self.a1_sf),
+                _p(self.a1_deq), _p(self.g1), _p(self.al.sorted_pair), _p(self.al.offsets),
+                _p(self.al.plan), _p(w.prep13), _p(w.g13), _p(self.g2), _p(self.a2_q), _p(self.a2_sf),
+                _p(self.a2_deq), part, st)
+            g2 = lambda part, st: call(
+                "grouped_gemm2_combine_part", ctypes.byref(d), _p(self.a2_q), _p(self.a2_sf),
+                _p(self.a2_deq), _p(self.g2), _p(self.al.offsets), _p(self.al.inv_pos), _p(self.al.plan),
+                _p(topk_w), _p(w.prep2), _p(w.g2), _p(out), _dtype_code(out), _p(self.ws),
+                self.ws.numel() * 4, part, st)
+            side = self.side if self.decoded_copies else None
         elif variant == "w4a16":
-            call("grouped_gemm1_swiglu_w4a16", ctypes.byref(d), _p(x), _p(self.al.sorted_pair),
-                 _p(self.al.offsets), _p(self.al.plan), _p(w.prep13), _p(w.g13),
-                 _p(self.a2_bf16), s)
-            if marks:
-                marks[1].record()
-            call("grouped_gemm2_combine_w4a16", ctypes.byref(d), _p(self.a2_bf16),
-                 _p(self.al.offsets), _p(self.al.inv_pos), _p(self.al.plan), _p(topk_w),
-                 _p(w.prep2), _p(w.g2), _p(out), _dtype_code(out), _p(self.ws),
-                 self.ws.numel() * 4, s)
+            g1 = lambda part, st: call(
+                "grouped_gemm1_swiglu_w4a16_part", ctypes.byref(d), _p(x), _p(self.al.sorted_pair),
+                _p(self.al.offsets), _p(self.al.plan), _p(w.prep13), _p(w.g13), _p(self.a2_bf16), part, st)
+            g2 = lambda part, st: call(
+                "grouped_gemm2_combine_w4a16_part", ctypes.byref(d), _p(self.a2_bf16),
+                _p(self.al.offsets), _p(self.al.inv_pos), _p(self.al.plan), _p(topk_w),
+                _p(w.prep2), _p(w.g2), _p(out), _dtype_code(out), _p(self.ws),
+                self.ws.numel() * 4, part, st)
+            side = self.side
         else:
             raise ValueError(variant)
-        if marks:
-            marks[2].record()
+        _run_gemms(side, g1, g2, marks)
         return out
 
 

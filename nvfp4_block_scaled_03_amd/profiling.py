@@ -176,10 +176,10 @@ class MxStep:
     gemm2 with a variant argument), so that timing and profiling code drives
     both layers alike."""
 
-    def __init__(self, d, weights, dev):
+    def __init__(self, d, weights, dev, side_stream=None):
         from nvfp4_block_scaled_03_amd import ops
         self.d = d
-        self.layer = ops.MxMoELayer(d, weights, device=dev)
+        self.layer = ops.MxMoELayer(d, weights, device=dev, side_stream=side_stream)
 
     def forward(self, x, ids, tw, variant, out=None, weights=None, marks=None):
         return self.layer.forward(x, ids, tw, out=out, weights=weights, marks=marks)

@@ -250,3 +250,33 @@ def test_mx_layer_errors(lib):
                                            None) == _lib.NVFP4_EINVAL
     big = _d(T=1 << 17, H=1 << 15)
     assert lib.grouped_gemm1_swiglu_mxfp4(ctypes.byref(big), *([None] * 8), None) == _lib.NVFP4_ESHAPE
+
+
+def test_parts_query_and_errors(lib):
+    """grouped_gemm_runs_in_parts says which dims split their GEMMs (short
+    tiles on average with an expert that can exceed 64 rows); a part outside
+    0..2 (GEMM1) or 0..3 (GEMM2) is rejected before anything else, naming
+    the *_part call; a valid part reaches the named call's own checks."""
+    assert lib.grouped_gemm_runs_in_parts(ctypes.byref(_d())) == 0            # decode: 4 rows per expert
+    large_e = _d(T=256, topk=10, E=512, H=4096, I=1024, shared=1)
+    assert lib.grouped_gemm_runs_in_parts(ctypes.byref(large_e)) == 1
+    assert lib.grouped_gemm_runs_in_parts(ctypes.byref(_d(T=4096))) == 0      # tall tiles on average
+    assert lib.grouped_gemm_runs_in_parts(ctypes.byref(_d(E=0))) == 0         # invalid dims
+    r = ctypes.byref(_d())
+    for part in (-1, 3):
+        assert lib.grouped_gemm1_swiglu_part(r, *([None] * 13), part, None) == _lib.NVFP4_EINVAL
+        assert f"grouped_gemm1_swiglu_part: EINVAL part={part}" in _lib.last_error()
+        assert lib.grouped_gemm1_swiglu_w4a16_part(r, *([None] * 7), part, None) == _lib.NVFP4_EINVAL
+        assert lib.grouped_gemm1_swiglu_mxfp4_part(r, *([None] * 8), part, None) == _lib.NVFP4_EINVAL
+    for part in (-1, 4):
+        assert lib.grouped_gemm2_combine_part(r, *([None] * 10), None, 0, None, 0, part, None) == _lib.NVFP4_EINVAL
+        assert f"grouped_gemm2_combine_part: EINVAL part={part}" in _lib.last_error()
+        assert lib.grouped_gemm2_combine_w4a16_part(r, *([None] * 7), None, 0, None, 0, part,
+                                                    None) == _lib.NVFP4_EINVAL
+        assert lib.grouped_gemm2_combine_mxfp4_part(r, *([None] * 7), None, 0, None, 0, part,
+                                                    None) == _lib.NVFP4_EINVAL
+    # valid parts: the named call's checks (missing workspace, missing operands)
+    assert lib.grouped_gemm2_combine_part(r, *([None] * 10), None, 0, None, 0, 3, None) == _lib.NVFP4_EWORKSPACE
+    assert "grouped_gemm2_combine_part: EWORKSPACE" in _lib.last_error()
+    assert lib.grouped_gemm1_swiglu_part(r, *([None] * 13), 2, None) == _lib.NVFP4_EINVAL
+    assert "grouped_gemm1_swiglu_part: EINVAL null" in _lib.last_error()
