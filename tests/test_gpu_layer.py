@@ -220,9 +220,10 @@ def test_w4a16_stages(dev, w):
 
 
 # ---------------------------------------------------------------- whole layer
-def _run_layer(case: Case, dev, variant, decoded_copies=None):
+def _run_layer(case: Case, dev, variant, decoded_copies=None, side_stream=None):
     g2 = torch.tensor([float(case.g2)], device=dev)
-    layer = ops.MoELayer(case.d, case.wq, g2, device=dev, decoded_copies=decoded_copies)
+    layer = ops.MoELayer(case.d, case.wq, g2, device=dev, decoded_copies=decoded_copies,
+                         side_stream=side_stream)
     out32 = layer.forward(case.x, case.ids, case.tw, variant, out_dtype=torch.float32).clone()
     out16 = layer.forward(case.x, case.ids, case.tw, variant, out_dtype=torch.bfloat16).clone()
     torch.cuda.synchronize()
@@ -290,6 +291,19 @@ def test_layer_full_size_every_token(dev, name, variant, decoded):
     print(f"full-size {name} {variant} decoded={decoded}", flush=True)
     case = cached_case(name, dev)
     _judge_layer(case, dev, variant, decoded)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("variant", ["w4a4", "w4a16"])
+def test_layer_full_size_two_streams(dev, variant):
+    """The 512-expert layer as the benchmark runs it: the tall experts' GEMM1
+    and GEMM2 on a second stream beside the short experts', joined before the
+    combine; every token judged against the oracle."""
+    print(f"full-size large_e {variant} two streams", flush=True)
+    case = cached_case("large_e", dev)
+    run = _run_layer(case, dev, variant, side_stream=torch.cuda.Stream())
+    assert run[0].side is not None
+    _judge_layer(case, dev, variant, run=run)
 
 
 def _rows_of(case, e):
