@@ -792,6 +792,7 @@ __device__ __forceinline__ void mx_tall_body(const MxMoeParams& p, uint8_t (*sa)
   // l taking row (l >> 3) + 8 h of its tile, bytes [16 (l & 3), +16) of chunk
   // kc0 + ((l >> 2) & 1), i.e. 128 contiguous bytes per row.
   constexpr bool PAIR = KCT > 0;
+  static_assert(KCT % 2 == 0, "pair gathers take whole chunk pairs");
   const int half = (lane >> 2) & 1;
   uint32_t vrow[AW][2];
 #pragma unroll
